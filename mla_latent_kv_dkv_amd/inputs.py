@@ -1,0 +1,222 @@
+"""Seeded synthetic inputs for the MLA decode workloads (no method arithmetic here).
+
+This module is the only thing the fp64 oracle and the GPU library have in
+common: it draws numbers, builds page tables and lengths, and nothing else.
+
+Generator (counter based, so any element can be produced on its own and the
+host and the GPU produce identical bits):
+
+* SplitMix64 (Steele, Lea & Flood, "Fast splittable pseudorandom number
+  generators", OOPSLA 2014): element ``i`` of a stream with key ``K`` is
+  ``mix64(K + (i+1)*GAMMA)`` with the published GAMMA and mixing constants.
+* A roughly normal value is the Irwin-Hall sum of the four 16-bit fields of
+  that word, centred: ``s = f0+f1+f2+f3 - 131070`` (an integer, exact in fp32),
+  then ``float32(s) * float32(std / sqrt(4*(65536**2-1)/12))`` -- one IEEE fp32
+  multiply -- and, for bf16 storage, round-to-nearest-even to bf16.
+* A uniform value in [0, 1) is ``(word >> 11) * 2**-53``.
+
+Stream keys are derived on the host from (seed, tensor name, layer) and passed
+to the device fill kernel as a 64-bit integer, so only ``mix64`` needs a device
+twin (in ``csrc/fill_inputs.hip``).
+"""
+from __future__ import annotations
+
+import math
+import zlib
+from dataclasses import dataclass, field
+
+import numpy as np
+
+GAMMA = np.uint64(0x9E3779B97F4A7C15)
+_M1 = np.uint64(0xBF58476D1CE4E5B9)
+_M2 = np.uint64(0x94D049BB133111EB)
+_IH_STD = math.sqrt(4.0 * (65536.0 ** 2 - 1.0) / 12.0)   # std of the 4-field sum
+_CHUNK = 1 << 22
+
+
+def mix64(z):
+    """SplitMix64 output mixing of a uint64 array (wrapping arithmetic)."""
+    z = np.asarray(z, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        z = (z ^ (z >> np.uint64(30))) * _M1
+        z = (z ^ (z >> np.uint64(27))) * _M2
+    return z ^ (z >> np.uint64(31))
+
+
+def stream_key(seed: int, name: str, layer: int = 0) -> int:
+    """64-bit stream key of tensor ``name`` (layer ``layer``) under ``seed``."""
+    tag = (zlib.crc32(name.encode()) << 16) ^ (layer & 0xFFFF)
+    with np.errstate(over="ignore"):
+        k = mix64(np.uint64(seed) + GAMMA)
+        k = mix64(k ^ (np.uint64(tag) + GAMMA))
+    return int(k)
+
+
+def words(key: int, start: int, n: int) -> np.ndarray:
+    """uint64 words ``start .. start+n-1`` of stream ``key``."""
+    idx = np.arange(start + 1, start + n + 1, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        return mix64(np.uint64(key) + idx * GAMMA)
+
+
+def normal_scale(std: float) -> np.float32:
+    """The single fp32 factor applied to the centred Irwin-Hall integer."""
+    return np.float32(std / _IH_STD)
+
+
+def normal_f32(key: int, start: int, n: int, std: float = 1.0) -> np.ndarray:
+    """fp32 values ``start .. start+n-1`` of stream ``key`` (approximately N(0, std^2))."""
+    out = np.empty(n, dtype=np.float32)
+    sc = normal_scale(std)
+    m16 = np.uint64(0xFFFF)
+    for a in range(0, n, _CHUNK):
+        b = min(n, a + _CHUNK)
+        w = words(key, start + a, b - a)
+        s = ((w & m16) + ((w >> np.uint64(16)) & m16) + ((w >> np.uint64(32)) & m16)
+             + (w >> np.uint64(48))).astype(np.int64) - 131070
+        out[a:b] = s.astype(np.float32) * sc
+    return out
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round-to-nearest-even fp32 -> bf16, returned as uint16 bit patterns."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    b = b + np.uint64(0x7FFF) + ((b >> np.uint64(16)) & np.uint64(1))
+    return (b >> np.uint64(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(
+        np.float32).astype(np.float64)
+
+
+def uniform01(key: int, start: int, n: int) -> np.ndarray:
+    return (words(key, start, n) >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
+
+
+# ----------------------------------------------------------------- workloads --
+@dataclass(frozen=True)
+class Workload:
+    """One decode-step workload: model dims, batch structure and seed."""
+    name: str
+    hidden: int
+    n_heads: int
+    d_head: int
+    d_latent: int
+    d_rope: int
+    dtype: str                      # "f32" | "bf16" storage; accumulation is fp32
+    batch: int
+    context: int                    # fixed length (ignored when ``ragged``)
+    seed: int
+    num_splits: int = 1
+    layers: int = 1
+    ragged: tuple = ()              # (lo, hi) for log-uniform lengths, else ()
+    permute_pages: bool = True
+    cache_from_h: bool = False      # build the cache through the append call
+    page_size: int = 64
+    rope_base: float = 10000.0
+    notes: str = field(default="", compare=False)
+
+    @property
+    def row(self) -> int:
+        return self.d_latent + self.d_rope
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    def fan_in(self, name: str) -> int:
+        return {"w_q": self.hidden, "w_qr": self.hidden, "w_dkv": self.hidden,
+                "w_kr": self.hidden, "w_uk": self.d_latent, "w_uv": self.d_latent,
+                "w_o": self.n_heads * self.d_head}[name]
+
+    def weight_shape(self, name: str) -> tuple:
+        nh, dh, dc, dr, H = self.n_heads, self.d_head, self.d_latent, self.d_rope, self.hidden
+        return {"w_q": (nh * dh, H), "w_qr": (nh * dr, H), "w_dkv": (dc, H), "w_kr": (dr, H),
+                "w_uk": (nh * dh, dc), "w_uv": (nh * dh, dc), "w_o": (H, nh * dh)}[name]
+
+
+WEIGHT_NAMES = ("w_q", "w_qr", "w_dkv", "w_kr", "w_uk", "w_uv", "w_o")
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 64, 4, 16, 32, 8, "f32", 1, 64, 1001, num_splits=1,
+                     permute_pages=False, cache_from_h=True),
+    "lite": Workload("lite", 2048, 16, 128, 512, 64, "bf16", 32, 4096, 1002, num_splits=2,
+                     cache_from_h=True),
+    "full": Workload("full", 5120, 128, 128, 512, 64, "bf16", 64, 4096, 1003, num_splits=4),
+    "long": Workload("long", 5120, 128, 128, 512, 64, "bf16", 4, 131072, 1004, num_splits=64),
+    "ragged": Workload("ragged", 5120, 128, 128, 512, 64, "bf16", 256, 0, 1005, num_splits=16,
+                       layers=60, ragged=(512, 32768)),
+}
+
+
+def seq_lengths(w: Workload) -> np.ndarray:
+    """Context length of every sequence (the decode token included).  Ragged
+    workloads draw L = min(hi, floor(lo * (hi/lo)**u)), u uniform in [0, 1)."""
+    if not w.ragged:
+        return np.full(w.batch, w.context, dtype=np.int32)
+    lo, hi = w.ragged
+    u = uniform01(stream_key(w.seed, "lengths"), 0, w.batch)
+    return np.minimum(hi, np.floor(lo * np.power(hi / lo, u))).astype(np.int32)
+
+
+def page_table(w: Workload, lens: np.ndarray):
+    """(block_table [B, max_pages] int32, num_pages).  Every sequence owns
+    ceil(L/page) pages; physical ids are a seeded permutation (identity when
+    ``permute_pages`` is off); unused table entries hold 0."""
+    pages = (lens.astype(np.int64) + w.page_size - 1) // w.page_size
+    total = int(pages.sum())
+    max_pages = int(pages.max())
+    if w.permute_pages:
+        keys = words(stream_key(w.seed, "page_perm"), 0, total)
+        perm = np.argsort(keys, kind="stable").astype(np.int32)
+    else:
+        perm = np.arange(total, dtype=np.int32)
+    bt = np.zeros((w.batch, max_pages), dtype=np.int32)
+    off = 0
+    for b in range(w.batch):
+        bt[b, :pages[b]] = perm[off:off + pages[b]]
+        off += pages[b]
+    return bt, total
+
+
+def tensor_values(w: Workload, name: str, shape, std: float = 1.0, layer: int = 0,
+                  start: int = 0, count: int | None = None) -> np.ndarray:
+    """Host copy of a seeded tensor in its storage format: fp32 values, or bf16
+    bit patterns (uint16) for bf16 workloads.  ``start``/``count`` select a flat
+    sub-range (the same elements the device fill writes there)."""
+    n = int(np.prod(shape)) if count is None else count
+    v = normal_f32(stream_key(w.seed, name, layer), start, n, std)
+    if count is None:
+        v = v.reshape(shape)
+    return v if w.dtype == "f32" else f32_to_bf16_bits(v)
+
+
+def weight_values(w: Workload, name: str, layer: int = 0) -> np.ndarray:
+    return tensor_values(w, name, w.weight_shape(name), 1.0 / math.sqrt(w.fan_in(name)), layer)
+
+
+def to_f64(w: Workload, arr: np.ndarray) -> np.ndarray:
+    """Upcast storage-format values (fp32, or bf16 bits) to fp64."""
+    return np.asarray(arr, dtype=np.float64) if w.dtype == "f32" else bf16_bits_to_f64(arr)
+
+
+def pool_rows(w: Workload, block_table: np.ndarray, seq: int, length: int, layer: int = 0):
+    """Storage-format pool rows of logical positions 0..length-1 of ``seq`` as the
+    device fill leaves them (the pool is filled linearly by physical element
+    index, stream "pool")."""
+    pos = np.arange(length)
+    phys = block_table[seq, pos // w.page_size].astype(np.int64) * w.page_size + pos % w.page_size
+    key = stream_key(w.seed, "pool", layer)
+    # contiguous runs of physical rows share one generator call
+    out = np.empty((length, w.row), dtype=np.float32 if w.dtype == "f32" else np.uint16)
+    j = 0
+    while j < length:
+        k = j
+        while k + 1 < length and phys[k + 1] == phys[k] + 1:
+            k += 1
+        v = normal_f32(key, int(phys[j]) * w.row, (k - j + 1) * w.row, 1.0)
+        v = v if w.dtype == "f32" else f32_to_bf16_bits(v)
+        out[j:k + 1] = v.reshape(k - j + 1, w.row)
+        j = k + 1
+    return out

@@ -1,0 +1,255 @@
+"""Plain, slow fp64 CPU oracle for one Multi-head Latent Attention (MLA) decode step.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module.  The GPU
+library never routes through it, and it shares no code, constant or helper with
+the HIP path; it imports numpy and nothing else.
+
+Sources (web pages, cited by title and section):
+  [Report]  "《DeepSeek-V2》深度解读报告" (zako-mio.github.io knowledge base):
+            §2.1 KV cache, §2.2 low-rank key-value joint compression,
+            §2.3 absorption, §2.4 decoupled RoPE, §3.1 full MLA data flow.
+  [Wiki]    "DeepSeek-V2" paper notes (wiki.hugogu.cn): the MLA inference flow
+            (latent cached, all history decompressed to per-head K/V, then
+            attention) and the decode timeline (Q is never cached).
+  [Digest]  "DeepSeek-V2论文解读 ... KV缓存压93.3%" (xdnf.cn), §2.1: cache size
+            2*n_h*d_h*l for MHA versus one latent per token for MLA.
+
+What is computed here is the NON-ABSORBED definition: per-head keys and values
+are decompressed explicitly from the cached latent and attention runs per head
+in fp64 ([Wiki] inference flow; [Report] §2.2).  A separately written absorbed
+companion ([Report] §2.3) is provided for cheap coverage of large inputs; the
+two must agree to rounding (associativity), which is one of the pins.
+
+Readings taken where the pages are silent (all inline formulas were lost):
+  * softmax scale tau = 1/sqrt(d_h + d_R) unless the caller passes one;
+  * RoPE rotates adjacent pairs (x[2k], x[2k+1]) by angle pos*theta_k with
+    theta_k = base**(-2k/d_R); angles in fp64;
+  * decode position t = L-1: the new token is appended first and attends to
+    positions 0..L-1 inclusive;
+  * no query compression (q^C = W_Q h); no norm on the latent;
+  * head i owns rows i*d_h:(i+1)*d_h of W_Q, W_UK, W_UV (and i*d_R:(i+1)*d_R
+    of W_QR) and columns i*d_h:(i+1)*d_h of W_O;
+  * cache row = [c^KV (d_c) | k^R (d_R)]; paged in pages of ``page_size`` rows:
+    logical position j of sequence b lives in physical row
+    block_table[b][j // page_size] * page_size + j % page_size;
+  * split s of a sequence of length L under S splits covers logical positions
+    [s*chunk, min(L, (s+1)*chunk)) with chunk = page_size*ceil(ceil(L/S)/page_size);
+    an empty split has lse = -inf and a zero output.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "rope_theta", "rope", "latent_rows", "page_slot", "query_heads",
+    "mla_decode_step", "mla_decode_step_absorbed", "split_bounds",
+    "attention_partials", "merge_lse", "absorb_q", "absorb_out",
+    "mla_cache_elems_per_token", "mha_cache_elems_per_token",
+]
+
+
+def _f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+# ---------------------------------------------------------------- positions --
+def rope_theta(d_rope: int, base: float) -> np.ndarray:
+    """theta_k = base**(-2k/d_R), k = 0..d_R/2-1 ([Report] §2.4: RoPE acts only on
+    the decoupled d_R-wide branch; base 10000 per the workload definitions)."""
+    k = np.arange(d_rope // 2, dtype=np.float64)
+    return np.power(float(base), -2.0 * k / d_rope)
+
+
+def rope(x, pos, base: float) -> np.ndarray:
+    """Rotate adjacent pairs of the last axis of ``x`` by pos*theta_k.
+
+    ``pos`` broadcasts against ``x.shape[:-1]``.  [Report] §2.4: the decoupled
+    query q^R and the shared key k^R carry the position; nothing else does.
+    """
+    x = _f64(x)
+    d = x.shape[-1]
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * rope_theta(d, base)
+    c, s = np.cos(ang), np.sin(ang)
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    y = np.empty_like(x)
+    y[..., 0::2] = x0 * c - x1 * s
+    y[..., 1::2] = x0 * s + x1 * c
+    return y
+
+
+# -------------------------------------------------------------- cache rows --
+def latent_rows(h, w_dkv, w_kr, pos, base: float) -> np.ndarray:
+    """Cache rows [c^KV | k^R] for hidden states ``h`` [N, H] at positions ``pos``.
+
+    c^KV = W_DKV h ([Report] §2.2: the joint down-projection; the latent is the
+    only K/V object that is cached) and k^R = RoPE(W_KR h, pos) ([Report] §2.4:
+    one RoPE key shared by every head, also cached).  Row width d_c + d_R.
+    """
+    h = _f64(h)
+    c = h @ _f64(w_dkv).T
+    kr = rope(h @ _f64(w_kr).T, pos, base)
+    return np.concatenate([c, kr], axis=-1)
+
+
+def page_slot(block_table, seq: int, pos, page_size: int = 64):
+    """Physical row of logical position(s) ``pos`` of sequence ``seq`` in a paged
+    pool (paged cache management is named in [Digest] §3.1; the page size and
+    the permuted page table are workload parameters)."""
+    pos = np.asarray(pos, dtype=np.int64)
+    bt = np.asarray(block_table, dtype=np.int64)
+    return bt[seq, pos // page_size] * page_size + pos % page_size
+
+
+def gather_rows(pool, block_table, seq: int, length: int, page_size: int = 64):
+    """Logical rows 0..length-1 of sequence ``seq`` read out of a paged pool
+    [num_pages, page_size, row] (any float dtype), upcast to fp64."""
+    flat = np.asarray(pool).reshape(-1, np.asarray(pool).shape[-1])
+    return _f64(flat[page_slot(block_table, seq, np.arange(length), page_size)])
+
+
+# ------------------------------------------------------------------- query --
+def query_heads(h_t, w_q, w_qr, pos: int, n_heads: int, d_head: int, d_rope: int,
+                base: float):
+    """q^C_i = W_Q,i h_t (d_h) and q^R_i = RoPE(W_QR,i h_t, t) (d_R) per head
+    ([Report] §3.1 data flow: per-head RoPE query from h_t; query is not cached,
+    [Wiki] decode timeline).  Returns ([n_h, d_h], [n_h, d_R])."""
+    h_t = _f64(h_t)
+    qc = (_f64(w_q) @ h_t).reshape(n_heads, d_head)
+    qr = rope((_f64(w_qr) @ h_t).reshape(n_heads, d_rope), pos, base)
+    return qc, qr
+
+
+def _default_scale(d_head: int, d_rope: int, scale):
+    return 1.0 / math.sqrt(d_head + d_rope) if (scale is None or scale <= 0) else float(scale)
+
+
+# -------------------------------------------------- the definition (oracle) --
+def mla_decode_step(h_t, rows, w_q, w_qr, w_uk, w_uv, w_o, pos: int, n_heads: int,
+                    d_head: int, d_latent: int, d_rope: int, base: float, scale=None):
+    """Non-absorbed MLA decode for one sequence, fp64.
+
+    ``rows`` [L, d_c + d_R] are the cached rows of logical positions 0..L-1 (the
+    decode token's own row included, at L-1 = ``pos``).  For each head i:
+      k^C_{j,i} = W_UK,i c_j, v^C_{j,i} = W_UV,i c_j      ([Report] §2.2)
+      k_{j,i} = [k^C_{j,i}; k^R_j],  q_i = [q^C_i; q^R_i]   ([Report] §2.4, the
+                content-channel and RoPE-channel scores add up)
+      p_i = softmax_j(tau * q_i . k_{j,i}),  o_i = sum_j p_ij v^C_{j,i}
+    then u = W_O [o_1; ...; o_n_h].  Returns dict(u [H], o [n_h, d_h],
+    lse [n_h]) where lse_i = log sum_j exp(s_ij).
+    """
+    rows = _f64(rows)
+    c, kr = rows[:, :d_latent], rows[:, d_latent:d_latent + d_rope]
+    tau = _default_scale(d_head, d_rope, scale)
+    qc, qr = query_heads(h_t, w_q, w_qr, pos, n_heads, d_head, d_rope, base)
+    w_uk, w_uv = _f64(w_uk), _f64(w_uv)
+    o = np.zeros((n_heads, d_head))
+    lse = np.zeros(n_heads)
+    for i in range(n_heads):
+        blk = slice(i * d_head, (i + 1) * d_head)
+        k_c = c @ w_uk[blk].T                      # [L, d_h] decompressed keys
+        v_c = c @ w_uv[blk].T                      # [L, d_h] decompressed values
+        k = np.concatenate([k_c, kr], axis=1)      # per-head key with shared RoPE key
+        q = np.concatenate([qc[i], qr[i]])
+        s = tau * (k @ q)
+        m = s.max()
+        e = np.exp(s - m)
+        z = e.sum()
+        o[i] = (e / z) @ v_c
+        lse[i] = m + math.log(z)
+    u = _f64(w_o) @ o.reshape(-1)
+    return {"u": u, "o": o, "lse": lse, "q_c": qc, "q_r": qr}
+
+
+# ------------------------------------------------ absorbed fp64 companion --
+def absorb_q(h_t, w_q, w_qr, w_uk, pos: int, n_heads: int, d_head: int, d_latent: int,
+             d_rope: int, base: float):
+    """Absorbed query: q_lat,i = W_UK,i^T q^C_i ([Report] §2.3: q.(W_UK c) is
+    regrouped as (W_UK^T q).c) and q_pe,i = q^R_i.  Returns ([n_h, d_c], [n_h, d_R])."""
+    qc, qr = query_heads(h_t, w_q, w_qr, pos, n_heads, d_head, d_rope, base)
+    w_uk = _f64(w_uk).reshape(n_heads, d_head, d_latent)
+    q_lat = np.einsum("ihc,ih->ic", w_uk, qc)
+    return q_lat, qr
+
+
+def absorb_out(o_lat, w_uv, w_o, n_heads: int, d_head: int, d_latent: int):
+    """Absorbed output for one token: o_i = W_UV,i o_lat,i, u = W_O [o_1..o_n_h]
+    ([Report] §2.3: W_UV is folded into the output projection)."""
+    w_uv = _f64(w_uv).reshape(n_heads, d_head, d_latent)
+    o = np.einsum("ihc,ic->ih", w_uv, _f64(o_lat))
+    return _f64(w_o) @ o.reshape(-1)
+
+
+def _latent_attention(q_lat, q_pe, rows, d_latent: int, d_rope: int, tau: float):
+    """Attention of every head over latent rows: s_ij = tau (q_lat,i.c_j + q_pe,i.k^R_j).
+    Returns (o_lat [n_h, d_c], lse [n_h]); an empty row set gives (0, -inf)."""
+    rows = _f64(rows)
+    n_h = np.asarray(q_lat).shape[0]
+    if rows.shape[0] == 0:
+        return np.zeros((n_h, d_latent)), np.full(n_h, -np.inf)
+    c, kr = rows[:, :d_latent], rows[:, d_latent:d_latent + d_rope]
+    s = tau * (_f64(q_lat) @ c.T + _f64(q_pe) @ kr.T)        # [n_h, L]
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    z = e.sum(axis=1, keepdims=True)
+    return (e / z) @ c, (m + np.log(z))[:, 0]
+
+
+def mla_decode_step_absorbed(h_t, rows, w_q, w_qr, w_uk, w_uv, w_o, pos: int,
+                             n_heads: int, d_head: int, d_latent: int, d_rope: int,
+                             base: float, scale=None):
+    """Absorbed fp64 form of :func:`mla_decode_step` (same inputs): attention runs
+    in the d_c-wide latent space and per-head K/V are never formed ([Report]
+    §2.3).  Returns dict(u, q_lat, q_pe, o_lat, lse)."""
+    tau = _default_scale(d_head, d_rope, scale)
+    q_lat, q_pe = absorb_q(h_t, w_q, w_qr, w_uk, pos, n_heads, d_head, d_latent, d_rope, base)
+    o_lat, lse = _latent_attention(q_lat, q_pe, rows, d_latent, d_rope, tau)
+    u = absorb_out(o_lat, w_uv, w_o, n_heads, d_head, d_latent)
+    return {"u": u, "q_lat": q_lat, "q_pe": q_pe, "o_lat": o_lat, "lse": lse}
+
+
+# ------------------------------------------------------- split and merge --
+def split_bounds(length: int, num_splits: int, page_size: int = 64):
+    """[(start, end)] of each split: page-aligned equal chunks, trailing splits empty."""
+    per = -(-length // num_splits)
+    chunk = page_size * (-(-per // page_size))
+    return [(min(length, s * chunk), min(length, (s + 1) * chunk)) for s in range(num_splits)]
+
+
+def attention_partials(q_lat, q_pe, rows, num_splits: int, d_latent: int, d_rope: int,
+                       scale: float, page_size: int = 64):
+    """Per-split partial attention of one sequence: for each split s,
+    (o_s [n_h, d_c] normalised within the split, lse_s [n_h])."""
+    out_o, out_l = [], []
+    for (a, b) in split_bounds(_f64(rows).shape[0], num_splits, page_size):
+        o, l = _latent_attention(q_lat, q_pe, _f64(rows)[a:b], d_latent, d_rope, scale)
+        out_o.append(o)
+        out_l.append(l)
+    return np.stack(out_o), np.stack(out_l)
+
+
+def merge_lse(o_parts, lse_parts):
+    """Combine split partials: lse* = max_s lse_s, w_s = exp(lse_s - lse*),
+    o = sum_s w_s o_s / sum_s w_s, lse = lse* + log sum_s w_s.  Splits with
+    lse = -inf carry zero weight.  o_parts [S, ..., d], lse_parts [S, ...]."""
+    o_parts, lse_parts = _f64(o_parts), _f64(lse_parts)
+    top = lse_parts.max(axis=0)
+    safe = np.where(np.isfinite(top), top, 0.0)
+    w = np.where(np.isfinite(lse_parts), np.exp(lse_parts - safe), 0.0)
+    z = w.sum(axis=0)
+    o = (w[..., None] * o_parts).sum(axis=0) / np.where(z > 0, z, 1.0)[..., None]
+    lse = np.where(z > 0, safe + np.log(np.where(z > 0, z, 1.0)), -np.inf)
+    return o, lse
+
+
+# ------------------------------------------------------------ cache sizes --
+def mla_cache_elems_per_token(d_latent: int, d_rope: int, layers: int = 1) -> int:
+    """Elements cached per token: (d_c + d_R) per layer ([Report] §2.4, §3.1)."""
+    return (d_latent + d_rope) * layers
+
+
+def mha_cache_elems_per_token(n_heads: int, d_head: int, layers: int = 1) -> int:
+    """MHA caches K and V per head: 2 n_h d_h per layer ([Digest] §2.1; [Report] §2.1)."""
+    return 2 * n_heads * d_head * layers

@@ -1,0 +1,346 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself.
+
+Each test names what fixes the expected value: numbers printed on the pages
+(tests/golden/), closed forms, textbook special cases written independently
+here (multi-head attention, a multi-query RoPE channel, RoPE as a complex
+multiplication), library routines (torch scaled_dot_product_attention,
+scipy logsumexp) and brute force on tiny inputs.
+"""
+import cmath
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _weights(rng, H, nh, dh, dc, dr):
+    return dict(
+        w_q=rng.normal(size=(nh * dh, H)) / math.sqrt(H),
+        w_qr=rng.normal(size=(nh * dr, H)) / math.sqrt(H),
+        w_dkv=rng.normal(size=(dc, H)) / math.sqrt(H),
+        w_kr=rng.normal(size=(dr, H)) / math.sqrt(H),
+        w_uk=rng.normal(size=(nh * dh, dc)) / math.sqrt(dc),
+        w_uv=rng.normal(size=(nh * dh, dc)) / math.sqrt(dc),
+        w_o=rng.normal(size=(H, nh * dh)) / math.sqrt(nh * dh),
+    )
+
+
+def _complex_rope(x, pos, base):
+    """RoPE written independently: pair (x[2k], x[2k+1]) as the complex number
+    x[2k] + i x[2k+1], multiplied by exp(i * pos * base**(-2k/d))."""
+    d = len(x)
+    out = []
+    for k in range(d // 2):
+        z = complex(x[2 * k], x[2 * k + 1]) * cmath.exp(1j * pos * base ** (-2.0 * k / d))
+        out += [z.real, z.imag]
+    return np.array(out)
+
+
+# ------------------------------------------------------------------- RoPE --
+def test_rope_closed_form_values():
+    # d=2: theta_0 = 1, so [1, 0] at position 1 becomes [cos 1, sin 1]
+    np.testing.assert_allclose(O.rope(np.array([1.0, 0.0]), 1, 10000.0),
+                               [math.cos(1.0), math.sin(1.0)], rtol=0, atol=1e-15)
+    # d=4, base 10000: theta_1 = 10000**(-1/2) = 0.01; position 100 turns pair 1 by 1 rad
+    np.testing.assert_allclose(O.rope(np.array([0.0, 0.0, 1.0, 0.0]), 100, 10000.0),
+                               [0.0, 0.0, math.cos(1.0), math.sin(1.0)], atol=1e-14)
+    # pair 0 at position 100 turns by 100 rad; [0, 1] -> [-sin, cos]
+    np.testing.assert_allclose(O.rope(np.array([0.0, 1.0, 0.0, 0.0]), 100, 10000.0),
+                               [-math.sin(100.0), math.cos(100.0), 0.0, 0.0], atol=1e-13)
+
+
+def test_rope_matches_complex_multiplication():
+    rng = _rng(1)
+    for d, pos, base in [(8, 0, 10000.0), (8, 63, 10000.0), (64, 4095, 10000.0),
+                         (64, 131071, 10000.0), (6, 17, 500.0)]:
+        x = rng.normal(size=d)
+        # fp64 angle pos*theta carries ~pos * 1e-16 rad of rounding in either form
+        np.testing.assert_allclose(O.rope(x, pos, base), _complex_rope(x, pos, base),
+                                   rtol=0, atol=1e-12 + 4e-15 * pos)
+
+
+def test_rope_invariants():
+    rng = _rng(2)
+    q, k = rng.normal(size=64), rng.normal(size=64)
+    np.testing.assert_array_equal(O.rope(q, 0, 10000.0), q)
+    for m in (1, 77, 131071):
+        assert abs(np.linalg.norm(O.rope(q, m, 10000.0)) - np.linalg.norm(q)) < 1e-12
+    # the score of a rotated pair depends only on the offset m - n
+    ref = O.rope(q, 40, 10000.0) @ O.rope(k, 15, 10000.0)
+    for shift in (1, 1000, 90000):
+        got = O.rope(q, 40 + shift, 10000.0) @ O.rope(k, 15 + shift, 10000.0)
+        assert abs(got - ref) < 1e-9 * max(1.0, abs(ref))
+
+
+# ---------------------------------------------------------- cache sizes --
+def test_cache_sizes_match_printed_numbers():
+    g = json.load(open(os.path.join(GOLDEN, "cache_sizes.json")))
+    d = g["full_model_dims"]
+    nh, dh, dc, dr, layers = d["n_heads"], d["d_head"], d["d_latent"], d["d_rope"], d["layers"]
+    assert O.mla_cache_elems_per_token(dc, dr) == g["mla_elems_per_token_per_layer"]["value"]
+    assert O.mla_cache_elems_per_token(dc, dr, layers) == g["mla_elems_per_token_60_layers"]["value"]
+    lat = g["latent_vs_per_head_kv_width"]
+    assert nh * dh == lat["per_head_kv"] and lat["per_head_kv"] // dc == lat["ratio"]
+    # GQA with g groups caches 2*g*d_h per token per layer
+    assert O.mla_cache_elems_per_token(dc, dr) / (2 * dh) == g["gqa_equivalent_groups"]["value"]
+    assert dr * 2 == dh
+    mha = g["mha_elems_per_token_60_layers_printed"]
+    assert O.mha_cache_elems_per_token(nh, dh, layers) == mha["formula_value"]
+    assert abs(O.mha_cache_elems_per_token(nh, dh, layers) / O.mla_cache_elems_per_token(dc, dr, layers)
+               - 56.888) < 1e-2
+
+
+def test_cache_row_width_is_latent_plus_rope():
+    rng = _rng(3)
+    H, dc, dr = 24, 12, 6
+    rows = O.latent_rows(rng.normal(size=(5, H)), rng.normal(size=(dc, H)),
+                         rng.normal(size=(dr, H)), np.arange(5), 10000.0)
+    assert rows.shape == (5, O.mla_cache_elems_per_token(dc, dr))
+
+
+def test_latent_rows_brute_force():
+    rng = _rng(4)
+    H, dc, dr = 10, 6, 4
+    h = rng.normal(size=(3, H))
+    wd, wk = rng.normal(size=(dc, H)), rng.normal(size=(dr, H))
+    rows = O.latent_rows(h, wd, wk, np.array([0, 5, 9]), 10000.0)
+    for r, p in enumerate([0, 5, 9]):
+        c = [sum(wd[a, b] * h[r, b] for b in range(H)) for a in range(dc)]
+        k = [sum(wk[a, b] * h[r, b] for b in range(H)) for a in range(dr)]
+        np.testing.assert_allclose(rows[r], np.concatenate([c, _complex_rope(k, p, 10000.0)]),
+                                   rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------- paging --
+def test_page_slot_brute_force():
+    page = 4
+    bt = np.array([[5, 2, 0], [1, 4, 3]])
+    expect = {}
+    for b in range(2):
+        for j in range(12):
+            expect[(b, j)] = bt[b][j // page] * page + (j % page)
+    for (b, j), slot in expect.items():
+        assert O.page_slot(bt, b, j, page) == slot
+    slots = sorted(expect.values())
+    assert slots == list(range(24))          # the table covers every physical row once
+    pool = np.full((6, page, 3), np.nan)
+    for (b, j), slot in expect.items():
+        pool.reshape(-1, 3)[slot] = [b, j, -j]
+    for b in range(2):
+        got = O.gather_rows(pool, bt, b, 11, page)
+        np.testing.assert_array_equal(got[:, 0], b)
+        np.testing.assert_array_equal(got[:, 1], np.arange(11))
+
+
+# --------------------------------------------- MLA reduces to plain MHA --
+def _mha_triple_loop(h_ctx, h_t, wq, wk, wv, wo, nh, dh, tau):
+    L, H = h_ctx.shape
+    q = [sum(wq[r, c] * h_t[c] for c in range(H)) for r in range(nh * dh)]
+    k = [[sum(wk[r, c] * h_ctx[j, c] for c in range(H)) for r in range(nh * dh)] for j in range(L)]
+    v = [[sum(wv[r, c] * h_ctx[j, c] for c in range(H)) for r in range(nh * dh)] for j in range(L)]
+    o = []
+    for i in range(nh):
+        s = [tau * sum(q[i * dh + a] * k[j][i * dh + a] for a in range(dh)) for j in range(L)]
+        m = max(s)
+        e = [math.exp(x - m) for x in s]
+        z = sum(e)
+        o += [sum(e[j] / z * v[j][i * dh + a] for j in range(L)) for a in range(dh)]
+    return np.array([sum(wo[r, c] * o[c] for c in range(nh * dh)) for r in range(wo.shape[0])])
+
+
+def _mha_as_mla(rng, H, nh, dh, dr):
+    """MLA weights that make MLA equal MHA: d_c = 2 n_h d_h, W_DKV = [W_K; W_V],
+    W_UK / W_UV select head i's K / V block, W_QR = 0 (RoPE channel adds 0)."""
+    dc = 2 * nh * dh
+    wq, wk, wv = (rng.normal(size=(nh * dh, H)) for _ in range(3))
+    wo = rng.normal(size=(H, nh * dh))
+    w_uk = np.zeros((nh * dh, dc))
+    w_uv = np.zeros((nh * dh, dc))
+    for r in range(nh * dh):
+        w_uk[r, r] = 1.0
+        w_uv[r, nh * dh + r] = 1.0
+    mla = dict(w_q=wq, w_qr=np.zeros((nh * dr, H)), w_dkv=np.concatenate([wk, wv]),
+               w_kr=rng.normal(size=(dr, H)), w_uk=w_uk, w_uv=w_uv, w_o=wo)
+    return mla, (wq, wk, wv, wo), dc
+
+
+@pytest.mark.parametrize("H,nh,dh,dr,L", [(6, 2, 3, 2, 5), (8, 3, 2, 4, 7), (5, 1, 4, 2, 1)])
+def test_mla_reduces_to_mha(H, nh, dh, dr, L):
+    rng = _rng(10 + L)
+    mla, (wq, wk, wv, wo), dc = _mha_as_mla(rng, H, nh, dh, dr)
+    h_ctx = rng.normal(size=(L, H))
+    rows = O.latent_rows(h_ctx, mla["w_dkv"], mla["w_kr"], np.arange(L), 10000.0)
+    tau = 1.0 / math.sqrt(dh + dr)
+    for fn in (O.mla_decode_step, O.mla_decode_step_absorbed):
+        out = fn(h_ctx[-1], rows, mla["w_q"], mla["w_qr"], mla["w_uk"], mla["w_uv"], mla["w_o"],
+                 L - 1, nh, dh, dc, dr, 10000.0)
+        ref = _mha_triple_loop(h_ctx, h_ctx[-1], wq, wk, wv, wo, nh, dh, tau)
+        np.testing.assert_allclose(out["u"], ref, rtol=1e-10, atol=1e-10)
+
+
+def test_mla_as_mha_matches_torch_sdpa():
+    torch = pytest.importorskip("torch")
+    rng = _rng(20)
+    H, nh, dh, dr, L = 16, 4, 8, 4, 33
+    mla, (wq, wk, wv, wo), dc = _mha_as_mla(rng, H, nh, dh, dr)
+    h_ctx = rng.normal(size=(L, H))
+    rows = O.latent_rows(h_ctx, mla["w_dkv"], mla["w_kr"], np.arange(L), 10000.0)
+    out = O.mla_decode_step(h_ctx[-1], rows, mla["w_q"], mla["w_qr"], mla["w_uk"], mla["w_uv"],
+                            mla["w_o"], L - 1, nh, dh, dc, dr, 10000.0)
+    tau = 1.0 / math.sqrt(dh + dr)
+    q = torch.tensor(wq @ h_ctx[-1]).view(1, nh, 1, dh)
+    k = torch.tensor(h_ctx @ wk.T).view(1, L, nh, dh).transpose(1, 2).contiguous()
+    v = torch.tensor(h_ctx @ wv.T).view(1, L, nh, dh).transpose(1, 2).contiguous()
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=tau)
+    ref = wo @ o.reshape(-1).numpy()
+    np.testing.assert_allclose(out["u"], ref, rtol=1e-10, atol=1e-10)
+
+
+def test_rope_channel_alone_is_mqa_with_shared_rotated_key():
+    """W_UK = 0: the score is the RoPE channel only, one rotated key shared by all heads."""
+    rng = _rng(30)
+    H, nh, dh, dc, dr, L = 7, 3, 2, 5, 4, 6
+    w = _weights(rng, H, nh, dh, dc, dr)
+    w["w_uk"] = np.zeros_like(w["w_uk"])
+    h_ctx = rng.normal(size=(L, H)) * 3.0
+    rows = O.latent_rows(h_ctx, w["w_dkv"], w["w_kr"], np.arange(L), 10000.0)
+    out = O.mla_decode_step(h_ctx[-1], rows, w["w_q"], w["w_qr"], w["w_uk"], w["w_uv"], w["w_o"],
+                            L - 1, nh, dh, dc, dr, 10000.0)
+    tau = 1.0 / math.sqrt(dh + dr)
+    kr = [_complex_rope(w["w_kr"] @ h_ctx[j], j, 10000.0) for j in range(L)]
+    c = [w["w_dkv"] @ h_ctx[j] for j in range(L)]
+    o = []
+    for i in range(nh):
+        qr = _complex_rope(w["w_qr"][i * dr:(i + 1) * dr] @ h_ctx[-1], L - 1, 10000.0)
+        s = [tau * float(qr @ kr[j]) for j in range(L)]
+        e = [math.exp(x - max(s)) for x in s]
+        v = [w["w_uv"][i * dh:(i + 1) * dh] @ c[j] for j in range(L)]
+        o.append(sum(e[j] * v[j] for j in range(L)) / sum(e))
+    np.testing.assert_allclose(out["u"], w["w_o"] @ np.concatenate(o), rtol=1e-11, atol=1e-12)
+
+
+# ------------------------------------------------------------ associativity --
+@pytest.mark.parametrize("H,nh,dh,dc,dr,L", [(64, 4, 16, 32, 8, 64), (40, 3, 8, 24, 6, 19),
+                                            (96, 2, 32, 128, 16, 130)])
+def test_absorbed_equals_non_absorbed(H, nh, dh, dc, dr, L):
+    rng = _rng(40 + L)
+    w = _weights(rng, H, nh, dh, dc, dr)
+    h_ctx = rng.normal(size=(L, H))
+    rows = O.latent_rows(h_ctx, w["w_dkv"], w["w_kr"], np.arange(L), 10000.0)
+    args = (h_ctx[-1], rows, w["w_q"], w["w_qr"], w["w_uk"], w["w_uv"], w["w_o"], L - 1,
+            nh, dh, dc, dr, 10000.0)
+    a, b = O.mla_decode_step(*args), O.mla_decode_step_absorbed(*args)
+    np.testing.assert_allclose(b["u"], a["u"], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(b["lse"], a["lse"], rtol=1e-12, atol=1e-12)
+    # o_lat is the softmax-weighted latent; W_UV,i o_lat,i must be the per-head output
+    per_head = np.stack([w["w_uv"][i * dh:(i + 1) * dh] @ b["o_lat"][i] for i in range(nh)])
+    np.testing.assert_allclose(per_head, a["o"], rtol=1e-10, atol=1e-12)
+
+
+def test_absorb_q_brute_force():
+    rng = _rng(50)
+    H, nh, dh, dc, dr = 6, 2, 3, 4, 2
+    w = _weights(rng, H, nh, dh, dc, dr)
+    h = rng.normal(size=H)
+    q_lat, q_pe = O.absorb_q(h, w["w_q"], w["w_qr"], w["w_uk"], 9, nh, dh, dc, dr, 10000.0)
+    for i in range(nh):
+        qc = [sum(w["w_q"][i * dh + a, b] * h[b] for b in range(H)) for a in range(dh)]
+        for cc in range(dc):
+            ref = sum(w["w_uk"][i * dh + a, cc] * qc[a] for a in range(dh))
+            assert abs(q_lat[i, cc] - ref) < 1e-12
+        qr = [sum(w["w_qr"][i * dr + a, b] * h[b] for b in range(H)) for a in range(dr)]
+        np.testing.assert_allclose(q_pe[i], _complex_rope(qr, 9, 10000.0), atol=1e-12)
+
+
+def test_absorb_out_brute_force():
+    rng = _rng(51)
+    H, nh, dh, dc = 5, 3, 2, 4
+    w_uv = rng.normal(size=(nh * dh, dc))
+    w_o = rng.normal(size=(H, nh * dh))
+    o_lat = rng.normal(size=(nh, dc))
+    u = O.absorb_out(o_lat, w_uv, w_o, nh, dh, dc)
+    o = [sum(w_uv[i * dh + a, c] * o_lat[i, c] for c in range(dc)) for i in range(nh) for a in range(dh)]
+    ref = [sum(w_o[r, k] * o[k] for k in range(nh * dh)) for r in range(H)]
+    np.testing.assert_allclose(u, ref, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------ closed forms --
+def test_single_token_context():
+    """L = 1: the one weight is 1, o_lat = c_t, u = W_O blockdiag(W_UV) c_t."""
+    rng = _rng(60)
+    H, nh, dh, dc, dr = 12, 3, 4, 8, 4
+    w = _weights(rng, H, nh, dh, dc, dr)
+    h = rng.normal(size=(1, H))
+    rows = O.latent_rows(h, w["w_dkv"], w["w_kr"], [0], 10000.0)
+    out = O.mla_decode_step(h[0], rows, w["w_q"], w["w_qr"], w["w_uk"], w["w_uv"], w["w_o"], 0,
+                            nh, dh, dc, dr, 10000.0)
+    c = w["w_dkv"] @ h[0]
+    np.testing.assert_allclose(out["u"], w["w_o"] @ (w["w_uv"] @ c), rtol=1e-12, atol=1e-12)
+
+
+def test_zero_query_gives_uniform_average_and_identical_rows_give_the_row():
+    rng = _rng(61)
+    nh, dc, dr, L = 3, 8, 4, 9
+    rows = rng.normal(size=(L, dc + dr))
+    o, lse = O.attention_partials(np.zeros((nh, dc)), np.zeros((nh, dr)), rows, 1, dc, dr, 0.3, 4)
+    np.testing.assert_allclose(o[0], np.tile(rows[:, :dc].mean(0), (nh, 1)), rtol=1e-12)
+    np.testing.assert_allclose(lse[0], np.full(nh, math.log(L)), rtol=1e-12)
+    same = np.tile(rows[:1], (L, 1))
+    o, _ = O.attention_partials(rng.normal(size=(nh, dc)), rng.normal(size=(nh, dr)), same, 1,
+                                dc, dr, 0.3, 4)
+    np.testing.assert_allclose(o[0], np.tile(rows[0, :dc], (nh, 1)), rtol=1e-12)
+
+
+# ------------------------------------------------------------ split / merge --
+def test_split_bounds_partition():
+    for L in (1, 63, 64, 65, 4096, 4097, 131072, 777):
+        for S in (1, 2, 3, 8, 64):
+            b = O.split_bounds(L, S, 64)
+            assert len(b) == S and b[0][0] == 0 and b[-1][1] == L
+            for (a0, a1), (b0, _) in zip(b, b[1:]):
+                assert a1 == b0 and a0 <= a1
+            for a0, a1 in b:
+                assert a0 % 64 == 0 or a0 == L
+    assert O.split_bounds(131072, 64, 64)[1] == (2048, 4096)
+
+
+def test_split_merge_equals_whole_and_lse_is_logsumexp():
+    sp = pytest.importorskip("scipy.special")
+    rng = _rng(70)
+    nh, dc, dr, L, tau = 4, 16, 8, 300, 0.2
+    q_lat, q_pe = rng.normal(size=(nh, dc)) * 2, rng.normal(size=(nh, dr)) * 2
+    rows = rng.normal(size=(L, dc + dr))
+    scores = np.array([[tau * (q_lat[i] @ rows[j, :dc] + q_pe[i] @ rows[j, dc:]) for j in range(L)]
+                       for i in range(nh)])
+    ref_lse = sp.logsumexp(scores, axis=1)
+    p = sp.softmax(scores, axis=1)
+    ref_o = p @ rows[:, :dc]
+    for S in (1, 2, 5, 16):
+        o_s, l_s = O.attention_partials(q_lat, q_pe, rows, S, dc, dr, tau, 16)
+        o, lse = O.merge_lse(o_s, l_s)
+        np.testing.assert_allclose(o, ref_o, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(lse, ref_lse, rtol=1e-12)
+        if S == 16:
+            assert np.isneginf(l_s[-1]).all() and not o_s[-1].any()   # 300 rows fill 10 of 16 splits
+
+
+def test_merge_lse_brute_force():
+    rng = _rng(71)
+    o_s = rng.normal(size=(3, 2, 5))
+    l_s = np.array([[0.5, -np.inf], [2.0, 1.0], [-np.inf, 3.0]])
+    o, lse = O.merge_lse(o_s, l_s)
+    for i in range(2):
+        ws = [math.exp(l_s[s, i]) if np.isfinite(l_s[s, i]) else 0.0 for s in range(3)]
+        ref = sum(ws[s] * o_s[s, i] for s in range(3)) / sum(ws)
+        np.testing.assert_allclose(o[i], ref, rtol=1e-12)
+        assert abs(lse[i] - math.log(sum(ws))) < 1e-12

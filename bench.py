@@ -1,0 +1,183 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the MLA latent-KV library on one MI355X.
+
+One step = the five calls of one MLA decode layer on the full-shape workload
+(hidden 5120, n_h 128, d_h 128, d_c 512, d_R 64, bf16 cache and weights; 64
+sequences at context 4096, 4 KV splits): absorb_q -> append_latent ->
+decode_attention -> merge_lse -> absorb_out.  Inputs are seeded synthetic data
+resident in HBM before timing; two independent copies of weights and cache
+alternate between steps so no step re-reads the previous step's bytes from
+the 256 MB last-level cache.
+
+Prints one JSON line: decoded tokens/s (value), latent-cache GB/s, the HBM
+roofline of the attention kernel measured with HIP events on the launch
+stream, and the fp64 CPU oracle timed on a bounded sample on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="full", help="full | lite | long (one layer each)")
+    p.add_argument("--splits", type=int, default=0, help="KV splits (0 = workload default)")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="budget of the oracle timing on the host (0 disables it)")
+    p.add_argument("--attention-only", action="store_true",
+                   help="time only the attention call (for profiling)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run only a plain 1 GiB device copy (calibrates HBM byte counters)")
+    return p.parse_args()
+
+
+def cpu_baseline(w, seconds: float):
+    """fp64 oracle (non-absorbed definition) on whole sequences of the same
+    workload until `seconds` of host time are spent; tokens/s = sequences/s."""
+    import numpy as np
+
+    import oracle as O
+    from mla_latent_kv_dkv_amd import inputs as I
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = len(os.sched_getaffinity(0))
+    lens = I.seq_lengths(w)
+    bt, _ = I.page_table(w, lens)
+    wt = {n: I.to_f64(w, I.weight_values(w, n, 0)) for n in I.WEIGHT_NAMES}
+    done, spent, b = 0, 0.0, 0
+    while spent < seconds and b < w.batch:
+        L = int(lens[b])
+        rows = I.to_f64(w, I.pool_rows(w, bt, b, L))
+        h = I.to_f64(w, I.tensor_values(w, "h_dec", None, 1.0, 0, start=b * w.hidden,
+                                         count=w.hidden))
+        t = time.perf_counter()
+        rows[L - 1] = O.latent_rows(h[None], wt["w_dkv"], wt["w_kr"], [L - 1], w.rope_base)[0]
+        O.mla_decode_step(h, rows, wt["w_q"], wt["w_qr"], wt["w_uk"], wt["w_uv"], wt["w_o"],
+                          L - 1, w.n_heads, w.d_head, w.d_latent, w.d_rope, w.rope_base)
+        spent += time.perf_counter() - t
+        done += 1
+        b += 1
+    return {"value": done / spent, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {w.batch} sequences (context {int(lens[0])}), non-absorbed "
+                      f"fp64 definition, {spent:.1f} s of host time"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    if args.copy_calibration:
+        a = torch.ones(1 << 29, dtype=torch.int16, device="cuda")   # 1 GiB
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_launch": 2 * a.numel() * a.element_size(),
+                          "read_bytes": a.numel() * a.element_size(),
+                          "write_bytes": b.numel() * b.element_size()}), flush=True)
+        return
+
+    import mla_latent_kv_dkv_amd as M
+    from mla_latent_kv_dkv_amd import inputs as I
+    from mla_latent_kv_dkv_amd.harness import DeviceWorkload
+    M.load()
+    w = I.WORKLOADS[args.workload]
+    S = args.splits or w.num_splits
+    sets = [DeviceWorkload(w, layer=l, num_splits=S) for l in (0, 1)]
+    torch.cuda.synchronize()
+    lens = sets[0].lens
+    cache_bytes = int(lens.sum()) * w.row * w.elem_bytes
+    attn_flop = 2 * w.n_heads * int(lens.sum()) * (2 * w.d_latent + w.d_rope)
+    stream = torch.cuda.current_stream()
+
+    def one(i, ev=None):
+        dw = sets[i & 1]
+        if args.attention_only:
+            dw.attention()
+            return
+        dw.absorb_q()
+        dw.append()
+        if ev is not None:
+            ev[0].record(stream)
+        dw.attention()
+        if ev is not None:
+            ev[1].record(stream)
+        dw.merge()
+        dw.absorb_out()
+
+    for i in range(args.warmup):
+        one(i)
+    torch.cuda.synchronize()
+    # timed region 1: whole steps
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one(i)
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / args.steps
+    # timed region 2: the attention kernel alone, HIP events on its launch stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        if args.attention_only:
+            evs[i][0].record(stream)
+            one(i)
+            evs[i][1].record(stream)
+        else:
+            one(i, evs[i])
+    torch.cuda.synchronize()
+    attn_s = sum(a.elapsed_time(b) for a, b in evs) / args.steps / 1e3
+    assert M.mla_device_error() == 0
+
+    B = w.batch
+    achieved = cache_bytes / attn_s / 1e9
+    line = {
+        "metric": "MLA decode tokens/s + latent-cache GB/s (% roofline), n_h=128 d_c=512 1 GPU",
+        "value": B / step_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded, counter-based generator; random-init weights)",
+        "config": {"workload": f"{w.name}: one MLA decode layer, hidden {w.hidden}, n_h {w.n_heads}, "
+                               f"d_h {w.d_head}, d_c {w.d_latent}, d_R {w.d_rope}, batch {B}, "
+                               f"context {int(lens.max())}, {S} KV splits, 64-token pages",
+                   "batch": B, "context": int(lens.max()), "num_splits": S},
+        "latent_cache_GBps": achieved,
+        "attention_us": attn_s * 1e6,
+        "attention_mfma_tflops": attn_flop / attn_s / 1e12,
+        "attention_mfma_frac": attn_flop / attn_s / 1e12 / BF16_PEAK_TFLOPS,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "k_attn_mfma_h128 (mla_decode_attention)",
+                     "algorithmic_bytes_per_launch": cache_bytes},
+    }
+    if args.cpu_seconds > 0:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

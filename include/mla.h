@@ -1,0 +1,184 @@
+/*
+ * mla.h -- C ABI of the MLA latent-KV decode library (libmla.so, gfx950).
+ *
+ * One decode step of Multi-head Latent Attention: every token is cached only as
+ * a latent row [c^KV (d_c) | k^R (d_R)], and attention runs with W_UK folded
+ * into the query and W_UV folded into the output, so per-head keys and values
+ * are never formed.  Sources (web pages, by title and section):
+ *   [Report] "《DeepSeek-V2》深度解读报告": §2.2 low-rank joint KV compression
+ *     (c^KV = W_DKV h; k^C = W_UK c, v^C = W_UV c), §2.3 absorption
+ *     (W_UK into the query side, W_UV into W_O), §2.4 decoupled RoPE (per-head
+ *     q^R, one k^R shared by all heads, score = content score + RoPE score),
+ *     §3.1 data flow and cache accounting (d_c + d_R elements per token).
+ *   [Digest] "DeepSeek-V2论文解读 ... KV缓存压93.3%": §2.1 (only the latent is cached),
+ *     §3.1 (paged cache management).
+ *
+ * Conventions shared by every call
+ *   - All tensor pointers are DEVICE pointers, row-major, densely packed, owned
+ *     by the caller.  The library never allocates, frees or synchronises; work
+ *     is enqueued on the caller's stream and the call returns at once.
+ *   - Storage type is mla_dims.dtype (fp32 or bf16) for h, the weights and the
+ *     pool.  Activations handed from one call to the next (q_lat, q_pe,
+ *     o_part, lse_part, o_lat, lse) and the output u are always fp32, so that
+ *     no extra rounding enters between the calls.  Accumulation is fp32.
+ *   - Weights (head i owns rows i*d_h..(i+1)*d_h-1, or i*d_R.. for W_QR):
+ *       w_q  [n_h*d_h, H]   w_qr [n_h*d_R, H]   w_dkv [d_c, H]   w_kr [d_R, H]
+ *       w_uk [n_h*d_h, d_c] w_uv [n_h*d_h, d_c] w_o   [H, n_h*d_h]
+ *   - Paged latent pool: [num_pages, page_size, d_c + d_R]; logical position j
+ *     of sequence b lives in row block_table[b*max_pages + j/page_size] *
+ *     page_size + j%page_size.  block_table is int32 [batch, max_pages].
+ *   - RoPE: adjacent pairs (x[2k], x[2k+1]) are turned by pos*theta_k,
+ *     theta_k = rope_base^(-2k/d_R), angles evaluated in fp64.
+ *   - Softmax scale tau = softmax_scale if > 0, else 1/sqrt(d_h + d_R).
+ *   - Errors: every argument the host can see is checked before anything is
+ *     enqueued; a failing check returns a negative mla_status and enqueues
+ *     nothing.  Device-side values the host cannot see (block-table entries,
+ *     positions, sequence lengths) are range-checked inside the kernels: an
+ *     out-of-range entry is skipped (never dereferenced) and sets a sticky
+ *     device error word, read with mla_device_error().  No call aborts.
+ *   - Thread safety: calls keep no state between invocations (apart from the
+ *     sticky error word and the kernel-path switch below).
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = -1,        /* a required pointer is NULL */
+  MLA_ERR_SHAPE = -2,       /* a dimension or count is out of range */
+  MLA_ERR_UNSUPPORTED = -3, /* dtype / abi_version / page_size not supported */
+  MLA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than mla_workspace_bytes() */
+  MLA_ERR_HIP = -5          /* a kernel launch was rejected by the HIP runtime */
+} mla_status;
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
+
+/* Model dimensions; passed by host pointer to every call. */
+typedef struct {
+  int32_t abi_version;   /* must equal MLA_ABI_VERSION */
+  int32_t hidden;        /* H */
+  int32_t n_heads;       /* n_h */
+  int32_t d_head;        /* d_h */
+  int32_t d_latent;      /* d_c, even */
+  int32_t d_rope;        /* d_R, even */
+  int32_t page_size;     /* rows per pool page, a power of two in [1, 1024] */
+  int32_t dtype;         /* mla_dtype */
+  float rope_base;       /* > 0, e.g. 10000 */
+  float softmax_scale;   /* <= 0 selects 1/sqrt(d_h + d_R) */
+} mla_dims;
+
+/*
+ * Latent append ([Report] §2.2 down-projection, §2.4 shared RoPE key).
+ * For each row r < n_rows: c = W_DKV h[r], k^R = RoPE(W_KR h[r], row_pos[r]);
+ * the row [c | k^R] (rounded to dtype) is written to the pool at logical
+ * position row_pos[r] of sequence row_seq[r].  Also the cache-fill path.
+ *   h        [n_rows, H] dtype          row_seq, row_pos  [n_rows] int32
+ *   block_table [n_seqs, max_pages] int32, pool [num_pages, page_size, d_c+d_R]
+ * Rows whose (seq, pos) or table entry is out of range are not written and set
+ * the device error word.  Rows must target distinct slots (else the last
+ * writer is unspecified).  n_rows == 0 is a no-op.
+ */
+mla_status mla_append_latent(const mla_dims* dims, const void* h, const void* w_dkv,
+                             const void* w_kr, const int32_t* row_seq, const int32_t* row_pos,
+                             int32_t n_rows, const int32_t* block_table, int32_t n_seqs,
+                             int32_t max_pages, void* pool, int64_t num_pages,
+                             hipStream_t stream);
+
+/*
+ * Absorbed query ([Report] §2.3: q.(W_UK c) regrouped as (W_UK^T q).c; §3.1:
+ * per-head RoPE query from h).  For each sequence b with decode position pos[b]:
+ *   q^C_i = W_Q,i h_b,  q_lat[b,i,:] = W_UK,i^T q^C_i           (d_c)
+ *   q_pe[b,i,:] = RoPE(W_QR,i h_b, pos[b])                        (d_R)
+ *   h [batch, H] dtype; pos [batch] int32; q_lat [batch, n_h, d_c] fp32;
+ *   q_pe [batch, n_h, d_R] fp32.
+ * Workspace: at least mla_workspace_bytes(dims, batch) bytes of device memory,
+ * used for q^C; its contents are scratch for the duration of the call.
+ */
+mla_status mla_absorb_q(const mla_dims* dims, const void* h, const void* w_q, const void* w_qr,
+                        const void* w_uk, const int32_t* pos, int32_t batch, float* q_lat,
+                        float* q_pe, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Split-KV latent attention ([Report] §2.3, §2.4: every head scores the same
+ * cached latent rows, s_ij = tau (q_lat,i . c_j + q_pe,i . k^R_j)).  Sequence b has
+ * seq_lens[b] = L tokens (positions 0..L-1, the decode token included).  With
+ * S = num_splits, chunk = page_size * ceil(ceil(L/S)/page_size); split s covers
+ * positions [s*chunk, min(L, (s+1)*chunk)).  For every (b, s, head i):
+ *   lse_part[b,s,i]   = log sum_{j in split} exp(s_ij)         (-inf if empty)
+ *   o_part[b,s,i,:]   = sum_j exp(s_ij - lse_part) c_j          (0 if empty)
+ *   q_lat [batch, n_h, d_c], q_pe [batch, n_h, d_R] fp32 (the MFMA path rounds
+ *   them to bf16 once per work unit); pool dtype;
+ *   seq_lens [batch] int32 in [0, max_pages*page_size];
+ *   o_part [batch, S, n_h, d_c] fp32; lse_part [batch, S, n_h] fp32.
+ * num_splits in [1, 4096].
+ */
+mla_status mla_decode_attention(const mla_dims* dims, const float* q_lat, const float* q_pe,
+                                const void* pool, int64_t num_pages, const int32_t* block_table,
+                                int32_t max_pages, const int32_t* seq_lens, int32_t batch,
+                                int32_t num_splits, float* o_part, float* lse_part,
+                                hipStream_t stream);
+
+/*
+ * Log-sum-exp merge of split partials: per (b, i), m = max_s lse_s,
+ * w_s = exp(lse_s - m), o_lat = sum_s w_s o_s / sum_s w_s, lse = m + log sum_s w_s.
+ * Splits with lse = -inf weigh 0; a row whose every split is empty gives
+ * o_lat = 0 and lse = -inf.
+ *   o_part [batch, S, n_h, d_c] fp32, lse_part [batch, S, n_h] fp32,
+ *   o_lat [batch, n_h, d_c] fp32, lse [batch, n_h] fp32 (may be NULL).
+ */
+mla_status mla_merge_lse(const mla_dims* dims, const float* o_part, const float* lse_part,
+                         int32_t batch, int32_t num_splits, float* o_lat, float* lse,
+                         hipStream_t stream);
+
+/*
+ * Absorbed output ([Report] §2.3: W_UV folded into the output projection):
+ *   o_i = W_UV,i o_lat[b,i,:] (d_h),  u[b,:] = W_O [o_1; ...; o_n_h]   (H)
+ *   o_lat [batch, n_h, d_c] fp32; u [batch, H] fp32.
+ * Workspace: at least mla_workspace_bytes(dims, batch) bytes, used for o.
+ */
+mla_status mla_absorb_out(const mla_dims* dims, const float* o_lat, const void* w_uv,
+                          const void* w_o, int32_t batch, float* u, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes needed by mla_absorb_q / mla_absorb_out for `batch` sequences
+ * (0 if dims are invalid). */
+size_t mla_workspace_bytes(const mla_dims* dims, int32_t batch);
+
+/* Static text for a status code. */
+const char* mla_status_string(int32_t status);
+
+/* Returns MLA_ABI_VERSION of the loaded library. */
+int32_t mla_abi_version(void);
+
+/*
+ * Sticky device error word: bit 0 = a block-table entry outside [0, num_pages),
+ * bit 1 = a position / length beyond max_pages*page_size or negative, bit 2 = a
+ * sequence index outside [0, n_seqs).  Synchronises `stream`, copies the word
+ * to *out and, if clear != 0, resets it.  Returns MLA_ERR_HIP on a runtime error.
+ */
+mla_status mla_device_error(int32_t* out, int32_t clear, hipStream_t stream);
+
+/*
+ * Kernel selection for the whole process: 0 = automatic (the MFMA kernels where
+ * the shape allows, else the plain vector kernels), 1 = plain vector kernels
+ * only.  Both compute the same quantities; the switch exists so both can be
+ * checked.  Returns the previous value.
+ */
+int32_t mla_set_kernel_path(int32_t path);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

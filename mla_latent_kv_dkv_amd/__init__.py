@@ -1,6 +1,213 @@
 """MLA latent-KV decode for MI355X (gfx950): Python binding over libmla.so.
 
-The compute lives in hand-written HIP kernels behind a C ABI; this package only
-marshals arguments.  The native library is loaded on first use and its absence
-is an error (there is no CPU fallback).
+The compute lives in hand-written HIP kernels behind the C ABI declared in
+``include/mla.h``; the functions here only marshal torch tensors (device
+memory) and the current HIP stream into that ABI.  The native library is
+loaded on first use; if it is missing the call raises -- there is no CPU
+fallback.  Build it with ``python -m mla_latent_kv_dkv_amd.build``.
 """
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla.so")
+
+MLA_ABI_VERSION = 1
+MLA_F32, MLA_BF16 = 0, 1
+
+__all__ = ["MlaDims", "MlaError", "make_dims", "load", "mla_append_latent", "mla_absorb_q",
+           "mla_decode_attention", "mla_merge_lse", "mla_absorb_out", "mla_workspace_bytes",
+           "mla_device_error", "mla_set_kernel_path", "mla_status_string", "LIB_PATH"]
+
+
+class MlaDims(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("n_heads", ctypes.c_int32), ("d_head", ctypes.c_int32),
+                ("d_latent", ctypes.c_int32), ("d_rope", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("rope_base", ctypes.c_float), ("softmax_scale", ctypes.c_float)]
+
+
+class MlaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} returned {status}: {mla_status_string(status)}")
+        self.status = status
+
+
+def make_dims(hidden, n_heads, d_head, d_latent, d_rope, dtype="bf16", page_size=64,
+              rope_base=10000.0, softmax_scale=0.0) -> MlaDims:
+    return MlaDims(MLA_ABI_VERSION, hidden, n_heads, d_head, d_latent, d_rope, page_size,
+                   MLA_BF16 if dtype in ("bf16", MLA_BF16) else MLA_F32, rope_base, softmax_scale)
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I32, _I64, _SZ = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_DIMS = ctypes.POINTER(MlaDims)
+
+_SIGS = {
+    "mla_append_latent": [_DIMS, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _P, _I64, _P],
+    "mla_absorb_q": [_DIMS, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P],
+    "mla_decode_attention": [_DIMS, _P, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _P, _P, _P],
+    "mla_merge_lse": [_DIMS, _P, _P, _I32, _I32, _P, _P, _P],
+    "mla_absorb_out": [_DIMS, _P, _P, _P, _I32, _P, _P, _SZ, _P],
+    "mla_workspace_bytes": [_DIMS, _I32],
+    "mla_status_string": [_I32],
+    "mla_abi_version": [],
+    "mla_device_error": [ctypes.POINTER(_I32), _I32, _P],
+    "mla_set_kernel_path": [_I32],
+}
+_RES = {"mla_workspace_bytes": _SZ, "mla_status_string": ctypes.c_char_p}
+
+
+def load(path: str = LIB_PATH):
+    """Load libmla.so (once) and declare its signatures; raises if it is absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run `python -m mla_latent_kv_dkv_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, args in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = _RES.get(name, _I32)
+        if lib.mla_abi_version() != MLA_ABI_VERSION:
+            raise RuntimeError("libmla.so ABI version mismatch")
+        _lib = lib
+    return _lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("tensors passed to libmla must be contiguous device tensors")
+    return _P(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return _P(s.cuda_stream)
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise MlaError(fn, status)
+
+
+def _elem(dims: MlaDims):
+    import torch
+    return torch.bfloat16 if dims.dtype == MLA_BF16 else torch.float32
+
+
+def _expect(t, shape, dtype, what):
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{what}: expected {tuple(shape)} {dtype}, got {tuple(t.shape)} {t.dtype}")
+
+
+def mla_status_string(status: int) -> str:
+    return load().mla_status_string(status).decode()
+
+
+def mla_workspace_bytes(dims: MlaDims, batch: int) -> int:
+    return int(load().mla_workspace_bytes(ctypes.byref(dims), batch))
+
+
+def mla_set_kernel_path(path: int) -> int:
+    return int(load().mla_set_kernel_path(path))
+
+
+def mla_device_error(clear: bool = True, stream=None) -> int:
+    out = _I32(0)
+    _check("mla_device_error", load().mla_device_error(ctypes.byref(out), int(clear), _stream(stream)))
+    return out.value
+
+
+def mla_append_latent(dims, h, w_dkv, w_kr, row_seq, row_pos, block_table, pool, stream=None):
+    """Write [W_DKV h | RoPE(W_KR h, pos)] of each row of ``h`` into the paged pool."""
+    import torch
+    n, row = h.shape[0], dims.d_latent + dims.d_rope
+    _expect(h, (n, dims.hidden), _elem(dims), "h")
+    _expect(w_dkv, (dims.d_latent, dims.hidden), _elem(dims), "w_dkv")
+    _expect(w_kr, (dims.d_rope, dims.hidden), _elem(dims), "w_kr")
+    _expect(row_seq, (n,), torch.int32, "row_seq")
+    _expect(row_pos, (n,), torch.int32, "row_pos")
+    _expect(pool, (pool.shape[0], dims.page_size, row), _elem(dims), "pool")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2:
+        raise ValueError("block_table must be int32 [n_seqs, max_pages]")
+    _check("mla_append_latent", load().mla_append_latent(
+        ctypes.byref(dims), _ptr(h), _ptr(w_dkv), _ptr(w_kr), _ptr(row_seq), _ptr(row_pos), n,
+        _ptr(block_table), block_table.shape[0], block_table.shape[1], _ptr(pool), pool.shape[0],
+        _stream(stream)))
+
+
+def mla_absorb_q(dims, h, w_q, w_qr, w_uk, pos, q_lat, q_pe, workspace, stream=None):
+    """q_lat = W_UK,i^T W_Q,i h and q_pe = RoPE(W_QR,i h, pos) for every head."""
+    import torch
+    B, nh = h.shape[0], dims.n_heads
+    e = _elem(dims)
+    _expect(h, (B, dims.hidden), e, "h")
+    _expect(w_q, (nh * dims.d_head, dims.hidden), e, "w_q")
+    _expect(w_qr, (nh * dims.d_rope, dims.hidden), e, "w_qr")
+    _expect(w_uk, (nh * dims.d_head, dims.d_latent), e, "w_uk")
+    _expect(pos, (B,), torch.int32, "pos")
+    _expect(q_lat, (B, nh, dims.d_latent), torch.float32, "q_lat")
+    _expect(q_pe, (B, nh, dims.d_rope), torch.float32, "q_pe")
+    _check("mla_absorb_q", load().mla_absorb_q(
+        ctypes.byref(dims), _ptr(h), _ptr(w_q), _ptr(w_qr), _ptr(w_uk), _ptr(pos), B, _ptr(q_lat),
+        _ptr(q_pe), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def mla_decode_attention(dims, q_lat, q_pe, pool, block_table, seq_lens, o_part, lse_part,
+                         stream=None):
+    """Split-KV latent attention; the split count is o_part.shape[1]."""
+    import torch
+    B, S = o_part.shape[0], o_part.shape[1]
+    nh, e = dims.n_heads, _elem(dims)
+    _expect(q_lat, (B, nh, dims.d_latent), torch.float32, "q_lat")
+    _expect(q_pe, (B, nh, dims.d_rope), torch.float32, "q_pe")
+    _expect(pool, (pool.shape[0], dims.page_size, dims.d_latent + dims.d_rope), e, "pool")
+    _expect(seq_lens, (B,), torch.int32, "seq_lens")
+    _expect(o_part, (B, S, nh, dims.d_latent), torch.float32, "o_part")
+    _expect(lse_part, (B, S, nh), torch.float32, "lse_part")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] < B:
+        raise ValueError("block_table must be int32 [>= batch, max_pages]")
+    _check("mla_decode_attention", load().mla_decode_attention(
+        ctypes.byref(dims), _ptr(q_lat), _ptr(q_pe), _ptr(pool), pool.shape[0], _ptr(block_table),
+        block_table.shape[1], _ptr(seq_lens), B, S, _ptr(o_part), _ptr(lse_part), _stream(stream)))
+
+
+def mla_merge_lse(dims, o_part, lse_part, o_lat, lse=None, stream=None):
+    """Log-sum-exp merge of the split partials into o_lat (and lse if given)."""
+    import torch
+    B, S = o_part.shape[0], o_part.shape[1]
+    nh = dims.n_heads
+    _expect(o_part, (B, S, nh, dims.d_latent), torch.float32, "o_part")
+    _expect(lse_part, (B, S, nh), torch.float32, "lse_part")
+    _expect(o_lat, (B, nh, dims.d_latent), torch.float32, "o_lat")
+    if lse is not None:
+        _expect(lse, (B, nh), torch.float32, "lse")
+    _check("mla_merge_lse", load().mla_merge_lse(
+        ctypes.byref(dims), _ptr(o_part), _ptr(lse_part), B, S, _ptr(o_lat), _ptr(lse),
+        _stream(stream)))
+
+
+def mla_absorb_out(dims, o_lat, w_uv, w_o, u, workspace, stream=None):
+    """u = W_O [W_UV,i o_lat,i]_i."""
+    import torch
+    B, nh, e = o_lat.shape[0], dims.n_heads, _elem(dims)
+    _expect(o_lat, (B, nh, dims.d_latent), torch.float32, "o_lat")
+    _expect(w_uv, (nh * dims.d_head, dims.d_latent), e, "w_uv")
+    _expect(w_o, (dims.hidden, nh * dims.d_head), e, "w_o")
+    _expect(u, (B, dims.hidden), torch.float32, "u")
+    _check("mla_absorb_out", load().mla_absorb_out(
+        ctypes.byref(dims), _ptr(o_lat), _ptr(w_uv), _ptr(w_o), B, _ptr(u), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def default_scale(dims: MlaDims) -> float:
+    return dims.softmax_scale if dims.softmax_scale > 0 else 1.0 / math.sqrt(dims.d_head + dims.d_rope)

@@ -1,0 +1,66 @@
+// Device-side helpers shared by the MLA kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef uint16_t bf16_t;
+
+// Sticky device error bits (mirrors mla_device_error in include/mla.h).
+enum : int { ERR_PAGE = 1, ERR_POS = 2, ERR_SEQ = 4 };
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest, ties to even (inputs are finite).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float ld(const float* p) { return *p; }
+__device__ __forceinline__ float ld(const bf16_t* p) { return bf16_to_f32(*p); }
+__device__ __forceinline__ void st(float* p, float v) { *p = v; }
+__device__ __forceinline__ void st(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+
+__device__ __forceinline__ void set_err(int* err, int bits) {
+  if (err) atomicOr(err, bits);
+}
+
+// cos/sin of pos * rope_base^(-2k/d_rope), evaluated in fp64 and rounded to fp32.
+__device__ __forceinline__ void rope_cs(int pos, int k, int d_rope, double log_base, float* c,
+                                        float* s) {
+  const double theta = exp(-2.0 * static_cast<double>(k) / static_cast<double>(d_rope) * log_base);
+  double sd, cd;
+  sincos(static_cast<double>(pos) * theta, &sd, &cd);
+  *c = static_cast<float>(cd);
+  *s = static_cast<float>(sd);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Split s of a length-L sequence under S splits: page-aligned equal chunks.
+__device__ __forceinline__ void split_range(int L, int S, int s, int page, int* t0, int* t1) {
+  const int per = (L + S - 1) / S;
+  const int chunk = ((per + page - 1) / page) * page;
+  const long a = static_cast<long>(s) * chunk;
+  *t0 = static_cast<int>(a < L ? a : L);
+  const long b = a + chunk;
+  *t1 = static_cast<int>(b < L ? b : L);
+}
+
+}  // namespace mla

@@ -1,0 +1,262 @@
+// Plain vector-ALU kernels for every MLA step, any shape, fp32 or bf16 storage.
+//
+// They are the shape-general path (the 64-wide fp32 workload runs here) and a
+// second implementation the MFMA kernels are checked against.  fp32
+// accumulation throughout.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace mla {
+
+// ----------------------------------------------------------------- GEMM --
+// Y[m, n] = sum_k X(m, k) W(n, k); tile 32 (m) x 64 (n) x 32 (k); each thread
+// owns 2 rows x 4 adjacent columns, so RoPE pairs (even, odd) stay in-thread.
+constexpr int GT_M = 32, GT_N = 64, GT_K = 32;
+
+// Element i of an activation that is fp32 or the storage type T.
+template <typename T>
+__device__ __forceinline__ float ld_act(const void* p, int64_t i, int f32) {
+  return f32 ? static_cast<const float*>(p)[i] : ld(static_cast<const T*>(p) + i);
+}
+template <typename T>
+__device__ __forceinline__ void st_act(void* p, int64_t i, float v, int f32) {
+  if (f32) static_cast<float*>(p)[i] = v; else st(static_cast<T*>(p) + i, v);
+}
+
+template <typename T>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, int z, int m, int n, float v0,
+                                              float v1) {
+  // columns n, n+1 (n even): a pair that never straddles n_split (n_split is even)
+  if (a.epi == EPI_STORE) {
+    const int64_t base = z * a.y_bs + static_cast<int64_t>(m) * a.ldy;
+    if (n < a.N) st_act<T>(a.y, base + n, v0, a.y_f32);
+    if (n + 1 < a.N) st_act<T>(a.y, base + n + 1, v1, a.y_f32);
+    return;
+  }
+  if (a.epi == EPI_QPROJ) {
+    if (n < a.n_split) {
+      T* y = static_cast<T*>(a.y) + static_cast<int64_t>(m) * a.ldy;
+      st(y + n, v0);
+      st(y + n + 1, v1);
+    } else {
+      const int r = n - a.n_split;              // column within q_pe row
+      const int k = (r % a.d_rope) >> 1;       // pair index within the head
+      float c, s;
+      rope_cs(a.pos[m], k, a.d_rope, a.log_base, &c, &s);
+      float* y2 = static_cast<float*>(a.y2) + static_cast<int64_t>(m) * (a.N - a.n_split);
+      y2[r] = v0 * c - v1 * s;
+      y2[r + 1] = v0 * s + v1 * c;
+    }
+    return;
+  }
+  // EPI_APPEND: destination slot of row m
+  const int seq = a.row_seq[m];
+  const int pos = a.pos[m];
+  if (seq < 0 || seq >= a.n_seqs) { if (n == 0) set_err(a.err, ERR_SEQ); return; }
+  if (pos < 0 || pos >= a.max_pages * a.page_size) { if (n == 0) set_err(a.err, ERR_POS); return; }
+  const int page = a.block_table[static_cast<int64_t>(seq) * a.max_pages + pos / a.page_size];
+  if (page < 0 || page >= a.num_pages) { if (n == 0) set_err(a.err, ERR_PAGE); return; }
+  T* row = static_cast<T*>(a.y) +
+           (static_cast<int64_t>(page) * a.page_size + pos % a.page_size) * a.row_width;
+  if (n < a.n_split) {
+    st(row + n, v0);
+    st(row + n + 1, v1);
+  } else {
+    const int k = (n - a.n_split) >> 1;
+    float c, s;
+    rope_cs(pos, k, a.d_rope, a.log_base, &c, &s);
+    st(row + n, v0 * c - v1 * s);
+    st(row + n + 1, v0 * s + v1 * c);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_gemm_generic(GemmArgs a) {
+  __shared__ float xs[GT_M][GT_K + 1];
+  __shared__ float ws[GT_N][GT_K + 1];
+  const int z = blockIdx.z;
+  const int m0 = blockIdx.y * GT_M, n0 = blockIdx.x * GT_N;
+  const int tid = threadIdx.x;
+  const int tx = tid & 15, ty = tid >> 4;
+  const int64_t xb = z * a.x_bs;
+  float acc[2][4] = {};
+  for (int k0 = 0; k0 < a.K; k0 += GT_K) {
+    for (int e = tid; e < GT_M * GT_K; e += 256) {
+      const int r = e / GT_K, kk = e % GT_K;
+      const int m = m0 + r, k = k0 + kk;
+      xs[r][kk] = (m < a.M && k < a.K) ? ld_act<T>(a.x, xb + m * a.ldx_m + k * a.ldx_k, a.x_f32)
+                                       : 0.f;
+    }
+    for (int e = tid; e < GT_N * GT_K; e += 256) {
+      const int r = e / GT_K, kk = e % GT_K;
+      const int n = n0 + r, k = k0 + kk;
+      float v = 0.f;
+      if (n < a.N && k < a.K) {
+        const T* w = n < a.n_split ? static_cast<const T*>(a.w1) + z * a.w_bs + n * a.ldw_n
+                                   : static_cast<const T*>(a.w2) + z * a.w_bs +
+                                         (n - a.n_split) * a.ldw_n;
+        v = ld(w + k * a.ldw_k);
+      }
+      ws[r][kk] = v;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int kk = 0; kk < GT_K; ++kk) {
+      const float x0 = xs[ty * 2][kk], x1 = xs[ty * 2 + 1][kk];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float w = ws[tx * 4 + j][kk];
+        acc[0][j] += x0 * w;
+        acc[1][j] += x1 * w;
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int m = m0 + ty * 2 + i;
+    if (m >= a.M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; j += 2) {
+      const int n = n0 + tx * 4 + j;
+      if (n < a.N) gemm_epilogue<T>(a, z, m, n, acc[i][j], acc[i][j + 1]);
+    }
+  }
+}
+
+hipError_t launch_gemm_generic(const GemmArgs& a, bool bf16, hipStream_t stream) {
+  if (a.M == 0 || a.N == 0 || a.batch == 0) return hipSuccess;
+  dim3 grid((a.N + GT_N - 1) / GT_N, (a.M + GT_M - 1) / GT_M, a.batch);
+  if (bf16)
+    hipLaunchKernelGGL(k_gemm_generic<bf16_t>, grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(k_gemm_generic<float>, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ attention --
+// One workgroup per (head, split, sequence).  Tokens are taken 256 at a time:
+// thread t scores token t (full d_c + d_R dot product), the chunk's weights
+// go through an online softmax, then each thread accumulates latent columns.
+template <typename T>
+__global__ __launch_bounds__(256) void k_attention_generic(AttnArgs a) {
+  extern __shared__ float smem[];
+  const int row_w = a.d_latent + a.d_rope;
+  float* qs = smem;                         // [row_w]
+  float* acc = qs + row_w;                  // [d_latent]
+  float* ps = acc + a.d_latent;             // [256]
+  float* red = ps + 256;                    // [8]
+  int64_t* rowoff = reinterpret_cast<int64_t*>(red + 8);  // [256]
+
+  const int i = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nh = a.n_heads;
+  int L = a.seq_lens[b];
+  if (L < 0 || L > a.max_pages * a.page_size) {
+    if (tid == 0) set_err(a.err, ERR_POS);
+    L = 0;
+  }
+  int t0, t1;
+  split_range(L, a.num_splits, s, a.page_size, &t0, &t1);
+
+  const float* ql = a.q_lat + (static_cast<int64_t>(b) * nh + i) * a.d_latent;
+  const float* qp = a.q_pe + (static_cast<int64_t>(b) * nh + i) * a.d_rope;
+  for (int e = tid; e < a.d_latent; e += 256) { qs[e] = ql[e]; acc[e] = 0.f; }
+  for (int e = tid; e < a.d_rope; e += 256) qs[a.d_latent + e] = qp[e];
+  __syncthreads();
+
+  const T* pool = static_cast<const T*>(a.pool);
+  float m_run = -INFINITY, l_run = 0.f;
+  for (int c0 = t0; c0 < t1; c0 += 256) {
+    const int j = c0 + tid;
+    float sc = -INFINITY;
+    int64_t off = -1;
+    if (j < t1) {
+      const int page = a.block_table[static_cast<int64_t>(b) * a.max_pages + j / a.page_size];
+      if (page < 0 || page >= a.num_pages) {
+        set_err(a.err, ERR_PAGE);
+      } else {
+        off = (static_cast<int64_t>(page) * a.page_size + j % a.page_size) * row_w;
+        const T* r = pool + off;
+        float d = 0.f;
+        for (int e = 0; e < row_w; ++e) d += qs[e] * ld(r + e);
+        sc = d * a.scale;
+      }
+    }
+    rowoff[tid] = off;
+    float cmax = wave_max(sc);
+    if (lane == 0) red[wv] = cmax;
+    __syncthreads();
+    cmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float m_new = fmaxf(m_run, cmax);
+    const float alpha = (m_new == -INFINITY) ? 1.f : __expf(m_run - m_new);
+    const float p = (off < 0 || m_new == -INFINITY) ? 0.f : __expf(sc - m_new);
+    ps[tid] = p;
+    float psum = wave_sum(p);
+    __syncthreads();
+    if (lane == 0) red[4 + wv] = psum;
+    __syncthreads();
+    psum = red[4] + red[5] + red[6] + red[7];
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    const int cnt = min(256, t1 - c0);
+    for (int d = tid; d < a.d_latent; d += 256) {
+      float v = acc[d] * alpha;
+      for (int jj = 0; jj < cnt; ++jj) {
+        const int64_t o = rowoff[jj];
+        if (o >= 0) v += ps[jj] * ld(pool + o + d);
+      }
+      acc[d] = v;
+    }
+    __syncthreads();
+  }
+  const int64_t ob = (static_cast<int64_t>(b) * a.num_splits + s) * nh + i;
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  for (int d = tid; d < a.d_latent; d += 256) a.o_part[ob * a.d_latent + d] = acc[d] * inv;
+  if (tid == 0) a.lse_part[ob] = l_run > 0.f ? m_run + __logf(l_run) : -INFINITY;
+}
+
+hipError_t launch_attention_generic(const AttnArgs& a, bool bf16, hipStream_t stream) {
+  if (a.batch == 0) return hipSuccess;
+  const size_t shm = (a.d_latent + a.d_rope + a.d_latent + 256 + 8) * sizeof(float) +
+                     256 * sizeof(int64_t) + 16;
+  dim3 grid(a.n_heads, a.num_splits, a.batch);
+  if (bf16)
+    hipLaunchKernelGGL(k_attention_generic<bf16_t>, grid, dim3(256), shm, stream, a);
+  else
+    hipLaunchKernelGGL(k_attention_generic<float>, grid, dim3(256), shm, stream, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- merge --
+__global__ __launch_bounds__(256) void k_merge_generic(MergeArgs a) {
+  const int d = blockIdx.x * 256 + threadIdx.x;
+  const int i = blockIdx.y, b = blockIdx.z;
+  const int S = a.num_splits, nh = a.n_heads;
+  const float* lse = a.lse_part + static_cast<int64_t>(b) * S * nh + i;
+  float m = -INFINITY;
+  for (int s = 0; s < S; ++s) m = fmaxf(m, lse[static_cast<int64_t>(s) * nh]);
+  float z = 0.f, o = 0.f;
+  if (m != -INFINITY) {
+    for (int s = 0; s < S; ++s) {
+      const float l = lse[static_cast<int64_t>(s) * nh];
+      if (l == -INFINITY) continue;
+      const float w = __expf(l - m);
+      z += w;
+      if (d < a.d_latent)
+        o += w * a.o_part[((static_cast<int64_t>(b) * S + s) * nh + i) * a.d_latent + d];
+    }
+  }
+  if (d < a.d_latent)
+    a.o_lat[(static_cast<int64_t>(b) * nh + i) * a.d_latent + d] = z > 0.f ? o / z : 0.f;
+  if (a.lse && d == 0) a.lse[static_cast<int64_t>(b) * nh + i] = z > 0.f ? m + __logf(z) : -INFINITY;
+}
+
+hipError_t launch_merge_generic(const MergeArgs& a, bool, hipStream_t stream) {
+  if (a.batch == 0) return hipSuccess;
+  dim3 grid((a.d_latent + 255) / 256, a.n_heads, a.batch);
+  hipLaunchKernelGGL(k_merge_generic, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,22 @@
+// Host-side launchers of the MFMA (gfx950 matrix core) kernels and the shape
+// predicates that decide when they apply.  Shapes they do not cover go to the
+// plain vector kernels in kernels_generic.hip.
+#pragma once
+
+#include "launch.hpp"
+
+namespace mla {
+
+// Address of the sticky device error word on the current device (nullptr on failure).
+int* error_word_address();
+
+bool fast_gemm_ok(const GemmArgs& a);
+hipError_t launch_gemm_fast(const GemmArgs& a, hipStream_t stream);
+
+bool fast_attention_ok(const AttnArgs& a);
+hipError_t launch_attention_fast(const AttnArgs& a, hipStream_t stream);
+
+bool fast_merge_ok(const MergeArgs& a);
+hipError_t launch_merge_fast(const MergeArgs& a, hipStream_t stream);
+
+}  // namespace mla

@@ -1,0 +1,251 @@
+// C ABI of libmla.so: argument checks, workspace layout and kernel selection.
+// The operations themselves are described in include/mla.h.
+#include "../../include/mla.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "launch.hpp"
+#include "launch_fast.hpp"
+
+namespace {
+
+std::atomic<int32_t> g_path{0};
+
+// Per-device address of the sticky error word (defined in errword.hip).
+constexpr int kMaxDevices = 64;
+int* g_err_ptr[kMaxDevices] = {};
+std::atomic<int> g_err_ready[kMaxDevices] = {};
+
+int* err_word() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  if (!g_err_ready[dev].load(std::memory_order_acquire)) {
+    int* p = mla::error_word_address();
+    if (!p) return nullptr;
+    g_err_ptr[dev] = p;
+    g_err_ready[dev].store(1, std::memory_order_release);
+  }
+  return g_err_ptr[dev];
+}
+
+bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+mla_status check_dims(const mla_dims* d) {
+  if (!d) return MLA_ERR_NULL;
+  if (d->abi_version != MLA_ABI_VERSION) return MLA_ERR_UNSUPPORTED;
+  if (d->dtype != MLA_F32 && d->dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+  if (!is_pow2(d->page_size) || d->page_size > 1024) return MLA_ERR_UNSUPPORTED;
+  if (d->hidden < 1 || d->n_heads < 1 || d->d_head < 2 || d->d_latent < 2 || d->d_rope < 2)
+    return MLA_ERR_SHAPE;
+  if ((d->d_head | d->d_latent | d->d_rope) & 1) return MLA_ERR_SHAPE;
+  if (d->hidden > (1 << 20) || d->n_heads > 4096 || d->d_head > 4096 || d->d_latent > 4096 ||
+      d->d_rope > 1024)
+    return MLA_ERR_SHAPE;
+  if (!(d->rope_base > 0.f) || !std::isfinite(d->rope_base)) return MLA_ERR_SHAPE;
+  if (!std::isfinite(d->softmax_scale)) return MLA_ERR_SHAPE;
+  return MLA_OK;
+}
+
+size_t elem_bytes(const mla_dims* d) { return d->dtype == MLA_BF16 ? 2 : 4; }
+
+float softmax_scale(const mla_dims* d) {
+  return d->softmax_scale > 0.f ? d->softmax_scale
+                                : 1.0f / std::sqrt(static_cast<float>(d->d_head + d->d_rope));
+}
+
+bool use_fast() { return g_path.load(std::memory_order_relaxed) == 0; }
+
+mla_status hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+int32_t mla_set_kernel_path(int32_t path) { return g_path.exchange(path == 1 ? 1 : 0); }
+
+const char* mla_status_string(int32_t s) {
+  switch (s) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_NULL: return "null pointer argument";
+    case MLA_ERR_SHAPE: return "dimension or count out of range";
+    case MLA_ERR_UNSUPPORTED: return "unsupported dtype, abi version or page size";
+    case MLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MLA_ERR_HIP: return "HIP runtime rejected a launch";
+    default: return "unknown status";
+  }
+}
+
+size_t mla_workspace_bytes(const mla_dims* d, int32_t batch) {
+  if (check_dims(d) != MLA_OK || batch < 0) return 0;
+  // q^C (absorb_q) or the per-head outputs o (absorb_out): [batch, n_h*d_h] in dtype
+  const size_t n = static_cast<size_t>(batch) * d->n_heads * d->d_head;
+  return ((n * elem_bytes(d) + 255) / 256) * 256 + 256;
+}
+
+mla_status mla_device_error(int32_t* out, int32_t clear, hipStream_t stream) {
+  if (!out) return MLA_ERR_NULL;
+  int* p = err_word();
+  if (!p) return MLA_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return MLA_ERR_HIP;
+  int v = 0;
+  if (hipMemcpy(&v, p, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return MLA_ERR_HIP;
+  *out = v;
+  if (clear) {
+    if (hipMemsetAsync(p, 0, sizeof(int), stream) != hipSuccess) return MLA_ERR_HIP;
+    if (hipStreamSynchronize(stream) != hipSuccess) return MLA_ERR_HIP;
+  }
+  return MLA_OK;
+}
+
+mla_status mla_append_latent(const mla_dims* d, const void* h, const void* w_dkv, const void* w_kr,
+                             const int32_t* row_seq, const int32_t* row_pos, int32_t n_rows,
+                             const int32_t* block_table, int32_t n_seqs, int32_t max_pages,
+                             void* pool, int64_t num_pages, hipStream_t stream) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (n_rows < 0 || n_seqs < 0 || max_pages < 0 || num_pages < 0) return MLA_ERR_SHAPE;
+  if (n_rows == 0) return MLA_OK;
+  if (n_seqs < 1 || max_pages < 1 || num_pages < 1) return MLA_ERR_SHAPE;
+  if (static_cast<int64_t>(max_pages) * d->page_size > (int64_t{1} << 30)) return MLA_ERR_SHAPE;
+  if (!h || !w_dkv || !w_kr || !row_seq || !row_pos || !block_table || !pool) return MLA_ERR_NULL;
+  int* err = err_word();
+  if (!err) return MLA_ERR_HIP;
+  const bool bf16 = d->dtype == MLA_BF16;
+  mla::GemmArgs a{};
+  a.x = h; a.ldx_m = d->hidden; a.ldx_k = 1; a.x_bs = 0;
+  a.w1 = w_dkv; a.w2 = w_kr; a.n_split = d->d_latent;
+  a.ldw_n = d->hidden; a.ldw_k = 1; a.w_bs = 0;
+  a.M = n_rows; a.N = d->d_latent + d->d_rope; a.K = d->hidden; a.batch = 1;
+  a.epi = mla::EPI_APPEND; a.x_f32 = !bf16;
+  a.y = pool; a.d_rope = d->d_rope; a.log_base = std::log(static_cast<double>(d->rope_base));
+  a.pos = row_pos; a.row_seq = row_seq; a.block_table = block_table;
+  a.n_seqs = n_seqs; a.max_pages = max_pages; a.page_size = d->page_size;
+  a.row_width = d->d_latent + d->d_rope; a.num_pages = num_pages; a.err = err;
+  if (use_fast() && bf16 && mla::fast_gemm_ok(a)) return hip_status(mla::launch_gemm_fast(a, stream));
+  return hip_status(mla::launch_gemm_generic(a, bf16, stream));
+}
+
+mla_status mla_absorb_q(const mla_dims* d, const void* h, const void* w_q, const void* w_qr,
+                        const void* w_uk, const int32_t* pos, int32_t batch, float* q_lat,
+                        float* q_pe, void* ws, size_t ws_bytes, hipStream_t stream) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || batch > (1 << 20)) return MLA_ERR_SHAPE;
+  if (batch == 0) return MLA_OK;
+  if (!h || !w_q || !w_qr || !w_uk || !pos || !q_lat || !q_pe) return MLA_ERR_NULL;
+  if (!ws || ws_bytes < mla_workspace_bytes(d, batch)) return MLA_ERR_WORKSPACE;
+  const bool bf16 = d->dtype == MLA_BF16;
+  const int64_t nhdh = static_cast<int64_t>(d->n_heads) * d->d_head;
+  // 1) [q^C | q^R] = h [W_Q; W_QR]^T, RoPE on the q^R columns
+  mla::GemmArgs a{};
+  a.x = h; a.ldx_m = d->hidden; a.ldx_k = 1;
+  a.w1 = w_q; a.w2 = w_qr; a.n_split = static_cast<int>(nhdh);
+  a.ldw_n = d->hidden; a.ldw_k = 1;
+  a.M = batch; a.N = static_cast<int>(nhdh + static_cast<int64_t>(d->n_heads) * d->d_rope);
+  a.K = d->hidden; a.batch = 1;
+  a.epi = mla::EPI_QPROJ; a.x_f32 = !bf16; a.y_f32 = !bf16;
+  a.y = ws; a.ldy = nhdh; a.y2 = q_pe; a.d_rope = d->d_rope;
+  a.log_base = std::log(static_cast<double>(d->rope_base)); a.pos = pos;
+  hipError_t e = (use_fast() && bf16 && mla::fast_gemm_ok(a)) ? mla::launch_gemm_fast(a, stream)
+                                                              : mla::launch_gemm_generic(a, bf16, stream);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  // 2) q_lat[b, i, :] = W_UK,i^T q^C[b, i, :] : per head i, X = q^C_i [B, d_h], W(n=c, k=dh)
+  mla::GemmArgs g{};
+  g.x = ws; g.ldx_m = nhdh; g.ldx_k = 1; g.x_bs = d->d_head;
+  g.w1 = w_uk; g.w2 = w_uk; g.n_split = d->d_latent;
+  g.ldw_n = 1; g.ldw_k = d->d_latent; g.w_bs = static_cast<int64_t>(d->d_head) * d->d_latent;
+  g.M = batch; g.N = d->d_latent; g.K = d->d_head; g.batch = d->n_heads;
+  g.epi = mla::EPI_STORE; g.x_f32 = !bf16; g.y_f32 = 1;
+  g.y = q_lat; g.ldy = static_cast<int64_t>(d->n_heads) * d->d_latent;
+  g.y_bs = d->d_latent;
+  e = (use_fast() && bf16 && mla::fast_gemm_ok(g)) ? mla::launch_gemm_fast(g, stream)
+                                                    : mla::launch_gemm_generic(g, bf16, stream);
+  return hip_status(e);
+}
+
+mla_status mla_decode_attention(const mla_dims* d, const float* q_lat, const float* q_pe,
+                                const void* pool, int64_t num_pages, const int32_t* block_table,
+                                int32_t max_pages, const int32_t* seq_lens, int32_t batch,
+                                int32_t num_splits, float* o_part, float* lse_part,
+                                hipStream_t stream) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || batch > 65535 || num_splits < 1 || num_splits > 4096 || max_pages < 1 ||
+      num_pages < 1)
+    return MLA_ERR_SHAPE;
+  if (static_cast<int64_t>(max_pages) * d->page_size > (int64_t{1} << 30)) return MLA_ERR_SHAPE;
+  if (batch == 0) return MLA_OK;
+  if (!q_lat || !q_pe || !pool || !block_table || !seq_lens || !o_part || !lse_part)
+    return MLA_ERR_NULL;
+  int* err = err_word();
+  if (!err) return MLA_ERR_HIP;
+  mla::AttnArgs a{};
+  a.q_lat = q_lat; a.q_pe = q_pe; a.pool = pool; a.num_pages = num_pages;
+  a.block_table = block_table; a.max_pages = max_pages; a.seq_lens = seq_lens;
+  a.batch = batch; a.num_splits = num_splits; a.n_heads = d->n_heads;
+  a.d_latent = d->d_latent; a.d_rope = d->d_rope; a.page_size = d->page_size;
+  a.scale = softmax_scale(d); a.o_part = o_part; a.lse_part = lse_part; a.err = err;
+  const bool bf16 = d->dtype == MLA_BF16;
+  if (use_fast() && bf16 && mla::fast_attention_ok(a))
+    return hip_status(mla::launch_attention_fast(a, stream));
+  return hip_status(mla::launch_attention_generic(a, bf16, stream));
+}
+
+mla_status mla_merge_lse(const mla_dims* d, const float* o_part, const float* lse_part,
+                         int32_t batch, int32_t num_splits, float* o_lat, float* lse,
+                         hipStream_t stream) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || batch > 65535 || num_splits < 1 || num_splits > 4096) return MLA_ERR_SHAPE;
+  if (batch == 0) return MLA_OK;
+  if (!o_part || !lse_part || !o_lat) return MLA_ERR_NULL;
+  mla::MergeArgs a{};
+  a.o_part = o_part; a.lse_part = lse_part; a.batch = batch; a.num_splits = num_splits;
+  a.n_heads = d->n_heads; a.d_latent = d->d_latent; a.o_lat = o_lat; a.lse = lse;
+  const bool bf16 = d->dtype == MLA_BF16;
+  if (use_fast() && bf16 && mla::fast_merge_ok(a)) return hip_status(mla::launch_merge_fast(a, stream));
+  return hip_status(mla::launch_merge_generic(a, bf16, stream));
+}
+
+mla_status mla_absorb_out(const mla_dims* d, const float* o_lat, const void* w_uv, const void* w_o,
+                          int32_t batch, float* u, void* ws, size_t ws_bytes, hipStream_t stream) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || batch > (1 << 20)) return MLA_ERR_SHAPE;
+  if (batch == 0) return MLA_OK;
+  if (!o_lat || !w_uv || !w_o || !u) return MLA_ERR_NULL;
+  if (!ws || ws_bytes < mla_workspace_bytes(d, batch)) return MLA_ERR_WORKSPACE;
+  const bool bf16 = d->dtype == MLA_BF16;
+  const int64_t nhdh = static_cast<int64_t>(d->n_heads) * d->d_head;
+  // 1) o[b, i*d_h + e] = sum_c W_UV[i*d_h + e, c] o_lat[b, i, c]   (per head i)
+  mla::GemmArgs g{};
+  g.x = o_lat; g.ldx_m = static_cast<int64_t>(d->n_heads) * d->d_latent; g.ldx_k = 1;
+  g.x_bs = d->d_latent;
+  g.w1 = w_uv; g.w2 = w_uv; g.n_split = d->d_head;
+  g.ldw_n = d->d_latent; g.ldw_k = 1; g.w_bs = static_cast<int64_t>(d->d_head) * d->d_latent;
+  g.M = batch; g.N = d->d_head; g.K = d->d_latent; g.batch = d->n_heads;
+  g.epi = mla::EPI_STORE; g.x_f32 = 1; g.y_f32 = !bf16;
+  g.y = ws; g.ldy = nhdh; g.y_bs = d->d_head;
+  hipError_t e = (use_fast() && bf16 && mla::fast_gemm_ok(g)) ? mla::launch_gemm_fast(g, stream)
+                                                              : mla::launch_gemm_generic(g, bf16, stream);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  // 2) u = o W_O^T
+  mla::GemmArgs a{};
+  a.x = ws; a.ldx_m = nhdh; a.ldx_k = 1;
+  a.w1 = w_o; a.w2 = w_o; a.n_split = d->hidden;
+  a.ldw_n = nhdh; a.ldw_k = 1;
+  a.M = batch; a.N = d->hidden; a.K = static_cast<int>(nhdh); a.batch = 1;
+  a.epi = mla::EPI_STORE; a.x_f32 = !bf16; a.y_f32 = 1;
+  a.y = u; a.ldy = d->hidden;
+  e = (use_fast() && bf16 && mla::fast_gemm_ok(a)) ? mla::launch_gemm_fast(a, stream)
+                                                    : mla::launch_gemm_generic(a, bf16, stream);
+  return hip_status(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,144 @@
+"""Device set-up of the synthetic decode workloads and the five-call decode step.
+
+Used by the GPU tests, ``bench.py`` and ``__graft_entry__.smoke()``.  All
+numbers come from the seeded generator in ``inputs.py`` (filled on the device
+by its twin kernel); all compute goes through the C ABI in ``__init__.py``.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import (make_dims, mla_absorb_out, mla_absorb_q, mla_append_latent, mla_decode_attention,
+               mla_merge_lse, mla_workspace_bytes)
+from . import inputs as I
+
+
+class DeviceWorkload:
+    """Weights, paged pool, page table, lengths and output buffers of one layer of
+    a :class:`inputs.Workload`, resident in device memory."""
+
+    def __init__(self, w: I.Workload, layer: int = 0, num_splits: int | None = None,
+                 device: str = "cuda", build_cache: bool = True, outputs_from=None):
+        import torch
+        self.torch = torch
+        self.w, self.layer = w, layer
+        self.dev = torch.device(device)
+        self.dims = make_dims(w.hidden, w.n_heads, w.d_head, w.d_latent, w.d_rope, w.dtype,
+                              w.page_size, w.rope_base)
+        self.dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+        self.S = num_splits or w.num_splits
+        self.lens = I.seq_lengths(w)
+        self.bt_host, self.num_pages = I.page_table(w, self.lens)
+        B = w.batch
+        self.seq_lens = torch.tensor(self.lens, dtype=torch.int32, device=self.dev)
+        self.pos = (self.seq_lens - 1).contiguous()
+        self.block_table = torch.tensor(self.bt_host, dtype=torch.int32, device=self.dev)
+        self.weights = {}
+        for name in I.WEIGHT_NAMES:
+            t = torch.empty(w.weight_shape(name), dtype=self.dt, device=self.dev)
+            I.fill_device(t, I.stream_key(w.seed, name, layer), 1.0 / np.sqrt(w.fan_in(name)))
+            self.weights[name] = t
+        self.pool = torch.empty((self.num_pages, w.page_size, w.row), dtype=self.dt, device=self.dev)
+        if w.cache_from_h:
+            L = int(self.lens.max())
+            self.h_ctx = torch.empty((B, L, w.hidden), dtype=self.dt, device=self.dev)
+            I.fill_device(self.h_ctx, I.stream_key(w.seed, "h_ctx", layer))
+            self.h = self.h_ctx[torch.arange(B, device=self.dev), self.pos.long()].contiguous()
+            self.pool.zero_()
+            if build_cache:
+                self.build_cache_from_h()
+        else:
+            self.h_ctx = None
+            self.h = torch.empty((B, w.hidden), dtype=self.dt, device=self.dev)
+            I.fill_device(self.h, I.stream_key(w.seed, "h_dec", layer))
+            I.fill_device(self.pool, I.stream_key(w.seed, "pool", layer))
+        nh = w.n_heads
+        if outputs_from is not None:     # share scratch/output buffers with another layer
+            for k in ("q_lat", "q_pe", "o_part", "lse_part", "o_lat", "lse", "u", "ws"):
+                setattr(self, k, getattr(outputs_from, k))
+            return
+        f32 = torch.float32
+        self.q_lat = torch.empty((B, nh, w.d_latent), dtype=f32, device=self.dev)
+        self.q_pe = torch.empty((B, nh, w.d_rope), dtype=f32, device=self.dev)
+        self.o_part = torch.empty((B, self.S, nh, w.d_latent), dtype=torch.float32, device=self.dev)
+        self.lse_part = torch.empty((B, self.S, nh), dtype=torch.float32, device=self.dev)
+        self.o_lat = torch.empty((B, nh, w.d_latent), dtype=f32, device=self.dev)
+        self.lse = torch.empty((B, nh), dtype=torch.float32, device=self.dev)
+        self.u = torch.empty((B, w.hidden), dtype=f32, device=self.dev)
+        self.ws = torch.empty(mla_workspace_bytes(self.dims, B), dtype=torch.uint8, device=self.dev)
+
+    def build_cache_from_h(self):
+        """Append rows 0..L_b-2 of every sequence from h_ctx (the context before
+        the decode token) through mla_append_latent."""
+        torch = self.torch
+        B, L = self.h_ctx.shape[0], self.h_ctx.shape[1]
+        seqs, poss = [], []
+        for b in range(B):
+            n = int(self.lens[b]) - 1
+            seqs.append(np.full(n, b, dtype=np.int32))
+            poss.append(np.arange(n, dtype=np.int32))
+        seq = torch.tensor(np.concatenate(seqs), device=self.dev)
+        pos = torch.tensor(np.concatenate(poss), device=self.dev)
+        rows = self.h_ctx.reshape(B * L, -1)[(seq.long() * L + pos.long())].contiguous()
+        mla_append_latent(self.dims, rows, self.weights["w_dkv"], self.weights["w_kr"], seq, pos,
+                          self.block_table, self.pool)
+
+    # ---- the five calls of one decode step ------------------------------
+    def absorb_q(self):
+        W = self.weights
+        mla_absorb_q(self.dims, self.h, W["w_q"], W["w_qr"], W["w_uk"], self.pos, self.q_lat,
+                     self.q_pe, self.ws)
+
+    def append(self):
+        B = self.w.batch
+        seq = self.torch.arange(B, dtype=self.torch.int32, device=self.dev)
+        mla_append_latent(self.dims, self.h, self.weights["w_dkv"], self.weights["w_kr"], seq,
+                          self.pos, self.block_table, self.pool)
+
+    def attention(self):
+        mla_decode_attention(self.dims, self.q_lat, self.q_pe, self.pool, self.block_table,
+                             self.seq_lens, self.o_part, self.lse_part)
+
+    def merge(self):
+        mla_merge_lse(self.dims, self.o_part, self.lse_part, self.o_lat, self.lse)
+
+    def absorb_out(self):
+        mla_absorb_out(self.dims, self.o_lat, self.weights["w_uv"], self.weights["w_o"], self.u,
+                       self.ws)
+
+    def step(self):
+        """absorb_q -> append (decode token at L-1) -> attention -> merge -> absorb_out."""
+        self.absorb_q()
+        self.append()
+        self.attention()
+        self.merge()
+        self.absorb_out()
+        return self.u
+
+    # ---- host copies of the same inputs, for the oracle ------------------
+    def host_weights(self):
+        """fp64 host copies of the weights, regenerated from the seed."""
+        return {n: I.to_f64(self.w, I.weight_values(self.w, n, self.layer)) for n in I.WEIGHT_NAMES}
+
+    def host_h(self, b: int) -> np.ndarray:
+        """fp64 hidden state of the decode token of sequence b."""
+        w, L = self.w, int(self.lens[b])
+        if w.cache_from_h:
+            Lmax = int(self.lens.max())
+            v = I.tensor_values(w, "h_ctx", None, 1.0, self.layer,
+                                start=(b * Lmax + L - 1) * w.hidden, count=w.hidden)
+        else:
+            v = I.tensor_values(w, "h_dec", None, 1.0, self.layer, start=b * w.hidden,
+                                count=w.hidden)
+        return I.to_f64(w, v)
+
+    def host_h_ctx(self, b: int) -> np.ndarray:
+        """fp64 hidden states of positions 0..L_b-1 of sequence b (cache-from-h workloads)."""
+        w, L, Lmax = self.w, int(self.lens[b]), int(self.lens.max())
+        v = I.tensor_values(w, "h_ctx", None, 1.0, self.layer, start=b * Lmax * w.hidden,
+                            count=L * w.hidden)
+        return I.to_f64(w, v).reshape(L, w.hidden)
+
+    def host_pool_rows(self, b: int, length: int) -> np.ndarray:
+        """fp64 generator-filled pool rows of logical positions 0..length-1 of b."""
+        return I.to_f64(self.w, I.pool_rows(self.w, self.bt_host, b, length, self.layer))

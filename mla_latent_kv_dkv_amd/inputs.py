@@ -22,6 +22,7 @@ twin (in ``csrc/fill_inputs.hip``).
 from __future__ import annotations
 
 import math
+import os
 import zlib
 from dataclasses import dataclass, field
 
@@ -31,7 +32,7 @@ GAMMA = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
 _IH_STD = math.sqrt(4.0 * (65536.0 ** 2 - 1.0) / 12.0)   # std of the 4-field sum
-_CHUNK = 1 << 22
+_CHUNK = 1 << 20
 
 
 def mix64(z):
@@ -64,25 +65,75 @@ def normal_scale(std: float) -> np.float32:
     return np.float32(std / _IH_STD)
 
 
-def normal_f32(key: int, start: int, n: int, std: float = 1.0) -> np.ndarray:
-    """fp32 values ``start .. start+n-1`` of stream ``key`` (approximately N(0, std^2))."""
-    out = np.empty(n, dtype=np.float32)
-    sc = normal_scale(std)
+def _normal_chunk(key: int, start: int, n: int, sc: np.float32, out: np.ndarray,
+                  bf16: bool = False) -> None:
+    z = np.arange(start + 1, start + n + 1, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        z *= GAMMA
+        z += np.uint64(key)
+        t = z >> np.uint64(30)
+        z ^= t
+        z *= _M1
+        np.right_shift(z, np.uint64(27), out=t)
+        z ^= t
+        z *= _M2
+        np.right_shift(z, np.uint64(31), out=t)
+        z ^= t
     m16 = np.uint64(0xFFFF)
-    for a in range(0, n, _CHUNK):
-        b = min(n, a + _CHUNK)
-        w = words(key, start + a, b - a)
-        s = ((w & m16) + ((w >> np.uint64(16)) & m16) + ((w >> np.uint64(32)) & m16)
-             + (w >> np.uint64(48))).astype(np.int64) - 131070
-        out[a:b] = s.astype(np.float32) * sc
+    np.bitwise_and(z, m16, out=t)
+    s = t.copy()
+    for sh in (16, 32):
+        np.right_shift(z, np.uint64(sh), out=t)
+        t &= m16
+        s += t
+    np.right_shift(z, np.uint64(48), out=t)
+    s += t
+    v = s.view(np.int64)
+    v -= 131070
+    f = v.astype(np.float32)
+    f *= sc
+    if bf16:
+        out[...] = f32_to_bf16_bits(f)
+    else:
+        out[...] = f
+
+
+def _normal(key: int, start: int, n: int, std: float, bf16: bool) -> np.ndarray:
+    out = np.empty(n, dtype=np.uint16 if bf16 else np.float32)
+    sc = normal_scale(std)
+    chunks = [(a, min(n, a + _CHUNK)) for a in range(0, n, _CHUNK)]
+    if len(chunks) <= 1:
+        for a, b in chunks:
+            _normal_chunk(key, start + a, b - a, sc, out[a:b], bf16)
+        return out
+    from concurrent.futures import ThreadPoolExecutor
+    workers = min(16, len(os.sched_getaffinity(0)), len(chunks))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(lambda ab: _normal_chunk(key, start + ab[0], ab[1] - ab[0], sc,
+                                              out[ab[0]:ab[1]], bf16), chunks))
     return out
 
 
+def normal_f32(key: int, start: int, n: int, std: float = 1.0) -> np.ndarray:
+    """fp32 values ``start .. start+n-1`` of stream ``key`` (approximately N(0, std^2))."""
+    return _normal(key, start, n, std, False)
+
+
+def normal_bf16_bits(key: int, start: int, n: int, std: float = 1.0) -> np.ndarray:
+    """The same values rounded to bf16 (nearest even), as uint16 bit patterns."""
+    return _normal(key, start, n, std, True)
+
+
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round-to-nearest-even fp32 -> bf16, returned as uint16 bit patterns."""
-    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    b = b + np.uint64(0x7FFF) + ((b >> np.uint64(16)) & np.uint64(1))
-    return (b >> np.uint64(16)).astype(np.uint16)
+    """Round-to-nearest-even fp32 -> bf16, returned as uint16 bit patterns
+    (finite inputs; the rounding increment cannot overflow for them)."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = b >> np.uint32(16)
+    r &= np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += b
+    r >>= np.uint32(16)
+    return r.astype(np.uint16)
 
 
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
@@ -186,10 +237,9 @@ def tensor_values(w: Workload, name: str, shape, std: float = 1.0, layer: int = 
     bit patterns (uint16) for bf16 workloads.  ``start``/``count`` select a flat
     sub-range (the same elements the device fill writes there)."""
     n = int(np.prod(shape)) if count is None else count
-    v = normal_f32(stream_key(w.seed, name, layer), start, n, std)
-    if count is None:
-        v = v.reshape(shape)
-    return v if w.dtype == "f32" else f32_to_bf16_bits(v)
+    gen = normal_f32 if w.dtype == "f32" else normal_bf16_bits
+    v = gen(stream_key(w.seed, name, layer), start, n, std)
+    return v.reshape(shape) if count is None else v
 
 
 def weight_values(w: Workload, name: str, layer: int = 0) -> np.ndarray:
@@ -215,8 +265,46 @@ def pool_rows(w: Workload, block_table: np.ndarray, seq: int, length: int, layer
         k = j
         while k + 1 < length and phys[k + 1] == phys[k] + 1:
             k += 1
-        v = normal_f32(key, int(phys[j]) * w.row, (k - j + 1) * w.row, 1.0)
-        v = v if w.dtype == "f32" else f32_to_bf16_bits(v)
+        gen = normal_f32 if w.dtype == "f32" else normal_bf16_bits
+        v = gen(key, int(phys[j]) * w.row, (k - j + 1) * w.row, 1.0)
         out[j:k + 1] = v.reshape(k - j + 1, w.row)
         j = k + 1
     return out
+
+
+# ------------------------------------------------------- device twin (GPU) --
+_inputs_lib = None
+
+
+def _device_lib():
+    global _inputs_lib
+    if _inputs_lib is None:
+        import ctypes
+        import os
+        path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_inputs.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run `python -m mla_latent_kv_dkv_amd.build`")
+        lib = ctypes.CDLL(path)
+        lib.mla_fill_normal.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                        ctypes.c_uint64, ctypes.c_uint64, ctypes.c_float,
+                                        ctypes.c_void_p]
+        lib.mla_fill_normal.restype = ctypes.c_int32
+        _inputs_lib = lib
+    return _inputs_lib
+
+
+def fill_device(t, key: int, std: float = 1.0, start: int = 0, stream=None):
+    """Fill contiguous device tensor ``t`` (fp32 or bf16) with elements
+    start .. start+numel-1 of stream ``key`` -- the same bits ``normal_f32`` /
+    ``tensor_values`` give on the host."""
+    import ctypes
+    import torch
+    if not t.is_cuda or not t.is_contiguous() or t.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("fill_device needs a contiguous fp32/bf16 device tensor")
+    s = torch.cuda.current_stream() if stream is None else stream
+    rc = _device_lib().mla_fill_normal(ctypes.c_void_p(t.data_ptr()), t.numel(),
+                                       0 if t.dtype == torch.float32 else 1, key, start,
+                                       float(normal_scale(std)), ctypes.c_void_p(s.cuda_stream))
+    if rc != 0:
+        raise RuntimeError(f"mla_fill_normal returned {rc}")
+    return t

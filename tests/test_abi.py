@@ -1,0 +1,114 @@
+"""Host-only checks of the C ABI: the libraries load, export every declared
+symbol, and reject bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mla_latent_kv_dkv_amd as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = {"mla.h": "libmla.so", "mla_inputs.h": "libmla_inputs.so"}
+
+
+def _declared(header):
+    text = open(os.path.join(ROOT, "include", header)).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text)))
+
+
+def _lib(name):
+    path = os.path.join(ROOT, "mla_latent_kv_dkv_amd", name)
+    if not os.path.exists(path):
+        pytest.fail(f"{name} not built (run python -m mla_latent_kv_dkv_amd.build)")
+    return ctypes.CDLL(path)
+
+
+@pytest.mark.parametrize("header", sorted(HEADERS))
+def test_every_declared_symbol_is_exported(header):
+    lib = _lib(HEADERS[header])
+    names = _declared(header)
+    assert names, header
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_the_five_decode_calls_are_declared():
+    assert {"mla_append_latent", "mla_absorb_q", "mla_decode_attention", "mla_merge_lse",
+            "mla_absorb_out"} <= set(_declared("mla.h"))
+
+
+def _dims(**kw):
+    base = dict(hidden=64, n_heads=4, d_head=16, d_latent=32, d_rope=8, dtype="f32")
+    base.update(kw)
+    return M.make_dims(**base)
+
+
+def test_status_strings_and_version():
+    lib = M.load()
+    assert lib.mla_abi_version() == M.MLA_ABI_VERSION
+    for s in (0, -1, -2, -3, -4, -5):
+        assert M.mla_status_string(s) != "unknown status"
+
+
+def test_workspace_bytes():
+    d = _dims()
+    assert M.mla_workspace_bytes(d, 8) >= 8 * 4 * 16 * 4
+    assert M.mla_workspace_bytes(_dims(dtype="bf16"), 8) >= 8 * 4 * 16 * 2
+    assert M.mla_workspace_bytes(_dims(d_rope=7), 8) == 0
+    assert M.mla_workspace_bytes(d, -1) == 0
+
+
+P = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+
+
+def test_invalid_dims_are_rejected_without_launch():
+    lib = M.load()
+    cases = [(_dims(d_rope=7), -2), (_dims(page_size=48), -3), (_dims(hidden=0), -2),
+             (_dims(rope_base=0.0), -2)]
+    bad_abi = _dims()
+    bad_abi.abi_version = 99
+    cases.append((bad_abi, -3))
+    bad_dtype = _dims()
+    bad_dtype.dtype = 7
+    cases.append((bad_dtype, -3))
+    for d, want in cases:
+        got = lib.mla_decode_attention(ctypes.byref(d), P, P, P, 1, P, 1, P, 1, 1, P, P, None)
+        assert got == want, (d.d_rope, d.page_size, got)
+        assert lib.mla_merge_lse(ctypes.byref(d), P, P, 1, 1, P, None, None) == want
+    assert lib.mla_decode_attention(None, P, P, P, 1, P, 1, P, 1, 1, P, P, None) == -1
+
+
+def test_argument_checks():
+    lib = M.load()
+    d = _dims()
+    # null pointers
+    assert lib.mla_decode_attention(ctypes.byref(d), None, P, P, 1, P, 1, P, 1, 1, P, P, None) == -1
+    assert lib.mla_merge_lse(ctypes.byref(d), P, None, 1, 1, P, None, None) == -1
+    assert lib.mla_absorb_out(ctypes.byref(d), P, P, None, 1, P, P, 1 << 20, None) == -1
+    assert lib.mla_append_latent(ctypes.byref(d), P, P, None, P, P, 1, P, 1, 1, P, 1, None) == -1
+    # counts
+    assert lib.mla_decode_attention(ctypes.byref(d), P, P, P, 1, P, 1, P, 1, 0, P, P, None) == -2
+    assert lib.mla_decode_attention(ctypes.byref(d), P, P, P, 1, P, 1, P, 1, 5000, P, P, None) == -2
+    assert lib.mla_decode_attention(ctypes.byref(d), P, P, P, 1, P, 1, P, -1, 1, P, P, None) == -2
+    assert lib.mla_merge_lse(ctypes.byref(d), P, P, 1, 0, P, None, None) == -2
+    assert lib.mla_append_latent(ctypes.byref(d), P, P, P, P, P, -3, P, 1, 1, P, 1, None) == -2
+    # workspace
+    assert lib.mla_absorb_q(ctypes.byref(d), P, P, P, P, P, 4, P, P, None, 1 << 20, None) == -4
+    assert lib.mla_absorb_q(ctypes.byref(d), P, P, P, P, P, 4, P, P, P, 16, None) == -4
+    assert lib.mla_absorb_out(ctypes.byref(d), P, P, P, 4, P, P, 16, None) == -4
+    # empty batches are no-ops that never touch the pointers
+    assert lib.mla_absorb_q(ctypes.byref(d), None, None, None, None, None, 0, None, None, None, 0,
+                            None) == 0
+    assert lib.mla_append_latent(ctypes.byref(d), None, None, None, None, None, 0, None, 0, 0, None,
+                                 0, None) == 0
+
+
+def test_device_fill_argument_checks():
+    lib = _lib("libmla_inputs.so")
+    lib.mla_fill_normal.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint64,
+                                    ctypes.c_uint64, ctypes.c_float, ctypes.c_void_p]
+    assert lib.mla_fill_normal(None, 0, 0, 1, 0, 1.0, None) == 0
+    assert lib.mla_fill_normal(None, 5, 0, 1, 0, 1.0, None) == -1
+    assert lib.mla_fill_normal(P, 5, 9, 1, 0, 1.0, None) == -3

@@ -1,0 +1,301 @@
+"""Per-call parity of the five C-ABI entry points against the fp64 oracle.
+
+Inputs of every call come from the seeded generator (never from another GPU
+call); both kernel paths (automatic = MFMA where the shape allows, and the
+plain vector kernels) are checked.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import mla_latent_kv_dkv_amd as M
+import oracle as O
+from mla_latent_kv_dkv_amd import inputs as I
+from tests.gpu_util import assert_parity, device_tensor, host_tensor, note, to_np
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+DIMS = {
+    "tiny": I.WORKLOADS["tiny"],
+    "lite": I.WORKLOADS["lite"],
+    "full": I.WORKLOADS["full"],
+}
+PATHS = [0, 1]
+
+
+@pytest.fixture(autouse=True)
+def _path_reset():
+    M.load()
+    yield
+    M.mla_set_kernel_path(0)
+
+
+def _wl(name, **kw):
+    w = DIMS[name]
+    fields = dict(w.__dict__)
+    fields.update(kw)
+    return I.Workload(**fields)
+
+
+def _dims(w):
+    return M.make_dims(w.hidden, w.n_heads, w.d_head, w.d_latent, w.d_rope, w.dtype, w.page_size,
+                       w.rope_base)
+
+
+# ------------------------------------------------------------ generator --
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_device_fill_is_bit_identical_to_host(dtype):
+    w = _wl("tiny", dtype=dtype)
+    note(f"fill {dtype}")
+    t = device_tensor(torch, w, "probe", (3, 1000), std=0.7)
+    torch.cuda.synchronize()
+    host = I.tensor_values(w, "probe", (3, 1000), 0.7)
+    if dtype == "f32":
+        np.testing.assert_array_equal(t.cpu().numpy().view(np.uint32), host.view(np.uint32))
+    else:
+        np.testing.assert_array_equal(t.view(torch.int16).cpu().numpy().view(np.uint16), host)
+    # sub-range start offset
+    u = torch.empty(500, dtype=t.dtype, device="cuda")
+    I.fill_device(u, I.stream_key(w.seed, "probe"), 0.7, start=1234)
+    np.testing.assert_array_equal(to_np(u), to_np(t).reshape(-1)[1234:1734])
+
+
+# --------------------------------------------------------------- append --
+def _sentinel_pool(w, pages):
+    pool = torch.full((pages, w.page_size, w.row), -3.5,
+                      dtype=torch.float32 if w.dtype == "f32" else torch.bfloat16, device="cuda")
+    return pool
+
+
+@pytest.mark.parametrize("name", ["tiny", "full"])
+@pytest.mark.parametrize("path", PATHS)
+def test_append_latent_placement_and_values(name, path):
+    w = _wl(name, batch=3)
+    M.mla_set_kernel_path(path)
+    lens = np.array([5, 130, 64], dtype=np.int32) if name == "tiny" else np.array([70, 200, 64],
+                                                                                    dtype=np.int32)
+    bt, total = I.page_table(w, lens)
+    rng = np.random.default_rng(5)
+    seqs = np.concatenate([np.full(l, b) for b, l in enumerate(lens)]).astype(np.int32)
+    poss = np.concatenate([np.arange(l) for l in lens]).astype(np.int32)
+    sel = rng.permutation(len(seqs))[:97]                  # 97 rows in scrambled order
+    seqs, poss = seqs[sel], poss[sel]
+    n = len(sel)
+    note(f"append {name} path={path} rows={n}")
+    h = device_tensor(torch, w, "h_rows", (n, w.hidden))
+    wd = device_tensor(torch, w, "w_dkv", (w.d_latent, w.hidden), 1 / math.sqrt(w.hidden))
+    wk = device_tensor(torch, w, "w_kr", (w.d_rope, w.hidden), 1 / math.sqrt(w.hidden))
+    pool = _sentinel_pool(w, total)
+    d = _dims(w)
+    M.mla_append_latent(d, h, wd, wk, torch.tensor(seqs, device="cuda"),
+                        torch.tensor(poss, device="cuda"),
+                        torch.tensor(bt, device="cuda"), pool)
+    got = to_np(pool).reshape(-1, w.row)
+    ref_rows = O.latent_rows(host_tensor(w, "h_rows", (n, w.hidden)),
+                             host_tensor(w, "w_dkv", (w.d_latent, w.hidden), 1 / math.sqrt(w.hidden)),
+                             host_tensor(w, "w_kr", (w.d_rope, w.hidden), 1 / math.sqrt(w.hidden)),
+                             poss, w.rope_base)
+    slots = np.array([O.page_slot(bt, s, p, w.page_size) for s, p in zip(seqs, poss)])
+    assert len(set(slots.tolist())) == n
+    untouched = np.ones(got.shape[0], bool)
+    untouched[slots] = False
+    assert (got[untouched] == -3.5).all(), "rows outside the written slots changed"
+    assert_parity(got[slots], ref_rows, w.dtype, "appended rows")
+    assert M.mla_device_error() == 0
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_append_is_page_table_invariant_bit_exact(path):
+    """The same rows appended under two page tables land as a bit-exact permutation."""
+    w = _wl("full", batch=2)
+    M.mla_set_kernel_path(path)
+    lens = np.array([256, 192], dtype=np.int32)
+    bt_perm, total = I.page_table(w, lens)
+    bt_id, _ = I.page_table(_wl("full", batch=2, permute_pages=False), lens)
+    seqs = np.concatenate([np.full(l, b) for b, l in enumerate(lens)]).astype(np.int32)
+    poss = np.concatenate([np.arange(l) for l in lens]).astype(np.int32)
+    note(f"append invariance path={path}")
+    h = device_tensor(torch, w, "h_rows", (len(seqs), w.hidden))
+    wd = device_tensor(torch, w, "w_dkv", (w.d_latent, w.hidden), 1 / math.sqrt(w.hidden))
+    wk = device_tensor(torch, w, "w_kr", (w.d_rope, w.hidden), 1 / math.sqrt(w.hidden))
+    out = []
+    for bt in (bt_perm, bt_id):
+        pool = _sentinel_pool(w, total)
+        M.mla_append_latent(_dims(w), h, wd, wk, torch.tensor(seqs, device="cuda"),
+                            torch.tensor(poss, device="cuda"), torch.tensor(bt, device="cuda"), pool)
+        bits = pool.view(torch.int16).cpu().numpy().reshape(-1, w.row)
+        out.append(np.stack([bits[O.page_slot(bt, s, p, 64)] for s, p in zip(seqs, poss)]))
+    np.testing.assert_array_equal(out[0], out[1])
+
+
+def test_append_bad_page_sets_error_and_writes_nothing():
+    w = _wl("tiny", batch=1)
+    pool = _sentinel_pool(w, 2)
+    h = device_tensor(torch, w, "h_rows", (2, w.hidden))
+    wd = device_tensor(torch, w, "w_dkv", (w.d_latent, w.hidden))
+    wk = device_tensor(torch, w, "w_kr", (w.d_rope, w.hidden))
+    bt = torch.tensor([[0, 9]], dtype=torch.int32, device="cuda")     # page 9 does not exist
+    note("append bad page")
+    M.mla_device_error(clear=True)
+    M.mla_append_latent(_dims(w), h, wd, wk, torch.zeros(2, dtype=torch.int32, device="cuda"),
+                        torch.tensor([70, 200], dtype=torch.int32, device="cuda"), bt, pool)
+    err = M.mla_device_error(clear=True)
+    assert err & 1 and err & 2          # bad table entry (pos 70) and position beyond the table (200)
+    assert (to_np(pool) == -3.5).all()
+
+
+# ------------------------------------------------------------- absorb_q --
+@pytest.mark.parametrize("name", ["tiny", "lite", "full"])
+@pytest.mark.parametrize("path", PATHS)
+def test_absorb_q(name, path):
+    w = _wl(name)
+    B = 5
+    M.mla_set_kernel_path(path)
+    note(f"absorb_q {name} path={path}")
+    sh = {n: w.weight_shape(n) for n in ("w_q", "w_qr", "w_uk")}
+    std = {n: 1 / math.sqrt(w.fan_in(n)) for n in sh}
+    dev = {n: device_tensor(torch, w, n, sh[n], std[n]) for n in sh}
+    h = device_tensor(torch, w, "h_q", (B, w.hidden))
+    pos_np = np.array([0, 1, 63, 4095, 131071][:B], dtype=np.int32)
+    q_lat = torch.empty((B, w.n_heads, w.d_latent), dtype=torch.float32, device="cuda")
+    q_pe = torch.empty((B, w.n_heads, w.d_rope), dtype=torch.float32, device="cuda")
+    d = _dims(w)
+    ws = torch.empty(M.mla_workspace_bytes(d, B), dtype=torch.uint8, device="cuda")
+    M.mla_absorb_q(d, h, dev["w_q"], dev["w_qr"], dev["w_uk"], torch.tensor(pos_np, device="cuda"),
+                   q_lat, q_pe, ws)
+    hh = host_tensor(w, "h_q", (B, w.hidden))
+    hw = {n: host_tensor(w, n, sh[n], std[n]) for n in sh}
+    ref_lat, ref_pe = [], []
+    for b in range(B):
+        ql, qp = O.absorb_q(hh[b], hw["w_q"], hw["w_qr"], hw["w_uk"], int(pos_np[b]), w.n_heads,
+                            w.d_head, w.d_latent, w.d_rope, w.rope_base)
+        ref_lat.append(ql)
+        ref_pe.append(qp)
+    assert_parity(to_np(q_lat), np.stack(ref_lat), w.dtype, "q_lat")
+    assert_parity(to_np(q_pe), np.stack(ref_pe), w.dtype, "q_pe")
+
+
+# ------------------------------------------------------------ attention --
+ATTN_CASES = [
+    ("tiny", [1, 64, 100, 129], 3, 16),
+    ("tiny", [64], 1, 64),
+    ("lite", [64, 777, 4096], 2, 64),
+    ("full", [1, 65, 1000, 4096], 4, 64),
+    ("full", [3000, 130], 8, 64),
+    ("full", [2], 5, 64),          # most splits empty
+]
+
+
+@pytest.mark.parametrize("name,lens,S,page", ATTN_CASES)
+@pytest.mark.parametrize("path", PATHS)
+def test_decode_attention_partials(name, lens, S, page, path):
+    w = _wl(name, batch=len(lens), page_size=page)
+    M.mla_set_kernel_path(path)
+    lens = np.array(lens, dtype=np.int32)
+    bt, total = I.page_table(w, lens)
+    B, nh = w.batch, w.n_heads
+    note(f"attention {name} lens={lens.tolist()} S={S} page={page} path={path}")
+    # q holds values exactly representable in the pool's storage type (the MFMA
+    # path rounds q to bf16 once per work unit; the rounding of computed
+    # queries is covered by the end-to-end step tests)
+    q_lat = device_tensor(torch, w, "q_lat_in", (B, nh, w.d_latent), 0.5).float().contiguous()
+    q_pe = device_tensor(torch, w, "q_pe_in", (B, nh, w.d_rope), 1.0).float().contiguous()
+    pool = device_tensor(torch, w, "pool", (total, page, w.row))
+    o_part = torch.full((B, S, nh, w.d_latent), 123.0, device="cuda")
+    lse_part = torch.full((B, S, nh), 123.0, device="cuda")
+    d = _dims(w)
+    M.mla_decode_attention(d, q_lat, q_pe, pool, torch.tensor(bt, device="cuda"),
+                           torch.tensor(lens, device="cuda"), o_part, lse_part)
+    got_o, got_l = to_np(o_part), to_np(lse_part)
+    hq = host_tensor(w, "q_lat_in", (B, nh, w.d_latent), 0.5)
+    hp = host_tensor(w, "q_pe_in", (B, nh, w.d_rope), 1.0)
+    tau = M.default_scale(d)
+    for b in range(B):
+        rows = I.to_f64(w, I.pool_rows(w, bt, b, int(lens[b])))
+        ro, rl = O.attention_partials(hq[b], hp[b], rows, S, w.d_latent, w.d_rope, tau, page)
+        assert_parity(got_o[b], ro, w.dtype, f"o_part b={b}")
+        assert_parity(got_l[b], rl, w.dtype, f"lse_part b={b}")
+    assert M.mla_device_error() == 0
+
+
+def test_attention_is_page_table_invariant():
+    """Output is bit-identical under a different physical placement of the same rows."""
+    w = _wl("full", batch=2)
+    lens = np.array([1000, 333], dtype=np.int32)
+    bt_p, total = I.page_table(w, lens)
+    bt_i, _ = I.page_table(_wl("full", batch=2, permute_pages=False), lens)
+    note("attention page-table invariance")
+    pool_p = device_tensor(torch, w, "pool", (total, 64, w.row))
+    # same logical rows, identity placement: move page bt_p[b][k] to page bt_i[b][k]
+    pool_i = torch.empty_like(pool_p)
+    src = torch.tensor(np.concatenate([bt_p[b, :(l + 63) // 64] for b, l in enumerate(lens)]),
+                       device="cuda").long()
+    dst = torch.tensor(np.concatenate([bt_i[b, :(l + 63) // 64] for b, l in enumerate(lens)]),
+                       device="cuda").long()
+    pool_i[dst] = pool_p[src]
+    q_lat = device_tensor(torch, w, "q_lat_in", (2, w.n_heads, w.d_latent), 0.5).float().contiguous()
+    q_pe = device_tensor(torch, w, "q_pe_in", (2, w.n_heads, w.d_rope), 1.0).float().contiguous()
+    res = []
+    for pool, bt in ((pool_p, bt_p), (pool_i, bt_i)):
+        o = torch.empty((2, 4, w.n_heads, w.d_latent), device="cuda")
+        l = torch.empty((2, 4, w.n_heads), device="cuda")
+        M.mla_decode_attention(_dims(w), q_lat, q_pe, pool, torch.tensor(bt, device="cuda"),
+                               torch.tensor(lens, device="cuda"), o, l)
+        res.append((o.cpu().numpy(), l.cpu().numpy()))
+    np.testing.assert_array_equal(res[0][0], res[1][0])
+    np.testing.assert_array_equal(res[0][1], res[1][1])
+
+
+# ---------------------------------------------------------------- merge --
+@pytest.mark.parametrize("name,S", [("tiny", 3), ("full", 8), ("full", 64)])
+@pytest.mark.parametrize("path", PATHS)
+def test_merge_lse(name, S, path):
+    w = _wl(name)
+    B, nh = 3, w.n_heads
+    M.mla_set_kernel_path(path)
+    note(f"merge {name} S={S} path={path}")
+    o_part = device_tensor(torch, w, "o_part_in", (B, S, nh, w.d_latent), 1.0, dtype=torch.float32)
+    lse_part = device_tensor(torch, w, "lse_part_in", (B, S, nh), 3.0, dtype=torch.float32)
+    lse_host = I.normal_f32(I.stream_key(w.seed, "lse_part_in"), 0, B * S * nh, 3.0).astype(
+        np.float64).reshape(B, S, nh)
+    # empty splits: every other split of sequence 1, and all splits of head 0 of sequence 2
+    lse_part[1, ::2] = -math.inf
+    lse_part[2, :, 0] = -math.inf
+    lse_host[1, ::2] = -np.inf
+    lse_host[2, :, 0] = -np.inf
+    o_host = I.normal_f32(I.stream_key(w.seed, "o_part_in"), 0, B * S * nh * w.d_latent).astype(
+        np.float64).reshape(B, S, nh, w.d_latent)
+    o_lat = torch.empty((B, nh, w.d_latent), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, nh), device="cuda")
+    M.mla_merge_lse(_dims(w), o_part, lse_part, o_lat, lse)
+    ro, rl = zip(*[O.merge_lse(o_host[b], lse_host[b]) for b in range(B)])
+    assert_parity(to_np(o_lat), np.stack(ro), w.dtype, "o_lat")
+    assert_parity(to_np(lse), np.stack(rl), w.dtype, "lse")
+    assert (to_np(o_lat)[2, 0] == 0).all() and np.isneginf(to_np(lse)[2, 0])
+
+
+# ----------------------------------------------------------- absorb_out --
+@pytest.mark.parametrize("name", ["tiny", "lite", "full"])
+@pytest.mark.parametrize("path", PATHS)
+def test_absorb_out(name, path):
+    w = _wl(name)
+    B = 6
+    M.mla_set_kernel_path(path)
+    note(f"absorb_out {name} path={path}")
+    std = {n: 1 / math.sqrt(w.fan_in(n)) for n in ("w_uv", "w_o")}
+    wuv = device_tensor(torch, w, "w_uv", w.weight_shape("w_uv"), std["w_uv"])
+    wo = device_tensor(torch, w, "w_o", w.weight_shape("w_o"), std["w_o"])
+    o_lat = device_tensor(torch, w, "o_lat_in", (B, w.n_heads, w.d_latent), dtype=torch.float32)
+    u = torch.empty((B, w.hidden), dtype=torch.float32, device="cuda")
+    d = _dims(w)
+    ws = torch.empty(M.mla_workspace_bytes(d, B), dtype=torch.uint8, device="cuda")
+    M.mla_absorb_out(d, o_lat, wuv, wo, u, ws)
+    hu = host_tensor(w, "w_uv", w.weight_shape("w_uv"), std["w_uv"])
+    ho = host_tensor(w, "w_o", w.weight_shape("w_o"), std["w_o"])
+    hl = I.normal_f32(I.stream_key(w.seed, "o_lat_in"), 0, B * w.n_heads * w.d_latent).astype(
+        np.float64).reshape(B, w.n_heads, w.d_latent)
+    ref = np.stack([O.absorb_out(hl[b], hu, ho, w.n_heads, w.d_head, w.d_latent) for b in range(B)])
+    assert_parity(to_np(u), ref, w.dtype, "u")

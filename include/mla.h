@@ -85,6 +85,8 @@ typedef struct {
  * position row_pos[r] of sequence row_seq[r].  Also the cache-fill path.
  *   h        [n_rows, H] dtype          row_seq, row_pos  [n_rows] int32
  *   block_table [n_seqs, max_pages] int32, pool [num_pages, page_size, d_c+d_R]
+ * Workspace: mla_append_workspace_bytes(dims, n_rows) bytes of device memory
+ * (may be 0, then workspace may be NULL); scratch for the duration of the call.
  * Rows whose (seq, pos) or table entry is out of range are not written and set
  * the device error word.  Rows must target distinct slots (else the last
  * writer is unspecified).  n_rows == 0 is a no-op.
@@ -92,8 +94,8 @@ typedef struct {
 mla_status mla_append_latent(const mla_dims* dims, const void* h, const void* w_dkv,
                              const void* w_kr, const int32_t* row_seq, const int32_t* row_pos,
                              int32_t n_rows, const int32_t* block_table, int32_t n_seqs,
-                             int32_t max_pages, void* pool, int64_t num_pages,
-                             hipStream_t stream);
+                             int32_t max_pages, void* pool, int64_t num_pages, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Absorbed query ([Report] §2.3: q.(W_UK c) regrouped as (W_UK^T q).c; §3.1:
@@ -152,8 +154,13 @@ mla_status mla_absorb_out(const mla_dims* dims, const float* o_lat, const void* 
                           size_t workspace_bytes, hipStream_t stream);
 
 /* Workspace bytes needed by mla_absorb_q / mla_absorb_out for `batch` sequences
- * (0 if dims are invalid). */
+ * (0 if dims are invalid): the intermediate q^C or o (batch x n_h*d_h in dtype)
+ * followed by fp32 partial sums of the projection GEMMs. */
 size_t mla_workspace_bytes(const mla_dims* dims, int32_t batch);
+
+/* Workspace bytes needed by mla_append_latent for `n_rows` rows (0 if none is
+ * needed or dims are invalid). */
+size_t mla_append_workspace_bytes(const mla_dims* dims, int32_t n_rows);
 
 /* Static text for a status code. */
 const char* mla_status_string(int32_t status);

@@ -20,7 +20,8 @@ MLA_F32, MLA_BF16 = 0, 1
 
 __all__ = ["MlaDims", "MlaError", "make_dims", "load", "mla_append_latent", "mla_absorb_q",
            "mla_decode_attention", "mla_merge_lse", "mla_absorb_out", "mla_workspace_bytes",
-           "mla_device_error", "mla_set_kernel_path", "mla_status_string", "LIB_PATH"]
+           "mla_append_workspace_bytes", "mla_device_error", "mla_set_kernel_path",
+           "mla_status_string", "LIB_PATH"]
 
 
 class MlaDims(ctypes.Structure):
@@ -49,18 +50,20 @@ _I32, _I64, _SZ = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 _DIMS = ctypes.POINTER(MlaDims)
 
 _SIGS = {
-    "mla_append_latent": [_DIMS, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _P, _I64, _P],
+    "mla_append_latent": [_DIMS, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _P, _I64, _P, _SZ, _P],
     "mla_absorb_q": [_DIMS, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P],
     "mla_decode_attention": [_DIMS, _P, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _P, _P, _P],
     "mla_merge_lse": [_DIMS, _P, _P, _I32, _I32, _P, _P, _P],
     "mla_absorb_out": [_DIMS, _P, _P, _P, _I32, _P, _P, _SZ, _P],
     "mla_workspace_bytes": [_DIMS, _I32],
+    "mla_append_workspace_bytes": [_DIMS, _I32],
     "mla_status_string": [_I32],
     "mla_abi_version": [],
     "mla_device_error": [ctypes.POINTER(_I32), _I32, _P],
     "mla_set_kernel_path": [_I32],
 }
-_RES = {"mla_workspace_bytes": _SZ, "mla_status_string": ctypes.c_char_p}
+_RES = {"mla_workspace_bytes": _SZ, "mla_append_workspace_bytes": _SZ,
+        "mla_status_string": ctypes.c_char_p}
 
 
 def load(path: str = LIB_PATH):
@@ -117,6 +120,10 @@ def mla_workspace_bytes(dims: MlaDims, batch: int) -> int:
     return int(load().mla_workspace_bytes(ctypes.byref(dims), batch))
 
 
+def mla_append_workspace_bytes(dims: MlaDims, n_rows: int) -> int:
+    return int(load().mla_append_workspace_bytes(ctypes.byref(dims), n_rows))
+
+
 def mla_set_kernel_path(path: int) -> int:
     return int(load().mla_set_kernel_path(path))
 
@@ -127,8 +134,11 @@ def mla_device_error(clear: bool = True, stream=None) -> int:
     return out.value
 
 
-def mla_append_latent(dims, h, w_dkv, w_kr, row_seq, row_pos, block_table, pool, stream=None):
-    """Write [W_DKV h | RoPE(W_KR h, pos)] of each row of ``h`` into the paged pool."""
+def mla_append_latent(dims, h, w_dkv, w_kr, row_seq, row_pos, block_table, pool, workspace=None,
+                      stream=None):
+    """Write [W_DKV h | RoPE(W_KR h, pos)] of each row of ``h`` into the paged pool.
+    ``workspace``: a device byte buffer of at least mla_append_workspace_bytes(dims,
+    n_rows) bytes (allocated here when omitted)."""
     import torch
     n, row = h.shape[0], dims.d_latent + dims.d_rope
     _expect(h, (n, dims.hidden), _elem(dims), "h")
@@ -139,10 +149,13 @@ def mla_append_latent(dims, h, w_dkv, w_kr, row_seq, row_pos, block_table, pool,
     _expect(pool, (pool.shape[0], dims.page_size, row), _elem(dims), "pool")
     if block_table.dtype != torch.int32 or block_table.dim() != 2:
         raise ValueError("block_table must be int32 [n_seqs, max_pages]")
+    if workspace is None:
+        need = mla_append_workspace_bytes(dims, n)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=h.device)
     _check("mla_append_latent", load().mla_append_latent(
         ctypes.byref(dims), _ptr(h), _ptr(w_dkv), _ptr(w_kr), _ptr(row_seq), _ptr(row_pos), n,
         _ptr(block_table), block_table.shape[0], block_table.shape[1], _ptr(pool), pool.shape[0],
-        _stream(stream)))
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def mla_absorb_q(dims, h, w_q, w_qr, w_uk, pos, q_lat, q_pe, workspace, stream=None):

@@ -21,7 +21,8 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-
          "-I" + os.path.join(ROOT, "include")]
 
 LIBS = {
-    "libmla.so": ["mla_api.cpp", "errword.hip", "kernels_generic.hip", "kernels_fast.hip"],
+    "libmla.so": ["mla_api.cpp", "errword.hip", "kernels_generic.hip", "kernels_fast.hip",
+                  "gemm_fast.hip"],
     "libmla_inputs.so": ["fill_inputs.hip"],
 }
 

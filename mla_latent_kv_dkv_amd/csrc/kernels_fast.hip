@@ -419,8 +419,6 @@ hipError_t launch_attention_fast(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-bool fast_gemm_ok(const GemmArgs&) { return false; }
-hipError_t launch_gemm_fast(const GemmArgs&, hipStream_t) { return hipErrorNotSupported; }
 bool fast_merge_ok(const MergeArgs&) { return false; }
 hipError_t launch_merge_fast(const MergeArgs&, hipStream_t) { return hipErrorNotSupported; }
 

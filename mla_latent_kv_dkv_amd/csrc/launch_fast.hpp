@@ -11,7 +11,10 @@ namespace mla {
 int* error_word_address();
 
 bool fast_gemm_ok(const GemmArgs& a);
-hipError_t launch_gemm_fast(const GemmArgs& a, hipStream_t stream);
+// fp32 scratch the fast GEMM needs for its K-split partials (0 if none)
+size_t gemm_partial_bytes(const GemmArgs& a);
+hipError_t launch_gemm_fast(const GemmArgs& a, void* partial, size_t partial_bytes,
+                            hipStream_t stream);
 
 bool fast_attention_ok(const AttnArgs& a);
 hipError_t launch_attention_fast(const AttnArgs& a, hipStream_t stream);

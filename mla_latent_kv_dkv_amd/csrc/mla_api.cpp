@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstring>
@@ -61,6 +62,97 @@ bool use_fast() { return g_path.load(std::memory_order_relaxed) == 0; }
 
 mla_status hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
 
+// Shapes of the projection GEMMs (pointers filled in by the callers).
+mla::GemmArgs qproj_args(const mla_dims* d, int batch) {
+  const bool bf16 = d->dtype == MLA_BF16;
+  const int64_t nhdh = static_cast<int64_t>(d->n_heads) * d->d_head;
+  mla::GemmArgs a{};
+  a.ldx_m = d->hidden; a.ldx_k = 1;
+  a.n_split = static_cast<int>(nhdh);
+  a.ldw_n = d->hidden; a.ldw_k = 1;
+  a.M = batch; a.N = static_cast<int>(nhdh + static_cast<int64_t>(d->n_heads) * d->d_rope);
+  a.K = d->hidden; a.batch = 1;
+  a.epi = mla::EPI_QPROJ; a.x_f32 = !bf16; a.y_f32 = !bf16;
+  a.ldy = nhdh; a.d_rope = d->d_rope;
+  a.log_base = std::log(static_cast<double>(d->rope_base));
+  return a;
+}
+
+mla::GemmArgs uk_args(const mla_dims* d, int batch) {
+  const bool bf16 = d->dtype == MLA_BF16;
+  const int64_t nhdh = static_cast<int64_t>(d->n_heads) * d->d_head;
+  mla::GemmArgs g{};
+  g.ldx_m = nhdh; g.ldx_k = 1; g.x_bs = d->d_head;
+  g.n_split = d->d_latent;
+  g.ldw_n = 1; g.ldw_k = d->d_latent; g.w_bs = static_cast<int64_t>(d->d_head) * d->d_latent;
+  g.M = batch; g.N = d->d_latent; g.K = d->d_head; g.batch = d->n_heads;
+  g.epi = mla::EPI_STORE; g.x_f32 = !bf16; g.y_f32 = 1;
+  g.ldy = static_cast<int64_t>(d->n_heads) * d->d_latent; g.y_bs = d->d_latent;
+  return g;
+}
+
+mla::GemmArgs uv_args(const mla_dims* d, int batch) {
+  const bool bf16 = d->dtype == MLA_BF16;
+  const int64_t nhdh = static_cast<int64_t>(d->n_heads) * d->d_head;
+  mla::GemmArgs g{};
+  g.ldx_m = static_cast<int64_t>(d->n_heads) * d->d_latent; g.ldx_k = 1; g.x_bs = d->d_latent;
+  g.n_split = d->d_head;
+  g.ldw_n = d->d_latent; g.ldw_k = 1; g.w_bs = static_cast<int64_t>(d->d_head) * d->d_latent;
+  g.M = batch; g.N = d->d_head; g.K = d->d_latent; g.batch = d->n_heads;
+  g.epi = mla::EPI_STORE; g.x_f32 = 1; g.y_f32 = !bf16;
+  g.ldy = nhdh; g.y_bs = d->d_head;
+  return g;
+}
+
+mla::GemmArgs oproj_args(const mla_dims* d, int batch) {
+  const bool bf16 = d->dtype == MLA_BF16;
+  const int64_t nhdh = static_cast<int64_t>(d->n_heads) * d->d_head;
+  mla::GemmArgs a{};
+  a.ldx_m = nhdh; a.ldx_k = 1;
+  a.n_split = d->hidden;
+  a.ldw_n = nhdh; a.ldw_k = 1;
+  a.M = batch; a.N = d->hidden; a.K = static_cast<int>(nhdh); a.batch = 1;
+  a.epi = mla::EPI_STORE; a.x_f32 = !bf16; a.y_f32 = 1;
+  a.ldy = d->hidden;
+  return a;
+}
+
+mla::GemmArgs append_args(const mla_dims* d, int n_rows) {
+  const bool bf16 = d->dtype == MLA_BF16;
+  mla::GemmArgs a{};
+  a.ldx_m = d->hidden; a.ldx_k = 1; a.x_bs = 0;
+  a.n_split = d->d_latent;
+  a.ldw_n = d->hidden; a.ldw_k = 1; a.w_bs = 0;
+  a.M = n_rows; a.N = d->d_latent + d->d_rope; a.K = d->hidden; a.batch = 1;
+  a.epi = mla::EPI_APPEND; a.x_f32 = !bf16;
+  a.d_rope = d->d_rope; a.log_base = std::log(static_cast<double>(d->rope_base));
+  a.row_width = d->d_latent + d->d_rope;
+  return a;
+}
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+// Bytes of the activation region (q^C or the per-head outputs o) at the front
+// of the workspace.
+size_t act_bytes(const mla_dims* d, int batch) {
+  return align256(static_cast<size_t>(batch) * d->n_heads * d->d_head * elem_bytes(d));
+}
+
+bool fast_for(const mla_dims* d, const mla::GemmArgs& a) {
+  return use_fast() && d->dtype == MLA_BF16 && mla::fast_gemm_ok(a);
+}
+
+size_t partial_bytes(const mla_dims* d, const mla::GemmArgs& a) {
+  return fast_for(d, a) ? align256(mla::gemm_partial_bytes(a)) : 0;
+}
+
+// Run one projection GEMM on the fast path when it applies, else the vector path.
+hipError_t run_gemm(const mla_dims* d, const mla::GemmArgs& a, void* partial, size_t pbytes,
+                    hipStream_t stream) {
+  if (fast_for(d, a)) return mla::launch_gemm_fast(a, partial, pbytes, stream);
+  return mla::launch_gemm_generic(a, d->dtype == MLA_BF16, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -83,9 +175,19 @@ const char* mla_status_string(int32_t s) {
 
 size_t mla_workspace_bytes(const mla_dims* d, int32_t batch) {
   if (check_dims(d) != MLA_OK || batch < 0) return 0;
-  // q^C (absorb_q) or the per-head outputs o (absorb_out): [batch, n_h*d_h] in dtype
-  const size_t n = static_cast<size_t>(batch) * d->n_heads * d->d_head;
-  return ((n * elem_bytes(d) + 255) / 256) * 256 + 256;
+  // [activation region: q^C or o, batch x n_h*d_h in dtype][fp32 K-split partials]
+  size_t part = 0;
+  if (batch > 0) {
+    for (const mla::GemmArgs& a : {qproj_args(d, batch), uk_args(d, batch), uv_args(d, batch),
+                                   oproj_args(d, batch), append_args(d, batch)})
+      part = std::max(part, partial_bytes(d, a));
+  }
+  return act_bytes(d, batch) + part + 256;
+}
+
+size_t mla_append_workspace_bytes(const mla_dims* d, int32_t n_rows) {
+  if (check_dims(d) != MLA_OK || n_rows < 0) return 0;
+  return n_rows > 0 ? partial_bytes(d, append_args(d, n_rows)) + 256 : 0;
 }
 
 mla_status mla_device_error(int32_t* out, int32_t clear, hipStream_t stream) {
@@ -106,7 +208,8 @@ mla_status mla_device_error(int32_t* out, int32_t clear, hipStream_t stream) {
 mla_status mla_append_latent(const mla_dims* d, const void* h, const void* w_dkv, const void* w_kr,
                              const int32_t* row_seq, const int32_t* row_pos, int32_t n_rows,
                              const int32_t* block_table, int32_t n_seqs, int32_t max_pages,
-                             void* pool, int64_t num_pages, hipStream_t stream) {
+                             void* pool, int64_t num_pages, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
   mla_status st = check_dims(d);
   if (st != MLA_OK) return st;
   if (n_rows < 0 || n_seqs < 0 || max_pages < 0 || num_pages < 0) return MLA_ERR_SHAPE;
@@ -114,21 +217,16 @@ mla_status mla_append_latent(const mla_dims* d, const void* h, const void* w_dkv
   if (n_seqs < 1 || max_pages < 1 || num_pages < 1) return MLA_ERR_SHAPE;
   if (static_cast<int64_t>(max_pages) * d->page_size > (int64_t{1} << 30)) return MLA_ERR_SHAPE;
   if (!h || !w_dkv || !w_kr || !row_seq || !row_pos || !block_table || !pool) return MLA_ERR_NULL;
+  mla::GemmArgs a = append_args(d, n_rows);
+  const size_t need = partial_bytes(d, a);
+  if (need > 0 && (!ws || ws_bytes < need)) return MLA_ERR_WORKSPACE;
   int* err = err_word();
   if (!err) return MLA_ERR_HIP;
-  const bool bf16 = d->dtype == MLA_BF16;
-  mla::GemmArgs a{};
-  a.x = h; a.ldx_m = d->hidden; a.ldx_k = 1; a.x_bs = 0;
-  a.w1 = w_dkv; a.w2 = w_kr; a.n_split = d->d_latent;
-  a.ldw_n = d->hidden; a.ldw_k = 1; a.w_bs = 0;
-  a.M = n_rows; a.N = d->d_latent + d->d_rope; a.K = d->hidden; a.batch = 1;
-  a.epi = mla::EPI_APPEND; a.x_f32 = !bf16;
-  a.y = pool; a.d_rope = d->d_rope; a.log_base = std::log(static_cast<double>(d->rope_base));
+  a.x = h; a.w1 = w_dkv; a.w2 = w_kr; a.y = pool;
   a.pos = row_pos; a.row_seq = row_seq; a.block_table = block_table;
   a.n_seqs = n_seqs; a.max_pages = max_pages; a.page_size = d->page_size;
-  a.row_width = d->d_latent + d->d_rope; a.num_pages = num_pages; a.err = err;
-  if (use_fast() && bf16 && mla::fast_gemm_ok(a)) return hip_status(mla::launch_gemm_fast(a, stream));
-  return hip_status(mla::launch_gemm_generic(a, bf16, stream));
+  a.num_pages = num_pages; a.err = err;
+  return hip_status(run_gemm(d, a, ws, ws_bytes, stream));
 }
 
 mla_status mla_absorb_q(const mla_dims* d, const void* h, const void* w_q, const void* w_qr,
@@ -140,33 +238,16 @@ mla_status mla_absorb_q(const mla_dims* d, const void* h, const void* w_q, const
   if (batch == 0) return MLA_OK;
   if (!h || !w_q || !w_qr || !w_uk || !pos || !q_lat || !q_pe) return MLA_ERR_NULL;
   if (!ws || ws_bytes < mla_workspace_bytes(d, batch)) return MLA_ERR_WORKSPACE;
-  const bool bf16 = d->dtype == MLA_BF16;
-  const int64_t nhdh = static_cast<int64_t>(d->n_heads) * d->d_head;
-  // 1) [q^C | q^R] = h [W_Q; W_QR]^T, RoPE on the q^R columns
-  mla::GemmArgs a{};
-  a.x = h; a.ldx_m = d->hidden; a.ldx_k = 1;
-  a.w1 = w_q; a.w2 = w_qr; a.n_split = static_cast<int>(nhdh);
-  a.ldw_n = d->hidden; a.ldw_k = 1;
-  a.M = batch; a.N = static_cast<int>(nhdh + static_cast<int64_t>(d->n_heads) * d->d_rope);
-  a.K = d->hidden; a.batch = 1;
-  a.epi = mla::EPI_QPROJ; a.x_f32 = !bf16; a.y_f32 = !bf16;
-  a.y = ws; a.ldy = nhdh; a.y2 = q_pe; a.d_rope = d->d_rope;
-  a.log_base = std::log(static_cast<double>(d->rope_base)); a.pos = pos;
-  hipError_t e = (use_fast() && bf16 && mla::fast_gemm_ok(a)) ? mla::launch_gemm_fast(a, stream)
-                                                              : mla::launch_gemm_generic(a, bf16, stream);
-  if (e != hipSuccess) return MLA_ERR_HIP;
-  // 2) q_lat[b, i, :] = W_UK,i^T q^C[b, i, :] : per head i, X = q^C_i [B, d_h], W(n=c, k=dh)
-  mla::GemmArgs g{};
-  g.x = ws; g.ldx_m = nhdh; g.ldx_k = 1; g.x_bs = d->d_head;
-  g.w1 = w_uk; g.w2 = w_uk; g.n_split = d->d_latent;
-  g.ldw_n = 1; g.ldw_k = d->d_latent; g.w_bs = static_cast<int64_t>(d->d_head) * d->d_latent;
-  g.M = batch; g.N = d->d_latent; g.K = d->d_head; g.batch = d->n_heads;
-  g.epi = mla::EPI_STORE; g.x_f32 = !bf16; g.y_f32 = 1;
-  g.y = q_lat; g.ldy = static_cast<int64_t>(d->n_heads) * d->d_latent;
-  g.y_bs = d->d_latent;
-  e = (use_fast() && bf16 && mla::fast_gemm_ok(g)) ? mla::launch_gemm_fast(g, stream)
-                                                    : mla::launch_gemm_generic(g, bf16, stream);
-  return hip_status(e);
+  char* part = static_cast<char*>(ws) + act_bytes(d, batch);
+  const size_t pbytes = ws_bytes - act_bytes(d, batch);
+  // 1) [q^C | q^R] = h [W_Q; W_QR]^T, RoPE on the q^R columns; q^C -> workspace
+  mla::GemmArgs a = qproj_args(d, batch);
+  a.x = h; a.w1 = w_q; a.w2 = w_qr; a.y = ws; a.y2 = q_pe; a.pos = pos;
+  if (run_gemm(d, a, part, pbytes, stream) != hipSuccess) return MLA_ERR_HIP;
+  // 2) q_lat[b, i, :] = W_UK,i^T q^C[b, i, :] per head i
+  mla::GemmArgs g = uk_args(d, batch);
+  g.x = ws; g.w1 = w_uk; g.w2 = w_uk; g.y = q_lat;
+  return hip_status(run_gemm(d, g, part, pbytes, stream));
 }
 
 mla_status mla_decode_attention(const mla_dims* d, const float* q_lat, const float* q_pe,
@@ -221,31 +302,16 @@ mla_status mla_absorb_out(const mla_dims* d, const float* o_lat, const void* w_u
   if (batch == 0) return MLA_OK;
   if (!o_lat || !w_uv || !w_o || !u) return MLA_ERR_NULL;
   if (!ws || ws_bytes < mla_workspace_bytes(d, batch)) return MLA_ERR_WORKSPACE;
-  const bool bf16 = d->dtype == MLA_BF16;
-  const int64_t nhdh = static_cast<int64_t>(d->n_heads) * d->d_head;
-  // 1) o[b, i*d_h + e] = sum_c W_UV[i*d_h + e, c] o_lat[b, i, c]   (per head i)
-  mla::GemmArgs g{};
-  g.x = o_lat; g.ldx_m = static_cast<int64_t>(d->n_heads) * d->d_latent; g.ldx_k = 1;
-  g.x_bs = d->d_latent;
-  g.w1 = w_uv; g.w2 = w_uv; g.n_split = d->d_head;
-  g.ldw_n = d->d_latent; g.ldw_k = 1; g.w_bs = static_cast<int64_t>(d->d_head) * d->d_latent;
-  g.M = batch; g.N = d->d_head; g.K = d->d_latent; g.batch = d->n_heads;
-  g.epi = mla::EPI_STORE; g.x_f32 = 1; g.y_f32 = !bf16;
-  g.y = ws; g.ldy = nhdh; g.y_bs = d->d_head;
-  hipError_t e = (use_fast() && bf16 && mla::fast_gemm_ok(g)) ? mla::launch_gemm_fast(g, stream)
-                                                              : mla::launch_gemm_generic(g, bf16, stream);
-  if (e != hipSuccess) return MLA_ERR_HIP;
+  char* part = static_cast<char*>(ws) + act_bytes(d, batch);
+  const size_t pbytes = ws_bytes - act_bytes(d, batch);
+  // 1) o[b, i*d_h + e] = sum_c W_UV[i*d_h + e, c] o_lat[b, i, c] per head i -> workspace
+  mla::GemmArgs g = uv_args(d, batch);
+  g.x = o_lat; g.w1 = w_uv; g.w2 = w_uv; g.y = ws;
+  if (run_gemm(d, g, part, pbytes, stream) != hipSuccess) return MLA_ERR_HIP;
   // 2) u = o W_O^T
-  mla::GemmArgs a{};
-  a.x = ws; a.ldx_m = nhdh; a.ldx_k = 1;
-  a.w1 = w_o; a.w2 = w_o; a.n_split = d->hidden;
-  a.ldw_n = nhdh; a.ldw_k = 1;
-  a.M = batch; a.N = d->hidden; a.K = static_cast<int>(nhdh); a.batch = 1;
-  a.epi = mla::EPI_STORE; a.x_f32 = !bf16; a.y_f32 = 1;
-  a.y = u; a.ldy = d->hidden;
-  e = (use_fast() && bf16 && mla::fast_gemm_ok(a)) ? mla::launch_gemm_fast(a, stream)
-                                                    : mla::launch_gemm_generic(a, bf16, stream);
-  return hip_status(e);
+  mla::GemmArgs a = oproj_args(d, batch);
+  a.x = ws; a.w1 = w_o; a.w2 = w_o; a.y = u;
+  return hip_status(run_gemm(d, a, part, pbytes, stream));
 }
 
 }  // extern "C"

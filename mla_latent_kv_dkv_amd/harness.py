@@ -8,8 +8,9 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (make_dims, mla_absorb_out, mla_absorb_q, mla_append_latent, mla_decode_attention,
-               mla_merge_lse, mla_workspace_bytes)
+from . import (make_dims, mla_absorb_out, mla_absorb_q, mla_append_latent,
+               mla_append_workspace_bytes, mla_decode_attention, mla_merge_lse,
+               mla_workspace_bytes)
 from . import inputs as I
 
 
@@ -53,6 +54,8 @@ class DeviceWorkload:
             I.fill_device(self.h, I.stream_key(w.seed, "h_dec", layer))
             I.fill_device(self.pool, I.stream_key(w.seed, "pool", layer))
         nh = w.n_heads
+        self.ws_append = torch.empty(max(1, mla_append_workspace_bytes(self.dims, B)),
+                                     dtype=torch.uint8, device=self.dev)
         if outputs_from is not None:     # share scratch/output buffers with another layer
             for k in ("q_lat", "q_pe", "o_part", "lse_part", "o_lat", "lse", "u", "ws"):
                 setattr(self, k, getattr(outputs_from, k))
@@ -93,7 +96,7 @@ class DeviceWorkload:
         B = self.w.batch
         seq = self.torch.arange(B, dtype=self.torch.int32, device=self.dev)
         mla_append_latent(self.dims, self.h, self.weights["w_dkv"], self.weights["w_kr"], seq,
-                          self.pos, self.block_table, self.pool)
+                          self.pos, self.block_table, self.pool, self.ws_append)
 
     def attention(self):
         mla_decode_attention(self.dims, self.q_lat, self.q_pe, self.pool, self.block_table,

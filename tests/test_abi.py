@@ -55,6 +55,12 @@ def test_status_strings_and_version():
 def test_workspace_bytes():
     d = _dims()
     assert M.mla_workspace_bytes(d, 8) >= 8 * 4 * 16 * 4
+    # full shape, bf16: the intermediate plus room for the fp32 K-split partials
+    full = M.make_dims(5120, 128, 128, 512, 64, "bf16")
+    assert M.mla_workspace_bytes(full, 64) >= 64 * 128 * 128 * 2 + 64 * 24576 * 4
+    assert M.mla_append_workspace_bytes(full, 64) >= 64 * 576 * 4
+    assert M.mla_append_workspace_bytes(full, 0) == 0
+    assert M.mla_append_workspace_bytes(d, 64) <= 256        # fp32 dims use the vector path
     assert M.mla_workspace_bytes(_dims(dtype="bf16"), 8) >= 8 * 4 * 16 * 2
     assert M.mla_workspace_bytes(_dims(d_rope=7), 8) == 0
     assert M.mla_workspace_bytes(d, -1) == 0
@@ -87,13 +93,15 @@ def test_argument_checks():
     assert lib.mla_decode_attention(ctypes.byref(d), None, P, P, 1, P, 1, P, 1, 1, P, P, None) == -1
     assert lib.mla_merge_lse(ctypes.byref(d), P, None, 1, 1, P, None, None) == -1
     assert lib.mla_absorb_out(ctypes.byref(d), P, P, None, 1, P, P, 1 << 20, None) == -1
-    assert lib.mla_append_latent(ctypes.byref(d), P, P, None, P, P, 1, P, 1, 1, P, 1, None) == -1
+    assert lib.mla_append_latent(ctypes.byref(d), P, P, None, P, P, 1, P, 1, 1, P, 1, None, 0,
+                                 None) == -1
     # counts
     assert lib.mla_decode_attention(ctypes.byref(d), P, P, P, 1, P, 1, P, 1, 0, P, P, None) == -2
     assert lib.mla_decode_attention(ctypes.byref(d), P, P, P, 1, P, 1, P, 1, 5000, P, P, None) == -2
     assert lib.mla_decode_attention(ctypes.byref(d), P, P, P, 1, P, 1, P, -1, 1, P, P, None) == -2
     assert lib.mla_merge_lse(ctypes.byref(d), P, P, 1, 0, P, None, None) == -2
-    assert lib.mla_append_latent(ctypes.byref(d), P, P, P, P, P, -3, P, 1, 1, P, 1, None) == -2
+    assert lib.mla_append_latent(ctypes.byref(d), P, P, P, P, P, -3, P, 1, 1, P, 1, None, 0,
+                                 None) == -2
     # workspace
     assert lib.mla_absorb_q(ctypes.byref(d), P, P, P, P, P, 4, P, P, None, 1 << 20, None) == -4
     assert lib.mla_absorb_q(ctypes.byref(d), P, P, P, P, P, 4, P, P, P, 16, None) == -4
@@ -102,7 +110,7 @@ def test_argument_checks():
     assert lib.mla_absorb_q(ctypes.byref(d), None, None, None, None, None, 0, None, None, None, 0,
                             None) == 0
     assert lib.mla_append_latent(ctypes.byref(d), None, None, None, None, None, 0, None, 0, 0, None,
-                                 0, None) == 0
+                                 0, None, 0, None) == 0
 
 
 def test_device_fill_argument_checks():

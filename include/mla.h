@@ -58,7 +58,8 @@ typedef enum {
   MLA_ERR_NULL = -1,        /* a required pointer is NULL */
   MLA_ERR_SHAPE = -2,       /* a dimension or count is out of range */
   MLA_ERR_UNSUPPORTED = -3, /* dtype / abi_version / page_size not supported */
-  MLA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than mla_workspace_bytes() */
+  MLA_ERR_WORKSPACE = -4,   /* workspace missing, smaller than mla_workspace_bytes() or
+                               not 256-byte aligned */
   MLA_ERR_HIP = -5          /* a kernel launch was rejected by the HIP runtime */
 } mla_status;
 
@@ -85,8 +86,9 @@ typedef struct {
  * position row_pos[r] of sequence row_seq[r].  Also the cache-fill path.
  *   h        [n_rows, H] dtype          row_seq, row_pos  [n_rows] int32
  *   block_table [n_seqs, max_pages] int32, pool [num_pages, page_size, d_c+d_R]
- * Workspace: mla_append_workspace_bytes(dims, n_rows) bytes of device memory
- * (may be 0, then workspace may be NULL); scratch for the duration of the call.
+ * Workspace: mla_append_workspace_bytes(dims, n_rows) bytes of device memory,
+ * 256-byte aligned (may be 0, then workspace may be NULL); scratch for the
+ * duration of the call.
  * Rows whose (seq, pos) or table entry is out of range are not written and set
  * the device error word.  Rows must target distinct slots (else the last
  * writer is unspecified).  n_rows == 0 is a no-op.
@@ -105,7 +107,8 @@ mla_status mla_append_latent(const mla_dims* dims, const void* h, const void* w_
  *   h [batch, H] dtype; pos [batch] int32; q_lat [batch, n_h, d_c] fp32;
  *   q_pe [batch, n_h, d_R] fp32.
  * Workspace: at least mla_workspace_bytes(dims, batch) bytes of device memory,
- * used for q^C; its contents are scratch for the duration of the call.
+ * 256-byte aligned, used for q^C; its contents are scratch for the duration of
+ * the call.
  */
 mla_status mla_absorb_q(const mla_dims* dims, const void* h, const void* w_q, const void* w_qr,
                         const void* w_uk, const int32_t* pos, int32_t batch, float* q_lat,
@@ -147,7 +150,8 @@ mla_status mla_merge_lse(const mla_dims* dims, const float* o_part, const float*
  * Absorbed output ([Report] §2.3: W_UV folded into the output projection):
  *   o_i = W_UV,i o_lat[b,i,:] (d_h),  u[b,:] = W_O [o_1; ...; o_n_h]   (H)
  *   o_lat [batch, n_h, d_c] fp32; u [batch, H] fp32.
- * Workspace: at least mla_workspace_bytes(dims, batch) bytes, used for o.
+ * Workspace: at least mla_workspace_bytes(dims, batch) bytes, 256-byte aligned,
+ * used for o.
  */
 mla_status mla_absorb_out(const mla_dims* dims, const float* o_lat, const void* w_uv,
                           const void* w_o, int32_t batch, float* u, void* workspace,

@@ -5,15 +5,20 @@
 // X[m, k] W[n, k] with M = batch (tens to hundreds), N and K in the thousands,
 // so the time is the time to read W once from HBM.
 //
-// k_gemm_skinny (W row-major [N, K], K contiguous): a workgroup of 4 waves owns
-// 64 rows of W and 64 rows of X; each wave takes a quarter of the workgroup's
-// K slice.  W and X fragments go straight from memory into MFMA operand
-// registers (no LDS on the way in): mfma_f32_32x32x16_bf16 with W rows as M and
-// X rows as N.  Inside each group of 64 k the lanes of k-group g hold
-// k = 32g + 8s + j for step s, so every lane reads 64 contiguous bytes per row.
-// The 4 wave partials are summed through LDS; with a K split across
-// workgroups the partial tiles go to an fp32 buffer that k_gemm_finish sums in
-// a fixed order (deterministic), applying the output stage.
+// k_gemm_ws (W row-major [N, K], K contiguous): a workgroup of 4 waves owns 64
+// rows of W, 16 per wave, and an M tile of up to 256 X rows.  Each wave
+// streams its 16 W rows straight from memory into MFMA A operands
+// (mfma_f32_16x16x32_bf16: lane l holds row l%16, k 8(l/16)..+7 of a 32-k
+// step), keeping kWsRing steps in flight per lane.  The X rows of the current
+// K chunk sit in LDS, shared by the 4 waves (B operands, one ds_read_b128 per
+// 16-row block and step); chunk c + kWsXAhead is loaded into registers when
+// chunk c starts and written to LDS one chunk before it is used, so that the
+// in-order completion count a wave waits on for X still leaves kWsRing W
+// steps in flight.  X is read once per workgroup (not once per wave),
+// so the vector memory path carries little beyond the W stream.  When the
+// W rows alone give too few workgroups to fill the chip, K is split across
+// workgroups: each writes an fp32 partial tile and k_gemm_finish sums them in
+// a fixed order (deterministic) and applies the output stage.
 //
 // k_gemm_uk (the per-head W_UK product, W row-major [K=d_h, N=d_c], N
 // contiguous): the workgroup stages a 128 x 128 W tile in LDS and reads MFMA
@@ -34,9 +39,14 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kTile = 64;        // W rows and X rows per workgroup
-constexpr int kGroupK = 64;      // k per load group (4 MFMA k-steps)
-constexpr int kWavesK = 4;       // waves splitting the workgroup's K slice
+constexpr int kTile = 64;        // X rows per W_UK workgroup
+constexpr int kWsWaves = 4;
+constexpr int kWsRows = 16;                     // W rows per wave (MFMA M)
+constexpr int kWsTile = kWsWaves * kWsRows;     // W rows per workgroup
+constexpr int kWsChunkBytes = 16384;            // one LDS buffer of X rows
+constexpr int kWsRing = 8;                      // W k-steps in flight per lane
+constexpr int kWsXAhead = 2;                    // X chunks held in registers
+constexpr int kWsMaxRows = 128;                 // X rows per workgroup at most
 
 __device__ __forceinline__ unsigned cvt2(float lo, float hi) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
@@ -47,131 +57,187 @@ __device__ __forceinline__ bf16x8_t ld8(const bf16_t* p) {
   return *reinterpret_cast<const bf16x8_t*>(p);
 }
 
-// 8 consecutive k of one row as an MFMA operand (fp32 source, rounded to bf16).
-__device__ __forceinline__ bf16x8_t ld8(const float* p) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  const float4 b = *reinterpret_cast<const float4*>(p + 4);
-  const u32x4_t u = {cvt2(a.x, a.y), cvt2(a.z, a.w), cvt2(b.x, b.y), cvt2(b.z, b.w)};
-  return __builtin_bit_cast(bf16x8_t, u);
+// Shape of one k_gemm_ws instance: MB blocks of 16 X rows.
+template <int MB>
+struct WsShape {
+  static constexpr int kRowsX = 16 * MB;
+  static constexpr int kKC = kWsChunkBytes / (2 * kRowsX);   // k per X chunk
+  static constexpr int kSPC = kKC / 32;                       // MFMA k-steps per chunk
+  static constexpr int kUnroll =
+      kSPC * kWsXAhead > kWsRing ? kSPC * kWsXAhead : kWsRing;   // powers of two: the lcm
+  static constexpr int kPitch = 2 * kKC + 16;                 // LDS bytes per X row
+  static constexpr int kVecRow = kKC / 8;                     // 16-byte vectors per row
+  static constexpr int kVecThread = kRowsX * kVecRow / 256;   // per thread per chunk
+  static_assert(kKC >= 32 && kKC % 32 == 0, "chunk");
+  static_assert(kUnroll % (kSPC * kWsXAhead) == 0 && kUnroll % kWsRing == 0, "unroll");
+  static_assert(kVecThread * 256 == kRowsX * kVecRow, "staging");
+};
+
+// k granule of one workgroup's K slice for an instance with MB row blocks
+constexpr int ws_kunit(int mb) {
+  return 32 * (kWsChunkBytes / (1024 * mb) * kWsXAhead > kWsRing
+                   ? kWsChunkBytes / (1024 * mb) * kWsXAhead
+                   : kWsRing);
 }
 
+// 16-row X blocks per workgroup for M rows (larger M takes several M tiles)
+constexpr int ws_mb(int M) {
+  return M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : kWsMaxRows / 16;
+}
+
+// One 16-byte vector of X (8 values), loaded now and stored to LDS as bf16 later.
 template <typename XT>
-__global__ __launch_bounds__(256, 2) void k_gemm_skinny(GemmArgs a, int ntiles, int ksplit,
-                                                        int kslice, float* partial) {
-  __shared__ float red[kWavesK][kTile][kTile + 1];
+struct XVec;
+template <>
+struct XVec<bf16_t> {
+  u32x4_t v;
+  __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const u32x4_t*>(p); }
+  __device__ __forceinline__ u32x4_t bits() const { return v; }
+};
+template <>
+struct XVec<float> {
+  float4 lo, hi;
+  __device__ __forceinline__ void load(const float* p) {
+    lo = *reinterpret_cast<const float4*>(p);
+    hi = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ u32x4_t bits() const {
+    return (u32x4_t){cvt2(lo.x, lo.y), cvt2(lo.z, lo.w), cvt2(hi.x, hi.y), cvt2(hi.z, hi.w)};
+  }
+};
+
+template <typename XT, int MB>
+__global__ __launch_bounds__(256) void k_gemm_ws(GemmArgs a, int ntiles, int ksplit, int kslice,
+                                                 float* partial) {
+  using S = WsShape<MB>;
+  __shared__ __attribute__((aligned(16))) char xs[2][S::kRowsX * S::kPitch];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int r = lane & 31, g = lane >> 5;
+  const int r16 = lane & 15, g = lane >> 4;
   const int zb = blockIdx.x / ntiles, nt = blockIdx.x - zb * ntiles;
-  const int n0 = nt * kTile, ks = blockIdx.y, m0 = blockIdx.z * kTile;
+  const int n0 = nt * kWsTile, ks = blockIdx.y, m0 = blockIdx.z * S::kRowsX;
+  const int nw = n0 + kWsRows * wv;   // first W row of this wave
+  const int64_t kbeg = static_cast<int64_t>(ks) * kslice;
 
-  // W rows n0+r and n0+32+r (the tile never straddles n_split)
-  const bf16_t* wbase = n0 < a.n_split
-                            ? static_cast<const bf16_t*>(a.w1) + zb * a.w_bs +
-                                  static_cast<int64_t>(n0) * a.ldw_n
-                            : static_cast<const bf16_t*>(a.w2) + zb * a.w_bs +
-                                  static_cast<int64_t>(n0 - a.n_split) * a.ldw_n;
-  const bf16_t* wr[2] = {wbase + static_cast<int64_t>(r) * a.ldw_n,
-                         wbase + static_cast<int64_t>(r + 32) * a.ldw_n};
-  // X rows m0+r and m0+32+r; rows past M read row 0 (their products are dropped)
-  const XT* xbase = static_cast<const XT*>(a.x) + zb * a.x_bs;
-  const XT* xr[2];
+  // this lane's W row (the 64-row tile never straddles n_split)
+  const bf16_t* wrow =
+      (n0 < a.n_split ? static_cast<const bf16_t*>(a.w1) + zb * a.w_bs +
+                            static_cast<int64_t>(nw + r16) * a.ldw_n
+                      : static_cast<const bf16_t*>(a.w2) + zb * a.w_bs +
+                            static_cast<int64_t>(nw - a.n_split + r16) * a.ldw_n) +
+      kbeg + 8 * g;
+
+  // X staging: vector v = tid + 256 i covers row v / kVecRow, k 8 (v % kVecRow);
+  // rows past M read row 0 (their outputs are never stored)
+  const XT* xsrc[S::kVecThread];
+  int xoff[S::kVecThread];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int m = m0 + 32 * q + r;
-    xr[q] = xbase + static_cast<int64_t>(m < a.M ? m : 0) * a.ldx_m;
+  for (int i = 0; i < S::kVecThread; ++i) {
+    const int v = tid + 256 * i, row = v / S::kVecRow, kv = v - row * S::kVecRow;
+    const int m = m0 + row;
+    xsrc[i] = static_cast<const XT*>(a.x) + zb * a.x_bs +
+              static_cast<int64_t>(m < a.M ? m : 0) * a.ldx_m + kbeg + 8 * kv;
+    xoff[i] = row * S::kPitch + 16 * kv;
   }
-
-  const int kw = kslice / kWavesK;
-  const int kbeg = ks * kslice + wv * kw;
-  f32x16_t acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-  bf16x8_t wf[2][2][4], xf[2][2][4];   // [buffer][block][step]
-  auto load = [&](int buf, int k) {
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        wf[buf][q][s] = ld8(wr[q] + k + 32 * g + 8 * s);
-        xf[buf][q][s] = ld8(xr[q] + k + 32 * g + 8 * s);
-      }
+  // The workgroup walks its K slice starting at chunk `rot` (wrapping), so at
+  // any moment the workgroups read different X chunks instead of all asking the
+  // same L2 lines for the same chunk.
+  const int nsteps = kslice / 32, nchunks = kslice / S::kKC;
+  const int rot = static_cast<int>(blockIdx.x % static_cast<unsigned>(nchunks));
+  auto wstep = [&](int st) {   // logical step -> step within the slice
+    const int p = st + rot * S::kSPC;
+    return p >= nsteps ? p - nsteps : p;
   };
-  load(0, kbeg);
-  for (int k = kbeg; k < kbeg + kw; k += 2 * kGroupK) {
-    if (k + kGroupK < kbeg + kw) load(1, k + kGroupK);
+  XVec<XT> xv[kWsXAhead][S::kVecThread];
+  auto xload = [&](int set, int c) {
+    const int pc = c + rot >= nchunks ? c + rot - nchunks : c + rot;
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int i = 0; i < S::kVecThread; ++i) xv[set][i].load(xsrc[i] + pc * S::kKC);
+  };
+  auto xstore = [&](int set, int buf) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[0][i][s], xf[0][j][s], acc[i][j],
-                                                              0, 0, 0);
-    if (k + kGroupK >= kbeg + kw) break;
-    if (k + 2 * kGroupK < kbeg + kw) load(0, k + 2 * kGroupK);
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[1][i][s], xf[1][j][s], acc[i][j],
-                                                              0, 0, 0);
-  }
+    for (int i = 0; i < S::kVecThread; ++i)
+      *reinterpret_cast<u32x4_t*>(&xs[buf][xoff[i]]) = xv[set][i].bits();
+  };
 
-  // acc[i][j] lane (x row r, g) holds W rows 32i + 8(e/4) + 4g + (e%4), X row 32j + r
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  f32x4_t acc[MB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MB; ++i) acc[i] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+  bf16x8_t wr[kWsRing];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+  for (int u = 0; u < kWsRing; ++u) wr[u] = ld8(wrow + 32 * wstep(u));
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        red[wv][32 * i + 8 * (e >> 2) + 4 * g + (e & 3)][32 * j + r] = acc[i][j][e];
+  for (int c = 0; c < kWsXAhead; ++c) xload(c, min(c, nchunks - 1));
+  xstore(0, 0);
   __syncthreads();
 
-  // thread -> output pairs (W rows 2p, 2p+1; X row xr) so RoPE pairs stay together
-  for (int p = tid; p < kTile * kTile / 2; p += 256) {
-    const int xrow = p & (kTile - 1), wp = p >> 6;
-    const int m = m0 + xrow;
-    if (m >= a.M) continue;
-    float v0 = 0.f, v1 = 0.f;
+  // B operand of block mb at step u of the chunk in buffer buf
+  const int boff = r16 * S::kPitch + 16 * g;
+  for (int s0 = 0; s0 < nsteps; s0 += S::kUnroll) {
 #pragma unroll
-    for (int w = 0; w < kWavesK; ++w) {
-      v0 += red[w][2 * wp][xrow];
-      v1 += red[w][2 * wp + 1][xrow];
+    for (int u = 0; u < S::kUnroll; ++u) {
+      // s0 is a multiple of kUnroll, so chunk parity and register set are static
+      const int s = s0 + u, cu = u / S::kSPC, su = u % S::kSPC;
+      const int c = s0 / S::kSPC + cu, buf = cu & 1, set = cu % kWsXAhead;
+      // prefetches past the slice re-read its last chunk / step instead of
+      // branching: the body stays branch-free, so every wait is exact
+      if (su == 0) xload(set, min(c + kWsXAhead, nchunks - 1));
+      const bf16x8_t wf = wr[u % kWsRing];
+      wr[u % kWsRing] = ld8(wrow + 32 * wstep(min(s + kWsRing, nsteps - 1)));
+      // keep every load at its own step: the scheduler would otherwise sink the
+      // refills below the products and drain the ring
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8_t xf[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        xf[mb] = *reinterpret_cast<const bf16x8_t*>(&xs[buf][boff + 16 * mb * S::kPitch + 64 * su]);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf[mb], acc[mb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (su == S::kSPC - 1) {
+        xstore((cu + 1) % kWsXAhead, buf ^ 1);   // past the end: a buffer nobody reads
+        __syncthreads();
+      }
     }
-    const int n = n0 + 2 * wp;
+  }
+
+  // acc[mb] lane (r16, g) holds W rows nw + 4g + e (e = 0..3), X row m0 + 16 mb + r16
+  const int n = nw + 4 * g;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int m = m0 + 16 * mb + r16;
+    if (m >= a.M) continue;
     if (ksplit == 1) {
-      gemm_epilogue<bf16_t>(a, zb, m, n, v0, v1);
+      gemm_epilogue<bf16_t>(a, zb, m, n, acc[mb][0], acc[mb][1]);
+      gemm_epilogue<bf16_t>(a, zb, m, n + 2, acc[mb][2], acc[mb][3]);
     } else {
       float* dst = partial + ((static_cast<int64_t>(ks) * a.batch + zb) * a.M + m) * a.N + n;
-      dst[0] = v0;
-      dst[1] = v1;
+      *reinterpret_cast<f32x4_t*>(dst) = acc[mb];
     }
   }
 }
 
-// Sum of the K-split partials (fixed order) followed by the output stage.
+// Sum of the K-split partials (fixed order) followed by the output stage; each
+// thread takes 4 consecutive columns of one output row.
 __global__ __launch_bounds__(256) void k_gemm_finish(GemmArgs a, int ksplit, const float* partial) {
-  const int64_t pairs = static_cast<int64_t>(a.batch) * a.M * (a.N / 2);
-  for (int64_t p = blockIdx.x * int64_t{256} + threadIdx.x; p < pairs;
-       p += int64_t{256} * gridDim.x) {
-    const int np = static_cast<int>(p % (a.N / 2));
-    const int64_t rest = p / (a.N / 2);
-    const int m = static_cast<int>(rest % a.M), zb = static_cast<int>(rest / a.M);
-    const int n = 2 * np;
-    float v0 = 0.f, v1 = 0.f;
-    for (int s = 0; s < ksplit; ++s) {
-      const float* src = partial + ((static_cast<int64_t>(s) * a.batch + zb) * a.M + m) * a.N + n;
-      v0 += src[0];
-      v1 += src[1];
+  const uint32_t quads_row = static_cast<uint32_t>(a.N) / 4;
+  const uint32_t quads = static_cast<uint32_t>(a.batch) * a.M * quads_row;
+  const int64_t plane = static_cast<int64_t>(a.batch) * a.M * a.N;
+  for (uint32_t q = blockIdx.x * 256u + threadIdx.x; q < quads; q += 256u * gridDim.x) {
+    const float* src = partial + static_cast<int64_t>(q) * 4;
+    float4 v = *reinterpret_cast<const float4*>(src);
+    for (int s = 1; s < ksplit; ++s) {
+      const float4 t = *reinterpret_cast<const float4*>(src + s * plane);
+      v.x += t.x; v.y += t.y; v.z += t.z; v.w += t.w;
     }
-    gemm_epilogue<bf16_t>(a, zb, m, n, v0, v1);
+    const uint32_t row = q / quads_row;
+    const int n = static_cast<int>(q - row * quads_row) * 4;
+    const int m = static_cast<int>(row % static_cast<uint32_t>(a.M));
+    const int zb = static_cast<int>(row / static_cast<uint32_t>(a.M));
+    gemm_epilogue<bf16_t>(a, zb, m, n, v.x, v.y);
+    gemm_epilogue<bf16_t>(a, zb, m, n + 2, v.z, v.w);
   }
 }
 
@@ -238,25 +304,55 @@ __global__ __launch_bounds__(256) void k_gemm_uk(GemmArgs a) {
   }
 }
 
-int divisor_plan(int tiles, int k_groups) {
-  // smallest divisor d of k_groups with tiles*d >= 1024 workgroups (else the largest)
-  int best = 1;
-  for (int d = 1; d <= k_groups; ++d) {
-    if (k_groups % d) continue;
-    best = d;
-    if (static_cast<int64_t>(tiles) * d >= 1024) break;
+constexpr int kWsMinGroups = 512;   // workgroups wanted before K is split further
+
+struct WsPlan {
+  int mb, mtiles, ntiles, d;
+};
+
+WsPlan ws_plan(const GemmArgs& a) {
+  WsPlan p{};
+  p.mb = ws_mb(a.M);
+  p.mtiles = (a.M + 16 * p.mb - 1) / (16 * p.mb);
+  p.ntiles = a.N / kWsTile;
+  const int64_t tiles = static_cast<int64_t>(a.batch) * p.ntiles * p.mtiles;
+  const int groups = a.K / ws_kunit(p.mb);
+  // smallest divisor of the K granules that reaches the workgroup target
+  p.d = 1;
+  for (int d = 1; d <= groups; ++d) {
+    if (groups % d) continue;
+    p.d = d;
+    if (tiles * d >= kWsMinGroups) break;
   }
-  return best;
+  return p;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+template <typename XT>
+void launch_ws(const GemmArgs& a, const WsPlan& p, float* partial, hipStream_t stream) {
+  const dim3 grid(a.batch * p.ntiles, p.d, p.mtiles);
+  const int kslice = a.K / p.d;
+  switch (p.mb) {
+    case 1: hipLaunchKernelGGL((k_gemm_ws<XT, 1>), grid, dim3(256), 0, stream, a, p.ntiles, p.d, kslice, partial); break;
+    case 2: hipLaunchKernelGGL((k_gemm_ws<XT, 2>), grid, dim3(256), 0, stream, a, p.ntiles, p.d, kslice, partial); break;
+    case 4: hipLaunchKernelGGL((k_gemm_ws<XT, 4>), grid, dim3(256), 0, stream, a, p.ntiles, p.d, kslice, partial); break;
+    default: hipLaunchKernelGGL((k_gemm_ws<XT, 8>), grid, dim3(256), 0, stream, a, p.ntiles, p.d, kslice, partial); break;
+  }
 }
 
 }  // namespace
 
-// NT form: W K-contiguous, X K-contiguous, bf16 weights, tiles of 64 that do not
-// straddle the W1/W2 boundary, K a multiple of 256.
-static bool skinny_ok(const GemmArgs& a) {
-  return a.ldw_k == 1 && a.ldx_k == 1 && a.N % kTile == 0 && a.n_split % kTile == 0 &&
-         a.K % (kGroupK * kWavesK) == 0 && a.K > 0 && a.M > 0 && a.ldw_n % 8 == 0 &&
-         a.ldx_m % 8 == 0 && a.x_bs % 8 == 0 && a.w_bs % 8 == 0;
+// NT form: W and X K-contiguous, 16-byte aligned rows, 64-row W tiles that do
+// not straddle the W1/W2 boundary, K a multiple of the instance's k granule.
+static bool ws_ok(const GemmArgs& a) {
+  if (!(a.ldw_k == 1 && a.ldx_k == 1 && a.K > 0 && a.M > 0 && a.N > 0 && a.batch > 0 &&
+        a.N % kWsTile == 0 && (a.n_split % kWsTile == 0 || a.n_split >= a.N) &&
+        a.ldw_n % 8 == 0 && a.ldx_m % 8 == 0 && a.x_bs % 8 == 0 && a.w_bs % 8 == 0 &&
+        aligned16(a.x) && aligned16(a.w1) && aligned16(a.w2)))
+    return false;
+  if (static_cast<int64_t>(a.batch) * a.M * a.N >= (int64_t{1} << 31)) return false;
+  return a.K % ws_kunit(ws_mb(a.M)) == 0;
 }
 
 // The per-head W_UK form: W is [K=128, N] N-contiguous, output fp32.
@@ -266,41 +362,36 @@ static bool uk_ok(const GemmArgs& a) {
          a.w1 == a.w2 && a.n_split >= a.N;
 }
 
-bool fast_gemm_ok(const GemmArgs& a) { return skinny_ok(a) || uk_ok(a); }
+bool fast_gemm_ok(const GemmArgs& a) { return ws_ok(a) || uk_ok(a); }
 
 size_t gemm_partial_bytes(const GemmArgs& a) {
-  if (!skinny_ok(a)) return 0;
-  const int tiles = a.batch * (a.N / kTile) * ((a.M + kTile - 1) / kTile);
-  const int d = divisor_plan(tiles, a.K / (kGroupK * kWavesK));
-  return d > 1 ? static_cast<size_t>(d) * a.batch * a.M * a.N * sizeof(float) : 0;
+  if (!ws_ok(a)) return 0;
+  const WsPlan p = ws_plan(a);
+  return p.d > 1 ? static_cast<size_t>(p.d) * a.batch * a.M * a.N * sizeof(float) : 0;
 }
 
 hipError_t launch_gemm_fast(const GemmArgs& a, void* partial, size_t partial_bytes,
                             hipStream_t stream) {
   if (a.M == 0 || a.N == 0 || a.batch == 0) return hipSuccess;
-  if (uk_ok(a) && !skinny_ok(a)) {
+  if (!ws_ok(a)) {
+    if (!uk_ok(a)) return hipErrorInvalidValue;
     dim3 grid(a.batch, a.N / kUkN, (a.M + kTile - 1) / kTile);
     hipLaunchKernelGGL(k_gemm_uk, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
   }
-  const int ntiles = a.N / kTile;
-  const int mtiles = (a.M + kTile - 1) / kTile;
-  const int d = divisor_plan(a.batch * ntiles * mtiles, a.K / (kGroupK * kWavesK));
-  if (d > 1 && (partial == nullptr || partial_bytes < gemm_partial_bytes(a)))
+  const WsPlan p = ws_plan(a);
+  if (p.d > 1 && (partial == nullptr || !aligned16(partial) ||
+                  partial_bytes < gemm_partial_bytes(a)))
     return hipErrorInvalidValue;
-  dim3 grid(a.batch * ntiles, d, mtiles);
-  const int kslice = a.K / d;
   if (a.x_f32)
-    hipLaunchKernelGGL(k_gemm_skinny<float>, grid, dim3(256), 0, stream, a, ntiles, d, kslice,
-                       static_cast<float*>(partial));
+    launch_ws<float>(a, p, static_cast<float*>(partial), stream);
   else
-    hipLaunchKernelGGL(k_gemm_skinny<bf16_t>, grid, dim3(256), 0, stream, a, ntiles, d, kslice,
-                       static_cast<float*>(partial));
+    launch_ws<bf16_t>(a, p, static_cast<float*>(partial), stream);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || d == 1) return e;
-  const int64_t pairs = static_cast<int64_t>(a.batch) * a.M * (a.N / 2);
-  const int blocks = static_cast<int>(std::min<int64_t>((pairs + 255) / 256, 8192));
-  hipLaunchKernelGGL(k_gemm_finish, dim3(blocks), dim3(256), 0, stream, a, d,
+  if (e != hipSuccess || p.d == 1) return e;
+  const int64_t quads = static_cast<int64_t>(a.batch) * a.M * (a.N / 4);
+  const int blocks = static_cast<int>(std::min<int64_t>((quads + 255) / 256, 8192));
+  hipLaunchKernelGGL(k_gemm_finish, dim3(blocks), dim3(256), 0, stream, a, p.d,
                      static_cast<const float*>(partial));
   return hipGetLastError();
 }

@@ -132,6 +132,8 @@ mla::GemmArgs append_args(const mla_dims* d, int n_rows) {
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
+bool ws_aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255) == 0; }
+
 // Bytes of the activation region (q^C or the per-head outputs o) at the front
 // of the workspace.
 size_t act_bytes(const mla_dims* d, int batch) {
@@ -219,7 +221,7 @@ mla_status mla_append_latent(const mla_dims* d, const void* h, const void* w_dkv
   if (!h || !w_dkv || !w_kr || !row_seq || !row_pos || !block_table || !pool) return MLA_ERR_NULL;
   mla::GemmArgs a = append_args(d, n_rows);
   const size_t need = partial_bytes(d, a);
-  if (need > 0 && (!ws || ws_bytes < need)) return MLA_ERR_WORKSPACE;
+  if (need > 0 && (!ws || ws_bytes < need || !ws_aligned(ws))) return MLA_ERR_WORKSPACE;
   int* err = err_word();
   if (!err) return MLA_ERR_HIP;
   a.x = h; a.w1 = w_dkv; a.w2 = w_kr; a.y = pool;
@@ -237,7 +239,7 @@ mla_status mla_absorb_q(const mla_dims* d, const void* h, const void* w_q, const
   if (batch < 0 || batch > (1 << 20)) return MLA_ERR_SHAPE;
   if (batch == 0) return MLA_OK;
   if (!h || !w_q || !w_qr || !w_uk || !pos || !q_lat || !q_pe) return MLA_ERR_NULL;
-  if (!ws || ws_bytes < mla_workspace_bytes(d, batch)) return MLA_ERR_WORKSPACE;
+  if (!ws || ws_bytes < mla_workspace_bytes(d, batch) || !ws_aligned(ws)) return MLA_ERR_WORKSPACE;
   char* part = static_cast<char*>(ws) + act_bytes(d, batch);
   const size_t pbytes = ws_bytes - act_bytes(d, batch);
   // 1) [q^C | q^R] = h [W_Q; W_QR]^T, RoPE on the q^R columns; q^C -> workspace
@@ -301,7 +303,7 @@ mla_status mla_absorb_out(const mla_dims* d, const float* o_lat, const void* w_u
   if (batch < 0 || batch > (1 << 20)) return MLA_ERR_SHAPE;
   if (batch == 0) return MLA_OK;
   if (!o_lat || !w_uv || !w_o || !u) return MLA_ERR_NULL;
-  if (!ws || ws_bytes < mla_workspace_bytes(d, batch)) return MLA_ERR_WORKSPACE;
+  if (!ws || ws_bytes < mla_workspace_bytes(d, batch) || !ws_aligned(ws)) return MLA_ERR_WORKSPACE;
   char* part = static_cast<char*>(ws) + act_bytes(d, batch);
   const size_t pbytes = ws_bytes - act_bytes(d, batch);
   // 1) o[b, i*d_h + e] = sum_c W_UV[i*d_h + e, c] o_lat[b, i, c] per head i -> workspace

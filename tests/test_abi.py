@@ -106,6 +106,10 @@ def test_argument_checks():
     assert lib.mla_absorb_q(ctypes.byref(d), P, P, P, P, P, 4, P, P, None, 1 << 20, None) == -4
     assert lib.mla_absorb_q(ctypes.byref(d), P, P, P, P, P, 4, P, P, P, 16, None) == -4
     assert lib.mla_absorb_out(ctypes.byref(d), P, P, P, 4, P, P, 16, None) == -4
+    misaligned = ctypes.c_void_p(0x1008)
+    assert lib.mla_absorb_q(ctypes.byref(d), P, P, P, P, P, 4, P, P, misaligned, 1 << 20,
+                            None) == -4
+    assert lib.mla_absorb_out(ctypes.byref(d), P, P, P, 4, P, misaligned, 1 << 20, None) == -4
     # empty batches are no-ops that never touch the pointers
     assert lib.mla_absorb_q(ctypes.byref(d), None, None, None, None, None, 0, None, None, None, 0,
                             None) == 0

@@ -4,32 +4,37 @@
 // ([Report] §2.3/§2.4 of "《DeepSeek-V2》深度解读报告": every head scores the
 // same cached latent rows [c | k^R]; s = tau (q_lat . c + q_pe . k^R)).
 //
-// Work unit = (sequence b, split s).  A 256-thread workgroup (4 waves) streams
-// the split's rows in tiles of 32 tokens (32 rows x 1152 bytes, contiguous
-// inside one 64-row page) through a 3-slot LDS ring filled by asynchronous
-// global->LDS copies (global_load_lds_dwordx4), two tiles ahead of the one
-// consumed.  Wave w owns heads 32w..32w+31:
-//   scores  S^T[t, h] = sum_k C[t, k] Q[h, k]   (M = 32 tokens, N = 32 heads,
-//           K = 576, 36 x mfma_f32_32x32x16_bf16; A = tile rows from LDS,
-//           B = the wave's queries: 27 k-steps in VGPRs, 9 in LDS)
-//   softmax per head in the exp2 domain, in-lane plus one cross-half
-//           max/sum.  The exponent reference of each head is fixed at the
-//           maximum of its first scored tile, so the accumulator is never
-//           rescaled and stays in AGPRs; later scores may exceed it by up to
-//           2^64 (no fp32/bf16 overflow).  A score beyond that headroom makes
-//           the whole unit run again with the larger reference (at most once).
-//   P.C     O[h, d] += sum_t P[h, t] C[t, d]   (M = 32 heads, N = 512 in 16
-//           blocks, K = 32 tokens); the S^T accumulator registers are, after
-//           conversion to bf16, exactly the A operand of this product, and the
-//           B operand is read from the same tile with ds_read_b64_tr_b16
-//           (hardware transpose), so no second copy exists.
-// LDS tile layout: 4 row groups x 9 chunk groups of 1 KB blocks; a block holds
-// 8 rows x 8 16-byte chunks (128 bytes per row), chunk c of row r stored at
-// chunk c ^ key(r), key(r) = 2(r&3) + (r>>2).  One wave-wide copy fills one
-// block, so every lane's global source offset is a per-lane constant, and both
-// the row reads of the score product (8 rows, one chunk) and the transposed
-// reads of the P.C product (4 rows, chunk pairs) hit distinct banks.  Row
-// groups are padded by 128 bytes so consecutive groups alternate bank halves.
+// Work unit = (sequence b, split s).  A 512-thread workgroup (8 waves, two per
+// SIMD so that one wave's softmax and LDS waits hide behind the other's matrix
+// products) streams the split's rows in tiles of 32 tokens (32 rows x 1152
+// bytes, contiguous inside one 64-row page) through a 3-slot LDS ring filled by
+// asynchronous global->LDS copies (global_load_lds_dwordx4), two tiles ahead
+// of the one consumed.  Wave w owns heads 16w..16w+15 (mfma_f32_16x16x32_bf16):
+//   scores  S^T[t, h] = sum_k C[t, k] Q[h, k]   (M = 16 tokens, two blocks;
+//           N = 16 heads; K = 576 in 18 steps; A = tile rows from LDS, B = the
+//           wave's queries: 14 k-steps in VGPRs, 4 in LDS, for the whole unit)
+//   softmax per head in the exp2 domain: in-lane over 8 tokens plus two
+//           cross-lane steps.  The exponent reference of each head is fixed at
+//           the maximum of its first scored tile, so the accumulator is never
+//           rescaled; later scores may exceed it by up to 2^64 (no fp32/bf16
+//           overflow).  A score beyond that headroom makes the whole unit run
+//           again with the larger reference (at most once).
+//   P.C     O[h, d] += sum_t P[h, t] C[t, d]   (M = 16 heads, N = 512 in 32
+//           blocks, K = 32 tokens).  The score accumulator of a lane holds one
+//           head and tokens 16 tb + 4 g + i; taking the contraction's k order
+//           as t(g, j) = 16 (j >> 2) + 4 g + (j & 3) makes the packed
+//           probabilities exactly the A operand, and the B operand (4 tokens
+//           of one column per half) is one ds_read_b64_tr_b16 (hardware
+//           transpose) per half from the same tile.
+// LDS tile layout (36 KB): the 512 latent values of row r fill one 1 KB block
+// (block r), chunk c (16 bytes) stored at c ^ 2(r & 7); the 64 RoPE values of
+// rows 8j..8j+7 fill block 32 + j, row r at 128 (r & 7), chunk c' at
+// c' ^ (r & 7).  Every copy fills one block.  LDS has 64 banks of 4 bytes; a
+// ds_read_b128 is served in four 16-lane phases, the lanes of a phase being
+// those with equal lane >> 5 and equal parity of bits 2..4 of the lane, and a
+// ds_read_b64(_tr_b16) in two 32-lane phases (lane >> 5).  Under this layout
+// no phase of a score read (16 rows, one chunk per lane group) or of a
+// transposed read (8 rows, a chunk pair) puts two addresses on one bank.
 #include "common.hpp"
 #include "launch_fast.hpp"
 
@@ -39,7 +44,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8;
@@ -47,22 +52,21 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
 
 constexpr int kDc = 512, kDr = 64, kPage = 64;
 constexpr int kTileTok = 32;
-constexpr int kRowBytes = (kDc + kDr) * 2;            // 1152
-constexpr int kChunkGroups = kRowBytes / 128;         // 9
-constexpr int kBlockBytes = 1024;                     // 8 rows x 128 bytes
-constexpr int kRowGroupBytes = kChunkGroups * kBlockBytes + 128;  // 9344
-constexpr int kTileBytes = 4 * kRowGroupBytes;        // 37376
-constexpr int kThreads = 256, kWaves = 4;
-constexpr int kBlocksPerTile = 4 * kChunkGroups;      // 36
-constexpr int kDmaPerWave = kBlocksPerTile / kWaves;  // 9 copies per wave per tile
-constexpr int kKSteps = (kDc + kDr) / 16;             // 36
-constexpr int kQReg = 27;                             // k-steps of Q held in VGPRs
-constexpr int kQLds = kKSteps - kQReg;                // k-steps of Q held in LDS
+constexpr int kRowBytes = (kDc + kDr) * 2;            // 1152: one cached row
+constexpr int kRopeOff = kTileTok * 1024;             // RoPE blocks follow the 32 latent blocks
+constexpr int kTileBytes = kRopeOff + (kTileTok / 8) * 1024;   // 36864
+constexpr int kThreads = 512, kWaves = 8;
+constexpr int kKSteps = (kDc + kDr) / 32;             // 18
+constexpr int kColBlocks = kDc / 16;                  // 32
 constexpr int kStages = 3;                            // LDS ring depth
+constexpr int kQReg = 14;                             // k-steps of Q held in VGPRs
+constexpr int kQLds = kKSteps - kQReg;                // k-steps of Q held in LDS
+constexpr int kPageWin = 2048;                        // page ids of the split held in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kHeadroom = 64.0f;                    // log2 units above the reference
 
-__device__ __forceinline__ int rkey(int r8) { return 2 * (r8 & 3) + (r8 >> 2); }
+__device__ __forceinline__ int ukey(int r) { return 2 * (r & 7); }
+__device__ __forceinline__ int vkey(int r) { return r & 7; }
 
 __device__ __forceinline__ unsigned cvt2(float lo, float hi) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
@@ -146,32 +150,40 @@ __device__ __forceinline__ void dma_block(uint64_t gbase, uint32_t voff, uint32_
 }
 
 // Start the asynchronous copy of the tile at `tok0` (32 rows of one page) into
-// the ring slot at LDS address `slot`.  Wave wv copies blocks wv, wv+4, ...;
-// `voff` is the lane's source offset inside a block of a full tile.  In a
-// partial tile, rows past the split's end re-read row 0 (finite data whose
-// score is masked); a page outside the pool reads pool row 0 (and is flagged).
+// the ring slot at LDS address `slot`.  Wave wv copies latent rows 4wv..4wv+3
+// and, for wv < 4, RoPE block wv (5 or 4 copies).  In a partial tile, rows past
+// the split's end re-read row 0 (finite data whose score is masked); a page
+// outside the pool reads pool row 0 (and is flagged).
 __device__ __forceinline__ void tile_issue(const char* __restrict__ pool, int page, bool ok,
-                                           int tok0, int t1, uint32_t slot, int wv, int lane,
-                                           uint32_t voff) {
+                                           int tok0, int t1, uint32_t slot, int wv, int lane) {
   const int nvalid = ok ? min(kTileTok, t1 - tok0) : 0;
   const uint64_t tile = reinterpret_cast<uint64_t>(
       ok ? pool + (static_cast<int64_t>(page) * kPage + (tok0 & (kPage - 1))) * kRowBytes : pool);
-  if (nvalid == kTileTok) {
 #pragma unroll
-    for (int r = 0; r < kDmaPerWave; ++r) {
-      const int bi = r * kWaves + wv, rg = bi / kChunkGroups, cg = bi - rg * kChunkGroups;
-      dma_block(tile + rg * 8 * kRowBytes + cg * 128, voff,
-                slot + rg * kRowGroupBytes + cg * kBlockBytes);
-    }
+  for (int q = 0; q < 4; ++q) {
+    const int r = 4 * wv + q;
+    dma_block(tile + (r < nvalid ? r : 0) * kRowBytes, 16 * (lane ^ ukey(r)), slot + 1024 * r);
+  }
+  if (wv < 4) {
+    const int rr = 8 * wv + (lane >> 3);
+    const uint32_t voff =
+        (rr < nvalid ? rr : 0) * kRowBytes + 2 * kDc + 16 * ((lane & 7) ^ vkey(rr));
+    dma_block(tile, voff, slot + kRopeOff + 1024 * wv);
+  }
+}
+
+// Wait until this wave's copies of the current tile have landed, `after` tiles
+// (0..kStages-2) having been issued since; waves 0..3 issue 5 copies per tile,
+// waves 4..7 issue 4.
+__device__ __forceinline__ void wait_tile(int after, bool five) {
+  if (after >= 3) {
+    if (five) wait_vmcnt<15>(); else wait_vmcnt<12>();
+  } else if (after == 2) {
+    if (five) wait_vmcnt<10>(); else wait_vmcnt<8>();
+  } else if (after == 1) {
+    if (five) wait_vmcnt<5>(); else wait_vmcnt<4>();
   } else {
-    const int r8 = lane >> 3, c8 = (lane & 7) ^ rkey(lane >> 3);
-#pragma unroll
-    for (int r = 0; r < kDmaPerWave; ++r) {
-      const int bi = r * kWaves + wv, rg = bi / kChunkGroups, cg = bi - rg * kChunkGroups;
-      const int row = rg * 8 + r8;
-      const uint32_t off = (row < nvalid ? row : 0) * kRowBytes + (cg * 8 + c8) * 16;
-      dma_block(tile, off, slot + rg * kRowGroupBytes + cg * kBlockBytes);
-    }
+    wait_vmcnt<0>();
   }
 }
 
@@ -179,13 +191,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
     AttnArgs a, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     const char* __restrict__ pool) {
   __shared__ __attribute__((aligned(1024))) char ring[kStages * kTileBytes];
+  __shared__ __attribute__((aligned(16))) float xch[kWaves][16];
   // k-steps kQReg.. of every wave's Q fragments: [wave][k-step][lane] x 16 B
   __shared__ __attribute__((aligned(16))) bf16x8_t qlds[kWaves][kQLds][64];
-  __shared__ __attribute__((aligned(16))) float xch[kWaves][32];
+  // page ids of the split's pages [wbase, wbase + kPageWin): a copy in LDS, so
+  // a tile's page costs a short LDS read instead of a scalar memory load whose
+  // wait would also block every LDS wait behind it
+  __shared__ int pwin[kPageWin];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int g = lane >> 5;            // k-group of the MFMA operands
-  const int hl = lane & 31;           // head (score N index / P.C M index) of this lane
+  const int g = lane >> 4;            // k-group of the MFMA operands
+  const int n16 = lane & 15;          // head (scores) / column (P.C output) of this lane
   const int S = a.num_splits;
   const int unit = unit_of(blockIdx.x, a.batch * S);
   const int b = unit / S, s = unit - b * S;
@@ -199,181 +215,192 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
   int t0, t1;
   split_range(L, S, s, kPage, &t0, &t1);
 
-  const int64_t ob = (static_cast<int64_t>(b) * S + s) * nh + 32 * wv;
+  const int64_t ob = (static_cast<int64_t>(b) * S + s) * nh + 16 * wv;
   float* o_out = a.o_part + ob * kDc;
   float* lse_out = a.lse_part + ob;
 
   if (t0 >= t1) {  // empty split (uniform across the workgroup)
-    for (int e = lane; e < 32 * kDc; e += 64) o_out[e] = 0.f;
-    if (lane < 32) lse_out[lane] = -INFINITY;
+    for (int e = lane; e < 16 * kDc; e += 64) o_out[e] = 0.f;
+    if (lane < 16) lse_out[lane] = -INFINITY;
     return;
   }
   const int32_t* bt = block_table + static_cast<int64_t>(b) * a.max_pages;
+  const int p_first = t0 / kPage, p_end = (t1 - 1) / kPage + 1;
+  int wbase = -1;
+  // (uniform) make pwin hold pages [base, base + kPageWin); drains every copy
+  auto load_window = [&](int base) {
+    wait_vmcnt<0>();
+    lds_barrier();                       // nobody still reads the old window
+    for (int i = tid; i < kPageWin; i += kThreads) {
+      const int pg = base + i;
+      pwin[i] = pg < p_end ? bt[pg] : 0;
+    }
+    __syncthreads();
+    wbase = base;
+  };
 
-  // ---- this wave's queries as MFMA B fragments: head hl, k = 16kk + 8g + j
+  // ---- this wave's queries as MFMA B fragments: head 16wv + n16, k = 32ks + 8g + j
   bf16x8_t qf[kQReg];
   {
-    const int h = 32 * wv + hl;
+    const int h = 16 * wv + n16;
     const float* ql = a.q_lat + (static_cast<int64_t>(b) * nh + h) * kDc + 8 * g;
     const float* qp = a.q_pe + (static_cast<int64_t>(b) * nh + h) * kDr + 8 * g;
 #pragma unroll
-    for (int kk = 0; kk < kKSteps; ++kk) {
-      const float* src = kk < kDc / 16 ? ql + 16 * kk : qp + 16 * (kk - kDc / 16);
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      const float* src = ks < kDc / 32 ? ql + 32 * ks : qp + 32 * (ks - kDc / 32);
       float v[8];
       const float4 lo = *reinterpret_cast<const float4*>(src);
       const float4 hi = *reinterpret_cast<const float4*>(src + 4);
       v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
       v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
-      if (kk < kQReg) qf[kk] = pack8(v);
-      else qlds[wv][kk - kQReg][lane] = pack8(v);
+      if (ks < kQReg) qf[ks] = pack8(v);
+      else qlds[wv][ks - kQReg][lane] = pack8(v);
     }
   }
   const uint32_t qtail = lds_addr(&qlds[wv][0][lane]);
 
   // ---- per-lane constant offsets inside a tile
-  // copy: lane l of a block moves row l>>3, logical chunk (l&7)^key(l>>3)
-  const uint32_t voff = (lane >> 3) * kRowBytes + (((lane & 7) ^ rkey(lane >> 3)) << 4);
-  // score A fragment: row trow, chunk 2kk+g -> soff[kk&3] + 1024*(kk>>2)
-  const int trow = lane & 31, tr8 = trow & 7;
-  uint32_t soff[4];
+  // score A fragment, token row 16tb + n16, latent chunk 4ks + g:
+  //   soff[ks & 3] + 256 (ks >> 2) + 16384 tb; RoPE chunk 4(ks-16) + g: roff[ks-16] + 2048 tb
+  const int u = ukey(n16), v = vkey(n16);
+  uint32_t soff[4], roff[2];
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    soff[q] = (trow >> 3) * kRowGroupBytes + tr8 * 128 + (((2 * q + g) ^ rkey(tr8)) << 4);
-  // P.C B fragment (transposed read): rows 16mi+8h+r8, chunk 4nb+2(G&1)+((i16&3)>>1)
-  //   -> toff[nb&1] + kRowGroupBytes*(2mi+h) + 1024*(nb>>1)
-  const int i16 = lane & 15, G = lane >> 4;
-  const int r8t = 4 * (G >> 1) + (i16 >> 2);
-  uint32_t toff[2];
+  for (int q = 0; q < 4; ++q) soff[q] = 1024 * n16 + 16 * ((4 * q + g) ^ u);
 #pragma unroll
   for (int q = 0; q < 2; ++q)
-    toff[q] = r8t * 128 + (((4 * q + 2 * (G & 1) + ((i16 & 3) >> 1)) ^ rkey(r8t)) << 4) +
-              8 * (i16 & 1);
+    roff[q] = kRopeOff + 1024 * (n16 >> 3) + 128 * (n16 & 7) + 16 * ((4 * q + g) ^ v);
+  // P.C B fragment, transposed read: this lane addresses token row rt (+16 for
+  // the second half) and columns 16nb + 4(n16 & 3)..+3: toff[nb & 7] + 256 (nb >> 3)
+  const int rt = 4 * g + (n16 >> 2);
+  const int wt = ((n16 & 3) >> 1) ^ ukey(rt);
+  uint32_t toff[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) toff[m] = 1024 * rt + 16 * ((2 * m) ^ wt) + 8 * (n16 & 1);
   const uint32_t ring0 = lds_addr(ring);
+  const bool five = wv < 4;
 
-  f32x16_t o[kDc / 32];
-  float m_ref = -INFINITY;   // exponent reference (log2 units) of head hl
-  float l_sum = 0.f;         // sum of exp2(x - m_ref) of head hl
+  f32x4_t o[kColBlocks];
+  float m_ref = -INFINITY;   // exponent reference (log2 units) of head n16
+  float l_sum = 0.f;         // sum of exp2(x - m_ref) of head n16
   const float cs = a.scale * kLog2e;
   bool bad_page = false;
   const int ntiles = (t1 - t0 + kTileTok - 1) / kTileTok;
 
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int nb = 0; nb < kDc / 32; ++nb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[nb][i] = 0.f;
+    for (int nb = 0; nb < kColBlocks; ++nb) o[nb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
     l_sum = 0.f;
     float seen = m_ref;        // largest tile maximum met in this pass
     bool over = false;
 
+    if (wbase != p_first) load_window(p_first);
     for (int j = 0; j < kStages - 1 && j < ntiles; ++j) {
       const int tok = t0 + j * kTileTok;
-      const int pg = bt[tok / kPage];
-      tile_issue(pool, pg, pg >= 0 && pg < a.num_pages, tok, t1, ring0 + j * kTileBytes, wv, lane,
-                 voff);
+      const int pg = pwin[tok / kPage - wbase];
+      tile_issue(pool, pg, pg >= 0 && pg < a.num_pages, tok, t1, ring0 + j * kTileBytes, wv, lane);
     }
 
-    uint32_t cur = 0;                                  // slot offset of tile `it`
+    int cur = 0;                                       // slot of tile `it`
     for (int it = 0; it < ntiles; ++it) {
       const int tok0 = t0 + it * kTileTok;
-      // copies issued after tile `it`: tile it+1 (if any)
-      if (it + 1 < ntiles) wait_vmcnt<kDmaPerWave>();
-      else wait_vmcnt<0>();
+      wait_tile(min(ntiles - 1 - it, kStages - 2), five);
       lds_barrier();   // tile `it` is in LDS for every wave; the slot of tile it-1 is free
-      const uint32_t nxt = cur == 0 ? (kStages - 1) * kTileBytes : cur - kTileBytes;
-      if (it + kStages - 1 < ntiles) {
-        const int tok = tok0 + (kStages - 1) * kTileTok;
-        const int pg = bt[tok / kPage];
-        tile_issue(pool, pg, pg >= 0 && pg < a.num_pages, tok, t1, ring0 + nxt, wv, lane, voff);
-      }
-      const int page = bt[tok0 / kPage];
+      const int page = pwin[tok0 / kPage - wbase];
       const bool ok = page >= 0 && page < a.num_pages;
       bad_page |= !ok;
       const int nvalid = ok ? min(kTileTok, t1 - tok0) : 0;
-      const uint32_t T = ring0 + cur;
-      cur = cur == (kStages - 1) * kTileBytes ? 0 : cur + kTileBytes;
+      if (it + kStages - 1 < ntiles) {
+        const int tok = tok0 + (kStages - 1) * kTileTok;
+        if (tok / kPage - wbase >= kPageWin) load_window(tok / kPage);   // splits > 2048 pages
+        const int pg = pwin[tok / kPage - wbase];
+        const int nxt = cur == 0 ? kStages - 1 : cur - 1;
+        tile_issue(pool, pg, pg >= 0 && pg < a.num_pages, tok, t1, ring0 + nxt * kTileBytes, wv,
+                   lane);
+      }
+      const uint32_t T = ring0 + cur * kTileBytes;
+      cur = cur == kStages - 1 ? 0 : cur + 1;
 
-      // ---- scores S^T (tokens x heads)
-      uint32_t sa[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) sa[q] = opaque(T + soff[q]);
-      f32x16_t sc;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sc[i] = 0.f;
+      // ---- scores S^T (tokens x heads): two 16-token blocks, independent chains
+      f32x4_t sc[2] = {(f32x4_t){0.f, 0.f, 0.f, 0.f}, (f32x4_t){0.f, 0.f, 0.f, 0.f}};
       {
-        bf16x8_t af[2][4];
+        uint32_t sa[4], ra[2];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) af[0][q] = lds_b128(sa[q]);
+        for (int q = 0; q < 4; ++q) sa[q] = opaque(T + soff[q]);
 #pragma unroll
-        for (int grp = 0; grp < kKSteps / 4; ++grp) {
-          if (grp + 1 < kKSteps / 4) {
+        for (int q = 0; q < 2; ++q) ra[q] = opaque(T + roff[q]);
+        auto lda = [&](int ks, int tb) {
+          return ks < kDc / 32 ? lds_b128(sa[ks & 3] + 256 * (ks >> 2) + 16384 * tb)
+                               : lds_b128(ra[ks - kDc / 32] + 2048 * tb);
+        };
+        // operands of step ks: A for both token blocks and, past kQReg, B from LDS
+        bf16x8_t af[2][3];
+        auto ld_step = [&](int ks, bf16x8_t (&dst)[3]) {
+          dst[0] = lda(ks, 0);
+          dst[1] = lda(ks, 1);
+          if (ks >= kQReg) dst[2] = lds_b128(qtail + (ks - kQReg) * 1024);
+        };
+        ld_step(0, af[0]);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) af[(grp + 1) & 1][q] = lds_b128(sa[q] + 1024 * (grp + 1));
-          }
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int kk = 4 * grp + q;
-            const bf16x8_t qb = kk < kQReg ? qf[kk < kQReg ? kk : 0]
-                                           : lds_b128(qtail + (kk - kQReg) * 1024);
-            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[grp & 1][q], qb, sc, 0, 0, 0);
-          }
-          __builtin_amdgcn_sched_barrier(0);
+        for (int ks = 0; ks < kKSteps; ++ks) {
+          if (ks + 1 < kKSteps) ld_step(ks + 1, af[(ks + 1) & 1]);
+          const bf16x8_t qb = ks < kQReg ? qf[ks < kQReg ? ks : 0] : af[ks & 1][2];
+          sc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks & 1][0], qb, sc[0], 0, 0, 0);
+          sc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks & 1][1], qb, sc[1], 0, 0, 0);
         }
       }
 
-      // ---- softmax weights of head hl for the tile's tokens 8(i/4)+4g+(i%4)
+      // ---- softmax weights of head n16 for tokens 16tb + 4g + i
       if (nvalid < kTileTok) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int tok = 8 * (i >> 2) + 4 * g + (i & 3);
-          if (tok >= nvalid) sc[i] = -INFINITY;
-        }
-      }
-      float tmax = sc[0];
+        for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-      for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, sc[i]);
+          for (int i = 0; i < 4; ++i)
+            if (16 * tb + 4 * g + i >= nvalid) sc[tb][i] = -INFINITY;
+      }
+      float tmax = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                         fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * cs;
       if (m_ref == -INFINITY) m_ref = tmax;      // first scored tile fixes the reference
       seen = fmaxf(seen, tmax);
       over |= tmax > m_ref + kHeadroom;
       const float mr = fmaxf(m_ref, -1e30f);
+      float pv[8];
       float psum = 0.f;
-      float pv[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        pv[i] = __builtin_amdgcn_exp2f(fminf(fmaf(sc[i], cs, -mr), kHeadroom));
-        psum += pv[i];
-      }
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pv[4 * tb + i] = __builtin_amdgcn_exp2f(fminf(fmaf(sc[tb][i], cs, -mr), kHeadroom));
+          psum += pv[4 * tb + i];
+        }
+      psum += __shfl_xor(psum, 16, 64);
       psum += __shfl_xor(psum, 32, 64);
       l_sum += psum;
-      const bf16x8_t pp[2] = {pack8(pv), pack8(pv + 8)};   // tokens 0..15 / 16..31
+      const bf16x8_t pp = pack8(pv);   // k order t(g, j) = 16(j >> 2) + 4g + (j & 3)
 
-      // ---- O += P . C  (B operand via transposed LDS reads), four MFMAs ahead
+      // ---- O += P . C  (B operand via transposed LDS reads), four products ahead
       {
-        uint32_t ta[2];
+        s16x4_t bv[2][2][2];
+        auto load_grp = [&](int grp, s16x4_t (&dst)[2][2]) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) ta[q] = opaque(T + toff[q]);
-        s16x4_t bv[2][4][2];
-        auto load_grp = [&](int grp, s16x4_t (&dst)[4][2]) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int f = 4 * grp + q, mi = f >> 4, nb = f & 15;
-            const uint32_t p0 = ta[nb & 1] + kRowGroupBytes * 2 * mi + 1024 * (nb >> 1);
+          for (int q = 0; q < 2; ++q) {
+            const int nb = 2 * grp + q;
+            const uint32_t p0 = T + toff[nb & 7] + 256 * (nb >> 3);
             dst[q][0] = lds_tr16(p0);
-            dst[q][1] = lds_tr16(p0 + kRowGroupBytes);
+            dst[q][1] = lds_tr16(p0 + 16384);
           }
         };
         load_grp(0, bv[0]);
 #pragma unroll
-        for (int grp = 0; grp < 8; ++grp) {
-          if (grp + 1 < 8) load_grp(grp + 1, bv[(grp + 1) & 1]);
+        for (int grp = 0; grp < kColBlocks / 2; ++grp) {
+          if (grp + 1 < kColBlocks / 2) load_grp(grp + 1, bv[(grp + 1) & 1]);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int f = 4 * grp + q, mi = f >> 4, nb = f & 15;
+          for (int q = 0; q < 2; ++q) {
+            const int nb = 2 * grp + q;
             const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, bv[grp & 1][q]);
-            o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pp[mi], bf, o[nb], 0, 0, 0);
+            o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pp, bf, o[nb], 0, 0, 0);
           }
-          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
@@ -383,26 +410,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
   }
   if (bad_page && tid == 0) set_err(a.err, ERR_PAGE);
 
-  // ---- epilogue: o_part = O / l, lse = (m + log2 l) ln 2
+  // ---- epilogue: o_part = O / l, lse = (m + log2 l) ln 2; lane holds heads 4g + i
   const float inv = l_sum > 0.f ? 1.f / l_sum : 0.f;
   if (g == 0) {
-    xch[wv][hl] = inv;
-    lse_out[hl] = l_sum > 0.f ? (m_ref + __log2f(l_sum)) * 0.6931471805599453f : -INFINITY;
+    xch[wv][n16] = inv;
+    lse_out[n16] = l_sum > 0.f ? (m_ref + __log2f(l_sum)) * 0.6931471805599453f : -INFINITY;
   }
   __builtin_amdgcn_wave_barrier();
-  float il[16];
+  const float4 il = *reinterpret_cast<const float4*>(&xch[wv][4 * g]);
+  const float ilv[4] = {il.x, il.y, il.z, il.w};
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float4 v = *reinterpret_cast<const float4*>(&xch[wv][8 * q + 4 * g]);
-    il[4 * q] = v.x; il[4 * q + 1] = v.y; il[4 * q + 2] = v.z; il[4 * q + 3] = v.w;
-  }
+  for (int nb = 0; nb < kColBlocks; ++nb)
 #pragma unroll
-  for (int nb = 0; nb < kDc / 32; ++nb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int hh = 8 * (i >> 2) + 4 * g + (i & 3);
-      o_out[hh * kDc + 32 * nb + hl] = o[nb][i] * il[i];
-    }
+    for (int i = 0; i < 4; ++i) o_out[(4 * g + i) * kDc + 16 * nb + n16] = o[nb][i] * ilv[i];
 }
 
 }  // namespace

@@ -16,6 +16,7 @@ stream, and the fp64 CPU oracle timed on a bounded sample on the host.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -42,6 +43,21 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain 1 GiB device copy (calibrates HBM byte counters)")
     return p.parse_args()
+
+
+def attention_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 counter runs
+    (FETCH_SIZE and WRITE_SIZE scaled by a plain-copy calibration), or None when the
+    kernel source changed since they were taken."""
+    path = os.path.join(ROOT, "profiles", "k_attn_mfma_h128_full_traffic.json")
+    try:
+        rec = json.load(open(path))
+        src = open(os.path.join(ROOT, rec["kernel_source"]), "rb").read()
+    except (OSError, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest() != rec.get("kernel_source_sha256"):
+        return None
+    return rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
 
 
 def cpu_baseline(w, seconds: float):
@@ -170,7 +186,8 @@ def main():
         "attention_mfma_tflops": attn_flop / attn_s / 1e12,
         "attention_mfma_frac": attn_flop / attn_s / 1e12 / BF16_PEAK_TFLOPS,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": attention_traffic() if w.name == "full" and S == 4 else None,
                      "kernel": "k_attn_mfma_h128 (mla_decode_attention)",
                      "algorithmic_bytes_per_launch": cache_bytes},
     }

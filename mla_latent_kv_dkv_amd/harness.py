@@ -33,6 +33,7 @@ class DeviceWorkload:
         B = w.batch
         self.seq_lens = torch.tensor(self.lens, dtype=torch.int32, device=self.dev)
         self.pos = (self.seq_lens - 1).contiguous()
+        self.seq_ids = torch.arange(B, dtype=torch.int32, device=self.dev)
         self.block_table = torch.tensor(self.bt_host, dtype=torch.int32, device=self.dev)
         self.weights = {}
         for name in I.WEIGHT_NAMES:
@@ -93,10 +94,8 @@ class DeviceWorkload:
                      self.q_pe, self.ws)
 
     def append(self):
-        B = self.w.batch
-        seq = self.torch.arange(B, dtype=self.torch.int32, device=self.dev)
-        mla_append_latent(self.dims, self.h, self.weights["w_dkv"], self.weights["w_kr"], seq,
-                          self.pos, self.block_table, self.pool, self.ws_append)
+        mla_append_latent(self.dims, self.h, self.weights["w_dkv"], self.weights["w_kr"],
+                          self.seq_ids, self.pos, self.block_table, self.pool, self.ws_append)
 
     def attention(self):
         mla_decode_attention(self.dims, self.q_lat, self.q_pe, self.pool, self.block_table,

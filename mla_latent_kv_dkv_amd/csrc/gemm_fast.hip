@@ -24,6 +24,7 @@
 // contiguous): the workgroup stages a 128 x 128 W tile in LDS and reads MFMA
 // operands from it with ds_read_b64_tr_b16, the hardware transpose.
 #include <algorithm>
+#include <atomic>
 
 #include "common.hpp"
 #include "epilogue.hpp"
@@ -219,6 +220,129 @@ __global__ __launch_bounds__(256) void k_gemm_ws(GemmArgs a, int ntiles, int ksp
   }
 }
 
+// ---- X-stationary weight stream (one K slice of X held in LDS per workgroup) ----
+// For one activation matrix (batch 1, M <= 64) the grid is one workgroup per CU;
+// workgroup w owns K slice w % d and keeps X[:, slice] in LDS for its whole
+// life, so after a one-time load the loop issues only weight loads: no X
+// traffic and no barriers.  Its kXsWaves waves walk 16-row weight strips (strip
+// s of the slice goes to wave s mod (kXsWaves G/d)), one strip after another with a
+// kXsRing-deep load ring that runs across strip boundaries, and write each
+// strip's result (or fp32 partial when d > 1) as soon as it is done.
+// X layout in LDS: row r at 2 kw r bytes, 16-byte chunk c at c ^ 2(r & 7): the
+// 16-row B-operand reads are bank-conflict free.
+constexpr int kXsLdsBytes = 128 * 1024;
+constexpr int kXsRing = 16;
+constexpr int kXsWaves = 4;                     // waves per workgroup
+
+template <typename XT, int MB>
+__global__ __launch_bounds__(64 * kXsWaves, 1) void k_gemm_xs(GemmArgs a, int d, int kw,
+                                                               float* partial) {
+  extern __shared__ __attribute__((aligned(16))) char xs[];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n16 = lane & 15, g = lane >> 4;
+  const int ks = blockIdx.x % d, wg = blockIdx.x / d, wgs = gridDim.x / d;
+  const int64_t kbeg = static_cast<int64_t>(ks) * kw;
+  const int nsteps = kw / 32, nstrips = a.N / 16;
+  const int wave = wg * kXsWaves + wv, nwaves = wgs * kXsWaves;
+  const int my = wave < nstrips ? (nstrips - 1 - wave) / nwaves + 1 : 0;
+  const int rowb = 2 * kw;   // LDS bytes per X row
+
+  // this lane's weight row in the wave's i-th strip, at the start of the slice
+  auto wrow = [&](int i) -> const bf16_t* {
+    const int n0 = 16 * (wave + i * nwaves);
+    const bf16_t* base = n0 < a.n_split
+                             ? static_cast<const bf16_t*>(a.w1) + static_cast<int64_t>(n0) * a.ldw_n
+                             : static_cast<const bf16_t*>(a.w2) +
+                                   static_cast<int64_t>(n0 - a.n_split) * a.ldw_n;
+    return base + static_cast<int64_t>(n16) * a.ldw_n + kbeg + 8 * g;
+  };
+  const int total = my * nsteps;   // steps of this wave over all its strips
+  bf16x8_t wr[kXsRing];
+  if (my > 0) {
+    const bf16_t* p0 = wrow(0);
+#pragma unroll
+    for (int u = 0; u < kXsRing; ++u) wr[u] = ld8(p0 + 32 * min(u, nsteps - 1));
+  }
+
+  // X slice -> LDS (rows past M repeat row 0; their outputs are never stored)
+  {
+    const int cpr = kw / 8;   // 16-byte chunks per row
+    const XT* xb = static_cast<const XT*>(a.x) + kbeg;
+#pragma unroll 4
+    for (int v = tid; v < 16 * MB * cpr; v += 64 * kXsWaves) {
+      const int r = v / cpr, c = v - r * cpr;
+      XVec<XT> t;
+      t.load(xb + static_cast<int64_t>(r < a.M ? r : 0) * a.ldx_m + 8 * c);
+      *reinterpret_cast<u32x4_t*>(&xs[r * rowb + 16 * (c ^ (2 * (r & 7)))]) = t.bits();
+    }
+  }
+  __syncthreads();
+  if (my == 0) return;
+
+  // B operand of block mb at step st: row 16mb + n16, chunk 4st + g (swizzled)
+  uint32_t xoff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) xoff[q] = n16 * rowb + 16 * ((4 * q + g) ^ (2 * (n16 & 7)));
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  f32x4_t acc[MB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) acc[i] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+  // operands of step 4j + q (q static): xoff[q] + 256 j, block mb at +16 rowb mb
+  auto ldx = [&](int q, int j, bf16x8_t (&dst)[MB]) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      dst[mb] = *reinterpret_cast<const bf16x8_t*>(&xs[xoff[q] + 256 * j + 16 * rowb * mb]);
+  };
+  bf16x8_t xc[MB];   // B operands of the current step, read one step ahead
+  ldx(0, 0, xc);
+  for (int t0 = 0; t0 < total; t0 += kXsRing) {
+    // the group t0..t0+R-1 lies in strip t0 / nsteps (nsteps is a multiple of R);
+    // its refills target the next group, in strip (t0+R) / nsteps (the last strip
+    // re-read past the end, so the body stays branch-free)
+    const int st0 = t0 % nsteps;
+    const int pt = min(t0 + kXsRing, total - 1);
+    const bf16_t* pp = wrow(pt / nsteps) + 32 * (pt % nsteps);
+    const int plim = total - 1 - pt;   // refills past this re-read pt
+    // st0 is a multiple of kXsRing: step st0 + u has q = u & 3, j = st0/4 + u/4
+    const int j0 = st0 >> 2;
+    const int jn = st0 + kXsRing == nsteps ? 0 : j0 + kXsRing / 4;   // first step of the next group
+#pragma unroll
+    for (int u = 0; u < kXsRing; ++u) {
+      bf16x8_t xn[MB];
+      if (u + 1 < kXsRing) ldx((u + 1) & 3, j0 + ((u + 1) >> 2), xn);
+      else ldx(0, jn, xn);
+      __builtin_amdgcn_sched_barrier(0);   // the reads go out a whole step before their use
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wr[u], xc[mb], acc[mb], 0, 0, 0);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) xc[mb] = xn[mb];
+      // the refill reuses the slot's registers once its products are issued (a
+      // load into fresh registers would force copies, and waits, at the loop edge)
+      wr[u] = ld8(pp + 32 * min(u, plim));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (st0 + kXsRing == nsteps) {   // strip done: lane (n16, g) holds rows n0 + 4g + e, X row 16mb + n16
+      const int n = 16 * (wave + (t0 / nsteps) * nwaves) + 4 * g;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int m = 16 * mb + n16;
+        if (m < a.M) {
+          if (d == 1) {
+            gemm_epilogue<bf16_t>(a, 0, m, n, acc[mb][0], acc[mb][1]);
+            gemm_epilogue<bf16_t>(a, 0, m, n + 2, acc[mb][2], acc[mb][3]);
+          } else {
+            *reinterpret_cast<f32x4_t*>(partial + (static_cast<int64_t>(ks) * a.M + m) * a.N + n) =
+                acc[mb];
+          }
+        }
+        acc[mb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  }
+}
+
 // Sum of the K-split partials (fixed order) followed by the output stage; each
 // thread takes 4 consecutive columns of one output row.
 __global__ __launch_bounds__(256) void k_gemm_finish(GemmArgs a, int ksplit, const float* partial) {
@@ -228,9 +352,15 @@ __global__ __launch_bounds__(256) void k_gemm_finish(GemmArgs a, int ksplit, con
   for (uint32_t q = blockIdx.x * 256u + threadIdx.x; q < quads; q += 256u * gridDim.x) {
     const float* src = partial + static_cast<int64_t>(q) * 4;
     float4 v = *reinterpret_cast<const float4*>(src);
-    for (int s = 1; s < ksplit; ++s) {
-      const float4 t = *reinterpret_cast<const float4*>(src + s * plane);
-      v.x += t.x; v.y += t.y; v.z += t.z; v.w += t.w;
+    // eight partials in flight at a time, summed in split order
+    for (int s0 = 1; s0 < ksplit; s0 += 8) {
+      float4 t[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (s0 + j < ksplit) t[j] = *reinterpret_cast<const float4*>(src + (s0 + j) * plane);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (s0 + j < ksplit) { v.x += t[j].x; v.y += t[j].y; v.z += t[j].z; v.w += t[j].w; }
     }
     const uint32_t row = q / quads_row;
     const int n = static_cast<int>(q - row * quads_row) * 4;
@@ -341,6 +471,65 @@ void launch_ws(const GemmArgs& a, const WsPlan& p, float* partial, hipStream_t s
   }
 }
 
+struct XsPlan {
+  int mb, d, kw;
+};
+
+XsPlan xs_plan(const GemmArgs& a) {
+  XsPlan p{};
+  p.mb = a.M <= 16 ? 1 : a.M <= 32 ? 2 : 4;
+  // slices are whole groups of 32 * kXsRing k (a strip's steps fill whole ring turns)
+  constexpr int kUnit = 32 * kXsRing;
+  const int kw_max = kXsLdsBytes / (2 * 16 * p.mb) / kUnit * kUnit;
+  const int groups = a.K / kUnit;
+  p.d = groups;
+  for (int d = 1; d <= groups; ++d)
+    if (groups % d == 0 && a.K / d <= kw_max) { p.d = d; break; }
+  p.kw = a.K / p.d;
+  return p;
+}
+
+int cu_count() {
+  static std::atomic<int> cached{0};
+  int v = cached.load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int dev = 0;
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess ||
+      prop.multiProcessorCount < 1)
+    return 256;
+  cached.store(prop.multiProcessorCount, std::memory_order_relaxed);
+  return prop.multiProcessorCount;
+}
+
+template <typename XT, int MB>
+hipError_t launch_xs_inst(const GemmArgs& a, const XsPlan& p, float* partial, hipStream_t stream) {
+  static std::atomic<int> attr_set{0};
+  if (!attr_set.load(std::memory_order_acquire)) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_xs<XT, MB>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             kXsLdsBytes);
+    if (e != hipSuccess) return e;
+    attr_set.store(1, std::memory_order_release);
+  }
+  const int grid = std::max(1, cu_count() / p.d) * p.d;
+  const size_t lds = static_cast<size_t>(16 * MB) * p.kw * 2;
+  hipLaunchKernelGGL((k_gemm_xs<XT, MB>), dim3(grid), dim3(64 * kXsWaves), lds, stream, a, p.d, p.kw,
+                     partial);
+  return hipGetLastError();
+}
+
+hipError_t launch_xs(const GemmArgs& a, const XsPlan& p, float* partial, hipStream_t stream) {
+  if (a.x_f32) {
+    if (p.mb == 1) return launch_xs_inst<float, 1>(a, p, partial, stream);
+    if (p.mb == 2) return launch_xs_inst<float, 2>(a, p, partial, stream);
+    return launch_xs_inst<float, 4>(a, p, partial, stream);
+  }
+  if (p.mb == 1) return launch_xs_inst<bf16_t, 1>(a, p, partial, stream);
+  if (p.mb == 2) return launch_xs_inst<bf16_t, 2>(a, p, partial, stream);
+  return launch_xs_inst<bf16_t, 4>(a, p, partial, stream);
+}
+
 }  // namespace
 
 // NT form: W and X K-contiguous, 16-byte aligned rows, 64-row W tiles that do
@@ -362,10 +551,20 @@ static bool uk_ok(const GemmArgs& a) {
          a.w1 == a.w2 && a.n_split >= a.N;
 }
 
+// One activation matrix of at most 64 rows: the X-stationary kernel.
+static bool xs_ok(const GemmArgs& a) {
+  return ws_ok(a) && a.batch == 1 && a.M <= 64 && a.N % 16 == 0 &&
+         (a.n_split % 16 == 0 || a.n_split >= a.N) && a.K % (32 * kXsRing) == 0;
+}
+
 bool fast_gemm_ok(const GemmArgs& a) { return ws_ok(a) || uk_ok(a); }
 
 size_t gemm_partial_bytes(const GemmArgs& a) {
   if (!ws_ok(a)) return 0;
+  if (xs_ok(a)) {
+    const XsPlan q = xs_plan(a);
+    return q.d > 1 ? static_cast<size_t>(q.d) * a.M * a.N * sizeof(float) : 0;
+  }
   const WsPlan p = ws_plan(a);
   return p.d > 1 ? static_cast<size_t>(p.d) * a.batch * a.M * a.N * sizeof(float) : 0;
 }
@@ -377,6 +576,19 @@ hipError_t launch_gemm_fast(const GemmArgs& a, void* partial, size_t partial_byt
     if (!uk_ok(a)) return hipErrorInvalidValue;
     dim3 grid(a.batch, a.N / kUkN, (a.M + kTile - 1) / kTile);
     hipLaunchKernelGGL(k_gemm_uk, grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
+  if (xs_ok(a)) {
+    const XsPlan q = xs_plan(a);
+    if (q.d > 1 && (partial == nullptr || !aligned16(partial) ||
+                    partial_bytes < gemm_partial_bytes(a)))
+      return hipErrorInvalidValue;
+    hipError_t e = launch_xs(a, q, static_cast<float*>(partial), stream);
+    if (e != hipSuccess || q.d == 1) return e;
+    const int64_t quads = static_cast<int64_t>(a.M) * (a.N / 4);
+    const int blocks = static_cast<int>(std::min<int64_t>((quads + 255) / 256, 8192));
+    hipLaunchKernelGGL(k_gemm_finish, dim3(blocks), dim3(256), 0, stream, a, q.d,
+                       static_cast<const float*>(partial));
     return hipGetLastError();
   }
   const WsPlan p = ws_plan(a);

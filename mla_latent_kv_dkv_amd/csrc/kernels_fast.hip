@@ -439,7 +439,57 @@ hipError_t launch_attention_fast(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-bool fast_merge_ok(const MergeArgs&) { return false; }
-hipError_t launch_merge_fast(const MergeArgs&, hipStream_t) { return hipErrorNotSupported; }
+// Log-sum-exp merge of split partials: one wave per (sequence, head) row, one
+// float4 of the row per lane and split, so every byte of o_part is read once
+// with 16-byte coalesced loads.  The split weights exp(lse_s - max) are
+// wave-uniform and recomputed by every lane.
+__global__ __launch_bounds__(256) void k_merge_rows(MergeArgs a, int rows) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int nh = a.n_heads, S = a.num_splits, dq = a.d_latent / 4;
+  const int b = row / nh, i = row - b * nh;
+  const float* lse = a.lse_part + static_cast<int64_t>(b) * S * nh + i;
+  float m = -INFINITY;
+  for (int s = lane; s < S; s += 64) m = fmaxf(m, lse[static_cast<int64_t>(s) * nh]);
+  m = wave_max(m);
+  const float4* src =
+      reinterpret_cast<const float4*>(a.o_part) + (static_cast<int64_t>(b) * S * nh + i) * dq;
+  const int64_t split_stride = static_cast<int64_t>(nh) * dq;   // float4s between splits
+  float4* dst = reinterpret_cast<float4*>(a.o_lat) + static_cast<int64_t>(row) * dq;
+  float z = 0.f;
+  for (int v = lane; v < dq; v += 64) {   // lane 0 always runs: dq >= 1
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float zz = 0.f;
+    if (m != -INFINITY) {
+#pragma unroll 4
+      for (int s = 0; s < S; ++s) {
+        const float l = lse[static_cast<int64_t>(s) * nh];
+        const float w = l == -INFINITY ? 0.f : __expf(l - m);
+        zz += w;
+        if (w != 0.f) {
+          const float4 x = src[s * split_stride + v];
+          acc.x += w * x.x; acc.y += w * x.y; acc.z += w * x.z; acc.w += w * x.w;
+        }
+      }
+    }
+    z = zz;
+    const float inv = zz > 0.f ? 1.f / zz : 0.f;
+    dst[v] = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  }
+  if (a.lse && lane == 0) a.lse[row] = z > 0.f ? m + __logf(z) : -INFINITY;
+}
+
+bool fast_merge_ok(const MergeArgs& a) {
+  return a.d_latent % 4 == 0 && (reinterpret_cast<uintptr_t>(a.o_part) & 15) == 0 &&
+         (reinterpret_cast<uintptr_t>(a.o_lat) & 15) == 0 &&
+         static_cast<int64_t>(a.batch) * a.n_heads < (int64_t{1} << 31) - 4;
+}
+
+hipError_t launch_merge_fast(const MergeArgs& a, hipStream_t stream) {
+  if (a.batch == 0) return hipSuccess;
+  const int rows = a.batch * a.n_heads;
+  hipLaunchKernelGGL(k_merge_rows, dim3((rows + 3) / 4), dim3(256), 0, stream, a, rows);
+  return hipGetLastError();
+}
 
 }  // namespace mla

@@ -349,7 +349,7 @@ __global__ __launch_bounds__(256) void k_gemm_finish(GemmArgs a, int ksplit, con
   const uint32_t quads_row = static_cast<uint32_t>(a.N) / 4;
   const uint32_t quads = static_cast<uint32_t>(a.batch) * a.M * quads_row;
   const int64_t plane = static_cast<int64_t>(a.batch) * a.M * a.N;
-  for (uint32_t q = blockIdx.x * 256u + threadIdx.x; q < quads; q += 256u * gridDim.x) {
+  for (uint32_t q = blockIdx.x * blockDim.x + threadIdx.x; q < quads; q += blockDim.x * gridDim.x) {
     const float* src = partial + static_cast<int64_t>(q) * 4;
     float4 v = *reinterpret_cast<const float4*>(src);
     // eight partials in flight at a time, summed in split order
@@ -471,6 +471,16 @@ void launch_ws(const GemmArgs& a, const WsPlan& p, float* partial, hipStream_t s
   }
 }
 
+// Sum of d fp32 partials + output stage; small outputs use 64-thread blocks so
+// that the (latency-bound) sums spread over more CUs.
+hipError_t launch_finish(const GemmArgs& a, int d, const float* partial, hipStream_t stream) {
+  const int64_t quads = static_cast<int64_t>(a.batch) * a.M * (a.N / 4);
+  const int threads = quads < 65536 ? 64 : 256;
+  const int blocks = static_cast<int>(std::min<int64_t>((quads + threads - 1) / threads, 8192));
+  hipLaunchKernelGGL(k_gemm_finish, dim3(blocks), dim3(threads), 0, stream, a, d, partial);
+  return hipGetLastError();
+}
+
 struct XsPlan {
   int mb, d, kw;
 };
@@ -551,9 +561,11 @@ static bool uk_ok(const GemmArgs& a) {
          a.w1 == a.w2 && a.n_split >= a.N;
 }
 
-// One activation matrix of at most 64 rows: the X-stationary kernel.
+// One activation matrix of at most 64 rows and enough weight rows to give every
+// wave of the grid strips to stream (narrow outputs, like the 576-wide latent
+// append, leave most waves idle there and go to k_gemm_ws): the X-stationary kernel.
 static bool xs_ok(const GemmArgs& a) {
-  return ws_ok(a) && a.batch == 1 && a.M <= 64 && a.N % 16 == 0 &&
+  return ws_ok(a) && a.batch == 1 && a.M <= 64 && a.N >= 2048 && a.N % 16 == 0 &&
          (a.n_split % 16 == 0 || a.n_split >= a.N) && a.K % (32 * kXsRing) == 0;
 }
 
@@ -585,11 +597,7 @@ hipError_t launch_gemm_fast(const GemmArgs& a, void* partial, size_t partial_byt
       return hipErrorInvalidValue;
     hipError_t e = launch_xs(a, q, static_cast<float*>(partial), stream);
     if (e != hipSuccess || q.d == 1) return e;
-    const int64_t quads = static_cast<int64_t>(a.M) * (a.N / 4);
-    const int blocks = static_cast<int>(std::min<int64_t>((quads + 255) / 256, 8192));
-    hipLaunchKernelGGL(k_gemm_finish, dim3(blocks), dim3(256), 0, stream, a, q.d,
-                       static_cast<const float*>(partial));
-    return hipGetLastError();
+    return launch_finish(a, q.d, static_cast<const float*>(partial), stream);
   }
   const WsPlan p = ws_plan(a);
   if (p.d > 1 && (partial == nullptr || !aligned16(partial) ||
@@ -601,11 +609,7 @@ hipError_t launch_gemm_fast(const GemmArgs& a, void* partial, size_t partial_byt
     launch_ws<bf16_t>(a, p, static_cast<float*>(partial), stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.d == 1) return e;
-  const int64_t quads = static_cast<int64_t>(a.batch) * a.M * (a.N / 4);
-  const int blocks = static_cast<int>(std::min<int64_t>((quads + 255) / 256, 8192));
-  hipLaunchKernelGGL(k_gemm_finish, dim3(blocks), dim3(256), 0, stream, a, p.d,
-                     static_cast<const float*>(partial));
-  return hipGetLastError();
+  return launch_finish(a, p.d, static_cast<const float*>(partial), stream);
 }
 
 }  // namespace mla

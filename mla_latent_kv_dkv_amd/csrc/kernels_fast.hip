@@ -4,37 +4,43 @@
 // ([Report] §2.3/§2.4 of "《DeepSeek-V2》深度解读报告": every head scores the
 // same cached latent rows [c | k^R]; s = tau (q_lat . c + q_pe . k^R)).
 //
-// Work unit = (sequence b, split s).  A 512-thread workgroup (8 waves, two per
-// SIMD so that one wave's softmax and LDS waits hide behind the other's matrix
-// products) streams the split's rows in tiles of 32 tokens (32 rows x 1152
-// bytes, contiguous inside one 64-row page) through a 3-slot LDS ring filled by
-// asynchronous global->LDS copies (global_load_lds_dwordx4), two tiles ahead
-// of the one consumed.  Wave w owns heads 16w..16w+15 (mfma_f32_16x16x32_bf16):
-//   scores  S^T[t, h] = sum_k C[t, k] Q[h, k]   (M = 16 tokens, two blocks;
-//           N = 16 heads; K = 576 in 18 steps; A = tile rows from LDS, B = the
-//           wave's queries: 14 k-steps in VGPRs, 4 in LDS, for the whole unit)
-//   softmax per head in the exp2 domain: in-lane over 8 tokens plus two
-//           cross-lane steps.  The exponent reference of each head is fixed at
-//           the maximum of its first scored tile, so the accumulator is never
-//           rescaled; later scores may exceed it by up to 2^64 (no fp32/bf16
-//           overflow).  A score beyond that headroom makes the whole unit run
-//           again with the larger reference (at most once).
-//   P.C     O[h, d] += sum_t P[h, t] C[t, d]   (M = 16 heads, N = 512 in 32
-//           blocks, K = 32 tokens).  The score accumulator of a lane holds one
-//           head and tokens 16 tb + 4 g + i; taking the contraction's k order
-//           as t(g, j) = 16 (j >> 2) + 4 g + (j & 3) makes the packed
-//           probabilities exactly the A operand, and the B operand (4 tokens
-//           of one column per half) is one ds_read_b64_tr_b16 (hardware
-//           transpose) per half from the same tile.
-// LDS tile layout (36 KB): the 512 latent values of row r fill one 1 KB block
-// (block r), chunk c (16 bytes) stored at c ^ 2(r & 7); the 64 RoPE values of
-// rows 8j..8j+7 fill block 32 + j, row r at 128 (r & 7), chunk c' at
-// c' ^ (r & 7).  Every copy fills one block.  LDS has 64 banks of 4 bytes; a
-// ds_read_b128 is served in four 16-lane phases, the lanes of a phase being
-// those with equal lane >> 5 and equal parity of bits 2..4 of the lane, and a
+// Work unit = (sequence b, split s).  A 256-thread workgroup (4 waves, one per
+// SIMD) streams the split's rows in tiles of 32 tokens (32 rows x 1152 bytes,
+// contiguous inside one 64-row page) through a 4-slot LDS ring filled by
+// asynchronous global->LDS copies (global_load_lds_dwordx4), two tiles ahead.
+// Wave w owns heads 32w..32w+31 and uses mfma_f32_32x32x16_bf16 throughout:
+//   scores  S^T[t, h] = sum_k C[t, k] Q[h, k]   (M = the tile's 32 tokens,
+//           N = the wave's 32 heads, K = 576 in 36 steps; A = tile rows from
+//           LDS, B = the wave's queries, all 36 k-steps held in VGPRs for the
+//           whole unit).  The accumulator stays in VGPRs (inline asm).
+//   softmax per head in the exp2 domain.  The exponent reference of each head
+//           is fixed at the maximum of the split's first tile, so the output
+//           accumulator is never rescaled; a later score more than 2^64 above
+//           it makes the whole unit run again with the split's maximum as
+//           reference (at most once).  Row sums and maxima stay per lane and
+//           are combined across the two lanes of a head at the end.
+//   P.C     O[h, d] += sum_t P[h, t] C[t, d]   (M = 32 heads, N = 512 in 16
+//           blocks, K = 32 tokens in 2 steps).  O (32 x 512 fp32 per wave)
+//           lives in the 256 AGPRs.  A lane's score accumulator holds head
+//           32w + (lane & 31) and tokens 8(i >> 2) + 4(lane >> 5) + (i & 3);
+//           taking the contraction's k order as t = 16kk + 8(j >> 2) +
+//           4(lane >> 5) + (j & 3) makes the packed weights exactly the A
+//           operand, and the B operand (4 tokens of one column per half) is
+//           one ds_read_b64_tr_b16 (hardware transpose) per half.
+// Pipeline: iteration t computes the scores of tile t, then the products of
+// tile t-1 with the weights of tile t computed between them, so the softmax
+// arithmetic runs in the shadow of the matrix products; tiles t-1, t and the
+// two in flight occupy the 4 slots.
+// LDS tile layout (38 KB): latent row r at 1088 r (1 KB + 64 bytes of pad),
+// its 16-byte chunk c at c ^ ((r >> 2) & 3); the 64 RoPE values of rows
+// 8j..8j+7 fill the 1 KB block j after the latent rows, row r at 128 (r & 7),
+// chunk c' at c' ^ ((r >> 1) & 7).  Every copy fills 1 KB.  LDS has 64 banks
+// of 4 bytes; a ds_read_b128 is served in four 16-lane phases (lanes with
+// equal lane >> 5 and equal parity of bits 2..4 of the lane), a
 // ds_read_b64(_tr_b16) in two 32-lane phases (lane >> 5).  Under this layout
-// no phase of a score read (16 rows, one chunk per lane group) or of a
-// transposed read (8 rows, a chunk pair) puts two addresses on one bank.
+// no phase of a score read (16 rows, one chunk) or of a transposed read (4
+// rows, 4 chunks) puts two addresses on one bank, and the per-step offsets of
+// both reads are instruction immediates.
 #include "common.hpp"
 #include "launch_fast.hpp"
 
@@ -44,7 +50,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8;
@@ -53,20 +59,27 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
 constexpr int kDc = 512, kDr = 64, kPage = 64;
 constexpr int kTileTok = 32;
 constexpr int kRowBytes = (kDc + kDr) * 2;            // 1152: one cached row
-constexpr int kRopeOff = kTileTok * 1024;             // RoPE blocks follow the 32 latent blocks
-constexpr int kTileBytes = kRopeOff + (kTileTok / 8) * 1024;   // 36864
-constexpr int kThreads = 512, kWaves = 8;
-constexpr int kKSteps = (kDc + kDr) / 32;             // 18
-constexpr int kColBlocks = kDc / 16;                  // 32
-constexpr int kStages = 3;                            // LDS ring depth
-constexpr int kQReg = 14;                             // k-steps of Q held in VGPRs
-constexpr int kQLds = kKSteps - kQReg;                // k-steps of Q held in LDS
-constexpr int kPageWin = 2048;                        // page ids of the split held in LDS
+constexpr int kPitch = 1088;                          // LDS bytes per latent row (1 KB + pad)
+constexpr int kRopeOff = kTileTok * kPitch;           // RoPE blocks follow the 32 latent rows
+constexpr int kTileBytes = kRopeOff + (kTileTok / 8) * 1024;   // 38912
+constexpr int kThreads = 256, kWaves = 4;             // one wave per SIMD
+constexpr int kHeads = 32;                            // heads of one wave
+constexpr int kKSteps = (kDc + kDr) / 16;             // 36 score k-steps
+constexpr int kLatSteps = kDc / 16;                   // 32 of them over the latent part
+constexpr int kColBlocks = kDc / 32;                  // 16 output column blocks
+constexpr int kStages = 4;                            // LDS ring depth
+constexpr int kCopies = 9;                            // copies per wave per tile
+constexpr int kARing = 6;                             // score operands in flight
+constexpr int kBRing = 4;                             // P.C operand pairs in flight
+constexpr int kPageWin = 512;                         // page ids of the split held in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kHeadroom = 64.0f;                    // log2 units above the reference
 
-__device__ __forceinline__ int ukey(int r) { return 2 * (r & 7); }
-__device__ __forceinline__ int vkey(int r) { return r & 7; }
+// 16-byte chunk c of latent row r sits at chunk c ^ lkey(r) of the row's
+// 1 KB (at kPitch r); chunk c' of the RoPE part of row r at chunk c' ^ rkey(r)
+// of its 128 bytes.
+__device__ __forceinline__ int lkey(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int rkey(int r) { return (r >> 1) & 7; }
 
 __device__ __forceinline__ unsigned cvt2(float lo, float hi) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
@@ -86,15 +99,33 @@ __device__ __forceinline__ s16x4_t lds_tr16(uint32_t addr) {
       static_cast<uintptr_t>(addr)));
 }
 
+// Keep a value in a register as computed (no reassociation or hoisting).
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
       (const __attribute__((address_space(3))) char*)(p)));
 }
 
-// Keep a value in a register as computed (no reassociation or hoisting).
-__device__ __forceinline__ uint32_t opaque(uint32_t v) {
-  asm volatile("" : "+v"(v));
-  return v;
+// Score products with the accumulator in VGPRs.  Written as inline asm
+// because the builtin takes the AGPR-accumulator form in a kernel that may use
+// more than 256 registers, and here the 256 AGPRs hold the P.C accumulators.
+// Wait states: back-to-back products on the same accumulator need none; a
+// VALU read of the result needs 12 after the last one (16 are given), and the
+// first product keeps 2 after any VALU write of registers it takes over.
+__device__ __forceinline__ f32x16_t mfma_v_first(const bf16x8_t& a, const bf16x8_t& b) {
+  f32x16_t d;
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  return d;
+}
+__device__ __forceinline__ void mfma_v(f32x16_t& d, const bf16x8_t& a, const bf16x8_t& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v_last(f32x16_t& d, const bf16x8_t& a, const bf16x8_t& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 15" : "+v"(d) : "v"(a), "v"(b));
 }
 
 // Work-unit index of workgroup x: consecutive splits of a sequence go to the
@@ -102,6 +133,19 @@ __device__ __forceinline__ uint32_t opaque(uint32_t v) {
 __device__ __forceinline__ int unit_of(int x, int units) {
   if ((units & 7) != 0) return x;
   return (x & 7) * (units >> 3) + (x >> 3);
+}
+
+// lgkmcnt(n) with vmcnt/expcnt left alone (gfx9 encoding of s_waitcnt).
+__device__ __forceinline__ void wait_lgkm(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0xC07F); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0xC17F); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0xC27F); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0xC37F); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0xC47F); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0xC57F); break;
+    default: __builtin_amdgcn_s_waitcnt(0xC67F); break;
+  }
 }
 
 // vmcnt(n) with expcnt/lgkmcnt left alone (gfx9 encoding of s_waitcnt).
@@ -150,58 +194,102 @@ __device__ __forceinline__ void dma_block(uint64_t gbase, uint32_t voff, uint32_
 }
 
 // Start the asynchronous copy of the tile at `tok0` (32 rows of one page) into
-// the ring slot at LDS address `slot`.  Wave wv copies latent rows 4wv..4wv+3
-// and, for wv < 4, RoPE block wv (5 or 4 copies).  In a partial tile, rows past
-// the split's end re-read row 0 (finite data whose score is masked); a page
-// outside the pool reads pool row 0 (and is flagged).
+// the ring slot at LDS address `slot`.  Wave wv copies latent rows
+// 8wv..8wv+7 and RoPE block wv (rows 8wv..8wv+7): kCopies copies.  In a
+// partial tile, rows past the split's end re-read row 0 (finite data whose
+// score is masked); a page outside the pool reads pool row 0 (masked, and
+// flagged by the caller).
 __device__ __forceinline__ void tile_issue(const char* __restrict__ pool, int page, bool ok,
                                            int tok0, int t1, uint32_t slot, int wv, int lane) {
   const int nvalid = ok ? min(kTileTok, t1 - tok0) : 0;
   const uint64_t tile = reinterpret_cast<uint64_t>(
       ok ? pool + (static_cast<int64_t>(page) * kPage + (tok0 & (kPage - 1))) * kRowBytes : pool);
+  lane = static_cast<int>(opaque(static_cast<uint32_t>(lane)));   // per-copy offsets stay unhoisted
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r = 4 * wv + q;
-    dma_block(tile + (r < nvalid ? r : 0) * kRowBytes, 16 * (lane ^ ukey(r)), slot + 1024 * r);
+  for (int q = 0; q < 8; ++q) {
+    const int r = 8 * wv + q;
+    dma_block(tile + (r < nvalid ? r : 0) * kRowBytes, 16 * (lane ^ lkey(r)), slot + kPitch * r);
   }
-  if (wv < 4) {
-    const int rr = 8 * wv + (lane >> 3);
-    const uint32_t voff =
-        (rr < nvalid ? rr : 0) * kRowBytes + 2 * kDc + 16 * ((lane & 7) ^ vkey(rr));
-    dma_block(tile, voff, slot + kRopeOff + 1024 * wv);
-  }
+  const int rr = 8 * wv + (lane >> 3);
+  const uint32_t voff =
+      (rr < nvalid ? rr : 0) * kRowBytes + 2 * kDc + 16 * ((lane & 7) ^ rkey(rr));
+  dma_block(tile, voff, slot + kRopeOff + 1024 * wv);
 }
 
-// Wait until this wave's copies of the current tile have landed, `after` tiles
-// (0..kStages-2) having been issued since; waves 0..3 issue 5 copies per tile,
-// waves 4..7 issue 4.
-__device__ __forceinline__ void wait_tile(int after, bool five) {
-  if (after >= 3) {
-    if (five) wait_vmcnt<15>(); else wait_vmcnt<12>();
-  } else if (after == 2) {
-    if (five) wait_vmcnt<10>(); else wait_vmcnt<8>();
-  } else if (after == 1) {
-    if (five) wait_vmcnt<5>(); else wait_vmcnt<4>();
-  } else {
-    wait_vmcnt<0>();
-  }
+// The same copies for a full tile of a valid page, as one block: M0 steps by
+// the LDS row pitch and the per-lane offset by the row stride, so the block
+// needs one VGPR temporary and no 64-bit address arithmetic.  `voff` =
+// 1152 (8 wv) + 16 (lane ^ lkey(8 wv)), `voff_hi` the same for row 8 wv + 4
+// (the key changes every 4 rows), `voff_rope` the RoPE copy's offset, `lds` =
+// slot + kPitch (8 wv).  Wait states: 5 after any VALU write of the SGPR
+// operands, 1 after each M0 write before the copy that reads it.
+__device__ __forceinline__ void tile_issue_full(uint64_t tile, uint32_t voff, uint32_t voff_hi,
+                                                uint32_t voff_rope, uint32_t lds,
+                                                uint32_t lds_rope) {
+  uint32_t save, tmp;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %6\n\t"
+      "s_nop 4\n\t"
+      "global_load_lds_dwordx4 %2, %5\n\t"
+      "v_add_u32 %1, 0x480, %2\n\t"
+      "s_add_u32 m0, m0, 0x440\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %5\n\t"
+      "v_add_u32 %1, 0x900, %2\n\t"
+      "s_add_u32 m0, m0, 0x440\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %5\n\t"
+      "v_add_u32 %1, 0xd80, %2\n\t"
+      "s_add_u32 m0, m0, 0x440\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %5\n\t"
+      "s_add_u32 m0, m0, 0x440\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, %5\n\t"
+      "v_add_u32 %1, 0x480, %3\n\t"
+      "s_add_u32 m0, m0, 0x440\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %5\n\t"
+      "v_add_u32 %1, 0x900, %3\n\t"
+      "s_add_u32 m0, m0, 0x440\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %5\n\t"
+      "v_add_u32 %1, 0xd80, %3\n\t"
+      "s_add_u32 m0, m0, 0x440\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %5\n\t"
+      "s_mov_b32 m0, %7\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %4, %5\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save), "=&v"(tmp)
+      : "v"(voff), "v"(voff_hi), "v"(voff_rope), "s"(tile), "s"(lds), "s"(lds_rope)
+      : "memory");
+}
+
+// Wait until this wave's copies of a tile have landed, `after` tiles (0..2)
+// having been issued since.
+__device__ __forceinline__ void wait_tile(int after) {
+  if (after >= 2) wait_vmcnt<2 * kCopies>();
+  else if (after == 1) wait_vmcnt<kCopies>();
+  else wait_vmcnt<0>();
 }
 
 __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
     AttnArgs a, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     const char* __restrict__ pool) {
   __shared__ __attribute__((aligned(1024))) char ring[kStages * kTileBytes];
-  __shared__ __attribute__((aligned(16))) float xch[kWaves][16];
-  // k-steps kQReg.. of every wave's Q fragments: [wave][k-step][lane] x 16 B
-  __shared__ __attribute__((aligned(16))) bf16x8_t qlds[kWaves][kQLds][64];
+  __shared__ __attribute__((aligned(16))) float xch[kWaves][kHeads];
   // page ids of the split's pages [wbase, wbase + kPageWin): a copy in LDS, so
   // a tile's page costs a short LDS read instead of a scalar memory load whose
   // wait would also block every LDS wait behind it
   __shared__ int pwin[kPageWin];
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int g = lane >> 4;            // k-group of the MFMA operands
-  const int n16 = lane & 15;          // head (scores) / column (P.C output) of this lane
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
+  const int g2 = lane >> 5;           // k-group of the 32x32 MFMA operands
+  const int r32 = lane & 31;          // token row (scores A) / head (scores B, P.C A)
   const int S = a.num_splits;
   const int unit = unit_of(blockIdx.x, a.batch * S);
   const int b = unit / S, s = unit - b * S;
@@ -215,13 +303,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
   int t0, t1;
   split_range(L, S, s, kPage, &t0, &t1);
 
-  const int64_t ob = (static_cast<int64_t>(b) * S + s) * nh + 16 * wv;
+  const int64_t ob = (static_cast<int64_t>(b) * S + s) * nh + kHeads * wv;
   float* o_out = a.o_part + ob * kDc;
   float* lse_out = a.lse_part + ob;
 
   if (t0 >= t1) {  // empty split (uniform across the workgroup)
-    for (int e = lane; e < 16 * kDc; e += 64) o_out[e] = 0.f;
-    if (lane < 16) lse_out[lane] = -INFINITY;
+    for (int e = lane; e < kHeads * kDc; e += 64) o_out[e] = 0.f;
+    if (lane < kHeads) lse_out[lane] = -INFINITY;
     return;
   }
   const int32_t* bt = block_table + static_cast<int64_t>(b) * a.max_pages;
@@ -239,190 +327,228 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
     wbase = base;
   };
 
-  // ---- this wave's queries as MFMA B fragments: head 16wv + n16, k = 32ks + 8g + j
-  bf16x8_t qf[kQReg];
+  // ---- this wave's queries as MFMA B fragments: head 32wv + r32, k = 16ks + 8g2 + j
+  bf16x8_t qf[kKSteps];
   {
-    const int h = 16 * wv + n16;
-    const float* ql = a.q_lat + (static_cast<int64_t>(b) * nh + h) * kDc + 8 * g;
-    const float* qp = a.q_pe + (static_cast<int64_t>(b) * nh + h) * kDr + 8 * g;
+    const int h = kHeads * wv + r32;
+    const float* ql = a.q_lat + (static_cast<int64_t>(b) * nh + h) * kDc + 8 * g2;
+    const float* qp = a.q_pe + (static_cast<int64_t>(b) * nh + h) * kDr + 8 * g2;
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) {
-      const float* src = ks < kDc / 32 ? ql + 32 * ks : qp + 32 * (ks - kDc / 32);
+      const float* src = ks < kLatSteps ? ql + 16 * ks : qp + 16 * (ks - kLatSteps);
       float v[8];
       const float4 lo = *reinterpret_cast<const float4*>(src);
       const float4 hi = *reinterpret_cast<const float4*>(src + 4);
       v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
       v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
-      if (ks < kQReg) qf[ks] = pack8(v);
-      else qlds[wv][ks - kQReg][lane] = pack8(v);
+      qf[ks] = pack8(v);
+      if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bounded loads in flight
     }
   }
-  const uint32_t qtail = lds_addr(&qlds[wv][0][lane]);
 
   // ---- per-lane constant offsets inside a tile
-  // score A fragment, token row 16tb + n16, latent chunk 4ks + g:
-  //   soff[ks & 3] + 256 (ks >> 2) + 16384 tb; RoPE chunk 4(ks-16) + g: roff[ks-16] + 2048 tb
-  const int u = ukey(n16), v = vkey(n16);
-  uint32_t soff[4], roff[2];
+  // score A fragment, token row r32, latent chunk 2ks + g2: soff[ks & 1] + 64 (ks >> 1);
+  // RoPE chunk 2q + g2 (q = ks - 32): roff[q]
+  const int ky = lkey(r32), vy = rkey(r32);
+  uint32_t soff[2], roff[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) soff[q] = 1024 * n16 + 16 * ((4 * q + g) ^ u);
+  for (int j = 0; j < 2; ++j) soff[j] = kPitch * r32 + 16 * ((2 * j + g2) ^ ky);
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
-    roff[q] = kRopeOff + 1024 * (n16 >> 3) + 128 * (n16 & 7) + 16 * ((4 * q + g) ^ v);
-  // P.C B fragment, transposed read: this lane addresses token row rt (+16 for
-  // the second half) and columns 16nb + 4(n16 & 3)..+3: toff[nb & 7] + 256 (nb >> 3)
-  const int rt = 4 * g + (n16 >> 2);
-  const int wt = ((n16 & 3) >> 1) ^ ukey(rt);
-  uint32_t toff[8];
+  for (int q = 0; q < 4; ++q) roff[q] = kRopeOff + 128 * r32 + 16 * ((2 * q + g2) ^ vy);
+  // P.C B fragment of 16-lane group (ch, g2), lane s16: token row 16kk + 8jj + 4g2 + (s16 >> 2),
+  // columns 32nb + 16ch + 4(s16 & 3)..+3: toff[jj] + 64 nb + 16 kPitch kk
+  const int s16 = lane & 15, ch = (lane >> 4) & 1;
+  const int cp = 2 * ch + ((s16 & 3) >> 1);
+  uint32_t toff[2];
 #pragma unroll
-  for (int m = 0; m < 8; ++m) toff[m] = 1024 * rt + 16 * ((2 * m) ^ wt) + 8 * (n16 & 1);
+  for (int jj = 0; jj < 2; ++jj)
+    toff[jj] = kPitch * (8 * jj + 4 * g2 + (s16 >> 2)) + 16 * (cp ^ (2 * jj + g2)) + 8 * (s16 & 1);
   const uint32_t ring0 = lds_addr(ring);
-  const bool five = wv < 4;
 
-  f32x4_t o[kColBlocks];
-  float m_ref = -INFINITY;   // exponent reference (log2 units) of head n16
-  float l_sum = 0.f;         // sum of exp2(x - m_ref) of head n16
+  // scores S^T[t, h] of the tile in slot T: lane holds head 32wv + r32 and
+  // tokens 8(i >> 2) + 4g2 + (i & 3), i = 0..15
+  auto scores = [&](uint32_t T) {
+    f32x16_t acc;
+    const uint32_t sa0 = T + soff[0], sa1 = T + soff[1];
+    auto lda = [&](int ks) {
+      return ks < kLatSteps ? lds_b128((ks & 1 ? sa1 : sa0) + 64 * (ks >> 1))
+                            : lds_b128(T + roff[ks < kLatSteps ? 0 : ks - kLatSteps]);
+    };
+    // operands of steps ks, ks+1 are awaited together; kARing - 2 steps are read ahead
+    bf16x8_t ar[kARing];
+#pragma unroll
+    for (int d = 0; d < kARing - 2; ++d) ar[d] = lda(d);
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ks += 2) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        if (ks + kARing - 2 + e < kKSteps) ar[(ks + kARing - 2 + e) % kARing] = lda(ks + kARing - 2 + e);
+      const int ahead = min(kARing - 2, kKSteps - ks - 2);   // reads issued after step ks+1's
+      wait_lgkm(ahead);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int k = ks + e;
+        if (k == 0) acc = mfma_v_first(ar[0], qf[0]);
+        else if (k == kKSteps - 1) mfma_v_last(acc, ar[k % kARing], qf[k]);
+        else mfma_v(acc, ar[k % kARing], qf[k]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return acc;
+  };
+  auto mask = [&](f32x16_t& x, int nvalid) {
+    if (nvalid < kTileTok) {   // partial tile only (a real branch: nvalid is uniform)
+      asm volatile("");
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (8 * (i >> 2) + 4 * g2 + (i & 3) >= nvalid) x[i] = -INFINITY;
+    }
+  };
+
+  f32x16_t o[kColBlocks];
+  float m_ref = -INFINITY;   // exponent reference (log2 units) of head 32wv + r32
+  float l_part = 0.f;        // this lane's share of sum exp2(x - m_ref)
   const float cs = a.scale * kLog2e;
   bool bad_page = false;
   const int ntiles = (t1 - t0 + kTileTok - 1) / kTileTok;
 
+  // per-lane offsets of the full-tile copies (rows 8wv.., 8wv+4.., RoPE block)
+  const uint32_t voff_lo = kRowBytes * 8 * wv + 16 * (lane ^ lkey(8 * wv));
+  const uint32_t voff_hi = kRowBytes * (8 * wv + 4) + 16 * (lane ^ lkey(8 * wv + 4));
+  const uint32_t voff_rope = kRowBytes * (8 * wv + (lane >> 3)) + 2 * kDc +
+                             16 * ((lane & 7) ^ rkey(8 * wv + (lane >> 3)));
+  // start the copy of tile j into slot j & 3; returns its count of valid rows
+  auto issue = [&](int j) {
+    const int tok = t0 + j * kTileTok;
+    if (tok / kPage - wbase >= kPageWin) load_window(tok / kPage);   // splits > kPageWin pages
+    const int pg = __builtin_amdgcn_readfirstlane(pwin[tok / kPage - wbase]);   // uniform
+    const bool ok = pg >= 0 && pg < a.num_pages;
+    bad_page |= !ok;
+    const uint32_t slot = ring0 + (j & 3) * kTileBytes;
+    const int nvalid = ok ? min(kTileTok, t1 - tok) : 0;
+    if (nvalid == kTileTok) {
+      const uint64_t tile = reinterpret_cast<uint64_t>(
+          pool + (static_cast<int64_t>(pg) * kPage + (tok & (kPage - 1))) * kRowBytes);
+      tile_issue_full(tile, voff_lo, voff_hi, voff_rope, slot + kPitch * 8 * wv,
+                      slot + kRopeOff + 1024 * wv);
+    } else {
+      tile_issue(pool, pg, ok, tok, t1, slot, wv, lane);
+    }
+    return nvalid;
+  };
+
+  float seen = -INFINITY;     // largest raw score of this lane in this pass
+  float p[16];                // softmax weights of the tile being scored
+  // weight i of scores x: exp2(x cs - m) (m: reference in log2 units)
+  auto weight = [&](const f32x16_t& x, int i, float mr) {
+    seen = fmaxf(seen, x[i]);
+    p[i] = __builtin_amdgcn_exp2f(fmaf(x[i], cs, -mr));
+  };
+  // O += P . C over the tile in slot T (pp0/pp1: packed weights of that tile);
+  // with `next`, the weights of the following tile (scores x) are computed
+  // between the products
+  auto pv_product = [&](uint32_t T, const bf16x8_t& pp0, const bf16x8_t& pp1, bool next,
+                        const f32x16_t& x, float mr) {
+    const uint32_t b0 = T + toff[0], b1 = T + toff[1];
+    // product m: column block m >> 1, token half m & 1
+    auto ldb = [&](int m, s16x4_t (&dst)[2]) {
+      const int off = 64 * (m >> 1) + 16 * kPitch * (m & 1);
+      dst[0] = lds_tr16(b0 + off);
+      dst[1] = lds_tr16(b1 + off);
+    };
+    // operands of products m, m+1 are awaited together; kBRing - 2 products read ahead
+    s16x4_t br[kBRing][2];
+#pragma unroll
+    for (int d = 0; d < kBRing - 2; ++d) ldb(d, br[d]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int m = 0; m < 2 * kColBlocks; m += 2) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        if (m + kBRing - 2 + e < 2 * kColBlocks) ldb(m + kBRing - 2 + e, br[(m + kBRing - 2 + e) % kBRing]);
+      wait_lgkm(2 * min(kBRing - 2, 2 * kColBlocks - m - 2));
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        o[(m + e) >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            e ? pp1 : pp0, __builtin_bit_cast(bf16x8_t, br[(m + e) % kBRing]), o[(m + e) >> 1], 0, 0, 0);
+      if (next) weight(x, m >> 1, mr);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto weight_sum = [&]() {
+    l_part += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])) +
+              (((p[8] + p[9]) + (p[10] + p[11])) + ((p[12] + p[13]) + (p[14] + p[15])));
+  };
+
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int nb = 0; nb < kColBlocks; ++nb) o[nb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-    l_sum = 0.f;
-    float seen = m_ref;        // largest tile maximum met in this pass
-    bool over = false;
+    for (int nb = 0; nb < kColBlocks; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[nb][i] = 0.f;
+    l_part = 0.f;
+    seen = -INFINITY;
 
     if (wbase != p_first) load_window(p_first);
-    for (int j = 0; j < kStages - 1 && j < ntiles; ++j) {
-      const int tok = t0 + j * kTileTok;
-      const int pg = pwin[tok / kPage - wbase];
-      tile_issue(pool, pg, pg >= 0 && pg < a.num_pages, tok, t1, ring0 + j * kTileBytes, wv, lane);
+    int nv0 = issue(0), nv1 = 0, nv2 = 0;   // valid rows of tiles t, t+1, t+2
+    if (ntiles > 1) nv1 = issue(1);
+    // ---- tile 0: scores and weights
+    wait_tile(ntiles > 1 ? 1 : 0);
+    lds_barrier();
+    if (ntiles > 2) nv2 = issue(2);
+    f32x16_t sc = scores(ring0);
+    mask(sc, nv0);
+    if (pass == 0) {            // the first tile fixes the reference
+      float tm = sc[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) tm = fmaxf(tm, sc[i]);
+      m_ref = fmaxf(tm, __shfl_xor(tm, 32, 64)) * cs;
     }
-
-    int cur = 0;                                       // slot of tile `it`
-    for (int it = 0; it < ntiles; ++it) {
-      const int tok0 = t0 + it * kTileTok;
-      wait_tile(min(ntiles - 1 - it, kStages - 2), five);
-      lds_barrier();   // tile `it` is in LDS for every wave; the slot of tile it-1 is free
-      const int page = pwin[tok0 / kPage - wbase];
-      const bool ok = page >= 0 && page < a.num_pages;
-      bad_page |= !ok;
-      const int nvalid = ok ? min(kTileTok, t1 - tok0) : 0;
-      if (it + kStages - 1 < ntiles) {
-        const int tok = tok0 + (kStages - 1) * kTileTok;
-        if (tok / kPage - wbase >= kPageWin) load_window(tok / kPage);   // splits > 2048 pages
-        const int pg = pwin[tok / kPage - wbase];
-        const int nxt = cur == 0 ? kStages - 1 : cur - 1;
-        tile_issue(pool, pg, pg >= 0 && pg < a.num_pages, tok, t1, ring0 + nxt * kTileBytes, wv,
-                   lane);
-      }
-      const uint32_t T = ring0 + cur * kTileBytes;
-      cur = cur == kStages - 1 ? 0 : cur + 1;
-
-      // ---- scores S^T (tokens x heads): two 16-token blocks, independent chains
-      f32x4_t sc[2] = {(f32x4_t){0.f, 0.f, 0.f, 0.f}, (f32x4_t){0.f, 0.f, 0.f, 0.f}};
-      {
-        uint32_t sa[4], ra[2];
+    const float mr = fmaxf(m_ref, -1e30f);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) sa[q] = opaque(T + soff[q]);
-#pragma unroll
-        for (int q = 0; q < 2; ++q) ra[q] = opaque(T + roff[q]);
-        auto lda = [&](int ks, int tb) {
-          return ks < kDc / 32 ? lds_b128(sa[ks & 3] + 256 * (ks >> 2) + 16384 * tb)
-                               : lds_b128(ra[ks - kDc / 32] + 2048 * tb);
-        };
-        // operands of step ks: A for both token blocks and, past kQReg, B from LDS
-        bf16x8_t af[2][3];
-        auto ld_step = [&](int ks, bf16x8_t (&dst)[3]) {
-          dst[0] = lda(ks, 0);
-          dst[1] = lda(ks, 1);
-          if (ks >= kQReg) dst[2] = lds_b128(qtail + (ks - kQReg) * 1024);
-        };
-        ld_step(0, af[0]);
-#pragma unroll
-        for (int ks = 0; ks < kKSteps; ++ks) {
-          if (ks + 1 < kKSteps) ld_step(ks + 1, af[(ks + 1) & 1]);
-          const bf16x8_t qb = ks < kQReg ? qf[ks < kQReg ? ks : 0] : af[ks & 1][2];
-          sc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks & 1][0], qb, sc[0], 0, 0, 0);
-          sc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks & 1][1], qb, sc[1], 0, 0, 0);
-        }
-      }
-
-      // ---- softmax weights of head n16 for tokens 16tb + 4g + i
-      if (nvalid < kTileTok) {
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (16 * tb + 4 * g + i >= nvalid) sc[tb][i] = -INFINITY;
-      }
-      float tmax = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                         fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * cs;
-      if (m_ref == -INFINITY) m_ref = tmax;      // first scored tile fixes the reference
-      seen = fmaxf(seen, tmax);
-      over |= tmax > m_ref + kHeadroom;
-      const float mr = fmaxf(m_ref, -1e30f);
-      float pv[8];
-      float psum = 0.f;
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pv[4 * tb + i] = __builtin_amdgcn_exp2f(fminf(fmaf(sc[tb][i], cs, -mr), kHeadroom));
-          psum += pv[4 * tb + i];
-        }
-      psum += __shfl_xor(psum, 16, 64);
-      psum += __shfl_xor(psum, 32, 64);
-      l_sum += psum;
-      const bf16x8_t pp = pack8(pv);   // k order t(g, j) = 16(j >> 2) + 4g + (j & 3)
-
-      // ---- O += P . C  (B operand via transposed LDS reads), four products ahead
-      {
-        s16x4_t bv[2][2][2];
-        auto load_grp = [&](int grp, s16x4_t (&dst)[2][2]) {
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int nb = 2 * grp + q;
-            const uint32_t p0 = T + toff[nb & 7] + 256 * (nb >> 3);
-            dst[q][0] = lds_tr16(p0);
-            dst[q][1] = lds_tr16(p0 + 16384);
-          }
-        };
-        load_grp(0, bv[0]);
-#pragma unroll
-        for (int grp = 0; grp < kColBlocks / 2; ++grp) {
-          if (grp + 1 < kColBlocks / 2) load_grp(grp + 1, bv[(grp + 1) & 1]);
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int nb = 2 * grp + q;
-            const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, bv[grp & 1][q]);
-            o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pp, bf, o[nb], 0, 0, 0);
-          }
-        }
-      }
+    for (int i = 0; i < 16; ++i) weight(sc, i, mr);
+    weight_sum();
+    bf16x8_t pp0 = pack8(p), pp1 = pack8(p + 8);   // k = 16kk + 8(j >> 2) + 4g2 + (j & 3)
+    nv0 = nv1; nv1 = nv2;
+    // ---- tile t: scores, then the products of tile t-1 with the weights of tile t between them
+    for (int t = 1; t < ntiles; ++t) {
+      wait_tile(t + 1 < ntiles ? 1 : 0);
+      lds_barrier();   // tile t is in LDS for every wave; the slot of tile t-2 is free
+      if (t + 2 < ntiles) nv2 = issue(t + 2);
+      sc = scores(ring0 + (t & 3) * kTileBytes);
+      mask(sc, nv0);
+      pv_product(ring0 + ((t - 1) & 3) * kTileBytes, pp0, pp1, true, sc, mr);
+      weight_sum();
+      pp0 = pack8(p);
+      pp1 = pack8(p + 8);
+      nv0 = nv1; nv1 = nv2;
     }
-    // every copy has landed (the last iteration waited for all of them)
-    if (!__syncthreads_or(over)) break;
-    m_ref = seen;              // run the unit again with the largest maximum as reference
+    pv_product(ring0 + ((ntiles - 1) & 3) * kTileBytes, pp0, pp1, false, sc, mr);
+    // every copy has landed (the last tile was waited for with vmcnt 0)
+    seen = fmaxf(seen, __shfl_xor(seen, 32, 64)) * cs;
+    if (!__syncthreads_or(seen > m_ref + kHeadroom)) break;
+    m_ref = seen;              // run the unit again with the largest score as reference
   }
   if (bad_page && tid == 0) set_err(a.err, ERR_PAGE);
 
-  // ---- epilogue: o_part = O / l, lse = (m + log2 l) ln 2; lane holds heads 4g + i
+  // ---- epilogue: o_part = O / l, lse = (m + log2 l) ln 2; lane holds heads 8(i>>2) + 4g2 + (i&3)
+  const float l_sum = l_part + __shfl_xor(l_part, 32, 64);
   const float inv = l_sum > 0.f ? 1.f / l_sum : 0.f;
-  if (g == 0) {
-    xch[wv][n16] = inv;
-    lse_out[n16] = l_sum > 0.f ? (m_ref + __log2f(l_sum)) * 0.6931471805599453f : -INFINITY;
+  if (g2 == 0) {
+    xch[wv][r32] = inv;
+    lse_out[r32] = l_sum > 0.f ? (m_ref + __log2f(l_sum)) * 0.6931471805599453f : -INFINITY;
   }
   __builtin_amdgcn_wave_barrier();
-  const float4 il = *reinterpret_cast<const float4*>(&xch[wv][4 * g]);
-  const float ilv[4] = {il.x, il.y, il.z, il.w};
+  float ilv[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 il = *reinterpret_cast<const float4*>(&xch[wv][8 * q + 4 * g2]);
+    ilv[4 * q] = il.x; ilv[4 * q + 1] = il.y; ilv[4 * q + 2] = il.z; ilv[4 * q + 3] = il.w;
+  }
 #pragma unroll
   for (int nb = 0; nb < kColBlocks; ++nb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o_out[(4 * g + i) * kDc + 16 * nb + n16] = o[nb][i] * ilv[i];
+    for (int i = 0; i < 16; ++i)
+      o_out[(8 * (i >> 2) + 4 * g2 + (i & 3)) * kDc + 32 * nb + r32] = o[nb][i] * ilv[i];
 }
 
 }  // namespace

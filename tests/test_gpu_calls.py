@@ -186,6 +186,7 @@ ATTN_CASES = [
     ("full", [1, 65, 1000, 4096], 4, 64),
     ("full", [3000, 130], 8, 64),
     ("full", [2], 5, 64),          # most splits empty
+    ("full", [33000], 1, 64),      # one split over 516 pages: the kernel's page-id window reloads
 ]
 
 
@@ -219,6 +220,37 @@ def test_decode_attention_partials(name, lens, S, page, path):
         assert_parity(got_o[b], ro, w.dtype, f"o_part b={b}")
         assert_parity(got_l[b], rl, w.dtype, f"lse_part b={b}")
     assert M.mla_device_error() == 0
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_attention_skips_bad_page(path):
+    """A table entry outside the pool is skipped (its tokens take no weight) and
+    flagged in the error word.  The bad page is the first one of the split, so
+    the MFMA kernel's first tile has no valid score."""
+    w = _wl("full", batch=1)
+    M.mla_set_kernel_path(path)
+    L = 200
+    lens = np.array([L], dtype=np.int32)
+    bt, total = I.page_table(w, lens)
+    bad = bt.copy()
+    bad[0, 0] = total + 7                                  # page 0 (tokens 0..63) is out of range
+    note(f"attention bad first page path={path}")
+    nh = w.n_heads
+    q_lat = device_tensor(torch, w, "q_lat_in", (1, nh, w.d_latent), 0.5).float().contiguous()
+    q_pe = device_tensor(torch, w, "q_pe_in", (1, nh, w.d_rope), 1.0).float().contiguous()
+    pool = device_tensor(torch, w, "pool", (total, 64, w.row))
+    o_part = torch.full((1, 1, nh, w.d_latent), 123.0, device="cuda")
+    lse_part = torch.full((1, 1, nh), 123.0, device="cuda")
+    M.mla_device_error(clear=True)
+    M.mla_decode_attention(_dims(w), q_lat, q_pe, pool, torch.tensor(bad, device="cuda"),
+                           torch.tensor(lens, device="cuda"), o_part, lse_part)
+    assert M.mla_device_error(clear=True) & 1
+    rows = I.to_f64(w, I.pool_rows(w, bt, 0, L))[64:]      # the tokens that remain
+    ro, rl = O.attention_partials(host_tensor(w, "q_lat_in", (1, nh, w.d_latent), 0.5)[0],
+                                  host_tensor(w, "q_pe_in", (1, nh, w.d_rope), 1.0)[0], rows, 1,
+                                  w.d_latent, w.d_rope, M.default_scale(_dims(w)), 64)
+    assert_parity(to_np(o_part)[0], ro, w.dtype, "o_part without the bad page")
+    assert_parity(to_np(lse_part)[0], rl, w.dtype, "lse_part without the bad page")
 
 
 def test_attention_is_page_table_invariant():

@@ -34,7 +34,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="full", help="full | lite | long (one layer each)")
+    p.add_argument("--workload", default="full",
+                   help="full | lite | long | full-cq (query compression) (one layer each)")
     p.add_argument("--splits", type=int, default=0, help="KV splits (0 = workload default)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="budget of the oracle timing on the host (0 disables it)")
@@ -74,7 +75,8 @@ def cpu_baseline(w, seconds: float):
         threads = len(os.sched_getaffinity(0))
     lens = I.seq_lengths(w)
     bt, _ = I.page_table(w, lens)
-    wt = {n: I.to_f64(w, I.weight_values(w, n, 0)) for n in I.WEIGHT_NAMES}
+    wt = {n: I.to_f64(w, I.weight_values(w, n, 0)) for n in w.weight_names}
+    cq = dict(w_dq=wt["w_dq"], w_uq=wt["w_uq"]) if w.d_cq else {}
     done, spent, b = 0, 0.0, 0
     while spent < seconds and b < w.batch:
         L = int(lens[b])
@@ -83,8 +85,8 @@ def cpu_baseline(w, seconds: float):
                                          count=w.hidden))
         t = time.perf_counter()
         rows[L - 1] = O.latent_rows(h[None], wt["w_dkv"], wt["w_kr"], [L - 1], w.rope_base)[0]
-        O.mla_decode_step(h, rows, wt["w_q"], wt["w_qr"], wt["w_uk"], wt["w_uv"], wt["w_o"],
-                          L - 1, w.n_heads, w.d_head, w.d_latent, w.d_rope, w.rope_base)
+        O.mla_decode_step(h, rows, wt.get("w_q"), wt["w_qr"], wt["w_uk"], wt["w_uv"], wt["w_o"],
+                          L - 1, w.n_heads, w.d_head, w.d_latent, w.d_rope, w.rope_base, **cq)
         spent += time.perf_counter() - t
         done += 1
         b += 1
@@ -179,7 +181,8 @@ def main():
         "data": "synthetic (seeded, counter-based generator; random-init weights)",
         "config": {"workload": f"{w.name}: one MLA decode layer, hidden {w.hidden}, n_h {w.n_heads}, "
                                f"d_h {w.d_head}, d_c {w.d_latent}, d_R {w.d_rope}, batch {B}, "
-                               f"context {int(lens.max())}, {S} KV splits, 64-token pages",
+                               f"context {int(lens.max())}, {S} KV splits, 64-token pages"
+                               + (f", query compression d_c' {w.d_cq}" if w.d_cq else ""),
                    "batch": B, "context": int(lens.max()), "num_splits": S},
         "latent_cache_GBps": achieved,
         "attention_us": attn_s * 1e6,

@@ -157,10 +157,30 @@ mla_status mla_absorb_out(const mla_dims* dims, const float* o_lat, const void* 
                           const void* w_o, int32_t batch, float* u, void* workspace,
                           size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Absorbed query with the query's low-rank compression (the MLA information
+ * flow of [Report] §3.1: h -> W_D^Q -> c^Q (d_c' = 1536 there) -> q^C, while the
+ * RoPE query q^R is still taken from h).  For each sequence b:
+ *   c^Q = W_DQ h_b (d_cq),  q^C_i = W_UQ,i c^Q,  q_lat[b,i,:] = W_UK,i^T q^C_i
+ *   q_pe[b,i,:] = RoPE(W_QR,i h_b, pos[b])
+ *   w_dq [d_cq, H] and w_uq [n_h*d_h, d_cq] in dtype (head i owns rows
+ *   i*d_h..(i+1)*d_h-1 of W_UQ); the rest as mla_absorb_q.  d_cq is even, in
+ *   [2, 65536]; c^Q is kept in fp32 inside the call.
+ * Workspace: at least mla_workspace_bytes_cq(dims, d_cq, batch) bytes,
+ * 256-byte aligned, used for c^Q and q^C (scratch for the duration of the call).
+ */
+mla_status mla_absorb_q_cq(const mla_dims* dims, int32_t d_cq, const void* h, const void* w_dq,
+                           const void* w_uq, const void* w_qr, const void* w_uk,
+                           const int32_t* pos, int32_t batch, float* q_lat, float* q_pe,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Workspace bytes needed by mla_absorb_q / mla_absorb_out for `batch` sequences
  * (0 if dims are invalid): the intermediate q^C or o (batch x n_h*d_h in dtype)
  * followed by fp32 partial sums of the projection GEMMs. */
 size_t mla_workspace_bytes(const mla_dims* dims, int32_t batch);
+/* Workspace bytes needed by mla_absorb_q_cq (0 if dims or d_cq are invalid):
+ * q^C as above, then c^Q (batch x d_cq fp32), then the GEMM partial sums. */
+size_t mla_workspace_bytes_cq(const mla_dims* dims, int32_t d_cq, int32_t batch);
 
 /* Workspace bytes needed by mla_append_latent for `n_rows` rows (0 if none is
  * needed or dims are invalid). */

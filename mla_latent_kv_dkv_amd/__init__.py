@@ -19,6 +19,7 @@ MLA_ABI_VERSION = 1
 MLA_F32, MLA_BF16 = 0, 1
 
 __all__ = ["MlaDims", "MlaError", "make_dims", "load", "mla_append_latent", "mla_absorb_q",
+           "mla_absorb_q_cq", "mla_workspace_bytes_cq",
            "mla_decode_attention", "mla_merge_lse", "mla_absorb_out", "mla_workspace_bytes",
            "mla_append_workspace_bytes", "mla_device_error", "mla_set_kernel_path",
            "mla_status_string", "LIB_PATH"]
@@ -52,17 +53,19 @@ _DIMS = ctypes.POINTER(MlaDims)
 _SIGS = {
     "mla_append_latent": [_DIMS, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _P, _I64, _P, _SZ, _P],
     "mla_absorb_q": [_DIMS, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P],
+    "mla_absorb_q_cq": [_DIMS, _I32, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P],
     "mla_decode_attention": [_DIMS, _P, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _P, _P, _P],
     "mla_merge_lse": [_DIMS, _P, _P, _I32, _I32, _P, _P, _P],
     "mla_absorb_out": [_DIMS, _P, _P, _P, _I32, _P, _P, _SZ, _P],
     "mla_workspace_bytes": [_DIMS, _I32],
+    "mla_workspace_bytes_cq": [_DIMS, _I32, _I32],
     "mla_append_workspace_bytes": [_DIMS, _I32],
     "mla_status_string": [_I32],
     "mla_abi_version": [],
     "mla_device_error": [ctypes.POINTER(_I32), _I32, _P],
     "mla_set_kernel_path": [_I32],
 }
-_RES = {"mla_workspace_bytes": _SZ, "mla_append_workspace_bytes": _SZ,
+_RES = {"mla_workspace_bytes": _SZ, "mla_workspace_bytes_cq": _SZ, "mla_append_workspace_bytes": _SZ,
         "mla_status_string": ctypes.c_char_p}
 
 
@@ -120,6 +123,10 @@ def mla_workspace_bytes(dims: MlaDims, batch: int) -> int:
     return int(load().mla_workspace_bytes(ctypes.byref(dims), batch))
 
 
+def mla_workspace_bytes_cq(dims: MlaDims, d_cq: int, batch: int) -> int:
+    return int(load().mla_workspace_bytes_cq(ctypes.byref(dims), d_cq, batch))
+
+
 def mla_append_workspace_bytes(dims: MlaDims, n_rows: int) -> int:
     return int(load().mla_append_workspace_bytes(ctypes.byref(dims), n_rows))
 
@@ -173,6 +180,27 @@ def mla_absorb_q(dims, h, w_q, w_qr, w_uk, pos, q_lat, q_pe, workspace, stream=N
     _check("mla_absorb_q", load().mla_absorb_q(
         ctypes.byref(dims), _ptr(h), _ptr(w_q), _ptr(w_qr), _ptr(w_uk), _ptr(pos), B, _ptr(q_lat),
         _ptr(q_pe), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def mla_absorb_q_cq(dims, h, w_dq, w_uq, w_qr, w_uk, pos, q_lat, q_pe, workspace, stream=None):
+    """q_lat = W_UK,i^T W_UQ,i W_DQ h and q_pe = RoPE(W_QR,i h, pos) for every head
+    (query low-rank compression; d_cq = w_dq.shape[0])."""
+    import torch
+    B, nh = h.shape[0], dims.n_heads
+    e = _elem(dims)
+    d_cq = w_dq.shape[0]
+    _expect(h, (B, dims.hidden), e, "h")
+    _expect(w_dq, (d_cq, dims.hidden), e, "w_dq")
+    _expect(w_uq, (nh * dims.d_head, d_cq), e, "w_uq")
+    _expect(w_qr, (nh * dims.d_rope, dims.hidden), e, "w_qr")
+    _expect(w_uk, (nh * dims.d_head, dims.d_latent), e, "w_uk")
+    _expect(pos, (B,), torch.int32, "pos")
+    _expect(q_lat, (B, nh, dims.d_latent), torch.float32, "q_lat")
+    _expect(q_pe, (B, nh, dims.d_rope), torch.float32, "q_pe")
+    _check("mla_absorb_q_cq", load().mla_absorb_q_cq(
+        ctypes.byref(dims), d_cq, _ptr(h), _ptr(w_dq), _ptr(w_uq), _ptr(w_qr), _ptr(w_uk),
+        _ptr(pos), B, _ptr(q_lat), _ptr(q_pe), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def mla_decode_attention(dims, q_lat, q_pe, pool, block_table, seq_lens, o_part, lse_part,

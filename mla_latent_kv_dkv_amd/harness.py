@@ -8,9 +8,9 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (make_dims, mla_absorb_out, mla_absorb_q, mla_append_latent,
+from . import (make_dims, mla_absorb_out, mla_absorb_q, mla_absorb_q_cq, mla_append_latent,
                mla_append_workspace_bytes, mla_decode_attention, mla_merge_lse,
-               mla_workspace_bytes)
+               mla_workspace_bytes, mla_workspace_bytes_cq)
 from . import inputs as I
 
 
@@ -36,7 +36,7 @@ class DeviceWorkload:
         self.seq_ids = torch.arange(B, dtype=torch.int32, device=self.dev)
         self.block_table = torch.tensor(self.bt_host, dtype=torch.int32, device=self.dev)
         self.weights = {}
-        for name in I.WEIGHT_NAMES:
+        for name in w.weight_names:
             t = torch.empty(w.weight_shape(name), dtype=self.dt, device=self.dev)
             I.fill_device(t, I.stream_key(w.seed, name, layer), 1.0 / np.sqrt(w.fan_in(name)))
             self.weights[name] = t
@@ -69,7 +69,10 @@ class DeviceWorkload:
         self.o_lat = torch.empty((B, nh, w.d_latent), dtype=f32, device=self.dev)
         self.lse = torch.empty((B, nh), dtype=torch.float32, device=self.dev)
         self.u = torch.empty((B, w.hidden), dtype=f32, device=self.dev)
-        self.ws = torch.empty(mla_workspace_bytes(self.dims, B), dtype=torch.uint8, device=self.dev)
+        ws_bytes = mla_workspace_bytes(self.dims, B)
+        if w.d_cq:
+            ws_bytes = max(ws_bytes, mla_workspace_bytes_cq(self.dims, w.d_cq, B))
+        self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=self.dev)
 
     def build_cache_from_h(self):
         """Append rows 0..L_b-2 of every sequence from h_ctx (the context before
@@ -90,8 +93,12 @@ class DeviceWorkload:
     # ---- the five calls of one decode step ------------------------------
     def absorb_q(self):
         W = self.weights
-        mla_absorb_q(self.dims, self.h, W["w_q"], W["w_qr"], W["w_uk"], self.pos, self.q_lat,
-                     self.q_pe, self.ws)
+        if self.w.d_cq:
+            mla_absorb_q_cq(self.dims, self.h, W["w_dq"], W["w_uq"], W["w_qr"], W["w_uk"],
+                            self.pos, self.q_lat, self.q_pe, self.ws)
+        else:
+            mla_absorb_q(self.dims, self.h, W["w_q"], W["w_qr"], W["w_uk"], self.pos, self.q_lat,
+                         self.q_pe, self.ws)
 
     def append(self):
         mla_append_latent(self.dims, self.h, self.weights["w_dkv"], self.weights["w_kr"],
@@ -120,7 +127,8 @@ class DeviceWorkload:
     # ---- host copies of the same inputs, for the oracle ------------------
     def host_weights(self):
         """fp64 host copies of the weights, regenerated from the seed."""
-        return {n: I.to_f64(self.w, I.weight_values(self.w, n, self.layer)) for n in I.WEIGHT_NAMES}
+        return {n: I.to_f64(self.w, I.weight_values(self.w, n, self.layer))
+                for n in self.w.weight_names}
 
     def host_h(self, b: int) -> np.ndarray:
         """fp64 hidden state of the decode token of sequence b."""

@@ -166,6 +166,7 @@ class Workload:
     cache_from_h: bool = False      # build the cache through the append call
     page_size: int = 64
     rope_base: float = 10000.0
+    d_cq: int = 0                   # query compression rank d_c' (0: q^C = W_Q h)
     notes: str = field(default="", compare=False)
 
     @property
@@ -179,12 +180,21 @@ class Workload:
     def fan_in(self, name: str) -> int:
         return {"w_q": self.hidden, "w_qr": self.hidden, "w_dkv": self.hidden,
                 "w_kr": self.hidden, "w_uk": self.d_latent, "w_uv": self.d_latent,
-                "w_o": self.n_heads * self.d_head}[name]
+                "w_o": self.n_heads * self.d_head, "w_dq": self.hidden,
+                "w_uq": self.d_cq}[name]
 
     def weight_shape(self, name: str) -> tuple:
         nh, dh, dc, dr, H = self.n_heads, self.d_head, self.d_latent, self.d_rope, self.hidden
         return {"w_q": (nh * dh, H), "w_qr": (nh * dr, H), "w_dkv": (dc, H), "w_kr": (dr, H),
-                "w_uk": (nh * dh, dc), "w_uv": (nh * dh, dc), "w_o": (H, nh * dh)}[name]
+                "w_uk": (nh * dh, dc), "w_uv": (nh * dh, dc), "w_o": (H, nh * dh),
+                "w_dq": (self.d_cq, H), "w_uq": (nh * dh, self.d_cq)}[name]
+
+    @property
+    def weight_names(self) -> tuple:
+        """The layer's weights: W_Q, or W_DQ and W_UQ when the query is compressed."""
+        if self.d_cq:
+            return ("w_dq", "w_uq") + WEIGHT_NAMES[1:]
+        return WEIGHT_NAMES
 
 
 WEIGHT_NAMES = ("w_q", "w_qr", "w_dkv", "w_kr", "w_uk", "w_uv", "w_o")
@@ -198,6 +208,13 @@ WORKLOADS = {
     "long": Workload("long", 5120, 128, 128, 512, 64, "bf16", 4, 131072, 1004, num_splits=64),
     "ragged": Workload("ragged", 5120, 128, 128, 512, 64, "bf16", 256, 0, 1005, num_splits=16,
                        layers=60, ragged=(512, 32768)),
+    # the same shapes with the query's low-rank compression (d_c' = 1536 at full size)
+    "tiny-cq": Workload("tiny-cq", 64, 4, 16, 32, 8, "f32", 1, 64, 1006, num_splits=1,
+                        permute_pages=False, cache_from_h=True, d_cq=24),
+    "lite-cq": Workload("lite-cq", 2048, 16, 128, 512, 64, "bf16", 32, 4096, 1007, num_splits=2,
+                        cache_from_h=True, d_cq=512),
+    "full-cq": Workload("full-cq", 5120, 128, 128, 512, 64, "bf16", 64, 4096, 1008, num_splits=4,
+                        d_cq=1536),
 }
 
 

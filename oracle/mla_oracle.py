@@ -27,7 +27,9 @@ Readings taken where the pages are silent (all inline formulas were lost):
     theta_k = base**(-2k/d_R); angles in fp64;
   * decode position t = L-1: the new token is appended first and attends to
     positions 0..L-1 inclusive;
-  * no query compression (q^C = W_Q h); no norm on the latent;
+  * q^C = W_Q h, or with the query's low-rank compression c^Q = W_DQ h and
+    q^C = W_UQ c^Q ([Report] §3.1 flow; no norm on c^Q, none is drawn); q^R is
+    taken from h either way; no norm on the latent;
   * head i owns rows i*d_h:(i+1)*d_h of W_Q, W_UK, W_UV (and i*d_R:(i+1)*d_R
     of W_QR) and columns i*d_h:(i+1)*d_h of W_O;
   * cache row = [c^KV (d_c) | k^R (d_R)]; paged in pages of ``page_size`` rows:
@@ -44,7 +46,8 @@ import math
 import numpy as np
 
 __all__ = [
-    "rope_theta", "rope", "latent_rows", "page_slot", "query_heads",
+    "rope_theta", "rope", "latent_rows", "page_slot", "query_heads", "compressed_query",
+    "query_heads_cq",
     "mla_decode_step", "mla_decode_step_absorbed", "split_bounds",
     "attention_partials", "merge_lse", "absorb_q", "absorb_out",
     "mla_cache_elems_per_token", "mha_cache_elems_per_token",
@@ -122,13 +125,31 @@ def query_heads(h_t, w_q, w_qr, pos: int, n_heads: int, d_head: int, d_rope: int
     return qc, qr
 
 
+def compressed_query(h_t, w_dq, w_uq):
+    """Query through its low-rank compression, the MLA information flow of
+    [Report] §3.1: c^Q = W_D^Q h_t (d_c', 1536 there), then q^C = W_U^Q c^Q
+    (n_h d_h; the up-projection's name follows W_U^K / W_U^V).  Returns q^C."""
+    c_q = _f64(w_dq) @ _f64(h_t)
+    return _f64(w_uq) @ c_q
+
+
+def query_heads_cq(h_t, w_dq, w_uq, w_qr, pos: int, n_heads: int, d_head: int, d_rope: int,
+                   base: float):
+    """q^C_i from the compressed query and q^R_i = RoPE(W_QR,i h_t, t): per the
+    same flow, the RoPE query is still taken from h_t.  Returns ([n_h, d_h], [n_h, d_R])."""
+    qc = compressed_query(h_t, w_dq, w_uq).reshape(n_heads, d_head)
+    qr = rope((_f64(w_qr) @ _f64(h_t)).reshape(n_heads, d_rope), pos, base)
+    return qc, qr
+
+
 def _default_scale(d_head: int, d_rope: int, scale):
     return 1.0 / math.sqrt(d_head + d_rope) if (scale is None or scale <= 0) else float(scale)
 
 
 # -------------------------------------------------- the definition (oracle) --
 def mla_decode_step(h_t, rows, w_q, w_qr, w_uk, w_uv, w_o, pos: int, n_heads: int,
-                    d_head: int, d_latent: int, d_rope: int, base: float, scale=None):
+                    d_head: int, d_latent: int, d_rope: int, base: float, scale=None,
+                    w_dq=None, w_uq=None):
     """Non-absorbed MLA decode for one sequence, fp64.
 
     ``rows`` [L, d_c + d_R] are the cached rows of logical positions 0..L-1 (the
@@ -138,12 +159,16 @@ def mla_decode_step(h_t, rows, w_q, w_qr, w_uk, w_uv, w_o, pos: int, n_heads: in
                 content-channel and RoPE-channel scores add up)
       p_i = softmax_j(tau * q_i . k_{j,i}),  o_i = sum_j p_ij v^C_{j,i}
     then u = W_O [o_1; ...; o_n_h].  Returns dict(u [H], o [n_h, d_h],
-    lse [n_h]) where lse_i = log sum_j exp(s_ij).
+    lse [n_h]) where lse_i = log sum_j exp(s_ij).  With ``w_dq``/``w_uq`` the
+    query goes through its compression (:func:`query_heads_cq`; ``w_q`` unused).
     """
     rows = _f64(rows)
     c, kr = rows[:, :d_latent], rows[:, d_latent:d_latent + d_rope]
     tau = _default_scale(d_head, d_rope, scale)
-    qc, qr = query_heads(h_t, w_q, w_qr, pos, n_heads, d_head, d_rope, base)
+    if w_dq is None:
+        qc, qr = query_heads(h_t, w_q, w_qr, pos, n_heads, d_head, d_rope, base)
+    else:
+        qc, qr = query_heads_cq(h_t, w_dq, w_uq, w_qr, pos, n_heads, d_head, d_rope, base)
     w_uk, w_uv = _f64(w_uk), _f64(w_uv)
     o = np.zeros((n_heads, d_head))
     lse = np.zeros(n_heads)
@@ -165,10 +190,14 @@ def mla_decode_step(h_t, rows, w_q, w_qr, w_uk, w_uv, w_o, pos: int, n_heads: in
 
 # ------------------------------------------------ absorbed fp64 companion --
 def absorb_q(h_t, w_q, w_qr, w_uk, pos: int, n_heads: int, d_head: int, d_latent: int,
-             d_rope: int, base: float):
+             d_rope: int, base: float, w_dq=None, w_uq=None):
     """Absorbed query: q_lat,i = W_UK,i^T q^C_i ([Report] §2.3: q.(W_UK c) is
-    regrouped as (W_UK^T q).c) and q_pe,i = q^R_i.  Returns ([n_h, d_c], [n_h, d_R])."""
-    qc, qr = query_heads(h_t, w_q, w_qr, pos, n_heads, d_head, d_rope, base)
+    regrouped as (W_UK^T q).c) and q_pe,i = q^R_i; q^C from W_Q, or from the
+    compression when ``w_dq``/``w_uq`` are given.  Returns ([n_h, d_c], [n_h, d_R])."""
+    if w_dq is None:
+        qc, qr = query_heads(h_t, w_q, w_qr, pos, n_heads, d_head, d_rope, base)
+    else:
+        qc, qr = query_heads_cq(h_t, w_dq, w_uq, w_qr, pos, n_heads, d_head, d_rope, base)
     w_uk = _f64(w_uk).reshape(n_heads, d_head, d_latent)
     q_lat = np.einsum("ihc,ih->ic", w_uk, qc)
     return q_lat, qr
@@ -199,12 +228,13 @@ def _latent_attention(q_lat, q_pe, rows, d_latent: int, d_rope: int, tau: float)
 
 def mla_decode_step_absorbed(h_t, rows, w_q, w_qr, w_uk, w_uv, w_o, pos: int,
                              n_heads: int, d_head: int, d_latent: int, d_rope: int,
-                             base: float, scale=None):
+                             base: float, scale=None, w_dq=None, w_uq=None):
     """Absorbed fp64 form of :func:`mla_decode_step` (same inputs): attention runs
     in the d_c-wide latent space and per-head K/V are never formed ([Report]
     §2.3).  Returns dict(u, q_lat, q_pe, o_lat, lse)."""
     tau = _default_scale(d_head, d_rope, scale)
-    q_lat, q_pe = absorb_q(h_t, w_q, w_qr, w_uk, pos, n_heads, d_head, d_latent, d_rope, base)
+    q_lat, q_pe = absorb_q(h_t, w_q, w_qr, w_uk, pos, n_heads, d_head, d_latent, d_rope, base,
+                           w_dq, w_uq)
     o_lat, lse = _latent_attention(q_lat, q_pe, rows, d_latent, d_rope, tau)
     u = absorb_out(o_lat, w_uv, w_o, n_heads, d_head, d_latent)
     return {"u": u, "q_lat": q_lat, "q_pe": q_pe, "o_lat": o_lat, "lse": lse}

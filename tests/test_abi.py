@@ -110,6 +110,20 @@ def test_argument_checks():
     assert lib.mla_absorb_q(ctypes.byref(d), P, P, P, P, P, 4, P, P, misaligned, 1 << 20,
                             None) == -4
     assert lib.mla_absorb_out(ctypes.byref(d), P, P, P, 4, P, misaligned, 1 << 20, None) == -4
+    # compressed query: rank, pointers, workspace
+    lib.mla_absorb_q_cq.argtypes = [ctypes.POINTER(M.MlaDims), ctypes.c_int32] + \
+        [ctypes.c_void_p] * 6 + [ctypes.c_int32] + [ctypes.c_void_p] * 3 + [ctypes.c_size_t,
+                                                                              ctypes.c_void_p]
+    cq = ctypes.byref(d)
+    assert lib.mla_absorb_q_cq(cq, 0, P, P, P, P, P, P, 4, P, P, P, 1 << 20, None) == -2
+    assert lib.mla_absorb_q_cq(cq, 7, P, P, P, P, P, P, 4, P, P, P, 1 << 20, None) == -2
+    assert lib.mla_absorb_q_cq(cq, 24, P, None, P, P, P, P, 4, P, P, P, 1 << 20, None) == -1
+    assert lib.mla_absorb_q_cq(cq, 24, P, P, P, P, P, P, 4, P, P, P, 16, None) == -4
+    assert lib.mla_absorb_q_cq(cq, 24, P, P, P, P, P, P, 4, P, P, misaligned, 1 << 20, None) == -4
+    assert lib.mla_absorb_q_cq(cq, 24, None, None, None, None, None, None, 0, None, None, None,
+                               0, None) == 0
+    assert M.mla_workspace_bytes_cq(d, 24, 8) >= M.mla_workspace_bytes(d, 8) + 8 * 24 * 4
+    assert M.mla_workspace_bytes_cq(d, 0, 8) == 0 and M.mla_workspace_bytes_cq(d, 5, 8) == 0
     # empty batches are no-ops that never touch the pointers
     assert lib.mla_absorb_q(ctypes.byref(d), None, None, None, None, None, 0, None, None, None, 0,
                             None) == 0

@@ -18,11 +18,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-DIMS = {
-    "tiny": I.WORKLOADS["tiny"],
-    "lite": I.WORKLOADS["lite"],
-    "full": I.WORKLOADS["full"],
-}
+DIMS = {n: I.WORKLOADS[n] for n in ("tiny", "lite", "full", "tiny-cq", "lite-cq", "full-cq")}
 PATHS = [0, 1]
 
 
@@ -172,6 +168,38 @@ def test_absorb_q(name, path):
     for b in range(B):
         ql, qp = O.absorb_q(hh[b], hw["w_q"], hw["w_qr"], hw["w_uk"], int(pos_np[b]), w.n_heads,
                             w.d_head, w.d_latent, w.d_rope, w.rope_base)
+        ref_lat.append(ql)
+        ref_pe.append(qp)
+    assert_parity(to_np(q_lat), np.stack(ref_lat), w.dtype, "q_lat")
+    assert_parity(to_np(q_pe), np.stack(ref_pe), w.dtype, "q_pe")
+
+
+@pytest.mark.parametrize("name", ["tiny-cq", "lite-cq", "full-cq"])
+@pytest.mark.parametrize("path", PATHS)
+def test_absorb_q_cq(name, path):
+    """Query through its low-rank compression (c^Q = W_DQ h, q^C = W_UQ c^Q)."""
+    w = _wl(name)
+    B = 5
+    M.mla_set_kernel_path(path)
+    note(f"absorb_q_cq {name} path={path}")
+    sh = {n: w.weight_shape(n) for n in ("w_dq", "w_uq", "w_qr", "w_uk")}
+    std = {n: 1 / math.sqrt(w.fan_in(n)) for n in sh}
+    dev = {n: device_tensor(torch, w, n, sh[n], std[n]) for n in sh}
+    h = device_tensor(torch, w, "h_q", (B, w.hidden))
+    pos_np = np.array([0, 1, 63, 4095, 131071][:B], dtype=np.int32)
+    q_lat = torch.empty((B, w.n_heads, w.d_latent), dtype=torch.float32, device="cuda")
+    q_pe = torch.empty((B, w.n_heads, w.d_rope), dtype=torch.float32, device="cuda")
+    d = _dims(w)
+    ws = torch.empty(M.mla_workspace_bytes_cq(d, w.d_cq, B), dtype=torch.uint8, device="cuda")
+    M.mla_absorb_q_cq(d, h, dev["w_dq"], dev["w_uq"], dev["w_qr"], dev["w_uk"],
+                      torch.tensor(pos_np, device="cuda"), q_lat, q_pe, ws)
+    hh = host_tensor(w, "h_q", (B, w.hidden))
+    hw = {n: host_tensor(w, n, sh[n], std[n]) for n in sh}
+    ref_lat, ref_pe = [], []
+    for b in range(B):
+        ql, qp = O.absorb_q(hh[b], None, hw["w_qr"], hw["w_uk"], int(pos_np[b]), w.n_heads,
+                            w.d_head, w.d_latent, w.d_rope, w.rope_base, w_dq=hw["w_dq"],
+                            w_uq=hw["w_uq"])
         ref_lat.append(ql)
         ref_pe.append(qp)
     assert_parity(to_np(q_lat), np.stack(ref_lat), w.dtype, "q_lat")

@@ -42,15 +42,16 @@ def _check(dw: DeviceWorkload, seqs, full_def=(), hw=None):
     for b in seqs:
         L = int(dw.lens[b])
         rows = _context_rows(dw, b, hw)
-        a = O.mla_decode_step_absorbed(dw.host_h(b), rows, hw["w_q"], hw["w_qr"], hw["w_uk"],
+        cq = dict(w_dq=hw["w_dq"], w_uq=hw["w_uq"]) if w.d_cq else {}
+        a = O.mla_decode_step_absorbed(dw.host_h(b), rows, hw.get("w_q"), hw["w_qr"], hw["w_uk"],
                                        hw["w_uv"], hw["w_o"], L - 1, w.n_heads, w.d_head,
-                                       w.d_latent, w.d_rope, w.rope_base)
+                                       w.d_latent, w.d_rope, w.rope_base, **cq)
         for k in ref:
             ref[k].append(a[k])
         if b in full_def:
-            nd = O.mla_decode_step(dw.host_h(b), rows, hw["w_q"], hw["w_qr"], hw["w_uk"],
+            nd = O.mla_decode_step(dw.host_h(b), rows, hw.get("w_q"), hw["w_qr"], hw["w_uk"],
                                    hw["w_uv"], hw["w_o"], L - 1, w.n_heads, w.d_head, w.d_latent,
-                                   w.d_rope, w.rope_base)
+                                   w.d_rope, w.rope_base, **cq)
             assert_parity(got["u"][b], nd["u"], w.dtype, f"u (definition) b={b}")
     for k in ref:
         assert_parity(got[k][list(seqs)], np.stack(ref[k]), w.dtype, f"{k} seqs={list(seqs)}")
@@ -86,6 +87,19 @@ def test_step_full_shape():
     dw.step()
     torch.cuda.synchronize()
     _check(dw, [0, 31, 63], full_def=[31])
+    assert M.mla_device_error() == 0
+
+
+@pytest.mark.parametrize("name", ["tiny-cq", "lite-cq", "full-cq"])
+def test_step_compressed_query(name):
+    """The step with the query's low-rank compression (c^Q = W_DQ h, q^C = W_UQ c^Q)."""
+    w = I.WORKLOADS[name]
+    note(f"step {name}")
+    dw = DeviceWorkload(w)
+    dw.step()
+    torch.cuda.synchronize()
+    seqs = list(range(w.batch)) if w.batch <= 4 else [0, w.batch // 2, w.batch - 1]
+    _check(dw, seqs, full_def=seqs[:1])
     assert M.mla_device_error() == 0
 
 

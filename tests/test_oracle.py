@@ -262,6 +262,43 @@ def test_absorb_q_brute_force():
         np.testing.assert_allclose(q_pe[i], _complex_rope(qr, 9, 10000.0), atol=1e-12)
 
 
+# -------------------------------------------------- query compression --
+@pytest.mark.parametrize("H,nh,dh,dc,dr,dcq,L", [(64, 4, 16, 32, 8, 24, 40), (48, 3, 8, 16, 4, 6, 9)])
+def test_compressed_query_equals_the_composed_projection(H, nh, dh, dc, dr, dcq, L):
+    """W_UQ (W_DQ h) = (W_UQ W_DQ) h: the compressed query path must reproduce the
+    uncompressed one whose W_Q is the product of the two factors, through the
+    absorbed query and the whole non-absorbed step (a transposed factor, a wrong
+    head split of W_UQ or a RoPE query taken from c^Q instead of h all fail)."""
+    rng = _rng(70 + L)
+    w = _weights(rng, H, nh, dh, dc, dr)
+    w_dq = rng.normal(size=(dcq, H)) / math.sqrt(H)
+    w_uq = rng.normal(size=(nh * dh, dcq)) / math.sqrt(dcq)
+    h_ctx = rng.normal(size=(L, H))
+    rows = O.latent_rows(h_ctx, w["w_dkv"], w["w_kr"], np.arange(L), 10000.0)
+    ql_c, qp_c = O.absorb_q(h_ctx[-1], None, w["w_qr"], w["w_uk"], L - 1, nh, dh, dc, dr, 10000.0,
+                            w_dq=w_dq, w_uq=w_uq)
+    ql, qp = O.absorb_q(h_ctx[-1], w_uq @ w_dq, w["w_qr"], w["w_uk"], L - 1, nh, dh, dc, dr,
+                        10000.0)
+    np.testing.assert_allclose(ql_c, ql, rtol=1e-11, atol=1e-12)
+    np.testing.assert_array_equal(qp_c, qp)
+    args = (h_ctx[-1], rows, None, w["w_qr"], w["w_uk"], w["w_uv"], w["w_o"], L - 1, nh, dh, dc,
+            dr, 10000.0)
+    a = O.mla_decode_step(*args, w_dq=w_dq, w_uq=w_uq)
+    b = O.mla_decode_step(h_ctx[-1], rows, w_uq @ w_dq, *args[3:])
+    np.testing.assert_allclose(a["u"], b["u"], rtol=1e-10, atol=1e-12)
+    c = O.mla_decode_step_absorbed(*args, w_dq=w_dq, w_uq=w_uq)
+    np.testing.assert_allclose(c["u"], a["u"], rtol=1e-10, atol=1e-12)
+
+
+def test_compressed_query_rank_one_closed_form():
+    """d_c' = 1: c^Q is the scalar w.h and q^C = (w.h) u, so q^C is a multiple of u."""
+    rng = _rng(77)
+    H, nh, dh = 10, 2, 3
+    wd, u, h = rng.normal(size=(1, H)), rng.normal(size=(nh * dh, 1)), rng.normal(size=H)
+    np.testing.assert_allclose(O.compressed_query(h, wd, u), float(wd[0] @ h) * u[:, 0],
+                               rtol=1e-13, atol=1e-14)
+
+
 def test_absorb_out_brute_force():
     rng = _rng(51)
     H, nh, dh, dc = 5, 3, 2, 4

@@ -165,7 +165,8 @@ mla_status mla_absorb_out(const mla_dims* dims, const float* o_lat, const void* 
  *   q_pe[b,i,:] = RoPE(W_QR,i h_b, pos[b])
  *   w_dq [d_cq, H] and w_uq [n_h*d_h, d_cq] in dtype (head i owns rows
  *   i*d_h..(i+1)*d_h-1 of W_UQ); the rest as mla_absorb_q.  d_cq is even, in
- *   [2, 65536]; c^Q is kept in fp32 inside the call.
+ *   [2, 65536]; inside the call c^Q and q^C are held in dtype (as q^C is in
+ *   mla_absorb_q).
  * Workspace: at least mla_workspace_bytes_cq(dims, d_cq, batch) bytes,
  * 256-byte aligned, used for c^Q and q^C (scratch for the duration of the call).
  */
@@ -179,7 +180,7 @@ mla_status mla_absorb_q_cq(const mla_dims* dims, int32_t d_cq, const void* h, co
  * followed by fp32 partial sums of the projection GEMMs. */
 size_t mla_workspace_bytes(const mla_dims* dims, int32_t batch);
 /* Workspace bytes needed by mla_absorb_q_cq (0 if dims or d_cq are invalid):
- * q^C as above, then c^Q (batch x d_cq fp32), then the GEMM partial sums. */
+ * q^C as above, then c^Q (batch x d_cq in dtype), then the GEMM partial sums. */
 size_t mla_workspace_bytes_cq(const mla_dims* dims, int32_t d_cq, int32_t batch);
 
 /* Workspace bytes needed by mla_append_latent for `n_rows` rows (0 if none is

@@ -78,20 +78,22 @@ mla::GemmArgs qproj_args(const mla_dims* d, int batch) {
   return a;
 }
 
-// Compressed query: c^Q = W_DQ h (fp32 out), q^C = W_UQ c^Q (fp32 in), and the
-// RoPE query on its own (every column goes to the rope branch of EPI_QPROJ).
-mla::GemmArgs dq_args(const mla_dims* d, int d_cq, int batch) {
+// Compressed query, first product: [c^Q | q^R] = h [W_DQ; W_QR]^T, RoPE on the
+// q^R columns (the q^C split of EPI_QPROJ with n_split = d_cq); c^Q in dtype.
+mla::GemmArgs cqproj_args(const mla_dims* d, int d_cq, int batch) {
   const bool bf16 = d->dtype == MLA_BF16;
   mla::GemmArgs a{};
   a.ldx_m = d->hidden; a.ldx_k = 1;
   a.n_split = d_cq;
   a.ldw_n = d->hidden; a.ldw_k = 1;
-  a.M = batch; a.N = d_cq; a.K = d->hidden; a.batch = 1;
-  a.epi = mla::EPI_STORE; a.x_f32 = !bf16; a.y_f32 = 1;
-  a.ldy = d_cq;
+  a.M = batch; a.N = d_cq + d->n_heads * d->d_rope; a.K = d->hidden; a.batch = 1;
+  a.epi = mla::EPI_QPROJ; a.x_f32 = !bf16; a.y_f32 = !bf16;
+  a.ldy = d_cq; a.d_rope = d->d_rope;
+  a.log_base = std::log(static_cast<double>(d->rope_base));
   return a;
 }
 
+// second product: q^C = W_UQ c^Q (c^Q and q^C in dtype)
 mla::GemmArgs uq_args(const mla_dims* d, int d_cq, int batch) {
   const bool bf16 = d->dtype == MLA_BF16;
   const int64_t nhdh = static_cast<int64_t>(d->n_heads) * d->d_head;
@@ -100,21 +102,8 @@ mla::GemmArgs uq_args(const mla_dims* d, int d_cq, int batch) {
   a.n_split = static_cast<int>(nhdh);
   a.ldw_n = d_cq; a.ldw_k = 1;
   a.M = batch; a.N = static_cast<int>(nhdh); a.K = d_cq; a.batch = 1;
-  a.epi = mla::EPI_STORE; a.x_f32 = 1; a.y_f32 = !bf16;
+  a.epi = mla::EPI_STORE; a.x_f32 = !bf16; a.y_f32 = !bf16;
   a.ldy = nhdh;
-  return a;
-}
-
-mla::GemmArgs qr_args(const mla_dims* d, int batch) {
-  const bool bf16 = d->dtype == MLA_BF16;
-  mla::GemmArgs a{};
-  a.ldx_m = d->hidden; a.ldx_k = 1;
-  a.n_split = 0;
-  a.ldw_n = d->hidden; a.ldw_k = 1;
-  a.M = batch; a.N = d->n_heads * d->d_rope; a.K = d->hidden; a.batch = 1;
-  a.epi = mla::EPI_QPROJ; a.x_f32 = !bf16; a.y_f32 = !bf16;
-  a.ldy = 0; a.d_rope = d->d_rope;
-  a.log_base = std::log(static_cast<double>(d->rope_base));
   return a;
 }
 
@@ -197,8 +186,8 @@ hipError_t run_gemm(const mla_dims* d, const mla::GemmArgs& a, void* partial, si
 
 bool cq_ok(int d_cq) { return d_cq >= 2 && d_cq <= 65536 && (d_cq & 1) == 0; }
 
-size_t cq_bytes(int d_cq, int batch) {
-  return align256(static_cast<size_t>(batch) * static_cast<size_t>(d_cq) * sizeof(float));
+size_t cq_bytes(const mla_dims* d, int d_cq, int batch) {
+  return align256(static_cast<size_t>(batch) * static_cast<size_t>(d_cq) * elem_bytes(d));
 }
 
 }  // namespace
@@ -223,14 +212,14 @@ const char* mla_status_string(int32_t s) {
 
 size_t mla_workspace_bytes_cq(const mla_dims* d, int32_t d_cq, int32_t batch) {
   if (check_dims(d) != MLA_OK || batch < 0 || !cq_ok(d_cq)) return 0;
-  // [q^C, batch x n_h*d_h in dtype][c^Q, batch x d_cq fp32][fp32 K-split partials]
+  // [q^C, batch x n_h*d_h in dtype][c^Q, batch x d_cq in dtype][fp32 K-split partials]
   size_t part = 0;
   if (batch > 0) {
-    for (const mla::GemmArgs& a : {dq_args(d, d_cq, batch), uq_args(d, d_cq, batch),
-                                   qr_args(d, batch), uk_args(d, batch)})
+    for (const mla::GemmArgs& a : {cqproj_args(d, d_cq, batch), uq_args(d, d_cq, batch),
+                                   uk_args(d, batch)})
       part = std::max(part, partial_bytes(d, a));
   }
-  return act_bytes(d, batch) + cq_bytes(d_cq, batch) + part + 256;
+  return act_bytes(d, batch) + cq_bytes(d, d_cq, batch) + part + 256;
 }
 
 size_t mla_workspace_bytes(const mla_dims* d, int32_t batch) {
@@ -323,21 +312,17 @@ mla_status mla_absorb_q_cq(const mla_dims* d, int32_t d_cq, const void* h, const
     return MLA_ERR_WORKSPACE;
   char* qc = static_cast<char*>(ws);
   char* cq = qc + act_bytes(d, batch);
-  char* part = cq + cq_bytes(d_cq, batch);
-  const size_t pbytes = ws_bytes - act_bytes(d, batch) - cq_bytes(d_cq, batch);
-  // 1) c^Q = W_DQ h (fp32)
-  mla::GemmArgs a = dq_args(d, d_cq, batch);
-  a.x = h; a.w1 = w_dq; a.w2 = w_dq; a.y = cq;
+  char* part = cq + cq_bytes(d, d_cq, batch);
+  const size_t pbytes = ws_bytes - act_bytes(d, batch) - cq_bytes(d, d_cq, batch);
+  // 1) [c^Q | q^R] = h [W_DQ; W_QR]^T, RoPE on the q^R columns; c^Q -> workspace
+  mla::GemmArgs a = cqproj_args(d, d_cq, batch);
+  a.x = h; a.w1 = w_dq; a.w2 = w_qr; a.y = cq; a.y2 = q_pe; a.pos = pos;
   if (run_gemm(d, a, part, pbytes, stream) != hipSuccess) return MLA_ERR_HIP;
   // 2) q^C = W_UQ c^Q -> workspace
   mla::GemmArgs u = uq_args(d, d_cq, batch);
   u.x = cq; u.w1 = w_uq; u.w2 = w_uq; u.y = qc;
   if (run_gemm(d, u, part, pbytes, stream) != hipSuccess) return MLA_ERR_HIP;
-  // 3) q_pe = RoPE(W_QR h)
-  mla::GemmArgs r = qr_args(d, batch);
-  r.x = h; r.w1 = w_qr; r.w2 = w_qr; r.y2 = q_pe; r.pos = pos;
-  if (run_gemm(d, r, part, pbytes, stream) != hipSuccess) return MLA_ERR_HIP;
-  // 4) q_lat[b, i, :] = W_UK,i^T q^C[b, i, :] per head i
+  // 3) q_lat[b, i, :] = W_UK,i^T q^C[b, i, :] per head i
   mla::GemmArgs g = uk_args(d, batch);
   g.x = qc; g.w1 = w_uk; g.w2 = w_uk; g.y = q_lat;
   return hip_status(run_gemm(d, g, part, pbytes, stream));

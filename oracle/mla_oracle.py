@@ -50,7 +50,9 @@ __all__ = [
     "query_heads_cq",
     "mla_decode_step", "mla_decode_step_absorbed", "split_bounds",
     "attention_partials", "merge_lse", "absorb_q", "absorb_out",
-    "mla_cache_elems_per_token", "mha_cache_elems_per_token",
+    "mla_cache_elems_per_token", "mha_cache_elems_per_token", "E4M3_MAX", "e4m3_values",
+    "e4m3_encode", "fp8_row_scale_exponent", "bf16_bits", "fp8_quantize_row",
+    "fp8_dequantize_row", "fp8_page_bytes", "fp8_page_image",
 ]
 
 
@@ -272,6 +274,105 @@ def merge_lse(o_parts, lse_parts):
     o = (w[..., None] * o_parts).sum(axis=0) / np.where(z > 0, z, 1.0)[..., None]
     lse = np.where(z > 0, safe + np.log(np.where(z > 0, z, 1.0)), -np.inf)
     return o, lse
+
+
+# ------------------------------------------------------------- FP8 cache --
+# [Report] §4.2: inference quantizes the (already 576-wide) latent cache to about
+# 6 bits per element; the scheme is not on the pages.  The reading used here:
+# c^KV in e4m3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, largest
+# finite 448, no infinities) with one power-of-two scale per row; k^R in bf16.
+E4M3_MAX = 448.0
+
+
+def e4m3_values() -> np.ndarray:
+    """Value of every e4m3 byte 0..255 from the format's definition (NaN for the
+    two NaN codes 0x7f, 0xff): exponent field 0 is subnormal, m * 2^-9."""
+    out = np.empty(256)
+    for code in range(256):
+        sign = -1.0 if code & 0x80 else 1.0
+        e, m = (code >> 3) & 0xF, code & 0x7
+        if e == 0xF and m == 0x7:
+            out[code] = np.nan
+        elif e == 0:
+            out[code] = sign * m * 2.0 ** -9
+        else:
+            out[code] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return out
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Round-to-nearest-even of each value (|x| <= 448) to its e4m3 byte: the
+    nearest of the finite codes, ties to the code with an even mantissa."""
+    x = np.asarray(x, dtype=np.float64)
+    vals = e4m3_values()
+    pos = np.array([c for c in range(128) if np.isfinite(vals[c])])   # 0x00..0x7e, increasing
+    pv = vals[pos]
+    a = np.abs(x)
+    if np.any(a > E4M3_MAX):
+        raise ValueError("value beyond the e4m3 range")
+    hi = np.searchsorted(pv, a, side="left")          # first code with value >= a
+    hi = np.minimum(hi, len(pv) - 1)
+    lo = np.maximum(hi - 1, 0)
+    dlo, dhi = a - pv[lo], pv[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (pos[hi] % 2 == 0))
+    pick_hi |= pv[hi] == a
+    code = np.where(pick_hi, pos[hi], pos[lo])
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def fp8_row_scale_exponent(amax: float) -> int:
+    """Exponent e of the row scale 2^e: the smallest e with amax / 2^e <= 448
+    (448 = 0.875 * 2^9).  With amax = m 2^x, m in [0.5, 1): e = x - 9, plus one
+    when m > 0.875; amax = 0 gives e = 0.  Clamped to [-126, 127]."""
+    if amax == 0.0:
+        return 0
+    m, x = math.frexp(amax)
+    e = x - 9 + (1 if m > 0.875 else 0)
+    return int(min(max(e, -126), 127))
+
+
+def bf16_bits(x) -> np.ndarray:
+    """bf16 bit patterns (round to nearest even) of fp32 values."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def fp8_quantize_row(row_f32, d_latent: int):
+    """One cache row [c (d_c) | k^R (d_R)] given in fp32 -> (e4m3 codes of c,
+    bf16 bits of k^R, scale exponent e): codes = RNE_e4m3(c / 2^e)."""
+    row = np.asarray(row_f32, dtype=np.float32)
+    c = row[:d_latent].astype(np.float64)
+    e = fp8_row_scale_exponent(float(np.abs(c).max()) if c.size else 0.0)
+    codes = e4m3_encode(np.ldexp(c, -e))             # exact: a power-of-two scale
+    return codes, bf16_bits(row[d_latent:]), e
+
+
+def fp8_dequantize_row(codes, kr_bits, e: int) -> np.ndarray:
+    """fp64 row [c^ | k^R] of a quantized row: c^ = code value * 2^e."""
+    c = np.ldexp(e4m3_values()[np.asarray(codes)], e)
+    kr = (np.asarray(kr_bits, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+    return np.concatenate([c, kr])
+
+
+def fp8_page_bytes(page_size: int, d_latent: int, d_rope: int) -> int:
+    """Bytes of one FP8 page: page_size rows of [d_c e4m3 bytes | d_R bf16], then
+    page_size fp32 row scales."""
+    return page_size * (d_latent + 2 * d_rope) + 4 * page_size
+
+
+def fp8_page_image(rows_f32, d_latent: int, d_rope: int) -> np.ndarray:
+    """Byte image of one FP8 page holding ``rows_f32`` [n <= page_size, d_c + d_R]
+    in slots 0..n-1 (other slots zero; page_size = n)."""
+    n = len(rows_f32)
+    rb = d_latent + 2 * d_rope
+    img = np.zeros(fp8_page_bytes(n, d_latent, d_rope), dtype=np.uint8)
+    for r, row in enumerate(rows_f32):
+        codes, kr, e = fp8_quantize_row(row, d_latent)
+        img[r * rb:r * rb + d_latent] = codes
+        img[r * rb + d_latent:(r + 1) * rb] = kr.view(np.uint8)
+        img[n * rb + 4 * r:n * rb + 4 * r + 4] = np.array([2.0 ** e], dtype=np.float32).view(np.uint8)
+    return img
 
 
 # ------------------------------------------------------------ cache sizes --

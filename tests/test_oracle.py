@@ -381,3 +381,58 @@ def test_merge_lse_brute_force():
         ref = sum(ws[s] * o_s[s, i] for s in range(3)) / sum(ws)
         np.testing.assert_allclose(o[i], ref, rtol=1e-12)
         assert abs(lse[i] - math.log(sum(ws))) < 1e-12
+
+
+# ------------------------------------------------------------- FP8 cache --
+def test_e4m3_table_matches_torch_float8():
+    torch = pytest.importorskip("torch")
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    got = O.e4m3_values()
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+    assert np.nanmax(got) == O.E4M3_MAX == 448.0
+
+
+def test_e4m3_encode_matches_torch_cast_including_ties():
+    torch = pytest.importorskip("torch")
+    rng = _rng(80)
+    x = np.concatenate([rng.normal(size=20000) * s for s in (1e-3, 0.05, 1.0, 30.0, 120.0)])
+    x = x[np.abs(x) <= 448.0]
+    fin = np.unique(O.e4m3_values()[np.isfinite(O.e4m3_values())])
+    mids = (fin[1:] + fin[:-1]) / 2                          # exact ties
+    x = np.concatenate([x, mids, -mids, [0.0, -0.0, 448.0, 2.0 ** -9, 2.0 ** -10]]).astype(np.float32)
+    want = torch.tensor(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(O.e4m3_encode(x), want)
+
+
+def test_fp8_scale_is_the_smallest_power_of_two_that_fits():
+    rng = _rng(81)
+    for amax in np.concatenate([np.exp(rng.uniform(-20, 20, 2000)), [448.0, 224.0, 448.0001, 1.0]]):
+        e = O.fp8_row_scale_exponent(float(amax))
+        assert amax / 2.0 ** e <= 448.0
+        assert amax / 2.0 ** (e - 1) > 448.0                  # e - 1 would overflow the format
+    assert O.fp8_row_scale_exponent(0.0) == 0
+
+
+def test_bf16_bits_match_torch():
+    torch = pytest.importorskip("torch")
+    x = _rng(82).normal(size=5000).astype(np.float32) * 7.0
+    want = torch.tensor(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(O.bf16_bits(x), want)
+
+
+def test_fp8_row_roundtrip_and_page_layout():
+    rng = _rng(83)
+    dc, dr = 32, 8
+    rows = (rng.normal(size=(5, dc + dr)) * np.array([[1e-3], [1.0], [50.0], [0.0], [3.0]])).astype(np.float32)
+    img = O.fp8_page_image(rows, dc, dr)
+    assert img.size == O.fp8_page_bytes(5, dc, dr) == 5 * (dc + 2 * dr) + 20
+    for r, row in enumerate(rows):
+        codes, kr, e = O.fp8_quantize_row(row, dc)
+        back = O.fp8_dequantize_row(codes, kr, e)
+        # every latent value lands on the nearest multiple of its e4m3 spacing
+        spacing = np.ldexp(2.0 ** (np.maximum(np.floor(np.log2(np.maximum(np.abs(row[:dc]) / 2.0 ** e, 2.0 ** -6))), -6) - 3), e)
+        assert np.all(np.abs(back[:dc] - row[:dc]) <= spacing / 2 + 1e-30)
+        np.testing.assert_allclose(back[dc:], row[dc:], rtol=2.0 ** -8)
+        assert img[5 * (dc + 2 * dr) + 4 * r:5 * (dc + 2 * dr) + 4 * r + 4].view(np.float32)[0] == 2.0 ** e
+    assert O.fp8_page_bytes(64, 512, 64) == 41216

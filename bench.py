@@ -35,7 +35,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="full",
-                   help="full | lite | long | full-cq (query compression) (one layer each)")
+                   help="full | lite | long | full-cq (query compression) | full-fp8 (FP8 latent "
+                        "pool) (one layer each)")
     p.add_argument("--splits", type=int, default=0, help="KV splits (0 = workload default)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="budget of the oracle timing on the host (0 disables it)")
@@ -80,11 +81,15 @@ def cpu_baseline(w, seconds: float):
     done, spent, b = 0, 0.0, 0
     while spent < seconds and b < w.batch:
         L = int(lens[b])
-        rows = I.to_f64(w, I.pool_rows(w, bt, b, L))
+        fp8 = w.cache == "fp8"
+        rows = I.pool_rows(w, bt, b, L, f32=fp8).astype(np.float64) if fp8 else I.to_f64(
+            w, I.pool_rows(w, bt, b, L))
         h = I.to_f64(w, I.tensor_values(w, "h_dec", None, 1.0, 0, start=b * w.hidden,
                                          count=w.hidden))
         t = time.perf_counter()
         rows[L - 1] = O.latent_rows(h[None], wt["w_dkv"], wt["w_kr"], [L - 1], w.rope_base)[0]
+        if fp8:     # the cache as the FP8 pool holds it
+            rows = np.stack([O.fp8_dequantize_row(*O.fp8_quantize_row(r, w.d_latent)) for r in rows])
         O.mla_decode_step(h, rows, wt.get("w_q"), wt["w_qr"], wt["w_uk"], wt["w_uv"], wt["w_o"],
                           L - 1, w.n_heads, w.d_head, w.d_latent, w.d_rope, w.rope_base, **cq)
         spent += time.perf_counter() - t
@@ -92,7 +97,8 @@ def cpu_baseline(w, seconds: float):
         b += 1
     return {"value": done / spent, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} of {w.batch} sequences (context {int(lens[0])}), non-absorbed "
-                      f"fp64 definition, {spent:.1f} s of host time"}
+                      f"fp64 definition" + (" on the FP8-quantized cache" if w.cache == "fp8" else "")
+                      + f", {spent:.1f} s of host time"}
 
 
 def main():
@@ -122,7 +128,10 @@ def main():
     sets = [DeviceWorkload(w, layer=l, num_splits=S) for l in (0, 1)]
     torch.cuda.synchronize()
     lens = sets[0].lens
-    cache_bytes = int(lens.sum()) * w.row * w.elem_bytes
+    # bytes of one cached row: d_c + d_R values in dtype, or (FP8 pool) d_c codes,
+    # d_R bf16 and one fp32 scale
+    row_bytes = (w.d_latent + 2 * w.d_rope + 4) if w.cache == "fp8" else w.row * w.elem_bytes
+    cache_bytes = int(lens.sum()) * row_bytes
     attn_flop = 2 * w.n_heads * int(lens.sum()) * (2 * w.d_latent + w.d_rope)
     stream = torch.cuda.current_stream()
 
@@ -182,7 +191,9 @@ def main():
         "config": {"workload": f"{w.name}: one MLA decode layer, hidden {w.hidden}, n_h {w.n_heads}, "
                                f"d_h {w.d_head}, d_c {w.d_latent}, d_R {w.d_rope}, batch {B}, "
                                f"context {int(lens.max())}, {S} KV splits, 64-token pages"
-                               + (f", query compression d_c' {w.d_cq}" if w.d_cq else ""),
+                               + (f", query compression d_c' {w.d_cq}" if w.d_cq else "")
+                               + (", FP8 latent pool (e4m3 c^KV + row scale, bf16 k^R)"
+                                  if w.cache == "fp8" else ""),
                    "batch": B, "context": int(lens.max()), "num_splits": S},
         "latent_cache_GBps": achieved,
         "attention_us": attn_s * 1e6,
@@ -191,7 +202,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": attention_traffic() if w.name == "full" and S == 4 else None,
-                     "kernel": "k_attn_mfma_h128 (mla_decode_attention)",
+                     "kernel": ("k_attn_mfma_h128<true> (mla_decode_attention_fp8)" if w.cache == "fp8"
+                                else "k_attn_mfma_h128<false> (mla_decode_attention)"),
                      "algorithmic_bytes_per_launch": cache_bytes},
     }
     if args.cpu_seconds > 0:

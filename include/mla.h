@@ -57,7 +57,7 @@ typedef enum {
   MLA_OK = 0,
   MLA_ERR_NULL = -1,        /* a required pointer is NULL */
   MLA_ERR_SHAPE = -2,       /* a dimension or count is out of range */
-  MLA_ERR_UNSUPPORTED = -3, /* dtype / abi_version / page_size not supported */
+  MLA_ERR_UNSUPPORTED = -3, /* dtype / abi_version / page_size / alignment not supported */
   MLA_ERR_WORKSPACE = -4,   /* workspace missing, smaller than mla_workspace_bytes() or
                                not 256-byte aligned */
   MLA_ERR_HIP = -5          /* a kernel launch was rejected by the HIP runtime */
@@ -186,6 +186,79 @@ size_t mla_workspace_bytes_cq(const mla_dims* dims, int32_t d_cq, int32_t batch)
 /* Workspace bytes needed by mla_append_latent for `n_rows` rows (0 if none is
  * needed or dims are invalid). */
 size_t mla_append_workspace_bytes(const mla_dims* dims, int32_t n_rows);
+
+/*
+ * FP8 latent pool ([Report] §4.2: at inference the 576-wide cached latent is
+ * further quantized, to about 6 bits per element on average; the pages do not
+ * give the scheme).  The format used by the *_fp8 calls (8.9 bits per cached
+ * element at d_c = 512, d_R = 64, scale included):
+ *   - the pool is [num_pages, page_bytes] bytes, page_bytes =
+ *     mla_fp8_page_bytes(dims) = page_size * (d_c + 2*d_R + 4), device memory
+ *     owned by the caller, 16-byte aligned;
+ *   - a page holds page_size rows of d_c + 2*d_R bytes, [c^KV as d_c e4m3 codes
+ *     | k^R as d_R bf16 (little-endian)], followed by page_size fp32 row
+ *     scales; logical position j of sequence b is row j%page_size of page
+ *     block_table[b*max_pages + j/page_size], its scale the (j%page_size)-th;
+ *   - e4m3 (OCP FP8): 1 sign, 4 exponent bits (bias 7), 3 mantissa bits,
+ *     largest finite 448, codes 0x7f/0xff are NaN and never written;
+ *   - a row's scale is 2^e with e the smallest integer such that
+ *     max_k |c_k| / 2^e <= 448 (e = 0 for an all-zero c), clamped to
+ *     [-126, 127]; code_k = round-to-nearest-even of c_k / 2^e (exact
+ *     division); the dequantized value is value(code_k) * 2^e.  k^R is rounded
+ *     to bf16 (nearest even).
+ * The *_fp8 calls need d_c a multiple of 8 (else MLA_ERR_UNSUPPORTED); dtype
+ * still gives the storage type of h and the weights.
+ */
+
+/* Bytes of one FP8 page (0 if dims are invalid or d_c is not a multiple of 8). */
+size_t mla_fp8_page_bytes(const mla_dims* dims);
+
+/*
+ * Quantize cache rows into the FP8 pool (the cache-fill path of the FP8 pool).
+ * Row r < n_rows is rows[r*ld_rows .. r*ld_rows + d_c + d_R) = [c | k^R] in
+ * fp32, k^R already rotated; it is written, as the format above fixes it, to
+ * logical position row_pos[r] of sequence row_seq[r].
+ *   rows fp32 device, 16-byte aligned, ld_rows >= d_c + d_R and a multiple
+ *   of 4; row_seq, row_pos [n_rows] int32; block_table [n_seqs, max_pages].
+ * Rows whose (seq, pos) or table entry is out of range are not written and set
+ * the device error word; rows must target distinct slots.  n_rows == 0 is a
+ * no-op.
+ */
+mla_status mla_quantize_rows_fp8(const mla_dims* dims, const float* rows, int64_t ld_rows,
+                                 const int32_t* row_seq, const int32_t* row_pos, int32_t n_rows,
+                                 const int32_t* block_table, int32_t n_seqs, int32_t max_pages,
+                                 void* pool, int64_t num_pages, hipStream_t stream);
+
+/*
+ * Latent append into the FP8 pool: as mla_append_latent (c = W_DKV h[r],
+ * k^R = RoPE(W_KR h[r], row_pos[r])), the row computed in fp32 and then
+ * quantized as mla_quantize_rows_fp8 does.
+ * Workspace: mla_append_workspace_bytes_fp8(dims, n_rows) bytes, 256-byte
+ * aligned (the fp32 rows, then GEMM partial sums), scratch for the call.
+ */
+mla_status mla_append_latent_fp8(const mla_dims* dims, const void* h, const void* w_dkv,
+                                 const void* w_kr, const int32_t* row_seq,
+                                 const int32_t* row_pos, int32_t n_rows,
+                                 const int32_t* block_table, int32_t n_seqs, int32_t max_pages,
+                                 void* pool, int64_t num_pages, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+/* Workspace bytes needed by mla_append_latent_fp8 (0 if n_rows is 0 or dims are
+ * invalid). */
+size_t mla_append_workspace_bytes_fp8(const mla_dims* dims, int32_t n_rows);
+
+/*
+ * Split-KV latent attention over the FP8 pool: mla_decode_attention with every
+ * cached row replaced by its dequantized value [value(code) * 2^e | k^R].
+ * The MFMA path (bf16 dtype, n_h = 128, d_c = 512, d_R = 64, page_size = 64)
+ * turns each tile into bf16 in LDS (exact: a power-of-two scale on a 4-bit
+ * significand) before the same bf16 products; other shapes use the plain
+ * vector kernel.  Arguments and outputs as mla_decode_attention.
+ */
+mla_status mla_decode_attention_fp8(const mla_dims* dims, const float* q_lat, const float* q_pe,
+                                    const void* pool, int64_t num_pages,
+                                    const int32_t* block_table, int32_t max_pages,
+                                    const int32_t* seq_lens, int32_t batch, int32_t num_splits,
+                                    float* o_part, float* lse_part, hipStream_t stream);
 
 /* Static text for a status code. */
 const char* mla_status_string(int32_t status);

@@ -22,7 +22,9 @@ __all__ = ["MlaDims", "MlaError", "make_dims", "load", "mla_append_latent", "mla
            "mla_absorb_q_cq", "mla_workspace_bytes_cq",
            "mla_decode_attention", "mla_merge_lse", "mla_absorb_out", "mla_workspace_bytes",
            "mla_append_workspace_bytes", "mla_device_error", "mla_set_kernel_path",
-           "mla_status_string", "LIB_PATH"]
+           "mla_status_string", "mla_fp8_page_bytes", "mla_quantize_rows_fp8",
+           "mla_append_latent_fp8", "mla_append_workspace_bytes_fp8", "mla_decode_attention_fp8",
+           "LIB_PATH"]
 
 
 class MlaDims(ctypes.Structure):
@@ -60,12 +62,19 @@ _SIGS = {
     "mla_workspace_bytes": [_DIMS, _I32],
     "mla_workspace_bytes_cq": [_DIMS, _I32, _I32],
     "mla_append_workspace_bytes": [_DIMS, _I32],
+    "mla_fp8_page_bytes": [_DIMS],
+    "mla_quantize_rows_fp8": [_DIMS, _P, _I64, _P, _P, _I32, _P, _I32, _I32, _P, _I64, _P],
+    "mla_append_latent_fp8": [_DIMS, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _P, _I64, _P, _SZ,
+                              _P],
+    "mla_append_workspace_bytes_fp8": [_DIMS, _I32],
+    "mla_decode_attention_fp8": [_DIMS, _P, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _P, _P, _P],
     "mla_status_string": [_I32],
     "mla_abi_version": [],
     "mla_device_error": [ctypes.POINTER(_I32), _I32, _P],
     "mla_set_kernel_path": [_I32],
 }
 _RES = {"mla_workspace_bytes": _SZ, "mla_workspace_bytes_cq": _SZ, "mla_append_workspace_bytes": _SZ,
+        "mla_fp8_page_bytes": _SZ, "mla_append_workspace_bytes_fp8": _SZ,
         "mla_status_string": ctypes.c_char_p}
 
 
@@ -248,6 +257,89 @@ def mla_absorb_out(dims, o_lat, w_uv, w_o, u, workspace, stream=None):
     _check("mla_absorb_out", load().mla_absorb_out(
         ctypes.byref(dims), _ptr(o_lat), _ptr(w_uv), _ptr(w_o), B, _ptr(u), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+# ------------------------------------------------------------- FP8 pool --
+def mla_fp8_page_bytes(dims: MlaDims) -> int:
+    return int(load().mla_fp8_page_bytes(ctypes.byref(dims)))
+
+
+def mla_append_workspace_bytes_fp8(dims: MlaDims, n_rows: int) -> int:
+    return int(load().mla_append_workspace_bytes_fp8(ctypes.byref(dims), n_rows))
+
+
+def _expect_fp8_pool(dims, pool):
+    import torch
+    pb = mla_fp8_page_bytes(dims)
+    if pool.dtype != torch.uint8 or pool.dim() != 2 or pool.shape[1] != pb:
+        raise ValueError(f"FP8 pool must be uint8 [num_pages, {pb}], got "
+                         f"{tuple(pool.shape)} {pool.dtype}")
+
+
+def _expect_table(block_table):
+    import torch
+    if block_table.dtype != torch.int32 or block_table.dim() != 2:
+        raise ValueError("block_table must be int32 [n_seqs, max_pages]")
+
+
+def mla_quantize_rows_fp8(dims, rows, row_seq, row_pos, block_table, pool, stream=None):
+    """Quantize fp32 rows [n, >= d_c + d_R] ([c | k^R], k^R already rotated) into
+    their slots of the FP8 pool (uint8 [num_pages, mla_fp8_page_bytes(dims)])."""
+    import torch
+    n = rows.shape[0]
+    if rows.dtype != torch.float32 or rows.dim() != 2 or rows.shape[1] < dims.d_latent + dims.d_rope:
+        raise ValueError("rows must be fp32 [n, >= d_c + d_R]")
+    _expect(row_seq, (n,), torch.int32, "row_seq")
+    _expect(row_pos, (n,), torch.int32, "row_pos")
+    _expect_table(block_table)
+    _expect_fp8_pool(dims, pool)
+    _check("mla_quantize_rows_fp8", load().mla_quantize_rows_fp8(
+        ctypes.byref(dims), _ptr(rows), rows.shape[1], _ptr(row_seq), _ptr(row_pos), n,
+        _ptr(block_table), block_table.shape[0], block_table.shape[1], _ptr(pool), pool.shape[0],
+        _stream(stream)))
+
+
+def mla_append_latent_fp8(dims, h, w_dkv, w_kr, row_seq, row_pos, block_table, pool,
+                          workspace=None, stream=None):
+    """mla_append_latent into the FP8 pool: rows in fp32, k^R rotated, then quantized.
+    ``workspace``: at least mla_append_workspace_bytes_fp8(dims, n_rows) bytes
+    (allocated here when omitted)."""
+    import torch
+    n = h.shape[0]
+    _expect(h, (n, dims.hidden), _elem(dims), "h")
+    _expect(w_dkv, (dims.d_latent, dims.hidden), _elem(dims), "w_dkv")
+    _expect(w_kr, (dims.d_rope, dims.hidden), _elem(dims), "w_kr")
+    _expect(row_seq, (n,), torch.int32, "row_seq")
+    _expect(row_pos, (n,), torch.int32, "row_pos")
+    _expect_table(block_table)
+    _expect_fp8_pool(dims, pool)
+    if workspace is None:
+        need = mla_append_workspace_bytes_fp8(dims, n)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=h.device)
+    _check("mla_append_latent_fp8", load().mla_append_latent_fp8(
+        ctypes.byref(dims), _ptr(h), _ptr(w_dkv), _ptr(w_kr), _ptr(row_seq), _ptr(row_pos), n,
+        _ptr(block_table), block_table.shape[0], block_table.shape[1], _ptr(pool), pool.shape[0],
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def mla_decode_attention_fp8(dims, q_lat, q_pe, pool, block_table, seq_lens, o_part, lse_part,
+                             stream=None):
+    """Split-KV latent attention over the FP8 pool; the split count is o_part.shape[1]."""
+    import torch
+    B, S = o_part.shape[0], o_part.shape[1]
+    nh = dims.n_heads
+    _expect(q_lat, (B, nh, dims.d_latent), torch.float32, "q_lat")
+    _expect(q_pe, (B, nh, dims.d_rope), torch.float32, "q_pe")
+    _expect_fp8_pool(dims, pool)
+    _expect(seq_lens, (B,), torch.int32, "seq_lens")
+    _expect(o_part, (B, S, nh, dims.d_latent), torch.float32, "o_part")
+    _expect(lse_part, (B, S, nh), torch.float32, "lse_part")
+    _expect_table(block_table)
+    if block_table.shape[0] < B:
+        raise ValueError("block_table must have at least batch rows")
+    _check("mla_decode_attention_fp8", load().mla_decode_attention_fp8(
+        ctypes.byref(dims), _ptr(q_lat), _ptr(q_pe), _ptr(pool), pool.shape[0], _ptr(block_table),
+        block_table.shape[1], _ptr(seq_lens), B, S, _ptr(o_part), _ptr(lse_part), _stream(stream)))
 
 
 def default_scale(dims: MlaDims) -> float:

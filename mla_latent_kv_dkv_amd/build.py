@@ -22,7 +22,7 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-
 
 LIBS = {
     "libmla.so": ["mla_api.cpp", "errword.hip", "kernels_generic.hip", "kernels_fast.hip",
-                  "gemm_fast.hip"],
+                  "gemm_fast.hip", "fp8_cache.hip"],
     "libmla_inputs.so": ["fill_inputs.hip"],
 }
 

@@ -73,6 +73,14 @@ constexpr int kARing = 6;                             // score operands in fligh
 constexpr int kBRing = 4;                             // P.C operand pairs in flight
 constexpr int kPageWin = 512;                         // page ids of the split held in LDS
 constexpr float kLog2e = 1.4426950408889634f;
+// FP8 pool: a page is 64 rows of [512 e4m3 | 64 bf16] (640 bytes), then 64 fp32
+// row scales; a tile is staged flat (32 rows, then its 32 scales) and
+// dequantized into the bf16 tile layout one iteration before it is scored.
+constexpr int kF8Row = kDc + 2 * kDr;                  // 640
+constexpr int kF8ScaleOff = kPage * kF8Row;             // 40960
+constexpr int64_t kF8PageBytes = kF8ScaleOff + 4 * kPage;   // 41216
+constexpr int kF8Stage = kTileTok * kF8Row + 4 * kTileTok;   // 20608
+constexpr int kF8Copies = 6;                            // copies per wave per tile
 constexpr float kHeadroom = 64.0f;                    // log2 units above the reference
 
 // 16-byte chunk c of latent row r sits at chunk c ^ lkey(r) of the row's
@@ -276,10 +284,53 @@ __device__ __forceinline__ void wait_tile(int after) {
   else wait_vmcnt<0>();
 }
 
+// FP8 pool: start the copy of the tile at `tok0` into the staging slot at LDS
+// address `stage`.  Wave wv copies rows 8wv..8wv+7 (5 KB, contiguous in the
+// page) flat to stage + 5120 wv, and their 8 row scales (two lanes) to the
+// scale block after the 32 rows: kF8Copies copies.  Rows past the split's end
+// re-read the tile's first row (their scores are masked); a page outside the
+// pool reads page 0 (masked and flagged by the caller).
+__device__ __forceinline__ void tile_issue_f8(const char* __restrict__ pool, int page, bool ok,
+                                              int tok0, int t1, uint32_t stage, int wv, int lane) {
+  const int nvalid = ok ? min(kTileTok, t1 - tok0) : 0;
+  const int64_t pbase = ok ? static_cast<int64_t>(page) * kF8PageBytes : 0;
+  const uint64_t rows = reinterpret_cast<uint64_t>(pool + pbase + (tok0 & (kPage - 1)) * kF8Row);
+  lane = static_cast<int>(opaque(static_cast<uint32_t>(lane)));
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int off = 1024 * i + 16 * lane;             // byte within the wave's 8 rows
+    const int r = off / kF8Row, col = off - r * kF8Row;
+    const int gr = 8 * wv + r;
+    dma_block(rows, (gr < nvalid ? gr : 0) * kF8Row + col, stage + 5120 * wv + 1024 * i);
+  }
+  const uint64_t scales =
+      reinterpret_cast<uint64_t>(pool + pbase + kF8ScaleOff + 4 * (tok0 & (kPage - 1)));
+  if (lane < 2) dma_block(scales, 32 * wv + 16 * lane, stage + kTileTok * kF8Row + 32 * wv);
+}
+
+// Wait until this wave's copies of a staged FP8 tile have landed, `after` tiles
+// (0..1) having been issued since; the wave then reads only its own rows.
+__device__ __forceinline__ void wait_tile_f8(int after) {
+  if (after >= 1) wait_vmcnt<kF8Copies>();
+  else wait_vmcnt<0>();
+  asm volatile("" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+__device__ __forceinline__ u32x4_t lds_ld128(uint32_t addr) {
+  return *reinterpret_cast<lds_u32x4*>(static_cast<uintptr_t>(addr));
+}
+__device__ __forceinline__ void lds_st128(uint32_t addr, u32x4_t v) {
+  *reinterpret_cast<lds_u32x4*>(static_cast<uintptr_t>(addr)) = v;
+}
+
+template <bool kF8>
 __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
     AttnArgs a, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     const char* __restrict__ pool) {
-  __shared__ __attribute__((aligned(1024))) char ring[kStages * kTileBytes];
+  // bf16 tile ring (4 slots; 3 for the FP8 pool, followed by its 2 staging slots)
+  __shared__ __attribute__((aligned(1024)))
+  char ring[kF8 ? 3 * kTileBytes + 2 * kF8Stage : kStages * kTileBytes];
   __shared__ __attribute__((aligned(16))) float xch[kWaves][kHeads];
   // page ids of the split's pages [wbase, wbase + kPageWin): a copy in LDS, so
   // a tile's page costs a short LDS read instead of a scalar memory load whose
@@ -437,6 +488,53 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
     return nvalid;
   };
 
+  // FP8 pool: copy of tile j into staging slot j & 1; returns its valid rows
+  const uint32_t stage0 = ring0 + 3 * kTileBytes;
+  auto issue_f8 = [&](int j) {
+    const int tok = t0 + j * kTileTok;
+    if (tok / kPage - wbase >= kPageWin) load_window(tok / kPage);   // splits > kPageWin pages
+    const int pg = __builtin_amdgcn_readfirstlane(pwin[tok / kPage - wbase]);   // uniform
+    const bool ok = pg >= 0 && pg < a.num_pages;
+    bad_page |= !ok;
+    tile_issue_f8(pool, pg, ok, tok, t1, stage0 + (j & 1) * kF8Stage, wv, lane);
+    return ok ? min(kTileTok, t1 - tok) : 0;
+  };
+  // FP8 pool: dequantize this wave's 8 rows of the staged tile into the bf16 tile
+  // at T: per step 16 e4m3 values -> two 16-byte bf16 chunks (the power-of-two
+  // row scale applied exactly by the conversion), and the bf16 k^R copied.
+  // Rows past the valid ones are written as zeros (their scores are masked, and
+  // zero weights times zeros keep O finite whatever those bytes held).  Ends
+  // with its LDS writes complete, so that a barrier publishes the tile.
+  auto convert_f8 = [&](uint32_t stage, uint32_t T, int nvalid) {
+    const int rl = lane >> 3, rr = 8 * wv + rl, q0 = lane & 7;
+    const bool live = rr < nvalid;
+    const uint32_t srow = stage + 5120 * wv + kF8Row * rl;
+    const float sig = live ? *reinterpret_cast<const __attribute__((address_space(3))) float*>(
+                                 static_cast<uintptr_t>(stage + kTileTok * kF8Row + 4 * rr))
+                           : 1.f;
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    const int key = lkey(rr);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int q = q0 + 8 * k;                     // 16-byte chunk of e4m3 values 16q..16q+15
+      const u32x4_t v = lds_ld128(srow + 16 * q);
+      u32x4_t lo, hi;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {   // bytes 0-1 (word 0) then 2-3 (word 1) of each dword
+        lo[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[j], sig, false));
+        lo[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[j], sig, true));
+        hi[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[2 + j], sig, false));
+        hi[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[2 + j], sig, true));
+      }
+      lds_st128(T + kPitch * rr + 16 * ((2 * q) ^ key), live ? lo : zero);
+      lds_st128(T + kPitch * rr + 16 * ((2 * q + 1) ^ key), live ? hi : zero);
+    }
+    const u32x4_t rope = lds_ld128(srow + kDc + 16 * q0);
+    lds_st128(T + kRopeOff + 1024 * (rr >> 3) + 128 * (rr & 7) + 16 * (q0 ^ rkey(rr)),
+              live ? rope : zero);
+    wait_lgkm(0);
+  };
+
   float seen = -INFINITY;     // largest raw score of this lane in this pass
   float p[16];                // softmax weights of the tile being scored
   // weight i of scores x: exp2(x cs - m) (m: reference in log2 units)
@@ -489,40 +587,95 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
     seen = -INFINITY;
 
     if (wbase != p_first) load_window(p_first);
-    int nv0 = issue(0), nv1 = 0, nv2 = 0;   // valid rows of tiles t, t+1, t+2
-    if (ntiles > 1) nv1 = issue(1);
-    // ---- tile 0: scores and weights
-    wait_tile(ntiles > 1 ? 1 : 0);
-    lds_barrier();
-    if (ntiles > 2) nv2 = issue(2);
-    f32x16_t sc = scores(ring0);
-    mask(sc, nv0);
-    if (pass == 0) {            // the first tile fixes the reference
-      float tm = sc[0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) tm = fmaxf(tm, sc[i]);
-      m_ref = fmaxf(tm, __shfl_xor(tm, 32, 64)) * cs;
-    }
-    const float mr = fmaxf(m_ref, -1e30f);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) weight(sc, i, mr);
-    weight_sum();
-    bf16x8_t pp0 = pack8(p), pp1 = pack8(p + 8);   // k = 16kk + 8(j >> 2) + 4g2 + (j & 3)
-    nv0 = nv1; nv1 = nv2;
-    // ---- tile t: scores, then the products of tile t-1 with the weights of tile t between them
-    for (int t = 1; t < ntiles; ++t) {
-      wait_tile(t + 1 < ntiles ? 1 : 0);
-      lds_barrier();   // tile t is in LDS for every wave; the slot of tile t-2 is free
-      if (t + 2 < ntiles) nv2 = issue(t + 2);
-      sc = scores(ring0 + (t & 3) * kTileBytes);
+    bf16x8_t pp0, pp1;        // packed weights of the previous tile
+    f32x16_t sc;
+    float mr;
+    if constexpr (!kF8) {
+      int nv0 = issue(0), nv1 = 0, nv2 = 0;   // valid rows of tiles t, t+1, t+2
+      if (ntiles > 1) nv1 = issue(1);
+      // ---- tile 0: scores and weights
+      wait_tile(ntiles > 1 ? 1 : 0);
+      lds_barrier();
+      if (ntiles > 2) nv2 = issue(2);
+      sc = scores(ring0);
       mask(sc, nv0);
-      pv_product(ring0 + ((t - 1) & 3) * kTileBytes, pp0, pp1, true, sc, mr);
+      if (pass == 0) {            // the first tile fixes the reference
+        float tm = sc[0];
+  #pragma unroll
+        for (int i = 1; i < 16; ++i) tm = fmaxf(tm, sc[i]);
+        m_ref = fmaxf(tm, __shfl_xor(tm, 32, 64)) * cs;
+      }
+      mr = fmaxf(m_ref, -1e30f);
+  #pragma unroll
+      for (int i = 0; i < 16; ++i) weight(sc, i, mr);
+      weight_sum();
+      pp0 = pack8(p);   // k = 16kk + 8(j >> 2) + 4g2 + (j & 3)
+      pp1 = pack8(p + 8);
+      nv0 = nv1; nv1 = nv2;
+      // ---- tile t: scores, then the products of tile t-1 with the weights of tile t between them
+      for (int t = 1; t < ntiles; ++t) {
+        wait_tile(t + 1 < ntiles ? 1 : 0);
+        lds_barrier();   // tile t is in LDS for every wave; the slot of tile t-2 is free
+        if (t + 2 < ntiles) nv2 = issue(t + 2);
+        sc = scores(ring0 + (t & 3) * kTileBytes);
+        mask(sc, nv0);
+        pv_product(ring0 + ((t - 1) & 3) * kTileBytes, pp0, pp1, true, sc, mr);
+        weight_sum();
+        pp0 = pack8(p);
+        pp1 = pack8(p + 8);
+        nv0 = nv1; nv1 = nv2;
+      }
+      pv_product(ring0 + ((ntiles - 1) & 3) * kTileBytes, pp0, pp1, false, sc, mr);
+    } else {
+      int nv0 = issue_f8(0), nv1 = 0, nv2 = 0;   // valid rows of tiles t, t+1, t+2
+      if (ntiles > 1) nv1 = issue_f8(1);
+      // ---- tile 0: dequantized, then scores and weights
+      wait_tile_f8(ntiles > 1 ? 1 : 0);
+      convert_f8(stage0, ring0, nv0);
+      lds_barrier();
+      if (ntiles > 2) nv2 = issue_f8(2);
+      sc = scores(ring0);
+      mask(sc, nv0);
+      if (pass == 0) {          // the first tile fixes the reference
+        float tm = sc[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) tm = fmaxf(tm, sc[i]);
+        m_ref = fmaxf(tm, __shfl_xor(tm, 32, 64)) * cs;
+      }
+      mr = fmaxf(m_ref, -1e30f);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) weight(sc, i, mr);
       weight_sum();
       pp0 = pack8(p);
       pp1 = pack8(p + 8);
+      if (ntiles > 1) {
+        wait_tile_f8(ntiles > 2 ? 1 : 0);
+        convert_f8(stage0 + kF8Stage, ring0 + kTileBytes, nv1);
+      }
       nv0 = nv1; nv1 = nv2;
+      // ---- tile t: scores, the products of tile t-1 with the weights of tile t
+      // between them, then tile t+1 dequantized (bf16 slots mod 3, staging mod 2)
+      int cur = 1, prev = 0;
+      for (int t = 1; t < ntiles; ++t) {
+        lds_barrier();   // tile t is dequantized for every wave; its staging slot and the bf16 slot of tile t-2 are free
+        if (t + 2 < ntiles) nv2 = issue_f8(t + 2);
+        const int nxt = cur == 2 ? 0 : cur + 1;
+        sc = scores(ring0 + cur * kTileBytes);
+        mask(sc, nv0);
+        pv_product(ring0 + prev * kTileBytes, pp0, pp1, true, sc, mr);
+        weight_sum();
+        pp0 = pack8(p);
+        pp1 = pack8(p + 8);
+        if (t + 1 < ntiles) {
+          wait_tile_f8(t + 2 < ntiles ? 1 : 0);
+          convert_f8(stage0 + ((t + 1) & 1) * kF8Stage, ring0 + nxt * kTileBytes, nv1);
+        }
+        nv0 = nv1; nv1 = nv2;
+        prev = cur;
+        cur = nxt;
+      }
+      pv_product(ring0 + prev * kTileBytes, pp0, pp1, false, sc, mr);
     }
-    pv_product(ring0 + ((ntiles - 1) & 3) * kTileBytes, pp0, pp1, false, sc, mr);
     // every copy has landed (the last tile was waited for with vmcnt 0)
     seen = fmaxf(seen, __shfl_xor(seen, 32, 64)) * cs;
     if (!__syncthreads_or(seen > m_ref + kHeadroom)) break;
@@ -560,7 +713,15 @@ bool fast_attention_ok(const AttnArgs& a) {
 hipError_t launch_attention_fast(const AttnArgs& a, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
   const int units = a.batch * a.num_splits;
-  hipLaunchKernelGGL(k_attn_mfma_h128, dim3(units), dim3(kThreads), 0, stream, a, a.block_table,
+  hipLaunchKernelGGL(k_attn_mfma_h128<false>, dim3(units), dim3(kThreads), 0, stream, a, a.block_table,
+                     a.seq_lens, static_cast<const char*>(a.pool));
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_fp8(const AttnArgs& a, hipStream_t stream) {
+  if (a.batch == 0) return hipSuccess;
+  const int units = a.batch * a.num_splits;
+  hipLaunchKernelGGL(k_attn_mfma_h128<true>, dim3(units), dim3(kThreads), 0, stream, a, a.block_table,
                      a.seq_lens, static_cast<const char*>(a.pool));
   return hipGetLastError();
 }

@@ -79,17 +79,54 @@ hipError_t launch_gemm_generic(const GemmArgs& a, bool bf16, hipStream_t stream)
 }
 
 // ------------------------------------------------------------ attention --
+// Row readers of the two pool formats.  row() gives a handle of the row at
+// (page, slot), scale() its multiplier and get() element e of it as fp32.
+template <typename T>
+struct PlainRows {   // pages of page_size rows of d_c + d_R values of T
+  const T* pool;
+  int row_w, page_size;
+  __device__ PlainRows(const AttnArgs& a)
+      : pool(static_cast<const T*>(a.pool)), row_w(a.d_latent + a.d_rope), page_size(a.page_size) {}
+  __device__ int64_t row(int page, int slot) const {
+    return (static_cast<int64_t>(page) * page_size + slot) * row_w;
+  }
+  __device__ float scale(int, int) const { return 1.f; }
+  __device__ float get(int64_t r, int e, float) const { return ld(pool + r + e); }
+};
+
+struct Fp8Rows {     // pages of page_size rows [d_c e4m3 | d_R bf16], then page_size fp32 scales
+  const uint8_t* pool;
+  int d_c, row_bytes, page_size;
+  int64_t page_bytes;
+  __device__ Fp8Rows(const AttnArgs& a)
+      : pool(static_cast<const uint8_t*>(a.pool)), d_c(a.d_latent),
+        row_bytes(a.d_latent + 2 * a.d_rope), page_size(a.page_size),
+        page_bytes(static_cast<int64_t>(a.page_size) * (a.d_latent + 2 * a.d_rope + 4)) {}
+  __device__ int64_t row(int page, int slot) const {
+    return static_cast<int64_t>(page) * page_bytes + static_cast<int64_t>(slot) * row_bytes;
+  }
+  __device__ float scale(int page, int slot) const {
+    return *reinterpret_cast<const float*>(pool + static_cast<int64_t>(page) * page_bytes +
+                                           static_cast<int64_t>(page_size) * row_bytes + 4 * slot);
+  }
+  __device__ float get(int64_t r, int e, float sc) const {
+    if (e < d_c) return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(pool[r + e]), 0) * sc;
+    return bf16_to_f32(*reinterpret_cast<const bf16_t*>(pool + r + d_c + 2 * (e - d_c)));
+  }
+};
+
 // One workgroup per (head, split, sequence).  Tokens are taken 256 at a time:
 // thread t scores token t (full d_c + d_R dot product), the chunk's weights
 // go through an online softmax, then each thread accumulates latent columns.
-template <typename T>
+template <typename Rows>
 __global__ __launch_bounds__(256) void k_attention_generic(AttnArgs a) {
   extern __shared__ float smem[];
   const int row_w = a.d_latent + a.d_rope;
   float* qs = smem;                         // [row_w]
   float* acc = qs + row_w;                  // [d_latent]
   float* ps = acc + a.d_latent;             // [256]
-  float* red = ps + 256;                    // [8]
+  float* rsc = ps + 256;                    // [256] row scales
+  float* red = rsc + 256;                   // [8]
   int64_t* rowoff = reinterpret_cast<int64_t*>(red + 8);  // [256]
 
   const int i = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
@@ -109,25 +146,26 @@ __global__ __launch_bounds__(256) void k_attention_generic(AttnArgs a) {
   for (int e = tid; e < a.d_rope; e += 256) qs[a.d_latent + e] = qp[e];
   __syncthreads();
 
-  const T* pool = static_cast<const T*>(a.pool);
+  const Rows rows(a);
   float m_run = -INFINITY, l_run = 0.f;
   for (int c0 = t0; c0 < t1; c0 += 256) {
     const int j = c0 + tid;
-    float sc = -INFINITY;
+    float sc = -INFINITY, rs = 0.f;
     int64_t off = -1;
     if (j < t1) {
       const int page = a.block_table[static_cast<int64_t>(b) * a.max_pages + j / a.page_size];
       if (page < 0 || page >= a.num_pages) {
         set_err(a.err, ERR_PAGE);
       } else {
-        off = (static_cast<int64_t>(page) * a.page_size + j % a.page_size) * row_w;
-        const T* r = pool + off;
+        off = rows.row(page, j % a.page_size);
+        rs = rows.scale(page, j % a.page_size);
         float d = 0.f;
-        for (int e = 0; e < row_w; ++e) d += qs[e] * ld(r + e);
+        for (int e = 0; e < row_w; ++e) d += qs[e] * rows.get(off, e, rs);
         sc = d * a.scale;
       }
     }
     rowoff[tid] = off;
+    rsc[tid] = rs;
     float cmax = wave_max(sc);
     if (lane == 0) red[wv] = cmax;
     __syncthreads();
@@ -148,7 +186,7 @@ __global__ __launch_bounds__(256) void k_attention_generic(AttnArgs a) {
       float v = acc[d] * alpha;
       for (int jj = 0; jj < cnt; ++jj) {
         const int64_t o = rowoff[jj];
-        if (o >= 0) v += ps[jj] * ld(pool + o + d);
+        if (o >= 0) v += ps[jj] * rows.get(o, d, rsc[jj]);
       }
       acc[d] = v;
     }
@@ -160,16 +198,27 @@ __global__ __launch_bounds__(256) void k_attention_generic(AttnArgs a) {
   if (tid == 0) a.lse_part[ob] = l_run > 0.f ? m_run + __logf(l_run) : -INFINITY;
 }
 
-hipError_t launch_attention_generic(const AttnArgs& a, bool bf16, hipStream_t stream) {
+// pool: 0 = fp32 rows, 1 = bf16 rows, 2 = FP8 pages
+static hipError_t launch_attention_rows(const AttnArgs& a, int pool, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
-  const size_t shm = (a.d_latent + a.d_rope + a.d_latent + 256 + 8) * sizeof(float) +
+  const size_t shm = (a.d_latent + a.d_rope + a.d_latent + 256 + 256 + 8) * sizeof(float) +
                      256 * sizeof(int64_t) + 16;
   dim3 grid(a.n_heads, a.num_splits, a.batch);
-  if (bf16)
-    hipLaunchKernelGGL(k_attention_generic<bf16_t>, grid, dim3(256), shm, stream, a);
+  if (pool == 2)
+    hipLaunchKernelGGL(k_attention_generic<Fp8Rows>, grid, dim3(256), shm, stream, a);
+  else if (pool == 1)
+    hipLaunchKernelGGL(k_attention_generic<PlainRows<bf16_t>>, grid, dim3(256), shm, stream, a);
   else
-    hipLaunchKernelGGL(k_attention_generic<float>, grid, dim3(256), shm, stream, a);
+    hipLaunchKernelGGL(k_attention_generic<PlainRows<float>>, grid, dim3(256), shm, stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_attention_generic(const AttnArgs& a, bool bf16, hipStream_t stream) {
+  return launch_attention_rows(a, bf16 ? 1 : 0, stream);
+}
+
+hipError_t launch_attention_generic_fp8(const AttnArgs& a, hipStream_t stream) {
+  return launch_attention_rows(a, 2, stream);
 }
 
 // ---------------------------------------------------------------- merge --

@@ -58,6 +58,26 @@ struct AttnArgs {
 };
 
 hipError_t launch_attention_generic(const AttnArgs& a, bool bf16, hipStream_t stream);
+// FP8 pool: pages of page_size rows [d_c e4m3 | d_R bf16], then page_size fp32 row scales
+hipError_t launch_attention_generic_fp8(const AttnArgs& a, hipStream_t stream);
+
+// FP8 latent pool: quantize fp32 rows [n_rows, d_c + d_R] into their page slots.
+struct QuantArgs {
+  const float* rows;
+  int64_t ld_rows;
+  int n_rows, d_latent, d_rope;
+  int rope;                 // rotate the k^R part at row_pos (rows straight from the projection)
+  double log_base;
+  const int32_t* row_seq;
+  const int32_t* row_pos;
+  const int32_t* block_table;
+  int n_seqs, max_pages, page_size;
+  int64_t num_pages, page_bytes, row_bytes;
+  uint8_t* pool;
+  int* err;
+};
+
+hipError_t launch_quantize_rows(const QuantArgs& a, hipStream_t stream);
 
 struct MergeArgs {
   const float* o_part;

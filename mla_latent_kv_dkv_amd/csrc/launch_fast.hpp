@@ -18,6 +18,8 @@ hipError_t launch_gemm_fast(const GemmArgs& a, void* partial, size_t partial_byt
 
 bool fast_attention_ok(const AttnArgs& a);
 hipError_t launch_attention_fast(const AttnArgs& a, hipStream_t stream);
+// FP8 pool (pages of 64 rows [512 e4m3 | 64 bf16] + 64 fp32 scales); same shapes as fast_attention_ok
+hipError_t launch_attention_fp8(const AttnArgs& a, hipStream_t stream);
 
 bool fast_merge_ok(const MergeArgs& a);
 hipError_t launch_merge_fast(const MergeArgs& a, hipStream_t stream);

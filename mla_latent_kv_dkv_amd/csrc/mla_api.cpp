@@ -190,6 +190,58 @@ size_t cq_bytes(const mla_dims* d, int d_cq, int batch) {
   return align256(static_cast<size_t>(batch) * static_cast<size_t>(d_cq) * elem_bytes(d));
 }
 
+// ---- FP8 pool: pages of page_size rows [d_c e4m3 | d_R bf16], then page_size fp32 scales
+bool fp8_ok(const mla_dims* d) { return d->d_latent % 8 == 0; }
+
+int64_t fp8_row_bytes(const mla_dims* d) { return d->d_latent + 2 * static_cast<int64_t>(d->d_rope); }
+
+int64_t fp8_page_bytes(const mla_dims* d) {
+  return static_cast<int64_t>(d->page_size) * (fp8_row_bytes(d) + 4);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Projection of appended rows into fp32 [c | k^R] (k^R not yet rotated).
+mla::GemmArgs append_rows_args(const mla_dims* d, int n_rows) {
+  mla::GemmArgs a{};
+  a.ldx_m = d->hidden; a.ldx_k = 1;
+  a.n_split = d->d_latent;
+  a.ldw_n = d->hidden; a.ldw_k = 1;
+  a.M = n_rows; a.N = d->d_latent + d->d_rope; a.K = d->hidden; a.batch = 1;
+  a.epi = mla::EPI_STORE; a.x_f32 = d->dtype != MLA_BF16; a.y_f32 = 1;
+  a.ldy = d->d_latent + d->d_rope;
+  return a;
+}
+
+size_t rows_bytes(const mla_dims* d, int n_rows) {
+  return align256(static_cast<size_t>(n_rows) * (d->d_latent + d->d_rope) * sizeof(float));
+}
+
+// Checks shared by the two attention calls; fills `a` (pool format aside).
+mla_status attention_args(const mla_dims* d, const float* q_lat, const float* q_pe,
+                          const void* pool, int64_t num_pages, const int32_t* block_table,
+                          int32_t max_pages, const int32_t* seq_lens, int32_t batch,
+                          int32_t num_splits, float* o_part, float* lse_part, mla::AttnArgs* a) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || batch > 65535 || num_splits < 1 || num_splits > 4096 || max_pages < 1 ||
+      num_pages < 1)
+    return MLA_ERR_SHAPE;
+  if (static_cast<int64_t>(max_pages) * d->page_size > (int64_t{1} << 30)) return MLA_ERR_SHAPE;
+  if (batch == 0) return MLA_OK;
+  if (!q_lat || !q_pe || !pool || !block_table || !seq_lens || !o_part || !lse_part)
+    return MLA_ERR_NULL;
+  int* err = err_word();
+  if (!err) return MLA_ERR_HIP;
+  *a = mla::AttnArgs{};
+  a->q_lat = q_lat; a->q_pe = q_pe; a->pool = pool; a->num_pages = num_pages;
+  a->block_table = block_table; a->max_pages = max_pages; a->seq_lens = seq_lens;
+  a->batch = batch; a->num_splits = num_splits; a->n_heads = d->n_heads;
+  a->d_latent = d->d_latent; a->d_rope = d->d_rope; a->page_size = d->page_size;
+  a->scale = softmax_scale(d); a->o_part = o_part; a->lse_part = lse_part; a->err = err;
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -333,27 +385,109 @@ mla_status mla_decode_attention(const mla_dims* d, const float* q_lat, const flo
                                 int32_t max_pages, const int32_t* seq_lens, int32_t batch,
                                 int32_t num_splits, float* o_part, float* lse_part,
                                 hipStream_t stream) {
-  mla_status st = check_dims(d);
-  if (st != MLA_OK) return st;
-  if (batch < 0 || batch > 65535 || num_splits < 1 || num_splits > 4096 || max_pages < 1 ||
-      num_pages < 1)
-    return MLA_ERR_SHAPE;
-  if (static_cast<int64_t>(max_pages) * d->page_size > (int64_t{1} << 30)) return MLA_ERR_SHAPE;
-  if (batch == 0) return MLA_OK;
-  if (!q_lat || !q_pe || !pool || !block_table || !seq_lens || !o_part || !lse_part)
-    return MLA_ERR_NULL;
-  int* err = err_word();
-  if (!err) return MLA_ERR_HIP;
   mla::AttnArgs a{};
-  a.q_lat = q_lat; a.q_pe = q_pe; a.pool = pool; a.num_pages = num_pages;
-  a.block_table = block_table; a.max_pages = max_pages; a.seq_lens = seq_lens;
-  a.batch = batch; a.num_splits = num_splits; a.n_heads = d->n_heads;
-  a.d_latent = d->d_latent; a.d_rope = d->d_rope; a.page_size = d->page_size;
-  a.scale = softmax_scale(d); a.o_part = o_part; a.lse_part = lse_part; a.err = err;
+  mla_status st = attention_args(d, q_lat, q_pe, pool, num_pages, block_table, max_pages, seq_lens,
+                                 batch, num_splits, o_part, lse_part, &a);
+  if (st != MLA_OK || batch == 0) return st;
   const bool bf16 = d->dtype == MLA_BF16;
   if (use_fast() && bf16 && mla::fast_attention_ok(a))
     return hip_status(mla::launch_attention_fast(a, stream));
   return hip_status(mla::launch_attention_generic(a, bf16, stream));
+}
+
+size_t mla_fp8_page_bytes(const mla_dims* d) {
+  if (check_dims(d) != MLA_OK || !fp8_ok(d)) return 0;
+  return static_cast<size_t>(fp8_page_bytes(d));
+}
+
+size_t mla_append_workspace_bytes_fp8(const mla_dims* d, int32_t n_rows) {
+  if (check_dims(d) != MLA_OK || !fp8_ok(d) || n_rows <= 0) return 0;
+  // [fp32 rows, n_rows x (d_c + d_R)][fp32 K-split partials]
+  return rows_bytes(d, n_rows) + partial_bytes(d, append_rows_args(d, n_rows)) + 256;
+}
+
+mla_status mla_quantize_rows_fp8(const mla_dims* d, const float* rows, int64_t ld_rows,
+                                 const int32_t* row_seq, const int32_t* row_pos, int32_t n_rows,
+                                 const int32_t* block_table, int32_t n_seqs, int32_t max_pages,
+                                 void* pool, int64_t num_pages, hipStream_t stream) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (!fp8_ok(d)) return MLA_ERR_UNSUPPORTED;
+  if (n_rows < 0 || n_seqs < 0 || max_pages < 0 || num_pages < 0) return MLA_ERR_SHAPE;
+  if (ld_rows < d->d_latent + d->d_rope || ld_rows % 4 != 0 || ld_rows > (int64_t{1} << 32))
+    return MLA_ERR_SHAPE;
+  if (n_rows == 0) return MLA_OK;
+  if (n_seqs < 1 || max_pages < 1 || num_pages < 1) return MLA_ERR_SHAPE;
+  if (static_cast<int64_t>(max_pages) * d->page_size > (int64_t{1} << 30)) return MLA_ERR_SHAPE;
+  if (!rows || !row_seq || !row_pos || !block_table || !pool) return MLA_ERR_NULL;
+  if (!aligned16(rows) || !aligned16(pool)) return MLA_ERR_UNSUPPORTED;
+  int* err = err_word();
+  if (!err) return MLA_ERR_HIP;
+  mla::QuantArgs q{};
+  q.rows = rows; q.ld_rows = ld_rows; q.n_rows = n_rows;
+  q.d_latent = d->d_latent; q.d_rope = d->d_rope; q.rope = 0;
+  q.log_base = std::log(static_cast<double>(d->rope_base));
+  q.row_seq = row_seq; q.row_pos = row_pos; q.block_table = block_table;
+  q.n_seqs = n_seqs; q.max_pages = max_pages; q.page_size = d->page_size;
+  q.num_pages = num_pages; q.page_bytes = fp8_page_bytes(d); q.row_bytes = fp8_row_bytes(d);
+  q.pool = static_cast<uint8_t*>(pool); q.err = err;
+  return hip_status(mla::launch_quantize_rows(q, stream));
+}
+
+mla_status mla_append_latent_fp8(const mla_dims* d, const void* h, const void* w_dkv,
+                                 const void* w_kr, const int32_t* row_seq,
+                                 const int32_t* row_pos, int32_t n_rows,
+                                 const int32_t* block_table, int32_t n_seqs, int32_t max_pages,
+                                 void* pool, int64_t num_pages, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (!fp8_ok(d)) return MLA_ERR_UNSUPPORTED;
+  if (n_rows < 0 || n_seqs < 0 || max_pages < 0 || num_pages < 0) return MLA_ERR_SHAPE;
+  if (n_rows == 0) return MLA_OK;
+  if (n_rows > (1 << 20) || n_seqs < 1 || max_pages < 1 || num_pages < 1) return MLA_ERR_SHAPE;
+  if (static_cast<int64_t>(max_pages) * d->page_size > (int64_t{1} << 30)) return MLA_ERR_SHAPE;
+  if (!h || !w_dkv || !w_kr || !row_seq || !row_pos || !block_table || !pool) return MLA_ERR_NULL;
+  if (!aligned16(pool)) return MLA_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < mla_append_workspace_bytes_fp8(d, n_rows) || !ws_aligned(ws))
+    return MLA_ERR_WORKSPACE;
+  int* err = err_word();
+  if (!err) return MLA_ERR_HIP;
+  // 1) fp32 rows [c | W_KR h] = h [W_DKV; W_KR]^T -> workspace
+  float* rows = static_cast<float*>(ws);
+  char* part = static_cast<char*>(ws) + rows_bytes(d, n_rows);
+  mla::GemmArgs a = append_rows_args(d, n_rows);
+  a.x = h; a.w1 = w_dkv; a.w2 = w_kr; a.y = rows;
+  if (run_gemm(d, a, part, ws_bytes - rows_bytes(d, n_rows), stream) != hipSuccess)
+    return MLA_ERR_HIP;
+  // 2) RoPE on k^R at row_pos, quantize, scatter into the pages
+  mla::QuantArgs q{};
+  q.rows = rows; q.ld_rows = d->d_latent + d->d_rope; q.n_rows = n_rows;
+  q.d_latent = d->d_latent; q.d_rope = d->d_rope; q.rope = 1;
+  q.log_base = std::log(static_cast<double>(d->rope_base));
+  q.row_seq = row_seq; q.row_pos = row_pos; q.block_table = block_table;
+  q.n_seqs = n_seqs; q.max_pages = max_pages; q.page_size = d->page_size;
+  q.num_pages = num_pages; q.page_bytes = fp8_page_bytes(d); q.row_bytes = fp8_row_bytes(d);
+  q.pool = static_cast<uint8_t*>(pool); q.err = err;
+  return hip_status(mla::launch_quantize_rows(q, stream));
+}
+
+mla_status mla_decode_attention_fp8(const mla_dims* d, const float* q_lat, const float* q_pe,
+                                    const void* pool, int64_t num_pages,
+                                    const int32_t* block_table, int32_t max_pages,
+                                    const int32_t* seq_lens, int32_t batch, int32_t num_splits,
+                                    float* o_part, float* lse_part, hipStream_t stream) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (!fp8_ok(d)) return MLA_ERR_UNSUPPORTED;
+  mla::AttnArgs a{};
+  st = attention_args(d, q_lat, q_pe, pool, num_pages, block_table, max_pages, seq_lens, batch,
+                      num_splits, o_part, lse_part, &a);
+  if (st != MLA_OK || batch == 0) return st;
+  if (!aligned16(pool)) return MLA_ERR_UNSUPPORTED;
+  if (use_fast() && d->dtype == MLA_BF16 && mla::fast_attention_ok(a))
+    return hip_status(mla::launch_attention_fp8(a, stream));
+  return hip_status(mla::launch_attention_generic_fp8(a, stream));
 }
 
 mla_status mla_merge_lse(const mla_dims* d, const float* o_part, const float* lse_part,

@@ -9,9 +9,32 @@ from __future__ import annotations
 import numpy as np
 
 from . import (make_dims, mla_absorb_out, mla_absorb_q, mla_absorb_q_cq, mla_append_latent,
-               mla_append_workspace_bytes, mla_decode_attention, mla_merge_lse,
-               mla_workspace_bytes, mla_workspace_bytes_cq)
+               mla_append_latent_fp8, mla_append_workspace_bytes, mla_append_workspace_bytes_fp8,
+               mla_decode_attention, mla_decode_attention_fp8, mla_fp8_page_bytes, mla_merge_lse,
+               mla_quantize_rows_fp8, mla_workspace_bytes, mla_workspace_bytes_cq)
 from . import inputs as I
+
+
+def fill_fp8_pool(dims, pool, key: int, chunk_rows: int = 1 << 16):
+    """Fill every row of an FP8 pool (uint8 [num_pages, page_bytes]) from the fp32
+    values of generator stream ``key``: physical row p takes elements
+    p*row .. p*row + row-1 (as in a plain pool).  fp32 rows are generated a chunk
+    at a time on the device and quantized into their slots by
+    mla_quantize_rows_fp8, physical page p addressed as a one-page sequence p."""
+    import torch
+    P, row = dims.page_size, dims.d_latent + dims.d_rope
+    pages = pool.shape[0]
+    total = pages * P
+    ident = torch.arange(pages, dtype=torch.int32, device=pool.device).reshape(-1, 1)
+    buf = torch.empty((min(chunk_rows, total), row), dtype=torch.float32, device=pool.device)
+    for r0 in range(0, total, chunk_rows):
+        n = min(chunk_rows, total - r0)
+        rows = buf[:n]
+        I.fill_device(rows, key, 1.0, start=r0 * row)
+        phys = torch.arange(r0, r0 + n, dtype=torch.int32, device=pool.device)
+        mla_quantize_rows_fp8(dims, rows, (phys // P).contiguous(), (phys % P).contiguous(), ident,
+                              pool)
+    torch.cuda.synchronize()
 
 
 class DeviceWorkload:
@@ -40,7 +63,13 @@ class DeviceWorkload:
             t = torch.empty(w.weight_shape(name), dtype=self.dt, device=self.dev)
             I.fill_device(t, I.stream_key(w.seed, name, layer), 1.0 / np.sqrt(w.fan_in(name)))
             self.weights[name] = t
-        self.pool = torch.empty((self.num_pages, w.page_size, w.row), dtype=self.dt, device=self.dev)
+        self.fp8 = w.cache == "fp8"
+        if self.fp8:
+            self.pool = torch.empty((self.num_pages, mla_fp8_page_bytes(self.dims)), dtype=torch.uint8,
+                                    device=self.dev)
+        else:
+            self.pool = torch.empty((self.num_pages, w.page_size, w.row), dtype=self.dt,
+                                    device=self.dev)
         if w.cache_from_h:
             L = int(self.lens.max())
             self.h_ctx = torch.empty((B, L, w.hidden), dtype=self.dt, device=self.dev)
@@ -53,10 +82,13 @@ class DeviceWorkload:
             self.h_ctx = None
             self.h = torch.empty((B, w.hidden), dtype=self.dt, device=self.dev)
             I.fill_device(self.h, I.stream_key(w.seed, "h_dec", layer))
-            I.fill_device(self.pool, I.stream_key(w.seed, "pool", layer))
+            if self.fp8:
+                self.fill_fp8_pool()
+            else:
+                I.fill_device(self.pool, I.stream_key(w.seed, "pool", layer))
         nh = w.n_heads
-        self.ws_append = torch.empty(max(1, mla_append_workspace_bytes(self.dims, B)),
-                                     dtype=torch.uint8, device=self.dev)
+        wsa = (mla_append_workspace_bytes_fp8 if self.fp8 else mla_append_workspace_bytes)(self.dims, B)
+        self.ws_append = torch.empty(max(1, wsa), dtype=torch.uint8, device=self.dev)
         if outputs_from is not None:     # share scratch/output buffers with another layer
             for k in ("q_lat", "q_pe", "o_part", "lse_part", "o_lat", "lse", "u", "ws"):
                 setattr(self, k, getattr(outputs_from, k))
@@ -74,6 +106,10 @@ class DeviceWorkload:
             ws_bytes = max(ws_bytes, mla_workspace_bytes_cq(self.dims, w.d_cq, B))
         self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=self.dev)
 
+    def fill_fp8_pool(self):
+        """Every row of the FP8 pool from the fp32 values of stream "pool"."""
+        fill_fp8_pool(self.dims, self.pool, I.stream_key(self.w.seed, "pool", self.layer))
+
     def build_cache_from_h(self):
         """Append rows 0..L_b-2 of every sequence from h_ctx (the context before
         the decode token) through mla_append_latent."""
@@ -87,8 +123,9 @@ class DeviceWorkload:
         seq = torch.tensor(np.concatenate(seqs), device=self.dev)
         pos = torch.tensor(np.concatenate(poss), device=self.dev)
         rows = self.h_ctx.reshape(B * L, -1)[(seq.long() * L + pos.long())].contiguous()
-        mla_append_latent(self.dims, rows, self.weights["w_dkv"], self.weights["w_kr"], seq, pos,
-                          self.block_table, self.pool)
+        append = mla_append_latent_fp8 if self.fp8 else mla_append_latent
+        append(self.dims, rows, self.weights["w_dkv"], self.weights["w_kr"], seq, pos,
+               self.block_table, self.pool)
 
     # ---- the five calls of one decode step ------------------------------
     def absorb_q(self):
@@ -101,12 +138,14 @@ class DeviceWorkload:
                          self.q_pe, self.ws)
 
     def append(self):
-        mla_append_latent(self.dims, self.h, self.weights["w_dkv"], self.weights["w_kr"],
-                          self.seq_ids, self.pos, self.block_table, self.pool, self.ws_append)
+        append = mla_append_latent_fp8 if self.fp8 else mla_append_latent
+        append(self.dims, self.h, self.weights["w_dkv"], self.weights["w_kr"], self.seq_ids,
+               self.pos, self.block_table, self.pool, self.ws_append)
 
     def attention(self):
-        mla_decode_attention(self.dims, self.q_lat, self.q_pe, self.pool, self.block_table,
-                             self.seq_lens, self.o_part, self.lse_part)
+        attend = mla_decode_attention_fp8 if self.fp8 else mla_decode_attention
+        attend(self.dims, self.q_lat, self.q_pe, self.pool, self.block_table, self.seq_lens,
+               self.o_part, self.lse_part)
 
     def merge(self):
         mla_merge_lse(self.dims, self.o_part, self.lse_part, self.o_lat, self.lse)
@@ -150,5 +189,9 @@ class DeviceWorkload:
         return I.to_f64(w, v).reshape(L, w.hidden)
 
     def host_pool_rows(self, b: int, length: int) -> np.ndarray:
-        """fp64 generator-filled pool rows of logical positions 0..length-1 of b."""
+        """fp64 generator-filled pool rows of logical positions 0..length-1 of b
+        (for an FP8 pool: the fp32 rows before quantization)."""
+        if self.fp8:
+            return I.pool_rows(self.w, self.bt_host, b, length, self.layer, f32=True).astype(
+                np.float64)
         return I.to_f64(self.w, I.pool_rows(self.w, self.bt_host, b, length, self.layer))

@@ -167,6 +167,7 @@ class Workload:
     page_size: int = 64
     rope_base: float = 10000.0
     d_cq: int = 0                   # query compression rank d_c' (0: q^C = W_Q h)
+    cache: str = "dtype"            # pool format: "dtype" rows, or "fp8" pages
     notes: str = field(default="", compare=False)
 
     @property
@@ -215,6 +216,14 @@ WORKLOADS = {
                         cache_from_h=True, d_cq=512),
     "full-cq": Workload("full-cq", 5120, 128, 128, 512, 64, "bf16", 64, 4096, 1008, num_splits=4,
                         d_cq=1536),
+    # the same shapes with the FP8 latent pool (the pool is filled from seeded fp32
+    # rows, or built through the FP8 append for the cache-from-h ones)
+    "tiny-fp8": Workload("tiny-fp8", 64, 4, 16, 32, 8, "f32", 1, 64, 1009, num_splits=1,
+                         permute_pages=False, cache_from_h=True, cache="fp8"),
+    "lite-fp8": Workload("lite-fp8", 2048, 16, 128, 512, 64, "bf16", 32, 4096, 1010, num_splits=2,
+                         cache_from_h=True, cache="fp8"),
+    "full-fp8": Workload("full-fp8", 5120, 128, 128, 512, 64, "bf16", 64, 4096, 1011, num_splits=4,
+                         cache="fp8"),
 }
 
 
@@ -268,21 +277,24 @@ def to_f64(w: Workload, arr: np.ndarray) -> np.ndarray:
     return np.asarray(arr, dtype=np.float64) if w.dtype == "f32" else bf16_bits_to_f64(arr)
 
 
-def pool_rows(w: Workload, block_table: np.ndarray, seq: int, length: int, layer: int = 0):
+def pool_rows(w: Workload, block_table: np.ndarray, seq: int, length: int, layer: int = 0,
+              f32: bool = False):
     """Storage-format pool rows of logical positions 0..length-1 of ``seq`` as the
     device fill leaves them (the pool is filled linearly by physical element
-    index, stream "pool")."""
+    index, stream "pool").  ``f32``: the fp32 values instead, whatever the
+    storage type (the source rows of an FP8 pool)."""
     pos = np.arange(length)
     phys = block_table[seq, pos // w.page_size].astype(np.int64) * w.page_size + pos % w.page_size
     key = stream_key(w.seed, "pool", layer)
     # contiguous runs of physical rows share one generator call
-    out = np.empty((length, w.row), dtype=np.float32 if w.dtype == "f32" else np.uint16)
+    as_f32 = f32 or w.dtype == "f32"
+    out = np.empty((length, w.row), dtype=np.float32 if as_f32 else np.uint16)
     j = 0
     while j < length:
         k = j
         while k + 1 < length and phys[k + 1] == phys[k] + 1:
             k += 1
-        gen = normal_f32 if w.dtype == "f32" else normal_bf16_bits
+        gen = normal_f32 if as_f32 else normal_bf16_bits
         v = gen(key, int(phys[j]) * w.row, (k - j + 1) * w.row, 1.0)
         out[j:k + 1] = v.reshape(k - j + 1, w.row)
         j = k + 1

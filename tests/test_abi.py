@@ -131,6 +131,46 @@ def test_argument_checks():
                                  0, None, 0, None) == 0
 
 
+def test_fp8_pool_sizes_and_argument_checks():
+    lib = M.load()
+    full = M.make_dims(5120, 128, 128, 512, 64, "bf16")
+    # [512 e4m3 | 64 bf16] rows of 640 bytes, 64 of them, then 64 fp32 scales
+    assert M.mla_fp8_page_bytes(full) == 64 * 640 + 64 * 4 == 41216
+    assert M.mla_fp8_page_bytes(_dims(page_size=1)) == 32 + 16 + 4
+    assert M.mla_fp8_page_bytes(_dims(d_latent=36)) == 0          # d_c must be a multiple of 8
+    assert M.mla_fp8_page_bytes(_dims(d_rope=7)) == 0
+    assert M.mla_append_workspace_bytes_fp8(full, 64) >= 64 * 576 * 4
+    assert M.mla_append_workspace_bytes_fp8(full, 0) == 0
+    d = ctypes.byref(_dims())
+    d36 = ctypes.byref(_dims(d_latent=36))
+    misaligned = ctypes.c_void_p(0x1008)
+    # quantize_rows: (dims, rows, ld_rows, seq, pos, n, table, n_seqs, max_pages, pool, pages, stream)
+    assert lib.mla_quantize_rows_fp8(d36, P, 44, P, P, 1, P, 1, 1, P, 1, None) == -3
+    assert lib.mla_quantize_rows_fp8(d, P, 39, P, P, 1, P, 1, 1, P, 1, None) == -2   # ld < d_c + d_R
+    assert lib.mla_quantize_rows_fp8(d, P, 42, P, P, 1, P, 1, 1, P, 1, None) == -2   # ld % 4
+    assert lib.mla_quantize_rows_fp8(d, P, 40, P, P, -1, P, 1, 1, P, 1, None) == -2
+    assert lib.mla_quantize_rows_fp8(d, None, 40, P, P, 1, P, 1, 1, P, 1, None) == -1
+    assert lib.mla_quantize_rows_fp8(d, misaligned, 40, P, P, 1, P, 1, 1, P, 1, None) == -3
+    assert lib.mla_quantize_rows_fp8(d, P, 40, P, P, 1, P, 1, 1, misaligned, 1, None) == -3
+    assert lib.mla_quantize_rows_fp8(d, None, 40, None, None, 0, None, 0, 0, None, 0, None) == 0
+    # append_fp8
+    assert lib.mla_append_latent_fp8(d36, P, P, P, P, P, 1, P, 1, 1, P, 1, P, 1 << 20, None) == -3
+    assert lib.mla_append_latent_fp8(d, P, P, None, P, P, 1, P, 1, 1, P, 1, P, 1 << 20, None) == -1
+    assert lib.mla_append_latent_fp8(d, P, P, P, P, P, 4, P, 1, 1, P, 1, P, 64, None) == -4
+    assert lib.mla_append_latent_fp8(d, P, P, P, P, P, 4, P, 1, 1, P, 1, misaligned, 1 << 20,
+                                     None) == -4
+    assert lib.mla_append_latent_fp8(d, P, P, P, P, P, 4, P, 1, 1, misaligned, 1, P, 1 << 20,
+                                     None) == -3
+    assert lib.mla_append_latent_fp8(d, None, None, None, None, None, 0, None, 0, 0, None, 0, None,
+                                     0, None) == 0
+    # attention_fp8: the same checks as the plain call, plus the FP8 format's
+    assert lib.mla_decode_attention_fp8(d36, P, P, P, 1, P, 1, P, 1, 1, P, P, None) == -3
+    assert lib.mla_decode_attention_fp8(d, None, P, P, 1, P, 1, P, 1, 1, P, P, None) == -1
+    assert lib.mla_decode_attention_fp8(d, P, P, P, 1, P, 1, P, 1, 0, P, P, None) == -2
+    assert lib.mla_decode_attention_fp8(d, None, None, None, 1, None, 1, None, 0, 1, None, None,
+                                        None) == 0
+
+
 def test_device_fill_argument_checks():
     lib = _lib("libmla_inputs.so")
     lib.mla_fill_normal.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint64,

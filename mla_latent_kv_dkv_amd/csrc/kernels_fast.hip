@@ -74,13 +74,18 @@ constexpr int kBRing = 4;                             // P.C operand pairs in fl
 constexpr int kPageWin = 512;                         // page ids of the split held in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 // FP8 pool: a page is 64 rows of [512 e4m3 | 64 bf16] (640 bytes), then 64 fp32
-// row scales; a tile is staged flat (32 rows, then its 32 scales) and
-// dequantized into the bf16 tile layout one iteration before it is scored.
+// row scales.  A tile is staged in LDS as its codes, its k^R block and its 32
+// scales, and the products read the codes directly (dequantized in registers).
 constexpr int kF8Row = kDc + 2 * kDr;                  // 640
 constexpr int kF8ScaleOff = kPage * kF8Row;             // 40960
 constexpr int64_t kF8PageBytes = kF8ScaleOff + 4 * kPage;   // 41216
-constexpr int kF8Stage = kTileTok * kF8Row + 4 * kTileTok;   // 20608
+constexpr int kF8RopeOff = kTileTok * kDc;              // 16384: k^R block of a staged tile
+constexpr int kF8ScaleLds = kF8RopeOff + kTileTok * 2 * kDr;   // 20480: its scales
+constexpr int kF8Stage = kF8ScaleLds + 4 * kTileTok;    // 20608
 constexpr int kF8Copies = 6;                            // copies per wave per tile
+constexpr int kF8Slots = 6, kF8Ahead = 4;               // staging slots; tiles copied ahead
+constexpr int kARingF8 = 3;                             // FP8 score reads in flight
+constexpr int kBRingF8 = 4;                             // FP8 P.C reads in flight + 2
 constexpr float kHeadroom = 64.0f;                    // log2 units above the reference
 
 // 16-byte chunk c of latent row r sits at chunk c ^ lkey(r) of the row's
@@ -132,8 +137,14 @@ __device__ __forceinline__ f32x16_t mfma_v_first(const bf16x8_t& a, const bf16x8
 __device__ __forceinline__ void mfma_v(f32x16_t& d, const bf16x8_t& a, const bf16x8_t& b) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
+__device__ __forceinline__ void mfma_v_nop(f32x16_t& d, const bf16x8_t& a, const bf16x8_t& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
 __device__ __forceinline__ void mfma_v_last(f32x16_t& d, const bf16x8_t& a, const bf16x8_t& b) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 15" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v_last_nop(f32x16_t& d, const bf16x8_t& a, const bf16x8_t& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 15" : "+v"(d) : "v"(a), "v"(b));
 }
 
 // Work-unit index of workgroup x: consecutive splits of a sequence go to the
@@ -143,7 +154,7 @@ __device__ __forceinline__ int unit_of(int x, int units) {
   return (x & 7) * (units >> 3) + (x >> 3);
 }
 
-// lgkmcnt(n) with vmcnt/expcnt left alone (gfx9 encoding of s_waitcnt).
+// lgkmcnt(n) with vmcnt/expcnt left alone (gfx9 encoding of s_waitcnt; n <= 15).
 __device__ __forceinline__ void wait_lgkm(int n) {
   switch (n) {
     case 0: __builtin_amdgcn_s_waitcnt(0xC07F); break;
@@ -152,7 +163,12 @@ __device__ __forceinline__ void wait_lgkm(int n) {
     case 3: __builtin_amdgcn_s_waitcnt(0xC37F); break;
     case 4: __builtin_amdgcn_s_waitcnt(0xC47F); break;
     case 5: __builtin_amdgcn_s_waitcnt(0xC57F); break;
-    default: __builtin_amdgcn_s_waitcnt(0xC67F); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0xC67F); break;
+    case 7: __builtin_amdgcn_s_waitcnt(0xC77F); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0xC87F); break;
+    case 9: __builtin_amdgcn_s_waitcnt(0xC97F); break;
+    case 10: __builtin_amdgcn_s_waitcnt(0xCA7F); break;
+    default: __builtin_amdgcn_s_waitcnt(0xCB7F); break;
   }
 }
 
@@ -284,12 +300,20 @@ __device__ __forceinline__ void wait_tile(int after) {
   else wait_vmcnt<0>();
 }
 
-// FP8 pool: start the copy of the tile at `tok0` into the staging slot at LDS
-// address `stage`.  Wave wv copies rows 8wv..8wv+7 (5 KB, contiguous in the
-// page) flat to stage + 5120 wv, and their 8 row scales (two lanes) to the
-// scale block after the 32 rows: kF8Copies copies.  Rows past the split's end
-// re-read the tile's first row (their scores are masked); a page outside the
-// pool reads page 0 (masked and flagged by the caller).
+// Staged FP8 tile (32 rows): the codes of row r at kDc r, its 16-byte chunk c at
+// chunk c ^ f8key(r); the k^R block of row r at kF8RopeOff + 128 r, chunk c at
+// c ^ rkey(r); the 32 row scales at kF8ScaleLds.  f8key puts the 16 rows that a
+// 128-bit score read serves together, and the 8 rows of a transposed P.C read,
+// on distinct banks.
+__device__ __forceinline__ int f8key(int r) {
+  return 2 * ((r & 3) | ((r >> 1) & 4)) + ((r >> 2) & 1);
+}
+
+// Start the copy of the FP8 tile at `tok0` into the staging slot at `stage`.
+// Wave wv copies rows 8wv..8wv+7: their codes (four 1 KB copies of two rows
+// each), their k^R (one copy) and their 8 scales (two lanes): kF8Copies
+// copies.  Rows past the split's end re-read the tile's first row; a page
+// outside the pool reads page 0 (the caller masks those rows and flags it).
 __device__ __forceinline__ void tile_issue_f8(const char* __restrict__ pool, int page, bool ok,
                                               int tok0, int t1, uint32_t stage, int wv, int lane) {
   const int nvalid = ok ? min(kTileTok, t1 - tok0) : 0;
@@ -297,23 +321,28 @@ __device__ __forceinline__ void tile_issue_f8(const char* __restrict__ pool, int
   const uint64_t rows = reinterpret_cast<uint64_t>(pool + pbase + (tok0 & (kPage - 1)) * kF8Row);
   lane = static_cast<int>(opaque(static_cast<uint32_t>(lane)));
 #pragma unroll
-  for (int i = 0; i < 5; ++i) {
-    const int off = 1024 * i + 16 * lane;             // byte within the wave's 8 rows
-    const int r = off / kF8Row, col = off - r * kF8Row;
-    const int gr = 8 * wv + r;
-    dma_block(rows, (gr < nvalid ? gr : 0) * kF8Row + col, stage + 5120 * wv + 1024 * i);
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * wv + 2 * i + (lane >> 5);
+    dma_block(rows, (r < nvalid ? r : 0) * kF8Row + 16 * ((lane & 31) ^ f8key(r)),
+              stage + kDc * (8 * wv + 2 * i));
   }
+  const int rr = 8 * wv + (lane >> 3);
+  dma_block(rows, (rr < nvalid ? rr : 0) * kF8Row + kDc + 16 * ((lane & 7) ^ rkey(rr)),
+            stage + kF8RopeOff + 1024 * wv);
   const uint64_t scales =
       reinterpret_cast<uint64_t>(pool + pbase + kF8ScaleOff + 4 * (tok0 & (kPage - 1)));
-  if (lane < 2) dma_block(scales, 32 * wv + 16 * lane, stage + kTileTok * kF8Row + 32 * wv);
+  if (lane < 2) dma_block(scales, 32 * wv + 16 * lane, stage + kF8ScaleLds + 32 * wv);
 }
 
-// Wait until this wave's copies of a staged FP8 tile have landed, `after` tiles
-// (0..1) having been issued since; the wave then reads only its own rows.
+// Wait until this wave's copies of a staged tile have landed, `after` (0..3)
+// tiles having been issued since.
 __device__ __forceinline__ void wait_tile_f8(int after) {
-  if (after >= 1) wait_vmcnt<kF8Copies>();
-  else wait_vmcnt<0>();
-  asm volatile("" ::: "memory");
+  switch (after) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<kF8Copies>(); break;
+    case 2: wait_vmcnt<2 * kF8Copies>(); break;
+    default: wait_vmcnt<3 * kF8Copies>(); break;
+  }
 }
 
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
@@ -323,14 +352,46 @@ __device__ __forceinline__ u32x4_t lds_ld128(uint32_t addr) {
 __device__ __forceinline__ void lds_st128(uint32_t addr, u32x4_t v) {
   *reinterpret_cast<lds_u32x4*>(static_cast<uintptr_t>(addr)) = v;
 }
+__device__ __forceinline__ void lds_st32(uint32_t addr, uint32_t v) {
+  *reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(static_cast<uintptr_t>(addr)) = v;
+}
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) const u32x2_t lds_u32x2;
+__device__ __forceinline__ u32x2_t lds_ld64(uint32_t addr) {
+  return *reinterpret_cast<lds_u32x2*>(static_cast<uintptr_t>(addr));
+}
+__device__ __forceinline__ float lds_f32(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) float*>(static_cast<uintptr_t>(addr));
+}
+// 4 e4m3 values (one dword, byte 0 first) times the power-of-two scale s as bf16 pairs
+__device__ __forceinline__ uint32_t f8lo(uint32_t v, float s) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, s, false));
+}
+__device__ __forceinline__ uint32_t f8hi(uint32_t v, float s) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, s, true));
+}
+// 8 bytes per lane, transposed across 16-lane groups: output lane i < 8 of a
+// group gets byte i of the blocks of its lanes 0, 2, .., 14, lane 8 + i byte i
+// of those of lanes 1, 3, .., 15
+__device__ __forceinline__ u32x2_t lds_tr8(uint32_t addr) {
+  typedef int i32x2_t __attribute__((ext_vector_type(2)));
+  const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      reinterpret_cast<__attribute__((address_space(3))) i32x2_t*>(static_cast<uintptr_t>(addr)));
+  return __builtin_bit_cast(u32x2_t, v);
+}
+// 8 e4m3 codes (two dwords) times the power-of-two scale s as a bf16 operand
+__device__ __forceinline__ bf16x8_t f8x8(u32x2_t v, float s) {
+  const u32x4_t o = {f8lo(v[0], s), f8hi(v[0], s), f8lo(v[1], s), f8hi(v[1], s)};
+  return __builtin_bit_cast(bf16x8_t, o);
+}
 
 template <bool kF8>
 __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
     AttnArgs a, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     const char* __restrict__ pool) {
-  // bf16 tile ring (4 slots; 3 for the FP8 pool, followed by its 2 staging slots)
+  // tile ring: 4 bf16 tiles, or kF8Slots staged FP8 tiles
   __shared__ __attribute__((aligned(1024)))
-  char ring[kF8 ? 3 * kTileBytes + 2 * kF8Stage : kStages * kTileBytes];
+  char ring[kF8 ? kF8Slots * kF8Stage : kStages * kTileBytes];
   __shared__ __attribute__((aligned(16))) float xch[kWaves][kHeads];
   // page ids of the split's pages [wbase, wbase + kPageWin): a copy in LDS, so
   // a tile's page costs a short LDS read instead of a scalar memory load whose
@@ -379,14 +440,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
   };
 
   // ---- this wave's queries as MFMA B fragments: head 32wv + r32, k = 16ks + 8g2 + j
+  // (FP8 pool, latent steps 2a + e: k = 32a + 16g2 + 8e + j, the order in which
+  // a 16-byte code chunk feeds two steps)
   bf16x8_t qf[kKSteps];
   {
     const int h = kHeads * wv + r32;
-    const float* ql = a.q_lat + (static_cast<int64_t>(b) * nh + h) * kDc + 8 * g2;
+    const float* ql = a.q_lat + (static_cast<int64_t>(b) * nh + h) * kDc;
     const float* qp = a.q_pe + (static_cast<int64_t>(b) * nh + h) * kDr + 8 * g2;
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) {
-      const float* src = ks < kLatSteps ? ql + 16 * ks : qp + 16 * (ks - kLatSteps);
+      const float* src = ks >= kLatSteps ? qp + 16 * (ks - kLatSteps)
+                         : kF8 ? ql + 32 * (ks >> 1) + 16 * g2 + 8 * (ks & 1)
+                               : ql + 16 * ks + 8 * g2;
       float v[8];
       const float4 lo = *reinterpret_cast<const float4*>(src);
       const float4 hi = *reinterpret_cast<const float4*>(src + 4);
@@ -405,7 +470,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
 #pragma unroll
   for (int j = 0; j < 2; ++j) soff[j] = kPitch * r32 + 16 * ((2 * j + g2) ^ ky);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) roff[q] = kRopeOff + 128 * r32 + 16 * ((2 * q + g2) ^ vy);
+  for (int q = 0; q < 4; ++q) roff[q] = (kF8 ? kF8RopeOff : kRopeOff) + 128 * r32 + 16 * ((2 * q + g2) ^ vy);
   // P.C B fragment of 16-lane group (ch, g2), lane s16: token row 16kk + 8jj + 4g2 + (s16 >> 2),
   // columns 32nb + 16ch + 4(s16 & 3)..+3: toff[jj] + 64 nb + 16 kPitch kk
   const int s16 = lane & 15, ch = (lane >> 4) & 1;
@@ -415,10 +480,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
   for (int jj = 0; jj < 2; ++jj)
     toff[jj] = kPitch * (8 * jj + 4 * g2 + (s16 >> 2)) + 16 * (cp ^ (2 * jj + g2)) + 8 * (s16 & 1);
   const uint32_t ring0 = lds_addr(ring);
+  // FP8 staging: score A read of latent steps 2a, 2a+1 (chunk 2a + g2 of row
+  // r32) at f8_soff + 32 ((a & 8) | ((a & 7) ^ f8_fh)); P.C B read (transposed,
+  // 8 tokens x 8 columns per lane pair) of column block nb, token half kk at
+  // f8_toff[kk] + 32 ((nb & 8) | ((nb & 7) ^ f8_m)): lane s16 of group (ch, g2)
+  // reads token row 16kk + 8(m >> 2) + 4g2 + (m & 3), m = s16 >> 1, columns
+  // 32nb + 16ch + 8(s16 & 1)..+7, and ends up with column 32nb + 16ch + s16 of
+  // tokens 16kk + 8(j >> 2) + 4g2 + (j & 3), j = 0..7 (f8key of that row is 2m + g2)
+  const int f8_fk = f8key(r32), f8_fh = f8_fk >> 1, f8_m = s16 >> 1;
+  const uint32_t f8_soff = kDc * r32 + 16 * (g2 ^ (f8_fk & 1));
+  uint32_t f8_toff[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+    f8_toff[kk] = kDc * (16 * kk + 8 * (f8_m >> 2) + 4 * g2 + (f8_m & 3)) + 16 * (ch ^ g2) +
+                  8 * (s16 & 1);
 
   // scores S^T[t, h] of the tile in slot T: lane holds head 32wv + r32 and
   // tokens 8(i >> 2) + 4g2 + (i & 3), i = 0..15
-  auto scores = [&](uint32_t T) {
+  // `hook` runs once, after the first products are issued (the next tile's
+  // copies go out there, in the shadow of the products)
+  auto scores = [&](uint32_t T, auto&& hook) {
     f32x16_t acc;
     const uint32_t sa0 = T + soff[0], sa1 = T + soff[1];
     auto lda = [&](int ks) {
@@ -443,6 +524,44 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
         else if (k == kKSteps - 1) mfma_v_last(acc, ar[k % kARing], qf[k]);
         else mfma_v(acc, ar[k % kARing], qf[k]);
       }
+      if (ks == 0) hook();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return acc;
+  };
+  // FP8: scores of the staged tile at T.  Read a < 16 holds latent steps 2a
+  // (bytes 0-7) and 2a + 1 (bytes 8-15), dequantized with row r32's scale by the
+  // conversion; reads 16..19 are the bf16 k^R steps.
+  auto scores_f8 = [&](uint32_t T, auto&& hook) {
+    f32x16_t acc;
+    const float sg = lds_f32(T + kF8ScaleLds + 4 * r32);
+    auto ldc = [&](int g) {
+      return g < 16 ? lds_ld128(T + f8_soff + 32 * ((g & 8) | ((g & 7) ^ f8_fh)))
+                    : lds_ld128(T + roff[g < 16 ? 0 : g - 16]);
+    };
+    constexpr int kRead = 20, kAhead = kARingF8;
+    u32x4_t cr[kAhead + 1];
+#pragma unroll
+    for (int d = 0; d < kAhead; ++d) cr[d] = ldc(d);
+#pragma unroll
+    for (int g = 0; g < kRead; ++g) {
+      if (g + kAhead < kRead) cr[(g + kAhead) % (kAhead + 1)] = ldc(g + kAhead);
+      wait_lgkm(min(kAhead, kRead - 1 - g));
+      const u32x4_t v = cr[g % (kAhead + 1)];
+      if (g < 16) {
+        const bf16x8_t lo = f8x8((u32x2_t){v[0], v[1]}, sg), hi = f8x8((u32x2_t){v[2], v[3]}, sg);
+        if (g == 0) {
+          acc = mfma_v_first(lo, qf[0]);
+        } else {
+          mfma_v_nop(acc, lo, qf[2 * g]);
+        }
+        mfma_v_nop(acc, hi, qf[2 * g + 1]);
+      } else if (g < kRead - 1) {
+        mfma_v(acc, __builtin_bit_cast(bf16x8_t, v), qf[kLatSteps + g - 16]);
+      } else {
+        mfma_v_last(acc, __builtin_bit_cast(bf16x8_t, v), qf[kLatSteps + g - 16]);
+      }
+      if (g == 0) hook();
       __builtin_amdgcn_sched_barrier(0);
     }
     return acc;
@@ -468,11 +587,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
   const uint32_t voff_hi = kRowBytes * (8 * wv + 4) + 16 * (lane ^ lkey(8 * wv + 4));
   const uint32_t voff_rope = kRowBytes * (8 * wv + (lane >> 3)) + 2 * kDc +
                              16 * ((lane & 7) ^ rkey(8 * wv + (lane >> 3)));
-  // start the copy of tile j into slot j & 3; returns its count of valid rows
-  auto issue = [&](int j) {
+  // page id of tile j, as loaded from the window (reloaded first when tile j is
+  // past it; uniform), so that the wait for the read falls where the id is used
+  auto page_load = [&](int j) {
     const int tok = t0 + j * kTileTok;
     if (tok / kPage - wbase >= kPageWin) load_window(tok / kPage);   // splits > kPageWin pages
-    const int pg = __builtin_amdgcn_readfirstlane(pwin[tok / kPage - wbase]);   // uniform
+    return pwin[tok / kPage - wbase];
+  };
+  // start the copy of tile j (page id pgv from page_load) into slot j & 3;
+  // returns its count of valid rows
+  auto issue_pg = [&](int j, int pgv) {
+    const int tok = t0 + j * kTileTok;
+    const int pg = __builtin_amdgcn_readfirstlane(pgv);   // uniform
     const bool ok = pg >= 0 && pg < a.num_pages;
     bad_page |= !ok;
     const uint32_t slot = ring0 + (j & 3) * kTileBytes;
@@ -487,53 +613,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
     }
     return nvalid;
   };
+  auto issue = [&](int j) { return issue_pg(j, page_load(j)); };
 
-  // FP8 pool: copy of tile j into staging slot j & 1; returns its valid rows
-  const uint32_t stage0 = ring0 + 3 * kTileBytes;
-  auto issue_f8 = [&](int j) {
+  // FP8 pool: tile j is staged in slot j % kF8Slots; start its copy, return its valid rows
+  auto stage_of = [&](int j) { return ring0 + static_cast<uint32_t>(j % kF8Slots) * kF8Stage; };
+  auto issue_pg_f8 = [&](int j, int pgv) {
     const int tok = t0 + j * kTileTok;
-    if (tok / kPage - wbase >= kPageWin) load_window(tok / kPage);   // splits > kPageWin pages
-    const int pg = __builtin_amdgcn_readfirstlane(pwin[tok / kPage - wbase]);   // uniform
+    const int pg = __builtin_amdgcn_readfirstlane(pgv);   // uniform
     const bool ok = pg >= 0 && pg < a.num_pages;
     bad_page |= !ok;
-    tile_issue_f8(pool, pg, ok, tok, t1, stage0 + (j & 1) * kF8Stage, wv, lane);
+    tile_issue_f8(pool, pg, ok, tok, t1, stage_of(j), wv, lane);
     return ok ? min(kTileTok, t1 - tok) : 0;
   };
-  // FP8 pool: dequantize this wave's 8 rows of the staged tile into the bf16 tile
-  // at T: per step 16 e4m3 values -> two 16-byte bf16 chunks (the power-of-two
-  // row scale applied exactly by the conversion), and the bf16 k^R copied.
-  // Rows past the valid ones are written as zeros (their scores are masked, and
-  // zero weights times zeros keep O finite whatever those bytes held).  Ends
-  // with its LDS writes complete, so that a barrier publishes the tile.
-  auto convert_f8 = [&](uint32_t stage, uint32_t T, int nvalid) {
-    const int rl = lane >> 3, rr = 8 * wv + rl, q0 = lane & 7;
-    const bool live = rr < nvalid;
-    const uint32_t srow = stage + 5120 * wv + kF8Row * rl;
-    const float sig = live ? *reinterpret_cast<const __attribute__((address_space(3))) float*>(
-                                 static_cast<uintptr_t>(stage + kTileTok * kF8Row + 4 * rr))
-                           : 1.f;
-    const u32x4_t zero = {0u, 0u, 0u, 0u};
-    const int key = lkey(rr);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int q = q0 + 8 * k;                     // 16-byte chunk of e4m3 values 16q..16q+15
-      const u32x4_t v = lds_ld128(srow + 16 * q);
-      u32x4_t lo, hi;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {   // bytes 0-1 (word 0) then 2-3 (word 1) of each dword
-        lo[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[j], sig, false));
-        lo[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[j], sig, true));
-        hi[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[2 + j], sig, false));
-        hi[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[2 + j], sig, true));
-      }
-      lds_st128(T + kPitch * rr + 16 * ((2 * q) ^ key), live ? lo : zero);
-      lds_st128(T + kPitch * rr + 16 * ((2 * q + 1) ^ key), live ? hi : zero);
-    }
-    const u32x4_t rope = lds_ld128(srow + kDc + 16 * q0);
-    lds_st128(T + kRopeOff + 1024 * (rr >> 3) + 128 * (rr & 7) + 16 * (q0 ^ rkey(rr)),
-              live ? rope : zero);
-    wait_lgkm(0);
-  };
+  auto issue_f8 = [&](int j) { return issue_pg_f8(j, page_load(j)); };
 
   float seen = -INFINITY;     // largest raw score of this lane in this pass
   float p[16];                // softmax weights of the tile being scored
@@ -573,6 +665,61 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  // FP8: rows nvalid..31 of the staged tile at T that this wave copied get zero
+  // codes and a zero scale (for a page outside the pool they may hold any
+  // bytes, NaN codes included), so that they add nothing to P'.codes; called
+  // for partial tiles only, its LDS writes complete on return
+  auto zero_tail = [&](uint32_t T, int nvalid) {
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 8 * wv + 2 * i + (lane >> 5);
+      if (r >= nvalid) lds_st128(T + kDc * r + 16 * (lane & 31), zero);
+    }
+    if (lane < 8 && 8 * wv + lane >= nvalid) lds_st32(T + kF8ScaleLds + 4 * (8 * wv + lane), 0u);
+    wait_lgkm(0);
+  };
+  // FP8: O += P'.codes over the staged tile at T, the B operand read transposed
+  // as 8 codes per lane and turned into bf16 unscaled (P' carries the row scales)
+  auto pv_product_f8 = [&](uint32_t T, const bf16x8_t& pp0, const bf16x8_t& pp1, bool next,
+                           const f32x16_t& x, float mr) {
+    auto ldb = [&](int m) {   // product m: column block m >> 1, token half m & 1
+      const int nb = m >> 1;
+      return lds_tr8(T + f8_toff[m & 1] + 32 * ((nb & 8) | ((nb & 7) ^ f8_m)));
+    };
+    constexpr int kRing = kBRingF8;
+    u32x2_t br[kRing];
+#pragma unroll
+    for (int d = 0; d < kRing - 2; ++d) br[d] = ldb(d);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int m = 0; m < 2 * kColBlocks; m += 2) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        if (m + kRing - 2 + e < 2 * kColBlocks) br[(m + kRing - 2 + e) % kRing] = ldb(m + kRing - 2 + e);
+      wait_lgkm(min(kRing - 2, 2 * kColBlocks - m - 2));
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        o[m >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e ? pp1 : pp0,
+                                                             f8x8(br[(m + e) % kRing], 1.0f),
+                                                             o[m >> 1], 0, 0, 0);
+      if (next) weight(x, m >> 1, mr);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // FP8: P' = p times the row scale of each of this lane's 16 tokens (rows past
+  // the valid ones have p = 0 and, after zero_tail, scale 0), packed as the A operand
+  auto scale_p = [&](uint32_t T, bf16x8_t& q0, bf16x8_t& q1) {
+    float ps[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4_t sv = lds_ld128(T + kF8ScaleLds + 4 * (8 * q + 4 * g2));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ps[4 * q + e] = p[4 * q + e] * __uint_as_float(sv[e]);
+    }
+    q0 = pack8(ps);
+    q1 = pack8(ps + 8);
+  };
   auto weight_sum = [&]() {
     l_part += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])) +
               (((p[8] + p[9]) + (p[10] + p[11])) + ((p[12] + p[13]) + (p[14] + p[15])));
@@ -593,11 +740,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
     if constexpr (!kF8) {
       int nv0 = issue(0), nv1 = 0, nv2 = 0;   // valid rows of tiles t, t+1, t+2
       if (ntiles > 1) nv1 = issue(1);
-      // ---- tile 0: scores and weights
+      // ---- tile 0: scores and weights (tile 2's copy starts among the products)
+      const int pgv2 = ntiles > 2 ? page_load(2) : 0;
       wait_tile(ntiles > 1 ? 1 : 0);
       lds_barrier();
-      if (ntiles > 2) nv2 = issue(2);
-      sc = scores(ring0);
+      sc = scores(ring0, [&] { if (ntiles > 2) nv2 = issue_pg(2, pgv2); });
       mask(sc, nv0);
       if (pass == 0) {            // the first tile fixes the reference
         float tm = sc[0];
@@ -614,10 +761,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
       nv0 = nv1; nv1 = nv2;
       // ---- tile t: scores, then the products of tile t-1 with the weights of tile t between them
       for (int t = 1; t < ntiles; ++t) {
+        const bool more = t + 2 < ntiles;
+        const int pgv = more ? page_load(t + 2) : 0;
         wait_tile(t + 1 < ntiles ? 1 : 0);
         lds_barrier();   // tile t is in LDS for every wave; the slot of tile t-2 is free
-        if (t + 2 < ntiles) nv2 = issue(t + 2);
-        sc = scores(ring0 + (t & 3) * kTileBytes);
+        sc = scores(ring0 + (t & 3) * kTileBytes, [&] { if (more) nv2 = issue_pg(t + 2, pgv); });
         mask(sc, nv0);
         pv_product(ring0 + ((t - 1) & 3) * kTileBytes, pp0, pp1, true, sc, mr);
         weight_sum();
@@ -627,14 +775,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
       }
       pv_product(ring0 + ((ntiles - 1) & 3) * kTileBytes, pp0, pp1, false, sc, mr);
     } else {
-      int nv0 = issue_f8(0), nv1 = 0, nv2 = 0;   // valid rows of tiles t, t+1, t+2
+      // valid rows of tiles t .. t+kF8Ahead (tiles are copied kF8Ahead ahead)
+      int nv0 = issue_f8(0), nv1 = 0, nv2 = 0, nv3 = 0, nv4 = 0;
       if (ntiles > 1) nv1 = issue_f8(1);
-      // ---- tile 0: dequantized, then scores and weights
-      wait_tile_f8(ntiles > 1 ? 1 : 0);
-      convert_f8(stage0, ring0, nv0);
-      lds_barrier();
       if (ntiles > 2) nv2 = issue_f8(2);
-      sc = scores(ring0);
+      if (ntiles > 3) nv3 = issue_f8(3);
+      // ---- tile 0: scores and weights (tile kF8Ahead's copy starts among the products)
+      const int pgv4 = ntiles > kF8Ahead ? page_load(kF8Ahead) : 0;
+      wait_tile_f8(min(kF8Ahead - 1, ntiles - 1));
+      if (nv0 < kTileTok) zero_tail(stage_of(0), nv0);
+      lds_barrier();
+      sc = scores_f8(stage_of(0), [&] { if (ntiles > kF8Ahead) nv4 = issue_pg_f8(kF8Ahead, pgv4); });
       mask(sc, nv0);
       if (pass == 0) {          // the first tile fixes the reference
         float tm = sc[0];
@@ -646,35 +797,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
 #pragma unroll
       for (int i = 0; i < 16; ++i) weight(sc, i, mr);
       weight_sum();
-      pp0 = pack8(p);
-      pp1 = pack8(p + 8);
-      if (ntiles > 1) {
-        wait_tile_f8(ntiles > 2 ? 1 : 0);
-        convert_f8(stage0 + kF8Stage, ring0 + kTileBytes, nv1);
-      }
-      nv0 = nv1; nv1 = nv2;
-      // ---- tile t: scores, the products of tile t-1 with the weights of tile t
-      // between them, then tile t+1 dequantized (bf16 slots mod 3, staging mod 2)
-      int cur = 1, prev = 0;
+      scale_p(stage_of(0), pp0, pp1);
+      nv0 = nv1; nv1 = nv2; nv2 = nv3; nv3 = nv4;
+      // ---- tile t: scores, then the products of tile t-1 with the weights of tile t between them
       for (int t = 1; t < ntiles; ++t) {
-        lds_barrier();   // tile t is dequantized for every wave; its staging slot and the bf16 slot of tile t-2 are free
-        if (t + 2 < ntiles) nv2 = issue_f8(t + 2);
-        const int nxt = cur == 2 ? 0 : cur + 1;
-        sc = scores(ring0 + cur * kTileBytes);
+        const bool more = t + kF8Ahead < ntiles;
+        const int pgv = more ? page_load(t + kF8Ahead) : 0;
+        wait_tile_f8(min(kF8Ahead - 1, ntiles - 1 - t));
+        if (nv0 < kTileTok) zero_tail(stage_of(t), nv0);
+        lds_barrier();   // tile t is staged for every wave; the slot of tile t-2 is free
+        sc = scores_f8(stage_of(t), [&] { if (more) nv4 = issue_pg_f8(t + kF8Ahead, pgv); });
         mask(sc, nv0);
-        pv_product(ring0 + prev * kTileBytes, pp0, pp1, true, sc, mr);
+        pv_product_f8(stage_of(t - 1), pp0, pp1, true, sc, mr);
         weight_sum();
-        pp0 = pack8(p);
-        pp1 = pack8(p + 8);
-        if (t + 1 < ntiles) {
-          wait_tile_f8(t + 2 < ntiles ? 1 : 0);
-          convert_f8(stage0 + ((t + 1) & 1) * kF8Stage, ring0 + nxt * kTileBytes, nv1);
-        }
-        nv0 = nv1; nv1 = nv2;
-        prev = cur;
-        cur = nxt;
+        scale_p(stage_of(t), pp0, pp1);
+        nv0 = nv1; nv1 = nv2; nv2 = nv3; nv3 = nv4;
       }
-      pv_product(ring0 + prev * kTileBytes, pp0, pp1, false, sc, mr);
+      pv_product_f8(stage_of(ntiles - 1), pp0, pp1, false, sc, mr);
     }
     // every copy has landed (the last tile was waited for with vmcnt 0)
     seen = fmaxf(seen, __shfl_xor(seen, 32, 64)) * cs;

@@ -270,6 +270,52 @@ def test_decode_attention_fp8(name, lens, S, page, path):
     assert M.mla_device_error() == 0
 
 
+def _row_factor(phys):
+    """Per-row magnitude 2^((p % 7) - 3) of physical row p: neighbouring rows of a
+    tile get different scales."""
+    return np.ldexp(1.0, (np.asarray(phys) % 7) - 3)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_attention_fp8_rows_with_different_scales(path):
+    """Each row's own scale must weigh its codes: rows of one tile alternate over
+    seven magnitudes (2^-3 .. 2^3), so a scale taken from the wrong row shows."""
+    w = _wl("full-fp8", batch=3)
+    lens = (1000, 4096, 77)
+    S = 4
+    M.mla_set_kernel_path(path)
+    note(f"attention fp8 varied row scales path={path}")
+    d = _dims(w)
+    bt, total = I.page_table(w, np.array(lens, dtype=np.int32))
+    nh = w.n_heads
+    rows = torch.empty((total * 64, w.row), dtype=torch.float32, device="cuda")
+    I.fill_device(rows, I.stream_key(w.seed, "pool"))
+    fac = torch.tensor(_row_factor(np.arange(total * 64)), dtype=torch.float32, device="cuda")
+    rows *= fac[:, None]
+    pool = torch.empty((total, M.mla_fp8_page_bytes(d)), dtype=torch.uint8, device="cuda")
+    phys = torch.arange(total * 64, dtype=torch.int32, device="cuda")
+    M.mla_quantize_rows_fp8(d, rows, (phys // 64).contiguous(), (phys % 64).contiguous(),
+                            torch.arange(total, dtype=torch.int32, device="cuda").reshape(-1, 1), pool)
+    q_lat = device_tensor(torch, w, "q_lat_in", (3, nh, w.d_latent), 0.5).float().contiguous()
+    q_pe = device_tensor(torch, w, "q_pe_in", (3, nh, w.d_rope), 1.0).float().contiguous()
+    o_part = torch.full((3, S, nh, w.d_latent), 123.0, device="cuda")
+    lse_part = torch.full((3, S, nh), 123.0, device="cuda")
+    M.mla_decode_attention_fp8(d, q_lat, q_pe, pool, torch.tensor(bt, device="cuda"),
+                               torch.tensor(np.array(lens, dtype=np.int32), device="cuda"), o_part,
+                               lse_part)
+    hq = host_tensor(w, "q_lat_in", (3, nh, w.d_latent), 0.5)
+    hp = host_tensor(w, "q_pe_in", (3, nh, w.d_rope), 1.0)
+    for b, L in enumerate(lens):
+        pos = np.arange(L)
+        ph = bt[b, pos // 64].astype(np.int64) * 64 + pos % 64
+        src = I.pool_rows(w, bt, b, L, f32=True).astype(np.float64) * _row_factor(ph)[:, None]
+        ro, rl = O.attention_partials(hq[b], hp[b], _fp8_rows(src.astype(np.float32), w.d_latent), S,
+                                      w.d_latent, w.d_rope, M.default_scale(d), 64)
+        assert_parity(to_np(o_part)[b], ro, w.dtype, f"o_part b={b}")
+        assert_parity(to_np(lse_part)[b], rl, w.dtype, f"lse_part b={b}")
+    assert M.mla_device_error() == 0
+
+
 @pytest.mark.parametrize("path", PATHS)
 def test_attention_fp8_skips_bad_page(path):
     """An out-of-pool table entry on the split's first page takes no weight and is

@@ -47,11 +47,11 @@ def parse():
     return p.parse_args()
 
 
-def attention_traffic():
-    """HBM bytes per attention launch from the committed rocprofv3 counter runs
-    (FETCH_SIZE and WRITE_SIZE scaled by a plain-copy calibration), or None when the
-    kernel source changed since they were taken."""
-    path = os.path.join(ROOT, "profiles", "k_attn_mfma_h128_full_traffic.json")
+def attention_traffic(workload: str):
+    """HBM bytes per attention launch on `workload` (4 splits) from the committed
+    rocprofv3 counter runs (FETCH_SIZE and WRITE_SIZE scaled by a plain-copy
+    calibration), or None when there are none or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", f"k_attn_mfma_h128_{workload}_traffic.json")
     try:
         rec = json.load(open(path))
         src = open(os.path.join(ROOT, rec["kernel_source"]), "rb").read()
@@ -201,7 +201,7 @@ def main():
         "attention_mfma_frac": attn_flop / attn_s / 1e12 / BF16_PEAK_TFLOPS,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": attention_traffic() if w.name == "full" and S == 4 else None,
+                     "traffic": attention_traffic(w.name) if S == 4 else None,
                      "kernel": ("k_attn_mfma_h128<true> (mla_decode_attention_fp8)" if w.cache == "fp8"
                                 else "k_attn_mfma_h128<false> (mla_decode_attention)"),
                      "algorithmic_bytes_per_launch": cache_bytes},

@@ -36,7 +36,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="full",
                    help="full | lite | long | full-cq (query compression) | full-fp8 (FP8 latent "
-                        "pool) (one layer each)")
+                        "pool) | full-pre (chunked prefill: 4 x 256 prompt tokens at context "
+                        "4096) (one layer each)")
     p.add_argument("--splits", type=int, default=0, help="KV splits (0 = workload default)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="budget of the oracle timing on the host (0 disables it)")
@@ -64,7 +65,10 @@ def attention_traffic(workload: str):
 
 def cpu_baseline(w, seconds: float):
     """fp64 oracle (non-absorbed definition) on whole sequences of the same
-    workload until `seconds` of host time are spent; tokens/s = sequences/s."""
+    workload until `seconds` of host time are spent; tokens/s = sequences/s.
+    Prefill workloads: the step's prompt tokens of sequence 0, one by one."""
+    if w.chunk:
+        return cpu_baseline_prefill(w, seconds)
     import numpy as np
 
     import oracle as O
@@ -101,12 +105,47 @@ def cpu_baseline(w, seconds: float):
                       + f", {spent:.1f} s of host time"}
 
 
+def cpu_baseline_prefill(w, seconds: float):
+    import numpy as np
+
+    import oracle as O
+    from mla_latent_kv_dkv_amd import inputs as I
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = len(os.sched_getaffinity(0))
+    lens = I.seq_lengths(w)
+    bt, _ = I.page_table(w, lens)
+    wt = {n: I.to_f64(w, I.weight_values(w, n, 0)) for n in w.weight_names}
+    L = int(lens[0])
+    P = L - w.chunk
+    rows = I.to_f64(w, I.pool_rows(w, bt, 0, L))
+    h = I.to_f64(w, I.tensor_values(w, "h_dec", None, 1.0, 0, start=0, count=w.chunk * w.hidden))
+    h = h.reshape(w.chunk, w.hidden)
+    done, spent = 0, 0.0
+    t = time.perf_counter()
+    rows[P:] = O.latent_rows(h, wt["w_dkv"], wt["w_kr"], np.arange(P, L), w.rope_base)
+    spent += time.perf_counter() - t
+    while spent < seconds and done < w.chunk:
+        t = time.perf_counter()
+        O.mla_decode_step(h[done], rows[:P + done + 1], wt["w_q"], wt["w_qr"], wt["w_uk"],
+                          wt["w_uv"], wt["w_o"], P + done, w.n_heads, w.d_head, w.d_latent,
+                          w.d_rope, w.rope_base)
+        spent += time.perf_counter() - t
+        done += 1
+    return {"value": done / spent, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {w.chunk} prompt tokens of sequence 0 (positions {P}..), "
+                      f"non-absorbed fp64 definition, {spent:.1f} s of host time"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    import numpy as np
     import torch
     if args.copy_calibration:
         a = torch.ones(1 << 29, dtype=torch.int16, device="cuda")   # 1 GiB
@@ -128,11 +167,13 @@ def main():
     sets = [DeviceWorkload(w, layer=l, num_splits=S) for l in (0, 1)]
     torch.cuda.synchronize()
     lens = sets[0].lens
+    nq = sets[0].nq                      # the step's tokens (decode: one per sequence)
+    attended = (sets[0].q_pos_host.astype(np.int64) + 1).sum()   # cached rows read per launch
     # bytes of one cached row: d_c + d_R values in dtype, or (FP8 pool) d_c codes,
     # d_R bf16 and one fp32 scale
     row_bytes = (w.d_latent + 2 * w.d_rope + 4) if w.cache == "fp8" else w.row * w.elem_bytes
-    cache_bytes = int(lens.sum()) * row_bytes
-    attn_flop = 2 * w.n_heads * int(lens.sum()) * (2 * w.d_latent + w.d_rope)
+    cache_bytes = int(attended) * row_bytes
+    attn_flop = 2 * w.n_heads * int(attended) * (2 * w.d_latent + w.d_rope)
     stream = torch.cuda.current_stream()
 
     def one(i, ev=None):
@@ -175,9 +216,24 @@ def main():
 
     B = w.batch
     achieved = cache_bytes / attn_s / 1e9
+    tflops = attn_flop / attn_s / 1e12
+    if w.chunk:     # prefill: the attention is a dense contraction; its bound is the MFMA rate
+        roofline = {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": tflops / BF16_PEAK_TFLOPS, "traffic": None,
+                    "kernel": "k_attn_mfma_h128 (mla_prefill_attention)",
+                    "algorithmic_flop_per_launch": attn_flop}
+    else:
+        roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBPS,
+                    "traffic": attention_traffic(w.name) if S == 4 else None,
+                    "kernel": ("k_attn_mfma_h128<true> (mla_decode_attention_fp8)"
+                               if w.cache == "fp8" else
+                               "k_attn_mfma_h128<false> (mla_decode_attention)"),
+                    "algorithmic_bytes_per_launch": cache_bytes}
     line = {
-        "metric": "MLA decode tokens/s + latent-cache GB/s (% roofline), n_h=128 d_c=512 1 GPU",
-        "value": B / step_s,
+        "metric": ("MLA chunked-prefill prompt tokens/s, n_h=128 d_c=512 1 GPU" if w.chunk else
+                   "MLA decode tokens/s + latent-cache GB/s (% roofline), n_h=128 d_c=512 1 GPU"),
+        "value": nq / step_s,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -193,18 +249,15 @@ def main():
                                f"context {int(lens.max())}, {S} KV splits, 64-token pages"
                                + (f", query compression d_c' {w.d_cq}" if w.d_cq else "")
                                + (", FP8 latent pool (e4m3 c^KV + row scale, bf16 k^R)"
-                                  if w.cache == "fp8" else ""),
+                                  if w.cache == "fp8" else "")
+                               + (f", prefill of the last {w.chunk} positions of every sequence "
+                                  f"({nq} prompt tokens per step)" if w.chunk else ""),
                    "batch": B, "context": int(lens.max()), "num_splits": S},
         "latent_cache_GBps": achieved,
         "attention_us": attn_s * 1e6,
-        "attention_mfma_tflops": attn_flop / attn_s / 1e12,
-        "attention_mfma_frac": attn_flop / attn_s / 1e12 / BF16_PEAK_TFLOPS,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": attention_traffic(w.name) if S == 4 else None,
-                     "kernel": ("k_attn_mfma_h128<true> (mla_decode_attention_fp8)" if w.cache == "fp8"
-                                else "k_attn_mfma_h128<false> (mla_decode_attention)"),
-                     "algorithmic_bytes_per_launch": cache_bytes},
+        "attention_mfma_tflops": tflops,
+        "attention_mfma_frac": tflops / BF16_PEAK_TFLOPS,
+        "roofline": roofline,
     }
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

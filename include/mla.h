@@ -135,6 +135,27 @@ mla_status mla_decode_attention(const mla_dims* dims, const float* q_lat, const 
                                 hipStream_t stream);
 
 /*
+ * Prefill (chunked-prefill) attention: many query tokens per sequence, each
+ * attending causally to the latent cache of its own sequence ([Report] §3.1: the
+ * same per-token MLA flow for every prompt token; the pages quote prompt
+ * throughput for it).  Query token i is the token at position q_pos[i] of
+ * sequence q_seq[i]; its row must already be in the pool (append the chunk
+ * first).  It attends to positions 0..q_pos[i] of that sequence, split as in
+ * mla_decode_attention with L = q_pos[i] + 1; outputs are indexed by query:
+ *   q_lat [n_q, n_h, d_c], q_pe [n_q, n_h, d_R] fp32 (from mla_absorb_q with
+ *   batch n_q and pos = q_pos); block_table [n_seqs, max_pages] int32;
+ *   q_seq, q_pos [n_q] int32; o_part [n_q, S, n_h, d_c], lse_part [n_q, S, n_h].
+ * n_q in [0, 65535].  A query whose sequence or position is out of range gets an
+ * empty result (lse = -inf) and sets the device error word.  mla_merge_lse and
+ * mla_absorb_out then run with batch = n_q.
+ */
+mla_status mla_prefill_attention(const mla_dims* dims, const float* q_lat, const float* q_pe,
+                                 const void* pool, int64_t num_pages, const int32_t* block_table,
+                                 int32_t n_seqs, int32_t max_pages, const int32_t* q_seq,
+                                 const int32_t* q_pos, int32_t n_q, int32_t num_splits,
+                                 float* o_part, float* lse_part, hipStream_t stream);
+
+/*
  * Log-sum-exp merge of split partials: per (b, i), m = max_s lse_s,
  * w_s = exp(lse_s - m), o_lat = sum_s w_s o_s / sum_s w_s, lse = m + log sum_s w_s.
  * Splits with lse = -inf weigh 0; a row whose every split is empty gives
@@ -259,6 +280,15 @@ mla_status mla_decode_attention_fp8(const mla_dims* dims, const float* q_lat, co
                                     const int32_t* block_table, int32_t max_pages,
                                     const int32_t* seq_lens, int32_t batch, int32_t num_splits,
                                     float* o_part, float* lse_part, hipStream_t stream);
+
+/* Prefill attention over the FP8 pool (as mla_prefill_attention, rows dequantized
+ * as in mla_decode_attention_fp8). */
+mla_status mla_prefill_attention_fp8(const mla_dims* dims, const float* q_lat, const float* q_pe,
+                                     const void* pool, int64_t num_pages,
+                                     const int32_t* block_table, int32_t n_seqs,
+                                     int32_t max_pages, const int32_t* q_seq,
+                                     const int32_t* q_pos, int32_t n_q, int32_t num_splits,
+                                     float* o_part, float* lse_part, hipStream_t stream);
 
 /* Static text for a status code. */
 const char* mla_status_string(int32_t status);

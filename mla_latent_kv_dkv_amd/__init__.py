@@ -24,7 +24,7 @@ __all__ = ["MlaDims", "MlaError", "make_dims", "load", "mla_append_latent", "mla
            "mla_append_workspace_bytes", "mla_device_error", "mla_set_kernel_path",
            "mla_status_string", "mla_fp8_page_bytes", "mla_quantize_rows_fp8",
            "mla_append_latent_fp8", "mla_append_workspace_bytes_fp8", "mla_decode_attention_fp8",
-           "LIB_PATH"]
+           "mla_prefill_attention", "mla_prefill_attention_fp8", "LIB_PATH"]
 
 
 class MlaDims(ctypes.Structure):
@@ -68,6 +68,9 @@ _SIGS = {
                               _P],
     "mla_append_workspace_bytes_fp8": [_DIMS, _I32],
     "mla_decode_attention_fp8": [_DIMS, _P, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _P, _P, _P],
+    "mla_prefill_attention": [_DIMS, _P, _P, _P, _I64, _P, _I32, _I32, _P, _P, _I32, _I32, _P, _P, _P],
+    "mla_prefill_attention_fp8": [_DIMS, _P, _P, _P, _I64, _P, _I32, _I32, _P, _P, _I32, _I32, _P, _P,
+                                  _P],
     "mla_status_string": [_I32],
     "mla_abi_version": [],
     "mla_device_error": [ctypes.POINTER(_I32), _I32, _P],
@@ -340,6 +343,39 @@ def mla_decode_attention_fp8(dims, q_lat, q_pe, pool, block_table, seq_lens, o_p
     _check("mla_decode_attention_fp8", load().mla_decode_attention_fp8(
         ctypes.byref(dims), _ptr(q_lat), _ptr(q_pe), _ptr(pool), pool.shape[0], _ptr(block_table),
         block_table.shape[1], _ptr(seq_lens), B, S, _ptr(o_part), _ptr(lse_part), _stream(stream)))
+
+
+# -------------------------------------------------------------- prefill --
+def mla_prefill_attention(dims, q_lat, q_pe, pool, block_table, q_seq, q_pos, o_part, lse_part,
+                          stream=None, fp8=False):
+    """Causal attention of query tokens (q_seq[i], q_pos[i]) over their sequences'
+    cached rows 0..q_pos[i]; the split count is o_part.shape[1].  ``fp8``: the pool
+    is an FP8 pool (uint8 [num_pages, mla_fp8_page_bytes(dims)])."""
+    import torch
+    n, S = o_part.shape[0], o_part.shape[1]
+    nh = dims.n_heads
+    _expect(q_lat, (n, nh, dims.d_latent), torch.float32, "q_lat")
+    _expect(q_pe, (n, nh, dims.d_rope), torch.float32, "q_pe")
+    if fp8:
+        _expect_fp8_pool(dims, pool)
+    else:
+        _expect(pool, (pool.shape[0], dims.page_size, dims.d_latent + dims.d_rope), _elem(dims), "pool")
+    _expect(q_seq, (n,), torch.int32, "q_seq")
+    _expect(q_pos, (n,), torch.int32, "q_pos")
+    _expect(o_part, (n, S, nh, dims.d_latent), torch.float32, "o_part")
+    _expect(lse_part, (n, S, nh), torch.float32, "lse_part")
+    _expect_table(block_table)
+    fn = "mla_prefill_attention_fp8" if fp8 else "mla_prefill_attention"
+    _check(fn, getattr(load(), fn)(
+        ctypes.byref(dims), _ptr(q_lat), _ptr(q_pe), _ptr(pool), pool.shape[0], _ptr(block_table),
+        block_table.shape[0], block_table.shape[1], _ptr(q_seq), _ptr(q_pos), n, S, _ptr(o_part),
+        _ptr(lse_part), _stream(stream)))
+
+
+def mla_prefill_attention_fp8(dims, q_lat, q_pe, pool, block_table, q_seq, q_pos, o_part, lse_part,
+                              stream=None):
+    mla_prefill_attention(dims, q_lat, q_pe, pool, block_table, q_seq, q_pos, o_part, lse_part,
+                          stream, fp8=True)
 
 
 def default_scale(dims: MlaDims) -> float:

@@ -41,6 +41,37 @@ __device__ __forceinline__ void rope_cs(int pos, int k, int d_rope, double log_b
   *s = static_cast<float>(sd);
 }
 
+// Block-table row and attended length of attention unit b.  Decode (q_seq null):
+// sequence b, length seq_lens[b].  Prefill: query token b at position q_pos[b] of
+// sequence q_seq[b], length q_pos[b] + 1 (causal, the token itself included).  A
+// value out of range flags the error word (when `flag`) and gives length 0.
+__device__ __forceinline__ void unit_seq_len(const int32_t* seq_lens, const int32_t* q_seq,
+                                             const int32_t* q_pos, int n_seqs, int max_len, int b,
+                                             bool flag, int* err, int* seq, int* len) {
+  int s = b, L;
+  if (q_seq) {
+    s = q_seq[b];
+    const int p = q_pos[b];
+    L = p + 1;
+    if (s < 0 || s >= n_seqs) {
+      if (flag) set_err(err, ERR_SEQ);
+      s = 0;
+      L = 0;
+    } else if (p < 0 || p >= max_len) {
+      if (flag) set_err(err, ERR_POS);
+      L = 0;
+    }
+  } else {
+    L = seq_lens[b];
+    if (L < 0 || L > max_len) {
+      if (flag) set_err(err, ERR_POS);
+      L = 0;
+    }
+  }
+  *seq = s;
+  *len = L;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

@@ -407,11 +407,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
   const int b = unit / S, s = unit - b * S;
   const int nh = 128;
 
-  int L = seq_lens[b];
-  if (L < 0 || L > a.max_pages * kPage) {
-    if (tid == 0) set_err(a.err, ERR_POS);
-    L = 0;
-  }
+  int sq, L;
+  unit_seq_len(seq_lens, a.q_seq, a.q_pos, a.n_seqs, a.max_pages * kPage, b, tid == 0, a.err, &sq,
+               &L);
+  sq = __builtin_amdgcn_readfirstlane(sq);   // uniform by construction; say so for the
+  L = __builtin_amdgcn_readfirstlane(L);     // scalar operands of the copies
+
   int t0, t1;
   split_range(L, S, s, kPage, &t0, &t1);
 
@@ -424,7 +425,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
     if (lane < kHeads) lse_out[lane] = -INFINITY;
     return;
   }
-  const int32_t* bt = block_table + static_cast<int64_t>(b) * a.max_pages;
+  const int32_t* bt = block_table + static_cast<int64_t>(sq) * a.max_pages;
   const int p_first = t0 / kPage, p_end = (t1 - 1) / kPage + 1;
   int wbase = -1;
   // (uniform) make pwin hold pages [base, base + kPageWin); drains every copy

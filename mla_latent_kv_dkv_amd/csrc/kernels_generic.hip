@@ -132,11 +132,9 @@ __global__ __launch_bounds__(256) void k_attention_generic(AttnArgs a) {
   const int i = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nh = a.n_heads;
-  int L = a.seq_lens[b];
-  if (L < 0 || L > a.max_pages * a.page_size) {
-    if (tid == 0) set_err(a.err, ERR_POS);
-    L = 0;
-  }
+  int sq, L;
+  unit_seq_len(a.seq_lens, a.q_seq, a.q_pos, a.n_seqs, a.max_pages * a.page_size, b, tid == 0,
+               a.err, &sq, &L);
   int t0, t1;
   split_range(L, a.num_splits, s, a.page_size, &t0, &t1);
 
@@ -153,7 +151,7 @@ __global__ __launch_bounds__(256) void k_attention_generic(AttnArgs a) {
     float sc = -INFINITY, rs = 0.f;
     int64_t off = -1;
     if (j < t1) {
-      const int page = a.block_table[static_cast<int64_t>(b) * a.max_pages + j / a.page_size];
+      const int page = a.block_table[static_cast<int64_t>(sq) * a.max_pages + j / a.page_size];
       if (page < 0 || page >= a.num_pages) {
         set_err(a.err, ERR_PAGE);
       } else {

@@ -55,6 +55,12 @@ struct AttnArgs {
   float* o_part;
   float* lse_part;
   int* err;
+  // prefill: unit b is query token b at position q_pos[b] of sequence q_seq[b]
+  // (block-table row q_seq[b], attended length q_pos[b] + 1); null for decode,
+  // where unit b is sequence b with length seq_lens[b]
+  const int32_t* q_seq;
+  const int32_t* q_pos;
+  int n_seqs;
 };
 
 hipError_t launch_attention_generic(const AttnArgs& a, bool bf16, hipStream_t stream);

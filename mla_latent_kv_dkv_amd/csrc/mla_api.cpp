@@ -217,29 +217,47 @@ size_t rows_bytes(const mla_dims* d, int n_rows) {
   return align256(static_cast<size_t>(n_rows) * (d->d_latent + d->d_rope) * sizeof(float));
 }
 
-// Checks shared by the two attention calls; fills `a` (pool format aside).
-mla_status attention_args(const mla_dims* d, const float* q_lat, const float* q_pe,
+// Checks shared by the attention calls; fills `a` (pool format aside).  Decode
+// units are sequences (seq_lens); prefill units are query tokens (q_seq, q_pos
+// into n_seqs block-table rows).
+mla_status attention_args(const mla_dims* d, bool prefill, const float* q_lat, const float* q_pe,
                           const void* pool, int64_t num_pages, const int32_t* block_table,
-                          int32_t max_pages, const int32_t* seq_lens, int32_t batch,
-                          int32_t num_splits, float* o_part, float* lse_part, mla::AttnArgs* a) {
+                          int32_t max_pages, const int32_t* seq_lens, const int32_t* q_seq,
+                          const int32_t* q_pos, int32_t n_seqs, int32_t batch, int32_t num_splits,
+                          float* o_part, float* lse_part, mla::AttnArgs* a) {
   mla_status st = check_dims(d);
   if (st != MLA_OK) return st;
   if (batch < 0 || batch > 65535 || num_splits < 1 || num_splits > 4096 || max_pages < 1 ||
       num_pages < 1)
     return MLA_ERR_SHAPE;
   if (static_cast<int64_t>(max_pages) * d->page_size > (int64_t{1} << 30)) return MLA_ERR_SHAPE;
+  if (prefill && n_seqs < 1) return MLA_ERR_SHAPE;
   if (batch == 0) return MLA_OK;
-  if (!q_lat || !q_pe || !pool || !block_table || !seq_lens || !o_part || !lse_part)
-    return MLA_ERR_NULL;
+  if (!q_lat || !q_pe || !pool || !block_table || !o_part || !lse_part) return MLA_ERR_NULL;
+  if (prefill ? (!q_seq || !q_pos) : !seq_lens) return MLA_ERR_NULL;
   int* err = err_word();
   if (!err) return MLA_ERR_HIP;
   *a = mla::AttnArgs{};
   a->q_lat = q_lat; a->q_pe = q_pe; a->pool = pool; a->num_pages = num_pages;
-  a->block_table = block_table; a->max_pages = max_pages; a->seq_lens = seq_lens;
+  a->block_table = block_table; a->max_pages = max_pages; a->seq_lens = prefill ? nullptr : seq_lens;
   a->batch = batch; a->num_splits = num_splits; a->n_heads = d->n_heads;
   a->d_latent = d->d_latent; a->d_rope = d->d_rope; a->page_size = d->page_size;
   a->scale = softmax_scale(d); a->o_part = o_part; a->lse_part = lse_part; a->err = err;
+  a->q_seq = prefill ? q_seq : nullptr; a->q_pos = prefill ? q_pos : nullptr;
+  a->n_seqs = prefill ? n_seqs : batch;
   return MLA_OK;
+}
+
+hipError_t launch_attention_plain(const mla_dims* d, const mla::AttnArgs& a, hipStream_t stream) {
+  const bool bf16 = d->dtype == MLA_BF16;
+  if (use_fast() && bf16 && mla::fast_attention_ok(a)) return mla::launch_attention_fast(a, stream);
+  return mla::launch_attention_generic(a, bf16, stream);
+}
+
+hipError_t launch_attention_f8(const mla_dims* d, const mla::AttnArgs& a, hipStream_t stream) {
+  if (use_fast() && d->dtype == MLA_BF16 && mla::fast_attention_ok(a))
+    return mla::launch_attention_fp8(a, stream);
+  return mla::launch_attention_generic_fp8(a, stream);
 }
 
 }  // namespace
@@ -386,13 +404,24 @@ mla_status mla_decode_attention(const mla_dims* d, const float* q_lat, const flo
                                 int32_t num_splits, float* o_part, float* lse_part,
                                 hipStream_t stream) {
   mla::AttnArgs a{};
-  mla_status st = attention_args(d, q_lat, q_pe, pool, num_pages, block_table, max_pages, seq_lens,
-                                 batch, num_splits, o_part, lse_part, &a);
+  mla_status st = attention_args(d, false, q_lat, q_pe, pool, num_pages, block_table, max_pages,
+                                 seq_lens, nullptr, nullptr, batch, batch, num_splits, o_part,
+                                 lse_part, &a);
   if (st != MLA_OK || batch == 0) return st;
-  const bool bf16 = d->dtype == MLA_BF16;
-  if (use_fast() && bf16 && mla::fast_attention_ok(a))
-    return hip_status(mla::launch_attention_fast(a, stream));
-  return hip_status(mla::launch_attention_generic(a, bf16, stream));
+  return hip_status(launch_attention_plain(d, a, stream));
+}
+
+mla_status mla_prefill_attention(const mla_dims* d, const float* q_lat, const float* q_pe,
+                                 const void* pool, int64_t num_pages, const int32_t* block_table,
+                                 int32_t n_seqs, int32_t max_pages, const int32_t* q_seq,
+                                 const int32_t* q_pos, int32_t n_q, int32_t num_splits,
+                                 float* o_part, float* lse_part, hipStream_t stream) {
+  mla::AttnArgs a{};
+  mla_status st = attention_args(d, true, q_lat, q_pe, pool, num_pages, block_table, max_pages,
+                                 nullptr, q_seq, q_pos, n_seqs, n_q, num_splits, o_part, lse_part,
+                                 &a);
+  if (st != MLA_OK || n_q == 0) return st;
+  return hip_status(launch_attention_plain(d, a, stream));
 }
 
 size_t mla_fp8_page_bytes(const mla_dims* d) {
@@ -481,13 +510,28 @@ mla_status mla_decode_attention_fp8(const mla_dims* d, const float* q_lat, const
   if (st != MLA_OK) return st;
   if (!fp8_ok(d)) return MLA_ERR_UNSUPPORTED;
   mla::AttnArgs a{};
-  st = attention_args(d, q_lat, q_pe, pool, num_pages, block_table, max_pages, seq_lens, batch,
-                      num_splits, o_part, lse_part, &a);
+  st = attention_args(d, false, q_lat, q_pe, pool, num_pages, block_table, max_pages, seq_lens,
+                      nullptr, nullptr, batch, batch, num_splits, o_part, lse_part, &a);
   if (st != MLA_OK || batch == 0) return st;
   if (!aligned16(pool)) return MLA_ERR_UNSUPPORTED;
-  if (use_fast() && d->dtype == MLA_BF16 && mla::fast_attention_ok(a))
-    return hip_status(mla::launch_attention_fp8(a, stream));
-  return hip_status(mla::launch_attention_generic_fp8(a, stream));
+  return hip_status(launch_attention_f8(d, a, stream));
+}
+
+mla_status mla_prefill_attention_fp8(const mla_dims* d, const float* q_lat, const float* q_pe,
+                                     const void* pool, int64_t num_pages,
+                                     const int32_t* block_table, int32_t n_seqs,
+                                     int32_t max_pages, const int32_t* q_seq,
+                                     const int32_t* q_pos, int32_t n_q, int32_t num_splits,
+                                     float* o_part, float* lse_part, hipStream_t stream) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (!fp8_ok(d)) return MLA_ERR_UNSUPPORTED;
+  mla::AttnArgs a{};
+  st = attention_args(d, true, q_lat, q_pe, pool, num_pages, block_table, max_pages, nullptr, q_seq,
+                      q_pos, n_seqs, n_q, num_splits, o_part, lse_part, &a);
+  if (st != MLA_OK || n_q == 0) return st;
+  if (!aligned16(pool)) return MLA_ERR_UNSUPPORTED;
+  return hip_status(launch_attention_f8(d, a, stream));
 }
 
 mla_status mla_merge_lse(const mla_dims* d, const float* o_part, const float* lse_part,

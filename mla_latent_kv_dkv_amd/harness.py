@@ -11,7 +11,8 @@ import numpy as np
 from . import (make_dims, mla_absorb_out, mla_absorb_q, mla_absorb_q_cq, mla_append_latent,
                mla_append_latent_fp8, mla_append_workspace_bytes, mla_append_workspace_bytes_fp8,
                mla_decode_attention, mla_decode_attention_fp8, mla_fp8_page_bytes, mla_merge_lse,
-               mla_quantize_rows_fp8, mla_workspace_bytes, mla_workspace_bytes_cq)
+               mla_prefill_attention, mla_quantize_rows_fp8, mla_workspace_bytes,
+               mla_workspace_bytes_cq)
 from . import inputs as I
 
 
@@ -55,8 +56,20 @@ class DeviceWorkload:
         self.bt_host, self.num_pages = I.page_table(w, self.lens)
         B = w.batch
         self.seq_lens = torch.tensor(self.lens, dtype=torch.int32, device=self.dev)
-        self.pos = (self.seq_lens - 1).contiguous()
-        self.seq_ids = torch.arange(B, dtype=torch.int32, device=self.dev)
+        # the step's tokens: the last position of every sequence (decode), or its last
+        # `chunk` positions (prefill); nq of them, token i at (q_seq[i], q_pos[i])
+        self.chunk = w.chunk
+        if self.chunk:
+            qs = np.repeat(np.arange(B, dtype=np.int32), self.chunk)
+            qp = np.concatenate([np.arange(int(L) - self.chunk, int(L), dtype=np.int32)
+                                 for L in self.lens])
+        else:
+            qs = np.arange(B, dtype=np.int32)
+            qp = (self.lens - 1).astype(np.int32)
+        self.q_seq_host, self.q_pos_host = qs, qp
+        self.nq = len(qs)
+        self.seq_ids = torch.tensor(qs, device=self.dev)
+        self.pos = torch.tensor(qp, device=self.dev)
         self.block_table = torch.tensor(self.bt_host, dtype=torch.int32, device=self.dev)
         self.weights = {}
         for name in w.weight_names:
@@ -74,19 +87,20 @@ class DeviceWorkload:
             L = int(self.lens.max())
             self.h_ctx = torch.empty((B, L, w.hidden), dtype=self.dt, device=self.dev)
             I.fill_device(self.h_ctx, I.stream_key(w.seed, "h_ctx", layer))
-            self.h = self.h_ctx[torch.arange(B, device=self.dev), self.pos.long()].contiguous()
+            self.h = self.h_ctx[self.seq_ids.long(), self.pos.long()].contiguous()
             self.pool.zero_()
             if build_cache:
                 self.build_cache_from_h()
         else:
             self.h_ctx = None
-            self.h = torch.empty((B, w.hidden), dtype=self.dt, device=self.dev)
+            self.h = torch.empty((self.nq, w.hidden), dtype=self.dt, device=self.dev)
             I.fill_device(self.h, I.stream_key(w.seed, "h_dec", layer))
             if self.fp8:
                 self.fill_fp8_pool()
             else:
                 I.fill_device(self.pool, I.stream_key(w.seed, "pool", layer))
         nh = w.n_heads
+        B = self.nq      # outputs and scratch are per step token
         wsa = (mla_append_workspace_bytes_fp8 if self.fp8 else mla_append_workspace_bytes)(self.dims, B)
         self.ws_append = torch.empty(max(1, wsa), dtype=torch.uint8, device=self.dev)
         if outputs_from is not None:     # share scratch/output buffers with another layer
@@ -111,13 +125,13 @@ class DeviceWorkload:
         fill_fp8_pool(self.dims, self.pool, I.stream_key(self.w.seed, "pool", self.layer))
 
     def build_cache_from_h(self):
-        """Append rows 0..L_b-2 of every sequence from h_ctx (the context before
-        the decode token) through mla_append_latent."""
+        """Append rows 0..L_b-2 (decode) or 0..L_b-chunk-1 (prefill) of every sequence
+        from h_ctx (the context before the step's tokens) through the append call."""
         torch = self.torch
         B, L = self.h_ctx.shape[0], self.h_ctx.shape[1]
         seqs, poss = [], []
         for b in range(B):
-            n = int(self.lens[b]) - 1
+            n = int(self.lens[b]) - max(1, self.chunk)
             seqs.append(np.full(n, b, dtype=np.int32))
             poss.append(np.arange(n, dtype=np.int32))
         seq = torch.tensor(np.concatenate(seqs), device=self.dev)
@@ -143,6 +157,10 @@ class DeviceWorkload:
                self.pos, self.block_table, self.pool, self.ws_append)
 
     def attention(self):
+        if self.chunk:
+            mla_prefill_attention(self.dims, self.q_lat, self.q_pe, self.pool, self.block_table,
+                                  self.seq_ids, self.pos, self.o_part, self.lse_part, fp8=self.fp8)
+            return
         attend = mla_decode_attention_fp8 if self.fp8 else mla_decode_attention
         attend(self.dims, self.q_lat, self.q_pe, self.pool, self.block_table, self.seq_lens,
                self.o_part, self.lse_part)
@@ -169,15 +187,16 @@ class DeviceWorkload:
         return {n: I.to_f64(self.w, I.weight_values(self.w, n, self.layer))
                 for n in self.w.weight_names}
 
-    def host_h(self, b: int) -> np.ndarray:
-        """fp64 hidden state of the decode token of sequence b."""
-        w, L = self.w, int(self.lens[b])
+    def host_h(self, i: int) -> np.ndarray:
+        """fp64 hidden state of step token i (decode: the token of sequence i)."""
+        w = self.w
+        b, p = int(self.q_seq_host[i]), int(self.q_pos_host[i])
         if w.cache_from_h:
             Lmax = int(self.lens.max())
             v = I.tensor_values(w, "h_ctx", None, 1.0, self.layer,
-                                start=(b * Lmax + L - 1) * w.hidden, count=w.hidden)
+                                start=(b * Lmax + p) * w.hidden, count=w.hidden)
         else:
-            v = I.tensor_values(w, "h_dec", None, 1.0, self.layer, start=b * w.hidden,
+            v = I.tensor_values(w, "h_dec", None, 1.0, self.layer, start=i * w.hidden,
                                 count=w.hidden)
         return I.to_f64(w, v)
 

@@ -168,6 +168,8 @@ class Workload:
     rope_base: float = 10000.0
     d_cq: int = 0                   # query compression rank d_c' (0: q^C = W_Q h)
     cache: str = "dtype"            # pool format: "dtype" rows, or "fp8" pages
+    chunk: int = 0                  # prefill: the last `chunk` positions of every sequence
+                                    # are the step's prompt tokens (0: decode, one token)
     notes: str = field(default="", compare=False)
 
     @property
@@ -224,6 +226,14 @@ WORKLOADS = {
                          cache_from_h=True, cache="fp8"),
     "full-fp8": Workload("full-fp8", 5120, 128, 128, 512, 64, "bf16", 64, 4096, 1011, num_splits=4,
                          cache="fp8"),
+    # chunked prefill: each sequence's last `chunk` positions are prompt tokens of the
+    # step, appended and attending causally (cache before them from h, or drawn)
+    "tiny-pre": Workload("tiny-pre", 64, 4, 16, 32, 8, "f32", 2, 64, 1012, num_splits=2,
+                         cache_from_h=True, page_size=16, chunk=24),
+    "lite-pre": Workload("lite-pre", 2048, 16, 128, 512, 64, "bf16", 4, 1024, 1013, num_splits=2,
+                         cache_from_h=True, chunk=64),
+    "full-pre": Workload("full-pre", 5120, 128, 128, 512, 64, "bf16", 4, 4096, 1014, num_splits=1,
+                         chunk=256),
 }
 
 

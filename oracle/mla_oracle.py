@@ -53,6 +53,7 @@ __all__ = [
     "mla_cache_elems_per_token", "mha_cache_elems_per_token", "E4M3_MAX", "e4m3_values",
     "e4m3_encode", "fp8_row_scale_exponent", "bf16_bits", "fp8_quantize_row",
     "fp8_dequantize_row", "fp8_page_bytes", "fp8_page_image",
+    "prefill_attention_partials", "mla_prefill_step",
 ]
 
 
@@ -260,6 +261,35 @@ def attention_partials(q_lat, q_pe, rows, num_splits: int, d_latent: int, d_rope
         out_o.append(o)
         out_l.append(l)
     return np.stack(out_o), np.stack(out_l)
+
+
+def prefill_attention_partials(q_lat, q_pe, rows, positions, num_splits: int, d_latent: int,
+                               d_rope: int, scale: float, page_size: int = 64):
+    """Chunked-prefill attention of one sequence: query t is the prompt token at
+    position ``positions[t]`` and attends causally to cached rows 0..positions[t]
+    (its own row included) -- every prompt token takes the per-token MLA flow of
+    [Report] §3.1 over the cache as it stands at its position.  Returns, per query,
+    the split partials of :func:`attention_partials` over those rows."""
+    rows = _f64(rows)
+    return [attention_partials(q_lat[t], q_pe[t], rows[:int(p) + 1], num_splits, d_latent,
+                               d_rope, scale, page_size) for t, p in enumerate(positions)]
+
+
+def mla_prefill_step(h_chunk, rows_before, w_q, w_qr, w_dkv, w_kr, w_uk, w_uv, w_o, n_heads: int,
+                     d_head: int, d_latent: int, d_rope: int, base: float, scale=None):
+    """Non-absorbed prefill of a chunk of T prompt tokens of one sequence whose
+    first P = len(rows_before) rows are cached: the chunk's tokens sit at
+    positions P..P+T-1, their latent rows are appended ([Report] §2.2, §2.4), and
+    token t's output is the decode step (:func:`mla_decode_step`) of the context
+    of rows 0..P+t.  Returns dict(u [T, H], o [T, n_h, d_h], lse [T, n_h])."""
+    h_chunk = _f64(h_chunk)
+    P, T = len(rows_before), len(h_chunk)
+    pos = np.arange(P, P + T)
+    rows = np.concatenate([_f64(rows_before).reshape(P, d_latent + d_rope),
+                           latent_rows(h_chunk, w_dkv, w_kr, pos, base)])
+    out = [mla_decode_step(h_chunk[t], rows[:P + t + 1], w_q, w_qr, w_uk, w_uv, w_o, P + t,
+                           n_heads, d_head, d_latent, d_rope, base, scale) for t in range(T)]
+    return {k: np.stack([o[k] for o in out]) for k in ("u", "o", "lse")}
 
 
 def merge_lse(o_parts, lse_parts):

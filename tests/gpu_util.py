@@ -40,6 +40,31 @@ def assert_parity(got, ref, dtype, what=""):
     return err
 
 
+def assert_partials_within_weight_rounding(got, ref, q_lat, q_pe, rows, length, num_splits,
+                                           page, tau, d_latent, what=""):
+    """Split partials of a bf16 MFMA path, element by element.  That path rounds
+    each softmax weight p_j to bf16 (relative error <= 2^-9) before the product
+    with the latent rows, while the normaliser sum_j p_j is kept in fp32, so
+    output element (i, k) of split s may be off by up to
+    2^-9 * sum_j p_j |c_jk| / sum_j p_j.  The bound taken is twice that (2^-8,
+    leaving room for the fp32 rounding of scores and sums) with the weighted mean
+    of |c| computed here from fp64 scores, plus 1e-6.  Queries must be exactly
+    representable in bf16.  A wrong row, scale or index lands far outside."""
+    import oracle as O
+    rows = np.asarray(rows, np.float64)[:length]
+    for s, (a, b) in enumerate(O.split_bounds(length, num_splits, page)):
+        if a >= b:
+            continue
+        c = rows[a:b, :d_latent]
+        sc = tau * (c @ q_lat.T + rows[a:b, d_latent:] @ q_pe.T)        # [tokens, heads]
+        p = np.exp(sc - sc.max(axis=0))
+        bound = 2.0 ** -8 * (p.T @ np.abs(c)) / p.sum(axis=0)[:, None] + 1e-6
+        err = np.abs(np.asarray(got[s], np.float64) - ref[s])
+        worst = (err / bound).max()
+        note(f"  o_part {what} split {s}: max err / bound {worst:.3f}")
+        assert worst <= 1.0, f"o_part {what} split {s}: error {worst:.2f}x the weight-rounding bound"
+
+
 def host_tensor(w, name, shape, std=1.0, layer=0):
     return I.to_f64(w, I.tensor_values(w, name, shape, std, layer))
 

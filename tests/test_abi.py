@@ -171,6 +171,23 @@ def test_fp8_pool_sizes_and_argument_checks():
                                         None) == 0
 
 
+def test_prefill_attention_argument_checks():
+    lib = M.load()
+    d = ctypes.byref(_dims())
+    # (dims, q_lat, q_pe, pool, pages, table, n_seqs, max_pages, q_seq, q_pos, n_q, S, o, lse, stream)
+    assert lib.mla_prefill_attention(d, P, P, P, 1, P, 0, 1, P, P, 4, 1, P, P, None) == -2  # n_seqs
+    assert lib.mla_prefill_attention(d, P, P, P, 1, P, 1, 1, None, P, 4, 1, P, P, None) == -1
+    assert lib.mla_prefill_attention(d, P, P, P, 1, P, 1, 1, P, None, 4, 1, P, P, None) == -1
+    assert lib.mla_prefill_attention(d, P, P, P, 1, P, 1, 1, P, P, 4, 0, P, P, None) == -2  # splits
+    assert lib.mla_prefill_attention(d, P, P, P, 1, P, 1, 1, P, P, 70000, 1, P, P, None) == -2
+    assert lib.mla_prefill_attention(d, None, None, None, 1, None, 1, 1, None, None, 0, 1, None,
+                                     None, None) == 0
+    d36 = ctypes.byref(_dims(d_latent=36))
+    assert lib.mla_prefill_attention_fp8(d36, P, P, P, 1, P, 1, 1, P, P, 4, 1, P, P, None) == -3
+    # the decode call still wants its lengths
+    assert lib.mla_decode_attention(d, P, P, P, 1, P, 1, None, 1, 1, P, P, None) == -1
+
+
 def test_device_fill_argument_checks():
     lib = _lib("libmla_inputs.so")
     lib.mla_fill_normal.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint64,

@@ -436,3 +436,57 @@ def test_fp8_row_roundtrip_and_page_layout():
         np.testing.assert_allclose(back[dc:], row[dc:], rtol=2.0 ** -8)
         assert img[5 * (dc + 2 * dr) + 4 * r:5 * (dc + 2 * dr) + 4 * r + 4].view(np.float32)[0] == 2.0 ** e
     assert O.fp8_page_bytes(64, 512, 64) == 41216
+
+
+# ---------------------------------------------------------------- prefill --
+def test_prefill_of_mha_as_mla_is_causally_masked_sdpa():
+    """A prompt chunk through the prefill definition equals causally masked
+    attention computed by torch's scaled_dot_product_attention on the plain MHA
+    the weights encode (token t of the chunk sees cache rows 0..P+t)."""
+    torch = pytest.importorskip("torch")
+    rng = _rng(60)
+    H, nh, dh, dr, P, T = 12, 3, 4, 2, 5, 7
+    mla, (wq, wk, wv, wo), dc = _mha_as_mla(rng, H, nh, dh, dr)
+    h_all = rng.normal(size=(P + T, H))
+    rows_before = O.latent_rows(h_all[:P], mla["w_dkv"], mla["w_kr"], np.arange(P), 10000.0)
+    out = O.mla_prefill_step(h_all[P:], rows_before, mla["w_q"], mla["w_qr"], mla["w_dkv"],
+                             mla["w_kr"], mla["w_uk"], mla["w_uv"], mla["w_o"], nh, dh, dc, dr,
+                             10000.0)
+    tau = 1.0 / math.sqrt(dh + dr)
+    q = torch.tensor(h_all[P:] @ wq.T).view(1, T, nh, dh).transpose(1, 2).contiguous()
+    k = torch.tensor(h_all @ wk.T).view(1, P + T, nh, dh).transpose(1, 2).contiguous()
+    v = torch.tensor(h_all @ wv.T).view(1, P + T, nh, dh).transpose(1, 2).contiguous()
+    allowed = torch.arange(P + T)[None, :] <= (P + torch.arange(T))[:, None]
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=allowed, scale=tau)
+    ref = o.transpose(1, 2).reshape(T, nh * dh).numpy() @ wo.T
+    np.testing.assert_allclose(out["u"], ref, rtol=1e-10, atol=1e-10)
+
+
+def test_prefill_chunks_compose_and_match_the_partials():
+    """Two chunks in turn give the same outputs as one chunk of both; each token's
+    split partials, merged, give its absorbed output (the attention call's
+    contract, checked against the step)."""
+    rng = _rng(61)
+    H, nh, dh, dc, dr, P, T = 20, 2, 8, 12, 4, 70, 9
+    w = _weights(rng, H, nh, dh, dc, dr)
+    h_all = rng.normal(size=(P + T, H))
+    rows_before = O.latent_rows(h_all[:P], w["w_dkv"], w["w_kr"], np.arange(P), 10000.0)
+    args = (w["w_q"], w["w_qr"], w["w_dkv"], w["w_kr"], w["w_uk"], w["w_uv"], w["w_o"], nh, dh, dc,
+            dr, 10000.0)
+    whole = O.mla_prefill_step(h_all[P:], rows_before, *args)
+    first = O.mla_prefill_step(h_all[P:P + 4], rows_before, *args)
+    rows_mid = O.latent_rows(h_all[:P + 4], w["w_dkv"], w["w_kr"], np.arange(P + 4), 10000.0)
+    second = O.mla_prefill_step(h_all[P + 4:], rows_mid, *args)
+    np.testing.assert_allclose(np.concatenate([first["u"], second["u"]]), whole["u"], rtol=1e-12,
+                               atol=1e-13)
+    rows = O.latent_rows(h_all, w["w_dkv"], w["w_kr"], np.arange(P + T), 10000.0)
+    tau = 1.0 / math.sqrt(dh + dr)
+    q = [O.absorb_q(h_all[P + t], w["w_q"], w["w_qr"], w["w_uk"], P + t, nh, dh, dc, dr, 10000.0)
+         for t in range(T)]
+    parts = O.prefill_attention_partials(np.stack([x[0] for x in q]), np.stack([x[1] for x in q]),
+                                         rows, np.arange(P, P + T), 3, dc, dr, tau, 16)
+    for t, (o_s, l_s) in enumerate(parts):
+        o_lat, lse = O.merge_lse(o_s, l_s)
+        np.testing.assert_allclose(lse, whole["lse"][t], rtol=1e-12, atol=1e-12)
+        per_head = np.stack([w["w_uv"][i * dh:(i + 1) * dh] @ o_lat[i] for i in range(nh)])
+        np.testing.assert_allclose(per_head, whole["o"][t], rtol=1e-10, atol=1e-12)

@@ -4,6 +4,10 @@
 // ([Report] §2.3/§2.4 of "《DeepSeek-V2》深度解读报告": every head scores the
 // same cached latent rows [c | k^R]; s = tau (q_lat . c + q_pe . k^R)).
 //
+// Two kernels share the structure below: k_attn_mfma_h128 for a bf16 pool and
+// k_attn_f8mma_h128 for the FP8 pool (its own header further down: the codes go
+// into the FP8 matrix instruction as stored).
+//
 // Work unit = (sequence b, split s).  A 256-thread workgroup (4 waves, one per
 // SIMD) streams the split's rows in tiles of 32 tokens (32 rows x 1152 bytes,
 // contiguous inside one 64-row page) through a 4-slot LDS ring filled by
@@ -75,7 +79,7 @@ constexpr int kPageWin = 512;                         // page ids of the split h
 constexpr float kLog2e = 1.4426950408889634f;
 // FP8 pool: a page is 64 rows of [512 e4m3 | 64 bf16] (640 bytes), then 64 fp32
 // row scales.  A tile is staged in LDS as its codes, its k^R block and its 32
-// scales, and the products read the codes directly (dequantized in registers).
+// scales (k_attn_f8mma_h128 below).
 constexpr int kF8Row = kDc + 2 * kDr;                  // 640
 constexpr int kF8ScaleOff = kPage * kF8Row;             // 40960
 constexpr int64_t kF8PageBytes = kF8ScaleOff + 4 * kPage;   // 41216
@@ -83,9 +87,6 @@ constexpr int kF8RopeOff = kTileTok * kDc;              // 16384: k^R block of a
 constexpr int kF8ScaleLds = kF8RopeOff + kTileTok * 2 * kDr;   // 20480: its scales
 constexpr int kF8Stage = kF8ScaleLds + 4 * kTileTok;    // 20608
 constexpr int kF8Copies = 6;                            // copies per wave per tile
-constexpr int kF8Slots = 6, kF8Ahead = 4;               // staging slots; tiles copied ahead
-constexpr int kARingF8 = 3;                             // FP8 score reads in flight
-constexpr int kBRingF8 = 4;                             // FP8 P.C reads in flight + 2
 constexpr float kHeadroom = 64.0f;                    // log2 units above the reference
 
 // 16-byte chunk c of latent row r sits at chunk c ^ lkey(r) of the row's
@@ -363,13 +364,6 @@ __device__ __forceinline__ u32x2_t lds_ld64(uint32_t addr) {
 __device__ __forceinline__ float lds_f32(uint32_t addr) {
   return *reinterpret_cast<const __attribute__((address_space(3))) float*>(static_cast<uintptr_t>(addr));
 }
-// 4 e4m3 values (one dword, byte 0 first) times the power-of-two scale s as bf16 pairs
-__device__ __forceinline__ uint32_t f8lo(uint32_t v, float s) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, s, false));
-}
-__device__ __forceinline__ uint32_t f8hi(uint32_t v, float s) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, s, true));
-}
 // 8 bytes per lane, transposed across 16-lane groups: output lane i < 8 of a
 // group gets byte i of the blocks of its lanes 0, 2, .., 14, lane 8 + i byte i
 // of those of lanes 1, 3, .., 15
@@ -379,19 +373,10 @@ __device__ __forceinline__ u32x2_t lds_tr8(uint32_t addr) {
       reinterpret_cast<__attribute__((address_space(3))) i32x2_t*>(static_cast<uintptr_t>(addr)));
   return __builtin_bit_cast(u32x2_t, v);
 }
-// 8 e4m3 codes (two dwords) times the power-of-two scale s as a bf16 operand
-__device__ __forceinline__ bf16x8_t f8x8(u32x2_t v, float s) {
-  const u32x4_t o = {f8lo(v[0], s), f8hi(v[0], s), f8lo(v[1], s), f8hi(v[1], s)};
-  return __builtin_bit_cast(bf16x8_t, o);
-}
-
-template <bool kF8>
 __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
     AttnArgs a, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     const char* __restrict__ pool) {
-  // tile ring: 4 bf16 tiles, or kF8Slots staged FP8 tiles
-  __shared__ __attribute__((aligned(1024)))
-  char ring[kF8 ? kF8Slots * kF8Stage : kStages * kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char ring[kStages * kTileBytes];   // tile ring
   __shared__ __attribute__((aligned(16))) float xch[kWaves][kHeads];
   // page ids of the split's pages [wbase, wbase + kPageWin): a copy in LDS, so
   // a tile's page costs a short LDS read instead of a scalar memory load whose
@@ -441,8 +426,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
   };
 
   // ---- this wave's queries as MFMA B fragments: head 32wv + r32, k = 16ks + 8g2 + j
-  // (FP8 pool, latent steps 2a + e: k = 32a + 16g2 + 8e + j, the order in which
-  // a 16-byte code chunk feeds two steps)
   bf16x8_t qf[kKSteps];
   {
     const int h = kHeads * wv + r32;
@@ -450,9 +433,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
     const float* qp = a.q_pe + (static_cast<int64_t>(b) * nh + h) * kDr + 8 * g2;
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) {
-      const float* src = ks >= kLatSteps ? qp + 16 * (ks - kLatSteps)
-                         : kF8 ? ql + 32 * (ks >> 1) + 16 * g2 + 8 * (ks & 1)
-                               : ql + 16 * ks + 8 * g2;
+      const float* src = ks >= kLatSteps ? qp + 16 * (ks - kLatSteps) : ql + 16 * ks + 8 * g2;
       float v[8];
       const float4 lo = *reinterpret_cast<const float4*>(src);
       const float4 hi = *reinterpret_cast<const float4*>(src + 4);
@@ -471,7 +452,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
 #pragma unroll
   for (int j = 0; j < 2; ++j) soff[j] = kPitch * r32 + 16 * ((2 * j + g2) ^ ky);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) roff[q] = (kF8 ? kF8RopeOff : kRopeOff) + 128 * r32 + 16 * ((2 * q + g2) ^ vy);
+  for (int q = 0; q < 4; ++q) roff[q] = kRopeOff + 128 * r32 + 16 * ((2 * q + g2) ^ vy);
   // P.C B fragment of 16-lane group (ch, g2), lane s16: token row 16kk + 8jj + 4g2 + (s16 >> 2),
   // columns 32nb + 16ch + 4(s16 & 3)..+3: toff[jj] + 64 nb + 16 kPitch kk
   const int s16 = lane & 15, ch = (lane >> 4) & 1;
@@ -481,20 +462,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
   for (int jj = 0; jj < 2; ++jj)
     toff[jj] = kPitch * (8 * jj + 4 * g2 + (s16 >> 2)) + 16 * (cp ^ (2 * jj + g2)) + 8 * (s16 & 1);
   const uint32_t ring0 = lds_addr(ring);
-  // FP8 staging: score A read of latent steps 2a, 2a+1 (chunk 2a + g2 of row
-  // r32) at f8_soff + 32 ((a & 8) | ((a & 7) ^ f8_fh)); P.C B read (transposed,
-  // 8 tokens x 8 columns per lane pair) of column block nb, token half kk at
-  // f8_toff[kk] + 32 ((nb & 8) | ((nb & 7) ^ f8_m)): lane s16 of group (ch, g2)
-  // reads token row 16kk + 8(m >> 2) + 4g2 + (m & 3), m = s16 >> 1, columns
-  // 32nb + 16ch + 8(s16 & 1)..+7, and ends up with column 32nb + 16ch + s16 of
-  // tokens 16kk + 8(j >> 2) + 4g2 + (j & 3), j = 0..7 (f8key of that row is 2m + g2)
-  const int f8_fk = f8key(r32), f8_fh = f8_fk >> 1, f8_m = s16 >> 1;
-  const uint32_t f8_soff = kDc * r32 + 16 * (g2 ^ (f8_fk & 1));
-  uint32_t f8_toff[2];
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-    f8_toff[kk] = kDc * (16 * kk + 8 * (f8_m >> 2) + 4 * g2 + (f8_m & 3)) + 16 * (ch ^ g2) +
-                  8 * (s16 & 1);
 
   // scores S^T[t, h] of the tile in slot T: lane holds head 32wv + r32 and
   // tokens 8(i >> 2) + 4g2 + (i & 3), i = 0..15
@@ -526,43 +493,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
         else mfma_v(acc, ar[k % kARing], qf[k]);
       }
       if (ks == 0) hook();
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    return acc;
-  };
-  // FP8: scores of the staged tile at T.  Read a < 16 holds latent steps 2a
-  // (bytes 0-7) and 2a + 1 (bytes 8-15), dequantized with row r32's scale by the
-  // conversion; reads 16..19 are the bf16 k^R steps.
-  auto scores_f8 = [&](uint32_t T, auto&& hook) {
-    f32x16_t acc;
-    const float sg = lds_f32(T + kF8ScaleLds + 4 * r32);
-    auto ldc = [&](int g) {
-      return g < 16 ? lds_ld128(T + f8_soff + 32 * ((g & 8) | ((g & 7) ^ f8_fh)))
-                    : lds_ld128(T + roff[g < 16 ? 0 : g - 16]);
-    };
-    constexpr int kRead = 20, kAhead = kARingF8;
-    u32x4_t cr[kAhead + 1];
-#pragma unroll
-    for (int d = 0; d < kAhead; ++d) cr[d] = ldc(d);
-#pragma unroll
-    for (int g = 0; g < kRead; ++g) {
-      if (g + kAhead < kRead) cr[(g + kAhead) % (kAhead + 1)] = ldc(g + kAhead);
-      wait_lgkm(min(kAhead, kRead - 1 - g));
-      const u32x4_t v = cr[g % (kAhead + 1)];
-      if (g < 16) {
-        const bf16x8_t lo = f8x8((u32x2_t){v[0], v[1]}, sg), hi = f8x8((u32x2_t){v[2], v[3]}, sg);
-        if (g == 0) {
-          acc = mfma_v_first(lo, qf[0]);
-        } else {
-          mfma_v_nop(acc, lo, qf[2 * g]);
-        }
-        mfma_v_nop(acc, hi, qf[2 * g + 1]);
-      } else if (g < kRead - 1) {
-        mfma_v(acc, __builtin_bit_cast(bf16x8_t, v), qf[kLatSteps + g - 16]);
-      } else {
-        mfma_v_last(acc, __builtin_bit_cast(bf16x8_t, v), qf[kLatSteps + g - 16]);
-      }
-      if (g == 0) hook();
       __builtin_amdgcn_sched_barrier(0);
     }
     return acc;
@@ -616,17 +546,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
   };
   auto issue = [&](int j) { return issue_pg(j, page_load(j)); };
 
-  // FP8 pool: tile j is staged in slot j % kF8Slots; start its copy, return its valid rows
-  auto stage_of = [&](int j) { return ring0 + static_cast<uint32_t>(j % kF8Slots) * kF8Stage; };
-  auto issue_pg_f8 = [&](int j, int pgv) {
-    const int tok = t0 + j * kTileTok;
-    const int pg = __builtin_amdgcn_readfirstlane(pgv);   // uniform
-    const bool ok = pg >= 0 && pg < a.num_pages;
-    bad_page |= !ok;
-    tile_issue_f8(pool, pg, ok, tok, t1, stage_of(j), wv, lane);
-    return ok ? min(kTileTok, t1 - tok) : 0;
-  };
-  auto issue_f8 = [&](int j) { return issue_pg_f8(j, page_load(j)); };
 
   float seen = -INFINITY;     // largest raw score of this lane in this pass
   float p[16];                // softmax weights of the tile being scored
@@ -666,61 +585,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // FP8: rows nvalid..31 of the staged tile at T that this wave copied get zero
-  // codes and a zero scale (for a page outside the pool they may hold any
-  // bytes, NaN codes included), so that they add nothing to P'.codes; called
-  // for partial tiles only, its LDS writes complete on return
-  auto zero_tail = [&](uint32_t T, int nvalid) {
-    const u32x4_t zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 8 * wv + 2 * i + (lane >> 5);
-      if (r >= nvalid) lds_st128(T + kDc * r + 16 * (lane & 31), zero);
-    }
-    if (lane < 8 && 8 * wv + lane >= nvalid) lds_st32(T + kF8ScaleLds + 4 * (8 * wv + lane), 0u);
-    wait_lgkm(0);
-  };
-  // FP8: O += P'.codes over the staged tile at T, the B operand read transposed
-  // as 8 codes per lane and turned into bf16 unscaled (P' carries the row scales)
-  auto pv_product_f8 = [&](uint32_t T, const bf16x8_t& pp0, const bf16x8_t& pp1, bool next,
-                           const f32x16_t& x, float mr) {
-    auto ldb = [&](int m) {   // product m: column block m >> 1, token half m & 1
-      const int nb = m >> 1;
-      return lds_tr8(T + f8_toff[m & 1] + 32 * ((nb & 8) | ((nb & 7) ^ f8_m)));
-    };
-    constexpr int kRing = kBRingF8;
-    u32x2_t br[kRing];
-#pragma unroll
-    for (int d = 0; d < kRing - 2; ++d) br[d] = ldb(d);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int m = 0; m < 2 * kColBlocks; m += 2) {
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-        if (m + kRing - 2 + e < 2 * kColBlocks) br[(m + kRing - 2 + e) % kRing] = ldb(m + kRing - 2 + e);
-      wait_lgkm(min(kRing - 2, 2 * kColBlocks - m - 2));
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-        o[m >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e ? pp1 : pp0,
-                                                             f8x8(br[(m + e) % kRing], 1.0f),
-                                                             o[m >> 1], 0, 0, 0);
-      if (next) weight(x, m >> 1, mr);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  // FP8: P' = p times the row scale of each of this lane's 16 tokens (rows past
-  // the valid ones have p = 0 and, after zero_tail, scale 0), packed as the A operand
-  auto scale_p = [&](uint32_t T, bf16x8_t& q0, bf16x8_t& q1) {
-    float ps[16];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const u32x4_t sv = lds_ld128(T + kF8ScaleLds + 4 * (8 * q + 4 * g2));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ps[4 * q + e] = p[4 * q + e] * __uint_as_float(sv[e]);
-    }
-    q0 = pack8(ps);
-    q1 = pack8(ps + 8);
-  };
   auto weight_sum = [&]() {
     l_part += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])) +
               (((p[8] + p[9]) + (p[10] + p[11])) + ((p[12] + p[13]) + (p[14] + p[15])));
@@ -738,55 +602,517 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
     bf16x8_t pp0, pp1;        // packed weights of the previous tile
     f32x16_t sc;
     float mr;
-    if constexpr (!kF8) {
-      int nv0 = issue(0), nv1 = 0, nv2 = 0;   // valid rows of tiles t, t+1, t+2
-      if (ntiles > 1) nv1 = issue(1);
-      // ---- tile 0: scores and weights (tile 2's copy starts among the products)
-      const int pgv2 = ntiles > 2 ? page_load(2) : 0;
-      wait_tile(ntiles > 1 ? 1 : 0);
-      lds_barrier();
-      sc = scores(ring0, [&] { if (ntiles > 2) nv2 = issue_pg(2, pgv2); });
+    int nv0 = issue(0), nv1 = 0, nv2 = 0;   // valid rows of tiles t, t+1, t+2
+    if (ntiles > 1) nv1 = issue(1);
+    // ---- tile 0: scores and weights (tile 2's copy starts among the products)
+    const int pgv2 = ntiles > 2 ? page_load(2) : 0;
+    wait_tile(ntiles > 1 ? 1 : 0);
+    lds_barrier();
+    sc = scores(ring0, [&] { if (ntiles > 2) nv2 = issue_pg(2, pgv2); });
+    mask(sc, nv0);
+    if (pass == 0) {            // the first tile fixes the reference
+      float tm = sc[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) tm = fmaxf(tm, sc[i]);
+      m_ref = fmaxf(tm, __shfl_xor(tm, 32, 64)) * cs;
+    }
+    mr = fmaxf(m_ref, -1e30f);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) weight(sc, i, mr);
+    weight_sum();
+    pp0 = pack8(p);   // k = 16kk + 8(j >> 2) + 4g2 + (j & 3)
+    pp1 = pack8(p + 8);
+    nv0 = nv1; nv1 = nv2;
+    // ---- tile t: scores, then the products of tile t-1 with the weights of tile t between them
+    for (int t = 1; t < ntiles; ++t) {
+      const bool more = t + 2 < ntiles;
+      const int pgv = more ? page_load(t + 2) : 0;
+      wait_tile(t + 1 < ntiles ? 1 : 0);
+      lds_barrier();   // tile t is in LDS for every wave; the slot of tile t-2 is free
+      sc = scores(ring0 + (t & 3) * kTileBytes, [&] { if (more) nv2 = issue_pg(t + 2, pgv); });
       mask(sc, nv0);
-      if (pass == 0) {            // the first tile fixes the reference
-        float tm = sc[0];
-  #pragma unroll
-        for (int i = 1; i < 16; ++i) tm = fmaxf(tm, sc[i]);
-        m_ref = fmaxf(tm, __shfl_xor(tm, 32, 64)) * cs;
-      }
-      mr = fmaxf(m_ref, -1e30f);
-  #pragma unroll
-      for (int i = 0; i < 16; ++i) weight(sc, i, mr);
+      pv_product(ring0 + ((t - 1) & 3) * kTileBytes, pp0, pp1, true, sc, mr);
       weight_sum();
-      pp0 = pack8(p);   // k = 16kk + 8(j >> 2) + 4g2 + (j & 3)
+      pp0 = pack8(p);
       pp1 = pack8(p + 8);
       nv0 = nv1; nv1 = nv2;
-      // ---- tile t: scores, then the products of tile t-1 with the weights of tile t between them
-      for (int t = 1; t < ntiles; ++t) {
-        const bool more = t + 2 < ntiles;
-        const int pgv = more ? page_load(t + 2) : 0;
-        wait_tile(t + 1 < ntiles ? 1 : 0);
-        lds_barrier();   // tile t is in LDS for every wave; the slot of tile t-2 is free
-        sc = scores(ring0 + (t & 3) * kTileBytes, [&] { if (more) nv2 = issue_pg(t + 2, pgv); });
-        mask(sc, nv0);
-        pv_product(ring0 + ((t - 1) & 3) * kTileBytes, pp0, pp1, true, sc, mr);
-        weight_sum();
-        pp0 = pack8(p);
-        pp1 = pack8(p + 8);
-        nv0 = nv1; nv1 = nv2;
+    }
+    pv_product(ring0 + ((ntiles - 1) & 3) * kTileBytes, pp0, pp1, false, sc, mr);
+    // every copy has landed (the last tile was waited for with vmcnt 0)
+    seen = fmaxf(seen, __shfl_xor(seen, 32, 64)) * cs;
+    if (!__syncthreads_or(seen > m_ref + kHeadroom)) break;
+    m_ref = seen;              // run the unit again with the largest score as reference
+  }
+  if (bad_page && tid == 0) set_err(a.err, ERR_PAGE);
+
+  // ---- epilogue: o_part = O / l, lse = (m + log2 l) ln 2; lane holds heads 8(i>>2) + 4g2 + (i&3)
+  const float l_sum = l_part + __shfl_xor(l_part, 32, 64);
+  const float inv = l_sum > 0.f ? 1.f / l_sum : 0.f;
+  if (g2 == 0) {
+    xch[wv][r32] = inv;
+    lse_out[r32] = l_sum > 0.f ? (m_ref + __log2f(l_sum)) * 0.6931471805599453f : -INFINITY;
+  }
+  __builtin_amdgcn_wave_barrier();
+  float ilv[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 il = *reinterpret_cast<const float4*>(&xch[wv][8 * q + 4 * g2]);
+    ilv[4 * q] = il.x; ilv[4 * q + 1] = il.y; ilv[4 * q + 2] = il.z; ilv[4 * q + 3] = il.w;
+  }
+#pragma unroll
+  for (int nb = 0; nb < kColBlocks; ++nb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      o_out[(8 * (i >> 2) + 4 * g2 + (i & 3)) * kDc + 32 * nb + r32] = o[nb][i] * ilv[i];
+}
+
+
+// ---- FP8 pool on the FP8 matrix cores ---------------------------------------
+// The staged codes feed v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3 x e4m3, K = 64)
+// as stored, with no conversion per element.  A lane of that product holds row
+// (A) or column (B) lane & 31 and 32 bytes; byte j of A lane (r, g) meets byte j
+// of B lane (n, g), and each operand row / column carries a power-of-two scale.
+//   scores  S^T[t, h] = sum_k code[t, k] 2^e_t q[h, k] + k^R[t] . q_pe[h]: the
+//           row scale 2^e_t is the hardware scale of A row t (E8M0 = the
+//           exponent field of the staged fp32 scale).  q is carried as two e4m3
+//           terms, q = 2^s_h (hi + lo), hi = RNE(q 2^-s_h), lo = RNE(q 2^-s_h - hi)
+//           (relative error <= 2^-8; bf16 has 2^-9), s_h putting the head's
+//           largest |q| in [128, 256).  Step st (64 latent columns): lane (r, g)
+//           holds columns 64st + 32g .. +31 of row r (two 16-byte chunks of the
+//           staged row), the queries laid out to match; one product with hi,
+//           one with lo.  Then the k^R part as four bf16 products.
+//   P.C     O[h, d] += sum_t P'[h, t] code[t, d], P' = p 2^e_t split the same
+//           way with a scale per head and tile.  The two terms share one
+//           product: K = 64 holds the tile's 32 tokens twice, A lane (h, g) =
+//           [hi | lo] of its 16 weights (tokens in the order of the score
+//           accumulator, so the weights never move across lanes) and B lane
+//           (n, g) = the same 16 codes of column n twice (two transposed 8-byte
+//           reads, duplicated in registers).
+// Per tile and wave that is 16 + 4 products for the scores and 16 for P.C, as
+// many matrix cycles as the bf16 pool, with 644 instead of 1152 bytes per token
+// and no conversion of the codes.
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// scaled e4m3 product with the accumulator in VGPRs (asm for the same reason as
+// mfma_v); the first of a chain gets 5 wait states after VALU writes of its
+// operands, chains on one accumulator need none
+__device__ __forceinline__ f32x16_t mfma8_first(const i32x8_t& a, const i32x8_t& b, uint32_t sa,
+                                                uint32_t sb) {
+  f32x16_t d;
+  asm("s_nop 4\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %4 op_sel_hi:[0,0,0]"
+      : "=&v"(d)
+      : "v"(a), "v"(b), "v"(sa), "v"(sb));
+  return d;
+}
+__device__ __forceinline__ void mfma8(f32x16_t& d, const i32x8_t& a, const i32x8_t& b, uint32_t sa,
+                                      uint32_t sb) {
+  asm("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+      : "+v"(d)
+      : "v"(a), "v"(b), "v"(sa), "v"(sb));
+}
+
+// Two-term e4m3 split of 4 values already scaled into (-256, 256): hi = RNE(x),
+// lo = RNE(x - hi), each packed as 4 bytes (value 0 in byte 0).
+__device__ __forceinline__ void split4(float x0, float x1, float x2, float x3, uint32_t& hi,
+                                       uint32_t& lo) {
+  int h = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  h = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, h, true);
+  const f32x2_t b0 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false);
+  const f32x2_t b1 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
+  int l = __builtin_amdgcn_cvt_pk_fp8_f32(x0 - b0[0], x1 - b0[1], 0, false);
+  l = __builtin_amdgcn_cvt_pk_fp8_f32(x2 - b1[0], x3 - b1[1], l, true);
+  hi = static_cast<uint32_t>(h);
+  lo = static_cast<uint32_t>(l);
+}
+
+// E8M0 scale k + 127 and multiplier 2^-k that put a largest magnitude m >= 0 in
+// [128, 256) (k clamped to [-126, 126]; m = 0 gives the smallest scale)
+__device__ __forceinline__ void e4m3_scale(float m, uint32_t& e8, float& mul) {
+  const int ex = static_cast<int>((__float_as_uint(m) >> 23) & 255u);   // m in [2^(ex-127), 2^(ex-126))
+  const int k = min(max(ex - 134, -126), 126);
+  e8 = static_cast<uint32_t>(k + 127);
+  mul = __uint_as_float(static_cast<uint32_t>(127 - k) << 23);
+}
+
+constexpr int kF8mSlots = 6, kF8mAhead = 4;   // staging slots; tiles copied ahead
+
+__global__ __launch_bounds__(kThreads, 1) void k_attn_f8mma_h128(
+    AttnArgs a, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
+    const char* __restrict__ pool) {
+  __shared__ __attribute__((aligned(1024))) char ring[kF8mSlots * kF8Stage];
+  __shared__ __attribute__((aligned(16))) float xch[kWaves][kHeads];
+  __shared__ int pwin[kPageWin];
+  // the k^R part of the queries as bf16 B fragments, wave w fragment q of lane l
+  // at 16 (64 (4w + q) + l) (registers are short: the latent part stays in VGPRs)
+  __shared__ __attribute__((aligned(16))) char qrope[kWaves * 4 * 64 * 16];
+  // the two e4m3 terms of the last latent step (st = 7) of the queries, wave w
+  // lane l: hi at 64 (64 w + l), lo 32 bytes after it
+  __shared__ __attribute__((aligned(16))) char qlast[kWaves * 64 * 64];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g2 = lane >> 5;
+  const int r32 = lane & 31;
+  const int S = a.num_splits;
+  const int unit = unit_of(blockIdx.x, a.batch * S);
+  const int b = unit / S, s = unit - b * S;
+  const int nh = 128;
+
+  int sq, L;
+  unit_seq_len(seq_lens, a.q_seq, a.q_pos, a.n_seqs, a.max_pages * kPage, b, tid == 0, a.err, &sq,
+               &L);
+  sq = __builtin_amdgcn_readfirstlane(sq);
+  L = __builtin_amdgcn_readfirstlane(L);
+
+  int t0, t1;
+  split_range(L, S, s, kPage, &t0, &t1);
+
+  const int64_t ob = (static_cast<int64_t>(b) * S + s) * nh + kHeads * wv;
+  float* o_out = a.o_part + ob * kDc;
+  float* lse_out = a.lse_part + ob;
+
+  if (t0 >= t1) {  // empty split (uniform across the workgroup)
+    for (int e = lane; e < kHeads * kDc; e += 64) o_out[e] = 0.f;
+    if (lane < kHeads) lse_out[lane] = -INFINITY;
+    return;
+  }
+  const int32_t* bt = block_table + static_cast<int64_t>(sq) * a.max_pages;
+  const int p_first = t0 / kPage, p_end = (t1 - 1) / kPage + 1;
+  int wbase = -1;
+  auto load_window = [&](int base) {
+    wait_vmcnt<0>();
+    lds_barrier();
+    for (int i = tid; i < kPageWin; i += kThreads) {
+      const int pg = base + i;
+      pwin[i] = pg < p_end ? bt[pg] : 0;
+    }
+    __syncthreads();
+    wbase = base;
+  };
+
+  // ---- queries of head h = 32wv + r32: two e4m3 terms of the latent part
+  // (lane (r32, g2), step st: columns 64st + 32g2 + j) with the head's scale,
+  // and the k^R part as bf16 fragments (k = 16q + 8g2 + j)
+  const int h = kHeads * wv + r32;
+  i32x8_t qh[7], ql[7];
+  uint32_t q_e8;
+  const uint32_t ql_lds = lds_addr(qlast) + 64 * (64 * wv + lane);
+  const uint32_t qr_lds = lds_addr(qrope) + 16 * (256 * wv + lane);
+  {
+    const float* ql_row = a.q_lat + (static_cast<int64_t>(b) * nh + h) * kDc + 32 * g2;
+    float mx = 0.f;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float4 v = *reinterpret_cast<const float4*>(ql_row + 64 * st + 4 * c);
+        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
       }
-      pv_product(ring0 + ((ntiles - 1) & 3) * kTileBytes, pp0, pp1, false, sc, mr);
+      __builtin_amdgcn_sched_barrier(0);   // bounded loads in flight
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    float mul;
+    e4m3_scale(mx, q_e8, mul);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      i32x8_t th, tl;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float4 v = *reinterpret_cast<const float4*>(ql_row + 64 * st + 4 * c);
+        uint32_t hi, lo;
+        split4(v.x * mul, v.y * mul, v.z * mul, v.w * mul, hi, lo);
+        th[c] = static_cast<int>(hi);
+        tl[c] = static_cast<int>(lo);
+      }
+      if (st < 7) {
+        qh[st] = th;
+        ql[st] = tl;
+      } else {
+        const u32x4_t* hv = reinterpret_cast<const u32x4_t*>(&th);
+        const u32x4_t* lv = reinterpret_cast<const u32x4_t*>(&tl);
+        lds_st128(ql_lds, hv[0]);
+        lds_st128(ql_lds + 16, hv[1]);
+        lds_st128(ql_lds + 32, lv[0]);
+        lds_st128(ql_lds + 48, lv[1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const float* qp = a.q_pe + (static_cast<int64_t>(b) * nh + h) * kDr + 8 * g2;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float v[8];
+      const float4 lo = *reinterpret_cast<const float4*>(qp + 16 * q);
+      const float4 hi = *reinterpret_cast<const float4*>(qp + 16 * q + 4);
+      v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+      v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+      lds_st128(qr_lds + 1024 * q, __builtin_bit_cast(u32x4_t, pack8(v)));
+    }
+    // read back by this wave only (after its own writes complete)
+  }
+
+  // ---- per-lane constant offsets inside a staged tile
+  // score A operand, step st, half hh: chunk 4st + 2g2 + hh of row r32, stored at
+  // chunk (4st + 2g2 + hh) ^ f8key(r32)
+  const int fk = f8key(r32);
+  const uint32_t a_row = kDc * r32;
+  const int a_kh = fk >> 2, a_kl = fk & 3;
+  // k^R fragment q of row r32: chunk 2q + g2 of its 128 bytes
+  const int vy = rkey(r32);
+  uint32_t roff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) roff[q] = kF8RopeOff + 128 * r32 + 16 * ((2 * q + g2) ^ vy);
+  // P.C B operand, column block nb, token half kk of a tile (transposed reads, as
+  // in the bf16-converting FP8 path): f8_toff[kk] + 32 ((nb & 8) | ((nb & 7) ^ f8_m))
+  const int s16 = lane & 15, ch = (lane >> 4) & 1;
+  const int f8_m = s16 >> 1;
+  uint32_t f8_toff[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+    f8_toff[kk] = kDc * (16 * kk + 8 * (f8_m >> 2) + 4 * g2 + (f8_m & 3)) + 16 * (ch ^ g2) +
+                  8 * (s16 & 1);
+  const uint32_t ring0 = lds_addr(ring);
+
+  // scores S^T[t, h] of the staged tile at T (lane: head r32, tokens
+  // 8(i >> 2) + 4g2 + (i & 3)); `hook` runs after the first products
+  auto scores = [&](uint32_t T, auto&& hook) {
+    // per-lane offsets are recomputed per call (opaque): hoisted out of the tile
+    // loop they would hold registers for the whole unit
+    const uint32_t arow = opaque(T + a_row), akh = opaque(a_kh);
+    const uint32_t c0 = 16 * ((2 * g2) ^ a_kl), c1 = c0 ^ 16;
+    const uint32_t sa = (__float_as_uint(lds_f32(T + kF8ScaleLds + 4 * r32)) >> 23) & 255u;
+    auto lda = [&](int st) {
+      const uint32_t base = arow + 64 * ((st & 4) | ((st & 3) ^ akh));
+      const u32x4_t x0 = lds_ld128(base + c0);
+      const u32x4_t x1 = lds_ld128(base + c1);
+      return (i32x8_t){static_cast<int>(x0[0]), static_cast<int>(x0[1]), static_cast<int>(x0[2]),
+                       static_cast<int>(x0[3]), static_cast<int>(x1[0]), static_cast<int>(x1[1]),
+                       static_cast<int>(x1[2]), static_cast<int>(x1[3])};
+    };
+    // queries of step 7 come from LDS, read along with the A operand of step 7
+    auto ldq = [&](uint32_t off) {
+      const u32x4_t x0 = lds_ld128(opaque(ql_lds) + off), x1 = lds_ld128(opaque(ql_lds) + off + 16);
+      return (i32x8_t){static_cast<int>(x0[0]), static_cast<int>(x0[1]), static_cast<int>(x0[2]),
+                       static_cast<int>(x0[3]), static_cast<int>(x1[0]), static_cast<int>(x1[1]),
+                       static_cast<int>(x1[2]), static_cast<int>(x1[3])};
+    };
+    i32x8_t q7h, q7l;
+    constexpr int kAh = 2;   // steps read ahead
+    i32x8_t ar[kAh + 1];
+#pragma unroll
+    for (int d = 0; d < kAh; ++d) ar[d] = lda(d);
+    f32x16_t acc;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      if (st + kAh < 8) ar[(st + kAh) % (kAh + 1)] = lda(st + kAh);
+      if (st + kAh == 7) {   // with the last A operand: the step-7 queries (4 more reads)
+        q7h = ldq(0);
+        q7l = ldq(32);
+      }
+      wait_lgkm(st + kAh >= 7 ? 2 * (7 - st) + (st < 7 ? 4 : 0) : 2 * kAh);
+      const i32x8_t& av = ar[st % (kAh + 1)];
+      if (st < 7) {
+        if (st == 0) acc = mfma8_first(av, qh[0], sa, q_e8);
+        else mfma8(acc, av, qh[st], sa, q_e8);
+        mfma8(acc, av, ql[st], sa, q_e8);
+      } else {
+        mfma8(acc, av, q7h, sa, q_e8);
+        mfma8(acc, av, q7l, sa, q_e8);
+      }
+      if (st == 0) hook();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // k^R part: tile fragment and query fragment of step q, one step read ahead
+    bf16x8_t rr[2], rq[2];
+    const uint32_t qrb = opaque(qr_lds);
+    rr[0] = lds_b128(opaque(T + roff[0]));
+    rq[0] = lds_b128(qrb);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (q < 3) {
+        rr[(q + 1) & 1] = lds_b128(opaque(T + roff[q + 1]));
+        rq[(q + 1) & 1] = lds_b128(qrb + 1024 * (q + 1));
+      }
+      wait_lgkm(q < 3 ? 2 : 0);
+      if (q < 3) mfma_v(acc, rr[q & 1], rq[q & 1]);
+      else mfma_v_last(acc, rr[q & 1], rq[q & 1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    return acc;
+  };
+  // scores of rows nvalid.. of a partial tile to -inf (one compare against an
+  // immediate per element)
+  auto mask = [&](f32x16_t& x, int nvalid) {
+    if (nvalid < kTileTok) {
+      asm volatile("");
+      const int lim = nvalid - 4 * g2;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (8 * (i >> 2) + (i & 3) >= lim) x[i] = -INFINITY;
+    }
+  };
+  // rows nvalid..31 of a partial staged tile (copied by this wave) get zero codes
+  // and a zero scale, so that they add nothing to the products
+  auto zero_tail = [&](uint32_t T, int nvalid) {
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    // row 8wv + 2i + (lane >> 5), chunk lane & 31: T + zt_base + 1024 i
+    const int lim = nvalid - 8 * wv - (lane >> 5);
+    const uint32_t zb = opaque(T + kDc * (8 * wv + (lane >> 5)) + 16 * (lane & 31));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (2 * i >= lim) lds_st128(zb + 1024 * i, zero);
+    if (lane < 8 && 8 * wv + lane >= nvalid) lds_st32(T + kF8ScaleLds + 4 * (8 * wv + lane), 0u);
+    wait_lgkm(0);
+  };
+  float m_ref = -INFINITY;
+  float l_part = 0.f;
+  f32x16_t o[kColBlocks];
+  float seen = -INFINITY;     // largest raw score of this lane in this pass
+  float p[16];                // softmax weights of the tile being scored
+  const float cs = a.scale * kLog2e;
+  auto weight = [&](const f32x16_t& x, int i, float mr) {
+    seen = fmaxf(seen, x[i]);
+    p[i] = __builtin_amdgcn_exp2f(fmaf(x[i], cs, -mr));
+  };
+  // O += P'.codes over the staged tile at T (pa: [hi | lo] of the lane's P', e8
+  // their scale); with `next`, the weights of the following tile (scores x) are
+  // computed between the products
+  auto pv_product = [&](uint32_t T, const i32x8_t& pa, uint32_t e8, bool next, const f32x16_t& x,
+                        float mr, auto&& copy) {
+    // token half 1 of a tile sits 16 rows (kDc 16 bytes) after token half 0; the
+    // operand's upper 16 bytes are the same two reads again (no register copies)
+    const uint32_t fm = opaque(f8_m), b0 = opaque(T + f8_toff[0]);
+    auto ldb = [&](int nb) {
+      const uint32_t c = b0 + 32 * ((nb & 8) | ((nb & 7) ^ fm));
+      const u32x2_t x0 = lds_tr8(c), x1 = lds_tr8(c + kDc * 16);
+      const uint32_t cc = opaque(c);   // a second load of the same bytes, not a copy
+      const u32x2_t x2 = lds_tr8(cc), x3 = lds_tr8(cc + kDc * 16);
+      return (i32x8_t){static_cast<int>(x0[0]), static_cast<int>(x0[1]), static_cast<int>(x1[0]),
+                       static_cast<int>(x1[1]), static_cast<int>(x2[0]), static_cast<int>(x2[1]),
+                       static_cast<int>(x3[0]), static_cast<int>(x3[1])};
+    };
+    constexpr int kBh = 2;   // column blocks read ahead
+    i32x8_t br[kBh + 1];
+#pragma unroll
+    for (int d = 0; d < kBh; ++d) br[d] = ldb(d);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int nb = 0; nb < kColBlocks; ++nb) {
+      if (nb + kBh < kColBlocks) br[(nb + kBh) % (kBh + 1)] = ldb(nb + kBh);
+      wait_lgkm(4 * min(kBh, kColBlocks - 1 - nb));
+      const i32x8_t& bv = br[nb % (kBh + 1)];
+      o[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pa, bv, o[nb], 0, 0, 0,
+                                                              static_cast<int>(e8), 0, 127);
+      if (next) weight(x, nb, mr);
+      if ((nb & 1) && nb < 2 * (kF8Copies - 1)) copy(nb >> 1);   // copy k after product 2k + 1
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // P' = p times the row scale of each of the lane's 16 tokens of the staged tile
+  // at T, as [hi | lo] e4m3 with a scale per head
+  auto pack_p = [&](uint32_t T, i32x8_t& pa, uint32_t& e8) {
+    float (&pw)[16] = p;   // scaled in place (the sum of the weights is taken first)
+    float mx = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4_t sv = lds_ld128(T + kF8ScaleLds + 4 * (8 * q + 4 * g2));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pw[4 * q + e] = p[4 * q + e] * __uint_as_float(sv[e]);
+        mx = fmaxf(mx, pw[4 * q + e]);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    float mul;
+    e4m3_scale(mx, e8, mul);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      uint32_t hi, lo;
+      split4(pw[4 * d] * mul, pw[4 * d + 1] * mul, pw[4 * d + 2] * mul, pw[4 * d + 3] * mul, hi, lo);
+      pa[d] = static_cast<int>(hi);
+      pa[d + 4] = static_cast<int>(lo);
+    }
+  };
+  auto weight_sum = [&]() {
+    l_part += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])) +
+              (((p[8] + p[9]) + (p[10] + p[11])) + ((p[12] + p[13]) + (p[14] + p[15])));
+  };
+
+  bool bad_page = false;
+  const int ntiles = (t1 - t0 + kTileTok - 1) / kTileTok;
+
+  auto page_load = [&](int j) {
+    const int tok = t0 + j * kTileTok;
+    if (tok / kPage - wbase >= kPageWin) load_window(tok / kPage);
+    return pwin[tok / kPage - wbase];
+  };
+  auto stage_of = [&](int j) { return ring0 + static_cast<uint32_t>(j % kF8mSlots) * kF8Stage; };
+  auto issue_pg = [&](int j, int pgv) {
+    const int tok = t0 + j * kTileTok;
+    const int pg = __builtin_amdgcn_readfirstlane(pgv);
+    const bool ok = pg >= 0 && pg < a.num_pages;
+    bad_page |= !ok;
+    tile_issue_f8(pool, pg, ok, tok, t1, stage_of(j), wv, lane);
+    return ok ? min(kTileTok, t1 - tok) : 0;
+  };
+  auto issue = [&](int j) { return issue_pg(j, page_load(j)); };
+  // the copies of one tile issued one at a time (spread over the products of a
+  // tile, so that the wave does not stall on a burst of them): cp_begin fixes
+  // the tile, cp_part(k) issues copy k (0..kF8Copies-1) in tile_issue_f8's order
+  uint64_t cp_rows = 0, cp_scales = 0;
+  int cp_nvalid = 0;
+  uint32_t cp_stage = 0;
+  auto cp_begin = [&](int j, int pgv) {
+    const int tok = t0 + j * kTileTok;
+    const int pg = __builtin_amdgcn_readfirstlane(pgv);
+    const bool ok = pg >= 0 && pg < a.num_pages;
+    bad_page |= !ok;
+    cp_nvalid = ok ? min(kTileTok, t1 - tok) : 0;
+    const int64_t pbase = ok ? static_cast<int64_t>(pg) * kF8PageBytes : 0;
+    cp_rows = reinterpret_cast<uint64_t>(pool + pbase + (tok & (kPage - 1)) * kF8Row);
+    cp_scales = reinterpret_cast<uint64_t>(pool + pbase + kF8ScaleOff + 4 * (tok & (kPage - 1)));
+    cp_stage = stage_of(j);
+    // the scale copy (two lanes) goes out here, the others among the products
+    if (lane < 2) dma_block(cp_scales, 32 * wv + 16 * lane, cp_stage + kF8ScaleLds + 32 * wv);
+    return cp_nvalid;
+  };
+  auto cp_part = [&](int k) {
+    const int ln = static_cast<int>(opaque(static_cast<uint32_t>(lane)));
+    if (k < 4) {
+      const int r = 8 * wv + 2 * k + (ln >> 5);
+      dma_block(cp_rows, (r < cp_nvalid ? r : 0) * kF8Row + 16 * ((ln & 31) ^ f8key(r)),
+                cp_stage + kDc * (8 * wv + 2 * k));
     } else {
-      // valid rows of tiles t .. t+kF8Ahead (tiles are copied kF8Ahead ahead)
-      int nv0 = issue_f8(0), nv1 = 0, nv2 = 0, nv3 = 0, nv4 = 0;
-      if (ntiles > 1) nv1 = issue_f8(1);
-      if (ntiles > 2) nv2 = issue_f8(2);
-      if (ntiles > 3) nv3 = issue_f8(3);
-      // ---- tile 0: scores and weights (tile kF8Ahead's copy starts among the products)
-      const int pgv4 = ntiles > kF8Ahead ? page_load(kF8Ahead) : 0;
-      wait_tile_f8(min(kF8Ahead - 1, ntiles - 1));
+      const int rr = 8 * wv + (ln >> 3);
+      dma_block(cp_rows, (rr < cp_nvalid ? rr : 0) * kF8Row + kDc + 16 * ((ln & 7) ^ rkey(rr)),
+                cp_stage + kF8RopeOff + 1024 * wv);
+    }
+  };
+
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int nb = 0; nb < kColBlocks; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[nb][i] = 0.f;
+    l_part = 0.f;
+    seen = -INFINITY;
+    if (wbase != p_first) load_window(p_first);
+
+    // valid rows of tiles t .. t + kF8mAhead (tiles are copied kF8mAhead ahead)
+    int nv0 = issue(0), nv1 = 0, nv2 = 0, nv3 = 0, nv4 = 0;
+    if (ntiles > 1) nv1 = issue(1);
+    if (ntiles > 2) nv2 = issue(2);
+    if (ntiles > 3) nv3 = issue(3);
+    i32x8_t pa;        // [hi | lo] of the previous tile's P'
+    uint32_t pe8;      // their scale
+    f32x16_t sc;
+    float mr;
+    // ---- tile 0: scores and weights (tile kF8mAhead's copy starts among the products)
+    {
+      const int pgv = ntiles > kF8mAhead ? page_load(kF8mAhead) : 0;
+      wait_tile_f8(min(kF8mAhead - 1, ntiles - 1));
       if (nv0 < kTileTok) zero_tail(stage_of(0), nv0);
       lds_barrier();
-      sc = scores_f8(stage_of(0), [&] { if (ntiles > kF8Ahead) nv4 = issue_pg_f8(kF8Ahead, pgv4); });
+      sc = scores(stage_of(0), [&] { if (ntiles > kF8mAhead) nv4 = issue_pg(kF8mAhead, pgv); });
       mask(sc, nv0);
       if (pass == 0) {          // the first tile fixes the reference
         float tm = sc[0];
@@ -798,24 +1124,31 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
 #pragma unroll
       for (int i = 0; i < 16; ++i) weight(sc, i, mr);
       weight_sum();
-      scale_p(stage_of(0), pp0, pp1);
+      pack_p(stage_of(0), pa, pe8);
       nv0 = nv1; nv1 = nv2; nv2 = nv3; nv3 = nv4;
-      // ---- tile t: scores, then the products of tile t-1 with the weights of tile t between them
-      for (int t = 1; t < ntiles; ++t) {
-        const bool more = t + kF8Ahead < ntiles;
-        const int pgv = more ? page_load(t + kF8Ahead) : 0;
-        wait_tile_f8(min(kF8Ahead - 1, ntiles - 1 - t));
-        if (nv0 < kTileTok) zero_tail(stage_of(t), nv0);
-        lds_barrier();   // tile t is staged for every wave; the slot of tile t-2 is free
-        sc = scores_f8(stage_of(t), [&] { if (more) nv4 = issue_pg_f8(t + kF8Ahead, pgv); });
-        mask(sc, nv0);
-        pv_product_f8(stage_of(t - 1), pp0, pp1, true, sc, mr);
-        weight_sum();
-        scale_p(stage_of(t), pp0, pp1);
-        nv0 = nv1; nv1 = nv2; nv2 = nv3; nv3 = nv4;
-      }
-      pv_product_f8(stage_of(ntiles - 1), pp0, pp1, false, sc, mr);
     }
+    // ---- tile t: scores, then the products of tile t-1 with the weights of tile t
+    // between them and the copies of tile t + kF8mAhead among those products.
+    // Tiles with a copy to start and the last kF8mAhead tiles run separate
+    // copies of the body, so that no branch splits the product sequence.
+    auto body = [&](int t, auto more_c) {
+      constexpr bool more = decltype(more_c)::value;
+      const int pgv = more ? page_load(t + kF8mAhead) : 0;
+      wait_tile_f8(more ? kF8mAhead - 1 : min(kF8mAhead - 1, ntiles - 1 - t));
+      if (nv0 < kTileTok) zero_tail(stage_of(t), nv0);
+      lds_barrier();   // tile t is staged for every wave; the slot of tile t-2 is free
+      if (more) nv4 = cp_begin(t + kF8mAhead, pgv);
+      sc = scores(stage_of(t), [&] {});
+      mask(sc, nv0);
+      pv_product(stage_of(t - 1), pa, pe8, true, sc, mr, [&](int k) { if (more) cp_part(k); });
+      weight_sum();
+      pack_p(stage_of(t), pa, pe8);
+      nv0 = nv1; nv1 = nv2; nv2 = nv3; nv3 = nv4;
+    };
+    int t = 1;
+    for (; t + kF8mAhead < ntiles; ++t) body(t, std::true_type{});
+    for (; t < ntiles; ++t) body(t, std::false_type{});
+    pv_product(stage_of(ntiles - 1), pa, pe8, false, sc, mr, [&](int) {});
     // every copy has landed (the last tile was waited for with vmcnt 0)
     seen = fmaxf(seen, __shfl_xor(seen, 32, 64)) * cs;
     if (!__syncthreads_or(seen > m_ref + kHeadroom)) break;
@@ -823,7 +1156,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
   }
   if (bad_page && tid == 0) set_err(a.err, ERR_PAGE);
 
-  // ---- epilogue: o_part = O / l, lse = (m + log2 l) ln 2; lane holds heads 8(i>>2) + 4g2 + (i&3)
+  // ---- epilogue: o_part = O / l, lse = (m + log2 l) ln 2
   const float l_sum = l_part + __shfl_xor(l_part, 32, 64);
   const float inv = l_sum > 0.f ? 1.f / l_sum : 0.f;
   if (g2 == 0) {
@@ -853,7 +1186,7 @@ bool fast_attention_ok(const AttnArgs& a) {
 hipError_t launch_attention_fast(const AttnArgs& a, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
   const int units = a.batch * a.num_splits;
-  hipLaunchKernelGGL(k_attn_mfma_h128<false>, dim3(units), dim3(kThreads), 0, stream, a, a.block_table,
+  hipLaunchKernelGGL(k_attn_mfma_h128, dim3(units), dim3(kThreads), 0, stream, a, a.block_table,
                      a.seq_lens, static_cast<const char*>(a.pool));
   return hipGetLastError();
 }
@@ -861,7 +1194,7 @@ hipError_t launch_attention_fast(const AttnArgs& a, hipStream_t stream) {
 hipError_t launch_attention_fp8(const AttnArgs& a, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
   const int units = a.batch * a.num_splits;
-  hipLaunchKernelGGL(k_attn_mfma_h128<true>, dim3(units), dim3(kThreads), 0, stream, a, a.block_table,
+  hipLaunchKernelGGL(k_attn_f8mma_h128, dim3(units), dim3(kThreads), 0, stream, a, a.block_table,
                      a.seq_lens, static_cast<const char*>(a.pool));
   return hipGetLastError();
 }

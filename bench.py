@@ -48,11 +48,17 @@ def parse():
     return p.parse_args()
 
 
-def attention_traffic(workload: str):
-    """HBM bytes per attention launch on `workload` (4 splits) from the committed
-    rocprofv3 counter runs (FETCH_SIZE and WRITE_SIZE scaled by a plain-copy
-    calibration), or None when there are none or the kernel source changed since."""
-    path = os.path.join(ROOT, "profiles", f"k_attn_mfma_h128_{workload}_traffic.json")
+def attention_kernel(w) -> str:
+    """Name of the attention kernel that runs for workload `w`."""
+    return "k_attn_f8mma_h128" if w.cache == "fp8" else "k_attn_mfma_h128"
+
+
+def attention_traffic(kernel: str, workload: str):
+    """HBM bytes per attention launch of `kernel` on `workload` (4 splits) from the
+    committed rocprofv3 counter runs (FETCH_SIZE and WRITE_SIZE scaled by a
+    plain-copy calibration), or None when there are none or the kernel source
+    changed since."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
     try:
         rec = json.load(open(path))
         src = open(os.path.join(ROOT, rec["kernel_source"]), "rb").read()
@@ -220,15 +226,14 @@ def main():
     if w.chunk:     # prefill: the attention is a dense contraction; its bound is the MFMA rate
         roofline = {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": tflops / BF16_PEAK_TFLOPS, "traffic": None,
-                    "kernel": "k_attn_mfma_h128 (mla_prefill_attention)",
+                    "kernel": f"{attention_kernel(w)} (mla_prefill_attention)",
                     "algorithmic_flop_per_launch": attn_flop}
     else:
         roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": achieved / HBM_PEAK_GBPS,
-                    "traffic": attention_traffic(w.name) if S == 4 else None,
-                    "kernel": ("k_attn_mfma_h128<true> (mla_decode_attention_fp8)"
-                               if w.cache == "fp8" else
-                               "k_attn_mfma_h128<false> (mla_decode_attention)"),
+                    "traffic": attention_traffic(attention_kernel(w), w.name) if S == 4 else None,
+                    "kernel": attention_kernel(w) + (" (mla_decode_attention_fp8)" if w.cache == "fp8"
+                                                     else " (mla_decode_attention)"),
                     "algorithmic_bytes_per_launch": cache_bytes}
     line = {
         "metric": ("MLA chunked-prefill prompt tokens/s, n_h=128 d_c=512 1 GPU" if w.chunk else

@@ -270,10 +270,13 @@ size_t mla_append_workspace_bytes_fp8(const mla_dims* dims, int32_t n_rows);
 /*
  * Split-KV latent attention over the FP8 pool: mla_decode_attention with every
  * cached row replaced by its dequantized value [value(code) * 2^e | k^R].
- * The MFMA path (bf16 dtype, n_h = 128, d_c = 512, d_R = 64, page_size = 64)
- * turns each tile into bf16 in LDS (exact: a power-of-two scale on a 4-bit
- * significand) before the same bf16 products; other shapes use the plain
- * vector kernel.  Arguments and outputs as mla_decode_attention.
+ * The matrix-core path (bf16 dtype, n_h = 128, d_c = 512, d_R = 64,
+ * page_size = 64) multiplies the stored e4m3 codes directly on the FP8 matrix
+ * cores (the row scale applied exactly as a power of two); the queries and
+ * the softmax weights enter those products as two e4m3 terms each (relative
+ * error <= 2^-8, the order of bf16 rounding), accumulation in fp32.  Other
+ * shapes use the plain vector kernel (fp32 arithmetic on the dequantized
+ * rows).  Arguments and outputs as mla_decode_attention.
  */
 mla_status mla_decode_attention_fp8(const mla_dims* dims, const float* q_lat, const float* q_pe,
                                     const void* pool, int64_t num_pages,

@@ -428,20 +428,37 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
   // ---- this wave's queries as MFMA B fragments: head 32wv + r32, k = 16ks + 8g2 + j
   bf16x8_t qf[kKSteps];
   {
-    const int h = kHeads * wv + r32;
-    const float* ql = a.q_lat + (static_cast<int64_t>(b) * nh + h) * kDc;
-    const float* qp = a.q_pe + (static_cast<int64_t>(b) * nh + h) * kDr + 8 * g2;
+    // the wave's 32 query rows are read as contiguous 1 KB blocks (every load a
+    // run of whole cache lines), turned into bf16 rows in the still unused tile
+    // ring (wave w at 32 kQPitch w, row r at kQPitch r: 1152 bytes + 16 of pad,
+    // so a fragment read of 32 rows is conflict-free), and read back as fragments
+    constexpr int kQPitch = (kDc + kDr) * 2 + 16;
+    const uint32_t qst = lds_addr(ring) + static_cast<uint32_t>(kHeads * kQPitch) * wv;
+    const float* qlb = a.q_lat + (static_cast<int64_t>(b) * nh + kHeads * wv) * kDc;
+    const float* qpb = a.q_pe + (static_cast<int64_t>(b) * nh + kHeads * wv) * kDr;
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) {
-      const float* src = ks >= kLatSteps ? qp + 16 * (ks - kLatSteps) : ql + 16 * ks + 8 * g2;
-      float v[8];
-      const float4 lo = *reinterpret_cast<const float4*>(src);
-      const float4 hi = *reinterpret_cast<const float4*>(src + 4);
-      v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
-      v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
-      qf[ks] = pack8(v);
-      if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bounded loads in flight
+    for (int i = 0; i < kHeads * kDc / 256; ++i) {   // 64 blocks of 64 float4
+      const int e = 4 * (64 * i + lane);
+      const float4 v = *reinterpret_cast<const float4*>(qlb + e);
+      const u32x2_t w2 = {cvt2(v.x, v.y), cvt2(v.z, v.w)};
+      *reinterpret_cast<__attribute__((address_space(3))) u32x2_t*>(static_cast<uintptr_t>(
+          qst + kQPitch * (e / kDc) + 2 * (e % kDc))) = w2;
+      if ((i & 7) == 7) __builtin_amdgcn_sched_barrier(0);   // bounded loads in flight
     }
+#pragma unroll
+    for (int i = 0; i < kHeads * kDr / 256; ++i) {   // 8 blocks
+      const int e = 4 * (64 * i + lane);
+      const float4 v = *reinterpret_cast<const float4*>(qpb + e);
+      const u32x2_t w2 = {cvt2(v.x, v.y), cvt2(v.z, v.w)};
+      *reinterpret_cast<__attribute__((address_space(3))) u32x2_t*>(static_cast<uintptr_t>(
+          qst + kQPitch * (e / kDr) + 2 * (kDc + e % kDr))) = w2;
+    }
+    wait_lgkm(0);   // this wave's rows are in LDS (a wave reads only its own rows)
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks)
+      qf[ks] = lds_b128(qst + kQPitch * r32 + 2 * (16 * ks + 8 * g2));
+    wait_lgkm(0);
+    lds_barrier();  // every wave is done with the ring before tiles are copied into it
   }
 
   // ---- per-lane constant offsets inside a tile

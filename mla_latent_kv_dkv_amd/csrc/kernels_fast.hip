@@ -810,61 +810,97 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_f8mma_h128(
   // ---- queries of head h = 32wv + r32: two e4m3 terms of the latent part
   // (lane (r32, g2), step st: columns 64st + 32g2 + j) with the head's scale,
   // and the k^R part as bf16 fragments (k = 16q + 8g2 + j)
-  const int h = kHeads * wv + r32;
   i32x8_t qh[7], ql[7];
   uint32_t q_e8;
   const uint32_t ql_lds = lds_addr(qlast) + 64 * (64 * wv + lane);
   const uint32_t qr_lds = lds_addr(qrope) + 16 * (256 * wv + lane);
   {
-    const float* ql_row = a.q_lat + (static_cast<int64_t>(b) * nh + h) * kDc + 32 * g2;
-    float mx = 0.f;
+    // The wave's 32 query rows are read as whole cache lines (two 512-byte row
+    // pieces per load) into a staging area in the still unused tile ring (wave w
+    // at 32 kQS w, row r at kQS r: 128 fp32 columns + 16 bytes of pad, so the
+    // fragment reads below are conflict-free), a quarter of the columns at a
+    // time, twice: once for the head's largest |q|, once for the two-term split.
+    constexpr int kQS = 128 * 4 + 16;
+    const uint32_t qst = lds_addr(ring) + static_cast<uint32_t>(kHeads * kQS) * wv;
+    const float* qlb = a.q_lat + (static_cast<int64_t>(b) * nh + kHeads * wv) * kDc;
+    const int sr = lane >> 5, sc4 = 4 * (lane & 31);
+    auto stage = [&](int qq) {   // columns 128qq.. of the 32 rows: row 2i + sr, columns sc4..+3
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float4 v = *reinterpret_cast<const float4*>(ql_row + 64 * st + 4 * c);
-        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+      for (int i = 0; i < 16; ++i) {
+        const float4 v = *reinterpret_cast<const float4*>(qlb + (2 * i + sr) * kDc + 128 * qq + sc4);
+        lds_st128(qst + kQS * (2 * i + sr) + 4 * sc4, __builtin_bit_cast(u32x4_t, v));
+        if ((i & 7) == 7) __builtin_amdgcn_sched_barrier(0);   // bounded loads in flight
       }
-      __builtin_amdgcn_sched_barrier(0);   // bounded loads in flight
+      wait_lgkm(0);
+    };
+    // columns 64 sp + 32 g2 + 4c .. +3 of row r32 within the staged quarter
+    auto frag = [&](int sp, int c) {
+      return __builtin_bit_cast(float4, lds_ld128(qst + kQS * r32 + 4 * (64 * sp + 32 * g2 + 4 * c)));
+    };
+    float mx = 0.f;
+    for (int qq = 0; qq < 4; ++qq) {
+      stage(qq);
+#pragma unroll
+      for (int sp = 0; sp < 2; ++sp)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const float4 v = frag(sp, c);
+          mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+        }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     float mul;
     e4m3_scale(mx, q_e8, mul);
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      i32x8_t th, tl;
+    for (int qq = 0; qq < 4; ++qq) {
+      stage(qq);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float4 v = *reinterpret_cast<const float4*>(ql_row + 64 * st + 4 * c);
-        uint32_t hi, lo;
-        split4(v.x * mul, v.y * mul, v.z * mul, v.w * mul, hi, lo);
-        th[c] = static_cast<int>(hi);
-        tl[c] = static_cast<int>(lo);
-      }
-      if (st < 7) {
-        qh[st] = th;
-        ql[st] = tl;
-      } else {
-        const u32x4_t* hv = reinterpret_cast<const u32x4_t*>(&th);
-        const u32x4_t* lv = reinterpret_cast<const u32x4_t*>(&tl);
-        lds_st128(ql_lds, hv[0]);
-        lds_st128(ql_lds + 16, hv[1]);
-        lds_st128(ql_lds + 32, lv[0]);
-        lds_st128(ql_lds + 48, lv[1]);
+      for (int sp = 0; sp < 2; ++sp) {
+        const int st = 2 * qq + sp;
+        i32x8_t th, tl;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const float4 v = frag(sp, c);
+          uint32_t hi, lo;
+          split4(v.x * mul, v.y * mul, v.z * mul, v.w * mul, hi, lo);
+          th[c] = static_cast<int>(hi);
+          tl[c] = static_cast<int>(lo);
+        }
+        if (st < 7) {
+          qh[st] = th;
+          ql[st] = tl;
+        } else {
+          const u32x4_t* hv = reinterpret_cast<const u32x4_t*>(&th);
+          const u32x4_t* lv = reinterpret_cast<const u32x4_t*>(&tl);
+          lds_st128(ql_lds, hv[0]);
+          lds_st128(ql_lds + 16, hv[1]);
+          lds_st128(ql_lds + 32, lv[0]);
+          lds_st128(ql_lds + 48, lv[1]);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    const float* qp = a.q_pe + (static_cast<int64_t>(b) * nh + h) * kDr + 8 * g2;
+    // k^R part: the 32 rows of 64 fp32 (8 KB, contiguous) staged the same way
+    // (row 4i + (lane >> 4), columns 4 (lane & 15)..+3), then packed as bf16 fragments
+    const float* qpb = a.q_pe + (static_cast<int64_t>(b) * nh + kHeads * wv) * kDr;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + (lane >> 4), c = 4 * (lane & 15);
+      const float4 v = *reinterpret_cast<const float4*>(qpb + r * kDr + c);
+      lds_st128(qst + kQS * r + 4 * c, __builtin_bit_cast(u32x4_t, v));
+    }
+    wait_lgkm(0);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       float v[8];
-      const float4 lo = *reinterpret_cast<const float4*>(qp + 16 * q);
-      const float4 hi = *reinterpret_cast<const float4*>(qp + 16 * q + 4);
+      const float4 lo = __builtin_bit_cast(float4, lds_ld128(qst + kQS * r32 + 4 * (16 * q + 8 * g2)));
+      const float4 hi = __builtin_bit_cast(float4, lds_ld128(qst + kQS * r32 + 4 * (16 * q + 8 * g2 + 4)));
       v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
       v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
       lds_st128(qr_lds + 1024 * q, __builtin_bit_cast(u32x4_t, pack8(v)));
     }
-    // read back by this wave only (after its own writes complete)
+    wait_lgkm(0);
+    lds_barrier();   // every wave is done with the staging area before tiles are copied
   }
 
   // ---- per-lane constant offsets inside a staged tile

@@ -914,8 +914,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_f8mma_h128(
   uint32_t roff[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) roff[q] = kF8RopeOff + 128 * r32 + 16 * ((2 * q + g2) ^ vy);
-  // P.C B operand, column block nb, token half kk of a tile (transposed reads, as
-  // in the bf16-converting FP8 path): f8_toff[kk] + 32 ((nb & 8) | ((nb & 7) ^ f8_m))
+  // P.C B operand, column block nb, token half kk of a tile: one transposed read
+  // (ds_read_b64_tr_b8) at f8_toff[kk] + 32 ((nb & 8) | ((nb & 7) ^ f8_m)).  Lane
+  // s16 of 16-lane group (ch, g2) addresses token row 16kk + 8(m >> 2) + 4g2 + (m & 3),
+  // m = s16 >> 1, columns 32nb + 16ch + 8(s16 & 1)..+7, and receives column
+  // 32nb + 16ch + s16 of tokens 16kk + 8(j >> 2) + 4g2 + (j & 3), j = 0..7 (f8key of
+  // that row is 2m + g2, so the 8 rows of a read fall on distinct banks)
   const int s16 = lane & 15, ch = (lane >> 4) & 1;
   const int f8_m = s16 >> 1;
   uint32_t f8_toff[2];
@@ -1007,7 +1011,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_f8mma_h128(
   // and a zero scale, so that they add nothing to the products
   auto zero_tail = [&](uint32_t T, int nvalid) {
     const u32x4_t zero = {0u, 0u, 0u, 0u};
-    // row 8wv + 2i + (lane >> 5), chunk lane & 31: T + zt_base + 1024 i
+    // row 8wv + 2i + (lane >> 5), chunk lane & 31: zb + 1024 i
     const int lim = nvalid - 8 * wv - (lane >> 5);
     const uint32_t zb = opaque(T + kDc * (8 * wv + (lane >> 5)) + 16 * (lane & 31));
 #pragma unroll
@@ -1109,8 +1113,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_f8mma_h128(
   };
   auto issue = [&](int j) { return issue_pg(j, page_load(j)); };
   // the copies of one tile issued one at a time (spread over the products of a
-  // tile, so that the wave does not stall on a burst of them): cp_begin fixes
-  // the tile, cp_part(k) issues copy k (0..kF8Copies-1) in tile_issue_f8's order
+  // tile rather than as one burst): cp_begin fixes the tile and issues its scale
+  // copy, cp_part(k) issues code copy k (k < 4, rows 8wv + 2k, +1) or the k^R
+  // copy (k = 4); kF8Copies in all, as tile_issue_f8
   uint64_t cp_rows = 0, cp_scales = 0;
   int cp_nvalid = 0;
   uint32_t cp_stage = 0;

@@ -25,6 +25,7 @@
 // operands from it with ds_read_b64_tr_b16, the hardware transpose.
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "common.hpp"
 #include "epilogue.hpp"
@@ -434,6 +435,135 @@ __global__ __launch_bounds__(256) void k_gemm_uk(GemmArgs a) {
   }
 }
 
+// ---- large-M tiled product (prefill batch sizes) ---------------------------
+// For M in the hundreds and more every weight tile is worth reusing across X
+// rows: a workgroup owns a 128 (n) x 128 (m) output tile and walks K in chunks of
+// 64 with both operand tiles in LDS (two buffers; chunk c + 1 is loaded into
+// registers while chunk c is multiplied, every load a run of whole 128-byte
+// lines).  4 waves, wave (wn, wm) a 64 x 64 block of 2 x 2 mfma_f32_32x32x16_bf16
+// tiles.  Weight rows are the MFMA M side and X rows its N side, so a lane ends
+// with column pairs (n, n + 1) of one output row m: the epilogue's unit.
+constexpr int kTt = 128, kTk = 64;
+constexpr int kTPitch = kTk * 2 + 16;   // LDS bytes per staged row (conflict-free 16-byte reads)
+
+template <typename XT>
+__global__ __launch_bounds__(256, 2) void k_gemm_tile(GemmArgs a) {
+  // operand tiles, buffer b: W at tiles[b][0], X at tiles[b][1]; one array, so the
+  // output tile staged at the end may span all four
+  __shared__ __attribute__((aligned(16))) char tiles[2][2][kTt * kTPitch];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int z = blockIdx.z, n0 = blockIdx.x * kTt, m0 = blockIdx.y * kTt;
+  // staging: thread t moves 16-byte chunk c = t + 256 j (j < 4) of each tile: row
+  // c >> 3, k 8 (c & 7); rows past N or M re-read the last row (never stored)
+  const bf16_t* wp[4];
+  const XT* xp[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = tid + 256 * j, r = c >> 3, kc = 8 * (c & 7);
+    const int n = min(n0 + r, a.N - 1), m = min(m0 + r, a.M - 1);
+    wp[j] = (n < a.n_split ? static_cast<const bf16_t*>(a.w1) + static_cast<int64_t>(n) * a.ldw_n
+                           : static_cast<const bf16_t*>(a.w2) +
+                                 static_cast<int64_t>(n - a.n_split) * a.ldw_n) +
+            static_cast<int64_t>(z) * a.w_bs + kc;
+    xp[j] = static_cast<const XT*>(a.x) + static_cast<int64_t>(z) * a.x_bs +
+            static_cast<int64_t>(m) * a.ldx_m + kc;
+  }
+  // two register sets of staged chunks: chunk c is loaded into set c & 1 two steps
+  // before it is multiplied (so two chunks are in flight while one is multiplied)
+  u32x4_t wreg[2][4];
+  XVec<XT> xreg[2][4];
+  auto gload = [&](auto set_c, int k0) {
+    constexpr int st = decltype(set_c)::value;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      wreg[st][j] = *reinterpret_cast<const u32x4_t*>(wp[j] + k0);
+      xreg[st][j].load(xp[j] + k0);
+    }
+  };
+  auto lstore = [&](auto set_c, int buf) {
+    constexpr int st = decltype(set_c)::value;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = tid + 256 * j, off = (c >> 3) * kTPitch + 16 * (c & 7);
+      *reinterpret_cast<u32x4_t*>(&tiles[buf][0][off]) = wreg[st][j];
+      *reinterpret_cast<u32x4_t*>(&tiles[buf][1][off]) = xreg[st][j].bits();
+    }
+  };
+  const int wn = wv & 1, wm = wv >> 1, r32 = lane & 31, h = lane >> 5;
+  // operand of 32-row block i at k-step s: row 32i + r32 of the wave's half, k 16s + 8h
+  const int aoff = (64 * wn + r32) * kTPitch + 16 * h, boff = (64 * wm + r32) * kTPitch + 16 * h;
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  auto multiply = [&](int buf) {
+#pragma unroll
+    for (int s = 0; s < kTk / 16; ++s) {
+      bf16x8_t af[2], bf[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        af[i] = *reinterpret_cast<const bf16x8_t*>(&tiles[buf][0][aoff + 32 * i * kTPitch + 32 * s]);
+        bf[i] = *reinterpret_cast<const bf16x8_t*>(&tiles[buf][1][boff + 32 * i * kTPitch + 32 * s]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  const int nk = a.K / kTk;
+  gload(S0{}, 0);
+  if (nk > 1) gload(S1{}, kTk);
+  lstore(S0{}, 0);
+  __syncthreads();
+  // step c multiplies buffer c & 1 (chunk c); before that, chunk c + 2 is loaded
+  // into the register set chunk c came from, and after it chunk c + 1 goes from its
+  // set into the other buffer (last read before the previous barrier)
+  for (int kb = 0; kb < nk; kb += 2) {
+    if (kb + 2 < nk) gload(S0{}, (kb + 2) * kTk);
+    multiply(0);
+    if (kb + 1 < nk) lstore(S1{}, 1);
+    __syncthreads();
+    if (kb + 1 >= nk) break;
+    if (kb + 3 < nk) gload(S1{}, (kb + 3) * kTk);
+    multiply(1);
+    if (kb + 2 < nk) lstore(S0{}, 0);
+    __syncthreads();
+  }
+  // acc[i][j] element e of lane (r32, h): row 64wm + 32j + r32, column
+  // 64wn + 32i + 8(e >> 2) + 4h + (e & 3) of the tile.  The tile goes to LDS (the
+  // operand buffers are free after the last barrier) and a compact loop applies the
+  // epilogue to column pairs: unrolled over the accumulators, the epilogue's
+  // registers made the compiler spill the accumulators on every K step.
+  constexpr int kOPitch = kTt + 4;   // floats per staged output row
+  static_assert(kTt * kOPitch * 4 <= static_cast<int>(sizeof(tiles)), "output tile fits the operand buffers");
+  float* ot = reinterpret_cast<float*>(&tiles[0][0][0]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; e += 2)
+        *reinterpret_cast<float2*>(
+            &ot[(64 * wm + 32 * j + r32) * kOPitch + 64 * wn + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3)]) =
+            make_float2(acc[i][j][e], acc[i][j][e + 1]);
+  __syncthreads();
+  for (int q = tid; q < kTt * kTt / 2; q += 256) {   // pair q: row q / 64, columns 2 (q % 64), +1
+    const int ml = q >> 6, nl = 2 * (q & 63);
+    const int m = m0 + ml, n = n0 + nl;
+    if (m < a.M && n < a.N) {
+      const float2 v = *reinterpret_cast<const float2*>(&ot[ml * kOPitch + nl]);
+      gemm_epilogue<bf16_t>(a, z, m, n, v.x, v.y);
+    }
+  }
+}
+
 constexpr int kWsMinGroups = 512;   // workgroups wanted before K is split further
 
 struct WsPlan {
@@ -569,10 +699,19 @@ static bool xs_ok(const GemmArgs& a) {
          (a.n_split % 16 == 0 || a.n_split >= a.N) && a.K % (32 * kXsRing) == 0;
 }
 
+// Prefill-sized activations (M >= 256): the tiled product.  Same operand forms as
+// k_gemm_ws; K a multiple of the 64-wide chunk.
+static bool tile_ok(const GemmArgs& a) {
+  const int64_t groups = static_cast<int64_t>((a.N + kTt - 1) / kTt) * ((a.M + kTt - 1) / kTt) * a.batch;
+  // grids of fewer than 256 output tiles (narrow outputs such as the latent append)
+  // would leave most of the chip idle: those stay with the K-split weight stream
+  return ws_ok(a) && a.M >= 256 && a.K % kTk == 0 && a.n_split % 2 == 0 && groups >= 256;
+}
+
 bool fast_gemm_ok(const GemmArgs& a) { return ws_ok(a) || uk_ok(a); }
 
 size_t gemm_partial_bytes(const GemmArgs& a) {
-  if (!ws_ok(a)) return 0;
+  if (!ws_ok(a) || tile_ok(a)) return 0;
   if (xs_ok(a)) {
     const XsPlan q = xs_plan(a);
     return q.d > 1 ? static_cast<size_t>(q.d) * a.M * a.N * sizeof(float) : 0;
@@ -588,6 +727,14 @@ hipError_t launch_gemm_fast(const GemmArgs& a, void* partial, size_t partial_byt
     if (!uk_ok(a)) return hipErrorInvalidValue;
     dim3 grid(a.batch, a.N / kUkN, (a.M + kTile - 1) / kTile);
     hipLaunchKernelGGL(k_gemm_uk, grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
+  if (tile_ok(a)) {
+    const dim3 grid((a.N + kTt - 1) / kTt, (a.M + kTt - 1) / kTt, a.batch);
+    if (a.x_f32)
+      hipLaunchKernelGGL(k_gemm_tile<float>, grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(k_gemm_tile<bf16_t>, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
   }
   if (xs_ok(a)) {

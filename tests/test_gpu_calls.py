@@ -359,3 +359,58 @@ def test_absorb_out(name, path):
         np.float64).reshape(B, w.n_heads, w.d_latent)
     ref = np.stack([O.absorb_out(hl[b], hu, ho, w.n_heads, w.d_head, w.d_latent) for b in range(B)])
     assert_parity(to_np(u), ref, w.dtype, "u")
+
+
+# ------------------------------------------- prefill-sized activation batches --
+# M = 300 rows takes the tiled large-M product (128-row tiles: two full ones and a
+# ragged tail of 44); the oracle is evaluated on sampled rows, tile edges included.
+ROWS = [0, 1, 127, 128, 200, 255, 256, 299]
+
+
+@pytest.mark.parametrize("name", ["lite", "full"])
+def test_absorb_q_large_batch(name):
+    w = _wl(name)
+    B = 300
+    note(f"absorb_q {name} B={B}")
+    sh = {n: w.weight_shape(n) for n in ("w_q", "w_qr", "w_uk")}
+    std = {n: 1 / math.sqrt(w.fan_in(n)) for n in sh}
+    dev = {n: device_tensor(torch, w, n, sh[n], std[n]) for n in sh}
+    h = device_tensor(torch, w, "h_q", (B, w.hidden))
+    pos_np = ((np.arange(B, dtype=np.int64) * 4099) % 131072).astype(np.int32)
+    q_lat = torch.empty((B, w.n_heads, w.d_latent), dtype=torch.float32, device="cuda")
+    q_pe = torch.empty((B, w.n_heads, w.d_rope), dtype=torch.float32, device="cuda")
+    d = _dims(w)
+    ws = torch.empty(max(1, M.mla_workspace_bytes(d, B)), dtype=torch.uint8, device="cuda")
+    M.mla_absorb_q(d, h, dev["w_q"], dev["w_qr"], dev["w_uk"], torch.tensor(pos_np, device="cuda"),
+                   q_lat, q_pe, ws)
+    hh = host_tensor(w, "h_q", (B, w.hidden))
+    hw = {n: host_tensor(w, n, sh[n], std[n]) for n in sh}
+    ref_lat, ref_pe = [], []
+    for b in ROWS:
+        ql, qp = O.absorb_q(hh[b], hw["w_q"], hw["w_qr"], hw["w_uk"], int(pos_np[b]), w.n_heads,
+                            w.d_head, w.d_latent, w.d_rope, w.rope_base)
+        ref_lat.append(ql)
+        ref_pe.append(qp)
+    assert_parity(to_np(q_lat)[ROWS], np.stack(ref_lat), w.dtype, "q_lat")
+    assert_parity(to_np(q_pe)[ROWS], np.stack(ref_pe), w.dtype, "q_pe")
+
+
+@pytest.mark.parametrize("name", ["lite", "full"])
+def test_absorb_out_large_batch(name):
+    w = _wl(name)
+    B = 300
+    note(f"absorb_out {name} B={B}")
+    std = {n: 1 / math.sqrt(w.fan_in(n)) for n in ("w_uv", "w_o")}
+    wuv = device_tensor(torch, w, "w_uv", w.weight_shape("w_uv"), std["w_uv"])
+    wo = device_tensor(torch, w, "w_o", w.weight_shape("w_o"), std["w_o"])
+    o_lat = device_tensor(torch, w, "o_lat_in", (B, w.n_heads, w.d_latent), dtype=torch.float32)
+    u = torch.empty((B, w.hidden), dtype=torch.float32, device="cuda")
+    d = _dims(w)
+    ws = torch.empty(max(1, M.mla_workspace_bytes(d, B)), dtype=torch.uint8, device="cuda")
+    M.mla_absorb_out(d, o_lat, wuv, wo, u, ws)
+    hu = host_tensor(w, "w_uv", w.weight_shape("w_uv"), std["w_uv"])
+    ho = host_tensor(w, "w_o", w.weight_shape("w_o"), std["w_o"])
+    hl = I.normal_f32(I.stream_key(w.seed, "o_lat_in"), 0, B * w.n_heads * w.d_latent).astype(
+        np.float64).reshape(B, w.n_heads, w.d_latent)
+    ref = np.stack([O.absorb_out(hl[b], hu, ho, w.n_heads, w.d_head, w.d_latent) for b in ROWS])
+    assert_parity(to_np(u)[ROWS], ref, w.dtype, "u")

@@ -112,8 +112,14 @@ class DeviceWorkload:
         self.q_pe = torch.empty((B, nh, w.d_rope), dtype=f32, device=self.dev)
         self.o_part = torch.empty((B, self.S, nh, w.d_latent), dtype=torch.float32, device=self.dev)
         self.lse_part = torch.empty((B, self.S, nh), dtype=torch.float32, device=self.dev)
-        self.o_lat = torch.empty((B, nh, w.d_latent), dtype=f32, device=self.dev)
-        self.lse = torch.empty((B, nh), dtype=torch.float32, device=self.dev)
+        if self.S == 1:
+            # one split: the merge is the identity, so the split's output (same layout)
+            # is the step's o_lat / lse and merge() has nothing to do
+            self.o_lat = self.o_part.view(B, nh, w.d_latent)
+            self.lse = self.lse_part.view(B, nh)
+        else:
+            self.o_lat = torch.empty((B, nh, w.d_latent), dtype=f32, device=self.dev)
+            self.lse = torch.empty((B, nh), dtype=torch.float32, device=self.dev)
         self.u = torch.empty((B, w.hidden), dtype=f32, device=self.dev)
         ws_bytes = mla_workspace_bytes(self.dims, B)
         if w.d_cq:
@@ -166,6 +172,8 @@ class DeviceWorkload:
                self.o_part, self.lse_part)
 
     def merge(self):
+        if self.S == 1:
+            return              # o_lat / lse are the single split's output
         mla_merge_lse(self.dims, self.o_part, self.lse_part, self.o_lat, self.lse)
 
     def absorb_out(self):

@@ -482,8 +482,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
 
   // scores S^T[t, h] of the tile in slot T: lane holds head 32wv + r32 and
   // tokens 8(i >> 2) + 4g2 + (i & 3), i = 0..15
-  // `hook` runs once, after the first products are issued (the next tile's
-  // copies go out there, in the shadow of the products)
+  // `hook` runs once, among the products (the next tile's copies go out there, in
+  // their shadow): wave w at k-step 8w, so the four waves do not all push their
+  // copies into the memory pipeline at the same moment
   auto scores = [&](uint32_t T, auto&& hook) {
     f32x16_t acc;
     const uint32_t sa0 = T + soff[0], sa1 = T + soff[1];
@@ -509,7 +510,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
         else if (k == kKSteps - 1) mfma_v_last(acc, ar[k % kARing], qf[k]);
         else mfma_v(acc, ar[k % kARing], qf[k]);
       }
-      if (ks == 0) hook();
+      if ((ks & 7) == 0 && (ks >> 3) == wv) hook();   // the waves issue their copies in turn
       __builtin_amdgcn_sched_barrier(0);
     }
     return acc;

@@ -138,14 +138,8 @@ __device__ __forceinline__ f32x16_t mfma_v_first(const bf16x8_t& a, const bf16x8
 __device__ __forceinline__ void mfma_v(f32x16_t& d, const bf16x8_t& a, const bf16x8_t& b) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
-__device__ __forceinline__ void mfma_v_nop(f32x16_t& d, const bf16x8_t& a, const bf16x8_t& b) {
-  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
-}
 __device__ __forceinline__ void mfma_v_last(f32x16_t& d, const bf16x8_t& a, const bf16x8_t& b) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 15" : "+v"(d) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_v_last_nop(f32x16_t& d, const bf16x8_t& a, const bf16x8_t& b) {
-  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 15" : "+v"(d) : "v"(a), "v"(b));
 }
 
 // Work-unit index of workgroup x: consecutive splits of a sequence go to the
@@ -357,10 +351,6 @@ __device__ __forceinline__ void lds_st32(uint32_t addr, uint32_t v) {
   *reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(static_cast<uintptr_t>(addr)) = v;
 }
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) const u32x2_t lds_u32x2;
-__device__ __forceinline__ u32x2_t lds_ld64(uint32_t addr) {
-  return *reinterpret_cast<lds_u32x2*>(static_cast<uintptr_t>(addr));
-}
 __device__ __forceinline__ float lds_f32(uint32_t addr) {
   return *reinterpret_cast<const __attribute__((address_space(3))) float*>(static_cast<uintptr_t>(addr));
 }

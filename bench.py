@@ -187,8 +187,7 @@ def main():
         if args.attention_only:
             dw.attention()
             return
-        dw.absorb_q()
-        dw.append()
+        dw.query_and_append()
         if ev is not None:
             ev[0].record(stream)
         dw.attention()

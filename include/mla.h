@@ -115,6 +115,27 @@ mla_status mla_absorb_q(const mla_dims* dims, const void* h, const void* w_q, co
                         float* q_pe, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * mla_absorb_q and mla_append_latent of the same rows in one call ([Report]
+ * §2.2/§2.3/§3.1: the step's new token is both queried and cached from the same
+ * h): row b is token (row_seq[b], pos[b]); its absorbed query goes to
+ * q_lat / q_pe and its latent row [W_DKV h | RoPE(W_KR h, pos)] to the pool,
+ * exactly as the two calls define them.  Both products read h once: on the
+ * matrix-core path (bf16 dtype, batch <= 64) they run as one projection over
+ * [W_Q; W_QR; W_DKV; W_KR]; other shapes make the two calls in turn.
+ * Arguments as in those calls (pos serves as row_pos); workspace: at least
+ * mla_workspace_bytes(dims, batch) bytes, 256-byte aligned.  Out-of-range rows
+ * are not written to the pool and set the device error word, as in
+ * mla_append_latent; their queries are still computed.
+ */
+mla_status mla_absorb_q_append(const mla_dims* dims, const void* h, const void* w_q,
+                               const void* w_qr, const void* w_uk, const void* w_dkv,
+                               const void* w_kr, const int32_t* pos, const int32_t* row_seq,
+                               int32_t batch, const int32_t* block_table, int32_t n_seqs,
+                               int32_t max_pages, void* pool, int64_t num_pages, float* q_lat,
+                               float* q_pe, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/*
  * Split-KV latent attention ([Report] §2.3, §2.4: every head scores the same
  * cached latent rows, s_ij = tau (q_lat,i . c_j + q_pe,i . k^R_j)).  Sequence b has
  * seq_lens[b] = L tokens (positions 0..L-1, the decode token included).  With

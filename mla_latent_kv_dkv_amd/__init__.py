@@ -19,7 +19,7 @@ MLA_ABI_VERSION = 1
 MLA_F32, MLA_BF16 = 0, 1
 
 __all__ = ["MlaDims", "MlaError", "make_dims", "load", "mla_append_latent", "mla_absorb_q",
-           "mla_absorb_q_cq", "mla_workspace_bytes_cq",
+           "mla_absorb_q_append", "mla_absorb_q_cq", "mla_workspace_bytes_cq",
            "mla_decode_attention", "mla_merge_lse", "mla_absorb_out", "mla_workspace_bytes",
            "mla_append_workspace_bytes", "mla_device_error", "mla_set_kernel_path",
            "mla_status_string", "mla_fp8_page_bytes", "mla_quantize_rows_fp8",
@@ -55,6 +55,8 @@ _DIMS = ctypes.POINTER(MlaDims)
 _SIGS = {
     "mla_append_latent": [_DIMS, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _P, _I64, _P, _SZ, _P],
     "mla_absorb_q": [_DIMS, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P],
+    "mla_absorb_q_append": [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _P, _I64,
+                            _P, _P, _P, _SZ, _P],
     "mla_absorb_q_cq": [_DIMS, _I32, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P],
     "mla_decode_attention": [_DIMS, _P, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _P, _P, _P],
     "mla_merge_lse": [_DIMS, _P, _P, _I32, _I32, _P, _P, _P],
@@ -192,6 +194,34 @@ def mla_absorb_q(dims, h, w_q, w_qr, w_uk, pos, q_lat, q_pe, workspace, stream=N
     _check("mla_absorb_q", load().mla_absorb_q(
         ctypes.byref(dims), _ptr(h), _ptr(w_q), _ptr(w_qr), _ptr(w_uk), _ptr(pos), B, _ptr(q_lat),
         _ptr(q_pe), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def mla_absorb_q_append(dims, h, w_q, w_qr, w_uk, w_dkv, w_kr, pos, row_seq, block_table, pool,
+                        q_lat, q_pe, workspace, stream=None):
+    """mla_absorb_q and mla_append_latent of the same rows (row b = token
+    (row_seq[b], pos[b])) in one call; one projection over all four weights
+    where the matrix-core path applies."""
+    import torch
+    B, nh, row = h.shape[0], dims.n_heads, dims.d_latent + dims.d_rope
+    e = _elem(dims)
+    _expect(h, (B, dims.hidden), e, "h")
+    _expect(w_q, (nh * dims.d_head, dims.hidden), e, "w_q")
+    _expect(w_qr, (nh * dims.d_rope, dims.hidden), e, "w_qr")
+    _expect(w_uk, (nh * dims.d_head, dims.d_latent), e, "w_uk")
+    _expect(w_dkv, (dims.d_latent, dims.hidden), e, "w_dkv")
+    _expect(w_kr, (dims.d_rope, dims.hidden), e, "w_kr")
+    _expect(pos, (B,), torch.int32, "pos")
+    _expect(row_seq, (B,), torch.int32, "row_seq")
+    _expect(pool, (pool.shape[0], dims.page_size, row), e, "pool")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2:
+        raise ValueError("block_table must be int32 [n_seqs, max_pages]")
+    _expect(q_lat, (B, nh, dims.d_latent), torch.float32, "q_lat")
+    _expect(q_pe, (B, nh, dims.d_rope), torch.float32, "q_pe")
+    _check("mla_absorb_q_append", load().mla_absorb_q_append(
+        ctypes.byref(dims), _ptr(h), _ptr(w_q), _ptr(w_qr), _ptr(w_uk), _ptr(w_dkv), _ptr(w_kr),
+        _ptr(pos), _ptr(row_seq), B, _ptr(block_table), block_table.shape[0], block_table.shape[1],
+        _ptr(pool), pool.shape[0], _ptr(q_lat), _ptr(q_pe), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def mla_absorb_q_cq(dims, h, w_dq, w_uq, w_qr, w_uk, pos, q_lat, q_pe, workspace, stream=None):

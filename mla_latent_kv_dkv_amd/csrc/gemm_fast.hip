@@ -249,12 +249,20 @@ __global__ __launch_bounds__(64 * kXsWaves, 1) void k_gemm_xs(GemmArgs a, int d,
   const int rowb = 2 * kw;   // LDS bytes per X row
 
   // this lane's weight row in the wave's i-th strip, at the start of the slice
+  // (with the fused latent append, strips from n_append on come from w3 / w4)
   auto wrow = [&](int i) -> const bf16_t* {
     const int n0 = 16 * (wave + i * nwaves);
-    const bf16_t* base = n0 < a.n_split
-                             ? static_cast<const bf16_t*>(a.w1) + static_cast<int64_t>(n0) * a.ldw_n
-                             : static_cast<const bf16_t*>(a.w2) +
-                                   static_cast<int64_t>(n0 - a.n_split) * a.ldw_n;
+    const bf16_t* base;
+    if (a.epi == EPI_QPROJ_APPEND && n0 >= a.n_append) {
+      const int r = n0 - a.n_append;
+      base = r < a.n_split3
+                 ? static_cast<const bf16_t*>(a.w3) + static_cast<int64_t>(r) * a.ldw_n
+                 : static_cast<const bf16_t*>(a.w4) + static_cast<int64_t>(r - a.n_split3) * a.ldw_n;
+    } else {
+      base = n0 < a.n_split
+                 ? static_cast<const bf16_t*>(a.w1) + static_cast<int64_t>(n0) * a.ldw_n
+                 : static_cast<const bf16_t*>(a.w2) + static_cast<int64_t>(n0 - a.n_split) * a.ldw_n;
+    }
     return base + static_cast<int64_t>(n16) * a.ldw_n + kbeg + 8 * g;
   };
   const int total = my * nsteps;   // steps of this wave over all its strips
@@ -695,9 +703,15 @@ static bool uk_ok(const GemmArgs& a) {
 // wave of the grid strips to stream (narrow outputs, like the 576-wide latent
 // append, leave most waves idle there and go to k_gemm_ws): the X-stationary kernel.
 static bool xs_ok(const GemmArgs& a) {
+  if (a.epi == EPI_QPROJ_APPEND &&
+      !(a.n_append % 16 == 0 && a.n_split3 % 16 == 0 && a.n_split < a.n_append))
+    return false;
   return ws_ok(a) && a.batch == 1 && a.M <= 64 && a.N >= 2048 && a.N % 16 == 0 &&
          (a.n_split % 16 == 0 || a.n_split >= a.N) && a.K % (32 * kXsRing) == 0;
 }
+
+// The fused query projection + latent append runs only on k_gemm_xs.
+bool fused_qa_ok(const GemmArgs& a) { return a.epi == EPI_QPROJ_APPEND && xs_ok(a); }
 
 // Prefill-sized activations (M >= 256): the tiled product.  Same operand forms as
 // k_gemm_ws; K a multiple of the 64-wide chunk.
@@ -705,7 +719,8 @@ static bool tile_ok(const GemmArgs& a) {
   const int64_t groups = static_cast<int64_t>((a.N + kTt - 1) / kTt) * ((a.M + kTt - 1) / kTt) * a.batch;
   // grids of fewer than 256 output tiles (narrow outputs such as the latent append)
   // would leave most of the chip idle: those stay with the K-split weight stream
-  return ws_ok(a) && a.M >= 256 && a.K % kTk == 0 && a.n_split % 2 == 0 && groups >= 256;
+  return ws_ok(a) && a.epi != EPI_QPROJ_APPEND && a.M >= 256 && a.K % kTk == 0 &&
+         a.n_split % 2 == 0 && groups >= 256;
 }
 
 bool fast_gemm_ok(const GemmArgs& a) { return ws_ok(a) || uk_ok(a); }
@@ -723,6 +738,7 @@ size_t gemm_partial_bytes(const GemmArgs& a) {
 hipError_t launch_gemm_fast(const GemmArgs& a, void* partial, size_t partial_bytes,
                             hipStream_t stream) {
   if (a.M == 0 || a.N == 0 || a.batch == 0) return hipSuccess;
+  if (a.epi == EPI_QPROJ_APPEND && !xs_ok(a)) return hipErrorInvalidValue;
   if (!ws_ok(a)) {
     if (!uk_ok(a)) return hipErrorInvalidValue;
     dim3 grid(a.batch, a.N / kUkN, (a.M + kTile - 1) / kTile);

@@ -12,6 +12,10 @@ enum GemmEpilogue : int {
   EPI_STORE = 0,   // y[z*y_bs + m*ldy + n]
   EPI_APPEND = 1,  // [c | RoPE(k^R, row_pos[m])] scattered into the paged pool
   EPI_QPROJ = 2,   // n < n_split -> y (q^C); n >= n_split -> RoPE per head -> y2 (q_pe)
+  // EPI_QPROJ for n < n_append, and the latent append of the same rows for
+  // n >= n_append: W rows from w3 (c^KV, n - n_append < n_split3) and w4 (k^R),
+  // written as EPI_APPEND does into the pool y3
+  EPI_QPROJ_APPEND = 3,
 };
 
 struct GemmArgs {
@@ -38,6 +42,11 @@ struct GemmArgs {
   int n_seqs, max_pages, page_size, row_width;
   int64_t num_pages;
   int* err;
+  // EPI_QPROJ_APPEND only
+  const void* w3;
+  const void* w4;
+  int n_append, n_split3;
+  void* y3;
 };
 
 hipError_t launch_gemm_generic(const GemmArgs& a, bool bf16, hipStream_t stream);

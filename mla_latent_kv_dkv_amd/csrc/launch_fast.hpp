@@ -11,6 +11,8 @@ namespace mla {
 int* error_word_address();
 
 bool fast_gemm_ok(const GemmArgs& a);
+// the query projection with the fused latent append (EPI_QPROJ_APPEND) on k_gemm_xs
+bool fused_qa_ok(const GemmArgs& a);
 // fp32 scratch the fast GEMM needs for its K-split partials (0 if none)
 size_t gemm_partial_bytes(const GemmArgs& a);
 hipError_t launch_gemm_fast(const GemmArgs& a, void* partial, size_t partial_bytes,

@@ -78,6 +78,18 @@ mla::GemmArgs qproj_args(const mla_dims* d, int batch) {
   return a;
 }
 
+// The query projection and the latent append of the same rows as one product:
+// columns [q^C | q^R | c^KV | k^R] over [W_Q; W_QR; W_DKV; W_KR].
+mla::GemmArgs qa_args(const mla_dims* d, int batch) {
+  mla::GemmArgs a = qproj_args(d, batch);
+  a.epi = mla::EPI_QPROJ_APPEND;
+  a.n_append = a.N;
+  a.n_split3 = d->d_latent;
+  a.N += d->d_latent + d->d_rope;
+  a.row_width = d->d_latent + d->d_rope;
+  return a;
+}
+
 // Compressed query, first product: [c^Q | q^R] = h [W_DQ; W_QR]^T, RoPE on the
 // q^R columns (the q^C split of EPI_QPROJ with n_split = d_cq); c^Q in dtype.
 mla::GemmArgs cqproj_args(const mla_dims* d, int d_cq, int batch) {
@@ -298,7 +310,7 @@ size_t mla_workspace_bytes(const mla_dims* d, int32_t batch) {
   size_t part = 0;
   if (batch > 0) {
     for (const mla::GemmArgs& a : {qproj_args(d, batch), uk_args(d, batch), uv_args(d, batch),
-                                   oproj_args(d, batch), append_args(d, batch)})
+                                   oproj_args(d, batch), append_args(d, batch), qa_args(d, batch)})
       part = std::max(part, partial_bytes(d, a));
   }
   return act_bytes(d, batch) + part + 256;
@@ -363,6 +375,48 @@ mla_status mla_absorb_q(const mla_dims* d, const void* h, const void* w_q, const
   mla::GemmArgs a = qproj_args(d, batch);
   a.x = h; a.w1 = w_q; a.w2 = w_qr; a.y = ws; a.y2 = q_pe; a.pos = pos;
   if (run_gemm(d, a, part, pbytes, stream) != hipSuccess) return MLA_ERR_HIP;
+  // 2) q_lat[b, i, :] = W_UK,i^T q^C[b, i, :] per head i
+  mla::GemmArgs g = uk_args(d, batch);
+  g.x = ws; g.w1 = w_uk; g.w2 = w_uk; g.y = q_lat;
+  return hip_status(run_gemm(d, g, part, pbytes, stream));
+}
+
+mla_status mla_absorb_q_append(const mla_dims* d, const void* h, const void* w_q,
+                               const void* w_qr, const void* w_uk, const void* w_dkv,
+                               const void* w_kr, const int32_t* pos, const int32_t* row_seq,
+                               int32_t batch, const int32_t* block_table, int32_t n_seqs,
+                               int32_t max_pages, void* pool, int64_t num_pages, float* q_lat,
+                               float* q_pe, void* ws, size_t ws_bytes, hipStream_t stream) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || batch > (1 << 20) || n_seqs < 0 || max_pages < 0 || num_pages < 0)
+    return MLA_ERR_SHAPE;
+  if (batch == 0) return MLA_OK;
+  if (n_seqs < 1 || max_pages < 1 || num_pages < 1) return MLA_ERR_SHAPE;
+  if (static_cast<int64_t>(max_pages) * d->page_size > (int64_t{1} << 30)) return MLA_ERR_SHAPE;
+  if (!h || !w_q || !w_qr || !w_uk || !w_dkv || !w_kr || !pos || !row_seq || !block_table ||
+      !pool || !q_lat || !q_pe)
+    return MLA_ERR_NULL;
+  if (!ws || ws_bytes < mla_workspace_bytes(d, batch) || !ws_aligned(ws)) return MLA_ERR_WORKSPACE;
+  mla::GemmArgs a = qa_args(d, batch);
+  if (!(use_fast() && d->dtype == MLA_BF16 && mla::fused_qa_ok(a))) {
+    // shapes the fused product does not take: the two calls one after the other
+    st = mla_absorb_q(d, h, w_q, w_qr, w_uk, pos, batch, q_lat, q_pe, ws, ws_bytes, stream);
+    if (st != MLA_OK) return st;
+    return mla_append_latent(d, h, w_dkv, w_kr, row_seq, pos, batch, block_table, n_seqs,
+                             max_pages, pool, num_pages, ws, ws_bytes, stream);
+  }
+  int* err = err_word();
+  if (!err) return MLA_ERR_HIP;
+  char* part = static_cast<char*>(ws) + act_bytes(d, batch);
+  const size_t pbytes = ws_bytes - act_bytes(d, batch);
+  // 1) [q^C | q^R | c^KV | k^R] = h [W_Q; W_QR; W_DKV; W_KR]^T: q^C -> workspace,
+  //    RoPE'd q^R -> q_pe, [c^KV | RoPE(k^R)] -> the rows' pool slots
+  a.x = h; a.w1 = w_q; a.w2 = w_qr; a.w3 = w_dkv; a.w4 = w_kr;
+  a.y = ws; a.y2 = q_pe; a.y3 = pool; a.pos = pos; a.row_seq = row_seq;
+  a.block_table = block_table; a.n_seqs = n_seqs; a.max_pages = max_pages;
+  a.page_size = d->page_size; a.num_pages = num_pages; a.err = err;
+  if (mla::launch_gemm_fast(a, part, pbytes, stream) != hipSuccess) return MLA_ERR_HIP;
   // 2) q_lat[b, i, :] = W_UK,i^T q^C[b, i, :] per head i
   mla::GemmArgs g = uk_args(d, batch);
   g.x = ws; g.w1 = w_uk; g.w2 = w_uk; g.y = q_lat;

@@ -8,7 +8,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (make_dims, mla_absorb_out, mla_absorb_q, mla_absorb_q_cq, mla_append_latent,
+from . import (make_dims, mla_absorb_out, mla_absorb_q, mla_absorb_q_append, mla_absorb_q_cq,
+               mla_append_latent,
                mla_append_latent_fp8, mla_append_workspace_bytes, mla_append_workspace_bytes_fp8,
                mla_decode_attention, mla_decode_attention_fp8, mla_fp8_page_bytes, mla_merge_lse,
                mla_prefill_attention, mla_quantize_rows_fp8, mla_workspace_bytes,
@@ -162,6 +163,23 @@ class DeviceWorkload:
         append(self.dims, self.h, self.weights["w_dkv"], self.weights["w_kr"], self.seq_ids,
                self.pos, self.block_table, self.pool, self.ws_append)
 
+    def absorb_q_append(self):
+        """absorb_q and append of the step's tokens in one call (bf16 or f32 pool,
+        uncompressed query): one projection reads h for both."""
+        W = self.weights
+        mla_absorb_q_append(self.dims, self.h, W["w_q"], W["w_qr"], W["w_uk"], W["w_dkv"],
+                            W["w_kr"], self.pos, self.seq_ids, self.block_table, self.pool,
+                            self.q_lat, self.q_pe, self.ws)
+
+    def query_and_append(self):
+        """The step's first two calls: fused where the pool format and query form
+        allow, else absorb_q then append."""
+        if self.fp8 or self.w.d_cq:
+            self.absorb_q()
+            self.append()
+        else:
+            self.absorb_q_append()
+
     def attention(self):
         if self.chunk:
             mla_prefill_attention(self.dims, self.q_lat, self.q_pe, self.pool, self.block_table,
@@ -181,9 +199,9 @@ class DeviceWorkload:
                        self.ws)
 
     def step(self):
-        """absorb_q -> append (decode token at L-1) -> attention -> merge -> absorb_out."""
-        self.absorb_q()
-        self.append()
+        """absorb_q -> append (decode token at L-1) -> attention -> merge -> absorb_out
+        (the first two as one call where the pool format and query form allow)."""
+        self.query_and_append()
         self.attention()
         self.merge()
         self.absorb_out()

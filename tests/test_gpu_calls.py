@@ -414,3 +414,47 @@ def test_absorb_out_large_batch(name):
         np.float64).reshape(B, w.n_heads, w.d_latent)
     ref = np.stack([O.absorb_out(hl[b], hu, ho, w.n_heads, w.d_head, w.d_latent) for b in ROWS])
     assert_parity(to_np(u)[ROWS], ref, w.dtype, "u")
+
+
+# ------------------------------------------------- fused absorb_q + append --
+@pytest.mark.parametrize("name,B", [("tiny", 5), ("full", 5), ("full", 64)])
+def test_absorb_q_append(name, B):
+    """The fused call against the oracle (queries and appended rows), its queries
+    equal to mla_absorb_q's, the pool untouched outside the appended slots (the
+    f32 shape exercises the fallback to the two calls)."""
+    w = _wl(name, batch=B)
+    note(f"absorb_q_append {name} B={B}")
+    lens = np.array([3 + 37 * b for b in range(B)], dtype=np.int32)   # token b at lens[b] - 1
+    bt, total = I.page_table(w, lens)
+    seqs = np.arange(B, dtype=np.int32)
+    poss = (lens - 1).astype(np.int32)
+    sh = {n: w.weight_shape(n) for n in ("w_q", "w_qr", "w_uk", "w_dkv", "w_kr")}
+    std = {n: 1 / math.sqrt(w.fan_in(n)) for n in sh}
+    dev = {n: device_tensor(torch, w, n, sh[n], std[n]) for n in sh}
+    h = device_tensor(torch, w, "h_q", (B, w.hidden))
+    d = _dims(w)
+    ws = torch.empty(M.mla_workspace_bytes(d, B), dtype=torch.uint8, device="cuda")
+    q_lat = torch.empty((B, w.n_heads, w.d_latent), dtype=torch.float32, device="cuda")
+    q_pe = torch.empty((B, w.n_heads, w.d_rope), dtype=torch.float32, device="cuda")
+    pool = _sentinel_pool(w, total)
+    pos_t, seq_t = torch.tensor(poss, device="cuda"), torch.tensor(seqs, device="cuda")
+    M.mla_device_error(clear=True)
+    M.mla_absorb_q_append(d, h, dev["w_q"], dev["w_qr"], dev["w_uk"], dev["w_dkv"], dev["w_kr"],
+                          pos_t, seq_t, torch.tensor(bt, device="cuda"), pool, q_lat, q_pe, ws)
+    q_lat2, q_pe2 = torch.empty_like(q_lat), torch.empty_like(q_pe)
+    M.mla_absorb_q(d, h, dev["w_q"], dev["w_qr"], dev["w_uk"], pos_t, q_lat2, q_pe2, ws)
+    assert torch.equal(q_lat, q_lat2) and torch.equal(q_pe, q_pe2), "queries differ from mla_absorb_q"
+    hh = host_tensor(w, "h_q", (B, w.hidden))
+    hw = {n: host_tensor(w, n, sh[n], std[n]) for n in sh}
+    rl, rp = zip(*[O.absorb_q(hh[b], hw["w_q"], hw["w_qr"], hw["w_uk"], int(poss[b]), w.n_heads,
+                              w.d_head, w.d_latent, w.d_rope, w.rope_base) for b in range(B)])
+    assert_parity(to_np(q_lat), np.stack(rl), w.dtype, "q_lat")
+    assert_parity(to_np(q_pe), np.stack(rp), w.dtype, "q_pe")
+    got = to_np(pool).reshape(-1, w.row)
+    ref_rows = O.latent_rows(hh, hw["w_dkv"], hw["w_kr"], poss, w.rope_base)
+    slots = np.array([O.page_slot(bt, s, p, w.page_size) for s, p in zip(seqs, poss)])
+    untouched = np.ones(got.shape[0], bool)
+    untouched[slots] = False
+    assert (got[untouched] == -3.5).all(), "rows outside the appended slots changed"
+    assert_parity(got[slots], ref_rows, w.dtype, "appended rows")
+    assert M.mla_device_error() == 0

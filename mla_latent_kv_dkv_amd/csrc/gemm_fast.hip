@@ -451,75 +451,92 @@ __global__ __launch_bounds__(256) void k_gemm_uk(GemmArgs a) {
 // lines).  4 waves, wave (wn, wm) a 64 x 64 block of 2 x 2 mfma_f32_32x32x16_bf16
 // tiles.  Weight rows are the MFMA M side and X rows its N side, so a lane ends
 // with column pairs (n, n + 1) of one output row m: the epilogue's unit.
-constexpr int kTt = 128, kTk = 64;
+constexpr int kTt = 128, kTk = 64;   // large tile; K chunk
 constexpr int kTPitch = kTk * 2 + 16;   // LDS bytes per staged row (conflict-free 16-byte reads)
 
-template <typename XT>
+// TN x TM output tile (TN, TM multiples of 64): 4 waves in 2 x 2, each wave
+// TN/64 x TM/64 blocks of 32 x 32.  TN = TM = 128 for prefill-sized X; 64 x 64 for
+// the per-head batched products at decode sizes, whose 128-row outputs give 2
+// tiles per head.
+template <typename XT, int TN, int TM>
 __global__ __launch_bounds__(256, 2) void k_gemm_tile(GemmArgs a) {
-  // operand tiles, buffer b: W at tiles[b][0], X at tiles[b][1]; one array, so the
-  // output tile staged at the end may span all four
-  __shared__ __attribute__((aligned(16))) char tiles[2][2][kTt * kTPitch];
+  constexpr int BN = TN / 64, BM = TM / 64;   // 32-row blocks per wave
+  constexpr int CW = TN / 32, CX = TM / 32;   // 16-byte chunks per thread per K chunk
+  // operand tiles, buffer b: W rows at tiles[b][0], X rows after them; one array,
+  // so the output tile staged at the end may span both buffers
+  __shared__ __attribute__((aligned(16))) char tiles[2][(TN + TM) * kTPitch];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int z = blockIdx.z, n0 = blockIdx.x * kTt, m0 = blockIdx.y * kTt;
-  // staging: thread t moves 16-byte chunk c = t + 256 j (j < 4) of each tile: row
-  // c >> 3, k 8 (c & 7); rows past N or M re-read the last row (never stored)
-  const bf16_t* wp[4];
-  const XT* xp[4];
+  const int z = blockIdx.z, n0 = blockIdx.x * TN, m0 = blockIdx.y * TM;
+  // staging: thread t moves 16-byte chunks c = t + 256 j of each tile: row c >> 3,
+  // k 8 (c & 7); rows past N or M re-read the last row (never stored)
+  const bf16_t* wp[CW];
+  const XT* xp[CX];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < CW; ++j) {
     const int c = tid + 256 * j, r = c >> 3, kc = 8 * (c & 7);
-    const int n = min(n0 + r, a.N - 1), m = min(m0 + r, a.M - 1);
+    const int n = min(n0 + r, a.N - 1);
     wp[j] = (n < a.n_split ? static_cast<const bf16_t*>(a.w1) + static_cast<int64_t>(n) * a.ldw_n
                            : static_cast<const bf16_t*>(a.w2) +
                                  static_cast<int64_t>(n - a.n_split) * a.ldw_n) +
             static_cast<int64_t>(z) * a.w_bs + kc;
+  }
+#pragma unroll
+  for (int j = 0; j < CX; ++j) {
+    const int c = tid + 256 * j, r = c >> 3, kc = 8 * (c & 7);
+    const int m = min(m0 + r, a.M - 1);
     xp[j] = static_cast<const XT*>(a.x) + static_cast<int64_t>(z) * a.x_bs +
             static_cast<int64_t>(m) * a.ldx_m + kc;
   }
   // two register sets of staged chunks: chunk c is loaded into set c & 1 two steps
   // before it is multiplied (so two chunks are in flight while one is multiplied)
-  u32x4_t wreg[2][4];
-  XVec<XT> xreg[2][4];
+  u32x4_t wreg[2][CW];
+  XVec<XT> xreg[2][CX];
   auto gload = [&](auto set_c, int k0) {
     constexpr int st = decltype(set_c)::value;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      wreg[st][j] = *reinterpret_cast<const u32x4_t*>(wp[j] + k0);
-      xreg[st][j].load(xp[j] + k0);
-    }
+    for (int j = 0; j < CW; ++j) wreg[st][j] = *reinterpret_cast<const u32x4_t*>(wp[j] + k0);
+#pragma unroll
+    for (int j = 0; j < CX; ++j) xreg[st][j].load(xp[j] + k0);
   };
   auto lstore = [&](auto set_c, int buf) {
     constexpr int st = decltype(set_c)::value;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = tid + 256 * j, off = (c >> 3) * kTPitch + 16 * (c & 7);
-      *reinterpret_cast<u32x4_t*>(&tiles[buf][0][off]) = wreg[st][j];
-      *reinterpret_cast<u32x4_t*>(&tiles[buf][1][off]) = xreg[st][j].bits();
+    for (int j = 0; j < CW; ++j) {
+      const int c = tid + 256 * j;
+      *reinterpret_cast<u32x4_t*>(&tiles[buf][(c >> 3) * kTPitch + 16 * (c & 7)]) = wreg[st][j];
+    }
+#pragma unroll
+    for (int j = 0; j < CX; ++j) {
+      const int c = tid + 256 * j;
+      *reinterpret_cast<u32x4_t*>(&tiles[buf][(TN + (c >> 3)) * kTPitch + 16 * (c & 7)]) =
+          xreg[st][j].bits();
     }
   };
   const int wn = wv & 1, wm = wv >> 1, r32 = lane & 31, h = lane >> 5;
   // operand of 32-row block i at k-step s: row 32i + r32 of the wave's half, k 16s + 8h
-  const int aoff = (64 * wn + r32) * kTPitch + 16 * h, boff = (64 * wm + r32) * kTPitch + 16 * h;
-  f32x16_t acc[2][2];
+  const int aoff = (32 * BN * wn + r32) * kTPitch + 16 * h;
+  const int boff = (TN + 32 * BM * wm + r32) * kTPitch + 16 * h;
+  f32x16_t acc[BN][BM];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < BN; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < BM; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
   auto multiply = [&](int buf) {
 #pragma unroll
     for (int s = 0; s < kTk / 16; ++s) {
-      bf16x8_t af[2], bf[2];
+      bf16x8_t af[BN], bf[BM];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        af[i] = *reinterpret_cast<const bf16x8_t*>(&tiles[buf][0][aoff + 32 * i * kTPitch + 32 * s]);
-        bf[i] = *reinterpret_cast<const bf16x8_t*>(&tiles[buf][1][boff + 32 * i * kTPitch + 32 * s]);
-      }
+      for (int i = 0; i < BN; ++i)
+        af[i] = *reinterpret_cast<const bf16x8_t*>(&tiles[buf][aoff + 32 * i * kTPitch + 32 * s]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < BM; ++j)
+        bf[j] = *reinterpret_cast<const bf16x8_t*>(&tiles[buf][boff + 32 * j * kTPitch + 32 * s]);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+      for (int i = 0; i < BN; ++i)
+#pragma unroll
+        for (int j = 0; j < BM; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
   };
@@ -544,26 +561,26 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile(GemmArgs a) {
     if (kb + 2 < nk) lstore(S0{}, 0);
     __syncthreads();
   }
-  // acc[i][j] element e of lane (r32, h): row 64wm + 32j + r32, column
-  // 64wn + 32i + 8(e >> 2) + 4h + (e & 3) of the tile.  The tile goes to LDS (the
+  // acc[i][j] element e of lane (r32, h): row 32 BM wm + 32j + r32, column
+  // 32 BN wn + 32i + 8(e >> 2) + 4h + (e & 3) of the tile.  The tile goes to LDS (the
   // operand buffers are free after the last barrier) and a compact loop applies the
   // epilogue to column pairs: unrolled over the accumulators, the epilogue's
   // registers made the compiler spill the accumulators on every K step.
-  constexpr int kOPitch = kTt + 4;   // floats per staged output row
-  static_assert(kTt * kOPitch * 4 <= static_cast<int>(sizeof(tiles)), "output tile fits the operand buffers");
-  float* ot = reinterpret_cast<float*>(&tiles[0][0][0]);
+  constexpr int kOPitch = TN + 4;   // floats per staged output row
+  static_assert(TM * kOPitch * 4 <= static_cast<int>(sizeof(tiles)), "output tile fits the operand buffers");
+  float* ot = reinterpret_cast<float*>(&tiles[0][0]);
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < BM; ++j)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < BN; ++i)
 #pragma unroll
       for (int e = 0; e < 16; e += 2)
-        *reinterpret_cast<float2*>(
-            &ot[(64 * wm + 32 * j + r32) * kOPitch + 64 * wn + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3)]) =
+        *reinterpret_cast<float2*>(&ot[(32 * BM * wm + 32 * j + r32) * kOPitch + 32 * BN * wn + 32 * i +
+                                       8 * (e >> 2) + 4 * h + (e & 3)]) =
             make_float2(acc[i][j][e], acc[i][j][e + 1]);
   __syncthreads();
-  for (int q = tid; q < kTt * kTt / 2; q += 256) {   // pair q: row q / 64, columns 2 (q % 64), +1
-    const int ml = q >> 6, nl = 2 * (q & 63);
+  for (int q = tid; q < TM * TN / 2; q += 256) {   // pair q: row q / (TN/2), columns 2 (q % (TN/2)), +1
+    const int ml = q / (TN / 2), nl = 2 * (q % (TN / 2));
     const int m = m0 + ml, n = n0 + nl;
     if (m < a.M && n < a.N) {
       const float2 v = *reinterpret_cast<const float2*>(&ot[ml * kOPitch + nl]);
@@ -723,10 +740,17 @@ static bool tile_ok(const GemmArgs& a) {
          a.n_split % 2 == 0 && groups >= 256;
 }
 
+// Per-head batched products at decode sizes (M <= 64, N a multiple of 64): one
+// 64 x 64 tile per workgroup, no K split, when that gives at least 256 workgroups.
+static bool small_tile_ok(const GemmArgs& a) {
+  return ws_ok(a) && a.epi == EPI_STORE && a.batch > 1 && a.M <= 64 && a.N % 64 == 0 &&
+         a.K % kTk == 0 && static_cast<int64_t>(a.N / 64) * a.batch >= 256;
+}
+
 bool fast_gemm_ok(const GemmArgs& a) { return ws_ok(a) || uk_ok(a); }
 
 size_t gemm_partial_bytes(const GemmArgs& a) {
-  if (!ws_ok(a) || tile_ok(a)) return 0;
+  if (!ws_ok(a) || tile_ok(a) || small_tile_ok(a)) return 0;
   if (xs_ok(a)) {
     const XsPlan q = xs_plan(a);
     return q.d > 1 ? static_cast<size_t>(q.d) * a.M * a.N * sizeof(float) : 0;
@@ -748,9 +772,17 @@ hipError_t launch_gemm_fast(const GemmArgs& a, void* partial, size_t partial_byt
   if (tile_ok(a)) {
     const dim3 grid((a.N + kTt - 1) / kTt, (a.M + kTt - 1) / kTt, a.batch);
     if (a.x_f32)
-      hipLaunchKernelGGL(k_gemm_tile<float>, grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((k_gemm_tile<float, kTt, kTt>), grid, dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL(k_gemm_tile<bf16_t>, grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((k_gemm_tile<bf16_t, kTt, kTt>), grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
+  if (small_tile_ok(a)) {
+    const dim3 grid(a.N / 64, 1, a.batch);
+    if (a.x_f32)
+      hipLaunchKernelGGL((k_gemm_tile<float, 64, 64>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_gemm_tile<bf16_t, 64, 64>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
   }
   if (xs_ok(a)) {

@@ -720,8 +720,10 @@ static bool uk_ok(const GemmArgs& a) {
 // wave of the grid strips to stream (narrow outputs, like the 576-wide latent
 // append, leave most waves idle there and go to k_gemm_ws): the X-stationary kernel.
 static bool xs_ok(const GemmArgs& a) {
+  // the fused append reads its two weights (w3, w4) with the same 16-byte loads
   if (a.epi == EPI_QPROJ_APPEND &&
-      !(a.n_append % 16 == 0 && a.n_split3 % 16 == 0 && a.n_split < a.n_append))
+      !(a.n_append % 16 == 0 && a.n_split3 % 16 == 0 && a.n_split < a.n_append &&
+        aligned16(a.w3) && aligned16(a.w4)))
     return false;
   return ws_ok(a) && a.batch == 1 && a.M <= 64 && a.N >= 2048 && a.N % 16 == 0 &&
          (a.n_split % 16 == 0 || a.n_split >= a.N) && a.K % (32 * kXsRing) == 0;

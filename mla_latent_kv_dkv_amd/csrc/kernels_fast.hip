@@ -593,9 +593,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto weight_sum = [&]() {
-    l_part += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])) +
-              (((p[8] + p[9]) + (p[10] + p[11])) + ((p[12] + p[13]) + (p[14] + p[15])));
+  // the normaliser sums the weights as rounded to bf16 for the P.C product, so the
+  // split's output is an exact convex combination of its rows (a dominant weight
+  // carries no rounding bias into the output)
+  auto weight_sum = [&](const bf16x8_t& a, const bf16x8_t& b) {
+    const u32x4_t ua = __builtin_bit_cast(u32x4_t, a), ub = __builtin_bit_cast(u32x4_t, b);
+    float v[16];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = __uint_as_float(ua[k] << 16);
+      v[2 * k + 1] = __uint_as_float(ua[k] & 0xFFFF0000u);
+      v[8 + 2 * k] = __uint_as_float(ub[k] << 16);
+      v[9 + 2 * k] = __uint_as_float(ub[k] & 0xFFFF0000u);
+    }
+    l_part += ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7])) +
+              (((v[8] + v[9]) + (v[10] + v[11])) + ((v[12] + v[13]) + (v[14] + v[15])));
   };
 
   for (int pass = 0; pass < 2; ++pass) {
@@ -627,9 +639,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
     mr = fmaxf(m_ref, -1e30f);
 #pragma unroll
     for (int i = 0; i < 16; ++i) weight(sc, i, mr);
-    weight_sum();
     pp0 = pack8(p);   // k = 16kk + 8(j >> 2) + 4g2 + (j & 3)
     pp1 = pack8(p + 8);
+    weight_sum(pp0, pp1);
     nv0 = nv1; nv1 = nv2;
     // ---- tile t: scores, then the products of tile t-1 with the weights of tile t between them
     for (int t = 1; t < ntiles; ++t) {
@@ -640,9 +652,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
       sc = scores(ring0 + (t & 3) * kTileBytes, [&] { if (more) nv2 = issue_pg(t + 2, pgv); });
       mask(sc, nv0);
       pv_product(ring0 + ((t - 1) & 3) * kTileBytes, pp0, pp1, true, sc, mr);
-      weight_sum();
       pp0 = pack8(p);
       pp1 = pack8(p + 8);
+      weight_sum(pp0, pp1);
       nv0 = nv1; nv1 = nv2;
     }
     pv_product(ring0 + ((ntiles - 1) & 3) * kTileBytes, pp0, pp1, false, sc, mr);
@@ -684,7 +696,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
 //           row scale 2^e_t is the hardware scale of A row t (E8M0 = the
 //           exponent field of the staged fp32 scale).  q is carried as two e4m3
 //           terms, q = 2^s_h (hi + lo), hi = RNE(q 2^-s_h), lo = RNE(q 2^-s_h - hi)
-//           (relative error <= 2^-8; bf16 has 2^-9), s_h putting the head's
+//           (relative error <= 2^-8, as for bf16), s_h putting the head's
 //           largest |q| in [128, 256).  Step st (64 latent columns): lane (r, g)
 //           holds columns 64st + 32g .. +31 of row r (two 16-byte chunks of the
 //           staged row), the queries laid out to match; one product with hi,

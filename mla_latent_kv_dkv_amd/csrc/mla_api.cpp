@@ -213,6 +213,10 @@ int64_t fp8_page_bytes(const mla_dims* d) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// fp32 stride of the appended rows in the workspace: d_c + d_R rounded up to a
+// multiple of 4, so every row starts 16-byte aligned for the quantizer's loads.
+int64_t rows_ld(const mla_dims* d) { return (static_cast<int64_t>(d->d_latent) + d->d_rope + 3) / 4 * 4; }
+
 // Projection of appended rows into fp32 [c | k^R] (k^R not yet rotated).
 mla::GemmArgs append_rows_args(const mla_dims* d, int n_rows) {
   mla::GemmArgs a{};
@@ -221,12 +225,12 @@ mla::GemmArgs append_rows_args(const mla_dims* d, int n_rows) {
   a.ldw_n = d->hidden; a.ldw_k = 1;
   a.M = n_rows; a.N = d->d_latent + d->d_rope; a.K = d->hidden; a.batch = 1;
   a.epi = mla::EPI_STORE; a.x_f32 = d->dtype != MLA_BF16; a.y_f32 = 1;
-  a.ldy = d->d_latent + d->d_rope;
+  a.ldy = rows_ld(d);
   return a;
 }
 
 size_t rows_bytes(const mla_dims* d, int n_rows) {
-  return align256(static_cast<size_t>(n_rows) * (d->d_latent + d->d_rope) * sizeof(float));
+  return align256(static_cast<size_t>(n_rows) * static_cast<size_t>(rows_ld(d)) * sizeof(float));
 }
 
 // Checks shared by the attention calls; fills `a` (pool format aside).  Decode
@@ -398,7 +402,18 @@ mla_status mla_absorb_q_append(const mla_dims* d, const void* h, const void* w_q
       !pool || !q_lat || !q_pe)
     return MLA_ERR_NULL;
   if (!ws || ws_bytes < mla_workspace_bytes(d, batch) || !ws_aligned(ws)) return MLA_ERR_WORKSPACE;
+  int* err = err_word();
+  if (!err) return MLA_ERR_HIP;
+  char* part = static_cast<char*>(ws) + act_bytes(d, batch);
+  const size_t pbytes = ws_bytes - act_bytes(d, batch);
+  // 1) [q^C | q^R | c^KV | k^R] = h [W_Q; W_QR; W_DKV; W_KR]^T: q^C -> workspace,
+  //    RoPE'd q^R -> q_pe, [c^KV | RoPE(k^R)] -> the rows' pool slots.  The
+  //    pointers are set before the shape check, which also tests their alignment.
   mla::GemmArgs a = qa_args(d, batch);
+  a.x = h; a.w1 = w_q; a.w2 = w_qr; a.w3 = w_dkv; a.w4 = w_kr;
+  a.y = ws; a.y2 = q_pe; a.y3 = pool; a.pos = pos; a.row_seq = row_seq;
+  a.block_table = block_table; a.n_seqs = n_seqs; a.max_pages = max_pages;
+  a.page_size = d->page_size; a.num_pages = num_pages; a.err = err;
   if (!(use_fast() && d->dtype == MLA_BF16 && mla::fused_qa_ok(a))) {
     // shapes the fused product does not take: the two calls one after the other
     st = mla_absorb_q(d, h, w_q, w_qr, w_uk, pos, batch, q_lat, q_pe, ws, ws_bytes, stream);
@@ -406,16 +421,6 @@ mla_status mla_absorb_q_append(const mla_dims* d, const void* h, const void* w_q
     return mla_append_latent(d, h, w_dkv, w_kr, row_seq, pos, batch, block_table, n_seqs,
                              max_pages, pool, num_pages, ws, ws_bytes, stream);
   }
-  int* err = err_word();
-  if (!err) return MLA_ERR_HIP;
-  char* part = static_cast<char*>(ws) + act_bytes(d, batch);
-  const size_t pbytes = ws_bytes - act_bytes(d, batch);
-  // 1) [q^C | q^R | c^KV | k^R] = h [W_Q; W_QR; W_DKV; W_KR]^T: q^C -> workspace,
-  //    RoPE'd q^R -> q_pe, [c^KV | RoPE(k^R)] -> the rows' pool slots
-  a.x = h; a.w1 = w_q; a.w2 = w_qr; a.w3 = w_dkv; a.w4 = w_kr;
-  a.y = ws; a.y2 = q_pe; a.y3 = pool; a.pos = pos; a.row_seq = row_seq;
-  a.block_table = block_table; a.n_seqs = n_seqs; a.max_pages = max_pages;
-  a.page_size = d->page_size; a.num_pages = num_pages; a.err = err;
   if (mla::launch_gemm_fast(a, part, pbytes, stream) != hipSuccess) return MLA_ERR_HIP;
   // 2) q_lat[b, i, :] = W_UK,i^T q^C[b, i, :] per head i
   mla::GemmArgs g = uk_args(d, batch);
@@ -545,7 +550,7 @@ mla_status mla_append_latent_fp8(const mla_dims* d, const void* h, const void* w
     return MLA_ERR_HIP;
   // 2) RoPE on k^R at row_pos, quantize, scatter into the pages
   mla::QuantArgs q{};
-  q.rows = rows; q.ld_rows = d->d_latent + d->d_rope; q.n_rows = n_rows;
+  q.rows = rows; q.ld_rows = rows_ld(d); q.n_rows = n_rows;
   q.d_latent = d->d_latent; q.d_rope = d->d_rope; q.rope = 1;
   q.log_base = std::log(static_cast<double>(d->rope_base));
   q.row_seq = row_seq; q.row_pos = row_pos; q.block_table = block_table;

@@ -41,15 +41,22 @@ def assert_parity(got, ref, dtype, what=""):
 
 
 def assert_partials_within_weight_rounding(got, ref, q_lat, q_pe, rows, length, num_splits,
-                                           page, tau, d_latent, what=""):
-    """Split partials of a bf16 MFMA path, element by element.  That path rounds
-    each softmax weight p_j to bf16 (relative error <= 2^-9) before the product
-    with the latent rows, while the normaliser sum_j p_j is kept in fp32, so
-    output element (i, k) of split s may be off by up to
-    2^-9 * sum_j p_j |c_jk| / sum_j p_j.  The bound taken is twice that (2^-8,
-    leaving room for the fp32 rounding of scores and sums) with the weighted mean
-    of |c| computed here from fp64 scores, plus 1e-6.  Queries must be exactly
-    representable in bf16.  A wrong row, scale or index lands far outside."""
+                                           page, tau, d_latent, what="", exact_normaliser=False):
+    """Split partials of an MFMA path, element by element.  The bf16-pool kernel
+    rounds each softmax weight p_j to bf16 (round to nearest even: relative error
+    at most 2^-8) before the product with the latent rows and normalises by the
+    sum of the rounded weights, so its output is sum_j p_j (1 + e_j) c_j /
+    sum_j p_j (1 + e_j) with |e_j| <= 2^-8; element (i, k) of split s is then off
+    from the exact average o_ik by at most
+    2^-8 * sum_j p_j |c_jk - o_ik| / ((1 - 2^-8) sum_j p_j).
+    With ``exact_normaliser`` (the FP8-pool kernel: weights carried as two e4m3
+    terms, relative error at most 2^-8, normalised by the sum of the exact
+    weights) the output is sum_j p_j (1 + e_j) c_j / sum_j p_j, off by at most
+    2^-8 * sum_j p_j |c_jk| / sum_j p_j.
+    The bound taken is that, with p_j and o_ik from fp64 scores computed here,
+    widened by 1% (and 1e-6 absolute) for the fp32 rounding of scores and sums.
+    Queries must be exactly representable in bf16.  A wrong row, scale or index
+    lands far outside."""
     import oracle as O
     rows = np.asarray(rows, np.float64)[:length]
     for s, (a, b) in enumerate(O.split_bounds(length, num_splits, page)):
@@ -58,7 +65,12 @@ def assert_partials_within_weight_rounding(got, ref, q_lat, q_pe, rows, length, 
         c = rows[a:b, :d_latent]
         sc = tau * (c @ q_lat.T + rows[a:b, d_latent:] @ q_pe.T)        # [tokens, heads]
         p = np.exp(sc - sc.max(axis=0))
-        bound = 2.0 ** -8 * (p.T @ np.abs(c)) / p.sum(axis=0)[:, None] + 1e-6
+        o = (p.T @ c) / p.sum(axis=0)[:, None]                           # [heads, d_c]
+        if exact_normaliser:
+            bound = 1.01 * 2.0 ** -8 * (p.T @ np.abs(c)) / p.sum(axis=0)[:, None] + 1e-6
+        else:
+            dev = np.stack([p[:, i] @ np.abs(c - o[i]) for i in range(p.shape[1])])
+            bound = 1.01 * 2.0 ** -8 * dev / ((1 - 2.0 ** -8) * p.sum(axis=0)[:, None]) + 1e-6
         err = np.abs(np.asarray(got[s], np.float64) - ref[s])
         worst = (err / bound).max()
         note(f"  o_part {what} split {s}: max err / bound {worst:.3f}")

@@ -124,6 +124,22 @@ def test_argument_checks():
                                0, None) == 0
     assert M.mla_workspace_bytes_cq(d, 24, 8) >= M.mla_workspace_bytes(d, 8) + 8 * 24 * 4
     assert M.mla_workspace_bytes_cq(d, 0, 8) == 0 and M.mla_workspace_bytes_cq(d, 5, 8) == 0
+    # fused query + append: (dims, h, w_q, w_qr, w_uk, w_dkv, w_kr, pos, row_seq, batch,
+    # table, n_seqs, max_pages, pool, num_pages, q_lat, q_pe, ws, ws_bytes, stream)
+    qa = lib.mla_absorb_q_append
+    big = 1 << 20
+    assert qa(ctypes.byref(d), P, P, P, P, None, P, P, P, 4, P, 1, 1, P, 1, P, P, P, big, None) == -1
+    assert qa(ctypes.byref(d), P, P, P, P, P, P, P, None, 4, P, 1, 1, P, 1, P, P, P, big, None) == -1
+    assert qa(ctypes.byref(d), P, P, P, P, P, P, P, P, 4, P, 1, 1, None, 1, P, P, P, big, None) == -1
+    assert qa(ctypes.byref(d), P, P, P, P, P, P, P, P, -2, P, 1, 1, P, 1, P, P, P, big, None) == -2
+    assert qa(ctypes.byref(d), P, P, P, P, P, P, P, P, 4, P, 0, 1, P, 1, P, P, P, big, None) == -2
+    assert qa(ctypes.byref(d), P, P, P, P, P, P, P, P, 4, P, 1, 0, P, 1, P, P, P, big, None) == -2
+    assert qa(ctypes.byref(d), P, P, P, P, P, P, P, P, 4, P, 1, 1, P, 0, P, P, P, big, None) == -2
+    assert qa(ctypes.byref(d), P, P, P, P, P, P, P, P, 4, P, 1, 1, P, 1, P, P, P, 16, None) == -4
+    assert qa(ctypes.byref(d), P, P, P, P, P, P, P, P, 4, P, 1, 1, P, 1, P, P, misaligned, big,
+              None) == -4
+    assert qa(ctypes.byref(d), None, None, None, None, None, None, None, None, 0, None, 0, 0, None,
+              0, None, None, None, 0, None) == 0
     # empty batches are no-ops that never touch the pointers
     assert lib.mla_absorb_q(ctypes.byref(d), None, None, None, None, None, 0, None, None, None, 0,
                             None) == 0

@@ -458,3 +458,88 @@ def test_absorb_q_append(name, B):
     assert (got[untouched] == -3.5).all(), "rows outside the appended slots changed"
     assert_parity(got[slots], ref_rows, w.dtype, "appended rows")
     assert M.mla_device_error() == 0
+
+
+@pytest.mark.parametrize("B", [5, 64])
+def test_absorb_q_append_out_of_range_rows(B):
+    """Rows whose table entry or sequence is out of range: nothing is written to
+    the pool, the error word says which, and their queries are still computed
+    (equal to mla_absorb_q's).  B = 5 goes through the K-split finish pass of the
+    fused product, B = 64 straight through its epilogue."""
+    w = _wl("full", batch=B)
+    lens = np.array([3 + 37 * b for b in range(B)], dtype=np.int32)
+    bt, total = I.page_table(w, lens)
+    seqs = np.arange(B, dtype=np.int32)
+    poss = (lens - 1).astype(np.int32)
+    bad_bt = bt.copy()
+    bad_bt[1, poss[1] // 64] = total + 3          # row 1: table entry outside the pool
+    seqs[3] = B + 9                               # row 3: sequence outside the table
+    note(f"absorb_q_append out-of-range rows B={B}")
+    sh = {n: w.weight_shape(n) for n in ("w_q", "w_qr", "w_uk", "w_dkv", "w_kr")}
+    std = {n: 1 / math.sqrt(w.fan_in(n)) for n in sh}
+    dev = {n: device_tensor(torch, w, n, sh[n], std[n]) for n in sh}
+    h = device_tensor(torch, w, "h_q", (B, w.hidden))
+    d = _dims(w)
+    ws = torch.empty(M.mla_workspace_bytes(d, B), dtype=torch.uint8, device="cuda")
+    q_lat = torch.empty((B, w.n_heads, w.d_latent), dtype=torch.float32, device="cuda")
+    q_pe = torch.empty((B, w.n_heads, w.d_rope), dtype=torch.float32, device="cuda")
+    pool = _sentinel_pool(w, total)
+    pos_t = torch.tensor(poss, device="cuda")
+    M.mla_device_error(clear=True)
+    M.mla_absorb_q_append(d, h, dev["w_q"], dev["w_qr"], dev["w_uk"], dev["w_dkv"], dev["w_kr"],
+                          pos_t, torch.tensor(seqs, device="cuda"),
+                          torch.tensor(bad_bt, device="cuda"), pool, q_lat, q_pe, ws)
+    err = M.mla_device_error(clear=True)
+    assert err & 1 and err & 4, err
+    q_lat2, q_pe2 = torch.empty_like(q_lat), torch.empty_like(q_pe)
+    M.mla_absorb_q(d, h, dev["w_q"], dev["w_qr"], dev["w_uk"], pos_t, q_lat2, q_pe2, ws)
+    assert torch.equal(q_lat, q_lat2) and torch.equal(q_pe, q_pe2)
+    got = to_np(pool).reshape(-1, w.row)
+    good = [b for b in range(B) if b not in (1, 3)]
+    slots = np.array([O.page_slot(bad_bt, seqs[b], poss[b], 64) for b in good])
+    untouched = np.ones(got.shape[0], bool)
+    untouched[slots] = False
+    assert (got[untouched] == -3.5).all(), "an out-of-range row was written"
+    hh = host_tensor(w, "h_q", (B, w.hidden))
+    hw = {n: host_tensor(w, n, sh[n], std[n]) for n in ("w_dkv", "w_kr")}
+    ref_rows = O.latent_rows(hh[good], hw["w_dkv"], hw["w_kr"], poss[good], w.rope_base)
+    assert_parity(got[slots], ref_rows, w.dtype, "appended rows")
+
+
+def test_absorb_q_append_misaligned_input_falls_back():
+    """h starting 2 bytes past a 16-byte boundary: the fused product cannot take it,
+    so the call makes the two calls in turn and gives their results."""
+    w = _wl("full", batch=8)
+    B = 8
+    lens = np.array([100 + 9 * b for b in range(B)], dtype=np.int32)
+    bt, total = I.page_table(w, lens)
+    poss = (lens - 1).astype(np.int32)
+    note("absorb_q_append misaligned h")
+    sh = {n: w.weight_shape(n) for n in ("w_q", "w_qr", "w_uk", "w_dkv", "w_kr")}
+    std = {n: 1 / math.sqrt(w.fan_in(n)) for n in sh}
+    dev = {n: device_tensor(torch, w, n, sh[n], std[n]) for n in sh}
+    h_al = device_tensor(torch, w, "h_q", (B, w.hidden))
+    flat = torch.empty(B * w.hidden + 1, dtype=h_al.dtype, device="cuda")
+    h = flat[1:].view(B, w.hidden)
+    h.copy_(h_al)
+    assert h.data_ptr() % 16 == 2 and h.is_contiguous()
+    d = _dims(w)
+    ws = torch.empty(M.mla_workspace_bytes(d, B), dtype=torch.uint8, device="cuda")
+    pos_t = torch.tensor(poss, device="cuda")
+    seq_t = torch.arange(B, dtype=torch.int32, device="cuda")
+    bt_t = torch.tensor(bt, device="cuda")
+    outs = []
+    for fused in (True, False):
+        q_lat = torch.empty((B, w.n_heads, w.d_latent), dtype=torch.float32, device="cuda")
+        q_pe = torch.empty((B, w.n_heads, w.d_rope), dtype=torch.float32, device="cuda")
+        pool = _sentinel_pool(w, total)
+        if fused:
+            M.mla_absorb_q_append(d, h, dev["w_q"], dev["w_qr"], dev["w_uk"], dev["w_dkv"],
+                                  dev["w_kr"], pos_t, seq_t, bt_t, pool, q_lat, q_pe, ws)
+        else:
+            M.mla_absorb_q(d, h, dev["w_q"], dev["w_qr"], dev["w_uk"], pos_t, q_lat, q_pe, ws)
+            M.mla_append_latent(d, h, dev["w_dkv"], dev["w_kr"], seq_t, pos_t, bt_t, pool)
+        outs.append((q_lat, q_pe, pool))
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)
+    assert M.mla_device_error() == 0

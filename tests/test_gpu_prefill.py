@@ -102,7 +102,7 @@ def test_prefill_attention(name, lens, page, S, queries, path, fp8):
             else:
                 assert_partials_within_weight_rounding(got_o[i], ref[k][0], hq[i], hp[i], rows,
                                                        int(qp[i]) + 1, S, page, tau, w.d_latent,
-                                                       what)
+                                                       what, exact_normaliser=fp8)
     assert M.mla_device_error() == 0
 
 

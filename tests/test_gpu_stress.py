@@ -1,0 +1,320 @@
+"""Stress and invariance cases of the attention calls against the fp64 oracle.
+
+* Peaky softmax: a row aligned with one head's query is planted in a later tile
+  of a split, so that head's score there exceeds the maximum of the split's
+  first tile by far more than the 64 log2 units the matrix-core kernels carry
+  above their per-head exponent reference (their re-run path), or by a little
+  less (the single-pass path at its edge).  The margins are confirmed on the
+  host from the oracle's own fp64 scores before anything runs.  The method is
+  a softmax over the sum of the content and RoPE scores ([Report] §2.4 of
+  "《DeepSeek-V2》深度解读报告"), so nothing bounds how far one score may stand
+  above the others.
+* Queries in fp32 as the absorbed-query call produces them (not values exact in
+  bf16), judged after the log-sum-exp merge.
+* Determinism: the same call twice gives bit-identical outputs.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import mla_latent_kv_dkv_amd as M
+import oracle as O
+from mla_latent_kv_dkv_amd import inputs as I
+from mla_latent_kv_dkv_amd.harness import DeviceWorkload
+from tests.gpu_util import (assert_parity, assert_partials_within_weight_rounding, host_tensor,
+                            device_tensor, note, to_np)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+LN2 = math.log(2.0)
+TILE = 32          # tokens per tile of the matrix-core kernels (first tile = reference)
+HEADROOM = 64.0    # log2 units carried above the reference before a unit runs again
+
+
+@pytest.fixture(autouse=True)
+def _path_reset():
+    M.load()
+    yield
+    M.mla_set_kernel_path(0)
+
+
+def _wl(name, **kw):
+    fields = dict(I.WORKLOADS[name].__dict__)
+    fields.update(kw)
+    return I.Workload(**fields)
+
+
+def _dims(w):
+    return M.make_dims(w.hidden, w.n_heads, w.d_head, w.d_latent, w.d_rope, w.dtype, w.page_size,
+                       w.rope_base)
+
+
+def _fp8_rows(rows, d_c):
+    return np.stack([O.fp8_dequantize_row(*O.fp8_quantize_row(r, d_c)) for r in rows])
+
+
+def _bf16(x):
+    return I.bf16_bits_to_f64(I.f32_to_bf16_bits(np.asarray(x, np.float32)))
+
+
+def _excess_log2(q_lat, q_pe, rows, bounds, tau, d_c):
+    """Per (split, head): (max score over the split - max over its first tile) in
+    log2 units, from fp64 scores; -inf for empty splits."""
+    out = np.full((len(bounds), q_lat.shape[0]), -np.inf)
+    for s, (a, b) in enumerate(bounds):
+        if a >= b:
+            continue
+        sc = tau * (rows[a:b, :d_c] @ q_lat.T + rows[a:b, d_c:] @ q_pe.T)
+        out[s] = (sc.max(axis=0) - sc[:TILE].max(axis=0)) / LN2
+    return out
+
+
+def _plant(rows, spikes, q_lat, q_pe, bounds, tau, d_c, margin, quantize):
+    """Rows with, for each (token j, head i) in ``spikes``, row j replaced by
+    beta * sign(q_lat,i) (k^R = 0) with beta chosen so that head i's score at j
+    stands ``margin`` log2 units above the maximum of the first tile of j's
+    split.  ``quantize`` maps rows to what the pool holds (bf16 or FP8)."""
+    rows = rows.copy()
+    for j, i in spikes:
+        a = next(a for a, b in bounds if a <= j < b)
+        assert j >= a + 2 * TILE, "the spike must sit in a later tile of its split"
+        held = quantize(rows[a:a + TILE])
+        m0 = (tau * (held[:, :d_c] @ q_lat[i] + held[:, d_c:] @ q_pe[i])).max()
+        sgn = np.where(q_lat[i] >= 0, 1.0, -1.0)
+        beta = (m0 + margin * LN2) / (tau * np.abs(q_lat[i]).sum())
+        rows[j, :d_c] = beta * sgn
+        rows[j, d_c:] = 0.0
+        rows[j] = quantize(rows[j:j + 1])[0]     # the value the pool will hold
+    return rows
+
+
+# (pool, workload, lens, S, spikes per sequence [(token, head)], margin in log2 units)
+PEAKY = [
+    ("bf16", "full", (1000, 700), 2, [[(300, 5), (900, 77), (995, 100)], [(650, 31)]], 90.0),
+    ("bf16", "full", (1000, 700), 2, [[(300, 5), (900, 77), (995, 100)], [(650, 31)]], 56.0),
+    ("fp8", "full-fp8", (1000, 700), 2, [[(300, 5), (900, 77), (995, 100)], [(650, 31)]], 90.0),
+    ("fp8", "full-fp8", (1000, 700), 2, [[(300, 5), (900, 77), (995, 100)], [(650, 31)]], 56.0),
+]
+
+
+def _peaky_inputs(pool_kind, name, lens, S, spikes, margin, prefill_pos=None):
+    w = _wl(name, batch=len(lens))
+    d = _dims(w)
+    tau = M.default_scale(d)
+    dc, row = w.d_latent, w.row
+    lens = np.array(lens, dtype=np.int32)
+    bt, total = I.page_table(w, lens)
+    B, nh = len(lens), w.n_heads
+    hq = host_tensor(w, "q_lat_in", (B, nh, dc), 0.5)
+    hp = host_tensor(w, "q_pe_in", (B, nh, w.d_rope), 1.0)
+    if pool_kind == "fp8":
+        quant = lambda r: _fp8_rows(r.astype(np.float32), dc)
+        src = I.normal_f32(I.stream_key(w.seed, "pool"), 0, total * 64 * row).astype(
+            np.float64).reshape(total * 64, row)
+    else:
+        quant = lambda r: _bf16(r)
+        src = I.to_f64(w, I.tensor_values(w, "pool", (total * 64, row)))
+    held_rows = []
+    for b in range(B):
+        pos = np.arange(int(lens[b]))
+        phys = bt[b, pos // 64].astype(np.int64) * 64 + pos % 64
+        bounds = O.split_bounds(int(lens[b]), S, 64)
+        planted = _plant(src[phys], spikes[b], hq[b], hp[b], bounds, tau, dc, margin, quant)
+        src[phys] = planted
+        held_rows.append(quant(planted))
+    # the margins the kernels will see, from the oracle's fp64 scores of the held rows
+    for b in range(B):
+        bounds = O.split_bounds(int(lens[b]), S, 64)
+        ex = _excess_log2(hq[b], hp[b], held_rows[b], bounds, tau, dc)
+        for j, i in spikes[b]:
+            s = next(k for k, (a, e) in enumerate(bounds) if a <= j < e)
+            note(f"  seq {b} head {i} split {s}: excess {ex[s, i]:.1f} log2 units")
+            if margin > HEADROOM:
+                assert ex[s, i] > HEADROOM + 10, "planted spike does not cross the headroom"
+        if margin < HEADROOM:
+            assert np.nanmax(ex) < HEADROOM - 2, "a score crosses the headroom in the under case"
+            assert np.nanmax(ex) > HEADROOM - 16, "the under case is not near the headroom"
+    dev_src = torch.tensor(src.astype(np.float32), device="cuda")
+    if pool_kind == "fp8":
+        pool = torch.empty((total, M.mla_fp8_page_bytes(d)), dtype=torch.uint8, device="cuda")
+        phys = torch.arange(total * 64, dtype=torch.int32, device="cuda")
+        M.mla_quantize_rows_fp8(d, dev_src, (phys // 64).contiguous(), (phys % 64).contiguous(),
+                                torch.arange(total, dtype=torch.int32, device="cuda").reshape(-1, 1),
+                                pool)
+    else:
+        pool = dev_src.to(torch.bfloat16).reshape(total, 64, row).contiguous()
+    q_lat = device_tensor(torch, w, "q_lat_in", (B, nh, dc), 0.5).float().contiguous()
+    q_pe = device_tensor(torch, w, "q_pe_in", (B, nh, w.d_rope), 1.0).float().contiguous()
+    return w, d, tau, lens, bt, pool, q_lat, q_pe, hq, hp, held_rows
+
+
+@pytest.mark.parametrize("pool_kind,name,lens,S,spikes,margin", PEAKY)
+@pytest.mark.parametrize("path", [0, 1])
+def test_decode_attention_peaky_softmax(pool_kind, name, lens, S, spikes, margin, path):
+    M.mla_set_kernel_path(path)
+    note(f"peaky attention {pool_kind} lens={list(lens)} S={S} margin={margin} path={path}")
+    w, d, tau, lens, bt, pool, q_lat, q_pe, hq, hp, rows = _peaky_inputs(pool_kind, name, lens, S,
+                                                                         spikes, margin)
+    B, nh = len(lens), w.n_heads
+    o_part = torch.full((B, S, nh, w.d_latent), 123.0, device="cuda")
+    lse_part = torch.full((B, S, nh), 123.0, device="cuda")
+    attend = M.mla_decode_attention_fp8 if pool_kind == "fp8" else M.mla_decode_attention
+    attend(d, q_lat, q_pe, pool, torch.tensor(bt, device="cuda"), torch.tensor(lens, device="cuda"),
+           o_part, lse_part)
+    o_lat = torch.empty((B, nh, w.d_latent), device="cuda")
+    lse = torch.empty((B, nh), device="cuda")
+    M.mla_merge_lse(d, o_part, lse_part, o_lat, lse)
+    got_o, got_l, got_m, got_ml = to_np(o_part), to_np(lse_part), to_np(o_lat), to_np(lse)
+    for b in range(B):
+        L = int(lens[b])
+        ro, rl = O.attention_partials(hq[b], hp[b], rows[b], S, w.d_latent, w.d_rope, tau, 64)
+        assert_parity(got_l[b], rl, w.dtype, f"lse_part b={b}")
+        if pool_kind == "bf16":
+            assert_partials_within_weight_rounding(got_o[b], ro, hq[b], hp[b], rows[b], L, S, 64,
+                                                   tau, w.d_latent, f"b={b}")
+        else:
+            assert_parity(got_o[b], ro, w.dtype, f"o_part b={b}")
+        # every spiked head on its own: its output is (nearly) the planted row
+        for j, i in spikes[b]:
+            s = next(k for k, (a, e) in enumerate(O.split_bounds(L, S, 64)) if a <= j < e)
+            assert_parity(got_o[b, s, i], ro[s, i], w.dtype, f"o_part b={b} head {i} split {s}")
+        rm, rml = O.merge_lse(ro, rl)
+        assert_parity(got_m[b], rm, w.dtype, f"o_lat b={b}")
+        assert_parity(got_ml[b], rml, w.dtype, f"lse b={b}")
+    assert M.mla_device_error() == 0
+
+
+@pytest.mark.parametrize("pool_kind,margin", [("bf16", 90.0), ("bf16", 56.0), ("fp8", 90.0)])
+def test_prefill_attention_peaky_softmax(pool_kind, margin):
+    """Prefill units: the query at the last position sees the spike in a later
+    tile; one just before the spike does not."""
+    name = "full" if pool_kind == "bf16" else "full-fp8"
+    spikes = [[(400, 9), (700, 120)]]
+    note(f"peaky prefill {pool_kind} margin={margin}")
+    w, d, tau, lens, bt, pool, q_lat1, q_pe1, hq1, hp1, rows = _peaky_inputs(
+        pool_kind, name, (760,), 1, spikes, margin)
+    qpos = np.array([759, 699, 420, 399], dtype=np.int32)
+    nq, nh = len(qpos), w.n_heads
+    hq = np.repeat(hq1, nq, axis=0)
+    hp = np.repeat(hp1, nq, axis=0)
+    q_lat = q_lat1.repeat(nq, 1, 1).contiguous()
+    q_pe = q_pe1.repeat(nq, 1, 1).contiguous()
+    o_part = torch.full((nq, 1, nh, w.d_latent), 123.0, device="cuda")
+    lse_part = torch.full((nq, 1, nh), 123.0, device="cuda")
+    M.mla_prefill_attention(d, q_lat, q_pe, pool, torch.tensor(bt, device="cuda"),
+                            torch.zeros(nq, dtype=torch.int32, device="cuda"),
+                            torch.tensor(qpos, device="cuda"), o_part, lse_part,
+                            fp8=pool_kind == "fp8")
+    ref = O.prefill_attention_partials(hq, hp, rows[0], qpos, 1, w.d_latent, w.d_rope, tau, 64)
+    got_o, got_l = to_np(o_part), to_np(lse_part)
+    for k in range(nq):
+        assert_parity(got_o[k], ref[k][0], w.dtype, f"o_part q_pos={qpos[k]}")
+        assert_parity(got_l[k], ref[k][1], w.dtype, f"lse_part q_pos={qpos[k]}")
+        for j, i in spikes[0]:
+            assert_parity(got_o[k, 0, i], ref[k][0][0, i], w.dtype,
+                          f"o_part q_pos={qpos[k]} head {i}")
+    assert M.mla_device_error() == 0
+
+
+# ------------------------------------------------ fp32 queries, merged --
+FP32Q = [
+    ("full", (1, 65, 1000, 4096), 4),
+    ("full", (3000, 130), 8),
+    ("full", (4096,) * 3, 4),
+    ("lite", (64, 777, 4096), 2),
+    ("full-fp8", (1, 65, 1000, 4096), 4),
+]
+
+
+@pytest.mark.parametrize("name,lens,S", FP32Q)
+def test_attention_fp32_queries_merged(name, lens, S):
+    """Queries as mla_absorb_q hands them over (fp32, not exact in bf16; the
+    matrix-core kernels round them once per work unit), judged after the merge:
+    o_lat and lse at the 2e-2 x RMS bar per sequence."""
+    fp8 = name.endswith("fp8")
+    w = _wl(name, batch=len(lens))
+    d = _dims(w)
+    tau = M.default_scale(d)
+    lens = np.array(lens, dtype=np.int32)
+    bt, total = I.page_table(w, lens)
+    B, nh, dc = len(lens), w.n_heads, w.d_latent
+    note(f"fp32 queries {name} lens={lens.tolist()} S={S}")
+    q_lat = device_tensor(torch, w, "q_lat_f32", (B, nh, dc), 0.5, dtype=torch.float32)
+    q_pe = device_tensor(torch, w, "q_pe_f32", (B, nh, w.d_rope), 1.0, dtype=torch.float32)
+    hq = I.normal_f32(I.stream_key(w.seed, "q_lat_f32"), 0, B * nh * dc, 0.5).astype(
+        np.float64).reshape(B, nh, dc)
+    hp = I.normal_f32(I.stream_key(w.seed, "q_pe_f32"), 0, B * nh * w.d_rope, 1.0).astype(
+        np.float64).reshape(B, nh, w.d_rope)
+    assert not np.array_equal(_bf16(hq), hq), "queries must not be exact in bf16"
+    if fp8:
+        from mla_latent_kv_dkv_amd.harness import fill_fp8_pool
+        pool = torch.empty((total, M.mla_fp8_page_bytes(d)), dtype=torch.uint8, device="cuda")
+        fill_fp8_pool(d, pool, I.stream_key(w.seed, "pool"))
+    else:
+        pool = device_tensor(torch, w, "pool", (total, 64, w.row))
+    o_part = torch.empty((B, S, nh, dc), device="cuda")
+    lse_part = torch.empty((B, S, nh), device="cuda")
+    attend = M.mla_decode_attention_fp8 if fp8 else M.mla_decode_attention
+    attend(d, q_lat, q_pe, pool, torch.tensor(bt, device="cuda"), torch.tensor(lens, device="cuda"),
+           o_part, lse_part)
+    o_lat = torch.empty((B, nh, dc), device="cuda")
+    lse = torch.empty((B, nh), device="cuda")
+    M.mla_merge_lse(d, o_part, lse_part, o_lat, lse)
+    got_m, got_ml = to_np(o_lat), to_np(lse)
+    for b in range(B):
+        L = int(lens[b])
+        if fp8:
+            rows = _fp8_rows(I.pool_rows(w, bt, b, L, f32=True), dc)
+        else:
+            rows = I.to_f64(w, I.pool_rows(w, bt, b, L))
+        ro, rl = O.attention_partials(hq[b], hp[b], rows, S, dc, w.d_rope, tau, 64)
+        rm, rml = O.merge_lse(ro, rl)
+        assert_parity(got_m[b], rm, w.dtype, f"o_lat b={b} L={L}")
+        assert_parity(got_ml[b], rml, w.dtype, f"lse b={b} L={L}")
+    assert M.mla_device_error() == 0
+
+
+# --------------------------------------------------------- determinism --
+@pytest.mark.parametrize("fp8", [False, True])
+def test_attention_twice_is_bit_identical(fp8):
+    w = _wl("full-fp8" if fp8 else "full", batch=3)
+    d = _dims(w)
+    lens = np.array([4096, 1000, 77], dtype=np.int32)
+    bt, total = I.page_table(w, lens)
+    nh, dc = w.n_heads, w.d_latent
+    note(f"attention twice fp8={fp8}")
+    q_lat = device_tensor(torch, w, "q_lat_f32", (3, nh, dc), 0.5, dtype=torch.float32)
+    q_pe = device_tensor(torch, w, "q_pe_f32", (3, nh, w.d_rope), 1.0, dtype=torch.float32)
+    if fp8:
+        from mla_latent_kv_dkv_amd.harness import fill_fp8_pool
+        pool = torch.empty((total, M.mla_fp8_page_bytes(d)), dtype=torch.uint8, device="cuda")
+        fill_fp8_pool(d, pool, I.stream_key(w.seed, "pool"))
+    else:
+        pool = device_tensor(torch, w, "pool", (total, 64, w.row))
+    attend = M.mla_decode_attention_fp8 if fp8 else M.mla_decode_attention
+    outs = []
+    for _ in range(2):
+        o = torch.full((3, 4, nh, dc), 7.0, device="cuda")
+        l = torch.full((3, 4, nh), 7.0, device="cuda")
+        attend(d, q_lat, q_pe, pool, torch.tensor(bt, device="cuda"),
+               torch.tensor(lens, device="cuda"), o, l)
+        outs.append((o.cpu(), l.cpu()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_step_twice_is_bit_identical():
+    """The whole decode step (full shape) run twice on the same inputs; the
+    append writes the same row again, so the second step sees the same cache."""
+    note("step twice full")
+    dw = DeviceWorkload(I.WORKLOADS["full"])
+    outs = []
+    for _ in range(2):
+        dw.step()
+        torch.cuda.synchronize()
+        outs.append({k: getattr(dw, k).clone() for k in ("u", "q_lat", "o_lat", "lse")})
+    for k in outs[0]:
+        assert torch.equal(outs[0][k], outs[1][k]), f"{k} differs between two identical steps"
+    assert M.mla_device_error() == 0

@@ -200,6 +200,26 @@ mla_status mla_absorb_out(const mla_dims* dims, const float* o_lat, const void* 
                           size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * mla_absorb_out for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same operation and arguments without the workspace.  Its scratch (the
+ * per-head products o, then the fp32 partial sums of the projection) is a
+ * static device array of mla_absorb_out_noalloc_max_bytes() bytes (32 MiB)
+ * inside the library, one per device, allocated when the library's code is
+ * loaded on that device and held until the process ends; no call allocates,
+ * frees or synchronises.  A call whose scratch need (the part of
+ * mla_workspace_bytes that mla_absorb_out uses: at the full shape H = 5120,
+ * n_h = d_h = 128, bf16, about 23 MiB at batch 64) exceeds that returns
+ * MLA_ERR_WORKSPACE and enqueues nothing.  Every call on one device shares the
+ * one array: calls that may overlap on a device (two streams, two threads)
+ * race and must be ordered by the caller.  Results equal mla_absorb_out's.
+ */
+mla_status mla_absorb_out_noalloc(const mla_dims* dims, const float* o_lat, const void* w_uv,
+                                  const void* w_o, int32_t batch, float* u, hipStream_t stream);
+/* Bytes of the static scratch array of mla_absorb_out_noalloc. */
+size_t mla_absorb_out_noalloc_max_bytes(void);
+
+/*
  * Absorbed query with the query's low-rank compression (the MLA information
  * flow of [Report] §3.1: h -> W_D^Q -> c^Q (d_c' = 1536 there) -> q^C, while the
  * RoPE query q^R is still taken from h).  For each sequence b:

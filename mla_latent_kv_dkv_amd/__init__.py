@@ -24,7 +24,8 @@ __all__ = ["MlaDims", "MlaError", "make_dims", "load", "mla_append_latent", "mla
            "mla_append_workspace_bytes", "mla_device_error", "mla_set_kernel_path",
            "mla_status_string", "mla_fp8_page_bytes", "mla_quantize_rows_fp8",
            "mla_append_latent_fp8", "mla_append_workspace_bytes_fp8", "mla_decode_attention_fp8",
-           "mla_prefill_attention", "mla_prefill_attention_fp8", "LIB_PATH"]
+           "mla_prefill_attention", "mla_prefill_attention_fp8", "mla_absorb_out_noalloc",
+           "mla_absorb_out_noalloc_max_bytes", "LIB_PATH"]
 
 
 class MlaDims(ctypes.Structure):
@@ -61,6 +62,8 @@ _SIGS = {
     "mla_decode_attention": [_DIMS, _P, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _P, _P, _P],
     "mla_merge_lse": [_DIMS, _P, _P, _I32, _I32, _P, _P, _P],
     "mla_absorb_out": [_DIMS, _P, _P, _P, _I32, _P, _P, _SZ, _P],
+    "mla_absorb_out_noalloc": [_DIMS, _P, _P, _P, _I32, _P, _P],
+    "mla_absorb_out_noalloc_max_bytes": [],
     "mla_workspace_bytes": [_DIMS, _I32],
     "mla_workspace_bytes_cq": [_DIMS, _I32, _I32],
     "mla_append_workspace_bytes": [_DIMS, _I32],
@@ -80,6 +83,7 @@ _SIGS = {
 }
 _RES = {"mla_workspace_bytes": _SZ, "mla_workspace_bytes_cq": _SZ, "mla_append_workspace_bytes": _SZ,
         "mla_fp8_page_bytes": _SZ, "mla_append_workspace_bytes_fp8": _SZ,
+        "mla_absorb_out_noalloc_max_bytes": _SZ,
         "mla_status_string": ctypes.c_char_p}
 
 
@@ -290,6 +294,23 @@ def mla_absorb_out(dims, o_lat, w_uv, w_o, u, workspace, stream=None):
     _check("mla_absorb_out", load().mla_absorb_out(
         ctypes.byref(dims), _ptr(o_lat), _ptr(w_uv), _ptr(w_o), B, _ptr(u), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def mla_absorb_out_noalloc(dims, o_lat, w_uv, w_o, u, stream=None):
+    """mla_absorb_out with the library's static scratch instead of a workspace
+    (nothing is allocated; calls overlapping on one device race)."""
+    import torch
+    B, nh, e = o_lat.shape[0], dims.n_heads, _elem(dims)
+    _expect(o_lat, (B, nh, dims.d_latent), torch.float32, "o_lat")
+    _expect(w_uv, (nh * dims.d_head, dims.d_latent), e, "w_uv")
+    _expect(w_o, (dims.hidden, nh * dims.d_head), e, "w_o")
+    _expect(u, (B, dims.hidden), torch.float32, "u")
+    _check("mla_absorb_out_noalloc", load().mla_absorb_out_noalloc(
+        ctypes.byref(dims), _ptr(o_lat), _ptr(w_uv), _ptr(w_o), B, _ptr(u), _stream(stream)))
+
+
+def mla_absorb_out_noalloc_max_bytes() -> int:
+    return int(load().mla_absorb_out_noalloc_max_bytes())
 
 
 # ------------------------------------------------------------- FP8 pool --

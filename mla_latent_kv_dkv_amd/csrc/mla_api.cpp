@@ -33,6 +33,29 @@ int* err_word() {
   return g_err_ptr[dev];
 }
 
+// Scratch of mla_absorb_out_noalloc: one array per device, held for the life of
+// the process.  In host code `scratch` names a host-side stand-in, never the
+// device memory: every host use goes through the address hipGetSymbolAddress
+// returns for the current device, cached per device below.
+constexpr size_t kScratchBytes = size_t{32} << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+void* g_scratch_ptr[kMaxDevices] = {};
+std::atomic<int> g_scratch_ready[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up once per device),
+// or nullptr when the runtime cannot say.
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  if (!g_scratch_ready[dev].load(std::memory_order_acquire)) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    g_scratch_ptr[dev] = p;
+    g_scratch_ready[dev].store(1, std::memory_order_release);
+  }
+  return g_scratch_ptr[dev];
+}
+
 bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 
 mla_status check_dims(const mla_dims* d) {
@@ -274,6 +297,29 @@ hipError_t launch_attention_f8(const mla_dims* d, const mla::AttnArgs& a, hipStr
   if (use_fast() && d->dtype == MLA_BF16 && mla::fast_attention_ok(a))
     return mla::launch_attention_fp8(a, stream);
   return mla::launch_attention_generic_fp8(a, stream);
+}
+
+// Bytes mla_absorb_out uses of its workspace: o in dtype, then the fp32 K-split
+// partial sums of the larger of its two products.
+size_t absorb_out_bytes(const mla_dims* d, int batch) {
+  return act_bytes(d, batch) + std::max(partial_bytes(d, uv_args(d, batch)),
+                                        partial_bytes(d, oproj_args(d, batch)));
+}
+
+// The two products of the absorbed output with `ws` (256-byte aligned, at least
+// absorb_out_bytes) as their scratch.
+mla_status absorb_out_run(const mla_dims* d, const float* o_lat, const void* w_uv, const void* w_o,
+                          int32_t batch, float* u, void* ws, size_t ws_bytes, hipStream_t stream) {
+  char* part = static_cast<char*>(ws) + act_bytes(d, batch);
+  const size_t pbytes = ws_bytes - act_bytes(d, batch);
+  // 1) o[b, i*d_h + e] = sum_c W_UV[i*d_h + e, c] o_lat[b, i, c] per head i -> workspace
+  mla::GemmArgs g = uv_args(d, batch);
+  g.x = o_lat; g.w1 = w_uv; g.w2 = w_uv; g.y = ws;
+  if (run_gemm(d, g, part, pbytes, stream) != hipSuccess) return MLA_ERR_HIP;
+  // 2) u = o W_O^T
+  mla::GemmArgs a = oproj_args(d, batch);
+  a.x = ws; a.w1 = w_o; a.w2 = w_o; a.y = u;
+  return hip_status(run_gemm(d, a, part, pbytes, stream));
 }
 
 }  // namespace
@@ -617,16 +663,22 @@ mla_status mla_absorb_out(const mla_dims* d, const float* o_lat, const void* w_u
   if (batch == 0) return MLA_OK;
   if (!o_lat || !w_uv || !w_o || !u) return MLA_ERR_NULL;
   if (!ws || ws_bytes < mla_workspace_bytes(d, batch) || !ws_aligned(ws)) return MLA_ERR_WORKSPACE;
-  char* part = static_cast<char*>(ws) + act_bytes(d, batch);
-  const size_t pbytes = ws_bytes - act_bytes(d, batch);
-  // 1) o[b, i*d_h + e] = sum_c W_UV[i*d_h + e, c] o_lat[b, i, c] per head i -> workspace
-  mla::GemmArgs g = uv_args(d, batch);
-  g.x = o_lat; g.w1 = w_uv; g.w2 = w_uv; g.y = ws;
-  if (run_gemm(d, g, part, pbytes, stream) != hipSuccess) return MLA_ERR_HIP;
-  // 2) u = o W_O^T
-  mla::GemmArgs a = oproj_args(d, batch);
-  a.x = ws; a.w1 = w_o; a.w2 = w_o; a.y = u;
-  return hip_status(run_gemm(d, a, part, pbytes, stream));
+  return absorb_out_run(d, o_lat, w_uv, w_o, batch, u, ws, ws_bytes, stream);
 }
 
+size_t mla_absorb_out_noalloc_max_bytes(void) { return kScratchBytes; }
+
+mla_status mla_absorb_out_noalloc(const mla_dims* d, const float* o_lat, const void* w_uv,
+                                  const void* w_o, int32_t batch, float* u, hipStream_t stream) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || batch > (1 << 20)) return MLA_ERR_SHAPE;
+  if (batch == 0) return MLA_OK;
+  if (!o_lat || !w_uv || !w_o || !u) return MLA_ERR_NULL;
+  const size_t need = absorb_out_bytes(d, batch);
+  if (need > kScratchBytes) return MLA_ERR_WORKSPACE;
+  void* ws = scratch_address();
+  if (!ws) return MLA_ERR_HIP;
+  return absorb_out_run(d, o_lat, w_uv, w_o, batch, u, ws, kScratchBytes, stream);
+}
 }  // extern "C"

@@ -24,7 +24,8 @@ two must agree to rounding (associativity), which is one of the pins.
 Readings taken where the pages are silent (all inline formulas were lost):
   * softmax scale tau = 1/sqrt(d_h + d_R) unless the caller passes one;
   * RoPE rotates adjacent pairs (x[2k], x[2k+1]) by angle pos*theta_k with
-    theta_k = base**(-2k/d_R); angles in fp64;
+    theta_k = base**(-2k/d_R); angles in fp64; YaRN ([Report] §3.3 gives only
+    its parameters) follows the published method (:class:`Yarn`);
   * decode position t = L-1: the new token is appended first and attends to
     positions 0..L-1 inclusive;
   * q^C = W_Q h, or with the query's low-rank compression c^Q = W_DQ h and
@@ -46,7 +47,7 @@ import math
 import numpy as np
 
 __all__ = [
-    "rope_theta", "rope", "latent_rows", "page_slot", "query_heads", "compressed_query",
+    "Yarn", "yarn_logit_factor", "rope_theta", "rope", "latent_rows", "page_slot", "query_heads", "compressed_query",
     "query_heads_cq",
     "mla_decode_step", "mla_decode_step_absorbed", "split_bounds",
     "attention_partials", "merge_lse", "absorb_q", "absorb_out",
@@ -62,11 +63,55 @@ def _f64(x):
 
 
 # ---------------------------------------------------------------- positions --
-def rope_theta(d_rope: int, base: float) -> np.ndarray:
+class Yarn:
+    """RoPE stretched by YaRN, the long-context extension [Report] §3.3 (its
+    long-context paragraph) names for DeepSeek-V2: the window is taken from 4K to
+    128K with scale 40, alpha = 1, beta = 32.  The pages give only those
+    numbers; the method followed is the published one (Peng, Quesnelle, Fan and
+    Shippole, "YaRN: Efficient Context Window Extension of Large Language Models",
+    2023), with ``orig_len`` the context the frequencies were trained for:
+
+      * pair k rotates r_k = orig_len / lambda_k times over the original window,
+        lambda_k = 2 pi / theta_k its wavelength;
+      * ramp gamma_k = 0 for r_k < alpha, 1 for r_k > beta, linear in between;
+      * theta'_k = (1 - gamma_k) theta_k / scale + gamma_k theta_k: pairs that turn
+        fewer than alpha times are interpolated by the scale, pairs that turn
+        more than beta times keep their frequency;
+      * the logits are multiplied by 1/t with sqrt(1/t) = 0.1 ln(scale) + 1
+        (the method's temperature; here on the whole score, content plus RoPE
+        channel, since [Report] §2.4 puts both under one softmax).
+
+    A scale <= 1 is plain RoPE.  Passed wherever a RoPE ``base`` is taken."""
+
+    def __init__(self, base: float, scale: float, orig_len: int, alpha: float, beta: float):
+        self.base, self.scale, self.orig_len = float(base), float(scale), int(orig_len)
+        self.alpha, self.beta = float(alpha), float(beta)
+
+
+def _base_of(base):
+    return base.base if isinstance(base, Yarn) else float(base)
+
+
+def yarn_logit_factor(base) -> float:
+    """1/t of YaRN's temperature, (0.1 ln s + 1)^2, for a :class:`Yarn` base with
+    s > 1; 1 for plain RoPE."""
+    if isinstance(base, Yarn) and base.scale > 1.0:
+        return (0.1 * math.log(base.scale) + 1.0) ** 2
+    return 1.0
+
+
+def rope_theta(d_rope: int, base) -> np.ndarray:
     """theta_k = base**(-2k/d_R), k = 0..d_R/2-1 ([Report] §2.4: RoPE acts only on
-    the decoupled d_R-wide branch; base 10000 per the workload definitions)."""
+    the decoupled d_R-wide branch; base 10000 per the workload definitions), or
+    the YaRN-stretched frequencies for a :class:`Yarn` base."""
     k = np.arange(d_rope // 2, dtype=np.float64)
-    return np.power(float(base), -2.0 * k / d_rope)
+    theta = np.power(_base_of(base), -2.0 * k / d_rope)
+    if not isinstance(base, Yarn) or base.scale <= 1.0:
+        return theta
+    wavelength = 2.0 * math.pi / theta
+    rotations = base.orig_len / wavelength
+    gamma = np.clip((rotations - base.alpha) / (base.beta - base.alpha), 0.0, 1.0)
+    return (1.0 - gamma) * theta / base.scale + gamma * theta
 
 
 def rope(x, pos, base: float) -> np.ndarray:
@@ -145,8 +190,11 @@ def query_heads_cq(h_t, w_dq, w_uq, w_qr, pos: int, n_heads: int, d_head: int, d
     return qc, qr
 
 
-def _default_scale(d_head: int, d_rope: int, scale):
-    return 1.0 / math.sqrt(d_head + d_rope) if (scale is None or scale <= 0) else float(scale)
+def _default_scale(d_head: int, d_rope: int, scale, base=None):
+    """tau: ``scale`` if given, else 1/sqrt(d_h + d_R); times YaRN's logit factor
+    when ``base`` is a stretched RoPE (:class:`Yarn`)."""
+    tau = 1.0 / math.sqrt(d_head + d_rope) if (scale is None or scale <= 0) else float(scale)
+    return tau * yarn_logit_factor(base)
 
 
 # -------------------------------------------------- the definition (oracle) --
@@ -167,7 +215,7 @@ def mla_decode_step(h_t, rows, w_q, w_qr, w_uk, w_uv, w_o, pos: int, n_heads: in
     """
     rows = _f64(rows)
     c, kr = rows[:, :d_latent], rows[:, d_latent:d_latent + d_rope]
-    tau = _default_scale(d_head, d_rope, scale)
+    tau = _default_scale(d_head, d_rope, scale, base)
     if w_dq is None:
         qc, qr = query_heads(h_t, w_q, w_qr, pos, n_heads, d_head, d_rope, base)
     else:
@@ -235,7 +283,7 @@ def mla_decode_step_absorbed(h_t, rows, w_q, w_qr, w_uk, w_uv, w_o, pos: int,
     """Absorbed fp64 form of :func:`mla_decode_step` (same inputs): attention runs
     in the d_c-wide latent space and per-head K/V are never formed ([Report]
     §2.3).  Returns dict(u, q_lat, q_pe, o_lat, lse)."""
-    tau = _default_scale(d_head, d_rope, scale)
+    tau = _default_scale(d_head, d_rope, scale, base)
     q_lat, q_pe = absorb_q(h_t, w_q, w_qr, w_uk, pos, n_heads, d_head, d_latent, d_rope, base,
                            w_dq, w_uq)
     o_lat, lse = _latent_attention(q_lat, q_pe, rows, d_latent, d_rope, tau)

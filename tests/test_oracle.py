@@ -490,3 +490,85 @@ def test_prefill_chunks_compose_and_match_the_partials():
         np.testing.assert_allclose(lse, whole["lse"][t], rtol=1e-12, atol=1e-12)
         per_head = np.stack([w["w_uv"][i * dh:(i + 1) * dh] @ o_lat[i] for i in range(nh)])
         np.testing.assert_allclose(per_head, whole["o"][t], rtol=1e-10, atol=1e-12)
+
+
+# ----------------------------------------------------------------- YaRN --
+# [Report] §3.3 (the long-context paragraph) gives YaRN's parameters for the
+# 4K -> 128K extension: scale 40, alpha 1, beta 32; the method is the published
+# one (oracle.Yarn).  These pins fix it by its limit case, by where the published
+# ramp must put the 64-wide RoPE branch's pairs, by position interpolation on the
+# stretched pairs and by its temperature's closed form.
+YARN_4K = dict(base=10000.0, scale=40.0, orig_len=4096, alpha=1.0, beta=32.0)
+
+
+def test_yarn_with_scale_one_is_plain_rope():
+    y = O.Yarn(10000.0, 1.0, 4096, 1.0, 32.0)
+    np.testing.assert_array_equal(O.rope_theta(64, y), O.rope_theta(64, 10000.0))
+    x = _rng(40).standard_normal((5, 64))
+    np.testing.assert_array_equal(O.rope(x, np.arange(5) * 977, y), O.rope(x, np.arange(5) * 977, 10000.0))
+    assert O.yarn_logit_factor(y) == 1.0 and O.yarn_logit_factor(10000.0) == 1.0
+
+
+def test_yarn_frequency_split_of_the_4k_to_128k_extension():
+    """d_R = 64, base 10000: theta_k = 10^(-k/8).  Pair k turns
+    r_k = 4096 theta_k / (2 pi) times over the 4K window: r_10 = 36.6 > beta = 32
+    and r_11 = 27.5 < 32, r_22 = 1.16 > alpha = 1 and r_23 = 0.87 < 1.  So pairs
+    0..10 keep their frequency, pairs 23..31 are divided by the scale 40 (their
+    wavelength stretched 40x, as position interpolation does), and 11..22 lie
+    strictly between, the stretch growing with k."""
+    plain = O.rope_theta(64, 10000.0)
+    yarn = O.rope_theta(64, O.Yarn(**YARN_4K))
+    np.testing.assert_array_equal(yarn[:11], plain[:11])
+    np.testing.assert_allclose(yarn[23:], plain[23:] / 40.0, rtol=1e-15)
+    ratio = yarn[11:23] / plain[11:23]
+    assert np.all(ratio < 1.0) and np.all(ratio > 1.0 / 40.0)
+    assert np.all(np.diff(ratio) < 0)
+
+
+def test_yarn_stretched_pairs_are_position_interpolation():
+    """On the pairs the ramp leaves fully interpolated (k >= 23 above), rotating at
+    position s*m with YaRN equals plain RoPE at position m."""
+    x = np.zeros((3, 64))
+    x[:, 46:] = _rng(41).standard_normal((3, 18))            # pairs 23..31 only
+    m = np.array([1, 777, 3000])
+    got = O.rope(x, 40 * m, O.Yarn(**YARN_4K))
+    np.testing.assert_allclose(got, O.rope(x, m, 10000.0), atol=1e-12)
+
+
+def test_yarn_keeps_rope_a_relative_rotation():
+    y = O.Yarn(**YARN_4K)
+    rng = _rng(42)
+    q, k = rng.standard_normal(64), rng.standard_normal(64)
+    for m, n in ((5, 2), (130000, 4096), (70000, 69999)):
+        a = O.rope(q, m, y) @ O.rope(k, n, y)
+        b = O.rope(q, m + 12345, y) @ O.rope(k, n + 12345, y)
+        assert abs(a - b) < 1e-9
+    np.testing.assert_allclose(np.linalg.norm(O.rope(q, 99999, y)), np.linalg.norm(q), rtol=1e-13)
+
+
+def test_yarn_temperature_closed_form():
+    """sqrt(1/t) = 0.1 ln s + 1: at s = e^10 the logits double twice (1/t = 4);
+    at s = 40, 1/t = (1 + 0.1 ln 40)^2 = 1.3688879^2 = 1.8738542..."""
+    assert abs(O.yarn_logit_factor(O.Yarn(10000.0, math.exp(10.0), 4096, 1, 32)) - 4.0) < 1e-12
+    assert abs(O.yarn_logit_factor(O.Yarn(**YARN_4K)) - 1.8738542071) < 1e-9
+
+
+def test_yarn_step_absorbed_equals_non_absorbed_and_scales_the_logits():
+    """Associativity still holds with the stretched RoPE; and with W_UK = 0 the
+    scores are tau/t q^R . k^R, so the lse of a one-token context is that score."""
+    H, nh, dh, dc, dr, L = 16, 2, 4, 8, 8, 9
+    rng = _rng(43)
+    w = _weights(rng, H, nh, dh, dc, dr)
+    y = O.Yarn(10000.0, 8.0, 4, 1.0, 4.0)
+    h_ctx = rng.standard_normal((L, H))
+    rows = O.latent_rows(h_ctx, w["w_dkv"], w["w_kr"], np.arange(L), y)
+    args = (h_ctx[-1], rows, w["w_q"], w["w_qr"], w["w_uk"], w["w_uv"], w["w_o"], L - 1, nh, dh,
+            dc, dr, y)
+    a = O.mla_decode_step_absorbed(*args)
+    d = O.mla_decode_step(*args)
+    np.testing.assert_allclose(a["u"], d["u"], rtol=1e-10, atol=1e-12)
+    one = O.mla_decode_step(h_ctx[0], rows[:1], w["w_q"], w["w_qr"], 0 * w["w_uk"], w["w_uv"],
+                            w["w_o"], 0, nh, dh, dc, dr, y)
+    qr = (w["w_qr"] @ h_ctx[0]).reshape(nh, dr)              # position 0: no rotation
+    want = O.yarn_logit_factor(y) / math.sqrt(dh + dr) * (qr @ rows[0, dc:])
+    np.testing.assert_allclose(one["lse"], want, rtol=1e-12)

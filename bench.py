@@ -88,6 +88,7 @@ def cpu_baseline(w, seconds: float):
     bt, _ = I.page_table(w, lens)
     wt = {n: I.to_f64(w, I.weight_values(w, n, 0)) for n in w.weight_names}
     cq = dict(w_dq=wt["w_dq"], w_uq=wt["w_uq"]) if w.d_cq else {}
+    base = O.Yarn(w.rope_base, *w.yarn) if w.yarn else w.rope_base
     done, spent, b = 0, 0.0, 0
     while spent < seconds and b < w.batch:
         L = int(lens[b])
@@ -97,11 +98,11 @@ def cpu_baseline(w, seconds: float):
         h = I.to_f64(w, I.tensor_values(w, "h_dec", None, 1.0, 0, start=b * w.hidden,
                                          count=w.hidden))
         t = time.perf_counter()
-        rows[L - 1] = O.latent_rows(h[None], wt["w_dkv"], wt["w_kr"], [L - 1], w.rope_base)[0]
+        rows[L - 1] = O.latent_rows(h[None], wt["w_dkv"], wt["w_kr"], [L - 1], base)[0]
         if fp8:     # the cache as the FP8 pool holds it
             rows = np.stack([O.fp8_dequantize_row(*O.fp8_quantize_row(r, w.d_latent)) for r in rows])
         O.mla_decode_step(h, rows, wt.get("w_q"), wt["w_qr"], wt["w_uk"], wt["w_uv"], wt["w_o"],
-                          L - 1, w.n_heads, w.d_head, w.d_latent, w.d_rope, w.rope_base, **cq)
+                          L - 1, w.n_heads, w.d_head, w.d_latent, w.d_rope, base, **cq)
         spent += time.perf_counter() - t
         done += 1
         b += 1

@@ -28,8 +28,10 @@
  *     of sequence b lives in row block_table[b*max_pages + j/page_size] *
  *     page_size + j%page_size.  block_table is int32 [batch, max_pages].
  *   - RoPE: adjacent pairs (x[2k], x[2k+1]) are turned by pos*theta_k,
- *     theta_k = rope_base^(-2k/d_R), angles evaluated in fp64.
- *   - Softmax scale tau = softmax_scale if > 0, else 1/sqrt(d_h + d_R).
+ *     theta_k = rope_base^(-2k/d_R) (YaRN-stretched when rope_scale > 1, see
+ *     mla_dims), angles evaluated in fp64.
+ *   - Softmax scale tau = softmax_scale if > 0, else 1/sqrt(d_h + d_R); with
+ *     YaRN times (0.1 ln rope_scale + 1)^2.
  *   - Errors: every argument the host can see is checked before anything is
  *     enqueued; a failing check returns a negative mla_status and enqueues
  *     nothing.  Device-side values the host cannot see (block-table entries,
@@ -51,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 1
+#define MLA_ABI_VERSION 2
 
 typedef enum {
   MLA_OK = 0,
@@ -77,6 +79,20 @@ typedef struct {
   int32_t dtype;         /* mla_dtype */
   float rope_base;       /* > 0, e.g. 10000 */
   float softmax_scale;   /* <= 0 selects 1/sqrt(d_h + d_R) */
+  /* YaRN-stretched RoPE ([Report] §3.3, long-context paragraph: 4K -> 128K with
+   * scale 40, alpha 1, beta 32; the method as published by Peng et al., "YaRN:
+   * Efficient Context Window Extension of Large Language Models", 2023).  With
+   * rope_scale = s > 1, pair k's frequency theta_k = rope_base^(-2k/d_R) becomes
+   * theta_k ((1 - g)/s + g), g = clamp((r - alpha)/(beta - alpha), 0, 1),
+   * r = rope_orig_len theta_k / (2 pi) (the pair's turns over the original
+   * window), and tau (as chosen above) is multiplied by (0.1 ln s + 1)^2, the
+   * method's temperature, over the whole score.  rope_scale <= 1: plain RoPE
+   * and the three fields below are ignored; else rope_orig_len >= 1 and
+   * 0 <= yarn_alpha < yarn_beta (MLA_ERR_SHAPE otherwise). */
+  float rope_scale;
+  int32_t rope_orig_len;
+  float yarn_alpha;
+  float yarn_beta;
 } mla_dims;
 
 /*
@@ -143,8 +159,10 @@ mla_status mla_absorb_q_append(const mla_dims* dims, const void* h, const void* 
  * positions [s*chunk, min(L, (s+1)*chunk)).  For every (b, s, head i):
  *   lse_part[b,s,i]   = log sum_{j in split} exp(s_ij)         (-inf if empty)
  *   o_part[b,s,i,:]   = sum_j exp(s_ij - lse_part) c_j          (0 if empty)
- *   q_lat [batch, n_h, d_c], q_pe [batch, n_h, d_R] fp32 (the MFMA path rounds
- *   them to bf16 once per work unit); pool dtype;
+ *   q_lat [batch, n_h, d_c], q_pe [batch, n_h, d_R] fp32 (the matrix-core path
+ *   -- bf16 dtype, n_h = 128, d_c = 512, d_R = 64, page_size = 64 -- rounds
+ *   them to bf16 once per work unit, which bounds its score precision: a
+ *   relative query error of up to 2^-8 per element); pool dtype;
  *   seq_lens [batch] int32 in [0, max_pages*page_size];
  *   o_part [batch, S, n_h, d_c] fp32; lse_part [batch, S, n_h] fp32.
  * num_splits in [1, 4096].
@@ -209,7 +227,7 @@ mla_status mla_absorb_out(const mla_dims* dims, const float* o_lat, const void* 
  * loaded on that device and held until the process ends; no call allocates,
  * frees or synchronises.  A call whose scratch need (the part of
  * mla_workspace_bytes that mla_absorb_out uses: at the full shape H = 5120,
- * n_h = d_h = 128, bf16, about 23 MiB at batch 64) exceeds that returns
+ * n_h = d_h = 128, bf16, about 25 MiB at batch 64) exceeds that returns
  * MLA_ERR_WORKSPACE and enqueues nothing.  Every call on one device shares the
  * one array: calls that may overlap on a device (two streams, two threads)
  * race and must be ordered by the caller.  Results equal mla_absorb_out's.
@@ -227,7 +245,7 @@ size_t mla_absorb_out_noalloc_max_bytes(void);
  *   q_pe[b,i,:] = RoPE(W_QR,i h_b, pos[b])
  *   w_dq [d_cq, H] and w_uq [n_h*d_h, d_cq] in dtype (head i owns rows
  *   i*d_h..(i+1)*d_h-1 of W_UQ); the rest as mla_absorb_q.  d_cq is even, in
- *   [2, 65536]; inside the call c^Q and q^C are held in dtype (as q^C is in
+ *   [2, 65536]; inside the call c^Q is held in dtype and q^C in fp32 (as in
  *   mla_absorb_q).
  * Workspace: at least mla_workspace_bytes_cq(dims, d_cq, batch) bytes,
  * 256-byte aligned, used for c^Q and q^C (scratch for the duration of the call).

@@ -15,7 +15,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmla.so")
 
-MLA_ABI_VERSION = 1
+MLA_ABI_VERSION = 2
 MLA_F32, MLA_BF16 = 0, 1
 
 __all__ = ["MlaDims", "MlaError", "make_dims", "load", "mla_append_latent", "mla_absorb_q",
@@ -33,7 +33,9 @@ class MlaDims(ctypes.Structure):
                 ("n_heads", ctypes.c_int32), ("d_head", ctypes.c_int32),
                 ("d_latent", ctypes.c_int32), ("d_rope", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("rope_base", ctypes.c_float), ("softmax_scale", ctypes.c_float)]
+                ("rope_base", ctypes.c_float), ("softmax_scale", ctypes.c_float),
+                ("rope_scale", ctypes.c_float), ("rope_orig_len", ctypes.c_int32),
+                ("yarn_alpha", ctypes.c_float), ("yarn_beta", ctypes.c_float)]
 
 
 class MlaError(RuntimeError):
@@ -43,9 +45,12 @@ class MlaError(RuntimeError):
 
 
 def make_dims(hidden, n_heads, d_head, d_latent, d_rope, dtype="bf16", page_size=64,
-              rope_base=10000.0, softmax_scale=0.0) -> MlaDims:
+              rope_base=10000.0, softmax_scale=0.0, yarn=None) -> MlaDims:
+    """``yarn``: None (plain RoPE) or (scale, orig_len, alpha, beta) of YaRN."""
+    s, n, a, b = yarn if yarn else (1.0, 0, 0.0, 0.0)
     return MlaDims(MLA_ABI_VERSION, hidden, n_heads, d_head, d_latent, d_rope, page_size,
-                   MLA_BF16 if dtype in ("bf16", MLA_BF16) else MLA_F32, rope_base, softmax_scale)
+                   MLA_BF16 if dtype in ("bf16", MLA_BF16) else MLA_F32, rope_base, softmax_scale,
+                   s, n, a, b)
 
 
 _lib = None
@@ -430,4 +435,8 @@ def mla_prefill_attention_fp8(dims, q_lat, q_pe, pool, block_table, q_seq, q_pos
 
 
 def default_scale(dims: MlaDims) -> float:
-    return dims.softmax_scale if dims.softmax_scale > 0 else 1.0 / math.sqrt(dims.d_head + dims.d_rope)
+    """tau as the library takes it from ``dims`` (YaRN's logit factor included)."""
+    tau = dims.softmax_scale if dims.softmax_scale > 0 else 1.0 / math.sqrt(dims.d_head + dims.d_rope)
+    if dims.rope_scale > 1.0:
+        tau *= (0.1 * math.log(dims.rope_scale) + 1.0) ** 2
+    return tau

@@ -31,10 +31,27 @@ __device__ __forceinline__ void set_err(int* err, int bits) {
   if (err) atomicOr(err, bits);
 }
 
-// cos/sin of pos * rope_base^(-2k/d_rope), evaluated in fp64 and rounded to fp32.
-__device__ __forceinline__ void rope_cs(int pos, int k, int d_rope, double log_base, float* c,
+// RoPE frequencies: theta_k = rope_base^(-2k/d_R); with yarn_scale > 1 they are
+// stretched by YaRN ("YaRN: Efficient Context Window Extension of Large Language
+// Models", Peng et al. 2023; the long-context extension of "《DeepSeek-V2》深度解读报告"
+// §3.3): pair k turns r = orig_len theta_k / (2 pi) times over the original window,
+// gamma = clamp((r - alpha) / (beta - alpha), 0, 1), theta'_k = theta_k ((1 - gamma) /
+// yarn_scale + gamma).
+struct RopeSpec {
+  double log_base;     // ln(rope_base)
+  double yarn_scale;   // <= 1: plain RoPE
+  double orig_len, alpha, beta;
+};
+
+// cos/sin of pos * theta_k (as RopeSpec defines it), evaluated in fp64 and rounded to fp32.
+__device__ __forceinline__ void rope_cs(int pos, int k, int d_rope, const RopeSpec& rs, float* c,
                                         float* s) {
-  const double theta = exp(-2.0 * static_cast<double>(k) / static_cast<double>(d_rope) * log_base);
+  double theta = exp(-2.0 * static_cast<double>(k) / static_cast<double>(d_rope) * rs.log_base);
+  if (rs.yarn_scale > 1.0) {
+    const double r = rs.orig_len * theta / 6.283185307179586;
+    const double g = fmin(fmax((r - rs.alpha) / (rs.beta - rs.alpha), 0.0), 1.0);
+    theta *= (1.0 - g) / rs.yarn_scale + g;
+  }
   double sd, cd;
   sincos(static_cast<double>(pos) * theta, &sd, &cd);
   *c = static_cast<float>(cd);

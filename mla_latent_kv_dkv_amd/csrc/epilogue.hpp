@@ -37,7 +37,7 @@ __device__ __forceinline__ void append_pair(const GemmArgs& a, void* pool, int s
   } else {
     const int k = (n - split) >> 1;
     float c, s;
-    rope_cs(pos, k, a.d_rope, a.log_base, &c, &s);
+    rope_cs(pos, k, a.d_rope, a.rope, &c, &s);
     st(row + n, v0 * c - v1 * s);
     st(row + n + 1, v0 * s + v1 * c);
   }
@@ -58,15 +58,15 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, int z, int m, i
     return;
   }
   if (a.epi == EPI_QPROJ || a.epi == EPI_QPROJ_APPEND) {
-    if (n < a.n_split) {
-      T* y = static_cast<T*>(a.y) + static_cast<int64_t>(m) * a.ldy;
-      st(y + n, v0);
-      st(y + n + 1, v1);
+    if (n < a.n_split) {   // q^C: fp32 (y_f32) or the storage type
+      const int64_t base = static_cast<int64_t>(m) * a.ldy;
+      st_act<T>(a.y, base + n, v0, a.y_f32);
+      st_act<T>(a.y, base + n + 1, v1, a.y_f32);
     } else {
       const int r = n - a.n_split;              // column within q_pe row
       const int k = (r % a.d_rope) >> 1;       // pair index within the head
       float c, s;
-      rope_cs(a.pos[m], k, a.d_rope, a.log_base, &c, &s);
+      rope_cs(a.pos[m], k, a.d_rope, a.rope, &c, &s);
       const int qpe_w = (a.epi == EPI_QPROJ_APPEND ? a.n_append : a.N) - a.n_split;
       float* y2 = static_cast<float*>(a.y2) + static_cast<int64_t>(m) * qpe_w;
       y2[r] = v0 * c - v1 * s;

@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256) void k_quantize_rows(QuantArgs a) {
     float v0 = src[a.d_latent + 2 * p], v1 = src[a.d_latent + 2 * p + 1];
     if (a.rope) {
       float cs, sn;
-      rope_cs(pos, p, a.d_rope, a.log_base, &cs, &sn);
+      rope_cs(pos, p, a.d_rope, a.rs, &cs, &sn);
       const float r0 = v0 * cs - v1 * sn, r1 = v0 * sn + v1 * cs;
       v0 = r0;
       v1 = r1;

@@ -386,7 +386,12 @@ __global__ __launch_bounds__(256) void k_gemm_finish(GemmArgs a, int ksplit, con
 // MFMA A operand (M = c) with transposed reads; X rows are the B operand (N = b).
 constexpr int kUkK = 128, kUkN = 128, kUkPad = kUkN * 2 + 16;   // LDS row bytes
 
+// An fp32 X (the absorbed query's q^C) enters as two bf16 terms, hi = RNE(x) and
+// lo = RNE(x - hi), each multiplied with the same W operand: the product is then
+// exact to about 2^-16 of x instead of bf16's 2^-8.
+template <typename XT>
 __global__ __launch_bounds__(256) void k_gemm_uk(GemmArgs a) {
+  constexpr bool kSplit = std::is_same<XT, float>::value;
   __shared__ __attribute__((aligned(16))) char wt[kUkK * kUkPad];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int head = blockIdx.x, c0 = blockIdx.y * kUkN, m0 = blockIdx.z * kTile;
@@ -399,14 +404,34 @@ __global__ __launch_bounds__(256) void k_gemm_uk(GemmArgs a) {
   }
   // X fragments: rows m0+r, m0+32+r, k = 16s + 8g + j
   const int r = lane & 31, g = lane >> 5;
-  const bf16_t* xb = static_cast<const bf16_t*>(a.x) + head * a.x_bs;
+  const XT* xb = static_cast<const XT*>(a.x) + head * a.x_bs;
   bf16x8_t xf[2][kUkK / 16];
+  bf16x8_t xl[kSplit ? 2 : 1][kSplit ? kUkK / 16 : 1];   // lo terms of an fp32 X
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int m = m0 + 32 * q + r;
-    const bf16_t* row = xb + static_cast<int64_t>(m < a.M ? m : 0) * a.ldx_m;
+    const XT* row = xb + static_cast<int64_t>(m < a.M ? m : 0) * a.ldx_m;
 #pragma unroll
-    for (int s = 0; s < kUkK / 16; ++s) xf[q][s] = ld8(row + 16 * s + 8 * g);
+    for (int s = 0; s < kUkK / 16; ++s) {
+      if constexpr (kSplit) {
+        const float4 v0 = *reinterpret_cast<const float4*>(row + 16 * s + 8 * g);
+        const float4 v1 = *reinterpret_cast<const float4*>(row + 16 * s + 8 * g + 4);
+        const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        const u32x4_t hi = {cvt2(v[0], v[1]), cvt2(v[2], v[3]), cvt2(v[4], v[5]), cvt2(v[6], v[7])};
+        float rl[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          rl[2 * j] = v[2 * j] - __uint_as_float(hi[j] << 16);
+          rl[2 * j + 1] = v[2 * j + 1] - __uint_as_float(hi[j] & 0xFFFF0000u);
+        }
+        const u32x4_t lo = {cvt2(rl[0], rl[1]), cvt2(rl[2], rl[3]), cvt2(rl[4], rl[5]),
+                            cvt2(rl[6], rl[7])};
+        xf[q][s] = __builtin_bit_cast(bf16x8_t, hi);
+        xl[q][s] = __builtin_bit_cast(bf16x8_t, lo);
+      } else {
+        xf[q][s] = ld8(row + 16 * s + 8 * g);
+      }
+    }
   }
   __syncthreads();
   // wave wv owns columns c0 + 32wv .. +31 (A operand M index = column)
@@ -428,8 +453,11 @@ __global__ __launch_bounds__(256) void k_gemm_uk(GemmArgs a) {
     const s16x4_t vv[2] = {v0, v1};
     const bf16x8_t af = __builtin_bit_cast(bf16x8_t, vv);
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+    for (int q = 0; q < 2; ++q) {
       acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, xf[q][s], acc[q], 0, 0, 0);
+      if constexpr (kSplit)
+        acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, xl[q][s], acc[q], 0, 0, 0);
+    }
   }
   // acc[q] lane (x row r, g): columns 32wv + 8(e/4) + 4g + (e%4), X row 32q + r
 #pragma unroll
@@ -709,11 +737,12 @@ static bool ws_ok(const GemmArgs& a) {
   return a.K % ws_kunit(ws_mb(a.M)) == 0;
 }
 
-// The per-head W_UK form: W is [K=128, N] N-contiguous, output fp32.
+// The per-head W_UK form: W is [K=128, N] N-contiguous, output fp32; X bf16, or
+// fp32 (taken as two bf16 terms).
 static bool uk_ok(const GemmArgs& a) {
   return a.ldw_n == 1 && a.ldw_k % 8 == 0 && a.K == kUkK && a.N % kUkN == 0 && a.ldx_k == 1 &&
-         !a.x_f32 && a.y_f32 && a.epi == EPI_STORE && a.ldx_m % 8 == 0 && a.x_bs % 8 == 0 &&
-         a.w1 == a.w2 && a.n_split >= a.N;
+         a.y_f32 && a.epi == EPI_STORE && a.ldx_m % 8 == 0 && a.x_bs % 8 == 0 &&
+         a.w1 == a.w2 && a.n_split >= a.N && aligned16(a.x) && aligned16(a.w1);
 }
 
 // One activation matrix of at most 64 rows and enough weight rows to give every
@@ -768,7 +797,10 @@ hipError_t launch_gemm_fast(const GemmArgs& a, void* partial, size_t partial_byt
   if (!ws_ok(a)) {
     if (!uk_ok(a)) return hipErrorInvalidValue;
     dim3 grid(a.batch, a.N / kUkN, (a.M + kTile - 1) / kTile);
-    hipLaunchKernelGGL(k_gemm_uk, grid, dim3(256), 0, stream, a);
+    if (a.x_f32)
+      hipLaunchKernelGGL(k_gemm_uk<float>, grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(k_gemm_uk<bf16_t>, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
   }
   if (tile_ok(a)) {

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.hpp"
+
 namespace mla {
 
 // Epilogues of the projection GEMM Y[m, n] = sum_k X(m, k) W(n, k).
@@ -30,12 +32,12 @@ struct GemmArgs {
   int M, N, K, batch;
   int epi;
   int x_f32;        // X is fp32 (else the storage dtype of W)
-  int y_f32;        // EPI_STORE output is fp32 (else the storage dtype)
+  int y_f32;        // EPI_STORE output / EPI_QPROJ's q^C is fp32 (else the storage dtype)
   void* y;
   int64_t ldy, y_bs;
   void* y2;         // EPI_QPROJ: q_pe [M, N - n_split], fp32
   int d_rope;       // EPI_APPEND / EPI_QPROJ: rope width (pairs restart every d_rope columns)
-  double log_base;  // ln(rope_base)
+  RopeSpec rope;    // RoPE frequencies (EPI_APPEND / EPI_QPROJ)
   const int32_t* pos;      // EPI_APPEND: row_pos; EPI_QPROJ: decode positions
   const int32_t* row_seq;  // EPI_APPEND
   const int32_t* block_table;
@@ -82,7 +84,7 @@ struct QuantArgs {
   int64_t ld_rows;
   int n_rows, d_latent, d_rope;
   int rope;                 // rotate the k^R part at row_pos (rows straight from the projection)
-  double log_base;
+  RopeSpec rs;
   const int32_t* row_seq;
   const int32_t* row_pos;
   const int32_t* block_table;

@@ -71,14 +71,39 @@ mla_status check_dims(const mla_dims* d) {
     return MLA_ERR_SHAPE;
   if (!(d->rope_base > 0.f) || !std::isfinite(d->rope_base)) return MLA_ERR_SHAPE;
   if (!std::isfinite(d->softmax_scale)) return MLA_ERR_SHAPE;
+  if (!std::isfinite(d->rope_scale)) return MLA_ERR_SHAPE;
+  if (d->rope_scale > 1.f &&
+      !(d->rope_orig_len >= 1 && std::isfinite(d->yarn_alpha) && std::isfinite(d->yarn_beta) &&
+        d->yarn_alpha >= 0.f && d->yarn_beta > d->yarn_alpha))
+    return MLA_ERR_SHAPE;
   return MLA_OK;
+}
+
+bool yarn_on(const mla_dims* d) { return d->rope_scale > 1.f; }
+
+// RoPE frequencies of the dims (YaRN-stretched when rope_scale > 1).
+mla::RopeSpec rope_spec(const mla_dims* d) {
+  mla::RopeSpec r{};
+  r.log_base = std::log(static_cast<double>(d->rope_base));
+  r.yarn_scale = yarn_on(d) ? static_cast<double>(d->rope_scale) : 1.0;
+  r.orig_len = static_cast<double>(d->rope_orig_len);
+  r.alpha = static_cast<double>(d->yarn_alpha);
+  r.beta = static_cast<double>(d->yarn_beta);
+  return r;
 }
 
 size_t elem_bytes(const mla_dims* d) { return d->dtype == MLA_BF16 ? 2 : 4; }
 
+// tau: softmax_scale, or 1/sqrt(d_h + d_R); with YaRN times its logit factor
+// (0.1 ln s + 1)^2
 float softmax_scale(const mla_dims* d) {
-  return d->softmax_scale > 0.f ? d->softmax_scale
-                                : 1.0f / std::sqrt(static_cast<float>(d->d_head + d->d_rope));
+  double tau = d->softmax_scale > 0.f ? d->softmax_scale
+                                      : 1.0 / std::sqrt(static_cast<double>(d->d_head + d->d_rope));
+  if (yarn_on(d)) {
+    const double m = 0.1 * std::log(static_cast<double>(d->rope_scale)) + 1.0;
+    tau *= m * m;
+  }
+  return static_cast<float>(tau);
 }
 
 bool use_fast() { return g_path.load(std::memory_order_relaxed) == 0; }
@@ -95,9 +120,10 @@ mla::GemmArgs qproj_args(const mla_dims* d, int batch) {
   a.ldw_n = d->hidden; a.ldw_k = 1;
   a.M = batch; a.N = static_cast<int>(nhdh + static_cast<int64_t>(d->n_heads) * d->d_rope);
   a.K = d->hidden; a.batch = 1;
-  a.epi = mla::EPI_QPROJ; a.x_f32 = !bf16; a.y_f32 = !bf16;
+  // q^C is kept in fp32 for the W_UK product (which takes it as two bf16 terms)
+  a.epi = mla::EPI_QPROJ; a.x_f32 = !bf16; a.y_f32 = 1;
   a.ldy = nhdh; a.d_rope = d->d_rope;
-  a.log_base = std::log(static_cast<double>(d->rope_base));
+  a.rope = rope_spec(d);
   return a;
 }
 
@@ -124,11 +150,11 @@ mla::GemmArgs cqproj_args(const mla_dims* d, int d_cq, int batch) {
   a.M = batch; a.N = d_cq + d->n_heads * d->d_rope; a.K = d->hidden; a.batch = 1;
   a.epi = mla::EPI_QPROJ; a.x_f32 = !bf16; a.y_f32 = !bf16;
   a.ldy = d_cq; a.d_rope = d->d_rope;
-  a.log_base = std::log(static_cast<double>(d->rope_base));
+  a.rope = rope_spec(d);
   return a;
 }
 
-// second product: q^C = W_UQ c^Q (c^Q and q^C in dtype)
+// second product: q^C = W_UQ c^Q (c^Q in dtype, q^C in fp32 for the W_UK product)
 mla::GemmArgs uq_args(const mla_dims* d, int d_cq, int batch) {
   const bool bf16 = d->dtype == MLA_BF16;
   const int64_t nhdh = static_cast<int64_t>(d->n_heads) * d->d_head;
@@ -137,20 +163,20 @@ mla::GemmArgs uq_args(const mla_dims* d, int d_cq, int batch) {
   a.n_split = static_cast<int>(nhdh);
   a.ldw_n = d_cq; a.ldw_k = 1;
   a.M = batch; a.N = static_cast<int>(nhdh); a.K = d_cq; a.batch = 1;
-  a.epi = mla::EPI_STORE; a.x_f32 = !bf16; a.y_f32 = !bf16;
+  a.epi = mla::EPI_STORE; a.x_f32 = !bf16; a.y_f32 = 1;
   a.ldy = nhdh;
   return a;
 }
 
-mla::GemmArgs uk_args(const mla_dims* d, int batch) {
-  const bool bf16 = d->dtype == MLA_BF16;
+// q_lat = W_UK^T q^C per head; q^C in fp32 (qc_f32) or the storage type
+mla::GemmArgs uk_args(const mla_dims* d, int batch, bool qc_f32) {
   const int64_t nhdh = static_cast<int64_t>(d->n_heads) * d->d_head;
   mla::GemmArgs g{};
   g.ldx_m = nhdh; g.ldx_k = 1; g.x_bs = d->d_head;
   g.n_split = d->d_latent;
   g.ldw_n = 1; g.ldw_k = d->d_latent; g.w_bs = static_cast<int64_t>(d->d_head) * d->d_latent;
   g.M = batch; g.N = d->d_latent; g.K = d->d_head; g.batch = d->n_heads;
-  g.epi = mla::EPI_STORE; g.x_f32 = !bf16; g.y_f32 = 1;
+  g.epi = mla::EPI_STORE; g.x_f32 = qc_f32; g.y_f32 = 1;
   g.ldy = static_cast<int64_t>(d->n_heads) * d->d_latent; g.y_bs = d->d_latent;
   return g;
 }
@@ -189,7 +215,7 @@ mla::GemmArgs append_args(const mla_dims* d, int n_rows) {
   a.ldw_n = d->hidden; a.ldw_k = 1; a.w_bs = 0;
   a.M = n_rows; a.N = d->d_latent + d->d_rope; a.K = d->hidden; a.batch = 1;
   a.epi = mla::EPI_APPEND; a.x_f32 = !bf16;
-  a.d_rope = d->d_rope; a.log_base = std::log(static_cast<double>(d->rope_base));
+  a.d_rope = d->d_rope; a.rope = rope_spec(d);
   a.row_width = d->d_latent + d->d_rope;
   return a;
 }
@@ -198,10 +224,10 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 bool ws_aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255) == 0; }
 
-// Bytes of the activation region (q^C or the per-head outputs o) at the front
-// of the workspace.
+// Bytes of the activation region (q^C, fp32, or the per-head outputs o in the
+// storage type) at the front of the workspace: sized for fp32.
 size_t act_bytes(const mla_dims* d, int batch) {
-  return align256(static_cast<size_t>(batch) * d->n_heads * d->d_head * elem_bytes(d));
+  return align256(static_cast<size_t>(batch) * d->n_heads * d->d_head * sizeof(float));
 }
 
 bool fast_for(const mla_dims* d, const mla::GemmArgs& a) {
@@ -348,7 +374,7 @@ size_t mla_workspace_bytes_cq(const mla_dims* d, int32_t d_cq, int32_t batch) {
   size_t part = 0;
   if (batch > 0) {
     for (const mla::GemmArgs& a : {cqproj_args(d, d_cq, batch), uq_args(d, d_cq, batch),
-                                   uk_args(d, batch)})
+                                   uk_args(d, batch, true)})
       part = std::max(part, partial_bytes(d, a));
   }
   return act_bytes(d, batch) + cq_bytes(d, d_cq, batch) + part + 256;
@@ -359,7 +385,7 @@ size_t mla_workspace_bytes(const mla_dims* d, int32_t batch) {
   // [activation region: q^C or o, batch x n_h*d_h in dtype][fp32 K-split partials]
   size_t part = 0;
   if (batch > 0) {
-    for (const mla::GemmArgs& a : {qproj_args(d, batch), uk_args(d, batch), uv_args(d, batch),
+    for (const mla::GemmArgs& a : {qproj_args(d, batch), uk_args(d, batch, true), uv_args(d, batch),
                                    oproj_args(d, batch), append_args(d, batch), qa_args(d, batch)})
       part = std::max(part, partial_bytes(d, a));
   }
@@ -425,8 +451,8 @@ mla_status mla_absorb_q(const mla_dims* d, const void* h, const void* w_q, const
   mla::GemmArgs a = qproj_args(d, batch);
   a.x = h; a.w1 = w_q; a.w2 = w_qr; a.y = ws; a.y2 = q_pe; a.pos = pos;
   if (run_gemm(d, a, part, pbytes, stream) != hipSuccess) return MLA_ERR_HIP;
-  // 2) q_lat[b, i, :] = W_UK,i^T q^C[b, i, :] per head i
-  mla::GemmArgs g = uk_args(d, batch);
+  // 2) q_lat[b, i, :] = W_UK,i^T q^C[b, i, :] per head i (q^C in fp32)
+  mla::GemmArgs g = uk_args(d, batch, true);
   g.x = ws; g.w1 = w_uk; g.w2 = w_uk; g.y = q_lat;
   return hip_status(run_gemm(d, g, part, pbytes, stream));
 }
@@ -468,8 +494,8 @@ mla_status mla_absorb_q_append(const mla_dims* d, const void* h, const void* w_q
                              max_pages, pool, num_pages, ws, ws_bytes, stream);
   }
   if (mla::launch_gemm_fast(a, part, pbytes, stream) != hipSuccess) return MLA_ERR_HIP;
-  // 2) q_lat[b, i, :] = W_UK,i^T q^C[b, i, :] per head i
-  mla::GemmArgs g = uk_args(d, batch);
+  // 2) q_lat[b, i, :] = W_UK,i^T q^C[b, i, :] per head i (q^C in fp32)
+  mla::GemmArgs g = uk_args(d, batch, true);
   g.x = ws; g.w1 = w_uk; g.w2 = w_uk; g.y = q_lat;
   return hip_status(run_gemm(d, g, part, pbytes, stream));
 }
@@ -497,8 +523,8 @@ mla_status mla_absorb_q_cq(const mla_dims* d, int32_t d_cq, const void* h, const
   mla::GemmArgs u = uq_args(d, d_cq, batch);
   u.x = cq; u.w1 = w_uq; u.w2 = w_uq; u.y = qc;
   if (run_gemm(d, u, part, pbytes, stream) != hipSuccess) return MLA_ERR_HIP;
-  // 3) q_lat[b, i, :] = W_UK,i^T q^C[b, i, :] per head i
-  mla::GemmArgs g = uk_args(d, batch);
+  // 3) q_lat[b, i, :] = W_UK,i^T q^C[b, i, :] per head i (q^C in fp32)
+  mla::GemmArgs g = uk_args(d, batch, true);
   g.x = qc; g.w1 = w_uk; g.w2 = w_uk; g.y = q_lat;
   return hip_status(run_gemm(d, g, part, pbytes, stream));
 }
@@ -560,7 +586,7 @@ mla_status mla_quantize_rows_fp8(const mla_dims* d, const float* rows, int64_t l
   mla::QuantArgs q{};
   q.rows = rows; q.ld_rows = ld_rows; q.n_rows = n_rows;
   q.d_latent = d->d_latent; q.d_rope = d->d_rope; q.rope = 0;
-  q.log_base = std::log(static_cast<double>(d->rope_base));
+  q.rs = rope_spec(d);
   q.row_seq = row_seq; q.row_pos = row_pos; q.block_table = block_table;
   q.n_seqs = n_seqs; q.max_pages = max_pages; q.page_size = d->page_size;
   q.num_pages = num_pages; q.page_bytes = fp8_page_bytes(d); q.row_bytes = fp8_row_bytes(d);
@@ -598,7 +624,7 @@ mla_status mla_append_latent_fp8(const mla_dims* d, const void* h, const void* w
   mla::QuantArgs q{};
   q.rows = rows; q.ld_rows = rows_ld(d); q.n_rows = n_rows;
   q.d_latent = d->d_latent; q.d_rope = d->d_rope; q.rope = 1;
-  q.log_base = std::log(static_cast<double>(d->rope_base));
+  q.rs = rope_spec(d);
   q.row_seq = row_seq; q.row_pos = row_pos; q.block_table = block_table;
   q.n_seqs = n_seqs; q.max_pages = max_pages; q.page_size = d->page_size;
   q.num_pages = num_pages; q.page_bytes = fp8_page_bytes(d); q.row_bytes = fp8_row_bytes(d);

@@ -50,7 +50,7 @@ class DeviceWorkload:
         self.w, self.layer = w, layer
         self.dev = torch.device(device)
         self.dims = make_dims(w.hidden, w.n_heads, w.d_head, w.d_latent, w.d_rope, w.dtype,
-                              w.page_size, w.rope_base)
+                              w.page_size, w.rope_base, yarn=w.yarn or None)
         self.dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
         self.S = num_splits or w.num_splits
         self.lens = I.seq_lengths(w)

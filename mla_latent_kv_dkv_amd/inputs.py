@@ -170,6 +170,7 @@ class Workload:
     cache: str = "dtype"            # pool format: "dtype" rows, or "fp8" pages
     chunk: int = 0                  # prefill: the last `chunk` positions of every sequence
                                     # are the step's prompt tokens (0: decode, one token)
+    yarn: tuple = ()                # YaRN-stretched RoPE: (scale, orig_len, alpha, beta)
     notes: str = field(default="", compare=False)
 
     @property
@@ -234,6 +235,15 @@ WORKLOADS = {
                          cache_from_h=True, chunk=64),
     "full-pre": Workload("full-pre", 5120, 128, 128, 512, 64, "bf16", 4, 4096, 1014, num_splits=1,
                          chunk=256),
+    # YaRN-stretched RoPE: the long-context extension's 4K -> 128K setting (scale 40,
+    # alpha 1, beta 32) on the full and long shapes; the tiny shape with a 16-token
+    # original window so its 64 positions cross the ramp
+    "tiny-yarn": Workload("tiny-yarn", 64, 4, 16, 32, 8, "f32", 1, 64, 1015, num_splits=1,
+                          permute_pages=False, cache_from_h=True, yarn=(4.0, 16, 1.0, 32.0)),
+    "full-yarn": Workload("full-yarn", 5120, 128, 128, 512, 64, "bf16", 64, 4096, 1016,
+                          num_splits=4, yarn=(40.0, 4096, 1.0, 32.0)),
+    "long-yarn": Workload("long-yarn", 5120, 128, 128, 512, 64, "bf16", 4, 131072, 1017,
+                          num_splits=64, yarn=(40.0, 4096, 1.0, 32.0)),
 }
 
 

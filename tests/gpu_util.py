@@ -77,6 +77,27 @@ def assert_partials_within_weight_rounding(got, ref, q_lat, q_pe, rows, length, 
         assert worst <= 1.0, f"o_part {what} split {s}: error {worst:.2f}x the weight-rounding bound"
 
 
+def attention_rounds_queries(w, path: int = 0) -> bool:
+    """True when the decode attention of workload ``w`` runs on a matrix-core
+    kernel (kernel path 0, bf16 storage, n_h 128, d_c 512, d_R 64, 64-token
+    pages), which rounds q_lat and q_pe to bf16 once per work unit as
+    include/mla.h states; the vector kernels keep them in fp32."""
+    return (path == 0 and w.dtype == "bf16" and w.n_heads == 128 and w.d_latent == 512 and
+            w.d_rope == 64 and w.page_size == 64)
+
+
+def bf16_round(x):
+    """Values rounded to bf16 (nearest even), as fp64."""
+    return I.bf16_bits_to_f64(I.f32_to_bf16_bits(np.asarray(x, np.float32)))
+
+
+def rope_base(w):
+    """The RoPE ``base`` argument of the oracle for workload ``w``: its base, or the
+    oracle's YaRN description when the workload stretches RoPE."""
+    import oracle as O
+    return O.Yarn(w.rope_base, *w.yarn) if w.yarn else w.rope_base
+
+
 def host_tensor(w, name, shape, std=1.0, layer=0):
     return I.to_f64(w, I.tensor_values(w, name, shape, std, layer))
 

@@ -79,6 +79,9 @@ def test_invalid_dims_are_rejected_without_launch():
     bad_dtype = _dims()
     bad_dtype.dtype = 7
     cases.append((bad_dtype, -3))
+    yarn_bad = [_dims(yarn=(40.0, 0, 1.0, 32.0)), _dims(yarn=(40.0, 4096, 32.0, 32.0)),
+                _dims(yarn=(40.0, 4096, -1.0, 32.0)), _dims(yarn=(float("nan"), 4096, 1.0, 32.0))]
+    cases += [(d, -2) for d in yarn_bad]
     for d, want in cases:
         got = lib.mla_decode_attention(ctypes.byref(d), P, P, P, 1, P, 1, P, 1, 1, P, P, None)
         assert got == want, (d.d_rope, d.page_size, got)

@@ -1,17 +1,20 @@
 #!/usr/bin/env python3
 """Decode-step benchmark of the MLA latent-KV library on one MI355X.
 
-One step = the five calls of one MLA decode layer on the full-shape workload
-(hidden 5120, n_h 128, d_h 128, d_c 512, d_R 64, bf16 cache and weights; 64
-sequences at context 4096, 4 KV splits): absorb_q -> append_latent ->
-decode_attention -> merge_lse -> absorb_out.  Inputs are seeded synthetic data
-resident in HBM before timing; two independent copies of weights and cache
-alternate between steps so no step re-reads the previous step's bytes from
-the 256 MB last-level cache.
+One step = one MLA decode layer (60 for the ragged workload) on the chosen
+workload, default the full shape (hidden 5120, n_h 128, d_h 128, d_c 512,
+d_R 64, bf16 cache and weights; 64 sequences at context 4096, 4 KV splits):
+absorbed query + latent append (one fused call) -> split-KV attention -> LSE
+merge -> absorbed output.  Inputs are seeded synthetic data resident in HBM
+before timing; for one-layer workloads two independent copies of weights and
+cache alternate between steps so no step re-reads the previous step's bytes
+from the 256 MB last-level cache (the 60 ragged layers hold ~137 GB of cache,
+far beyond it).
 
 Prints one JSON line: decoded tokens/s (value), latent-cache GB/s, the HBM
 roofline of the attention kernel measured with HIP events on the launch
-stream, and the fp64 CPU oracle timed on a bounded sample on the host.
+stream, the step's roofline (cache + weight bytes over the step time), and the
+fp64 CPU oracle timed on a bounded sample on the host.
 """
 from __future__ import annotations
 
@@ -35,9 +38,10 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="full",
-                   help="full | lite | long | full-cq (query compression) | full-fp8 (FP8 latent "
-                        "pool) | full-pre (chunked prefill: 4 x 256 prompt tokens at context "
-                        "4096) (one layer each)")
+                   help="full | lite | long | ragged (256 sequences, 60 layers) | full-cq (query "
+                        "compression) | full-fp8 (FP8 latent pool) | full-pre (chunked prefill: "
+                        "4 x 256 prompt tokens at context 4096) | full-yarn | long-yarn (YaRN "
+                        "RoPE); one layer each unless stated")
     p.add_argument("--splits", type=int, default=0, help="KV splits (0 = workload default)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="budget of the oracle timing on the host (0 disables it)")
@@ -50,7 +54,31 @@ def parse():
 
 def attention_kernel(w) -> str:
     """Name of the attention kernel that runs for workload `w`."""
+    if w.n_heads != 128 or w.dtype != "bf16":
+        return "k_attention_generic"
     return "k_attn_f8mma_h128" if w.cache == "fp8" else "k_attn_mfma_h128"
+
+
+def host_info():
+    """What the oracle timing ran on: usable cores, CPU model, BLAS and its threads."""
+    import numpy as np
+    info = {"cores_usable": len(os.sched_getaffinity(0)), "numpy": np.__version__}
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                info["cpu_model"] = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            info["blas"] = f"{blas[0].get('internal_api')} {blas[0].get('version')}"
+            info["blas_threads"] = int(blas[0].get("num_threads", 1))
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        pass
+    return info
 
 
 def attention_traffic(kernel: str, workload: str):
@@ -71,19 +99,17 @@ def attention_traffic(kernel: str, workload: str):
 
 def cpu_baseline(w, seconds: float):
     """fp64 oracle (non-absorbed definition) on whole sequences of the same
-    workload until `seconds` of host time are spent; tokens/s = sequences/s.
-    Prefill workloads: the step's prompt tokens of sequence 0, one by one."""
+    workload (layer 0) until `seconds` of host time are spent; tokens/s =
+    sequences/s divided by the layers of one step.  Prefill workloads: the step's
+    prompt tokens of sequence 0, one by one."""
     if w.chunk:
         return cpu_baseline_prefill(w, seconds)
     import numpy as np
 
     import oracle as O
     from mla_latent_kv_dkv_amd import inputs as I
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover - threadpoolctl is optional
-        threads = len(os.sched_getaffinity(0))
+    info = host_info()
+    threads = info.get("blas_threads", info["cores_usable"])
     lens = I.seq_lengths(w)
     bt, _ = I.page_table(w, lens)
     wt = {n: I.to_f64(w, I.weight_values(w, n, 0)) for n in w.weight_names}
@@ -106,10 +132,15 @@ def cpu_baseline(w, seconds: float):
         spent += time.perf_counter() - t
         done += 1
         b += 1
-    return {"value": done / spent, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {w.batch} sequences (context {int(lens[0])}), non-absorbed "
-                      f"fp64 definition" + (" on the FP8-quantized cache" if w.cache == "fp8" else "")
-                      + f", {spent:.1f} s of host time"}
+    ctx = (f"context {int(lens[0])}" if not w.ragged else
+           f"contexts {', '.join(str(int(x)) for x in lens[:done])}")
+    return {"value": done / spent / w.layers, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {w.batch} sequences ({ctx}) of layer 0, non-absorbed fp64 "
+                      f"definition" + (" on the FP8-quantized cache" if w.cache == "fp8" else "")
+                      + (f", per-layer rate divided by {w.layers} layers" if w.layers > 1 else "")
+                      + f", {spent:.1f} s of host time",
+            **{k: v for k, v in info.items() if k != "cores_usable"}}
 
 
 def cpu_baseline_prefill(w, seconds: float):
@@ -117,11 +148,8 @@ def cpu_baseline_prefill(w, seconds: float):
 
     import oracle as O
     from mla_latent_kv_dkv_amd import inputs as I
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover - threadpoolctl is optional
-        threads = len(os.sched_getaffinity(0))
+    info = host_info()
+    threads = info.get("blas_threads", info["cores_usable"])
     lens = I.seq_lengths(w)
     bt, _ = I.page_table(w, lens)
     wt = {n: I.to_f64(w, I.weight_values(w, n, 0)) for n in w.weight_names}
@@ -143,7 +171,8 @@ def cpu_baseline_prefill(w, seconds: float):
         done += 1
     return {"value": done / spent, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} of {w.chunk} prompt tokens of sequence 0 (positions {P}..), "
-                      f"non-absorbed fp64 definition, {spent:.1f} s of host time"}
+                      f"non-absorbed fp64 definition, {spent:.1f} s of host time",
+            **{k: v for k, v in info.items() if k != "cores_usable"}}
 
 
 def main():
@@ -171,31 +200,47 @@ def main():
     M.load()
     w = I.WORKLOADS[args.workload]
     S = args.splits or w.num_splits
-    sets = [DeviceWorkload(w, layer=l, num_splits=S) for l in (0, 1)]
+    if w.layers > 1:
+        # every layer has its own weights and pool; outputs and scratch are shared
+        first = DeviceWorkload(w, layer=0, num_splits=S)
+        sets = [[first] + [DeviceWorkload(w, layer=l, num_splits=S, outputs_from=first)
+                           for l in range(1, w.layers)]]
+    else:
+        sets = [[DeviceWorkload(w, layer=l, num_splits=S)] for l in (0, 1)]
     torch.cuda.synchronize()
-    lens = sets[0].lens
-    nq = sets[0].nq                      # the step's tokens (decode: one per sequence)
-    attended = (sets[0].q_pos_host.astype(np.int64) + 1).sum()   # cached rows read per launch
+    dw0 = sets[0][0]
+    lens = dw0.lens
+    nq = dw0.nq                          # the step's tokens (decode: one per sequence)
+    attended = (dw0.q_pos_host.astype(np.int64) + 1).sum()   # cached rows read per launch
     # bytes of one cached row: d_c + d_R values in dtype, or (FP8 pool) d_c codes,
     # d_R bf16 and one fp32 scale
     row_bytes = (w.d_latent + 2 * w.d_rope + 4) if w.cache == "fp8" else w.row * w.elem_bytes
     cache_bytes = int(attended) * row_bytes
+    weight_bytes = sum(t.numel() * t.element_size() for t in dw0.weights.values())
     attn_flop = 2 * w.n_heads * int(attended) * (2 * w.d_latent + w.d_rope)
     stream = torch.cuda.current_stream()
 
-    def one(i, ev=None):
-        dw = sets[i & 1]
-        if args.attention_only:
+    def one(i, evs=None):
+        for dw in sets[i % len(sets)]:
+            if args.attention_only:
+                if evs is not None:
+                    evs.append((torch.cuda.Event(enable_timing=True),
+                                torch.cuda.Event(enable_timing=True)))
+                    evs[-1][0].record(stream)
+                dw.attention()
+                if evs is not None:
+                    evs[-1][1].record(stream)
+                continue
+            dw.query_and_append()
+            if evs is not None:
+                evs.append((torch.cuda.Event(enable_timing=True),
+                            torch.cuda.Event(enable_timing=True)))
+                evs[-1][0].record(stream)
             dw.attention()
-            return
-        dw.query_and_append()
-        if ev is not None:
-            ev[0].record(stream)
-        dw.attention()
-        if ev is not None:
-            ev[1].record(stream)
-        dw.merge()
-        dw.absorb_out()
+            if evs is not None:
+                evs[-1][1].record(stream)
+            dw.merge()
+            dw.absorb_out()
 
     for i in range(args.warmup):
         one(i)
@@ -206,35 +251,39 @@ def main():
         one(i)
     torch.cuda.synchronize()
     step_s = (time.perf_counter() - t0) / args.steps
-    # timed region 2: the attention kernel alone, HIP events on its launch stream
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # timed region 2: the same steps, HIP events around every attention launch on
+    # its launch stream
+    evs = []
     for i in range(args.steps):
-        if args.attention_only:
-            evs[i][0].record(stream)
-            one(i)
-            evs[i][1].record(stream)
-        else:
-            one(i, evs[i])
+        one(i, evs)
     torch.cuda.synchronize()
-    attn_s = sum(a.elapsed_time(b) for a, b in evs) / args.steps / 1e3
+    attn_s = sum(a.elapsed_time(b) for a, b in evs) / len(evs) / 1e3
     assert M.mla_device_error() == 0
 
     B = w.batch
     achieved = cache_bytes / attn_s / 1e9
     tflops = attn_flop / attn_s / 1e12
+    kernel = attention_kernel(w)
     if w.chunk:     # prefill: the attention is a dense contraction; its bound is the MFMA rate
         roofline = {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": tflops / BF16_PEAK_TFLOPS, "traffic": None,
-                    "kernel": f"{attention_kernel(w)} (mla_prefill_attention)",
+                    "kernel": f"{kernel} (mla_prefill_attention)",
                     "algorithmic_flop_per_launch": attn_flop}
     else:
+        traffic = attention_traffic(kernel, w.name) if S == 4 else None
         roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": achieved / HBM_PEAK_GBPS,
-                    "traffic": attention_traffic(attention_kernel(w), w.name) if S == 4 else None,
-                    "kernel": attention_kernel(w) + (" (mla_decode_attention_fp8)" if w.cache == "fp8"
-                                                     else " (mla_decode_attention)"),
+                    "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                    "traffic_source": (f"profiles/{kernel}_{w.name}_traffic.json: rocprofv3 "
+                                       "FETCH_SIZE + WRITE_SIZE per launch, scaled by a plain-copy "
+                                       "calibration; valid while the kernel source hash matches"
+                                       if traffic is not None else None),
+                    "kernel": kernel + (" (mla_decode_attention_fp8)" if w.cache == "fp8"
+                                        else " (mla_decode_attention)"),
                     "algorithmic_bytes_per_launch": cache_bytes}
+    step_bytes = w.layers * (cache_bytes + weight_bytes)
+    layers = f"{w.layers} MLA decode layers" if w.layers > 1 else "one MLA decode layer"
+    ctx = (f"context {int(lens.max())}" if not w.ragged else
+           f"contexts log-uniform in [{w.ragged[0]}, {w.ragged[1]}] (mean {lens.mean():.0f})")
     line = {
         "metric": ("MLA chunked-prefill prompt tokens/s, n_h=128 d_c=512 1 GPU" if w.chunk else
                    "MLA decode tokens/s + latent-cache GB/s (% roofline), n_h=128 d_c=512 1 GPU"),
@@ -249,20 +298,28 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic (seeded, counter-based generator; random-init weights)",
-        "config": {"workload": f"{w.name}: one MLA decode layer, hidden {w.hidden}, n_h {w.n_heads}, "
+        "config": {"workload": f"{w.name}: {layers}, hidden {w.hidden}, n_h {w.n_heads}, "
                                f"d_h {w.d_head}, d_c {w.d_latent}, d_R {w.d_rope}, batch {B}, "
-                               f"context {int(lens.max())}, {S} KV splits, 64-token pages"
+                               f"{ctx}, {S} KV splits, 64-token pages"
                                + (f", query compression d_c' {w.d_cq}" if w.d_cq else "")
                                + (", FP8 latent pool (e4m3 c^KV + row scale, bf16 k^R)"
                                   if w.cache == "fp8" else "")
+                               + (f", YaRN RoPE (scale {w.yarn[0]:g}, original window "
+                                  f"{w.yarn[1]}, alpha {w.yarn[2]:g}, beta {w.yarn[3]:g})"
+                                  if w.yarn else "")
                                + (f", prefill of the last {w.chunk} positions of every sequence "
                                   f"({nq} prompt tokens per step)" if w.chunk else ""),
-                   "batch": B, "context": int(lens.max()), "num_splits": S},
+                   "batch": B, "context": int(lens.max()), "num_splits": S, "layers": w.layers},
         "latent_cache_GBps": achieved,
         "attention_us": attn_s * 1e6,
         "attention_mfma_tflops": tflops,
         "attention_mfma_frac": tflops / BF16_PEAK_TFLOPS,
         "roofline": roofline,
+        "step_roofline": {"bound": "hbm", "bytes_per_step": step_bytes,
+                          "what": "latent cache read by the attention plus every weight of the "
+                                  "layer(s), once per step",
+                          "achieved": step_bytes / step_s / 1e9, "peak": HBM_PEAK_GBPS,
+                          "unit": "GB/s", "frac": step_bytes / step_s / 1e9 / HBM_PEAK_GBPS},
     }
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

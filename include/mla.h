@@ -160,9 +160,10 @@ mla_status mla_absorb_q_append(const mla_dims* dims, const void* h, const void* 
  *   lse_part[b,s,i]   = log sum_{j in split} exp(s_ij)         (-inf if empty)
  *   o_part[b,s,i,:]   = sum_j exp(s_ij - lse_part) c_j          (0 if empty)
  *   q_lat [batch, n_h, d_c], q_pe [batch, n_h, d_R] fp32 (the matrix-core path
- *   -- bf16 dtype, n_h = 128, d_c = 512, d_R = 64, page_size = 64 -- rounds
- *   them to bf16 once per work unit, which bounds its score precision: a
- *   relative query error of up to 2^-8 per element); pool dtype;
+ *   -- bf16 dtype, n_h = 128 or 16, d_c = 512, d_R = 64, page_size = 64,
+ *   q_lat and q_pe 16-byte aligned -- rounds them to bf16 once per work unit,
+ *   which bounds its score precision: a relative query error of up to 2^-8 per
+ *   element); pool dtype;
  *   seq_lens [batch] int32 in [0, max_pages*page_size];
  *   o_part [batch, S, n_h, d_c] fp32; lse_part [batch, S, n_h] fp32.
  * num_splits in [1, 4096].

@@ -1238,17 +1238,317 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_f8mma_h128(
       o_out[(8 * (i >> 2) + 4 * g2 + (i & 3)) * kDc + 32 * nb + r32] = o[nb][i] * ilv[i];
 }
 
+
+// ---- 16 heads (the Lite shape) ---------------------------------------------
+// With n_h = 16 the heads fill one 16-wide MFMA dimension and the work per
+// cached token is an eighth of the 128-head kernel's, so the kernel is a pure
+// cache stream.  Work unit = (sequence, split) as above; its 4 waves stream
+// disjoint 16-token tiles (wave w takes tiles w, w+4, ...) through two LDS slots
+// each and never wait for one another inside the loop: a wave's copies land in
+// its own slots and it waits only on its own copy counter.  Per tile and wave:
+//   scores  S^T[t, h] = sum_k C[t, k] Q[h, k]: 18 mfma_f32_16x16x32_bf16
+//           (M = the tile's 16 tokens, N = the 16 heads, K = 576), A = tile
+//           rows from LDS, B = the queries (all 18 k-steps in VGPRs).  MFMA row
+//           t reads LDS row pi(t) (rows 4g..4g+3 of row group g taken from LDS
+//           row group (0, 2, 1, 3)[g]), which keeps both LDS reads below free
+//           of bank conflicts.
+//   softmax per head in the exp2 domain with a per-wave reference fixed at the
+//           wave's first tile (the single-reference scheme of the 128-head
+//           kernel: a unit's wave re-runs its tiles when a later score exceeds
+//           it by more than 2^64).
+//   P.C     O[h, d] += sum_t P[h, t] C[t, d]: 32 mfma_f32_16x16x16bf16_1k
+//           (M = heads, N = 16 columns, K = the 16 tokens).  A lane's score
+//           accumulator holds head lane & 15 and MFMA rows 4g..4g+3
+//           (g = lane >> 4), which is exactly the A operand; the B operand (4
+//           tokens of one column) is one ds_read_b64_tr_b16.
+// At the end the 4 waves' (reference, sum, O) are combined through LDS.
+// LDS slot (19,456 B): latent row r at 1088 r, 16-byte chunk c at
+// c ^ h16key(r); the 16 RoPE rows after them, row r at 128 r, chunk c' at
+// c' ^ rkey(r).
+constexpr int kH16Tok = 16;                                   // tokens per tile
+constexpr int kH16Slot = kH16Tok * kPitch + kH16Tok * 2 * kDr;  // 19456
+constexpr int kH16Copies = kH16Tok + 2;                       // per tile: rows, then 2 RoPE blocks
+constexpr int kH16Steps = (kDc + kDr) / 32;                   // 18 score k-steps
+constexpr int kH16Blocks = kDc / 16;                          // 32 output column blocks
+
+__device__ __forceinline__ int h16key(int r) { return 2 * ((r >> 2) & 1) ^ 3 * ((r >> 3) & 1); }
+__device__ __forceinline__ int h16row(int t) {   // LDS row of MFMA row t
+  return (((t >> 2) & 1) << 3) | (((t >> 3) & 1) << 2) | (t & 3);
+}
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h16(
+    AttnArgs a, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
+    const char* __restrict__ pool) {
+  __shared__ __attribute__((aligned(1024))) char ring[kWaves * 2 * kH16Slot];   // 155,648 B
+  __shared__ float wstate[kWaves][2][16];   // per wave: reference and sum of each head
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane & 15, g = lane >> 4;   // head (B/D column) and row group of this lane
+  const int S = a.num_splits;
+  const int unit = unit_of(blockIdx.x, a.batch * S);
+  const int b = unit / S, s = unit - b * S;
+  constexpr int nh = 16;
+
+  int sq, L;
+  unit_seq_len(seq_lens, a.q_seq, a.q_pos, a.n_seqs, a.max_pages * kPage, b, tid == 0, a.err, &sq,
+               &L);
+  sq = __builtin_amdgcn_readfirstlane(sq);
+  L = __builtin_amdgcn_readfirstlane(L);
+  int t0, t1;
+  split_range(L, S, s, kPage, &t0, &t1);
+  const int64_t ob = (static_cast<int64_t>(b) * S + s) * nh;
+  float* o_out = a.o_part + ob * kDc;
+  float* lse_out = a.lse_part + ob;
+  if (t0 >= t1) {   // empty split (uniform across the workgroup)
+    for (int e = tid; e < nh * kDc; e += kThreads) o_out[e] = 0.f;
+    if (tid < nh) lse_out[tid] = -INFINITY;
+    return;
+  }
+  const int32_t* bt = block_table + static_cast<int64_t>(sq) * a.max_pages;
+  const int ntiles = (t1 - t0 + kH16Tok - 1) / kH16Tok;
+  const int mine = ntiles > wv ? (ntiles - wv + kWaves - 1) / kWaves : 0;   // this wave's tiles
+
+  // queries as B fragments: head h, k = 32 ks + 8 g .. + 7, rounded to bf16
+  bf16x8_t qf[kH16Steps];
+  {
+    const float* ql = a.q_lat + (static_cast<int64_t>(b) * nh + h) * kDc;
+    const float* qp = a.q_pe + (static_cast<int64_t>(b) * nh + h) * kDr;
+#pragma unroll
+    for (int ks = 0; ks < kH16Steps; ++ks) {
+      const float* src = ks < kDc / 32 ? ql + 32 * ks + 8 * g : qp + 32 * (ks - kDc / 32) + 8 * g;
+      const float4 v0 = *reinterpret_cast<const float4*>(src);
+      const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
+      const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      qf[ks] = pack8(v);
+    }
+  }
+
+  const uint32_t slot0 = lds_addr(ring) + static_cast<uint32_t>(2 * kH16Slot) * wv;
+  // score A operand of MFMA row t = lane & 15 (LDS row h16row(t)), latent chunk
+  // 4 ks + g: aoff + 16 ((4 ks + g) ^ key); RoPE chunk 4 (ks - 16) + g: roff_r
+  const int ar = h16row(lane & 15);
+  const uint32_t aoff = kPitch * ar;
+  const int akey = h16key(ar);
+  uint32_t roff_r[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    roff_r[q] = kH16Tok * kPitch + 128 * ar + 16 * ((4 * q + g) ^ rkey(ar));
+  // P.C B operand (transposed read) of row group g, lane s16 = lane & 15: LDS row
+  // h16row(4 g + (s16 >> 2)), bytes 8 (s16 & 3) of column block nb's 32 bytes
+  const int s16 = lane & 15;
+  const int br = h16row(4 * g + (s16 >> 2));
+  const int bkey = h16key(br);
+  const uint32_t boff = kPitch * br + 8 * (s16 & 1);
+  const int bsub = (s16 & 3) >> 1;
+
+  const float cs = a.scale * kLog2e;
+  bool bad_page = false;
+
+  // page ids: t0 is page-aligned and a page holds 4 tiles, so this wave's tile u
+  // is the quarter wv of page t0/64 + u.  Lane i of `pwin` holds the id of page
+  // t0/64 + wbase + i (a window of 64 pages, reloaded when a tile is past it)
+  const int p0 = t0 / kPage, p_end = (t1 - 1) / kPage + 1;
+  int pwin = 0, wbase = -kPage;
+  auto page_of = [&](int u) {
+    if (u - wbase >= 64) {        // uniform; drains this wave's copies in flight
+      wbase = u;
+      const int pg = p0 + wbase + lane;
+      pwin = pg < p_end ? bt[pg] : 0;
+      wait_vmcnt<0>();
+    }
+    return __builtin_amdgcn_readlane(pwin, u - wbase);
+  };
+  // tile u of this wave (tokens t0 + 16 (wv + 4u) ..) into slot u & 1
+  auto issue = [&](int u) {
+    const int tok = t0 + kH16Tok * (wv + kWaves * u);
+    const int pg = page_of(u);
+    const bool ok = pg >= 0 && pg < a.num_pages;
+    bad_page |= !ok;
+    const int nvalid = ok ? min(kH16Tok, t1 - tok) : 0;
+    const uint64_t tile = reinterpret_cast<uint64_t>(
+        ok ? pool + (static_cast<int64_t>(pg) * kPage + (tok & (kPage - 1))) * kRowBytes : pool);
+    const uint32_t slot = slot0 + (u & 1) * kH16Slot;
+#pragma unroll
+    for (int r = 0; r < kH16Tok; ++r) {
+      const int rv = r < nvalid ? r : 0;
+      dma_block(tile, kRowBytes * rv + 16 * (lane ^ h16key(r)), slot + kPitch * r);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int rr = 8 * q + (lane >> 3);
+      const int rv = rr < nvalid ? rr : 0;
+      dma_block(tile, kRowBytes * rv + 2 * kDc + 16 * ((lane & 7) ^ rkey(rr)),
+                slot + kH16Tok * kPitch + 1024 * q);
+    }
+    return nvalid;
+  };
+
+  // O starts at zero also for a wave without tiles (its share is scaled by 0 below)
+  f32x4_t o[kH16Blocks];
+#pragma unroll
+  for (int nb = 0; nb < kH16Blocks; ++nb) o[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY, l_part = 0.f;
+  constexpr int kAAhead = 4, kARing = 6;    // score operands read ahead
+  constexpr int kBAhead = 6, kBRing = 8;    // P.C operands read ahead
+  for (int pass = 0; pass < 2 && mine > 0; ++pass) {
+    if (pass > 0) {
+#pragma unroll
+      for (int nb = 0; nb < kH16Blocks; ++nb) o[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    l_part = 0.f;
+    float seen = -INFINITY;
+    int nv0 = issue(0), nv1 = mine > 1 ? issue(1) : 0;
+    for (int u = 0; u < mine; ++u) {
+      if (u + 1 < mine) wait_vmcnt<kH16Copies>();
+      else wait_vmcnt<0>();
+      const uint32_t T = slot0 + (u & 1) * kH16Slot;
+      // scores of the tile: lane holds head h, MFMA rows 4g + i; operands read
+      // kAAhead steps ahead, waited for one by one
+      auto lda = [&](int ks) {
+        return ks < kDc / 32 ? lds_b128(T + aoff + 16 * ((4 * ks + g) ^ akey))
+                             : lds_b128(T + roff_r[ks - kDc / 32]);
+      };
+      bf16x8_t ar[kARing];
+#pragma unroll
+      for (int d = 0; d < kAAhead; ++d) ar[d] = lda(d);
+      f32x4_t x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kH16Steps; ++ks) {
+        if (ks + kAAhead < kH16Steps) ar[(ks + kAAhead) % kARing] = lda(ks + kAAhead);
+        wait_lgkm(min(kAAhead, kH16Steps - 1 - ks));
+        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar[ks % kARing], qf[ks], x, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // the P.C operands of the first blocks are read while the weights are formed
+      auto ldb = [&](int nb) { return lds_tr16(T + boff + 16 * ((2 * nb + bsub) ^ bkey)); };
+      s16x4_t bb[kBRing];
+#pragma unroll
+      for (int d = 0; d < kBAhead; ++d) bb[d] = ldb(d);
+      if (nv0 < kH16Tok) {   // rows past the split's end (or of an unusable page)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (h16row(4 * g + i) >= nv0) x[i] = -INFINITY;
+      }
+      if (pass == 0 && u == 0) {   // the wave's first tile fixes its reference
+        float tm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
+        tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+        m_ref = tm * cs;
+      }
+      const float mr = fmaxf(m_ref, -1e30f);
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        seen = fmaxf(seen, x[i]);
+        p[i] = __builtin_amdgcn_exp2f(fmaf(x[i], cs, -mr));
+      }
+      // P as bf16 (the A operand as it stands); the sum takes the rounded values
+      const unsigned w01 = cvt2(p[0], p[1]), w23 = cvt2(p[2], p[3]);
+      l_part += (__uint_as_float(w01 << 16) + __uint_as_float(w01 & 0xFFFF0000u)) +
+                (__uint_as_float(w23 << 16) + __uint_as_float(w23 & 0xFFFF0000u));
+      const u32x2_t pw = {w01, w23};
+      const s16x4_t pa = __builtin_bit_cast(s16x4_t, pw);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int nb = 0; nb < kH16Blocks; ++nb) {
+        if (nb + kBAhead < kH16Blocks) bb[(nb + kBAhead) % kBRing] = ldb(nb + kBAhead);
+        wait_lgkm(min(kBAhead, kH16Blocks - 1 - nb));
+        o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, bb[nb % kBRing], o[nb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // every read of this slot has returned (the last wait was lgkmcnt(0)): refill it
+      nv0 = nv1;
+      if (u + 2 < mine) nv1 = issue(u + 2);
+    }
+    // largest score of each head over this wave's tiles (log2 units)
+    seen = fmaxf(seen, __shfl_xor(seen, 16, 64));
+    seen = fmaxf(seen, __shfl_xor(seen, 32, 64));
+    seen *= cs;
+    // wave-uniform: the pass loop holds copies and matrix products, which must run
+    // with every lane active
+    if (__ballot(seen > m_ref + kHeadroom) == 0) break;
+    m_ref = seen;                // this wave runs its tiles again with its heads' maxima
+  }
+  if (bad_page) set_err(a.err, ERR_PAGE);
+
+  // ---- combine the 4 waves: common reference M_h per head, each wave's share of
+  // O scaled by 2^(m_w - M_h), summed per column by the wave that owns the column
+  // block; the normaliser and the lse are formed once per head
+  float lsum = l_part + __shfl_xor(l_part, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  const float mw = mine > 0 ? m_ref : -INFINITY;
+  __syncthreads();   // every wave's copies have landed and been read: the ring is free
+  if (g == 0) {
+    wstate[wv][0][h] = mw;
+    wstate[wv][1][h] = mine > 0 ? lsum : 0.f;
+  }
+  __syncthreads();
+  float mh = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) mh = fmaxf(mh, wstate[w][0][h]);
+  const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - mh);
+  if (wv == 0 && g == 0) {   // head h: 1 / sum_w l_w 2^(m_w - M) and the lse
+    float z = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float m = wstate[w][0][h];
+      if (m != -INFINITY) z += wstate[w][1][h] * __builtin_amdgcn_exp2f(m - mh);
+    }
+    wstate[0][1][h] = z > 0.f ? 1.f / z : 0.f;   // read back below (after the barrier)
+    lse_out[h] = z > 0.f ? (mh + __log2f(z)) * 0.6931471805599453f : -INFINITY;
+  }
+  // this wave's scaled O: head row hr at kRowW hr floats (padded: conflict-free writes)
+  constexpr int kRowW = kDc + 4;
+  float* stage = reinterpret_cast<float*>(ring) + wv * nh * kRowW;
+  float fh[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fh[i] = __shfl(f, 4 * g + i, 64);   // scale of head 4g + i
+#pragma unroll
+  for (int nb = 0; nb < kH16Blocks; ++nb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) stage[(4 * g + i) * kRowW + 16 * nb + s16] = o[nb][i] * fh[i];
+  __syncthreads();
+  // wave wv: columns 128 wv .. 128 wv + 127 of every head; step i covers head i / 2
+  const float* st_all = reinterpret_cast<const float*>(ring);
+#pragma unroll 4
+  for (int i = 0; i < 2 * nh; ++i) {
+    const int hr = i >> 1, c = 128 * wv + 64 * (i & 1) + lane;
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) acc += st_all[(w * nh + hr) * kRowW + c];
+    o_out[hr * kDc + c] = acc * wstate[0][1][hr];
+  }
+}
+
 }  // namespace
 
+// the matrix-core kernels read the fp32 queries 16 bytes at a time
+static bool queries_aligned(const AttnArgs& a) {
+  return ((reinterpret_cast<uintptr_t>(a.q_lat) | reinterpret_cast<uintptr_t>(a.q_pe)) & 15) == 0;
+}
+
 bool fast_attention_ok(const AttnArgs& a) {
-  return a.n_heads == 128 && a.d_latent == kDc && a.d_rope == kDr && a.page_size == kPage;
+  return a.n_heads == 128 && a.d_latent == kDc && a.d_rope == kDr && a.page_size == kPage &&
+         queries_aligned(a);
+}
+
+bool fast_attention_h16_ok(const AttnArgs& a) {
+  return a.n_heads == 16 && a.d_latent == kDc && a.d_rope == kDr && a.page_size == kPage &&
+         queries_aligned(a);
 }
 
 hipError_t launch_attention_fast(const AttnArgs& a, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
   const int units = a.batch * a.num_splits;
-  hipLaunchKernelGGL(k_attn_mfma_h128, dim3(units), dim3(kThreads), 0, stream, a, a.block_table,
-                     a.seq_lens, static_cast<const char*>(a.pool));
+  if (fast_attention_h16_ok(a))
+    hipLaunchKernelGGL(k_attn_mfma_h16, dim3(units), dim3(kThreads), 0, stream, a, a.block_table,
+                       a.seq_lens, static_cast<const char*>(a.pool));
+  else
+    hipLaunchKernelGGL(k_attn_mfma_h128, dim3(units), dim3(kThreads), 0, stream, a,
+                       a.block_table, a.seq_lens, static_cast<const char*>(a.pool));
   return hipGetLastError();
 }
 

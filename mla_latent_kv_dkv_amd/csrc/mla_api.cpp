@@ -315,7 +315,8 @@ mla_status attention_args(const mla_dims* d, bool prefill, const float* q_lat, c
 
 hipError_t launch_attention_plain(const mla_dims* d, const mla::AttnArgs& a, hipStream_t stream) {
   const bool bf16 = d->dtype == MLA_BF16;
-  if (use_fast() && bf16 && mla::fast_attention_ok(a)) return mla::launch_attention_fast(a, stream);
+  if (use_fast() && bf16 && (mla::fast_attention_ok(a) || mla::fast_attention_h16_ok(a)))
+    return mla::launch_attention_fast(a, stream);
   return mla::launch_attention_generic(a, bf16, stream);
 }
 

@@ -206,7 +206,7 @@ WEIGHT_NAMES = ("w_q", "w_qr", "w_dkv", "w_kr", "w_uk", "w_uv", "w_o")
 WORKLOADS = {
     "tiny": Workload("tiny", 64, 4, 16, 32, 8, "f32", 1, 64, 1001, num_splits=1,
                      permute_pages=False, cache_from_h=True),
-    "lite": Workload("lite", 2048, 16, 128, 512, 64, "bf16", 32, 4096, 1002, num_splits=2,
+    "lite": Workload("lite", 2048, 16, 128, 512, 64, "bf16", 32, 4096, 1002, num_splits=8,
                      cache_from_h=True),
     "full": Workload("full", 5120, 128, 128, 512, 64, "bf16", 64, 4096, 1003, num_splits=4),
     "long": Workload("long", 5120, 128, 128, 512, 64, "bf16", 4, 131072, 1004, num_splits=64),
@@ -215,7 +215,7 @@ WORKLOADS = {
     # the same shapes with the query's low-rank compression (d_c' = 1536 at full size)
     "tiny-cq": Workload("tiny-cq", 64, 4, 16, 32, 8, "f32", 1, 64, 1006, num_splits=1,
                         permute_pages=False, cache_from_h=True, d_cq=24),
-    "lite-cq": Workload("lite-cq", 2048, 16, 128, 512, 64, "bf16", 32, 4096, 1007, num_splits=2,
+    "lite-cq": Workload("lite-cq", 2048, 16, 128, 512, 64, "bf16", 32, 4096, 1007, num_splits=8,
                         cache_from_h=True, d_cq=512),
     "full-cq": Workload("full-cq", 5120, 128, 128, 512, 64, "bf16", 64, 4096, 1008, num_splits=4,
                         d_cq=1536),

@@ -79,10 +79,12 @@ def assert_partials_within_weight_rounding(got, ref, q_lat, q_pe, rows, length, 
 
 def attention_rounds_queries(w, path: int = 0) -> bool:
     """True when the decode attention of workload ``w`` runs on a matrix-core
-    kernel (kernel path 0, bf16 storage, n_h 128, d_c 512, d_R 64, 64-token
-    pages), which rounds q_lat and q_pe to bf16 once per work unit as
-    include/mla.h states; the vector kernels keep them in fp32."""
-    return (path == 0 and w.dtype == "bf16" and w.n_heads == 128 and w.d_latent == 512 and
+    kernel (kernel path 0, bf16 storage, n_h 128 or 16 -- 128 only for the FP8
+    pool --, d_c 512, d_R 64, 64-token pages), which rounds q_lat and q_pe to
+    bf16 once per work unit as include/mla.h states; the vector kernels keep
+    them in fp32."""
+    heads = (128,) if w.cache == "fp8" else (128, 16)
+    return (path == 0 and w.dtype == "bf16" and w.n_heads in heads and w.d_latent == 512 and
             w.d_rope == 64 and w.page_size == 64)
 
 

@@ -215,6 +215,10 @@ ATTN_CASES = [
     ("full", [3000, 130], 8, 64),
     ("full", [2], 5, 64),          # most splits empty
     ("full", [33000], 1, 64),      # one split over 516 pages: the kernel's page-id window reloads
+    # 16 heads: the Lite kernel (each wave its own 16-token tiles)
+    ("lite", [1, 65, 1000, 4096], 8, 64),
+    ("lite", [17, 33, 130], 5, 64),   # partial tiles, waves without tiles, empty splits
+    ("lite", [33000], 1, 64),         # one split: every wave streams 516 tiles
 ]
 
 
@@ -250,19 +254,20 @@ def test_decode_attention_partials(name, lens, S, page, path):
     assert M.mla_device_error() == 0
 
 
+@pytest.mark.parametrize("name", ["full", "lite"])
 @pytest.mark.parametrize("path", PATHS)
-def test_attention_skips_bad_page(path):
+def test_attention_skips_bad_page(path, name):
     """A table entry outside the pool is skipped (its tokens take no weight) and
     flagged in the error word.  The bad page is the first one of the split, so
     the MFMA kernel's first tile has no valid score."""
-    w = _wl("full", batch=1)
+    w = _wl(name, batch=1)
     M.mla_set_kernel_path(path)
     L = 200
     lens = np.array([L], dtype=np.int32)
     bt, total = I.page_table(w, lens)
     bad = bt.copy()
     bad[0, 0] = total + 7                                  # page 0 (tokens 0..63) is out of range
-    note(f"attention bad first page path={path}")
+    note(f"attention bad first page {name} path={path}")
     nh = w.n_heads
     q_lat = device_tensor(torch, w, "q_lat_in", (1, nh, w.d_latent), 0.5).float().contiguous()
     q_pe = device_tensor(torch, w, "q_pe_in", (1, nh, w.d_rope), 1.0).float().contiguous()

@@ -46,6 +46,8 @@ CASES = [
     ("full", (300, 77), 64, 2, [(0, 0), (0, 31), (0, 32), (0, 63), (0, 64), (0, 150), (0, 299),
                                 (1, 0), (1, 5), (1, 76)]),
     ("full", (2100,), 64, 3, [(0, 2099), (0, 1024), (0, 64), (0, 700)]),
+    ("lite", (300, 77), 64, 2, [(0, 0), (0, 15), (0, 16), (0, 63), (0, 64), (0, 299), (1, 5),
+                                (1, 76)]),
 ]
 
 

@@ -18,6 +18,19 @@ __device__ __forceinline__ void st_act(void* p, int64_t i, float v, int f32) {
   if (f32) static_cast<float*>(p)[i] = v; else st(static_cast<T*>(p) + i, v);
 }
 
+// cos/sin of the RoPE angle (pos, pair k) of output row m: from the table when
+// the caller computed one, else evaluated here.
+__device__ __forceinline__ void rope_row(const GemmArgs& a, int m, int pos, int k, float* c,
+                                         float* s) {
+  if (a.rope_tab) {
+    const float2 t = *reinterpret_cast<const float2*>(a.rope_tab + 2 * (m * (a.d_rope / 2) + k));
+    *c = t.x;
+    *s = t.y;
+  } else {
+    rope_cs(pos, k, a.d_rope, a.rope, c, s);
+  }
+}
+
 // Latent-append columns (n even) of row m: [c | RoPE(k^R, row_pos[m])] into
 // the pool slot of (row_seq[m], row_pos[m]); pool, c/k^R split given.
 template <typename T>
@@ -37,7 +50,7 @@ __device__ __forceinline__ void append_pair(const GemmArgs& a, void* pool, int s
   } else {
     const int k = (n - split) >> 1;
     float c, s;
-    rope_cs(pos, k, a.d_rope, a.rope, &c, &s);
+    rope_row(a, m, pos, k, &c, &s);
     st(row + n, v0 * c - v1 * s);
     st(row + n + 1, v0 * s + v1 * c);
   }
@@ -66,7 +79,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, int z, int m, i
       const int r = n - a.n_split;              // column within q_pe row
       const int k = (r % a.d_rope) >> 1;       // pair index within the head
       float c, s;
-      rope_cs(a.pos[m], k, a.d_rope, a.rope, &c, &s);
+      rope_row(a, m, a.pos[m], k, &c, &s);
       const int qpe_w = (a.epi == EPI_QPROJ_APPEND ? a.n_append : a.N) - a.n_split;
       float* y2 = static_cast<float*>(a.y2) + static_cast<int64_t>(m) * qpe_w;
       y2[r] = v0 * c - v1 * s;

@@ -30,6 +30,7 @@
 #include "common.hpp"
 #include "epilogue.hpp"
 #include "launch_fast.hpp"
+#include "lds_copy.hpp"
 
 namespace mla {
 namespace {
@@ -221,21 +222,40 @@ __global__ __launch_bounds__(256) void k_gemm_ws(GemmArgs a, int ntiles, int ksp
   }
 }
 
+// cos/sin of the RoPE angles of the output rows, (pos[m], pair k) at
+// rope_tab[2 (m d_R/2 + k)], computed once per call by the K-split weight stream
+// (strided over the grid's threads) for its output stage in k_gemm_finish_xs,
+// which would otherwise evaluate them once per head.
+__device__ __forceinline__ void rope_table_fill(const GemmArgs& a, int e0, int stride) {
+  if (a.rope_tab == nullptr) return;
+  for (int e = e0; e < a.M * (a.d_rope / 2); e += stride) {
+    const int m = e / (a.d_rope / 2), k = e - m * (a.d_rope / 2);
+    float c, sn;
+    rope_cs(a.pos[m], k, a.d_rope, a.rope, &c, &sn);
+    a.rope_tab[2 * e] = c;
+    a.rope_tab[2 * e + 1] = sn;
+  }
+}
+
 // ---- X-stationary weight stream (one K slice of X held in LDS per workgroup) ----
 // For one activation matrix (batch 1, M <= 64) the grid is one workgroup per CU;
 // workgroup w owns K slice w % d and keeps X[:, slice] in LDS for its whole
 // life, so after a one-time load the loop issues only weight loads: no X
 // traffic and no barriers.  Its kXsWaves waves walk 16-row weight strips (strip
-// s of the slice goes to wave s mod (kXsWaves G/d)), one strip after another with a
-// kXsRing-deep load ring that runs across strip boundaries, and write each
+// s of the slice goes to wave s mod (kXsWaves G/d)), one strip after another with an
+// R-deep load ring that runs across strip boundaries, and write each
 // strip's result (or fp32 partial when d > 1) as soon as it is done.
 // X layout in LDS: row r at 2 kw r bytes, 16-byte chunk c at c ^ 2(r & 7): the
-// 16-row B-operand reads are bank-conflict free.
-constexpr int kXsLdsBytes = 128 * 1024;
-constexpr int kXsRing = 16;
+// 16-row B-operand reads are bank-conflict free.  A bf16 X slice arrives by
+// asynchronous copies (1 KB per wave instruction, all of them in flight at once);
+// an fp32 X is converted in registers on the way.
+constexpr int kXsLdsBytes = 128 * 1024;   // the largest X slice
 constexpr int kXsWaves = 4;                     // waves per workgroup
 
-template <typename XT, int MB>
+// kSplit (d > 1): the strip results are fp32 partials, and the instance holds no
+// output-stage code at all (the compiler would otherwise evaluate parts of it,
+// such as the RoPE angles, on every strip end before testing d).
+template <typename XT, int MB, int R, bool kSplit>
 __global__ __launch_bounds__(64 * kXsWaves, 1) void k_gemm_xs(GemmArgs a, int d, int kw,
                                                                float* partial) {
   extern __shared__ __attribute__((aligned(16))) char xs[];
@@ -266,27 +286,48 @@ __global__ __launch_bounds__(64 * kXsWaves, 1) void k_gemm_xs(GemmArgs a, int d,
     return base + static_cast<int64_t>(n16) * a.ldw_n + kbeg + 8 * g;
   };
   const int total = my * nsteps;   // steps of this wave over all its strips
-  bf16x8_t wr[kXsRing];
+  bf16x8_t wr[R];
   if (my > 0) {
     const bf16_t* p0 = wrow(0);
 #pragma unroll
-    for (int u = 0; u < kXsRing; ++u) wr[u] = ld8(p0 + 32 * min(u, nsteps - 1));
+    for (int u = 0; u < R; ++u) wr[u] = ld8(p0 + 32 * min(u, nsteps - 1));
   }
 
   // X slice -> LDS (rows past M repeat row 0; their outputs are never stored)
-  {
+  if constexpr (std::is_same<XT, bf16_t>::value) {
+    // LDS block j (1 KB) is one copy: lane l fills bytes 1024 j + 16 l, i.e. row
+    // r, stored chunk cs, which holds source chunk cs ^ 2(r & 7)
+    const int nblk = 16 * MB * rowb / 1024;
+    const uint64_t xg = reinterpret_cast<uint64_t>(static_cast<const bf16_t*>(a.x) + kbeg);
+    const uint32_t x0 = lds_addr(xs);
+    for (int j = wv; j < nblk; j += kXsWaves) {
+      const int byte = 1024 * j + 16 * lane;
+      const int r = byte / rowb, cs = (byte - r * rowb) >> 4;
+      const uint32_t voff = static_cast<uint32_t>(
+          (static_cast<int64_t>(r < a.M ? r : 0) * a.ldx_m + 8 * (cs ^ (2 * (r & 7)))) * 2);
+      dma_block(xg, voff, x0 + 1024 * j);
+    }
+    wait_vmcnt<0>();
+    lds_barrier();
+  } else {
     const int cpr = kw / 8;   // 16-byte chunks per row
     const XT* xb = static_cast<const XT*>(a.x) + kbeg;
-#pragma unroll 4
+#pragma unroll 8
     for (int v = tid; v < 16 * MB * cpr; v += 64 * kXsWaves) {
       const int r = v / cpr, c = v - r * cpr;
       XVec<XT> t;
       t.load(xb + static_cast<int64_t>(r < a.M ? r : 0) * a.ldx_m + 8 * c);
       *reinterpret_cast<u32x4_t*>(&xs[r * rowb + 16 * (c ^ (2 * (r & 7)))]) = t.bits();
     }
+    __syncthreads();
   }
-  __syncthreads();
-  if (my == 0) return;
+  // the RoPE table (split instances): entry blockIdx + grid * tid, once the
+  // thread's strips are done (the fp64 angles would otherwise stall the stream)
+  const int tab_e = blockIdx.x + gridDim.x * tid, tab_stride = gridDim.x * 256;
+  if (my == 0) {
+    if constexpr (kSplit) rope_table_fill(a, tab_e, tab_stride);
+    return;
+  }
 
   // B operand of block mb at step st: row 16mb + n16, chunk 4st + g (swizzled)
   uint32_t xoff[4];
@@ -305,21 +346,21 @@ __global__ __launch_bounds__(64 * kXsWaves, 1) void k_gemm_xs(GemmArgs a, int d,
   };
   bf16x8_t xc[MB];   // B operands of the current step, read one step ahead
   ldx(0, 0, xc);
-  for (int t0 = 0; t0 < total; t0 += kXsRing) {
+  for (int t0 = 0; t0 < total; t0 += R) {
     // the group t0..t0+R-1 lies in strip t0 / nsteps (nsteps is a multiple of R);
     // its refills target the next group, in strip (t0+R) / nsteps (the last strip
     // re-read past the end, so the body stays branch-free)
     const int st0 = t0 % nsteps;
-    const int pt = min(t0 + kXsRing, total - 1);
+    const int pt = min(t0 + R, total - 1);
     const bf16_t* pp = wrow(pt / nsteps) + 32 * (pt % nsteps);
     const int plim = total - 1 - pt;   // refills past this re-read pt
-    // st0 is a multiple of kXsRing: step st0 + u has q = u & 3, j = st0/4 + u/4
+    // st0 is a multiple of R: step st0 + u has q = u & 3, j = st0/4 + u/4
     const int j0 = st0 >> 2;
-    const int jn = st0 + kXsRing == nsteps ? 0 : j0 + kXsRing / 4;   // first step of the next group
+    const int jn = st0 + R == nsteps ? 0 : j0 + R / 4;   // first step of the next group
 #pragma unroll
-    for (int u = 0; u < kXsRing; ++u) {
+    for (int u = 0; u < R; ++u) {
       bf16x8_t xn[MB];
-      if (u + 1 < kXsRing) ldx((u + 1) & 3, j0 + ((u + 1) >> 2), xn);
+      if (u + 1 < R) ldx((u + 1) & 3, j0 + ((u + 1) >> 2), xn);
       else ldx(0, jn, xn);
       __builtin_amdgcn_sched_barrier(0);   // the reads go out a whole step before their use
 #pragma unroll
@@ -332,24 +373,27 @@ __global__ __launch_bounds__(64 * kXsWaves, 1) void k_gemm_xs(GemmArgs a, int d,
       wr[u] = ld8(pp + 32 * min(u, plim));
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (st0 + kXsRing == nsteps) {   // strip done: lane (n16, g) holds rows n0 + 4g + e, X row 16mb + n16
-      const int n = 16 * (wave + (t0 / nsteps) * nwaves) + 4 * g;
+    if (st0 + R == nsteps) {   // strip done: lane (n16, g) holds rows n0 + 4g + e, X row 16mb + n16
+      const int strip = wave + (t0 / nsteps) * nwaves;
+      const int n = 16 * strip + 4 * g;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const int m = 16 * mb + n16;
         if (m < a.M) {
-          if (d == 1) {
+          if constexpr (!kSplit) {
             gemm_epilogue<bf16_t>(a, 0, m, n, acc[mb][0], acc[mb][1]);
             gemm_epilogue<bf16_t>(a, 0, m, n + 2, acc[mb][2], acc[mb][3]);
           } else {
-            *reinterpret_cast<f32x4_t*>(partial + (static_cast<int64_t>(ks) * a.M + m) * a.N + n) =
-                acc[mb];
+            // partial tile of (slice, strip): [16 MB rows m][16 columns], 1 KB per block
+            float* tile = partial + (static_cast<int64_t>(ks) * nstrips + strip) * (256 * MB);
+            *reinterpret_cast<f32x4_t*>(tile + 16 * m + 4 * g) = acc[mb];
           }
         }
         acc[mb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
       }
     }
   }
+  if constexpr (kSplit) rope_table_fill(a, tab_e, tab_stride);
 }
 
 // Sum of the K-split partials (fixed order) followed by the output stage; each
@@ -377,6 +421,36 @@ __global__ __launch_bounds__(256) void k_gemm_finish(GemmArgs a, int ksplit, con
     const int zb = static_cast<int>(row / static_cast<uint32_t>(a.M));
     gemm_epilogue<bf16_t>(a, zb, m, n, v.x, v.y);
     gemm_epilogue<bf16_t>(a, zb, m, n + 2, v.z, v.w);
+  }
+}
+
+// Sum of the K-split partial tiles of k_gemm_xs (fixed order) followed by the
+// output stage.  Thread q takes 4 columns of one row: strip q / (4 M), row
+// (q / 4) mod M, columns 4 (q mod 4)..+3 of the strip, so that a wave reads
+// whole 1 KB pieces of a tile.
+__global__ __launch_bounds__(256) void k_gemm_finish_xs(GemmArgs a, int ksplit, int rows_pad,
+                                                        const float* partial) {
+  const uint32_t per_strip = static_cast<uint32_t>(a.M) * 4;
+  const uint32_t nstrips = static_cast<uint32_t>(a.N) / 16;
+  const uint32_t quads = nstrips * per_strip;
+  const int64_t plane = static_cast<int64_t>(nstrips) * rows_pad * 16;   // one slice
+  for (uint32_t q = blockIdx.x * blockDim.x + threadIdx.x; q < quads; q += blockDim.x * gridDim.x) {
+    const uint32_t strip = q / per_strip, r = q - strip * per_strip;
+    const int m = static_cast<int>(r >> 2), g = static_cast<int>(r & 3);
+    const float* src = partial + static_cast<int64_t>(strip) * rows_pad * 16 + 16 * m + 4 * g;
+    float4 v = *reinterpret_cast<const float4*>(src);
+    for (int s0 = 1; s0 < ksplit; s0 += 8) {   // eight partials in flight, summed in slice order
+      float4 t[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (s0 + j < ksplit) t[j] = *reinterpret_cast<const float4*>(src + (s0 + j) * plane);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (s0 + j < ksplit) { v.x += t[j].x; v.y += t[j].y; v.z += t[j].z; v.w += t[j].w; }
+    }
+    const int n = 16 * static_cast<int>(strip) + 4 * g;
+    gemm_epilogue<bf16_t>(a, 0, m, n, v.x, v.y);
+    gemm_epilogue<bf16_t>(a, 0, m, n + 2, v.z, v.w);
   }
 }
 
@@ -664,24 +738,6 @@ hipError_t launch_finish(const GemmArgs& a, int d, const float* partial, hipStre
   return hipGetLastError();
 }
 
-struct XsPlan {
-  int mb, d, kw;
-};
-
-XsPlan xs_plan(const GemmArgs& a) {
-  XsPlan p{};
-  p.mb = a.M <= 16 ? 1 : a.M <= 32 ? 2 : 4;
-  // slices are whole groups of 32 * kXsRing k (a strip's steps fill whole ring turns)
-  constexpr int kUnit = 32 * kXsRing;
-  const int kw_max = kXsLdsBytes / (2 * 16 * p.mb) / kUnit * kUnit;
-  const int groups = a.K / kUnit;
-  p.d = groups;
-  for (int d = 1; d <= groups; ++d)
-    if (groups % d == 0 && a.K / d <= kw_max) { p.d = d; break; }
-  p.kw = a.K / p.d;
-  return p;
-}
-
 int cu_count() {
   static std::atomic<int> cached{0};
   int v = cached.load(std::memory_order_relaxed);
@@ -695,19 +751,77 @@ int cu_count() {
   return prop.multiProcessorCount;
 }
 
-template <typename XT, int MB>
-hipError_t launch_xs_inst(const GemmArgs& a, const XsPlan& p, float* partial, hipStream_t stream) {
+constexpr int kXsRing = 8;   // weight loads in flight per lane
+
+struct XsPlan {
+  int mb, d, kw;
+};
+
+// K slices d: the fewest whole groups of 32 kXsRing k (a strip's steps fill
+// whole ring turns) whose X slice fits kXsLdsBytes.  The plan depends on M and
+// K only, so the fused query projection + latent append takes the same slices,
+// and produces the same queries bit for bit, as the query projection alone.
+// (At 64 rows: 5 slices of 1024 for K = 5120, where the 1572 strips of the fused
+// call come to 7.7 per wave against a busiest wave's 8, and 16 slices for
+// K = 16384.)
+XsPlan xs_plan(const GemmArgs& a) {
+  XsPlan p{};
+  p.mb = a.M <= 16 ? 1 : a.M <= 32 ? 2 : 4;
+  constexpr int kUnit = 32 * kXsRing;
+  const int kw_max = kXsLdsBytes / (2 * 16 * p.mb) / kUnit * kUnit;
+  const int groups = a.K / kUnit;
+  p.d = groups;
+  for (int d = 1; d <= groups; ++d)
+    if (groups % d == 0 && a.K / d <= kw_max) {
+      p.d = d;
+      break;
+    }
+  p.kw = a.K / p.d;
+  return p;
+}
+
+template <typename XT, int MB, bool kSplit>
+hipError_t launch_xs_kernel(const GemmArgs& a, const XsPlan& p, float* partial, hipStream_t stream) {
   static std::atomic<int> attr_set{0};
   if (!attr_set.load(std::memory_order_acquire)) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_xs<XT, MB>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             kXsLdsBytes);
+    const hipError_t e =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_xs<XT, MB, kXsRing, kSplit>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kXsLdsBytes);
     if (e != hipSuccess) return e;
     attr_set.store(1, std::memory_order_release);
   }
   const int grid = std::max(1, cu_count() / p.d) * p.d;
   const size_t lds = static_cast<size_t>(16 * MB) * p.kw * 2;
-  hipLaunchKernelGGL((k_gemm_xs<XT, MB>), dim3(grid), dim3(64 * kXsWaves), lds, stream, a, p.d, p.kw,
+  hipLaunchKernelGGL((k_gemm_xs<XT, MB, kXsRing, kSplit>), dim3(grid), dim3(64 * kXsWaves), lds,
+                     stream, a, p.d, p.kw, partial);
+  return hipGetLastError();
+}
+
+template <typename XT, int MB>
+hipError_t launch_xs_inst(const GemmArgs& a, const XsPlan& p, float* partial, hipStream_t stream) {
+  return p.d > 1 ? launch_xs_kernel<XT, MB, true>(a, p, partial, stream)
+                 : launch_xs_kernel<XT, MB, false>(a, p, partial, stream);
+}
+
+// K-split partial tiles of k_gemm_xs: d slices x N/16 strips x [16 mb rows][16]
+size_t xs_tiles_bytes(const GemmArgs& a, const XsPlan& p) {
+  return static_cast<size_t>(p.d) * (a.N / 16) * (256 * p.mb) * sizeof(float);
+}
+
+// the RoPE cos/sin table behind the tiles (output stages that rotate)
+bool epi_rotates(const GemmArgs& a) {
+  return a.epi == EPI_QPROJ || a.epi == EPI_QPROJ_APPEND || a.epi == EPI_APPEND;
+}
+size_t xs_rope_bytes(const GemmArgs& a) {
+  return epi_rotates(a) ? static_cast<size_t>(a.M) * a.d_rope * sizeof(float) : 0;
+}
+
+hipError_t launch_finish_xs(const GemmArgs& a, const XsPlan& p, const float* partial,
+                            hipStream_t stream) {
+  const int64_t quads = static_cast<int64_t>(a.N / 16) * a.M * 4;
+  const int threads = quads < 65536 ? 64 : 256;
+  const int blocks = static_cast<int>(std::min<int64_t>((quads + threads - 1) / threads, 8192));
+  hipLaunchKernelGGL(k_gemm_finish_xs, dim3(blocks), dim3(threads), 0, stream, a, p.d, 16 * p.mb,
                      partial);
   return hipGetLastError();
 }
@@ -754,8 +868,10 @@ static bool xs_ok(const GemmArgs& a) {
       !(a.n_append % 16 == 0 && a.n_split3 % 16 == 0 && a.n_split < a.n_append &&
         aligned16(a.w3) && aligned16(a.w4)))
     return false;
+  // (the asynchronous X copies address X with 32-bit byte offsets)
   return ws_ok(a) && a.batch == 1 && a.M <= 64 && a.N >= 2048 && a.N % 16 == 0 &&
-         (a.n_split % 16 == 0 || a.n_split >= a.N) && a.K % (32 * kXsRing) == 0;
+         (a.n_split % 16 == 0 || a.n_split >= a.N) && a.K % (32 * kXsRing) == 0 &&
+         (static_cast<int64_t>(a.M) * a.ldx_m + a.K) * 4 < (int64_t{1} << 31);
 }
 
 // The fused query projection + latent append runs only on k_gemm_xs.
@@ -784,7 +900,7 @@ size_t gemm_partial_bytes(const GemmArgs& a) {
   if (!ws_ok(a) || tile_ok(a) || small_tile_ok(a)) return 0;
   if (xs_ok(a)) {
     const XsPlan q = xs_plan(a);
-    return q.d > 1 ? static_cast<size_t>(q.d) * a.M * a.N * sizeof(float) : 0;
+    return q.d > 1 ? xs_tiles_bytes(a, q) + xs_rope_bytes(a) : 0;
   }
   const WsPlan p = ws_plan(a);
   return p.d > 1 ? static_cast<size_t>(p.d) * a.batch * a.M * a.N * sizeof(float) : 0;
@@ -824,9 +940,15 @@ hipError_t launch_gemm_fast(const GemmArgs& a, void* partial, size_t partial_byt
     if (q.d > 1 && (partial == nullptr || !aligned16(partial) ||
                     partial_bytes < gemm_partial_bytes(a)))
       return hipErrorInvalidValue;
-    hipError_t e = launch_xs(a, q, static_cast<float*>(partial), stream);
-    if (e != hipSuccess || q.d == 1) return e;
-    return launch_finish(a, q.d, static_cast<const float*>(partial), stream);
+    if (q.d == 1) return launch_xs(a, q, nullptr, stream);
+    // both kernels take the RoPE angles from the table behind the partial tiles
+    GemmArgs b = a;
+    b.rope_tab = epi_rotates(a) ? reinterpret_cast<float*>(static_cast<char*>(partial) +
+                                                           xs_tiles_bytes(a, q))
+                                : nullptr;
+    hipError_t e = launch_xs(b, q, static_cast<float*>(partial), stream);
+    if (e != hipSuccess) return e;
+    return launch_finish_xs(b, q, static_cast<const float*>(partial), stream);
   }
   const WsPlan p = ws_plan(a);
   if (p.d > 1 && (partial == nullptr || !aligned16(partial) ||

@@ -38,6 +38,7 @@ struct GemmArgs {
   void* y2;         // EPI_QPROJ: q_pe [M, N - n_split], fp32
   int d_rope;       // EPI_APPEND / EPI_QPROJ: rope width (pairs restart every d_rope columns)
   RopeSpec rope;    // RoPE frequencies (EPI_APPEND / EPI_QPROJ)
+  float* rope_tab;  // optional cos/sin of the rows' RoPE angles, [M][d_rope/2][2] (else computed)
   const int32_t* pos;      // EPI_APPEND: row_pos; EPI_QPROJ: decode positions
   const int32_t* row_seq;  // EPI_APPEND
   const int32_t* block_table;

@@ -41,6 +41,7 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kTile = 64;        // X rows per W_UK workgroup
 constexpr int kWsWaves = 4;
@@ -545,6 +546,234 @@ __global__ __launch_bounds__(256) void k_gemm_uk(GemmArgs a) {
   }
 }
 
+// ---- the same product for an fp32 X, with asynchronous copies ---------------
+// Workgroup = (head, NW columns c, 64 rows b): the W tile [128 d x NW c] and the
+// fp32 X tile [64 b x 128 d] (32 KB) arrive by asynchronous copies of 1 KB, all
+// in flight at once, and the output tile leaves through the same LDS as whole
+// rows.  LDS layouts (16-byte chunks swizzled so that no read phase puts two
+// addresses on one bank):
+//   W: row d at 2 NW d, chunk q (8 columns) at q ^ 4(d & 3); A fragments by
+//      transposed reads, four rows by four column quads per 16-lane group
+//   X: row b at 512 b, chunk q (4 values) at q ^ (b & 15); B fragments as two
+//      16-byte reads per lane, split into hi + lo bf16 terms
+//   Y: row b at 4 NW b, chunk q (4 columns) at q ^ (b & 15)
+// Wave w computes the NW / 128 column tiles (32 columns each) from 32 NW w / 128
+// for both 32-row halves of b.  NW = 128 keeps two workgroups on a CU (64 KB of
+// LDS each), so that one's copies overlap the other's products and stores.
+constexpr int kUwM = 64;
+__device__ __forceinline__ s16x4_t lds_tr16_u(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<__attribute__((address_space(3))) s16x4_t*>(static_cast<uintptr_t>(addr)));
+}
+__device__ __forceinline__ u32x4_t lds_u128(uint32_t addr) {
+  return *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(static_cast<uintptr_t>(addr));
+}
+__device__ __forceinline__ void lds_st128(uint32_t addr, u32x4_t v) {
+  *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(static_cast<uintptr_t>(addr)) = v;
+}
+
+template <int NW>
+__global__ __launch_bounds__(256, 2) void k_gemm_uk_wide(GemmArgs a) {
+  constexpr int kWRow = 2 * NW, kWBytes = kUkK * kWRow, kCT = NW / 128;
+  constexpr int kYRow = 4 * NW;
+  static_assert(kUwM * kYRow <= kWBytes, "output staging fits the W region");
+  __shared__ __attribute__((aligned(1024))) char lds[kWBytes + kUwM * 512];   // W, then X
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int head = blockIdx.x, c0 = blockIdx.y * NW, m0 = blockIdx.z * kUwM;
+  const uint32_t wl = lds_addr(lds), xl = wl + kWBytes;
+
+  // ---- copies: 1 KB blocks; W block j = rows (1024 / kWRow) j .., X block j = rows 2j, 2j+1
+  {
+    const uint64_t wg = reinterpret_cast<uint64_t>(static_cast<const bf16_t*>(a.w1) +
+                                                   head * a.w_bs + c0);
+    const uint64_t xg = reinterpret_cast<uint64_t>(static_cast<const float*>(a.x) +
+                                                   head * a.x_bs + static_cast<int64_t>(m0) * a.ldx_m);
+    constexpr int kQW = NW / 8;   // 16-byte chunks per W row
+    for (int j = wv; j < kWBytes / 1024; j += 4) {
+      const int byte = 1024 * j + 16 * lane;
+      const int d = byte / kWRow, qs = (byte % kWRow) >> 4;
+      const uint32_t voff = static_cast<uint32_t>((static_cast<int64_t>(d) * a.ldw_k +
+                                                   8 * (qs ^ (4 * (d & 3)))) * 2);
+      dma_block(wg, voff, wl + 1024 * j);
+      static_assert(kQW % 16 == 0, "swizzle stays inside a row");
+    }
+    for (int j = wv; j < kUwM / 2; j += 4) {
+      const int b = 2 * j + (lane >> 5), qs = lane & 31;
+      const int br = m0 + b < a.M ? b : a.M - 1 - m0;   // rows past M repeat the last one
+      const uint32_t voff = static_cast<uint32_t>((static_cast<int64_t>(br) * a.ldx_m +
+                                                   4 * (qs ^ (b & 15))) * 4);
+      dma_block(xg, voff, xl + 1024 * j);
+    }
+    wait_vmcnt<0>();
+    lds_barrier();
+  }
+
+  // ---- products: acc[ct][mt], column tile kCT wv + ct, row half mt
+  const int i16 = lane & 15, G = lane >> 4, j32 = lane & 31, g = lane >> 5;
+  f32x16_t acc[kCT][2];
+#pragma unroll
+  for (int ct = 0; ct < kCT; ++ct)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[ct][mt][e] = 0.f;
+#pragma unroll 2
+  for (int s = 0; s < kUkK / 16; ++s) {
+    // A (W^T): lane group G: columns +16(G & 1) + 4(i16 & 3), rows 16s + 8(G >> 1) + (i16 >> 2) (+4)
+    bf16x8_t af[kCT];
+#pragma unroll
+    for (int ct = 0; ct < kCT; ++ct) {
+      const int col = 32 * (kCT * wv + ct) + 16 * (G & 1) + 4 * (i16 & 3);
+      const int d = 16 * s + 8 * (G >> 1) + (i16 >> 2);
+      const int q = col >> 3, h8 = 8 * ((col >> 2) & 1);
+      const s16x4_t v0 = lds_tr16_u(wl + kWRow * d + 16 * (q ^ (4 * (d & 3))) + h8);
+      const s16x4_t v1 = lds_tr16_u(wl + kWRow * (d + 4) + 16 * (q ^ (4 * ((d + 4) & 3))) + h8);
+      const s16x4_t vv[2] = {v0, v1};
+      af[ct] = __builtin_bit_cast(bf16x8_t, vv);
+    }
+    // B (X^T): lane (row 32mt + j32, k group g): values 16s + 8g .. +7 as hi + lo
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int b = 32 * mt + j32;
+      const int q = 4 * s + 2 * g;
+      const u32x4_t x0 = lds_u128(xl + 512 * b + 16 * (q ^ (b & 15)));
+      const u32x4_t x1 = lds_u128(xl + 512 * b + 16 * ((q + 1) ^ (b & 15)));
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = __uint_as_float(x0[e]);
+        v[4 + e] = __uint_as_float(x1[e]);
+      }
+      const u32x4_t hi = {cvt2(v[0], v[1]), cvt2(v[2], v[3]), cvt2(v[4], v[5]), cvt2(v[6], v[7])};
+      float rl[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        rl[2 * e] = v[2 * e] - __uint_as_float(hi[e] << 16);
+        rl[2 * e + 1] = v[2 * e + 1] - __uint_as_float(hi[e] & 0xFFFF0000u);
+      }
+      const u32x4_t lo = {cvt2(rl[0], rl[1]), cvt2(rl[2], rl[3]), cvt2(rl[4], rl[5]),
+                          cvt2(rl[6], rl[7])};
+#pragma unroll
+      for (int ct = 0; ct < kCT; ++ct) {
+        acc[ct][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ct], __builtin_bit_cast(bf16x8_t, hi),
+                                                              acc[ct][mt], 0, 0, 0);
+        acc[ct][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ct], __builtin_bit_cast(bf16x8_t, lo),
+                                                              acc[ct][mt], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- output: stage in the W region (every wave done with it), then whole rows
+  __syncthreads();
+  // acc[ct][mt] lane (j32, g): columns 32(kCT wv + ct) + 8(e >> 2) + 4g + (e & 3), row 32mt + j32
+#pragma unroll
+  for (int ct = 0; ct < kCT; ++ct)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int b = 32 * mt + j32;
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int q = (32 * (kCT * wv + ct) + 8 * e4 + 4 * g) >> 2;
+        const u32x4_t v = {__float_as_uint(acc[ct][mt][4 * e4]), __float_as_uint(acc[ct][mt][4 * e4 + 1]),
+                           __float_as_uint(acc[ct][mt][4 * e4 + 2]), __float_as_uint(acc[ct][mt][4 * e4 + 3])};
+        lds_st128(wl + kYRow * b + 16 * (q ^ (b & 15)), v);
+      }
+    }
+  __syncthreads();
+  // one 1 KB store per wave instruction: rows 1024 / kYRow at a time
+  float* y = static_cast<float*>(a.y) + head * a.y_bs + c0;
+  constexpr int kRowsPer = 1024 / kYRow, kLanesRow = kYRow / 16;
+  for (int r0 = kRowsPer * wv; r0 < kUwM; r0 += 4 * kRowsPer) {
+    const int b = r0 + lane / kLanesRow, q = lane % kLanesRow;
+    if (m0 + b < a.M) {
+      const u32x4_t v = lds_u128(wl + kYRow * b + 16 * (q ^ (b & 15)));
+      *reinterpret_cast<u32x4_t*>(y + static_cast<int64_t>(m0 + b) * a.ldy + 4 * q) = v;
+    }
+  }
+}
+
+constexpr int kUwN = 256;   // columns per workgroup of the fp32-X W_UK product
+
+// ---- per-head o[b, i, d] = sum_c X[b, i, c] W_UV[i*d_h + d, c], fp32 X ---------
+// (the absorbed output's first product: X = o_lat, K = d_c = 512, N = d_h.)
+// Workgroup = (head, 64 rows d of W, 64 rows b).  The W rows (64 KB) arrive by
+// asynchronous copies; the fp32 X rows (128 KB) are read into registers, all in
+// flight at once, rounded to bf16 (the product's input precision) and stored to
+// LDS.  Both are K-contiguous, so every fragment is one 16-byte read: row r at
+// 1 KB r, chunk q (8 values) at q ^ (r & 15).  Wave w computes the 32 x 32 tile
+// (d half w & 1, b half w >> 1) over the 32 k-steps.  The two d halves of a head
+// run on one XCD (workgroups 8 apart), so the second reads X from its L2.
+constexpr int kUvK = 512, kUvN = 64, kUvM = 64;
+
+__global__ __launch_bounds__(256, 1) void k_gemm_uv_wide(GemmArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds[(kUvN + kUvM) * 1024];   // W rows, X rows
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int L = blockIdx.x, halves = a.N / kUvN;   // (head, half) pairs, XCD-paired
+  const int pair = (L >> 3) / halves * 8 + (L & 7), half = (L >> 3) % halves;
+  const int head = pair, n0 = half * kUvN, m0 = blockIdx.y * kUvM;
+  const uint32_t wl = lds_addr(lds), xl = wl + kUvN * 1024;
+
+  // ---- W rows n0 .. n0+63 of the head: one 1 KB copy each
+  {
+    const uint64_t wg = reinterpret_cast<uint64_t>(static_cast<const bf16_t*>(a.w1) +
+                                                   head * a.w_bs + static_cast<int64_t>(n0) * a.ldw_n);
+    for (int r = wv; r < kUvN; r += 4) {
+      const uint32_t voff = static_cast<uint32_t>((static_cast<int64_t>(r) * a.ldw_n +
+                                                   8 * (lane ^ (r & 15))) * 2);
+      dma_block(wg, voff, wl + 1024 * r);
+    }
+  }
+  // ---- X rows: 32 float4 per thread in flight, then bf16 into LDS
+  {
+    const float* xb = static_cast<const float*>(a.x) + head * a.x_bs;
+    float4 v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int e = 4 * (256 * i + tid);   // element of the 64 x 512 tile
+      const int b = e >> 9, c = e & 511;
+      const int br = m0 + b < a.M ? m0 + b : a.M - 1;   // rows past M repeat the last one
+      v[i] = *reinterpret_cast<const float4*>(xb + static_cast<int64_t>(br) * a.ldx_m + c);
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int e = 4 * (256 * i + tid);
+      const int b = e >> 9, c = e & 511;
+      const uint32_t addr = xl + 1024 * b + 16 * ((c >> 3) ^ (b & 15)) + 8 * ((c >> 2) & 1);
+      *reinterpret_cast<__attribute__((address_space(3))) u32x2_t*>(static_cast<uintptr_t>(addr)) =
+          (u32x2_t){cvt2(v[i].x, v[i].y), cvt2(v[i].z, v[i].w)};
+    }
+    wait_vmcnt<0>();   // the W copies
+    __syncthreads();
+  }
+
+  // ---- products: wave tile (d rows 32(wv & 1) .., b rows 32(wv >> 1) ..)
+  const int j32 = lane & 31, g = lane >> 5;
+  const int dr = 32 * (wv & 1) + j32, br = 32 * (wv >> 1) + j32;
+  f32x16_t acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll 8
+  for (int s = 0; s < kUvK / 16; ++s) {
+    const int q = 2 * s + g;
+    const u32x4_t av = lds_u128(wl + 1024 * dr + 16 * (q ^ (dr & 15)));
+    const u32x4_t bv = lds_u128(xl + 1024 * br + 16 * (q ^ (br & 15)));
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                  __builtin_bit_cast(bf16x8_t, bv), acc, 0, 0, 0);
+  }
+  // acc lane (j32, g): d = n0 + 32(wv & 1) + 8(e >> 2) + 4g + (e & 3), b = m0 + 32(wv >> 1) + j32
+  const int b = m0 + 32 * (wv >> 1) + j32;
+  if (b < a.M) {
+    bf16_t* y = static_cast<bf16_t*>(a.y) + head * a.y_bs + static_cast<int64_t>(b) * a.ldy + n0 +
+                32 * (wv & 1) + 4 * g;
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4)
+      *reinterpret_cast<u32x2_t*>(y + 8 * e4) =
+          (u32x2_t){cvt2(acc[4 * e4], acc[4 * e4 + 1]), cvt2(acc[4 * e4 + 2], acc[4 * e4 + 3])};
+  }
+}
+
 // ---- large-M tiled product (prefill batch sizes) ---------------------------
 // For M in the hundreds and more every weight tile is worth reusing across X
 // rows: a workgroup owns a 128 (n) x 128 (m) output tile and walks K in chunks of
@@ -859,6 +1088,14 @@ static bool uk_ok(const GemmArgs& a) {
          a.w1 == a.w2 && a.n_split >= a.N && aligned16(a.x) && aligned16(a.w1);
 }
 
+// The wide W_UK form: an fp32 X, 256-column tiles, every row and block start
+// 16-byte aligned (asynchronous copies and 16-byte stores), copy offsets in 32 bits.
+static bool uk_wide_ok(const GemmArgs& a) {
+  return uk_ok(a) && a.x_f32 && a.N % kUwN == 0 && a.ldw_k % 8 == 0 && a.w_bs % 8 == 0 &&
+         a.ldx_m % 4 == 0 && a.x_bs % 4 == 0 && a.ldy % 4 == 0 && a.y_bs % 4 == 0 &&
+         aligned16(a.y) && static_cast<int64_t>(kUwM) * a.ldx_m * 4 < (int64_t{1} << 31);
+}
+
 // One activation matrix of at most 64 rows and enough weight rows to give every
 // wave of the grid strips to stream (narrow outputs, like the 576-wide latent
 // append, leave most waves idle there and go to k_gemm_ws): the X-stationary kernel.
@@ -894,10 +1131,20 @@ static bool small_tile_ok(const GemmArgs& a) {
          a.K % kTk == 0 && static_cast<int64_t>(a.N / 64) * a.batch >= 256;
 }
 
+// The per-head W_UV form for an fp32 X and bf16 output: K = 512, N a multiple of
+// 64, heads a multiple of 8 (XCD pairing), rows 16-byte aligned, bf16 stores of 8 bytes.
+static bool uv_wide_ok(const GemmArgs& a) {
+  return ws_ok(a) && a.epi == EPI_STORE && a.x_f32 && !a.y_f32 && a.K == kUvK &&
+         a.N % kUvN == 0 && a.batch % 8 == 0 && a.n_split >= a.N && a.x_bs % 4 == 0 &&
+         a.ldx_m % 4 == 0 && a.ldy % 4 == 0 && a.y_bs % 4 == 0 &&
+         (reinterpret_cast<uintptr_t>(a.y) & 7) == 0 &&
+         static_cast<int64_t>(a.batch) * (a.N / kUvN) < 65536;
+}
+
 bool fast_gemm_ok(const GemmArgs& a) { return ws_ok(a) || uk_ok(a); }
 
 size_t gemm_partial_bytes(const GemmArgs& a) {
-  if (!ws_ok(a) || tile_ok(a) || small_tile_ok(a)) return 0;
+  if (!ws_ok(a) || tile_ok(a) || uv_wide_ok(a) || small_tile_ok(a)) return 0;
   if (xs_ok(a)) {
     const XsPlan q = xs_plan(a);
     return q.d > 1 ? xs_tiles_bytes(a, q) + xs_rope_bytes(a) : 0;
@@ -912,6 +1159,11 @@ hipError_t launch_gemm_fast(const GemmArgs& a, void* partial, size_t partial_byt
   if (a.epi == EPI_QPROJ_APPEND && !xs_ok(a)) return hipErrorInvalidValue;
   if (!ws_ok(a)) {
     if (!uk_ok(a)) return hipErrorInvalidValue;
+    if (uk_wide_ok(a)) {
+      dim3 grid(a.batch, a.N / kUwN, (a.M + kUwM - 1) / kUwM);
+      hipLaunchKernelGGL(k_gemm_uk_wide<kUwN>, grid, dim3(256), 0, stream, a);
+      return hipGetLastError();
+    }
     dim3 grid(a.batch, a.N / kUkN, (a.M + kTile - 1) / kTile);
     if (a.x_f32)
       hipLaunchKernelGGL(k_gemm_uk<float>, grid, dim3(256), 0, stream, a);
@@ -925,6 +1177,11 @@ hipError_t launch_gemm_fast(const GemmArgs& a, void* partial, size_t partial_byt
       hipLaunchKernelGGL((k_gemm_tile<float, kTt, kTt>), grid, dim3(256), 0, stream, a);
     else
       hipLaunchKernelGGL((k_gemm_tile<bf16_t, kTt, kTt>), grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
+  if (uv_wide_ok(a)) {
+    const dim3 grid(a.batch * (a.N / kUvN), (a.M + kUvM - 1) / kUvM);
+    hipLaunchKernelGGL(k_gemm_uv_wide, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
   }
   if (small_tile_ok(a)) {

@@ -91,4 +91,43 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, int z, int m, i
   append_pair<T>(a, a.y, a.n_split, m, n, v0, v1);
 }
 
+// Columns n .. n+3 of row m (n a multiple of 4): one 16-byte store for an fp32
+// plain output, for q^C and for q_pe when the four columns lie in one region and
+// the destination is 16-byte aligned; the pair stages otherwise.
+template <typename T>
+__device__ __forceinline__ void gemm_epilogue4(const GemmArgs& a, int z, int m, int n, float4 v) {
+  auto aligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  if (a.epi == EPI_STORE && a.y_f32 && n + 3 < a.N) {
+    float* y = static_cast<float*>(a.y) + z * a.y_bs + static_cast<int64_t>(m) * a.ldy + n;
+    if (aligned(y)) {
+      *reinterpret_cast<float4*>(y) = v;
+      return;
+    }
+  }
+  const bool qproj = a.epi == EPI_QPROJ || a.epi == EPI_QPROJ_APPEND;
+  const int n_q = a.epi == EPI_QPROJ_APPEND ? a.n_append : a.N;   // end of the query columns
+  if (qproj && a.y_f32 && n + 3 < a.n_split) {
+    float* y = static_cast<float*>(a.y) + static_cast<int64_t>(m) * a.ldy + n;
+    if (aligned(y)) {
+      *reinterpret_cast<float4*>(y) = v;
+      return;
+    }
+  }
+  if (qproj && n >= a.n_split && n + 3 < n_q && (a.d_rope & 3) == 0) {
+    const int r = n - a.n_split;   // two pairs of one head
+    const int k = (r % a.d_rope) >> 1;
+    float* y2 = static_cast<float*>(a.y2) + static_cast<int64_t>(m) * (n_q - a.n_split) + r;
+    if (aligned(y2)) {
+      float c0, s0, c1, s1;
+      rope_row(a, m, a.pos[m], k, &c0, &s0);
+      rope_row(a, m, a.pos[m], k + 1, &c1, &s1);
+      *reinterpret_cast<float4*>(y2) = make_float4(v.x * c0 - v.y * s0, v.x * s0 + v.y * c0,
+                                                   v.z * c1 - v.w * s1, v.z * s1 + v.w * c1);
+      return;
+    }
+  }
+  gemm_epilogue<T>(a, z, m, n, v.x, v.y);
+  gemm_epilogue<T>(a, z, m, n + 2, v.z, v.w);
+}
+
 }  // namespace mla

@@ -426,8 +426,9 @@ __global__ __launch_bounds__(256) void k_gemm_finish(GemmArgs a, int ksplit, con
 }
 
 // Sum of the K-split partial tiles of k_gemm_xs (fixed order) followed by the
-// output stage.  Thread q takes 4 columns of one row: strip q / (4 M), row
-// (q / 4) mod M, columns 4 (q mod 4)..+3 of the strip, so that a wave reads
+// output stage.  Thread q takes 4 columns of one row: strip q / (4 M) (rotated so
+// that the latent-append strips, whose stores wait on a page lookup, go first),
+// row (q / 4) mod M, columns 4 (q mod 4)..+3 of the strip, so that a wave reads
 // whole 1 KB pieces of a tile.
 __global__ __launch_bounds__(256) void k_gemm_finish_xs(GemmArgs a, int ksplit, int rows_pad,
                                                         const float* partial) {
@@ -435,8 +436,10 @@ __global__ __launch_bounds__(256) void k_gemm_finish_xs(GemmArgs a, int ksplit, 
   const uint32_t nstrips = static_cast<uint32_t>(a.N) / 16;
   const uint32_t quads = nstrips * per_strip;
   const int64_t plane = static_cast<int64_t>(nstrips) * rows_pad * 16;   // one slice
+  const uint32_t first = a.epi == EPI_QPROJ_APPEND ? static_cast<uint32_t>(a.n_append) / 16 : 0;
   for (uint32_t q = blockIdx.x * blockDim.x + threadIdx.x; q < quads; q += blockDim.x * gridDim.x) {
-    const uint32_t strip = q / per_strip, r = q - strip * per_strip;
+    const uint32_t qs = q / per_strip, r = q - qs * per_strip;
+    const uint32_t strip = qs + first < nstrips ? qs + first : qs + first - nstrips;
     const int m = static_cast<int>(r >> 2), g = static_cast<int>(r & 3);
     const float* src = partial + static_cast<int64_t>(strip) * rows_pad * 16 + 16 * m + 4 * g;
     float4 v = *reinterpret_cast<const float4*>(src);
@@ -449,9 +452,7 @@ __global__ __launch_bounds__(256) void k_gemm_finish_xs(GemmArgs a, int ksplit, 
       for (int j = 0; j < 8; ++j)
         if (s0 + j < ksplit) { v.x += t[j].x; v.y += t[j].y; v.z += t[j].z; v.w += t[j].w; }
     }
-    const int n = 16 * static_cast<int>(strip) + 4 * g;
-    gemm_epilogue<bf16_t>(a, 0, m, n, v.x, v.y);
-    gemm_epilogue<bf16_t>(a, 0, m, n + 2, v.z, v.w);
+    gemm_epilogue4<bf16_t>(a, 0, m, 16 * static_cast<int>(strip) + 4 * g, v);
   }
 }
 

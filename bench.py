@@ -300,7 +300,10 @@ def main():
         "data": "synthetic (seeded, counter-based generator; random-init weights)",
         "config": {"workload": f"{w.name}: {layers}, hidden {w.hidden}, n_h {w.n_heads}, "
                                f"d_h {w.d_head}, d_c {w.d_latent}, d_R {w.d_rope}, batch {B}, "
-                               f"{ctx}, {S} KV splits, 64-token pages"
+                               f"{ctx}, "
+                               + (f"length-proportional plan of {dw0.n_units} attention units "
+                                  f"(target {w.plan_units})" if dw0.plan is not None
+                                  else f"{S} KV splits") + ", 64-token pages"
                                + (f", query compression d_c' {w.d_cq}" if w.d_cq else "")
                                + (", FP8 latent pool (e4m3 c^KV + row scale, bf16 k^R)"
                                   if w.cache == "fp8" else "")
@@ -309,7 +312,10 @@ def main():
                                   if w.yarn else "")
                                + (f", prefill of the last {w.chunk} positions of every sequence "
                                   f"({nq} prompt tokens per step)" if w.chunk else ""),
-                   "batch": B, "context": int(lens.max()), "num_splits": S, "layers": w.layers},
+                   "batch": B, "context": int(lens.max()),
+                   "num_splits": None if dw0.plan is not None else S,
+                   "attention_units": dw0.n_units if dw0.plan is not None else B * S,
+                   "layers": w.layers},
         "latent_cache_GBps": achieved,
         "attention_us": attn_s * 1e6,
         "attention_mfma_tflops": tflops,

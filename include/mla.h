@@ -175,6 +175,46 @@ mla_status mla_decode_attention(const mla_dims* dims, const float* q_lat, const 
                                 hipStream_t stream);
 
 /*
+ * Length-proportional work list for the decode attention of a ragged batch
+ * ([Report] §2.3: the work of one head group is a pass over its sequence's
+ * cached rows, so equal work means equal token counts).  Host function: from
+ * seq_lens [batch] (host memory), unit length
+ *   U = page_size * ceil(ceil(sum_b L_b / target_units) / page_size),
+ * sequence b gets n_b = max(1, ceil(L_b / U)) units, the page-aligned chunks of
+ * mla_decode_attention's split rule with S = n_b (trailing empty chunks dropped;
+ * an empty sequence keeps one empty unit).  Writes to plan (host memory, at
+ * least mla_decode_plan_capacity(batch, target_units) entries):
+ *   plan[3u], plan[3u+1], plan[3u+2] = (b, t0, t1) for u < n_units, units of
+ *     one sequence consecutive and in order; n_units padded to a multiple of 8
+ *     with empty units (0, 0, 0);
+ *   plan[3 n_units + b] = first unit of sequence b, b = 0..batch (the last entry
+ *     is the number of units before the padding).
+ * Returns n_units (>= 8), or a negative mla_status: null pointers, a negative
+ * length, batch outside [1, 65535], page_size < 1, target_units outside
+ * [1, 2^20], or a capacity below mla_decode_plan_capacity.  The plan is copied
+ * to device memory by the caller for the *_planned calls.
+ */
+int64_t mla_decode_plan_capacity(int32_t batch, int32_t target_units);
+int32_t mla_decode_plan(const int32_t* seq_lens, int32_t batch, int32_t page_size,
+                        int32_t target_units, int32_t* plan, int64_t capacity);
+
+/*
+ * mla_decode_attention over the units of a plan (device copy of
+ * mla_decode_plan's output, n_units as it returned): unit u = (b, t0, t1)
+ * attends query row b to positions [t0, t1) of sequence b (block_table row b):
+ *   o_part [n_units, n_h, d_c] fp32, lse_part [n_units, n_h] fp32 (unit u's
+ *   partials, the padding units' empty).
+ * A unit with b outside [0, batch) or a range outside [0, max_pages*page_size]
+ * is treated as empty and sets bit 1 of the device error word.  Other
+ * arguments as in mla_decode_attention; n_units a positive multiple of 8.
+ */
+mla_status mla_decode_attention_planned(const mla_dims* dims, const float* q_lat,
+                                        const float* q_pe, const void* pool, int64_t num_pages,
+                                        const int32_t* block_table, int32_t max_pages,
+                                        const int32_t* plan, int32_t n_units, int32_t batch,
+                                        float* o_part, float* lse_part, hipStream_t stream);
+
+/*
  * Prefill (chunked-prefill) attention: many query tokens per sequence, each
  * attending causally to the latent cache of its own sequence ([Report] §3.1: the
  * same per-token MLA flow for every prompt token; the pages quote prompt
@@ -206,6 +246,17 @@ mla_status mla_prefill_attention(const mla_dims* dims, const float* q_lat, const
 mla_status mla_merge_lse(const mla_dims* dims, const float* o_part, const float* lse_part,
                          int32_t batch, int32_t num_splits, float* o_lat, float* lse,
                          hipStream_t stream);
+
+/*
+ * mla_merge_lse over the partials of a plan: row b merges units
+ * plan[3 n_units + b] .. plan[3 n_units + b + 1] - 1 (same rules; a range
+ * outside [0, n_units] merges nothing and sets bit 1 of the device error word).
+ *   o_part [n_units, n_h, d_c], lse_part [n_units, n_h]; o_lat, lse as in
+ *   mla_merge_lse.
+ */
+mla_status mla_merge_lse_planned(const mla_dims* dims, const float* o_part, const float* lse_part,
+                                 const int32_t* plan, int32_t n_units, int32_t batch,
+                                 float* o_lat, float* lse, hipStream_t stream);
 
 /*
  * Absorbed output ([Report] §2.3: W_UV folded into the output projection):
@@ -344,6 +395,15 @@ mla_status mla_decode_attention_fp8(const mla_dims* dims, const float* q_lat, co
                                     const int32_t* seq_lens, int32_t batch, int32_t num_splits,
                                     float* o_part, float* lse_part, hipStream_t stream);
 
+/* mla_decode_attention_planned over the FP8 pool (rows as in
+ * mla_decode_attention_fp8). */
+mla_status mla_decode_attention_fp8_planned(const mla_dims* dims, const float* q_lat,
+                                            const float* q_pe, const void* pool,
+                                            int64_t num_pages, const int32_t* block_table,
+                                            int32_t max_pages, const int32_t* plan,
+                                            int32_t n_units, int32_t batch, float* o_part,
+                                            float* lse_part, hipStream_t stream);
+
 /* Prefill attention over the FP8 pool (as mla_prefill_attention, rows dequantized
  * as in mla_decode_attention_fp8). */
 mla_status mla_prefill_attention_fp8(const mla_dims* dims, const float* q_lat, const float* q_pe,
@@ -361,8 +421,8 @@ int32_t mla_abi_version(void);
 
 /*
  * Sticky device error word: bit 0 = a block-table entry outside [0, num_pages),
- * bit 1 = a position / length beyond max_pages*page_size or negative, bit 2 = a
- * sequence index outside [0, n_seqs).  Synchronises `stream`, copies the word
+ * bit 1 = a position / length beyond max_pages*page_size or negative (also a bad
+ * plan entry or unit range), bit 2 = a sequence index outside [0, n_seqs).  Synchronises `stream`, copies the word
  * to *out and, if clear != 0, resets it.  Returns MLA_ERR_HIP on a runtime error.
  */
 mla_status mla_device_error(int32_t* out, int32_t clear, hipStream_t stream);

@@ -25,7 +25,9 @@ __all__ = ["MlaDims", "MlaError", "make_dims", "load", "mla_append_latent", "mla
            "mla_status_string", "mla_fp8_page_bytes", "mla_quantize_rows_fp8",
            "mla_append_latent_fp8", "mla_append_workspace_bytes_fp8", "mla_decode_attention_fp8",
            "mla_prefill_attention", "mla_prefill_attention_fp8", "mla_absorb_out_noalloc",
-           "mla_absorb_out_noalloc_max_bytes", "LIB_PATH"]
+           "mla_absorb_out_noalloc_max_bytes", "mla_decode_plan", "mla_decode_plan_capacity",
+           "mla_decode_attention_planned", "mla_decode_attention_fp8_planned",
+           "mla_merge_lse_planned", "LIB_PATH"]
 
 
 class MlaDims(ctypes.Structure):
@@ -66,6 +68,13 @@ _SIGS = {
     "mla_absorb_q_cq": [_DIMS, _I32, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P],
     "mla_decode_attention": [_DIMS, _P, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _P, _P, _P],
     "mla_merge_lse": [_DIMS, _P, _P, _I32, _I32, _P, _P, _P],
+    "mla_decode_plan_capacity": [_I32, _I32],
+    "mla_decode_plan": [_P, _I32, _I32, _I32, _P, _I64],
+    "mla_decode_attention_planned": [_DIMS, _P, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _P, _P,
+                                     _P],
+    "mla_decode_attention_fp8_planned": [_DIMS, _P, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _P,
+                                         _P, _P],
+    "mla_merge_lse_planned": [_DIMS, _P, _P, _P, _I32, _I32, _P, _P, _P],
     "mla_absorb_out": [_DIMS, _P, _P, _P, _I32, _P, _P, _SZ, _P],
     "mla_absorb_out_noalloc": [_DIMS, _P, _P, _P, _I32, _P, _P],
     "mla_absorb_out_noalloc_max_bytes": [],
@@ -88,7 +97,7 @@ _SIGS = {
 }
 _RES = {"mla_workspace_bytes": _SZ, "mla_workspace_bytes_cq": _SZ, "mla_append_workspace_bytes": _SZ,
         "mla_fp8_page_bytes": _SZ, "mla_append_workspace_bytes_fp8": _SZ,
-        "mla_absorb_out_noalloc_max_bytes": _SZ,
+        "mla_absorb_out_noalloc_max_bytes": _SZ, "mla_decode_plan_capacity": _I64,
         "mla_status_string": ctypes.c_char_p}
 
 
@@ -286,6 +295,79 @@ def mla_merge_lse(dims, o_part, lse_part, o_lat, lse=None, stream=None):
     _check("mla_merge_lse", load().mla_merge_lse(
         ctypes.byref(dims), _ptr(o_part), _ptr(lse_part), B, S, _ptr(o_lat), _ptr(lse),
         _stream(stream)))
+
+
+def mla_decode_plan_capacity(batch: int, target_units: int) -> int:
+    return int(load().mla_decode_plan_capacity(batch, target_units))
+
+
+def mla_decode_plan(seq_lens, page_size: int, target_units: int):
+    """Length-proportional work list (host): returns (n_units, plan) with plan an
+    int32 numpy array of 3 n_units unit entries followed by batch + 1 unit starts."""
+    import numpy as np
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    cap = mla_decode_plan_capacity(len(lens), target_units)
+    if cap <= 0:
+        raise ValueError("batch or target_units out of range")
+    plan = np.zeros(cap, dtype=np.int32)
+    n = int(load().mla_decode_plan(lens.ctypes.data_as(_P), len(lens), page_size, target_units,
+                                   plan.ctypes.data_as(_P), cap))
+    if n < 0:
+        raise MlaError("mla_decode_plan", n)
+    return n, plan[:3 * n + len(lens) + 1].copy()
+
+
+def _attention_planned(name, fp8, dims, q_lat, q_pe, pool, block_table, plan, n_units, o_part,
+                       lse_part, stream):
+    import torch
+    B, nh = q_lat.shape[0], dims.n_heads
+    _expect(q_lat, (B, nh, dims.d_latent), torch.float32, "q_lat")
+    _expect(q_pe, (B, nh, dims.d_rope), torch.float32, "q_pe")
+    if fp8:
+        _expect_fp8_pool(dims, pool)
+    else:
+        _expect(pool, (pool.shape[0], dims.page_size, dims.d_latent + dims.d_rope), _elem(dims),
+                "pool")
+    _expect(plan, (3 * n_units + B + 1,), torch.int32, "plan")
+    _expect(o_part, (n_units, nh, dims.d_latent), torch.float32, "o_part")
+    _expect(lse_part, (n_units, nh), torch.float32, "lse_part")
+    _expect_table(block_table)
+    if block_table.shape[0] < B:
+        raise ValueError("block_table must have at least batch rows")
+    _check(name, getattr(load(), name)(
+        ctypes.byref(dims), _ptr(q_lat), _ptr(q_pe), _ptr(pool), pool.shape[0], _ptr(block_table),
+        block_table.shape[1], _ptr(plan), n_units, B, _ptr(o_part), _ptr(lse_part),
+        _stream(stream)))
+
+
+def mla_decode_attention_planned(dims, q_lat, q_pe, pool, block_table, plan, n_units, o_part,
+                                 lse_part, stream=None):
+    """Split-KV latent attention over the units of a plan (device int32 copy of
+    mla_decode_plan's array)."""
+    _attention_planned("mla_decode_attention_planned", False, dims, q_lat, q_pe, pool,
+                       block_table, plan, n_units, o_part, lse_part, stream)
+
+
+def mla_decode_attention_fp8_planned(dims, q_lat, q_pe, pool, block_table, plan, n_units, o_part,
+                                     lse_part, stream=None):
+    """mla_decode_attention_planned over the FP8 pool."""
+    _attention_planned("mla_decode_attention_fp8_planned", True, dims, q_lat, q_pe, pool,
+                       block_table, plan, n_units, o_part, lse_part, stream)
+
+
+def mla_merge_lse_planned(dims, o_part, lse_part, plan, n_units, o_lat, lse=None, stream=None):
+    """Log-sum-exp merge of a plan's unit partials into o_lat (and lse if given)."""
+    import torch
+    B, nh = o_lat.shape[0], dims.n_heads
+    _expect(o_part, (n_units, nh, dims.d_latent), torch.float32, "o_part")
+    _expect(lse_part, (n_units, nh), torch.float32, "lse_part")
+    _expect(plan, (3 * n_units + B + 1,), torch.int32, "plan")
+    _expect(o_lat, (B, nh, dims.d_latent), torch.float32, "o_lat")
+    if lse is not None:
+        _expect(lse, (B, nh), torch.float32, "lse")
+    _check("mla_merge_lse_planned", load().mla_merge_lse_planned(
+        ctypes.byref(dims), _ptr(o_part), _ptr(lse_part), _ptr(plan), n_units, B, _ptr(o_lat),
+        _ptr(lse), _stream(stream)))
 
 
 def mla_absorb_out(dims, o_lat, w_uv, w_o, u, workspace, stream=None):

@@ -315,8 +315,7 @@ __device__ __forceinline__ u32x2_t lds_tr8(uint32_t addr) {
   return __builtin_bit_cast(u32x2_t, v);
 }
 __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
-    AttnArgs a, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
-    const char* __restrict__ pool) {
+    AttnArgs a, const int32_t* __restrict__ block_table, const char* __restrict__ pool) {
   __shared__ __attribute__((aligned(1024))) char ring[kStages * kTileBytes];   // tile ring
   __shared__ __attribute__((aligned(16))) float xch[kWaves][kHeads];
   // page ids of the split's pages [wbase, wbase + kPageWin): a copy in LDS, so
@@ -328,21 +327,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
   const int g2 = lane >> 5;           // k-group of the 32x32 MFMA operands
   const int r32 = lane & 31;          // token row (scores A) / head (scores B, P.C A)
-  const int S = a.num_splits;
-  const int unit = unit_of(blockIdx.x, a.batch * S);
-  const int b = unit / S, s = unit - b * S;
+  const int unit = unit_of(blockIdx.x, a.units);
   const int nh = 128;
 
-  int sq, L;
-  unit_seq_len(seq_lens, a.q_seq, a.q_pos, a.n_seqs, a.max_pages * kPage, b, tid == 0, a.err, &sq,
-               &L);
-  sq = __builtin_amdgcn_readfirstlane(sq);   // uniform by construction; say so for the
-  L = __builtin_amdgcn_readfirstlane(L);     // scalar operands of the copies
+  int b, sq, t0, t1;
+  attn_unit(a, unit, tid == 0, &b, &sq, &t0, &t1);
+  b = __builtin_amdgcn_readfirstlane(b);     // uniform by construction; say so for the
+  sq = __builtin_amdgcn_readfirstlane(sq);   // scalar operands of the copies
+  t0 = __builtin_amdgcn_readfirstlane(t0);
+  t1 = __builtin_amdgcn_readfirstlane(t1);
 
-  int t0, t1;
-  split_range(L, S, s, kPage, &t0, &t1);
-
-  const int64_t ob = (static_cast<int64_t>(b) * S + s) * nh + kHeads * wv;
+  const int64_t ob = static_cast<int64_t>(unit) * nh + kHeads * wv;
   float* o_out = a.o_part + ob * kDc;
   float* lse_out = a.lse_part + ob;
 
@@ -708,8 +703,7 @@ __device__ __forceinline__ void e4m3_scale(float m, uint32_t& e8, float& mul) {
 constexpr int kF8mSlots = 6, kF8mAhead = 4;   // staging slots; tiles copied ahead
 
 __global__ __launch_bounds__(kThreads, 1) void k_attn_f8mma_h128(
-    AttnArgs a, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
-    const char* __restrict__ pool) {
+    AttnArgs a, const int32_t* __restrict__ block_table, const char* __restrict__ pool) {
   __shared__ __attribute__((aligned(1024))) char ring[kF8mSlots * kF8Stage];
   __shared__ __attribute__((aligned(16))) float xch[kWaves][kHeads];
   __shared__ int pwin[kPageWin];
@@ -724,21 +718,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_f8mma_h128(
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g2 = lane >> 5;
   const int r32 = lane & 31;
-  const int S = a.num_splits;
-  const int unit = unit_of(blockIdx.x, a.batch * S);
-  const int b = unit / S, s = unit - b * S;
+  const int unit = unit_of(blockIdx.x, a.units);
   const int nh = 128;
 
-  int sq, L;
-  unit_seq_len(seq_lens, a.q_seq, a.q_pos, a.n_seqs, a.max_pages * kPage, b, tid == 0, a.err, &sq,
-               &L);
-  sq = __builtin_amdgcn_readfirstlane(sq);
-  L = __builtin_amdgcn_readfirstlane(L);
+  int b, sq, t0, t1;
+  attn_unit(a, unit, tid == 0, &b, &sq, &t0, &t1);
+  b = __builtin_amdgcn_readfirstlane(b);     // uniform by construction; say so for the
+  sq = __builtin_amdgcn_readfirstlane(sq);   // scalar operands of the copies
+  t0 = __builtin_amdgcn_readfirstlane(t0);
+  t1 = __builtin_amdgcn_readfirstlane(t1);
 
-  int t0, t1;
-  split_range(L, S, s, kPage, &t0, &t1);
-
-  const int64_t ob = (static_cast<int64_t>(b) * S + s) * nh + kHeads * wv;
+  const int64_t ob = static_cast<int64_t>(unit) * nh + kHeads * wv;
   float* o_out = a.o_part + ob * kDc;
   float* lse_out = a.lse_part + ob;
 
@@ -1230,27 +1220,23 @@ __device__ __forceinline__ int h16row(int t) {   // LDS row of MFMA row t
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h16(
-    AttnArgs a, const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
-    const char* __restrict__ pool) {
+    AttnArgs a, const int32_t* __restrict__ block_table, const char* __restrict__ pool) {
   __shared__ __attribute__((aligned(1024))) char ring[kWaves * 2 * kH16Slot];   // 155,648 B
   __shared__ float wstate[kWaves][2][16];   // per wave: reference and sum of each head
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane & 15, g = lane >> 4;   // head (B/D column) and row group of this lane
-  const int S = a.num_splits;
-  const int unit = unit_of(blockIdx.x, a.batch * S);
-  const int b = unit / S, s = unit - b * S;
+  const int unit = unit_of(blockIdx.x, a.units);
   constexpr int nh = 16;
 
-  int sq, L;
-  unit_seq_len(seq_lens, a.q_seq, a.q_pos, a.n_seqs, a.max_pages * kPage, b, tid == 0, a.err, &sq,
-               &L);
+  int b, sq, t0, t1;
+  attn_unit(a, unit, tid == 0, &b, &sq, &t0, &t1);
+  b = __builtin_amdgcn_readfirstlane(b);
   sq = __builtin_amdgcn_readfirstlane(sq);
-  L = __builtin_amdgcn_readfirstlane(L);
-  int t0, t1;
-  split_range(L, S, s, kPage, &t0, &t1);
-  const int64_t ob = (static_cast<int64_t>(b) * S + s) * nh;
+  t0 = __builtin_amdgcn_readfirstlane(t0);
+  t1 = __builtin_amdgcn_readfirstlane(t1);
+  const int64_t ob = static_cast<int64_t>(unit) * nh;
   float* o_out = a.o_part + ob * kDc;
   float* lse_out = a.lse_part + ob;
   if (t0 >= t1) {   // empty split (uniform across the workgroup)
@@ -1492,22 +1478,22 @@ bool fast_attention_h16_ok(const AttnArgs& a) {
 }
 
 hipError_t launch_attention_fast(const AttnArgs& a, hipStream_t stream) {
-  if (a.batch == 0) return hipSuccess;
-  const int units = a.batch * a.num_splits;
+  if (a.units == 0) return hipSuccess;
+  const int units = a.units;
   if (fast_attention_h16_ok(a))
     hipLaunchKernelGGL(k_attn_mfma_h16, dim3(units), dim3(kThreads), 0, stream, a, a.block_table,
-                       a.seq_lens, static_cast<const char*>(a.pool));
+                       static_cast<const char*>(a.pool));
   else
     hipLaunchKernelGGL(k_attn_mfma_h128, dim3(units), dim3(kThreads), 0, stream, a,
-                       a.block_table, a.seq_lens, static_cast<const char*>(a.pool));
+                       a.block_table, static_cast<const char*>(a.pool));
   return hipGetLastError();
 }
 
 hipError_t launch_attention_fp8(const AttnArgs& a, hipStream_t stream) {
-  if (a.batch == 0) return hipSuccess;
-  const int units = a.batch * a.num_splits;
+  if (a.units == 0) return hipSuccess;
+  const int units = a.units;
   hipLaunchKernelGGL(k_attn_f8mma_h128, dim3(units), dim3(kThreads), 0, stream, a, a.block_table,
-                     a.seq_lens, static_cast<const char*>(a.pool));
+                     static_cast<const char*>(a.pool));
   return hipGetLastError();
 }
 
@@ -1518,14 +1504,16 @@ hipError_t launch_attention_fp8(const AttnArgs& a, hipStream_t stream) {
 __global__ __launch_bounds__(256) void k_merge_rows(MergeArgs a, int rows) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= rows) return;
-  const int nh = a.n_heads, S = a.num_splits, dq = a.d_latent / 4;
+  const int nh = a.n_heads, dq = a.d_latent / 4;
   const int b = row / nh, i = row - b * nh;
-  const float* lse = a.lse_part + static_cast<int64_t>(b) * S * nh + i;
+  int first, S;
+  merge_units(a, b, lane == 0 && i == 0, &first, &S);
+  const float* lse = a.lse_part + static_cast<int64_t>(first) * nh + i;
   float m = -INFINITY;
   for (int s = lane; s < S; s += 64) m = fmaxf(m, lse[static_cast<int64_t>(s) * nh]);
   m = wave_max(m);
   const float4* src =
-      reinterpret_cast<const float4*>(a.o_part) + (static_cast<int64_t>(b) * S * nh + i) * dq;
+      reinterpret_cast<const float4*>(a.o_part) + (static_cast<int64_t>(first) * nh + i) * dq;
   const int64_t split_stride = static_cast<int64_t>(nh) * dq;   // float4s between splits
   float4* dst = reinterpret_cast<float4*>(a.o_lat) + static_cast<int64_t>(row) * dq;
   float z = 0.f;

@@ -129,14 +129,13 @@ __global__ __launch_bounds__(256) void k_attention_generic(AttnArgs a) {
   float* red = rsc + 256;                   // [8]
   int64_t* rowoff = reinterpret_cast<int64_t*>(red + 8);  // [256]
 
-  const int i = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
+  const int i = blockIdx.x;
+  const int u = blockIdx.y + blockIdx.z * gridDim.y;   // work unit
+  if (u >= a.units) return;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nh = a.n_heads;
-  int sq, L;
-  unit_seq_len(a.seq_lens, a.q_seq, a.q_pos, a.n_seqs, a.max_pages * a.page_size, b, tid == 0,
-               a.err, &sq, &L);
-  int t0, t1;
-  split_range(L, a.num_splits, s, a.page_size, &t0, &t1);
+  int b, sq, t0, t1;
+  attn_unit(a, u, tid == 0 && i == 0, &b, &sq, &t0, &t1);
 
   const float* ql = a.q_lat + (static_cast<int64_t>(b) * nh + i) * a.d_latent;
   const float* qp = a.q_pe + (static_cast<int64_t>(b) * nh + i) * a.d_rope;
@@ -190,7 +189,7 @@ __global__ __launch_bounds__(256) void k_attention_generic(AttnArgs a) {
     }
     __syncthreads();
   }
-  const int64_t ob = (static_cast<int64_t>(b) * a.num_splits + s) * nh + i;
+  const int64_t ob = static_cast<int64_t>(u) * nh + i;
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
   for (int d = tid; d < a.d_latent; d += 256) a.o_part[ob * a.d_latent + d] = acc[d] * inv;
   if (tid == 0) a.lse_part[ob] = l_run > 0.f ? m_run + __logf(l_run) : -INFINITY;
@@ -198,10 +197,11 @@ __global__ __launch_bounds__(256) void k_attention_generic(AttnArgs a) {
 
 // pool: 0 = fp32 rows, 1 = bf16 rows, 2 = FP8 pages
 static hipError_t launch_attention_rows(const AttnArgs& a, int pool, hipStream_t stream) {
-  if (a.batch == 0) return hipSuccess;
+  if (a.units == 0) return hipSuccess;
   const size_t shm = (a.d_latent + a.d_rope + a.d_latent + 256 + 256 + 8) * sizeof(float) +
                      256 * sizeof(int64_t) + 16;
-  dim3 grid(a.n_heads, a.num_splits, a.batch);
+  const int gy = a.units < 32768 ? a.units : 32768;   // units over y and z
+  dim3 grid(a.n_heads, gy, (a.units + gy - 1) / gy);
   if (pool == 2)
     hipLaunchKernelGGL(k_attention_generic<Fp8Rows>, grid, dim3(256), shm, stream, a);
   else if (pool == 1)
@@ -223,8 +223,10 @@ hipError_t launch_attention_generic_fp8(const AttnArgs& a, hipStream_t stream) {
 __global__ __launch_bounds__(256) void k_merge_generic(MergeArgs a) {
   const int d = blockIdx.x * 256 + threadIdx.x;
   const int i = blockIdx.y, b = blockIdx.z;
-  const int S = a.num_splits, nh = a.n_heads;
-  const float* lse = a.lse_part + static_cast<int64_t>(b) * S * nh + i;
+  const int nh = a.n_heads;
+  int first, S;
+  merge_units(a, b, d == 0 && i == 0, &first, &S);
+  const float* lse = a.lse_part + static_cast<int64_t>(first) * nh + i;
   float m = -INFINITY;
   for (int s = 0; s < S; ++s) m = fmaxf(m, lse[static_cast<int64_t>(s) * nh]);
   float z = 0.f, o = 0.f;
@@ -235,7 +237,7 @@ __global__ __launch_bounds__(256) void k_merge_generic(MergeArgs a) {
       const float w = __expf(l - m);
       z += w;
       if (d < a.d_latent)
-        o += w * a.o_part[((static_cast<int64_t>(b) * S + s) * nh + i) * a.d_latent + d];
+        o += w * a.o_part[((static_cast<int64_t>(first) + s) * nh + i) * a.d_latent + d];
     }
   }
   if (d < a.d_latent)

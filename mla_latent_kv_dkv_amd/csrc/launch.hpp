@@ -73,7 +73,36 @@ struct AttnArgs {
   const int32_t* q_seq;
   const int32_t* q_pos;
   int n_seqs;
+  // work units: batch * num_splits uniform splits (plan null), or the entries
+  // (b, t0, t1) of a length-proportional plan (decode only); partials of unit u
+  // at head rows u * n_heads ..
+  const int32_t* plan;
+  int units;
 };
+
+// Work unit u: query row b, block-table row sq and token range [t0, t1).
+// Uniform splits: split u mod S of query row u / S (split_range).  Plan: entry
+// (b, t0, t1), checked against the batch and the table's length; a bad entry
+// sets ERR_POS (when `flag`) and gives an empty range.
+__device__ __forceinline__ void attn_unit(const AttnArgs& a, int u, bool flag, int* b, int* sq,
+                                          int* t0, int* t1) {
+  if (a.plan) {
+    const int pb = a.plan[3 * u], p0 = a.plan[3 * u + 1], p1 = a.plan[3 * u + 2];
+    if (pb < 0 || pb >= a.batch || p0 < 0 || p0 > p1 || p1 > a.max_pages * a.page_size) {
+      if (flag) set_err(a.err, ERR_POS);
+      *b = 0; *sq = 0; *t0 = 0; *t1 = 0;
+    } else {
+      *b = pb; *sq = pb; *t0 = p0; *t1 = p1;
+    }
+    return;
+  }
+  const int S = a.num_splits;
+  *b = u / S;
+  int L;
+  unit_seq_len(a.seq_lens, a.q_seq, a.q_pos, a.n_seqs, a.max_pages * a.page_size, *b, flag, a.err,
+               sq, &L);
+  split_range(L, S, u - *b * S, a.page_size, t0, t1);
+}
 
 hipError_t launch_attention_generic(const AttnArgs& a, bool bf16, hipStream_t stream);
 // FP8 pool: pages of page_size rows [d_c e4m3 | d_R bf16], then page_size fp32 row scales
@@ -103,7 +132,31 @@ struct MergeArgs {
   int batch, num_splits, n_heads, d_latent;
   float* o_lat;
   float* lse;
+  // plan: the partials of row b are units unit_start[b] .. unit_start[b+1]-1 of
+  // `units` (else b * num_splits .. + num_splits - 1); a bad range sets ERR_POS
+  const int32_t* unit_start;
+  int units;
+  int* err;
 };
+
+// Partials of merge row b: first unit and count.
+__device__ __forceinline__ void merge_units(const MergeArgs& a, int b, bool flag, int* first,
+                                            int* count) {
+  if (!a.unit_start) {
+    *first = b * a.num_splits;
+    *count = a.num_splits;
+    return;
+  }
+  const int f = a.unit_start[b], e = a.unit_start[b + 1];
+  if (f < 0 || f > e || e > a.units) {
+    if (flag && a.err) set_err(a.err, ERR_POS);
+    *first = 0;
+    *count = 0;
+    return;
+  }
+  *first = f;
+  *count = e - f;
+}
 
 hipError_t launch_merge_generic(const MergeArgs& a, bool bf16, hipStream_t stream);
 

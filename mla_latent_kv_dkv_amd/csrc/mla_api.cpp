@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <vector>
 #include <atomic>
 #include <cmath>
 #include <cstring>
@@ -310,6 +311,15 @@ mla_status attention_args(const mla_dims* d, bool prefill, const float* q_lat, c
   a->scale = softmax_scale(d); a->o_part = o_part; a->lse_part = lse_part; a->err = err;
   a->q_seq = prefill ? q_seq : nullptr; a->q_pos = prefill ? q_pos : nullptr;
   a->n_seqs = prefill ? n_seqs : batch;
+  a->units = batch * num_splits;
+  return MLA_OK;
+}
+
+// Checks of the planned calls: the plan pointer and its unit count (a multiple
+// of 8, as mla_decode_plan pads it).
+mla_status plan_args(const int32_t* plan, int32_t n_units) {
+  if (!plan) return MLA_ERR_NULL;
+  if (n_units < 8 || n_units % 8 != 0 || n_units > (1 << 24)) return MLA_ERR_SHAPE;
   return MLA_OK;
 }
 
@@ -666,6 +676,26 @@ mla_status mla_prefill_attention_fp8(const mla_dims* d, const float* q_lat, cons
   return hip_status(launch_attention_f8(d, a, stream));
 }
 
+}  // extern "C"
+
+namespace {
+mla_status merge_run(const mla_dims* d, const float* o_part, const float* lse_part, int32_t batch,
+                     int32_t num_splits, const int32_t* unit_start, int32_t n_units, float* o_lat,
+                     float* lse, hipStream_t stream) {
+  mla::MergeArgs a{};
+  a.o_part = o_part; a.lse_part = lse_part; a.batch = batch; a.num_splits = num_splits;
+  a.n_heads = d->n_heads; a.d_latent = d->d_latent; a.o_lat = o_lat; a.lse = lse;
+  a.unit_start = unit_start; a.units = n_units;
+  a.err = err_word();
+  if (!a.err) return MLA_ERR_HIP;
+  const bool bf16 = d->dtype == MLA_BF16;
+  if (use_fast() && bf16 && mla::fast_merge_ok(a)) return hip_status(mla::launch_merge_fast(a, stream));
+  return hip_status(mla::launch_merge_generic(a, bf16, stream));
+}
+}  // namespace
+
+extern "C" {
+
 mla_status mla_merge_lse(const mla_dims* d, const float* o_part, const float* lse_part,
                          int32_t batch, int32_t num_splits, float* o_lat, float* lse,
                          hipStream_t stream) {
@@ -674,12 +704,105 @@ mla_status mla_merge_lse(const mla_dims* d, const float* o_part, const float* ls
   if (batch < 0 || batch > 65535 || num_splits < 1 || num_splits > 4096) return MLA_ERR_SHAPE;
   if (batch == 0) return MLA_OK;
   if (!o_part || !lse_part || !o_lat) return MLA_ERR_NULL;
-  mla::MergeArgs a{};
-  a.o_part = o_part; a.lse_part = lse_part; a.batch = batch; a.num_splits = num_splits;
-  a.n_heads = d->n_heads; a.d_latent = d->d_latent; a.o_lat = o_lat; a.lse = lse;
-  const bool bf16 = d->dtype == MLA_BF16;
-  if (use_fast() && bf16 && mla::fast_merge_ok(a)) return hip_status(mla::launch_merge_fast(a, stream));
-  return hip_status(mla::launch_merge_generic(a, bf16, stream));
+  return merge_run(d, o_part, lse_part, batch, num_splits, nullptr, batch * num_splits, o_lat, lse,
+                   stream);
+}
+
+int64_t mla_decode_plan_capacity(int32_t batch, int32_t target_units) {
+  if (batch < 0 || batch > 65535 || target_units < 1 || target_units > (1 << 20)) return 0;
+  return 3 * (static_cast<int64_t>(batch) + target_units + 8) + batch + 1;
+}
+
+int32_t mla_decode_plan(const int32_t* seq_lens, int32_t batch, int32_t page_size,
+                        int32_t target_units, int32_t* plan, int64_t capacity) {
+  if (!seq_lens || !plan) return MLA_ERR_NULL;
+  if (batch < 1 || batch > 65535 || page_size < 1 || target_units < 1 ||
+      target_units > (1 << 20))
+    return MLA_ERR_SHAPE;
+  if (capacity < mla_decode_plan_capacity(batch, target_units)) return MLA_ERR_WORKSPACE;
+  int64_t total = 0;
+  for (int b = 0; b < batch; ++b) {
+    if (seq_lens[b] < 0) return MLA_ERR_SHAPE;
+    total += seq_lens[b];
+  }
+  // unit length: the tokens of one target unit, in whole pages
+  int64_t unit = (total + target_units - 1) / target_units;
+  unit = std::max<int64_t>(page_size, (unit + page_size - 1) / page_size * page_size);
+  int32_t* units = plan;
+  std::vector<int32_t> start(batch + 1);
+  int64_t n = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int64_t L = seq_lens[b];
+    const int64_t parts = std::max<int64_t>(1, (L + unit - 1) / unit);
+    // page-aligned equal chunks, as the uniform splits take them
+    const int64_t per = (L + parts - 1) / parts;
+    const int64_t chunk = std::max<int64_t>(page_size, (per + page_size - 1) / page_size * page_size);
+    start[b] = static_cast<int32_t>(n);
+    for (int64_t p = 0; p < parts; ++p) {
+      const int64_t t0 = std::min(L, p * chunk), t1 = std::min(L, (p + 1) * chunk);
+      if (t0 >= t1 && p > 0) break;   // one (empty) unit for an empty sequence
+      units[3 * n] = b;
+      units[3 * n + 1] = static_cast<int32_t>(t0);
+      units[3 * n + 2] = static_cast<int32_t>(t1);
+      ++n;
+    }
+  }
+  start[batch] = static_cast<int32_t>(n);
+  while (n % 8 != 0 || n < 8) {   // empty units of sequence 0 (no sequence's range holds them)
+    units[3 * n] = 0;
+    units[3 * n + 1] = 0;
+    units[3 * n + 2] = 0;
+    ++n;
+  }
+  std::copy(start.begin(), start.end(), plan + 3 * n);
+  return static_cast<int32_t>(n);
+}
+
+mla_status mla_decode_attention_planned(const mla_dims* d, const float* q_lat, const float* q_pe,
+                                        const void* pool, int64_t num_pages,
+                                        const int32_t* block_table, int32_t max_pages,
+                                        const int32_t* plan, int32_t n_units, int32_t batch,
+                                        float* o_part, float* lse_part, hipStream_t stream) {
+  mla::AttnArgs a{};
+  // validated as decode with one split (the plan stands in for the lengths)
+  mla_status st = attention_args(d, false, q_lat, q_pe, pool, num_pages, block_table, max_pages,
+                                 plan, nullptr, nullptr, batch, batch, 1, o_part, lse_part, &a);
+  if (st != MLA_OK || batch == 0) return st;
+  if ((st = plan_args(plan, n_units)) != MLA_OK) return st;
+  a.seq_lens = nullptr; a.plan = plan; a.units = n_units;
+  return hip_status(launch_attention_plain(d, a, stream));
+}
+
+mla_status mla_decode_attention_fp8_planned(const mla_dims* d, const float* q_lat,
+                                            const float* q_pe, const void* pool,
+                                            int64_t num_pages, const int32_t* block_table,
+                                            int32_t max_pages, const int32_t* plan,
+                                            int32_t n_units, int32_t batch, float* o_part,
+                                            float* lse_part, hipStream_t stream) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (!fp8_ok(d)) return MLA_ERR_UNSUPPORTED;
+  mla::AttnArgs a{};
+  st = attention_args(d, false, q_lat, q_pe, pool, num_pages, block_table, max_pages, plan,
+                      nullptr, nullptr, batch, batch, 1, o_part, lse_part, &a);
+  if (st != MLA_OK || batch == 0) return st;
+  if ((st = plan_args(plan, n_units)) != MLA_OK) return st;
+  if (!aligned16(pool)) return MLA_ERR_UNSUPPORTED;
+  a.seq_lens = nullptr; a.plan = plan; a.units = n_units;
+  return hip_status(launch_attention_f8(d, a, stream));
+}
+
+mla_status mla_merge_lse_planned(const mla_dims* d, const float* o_part, const float* lse_part,
+                                 const int32_t* plan, int32_t n_units, int32_t batch,
+                                 float* o_lat, float* lse, hipStream_t stream) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || batch > 65535) return MLA_ERR_SHAPE;
+  if (batch == 0) return MLA_OK;
+  if (!o_part || !lse_part || !o_lat) return MLA_ERR_NULL;
+  if ((st = plan_args(plan, n_units)) != MLA_OK) return st;
+  return merge_run(d, o_part, lse_part, batch, 1, plan + 3 * static_cast<int64_t>(n_units),
+                   n_units, o_lat, lse, stream);
 }
 
 mla_status mla_absorb_out(const mla_dims* d, const float* o_lat, const void* w_uv, const void* w_o,

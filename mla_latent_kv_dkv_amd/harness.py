@@ -11,7 +11,9 @@ import numpy as np
 from . import (make_dims, mla_absorb_out, mla_absorb_q, mla_absorb_q_append, mla_absorb_q_cq,
                mla_append_latent,
                mla_append_latent_fp8, mla_append_workspace_bytes, mla_append_workspace_bytes_fp8,
-               mla_decode_attention, mla_decode_attention_fp8, mla_fp8_page_bytes, mla_merge_lse,
+               mla_decode_attention, mla_decode_attention_fp8, mla_decode_attention_fp8_planned,
+               mla_decode_attention_planned, mla_decode_plan, mla_fp8_page_bytes, mla_merge_lse,
+               mla_merge_lse_planned,
                mla_prefill_attention, mla_quantize_rows_fp8, mla_workspace_bytes,
                mla_workspace_bytes_cq)
 from . import inputs as I
@@ -102,6 +104,11 @@ class DeviceWorkload:
                 I.fill_device(self.pool, I.stream_key(w.seed, "pool", layer))
         nh = w.n_heads
         B = self.nq      # outputs and scratch are per step token
+        # decode over a length-proportional plan (host-built, copied to the device)
+        self.n_units, self.plan = 0, None
+        if w.plan_units and not self.chunk:
+            self.n_units, plan = mla_decode_plan(self.lens, w.page_size, w.plan_units)
+            self.plan = torch.tensor(plan, dtype=torch.int32, device=self.dev)
         wsa = (mla_append_workspace_bytes_fp8 if self.fp8 else mla_append_workspace_bytes)(self.dims, B)
         self.ws_append = torch.empty(max(1, wsa), dtype=torch.uint8, device=self.dev)
         if outputs_from is not None:     # share scratch/output buffers with another layer
@@ -111,9 +118,13 @@ class DeviceWorkload:
         f32 = torch.float32
         self.q_lat = torch.empty((B, nh, w.d_latent), dtype=f32, device=self.dev)
         self.q_pe = torch.empty((B, nh, w.d_rope), dtype=f32, device=self.dev)
-        self.o_part = torch.empty((B, self.S, nh, w.d_latent), dtype=torch.float32, device=self.dev)
-        self.lse_part = torch.empty((B, self.S, nh), dtype=torch.float32, device=self.dev)
-        if self.S == 1:
+        if self.plan is not None:   # partials per plan unit
+            self.o_part = torch.empty((self.n_units, nh, w.d_latent), dtype=f32, device=self.dev)
+            self.lse_part = torch.empty((self.n_units, nh), dtype=f32, device=self.dev)
+        else:
+            self.o_part = torch.empty((B, self.S, nh, w.d_latent), dtype=f32, device=self.dev)
+            self.lse_part = torch.empty((B, self.S, nh), dtype=f32, device=self.dev)
+        if self.S == 1 and self.plan is None:
             # one split: the merge is the identity, so the split's output (same layout)
             # is the step's o_lat / lse and merge() has nothing to do
             self.o_lat = self.o_part.view(B, nh, w.d_latent)
@@ -185,11 +196,20 @@ class DeviceWorkload:
             mla_prefill_attention(self.dims, self.q_lat, self.q_pe, self.pool, self.block_table,
                                   self.seq_ids, self.pos, self.o_part, self.lse_part, fp8=self.fp8)
             return
+        if self.plan is not None:
+            attend = mla_decode_attention_fp8_planned if self.fp8 else mla_decode_attention_planned
+            attend(self.dims, self.q_lat, self.q_pe, self.pool, self.block_table, self.plan,
+                   self.n_units, self.o_part, self.lse_part)
+            return
         attend = mla_decode_attention_fp8 if self.fp8 else mla_decode_attention
         attend(self.dims, self.q_lat, self.q_pe, self.pool, self.block_table, self.seq_lens,
                self.o_part, self.lse_part)
 
     def merge(self):
+        if self.plan is not None:
+            mla_merge_lse_planned(self.dims, self.o_part, self.lse_part, self.plan, self.n_units,
+                                  self.o_lat, self.lse)
+            return
         if self.S == 1:
             return              # o_lat / lse are the single split's output
         mla_merge_lse(self.dims, self.o_part, self.lse_part, self.o_lat, self.lse)

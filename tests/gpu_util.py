@@ -35,7 +35,7 @@ def assert_parity(got, ref, dtype, what=""):
         assert err <= F32_ABS, f"{what}: max|err| {err:.3e} > {F32_ABS}"
     else:
         rms = np.sqrt(np.mean(ref[fin] ** 2))
-        note(f"  {what}: max|err|/rms {err / rms:.4f} (bound {BF16_REL_RMS})")
+        note(f"  {what}: max|err|/rms {err / rms if rms > 0 else err:.4f} (bound {BF16_REL_RMS})")
         assert err <= BF16_REL_RMS * rms, f"{what}: max|err| {err:.3e} > {BF16_REL_RMS} * rms {rms:.3e}"
     return err
 

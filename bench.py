@@ -81,11 +81,11 @@ def host_info():
     return info
 
 
-def attention_traffic(kernel: str, workload: str):
-    """HBM bytes per attention launch of `kernel` on `workload` (4 splits) from the
-    committed rocprofv3 counter runs (FETCH_SIZE and WRITE_SIZE scaled by a
-    plain-copy calibration), or None when there are none or the kernel source
-    changed since."""
+def attention_traffic(kernel: str, workload: str, units: int):
+    """HBM bytes per attention launch of `kernel` on `workload` from the committed
+    rocprofv3 counter runs (FETCH_SIZE and WRITE_SIZE scaled by a plain-copy
+    calibration), or None when there are none, they were taken with another
+    number of work units, or the kernel source changed since."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
     try:
         rec = json.load(open(path))
@@ -93,6 +93,8 @@ def attention_traffic(kernel: str, workload: str):
     except (OSError, ValueError, KeyError):
         return None
     if hashlib.sha256(src).hexdigest() != rec.get("kernel_source_sha256"):
+        return None
+    if rec.get("attention_units") != units:
         return None
     return rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
 
@@ -270,7 +272,8 @@ def main():
                     "kernel": f"{kernel} (mla_prefill_attention)",
                     "algorithmic_flop_per_launch": attn_flop}
     else:
-        traffic = attention_traffic(kernel, w.name) if S == 4 else None
+        units = dw0.n_units if dw0.plan is not None else B * S
+        traffic = attention_traffic(kernel, w.name, units)
         roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                     "traffic_source": (f"profiles/{kernel}_{w.name}_traffic.json: rocprofv3 "

@@ -43,6 +43,9 @@ def parse():
                         "4 x 256 prompt tokens at context 4096) | full-yarn | long-yarn (YaRN "
                         "RoPE); one layer each unless stated")
     p.add_argument("--splits", type=int, default=0, help="KV splits (0 = workload default)")
+    p.add_argument("--plan-units", type=int, default=-1,
+                   help="target units of a length-proportional attention plan (0 = uniform "
+                        "splits, -1 = workload default)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="budget of the oracle timing on the host (0 disables it)")
     p.add_argument("--attention-only", action="store_true",
@@ -201,6 +204,9 @@ def main():
     from mla_latent_kv_dkv_amd.harness import DeviceWorkload
     M.load()
     w = I.WORKLOADS[args.workload]
+    if args.plan_units >= 0:
+        import dataclasses
+        w = dataclasses.replace(w, plan_units=args.plan_units)
     S = args.splits or w.num_splits
     if w.layers > 1:
         # every layer has its own weights and pool; outputs and scratch are shared

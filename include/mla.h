@@ -422,8 +422,9 @@ int32_t mla_abi_version(void);
 /*
  * Sticky device error word: bit 0 = a block-table entry outside [0, num_pages),
  * bit 1 = a position / length beyond max_pages*page_size or negative (also a bad
- * plan entry or unit range), bit 2 = a sequence index outside [0, n_seqs).  Synchronises `stream`, copies the word
- * to *out and, if clear != 0, resets it.  Returns MLA_ERR_HIP on a runtime error.
+ * plan entry or unit range), bit 2 = a sequence index outside [0, n_seqs).
+ * Synchronises `stream`, copies the word to *out and, if clear != 0, resets it.
+ * Returns MLA_ERR_HIP on a runtime error.
  */
 mla_status mla_device_error(int32_t* out, int32_t clear, hipStream_t stream);
 
@@ -431,7 +432,10 @@ mla_status mla_device_error(int32_t* out, int32_t clear, hipStream_t stream);
  * Kernel selection for the whole process: 0 = automatic (the MFMA kernels where
  * the shape allows, else the plain vector kernels), 1 = plain vector kernels
  * only.  Both compute the same quantities; the switch exists so both can be
- * checked.  Returns the previous value.
+ * checked (a test hook).  It is one process-wide setting, read when each call
+ * is made: it changes the path for every caller in the process, and a call on
+ * another thread concurrent with the switch may take either path.  Returns the
+ * previous value.
  */
 int32_t mla_set_kernel_path(int32_t path);
 

@@ -247,8 +247,7 @@ def main():
             dw.attention()
             if evs is not None:
                 evs[-1][1].record(stream)
-            dw.merge()
-            dw.absorb_out()
+            dw.merge_absorb_out()
 
     for i in range(args.warmup):
         one(i)

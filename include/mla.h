@@ -270,6 +270,30 @@ mla_status mla_absorb_out(const mla_dims* dims, const float* o_lat, const void* 
                           size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * mla_merge_lse and mla_absorb_out as one call ([Report] §2.3: the merged
+ * latent output o_lat is only the input of the W_UV product, so the merge is
+ * folded into that product's operand loads and o_lat is never stored):
+ *   u [batch, H] fp32 = mla_absorb_out of the o_lat that mla_merge_lse (plan
+ *   NULL) or mla_merge_lse_planned (plan != NULL) forms from o_part / lse_part,
+ *   lse [batch, n_h] fp32 (may be NULL) = that merge's lse.
+ * plan NULL: uniform splits, o_part [batch, num_splits, n_h, d_c], lse_part
+ * [batch, num_splits, n_h], n_units ignored.  plan != NULL: the plan of
+ * mla_decode_plan, o_part [n_units, n_h, d_c], lse_part [n_units, n_h],
+ * num_splits ignored; bad ranges as mla_merge_lse_planned.
+ * Workspace: at least mla_merge_absorb_out_workspace_bytes(dims, batch) bytes,
+ * 256-byte aligned.  bf16 runs at n_h % 8 = 0, d_c = 512, d_h % 64 = 0 take the
+ * fused product, whose u and lse are bit-identical to the two calls; other
+ * shapes run the two calls inside (same results).
+ */
+mla_status mla_merge_absorb_out(const mla_dims* dims, const float* o_part, const float* lse_part,
+                                int32_t batch, int32_t num_splits, const int32_t* plan,
+                                int32_t n_units, const void* w_uv, const void* w_o, float* u,
+                                float* lse, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+/* Workspace bytes of mla_merge_absorb_out (0 for bad dims or batch). */
+size_t mla_merge_absorb_out_workspace_bytes(const mla_dims* dims, int32_t batch);
+
+/*
  * mla_absorb_out for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
  * same operation and arguments without the workspace.  Its scratch (the

@@ -27,7 +27,8 @@ __all__ = ["MlaDims", "MlaError", "make_dims", "load", "mla_append_latent", "mla
            "mla_prefill_attention", "mla_prefill_attention_fp8", "mla_absorb_out_noalloc",
            "mla_absorb_out_noalloc_max_bytes", "mla_decode_plan", "mla_decode_plan_capacity",
            "mla_decode_attention_planned", "mla_decode_attention_fp8_planned",
-           "mla_merge_lse_planned", "LIB_PATH"]
+           "mla_merge_lse_planned", "mla_merge_absorb_out", "mla_merge_absorb_out_workspace_bytes",
+           "LIB_PATH"]
 
 
 class MlaDims(ctypes.Structure):
@@ -76,6 +77,8 @@ _SIGS = {
                                          _P, _P],
     "mla_merge_lse_planned": [_DIMS, _P, _P, _P, _I32, _I32, _P, _P, _P],
     "mla_absorb_out": [_DIMS, _P, _P, _P, _I32, _P, _P, _SZ, _P],
+    "mla_merge_absorb_out": [_DIMS, _P, _P, _I32, _I32, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P],
+    "mla_merge_absorb_out_workspace_bytes": [_DIMS, _I32],
     "mla_absorb_out_noalloc": [_DIMS, _P, _P, _P, _I32, _P, _P],
     "mla_absorb_out_noalloc_max_bytes": [],
     "mla_workspace_bytes": [_DIMS, _I32],
@@ -98,6 +101,7 @@ _SIGS = {
 _RES = {"mla_workspace_bytes": _SZ, "mla_workspace_bytes_cq": _SZ, "mla_append_workspace_bytes": _SZ,
         "mla_fp8_page_bytes": _SZ, "mla_append_workspace_bytes_fp8": _SZ,
         "mla_absorb_out_noalloc_max_bytes": _SZ, "mla_decode_plan_capacity": _I64,
+        "mla_merge_absorb_out_workspace_bytes": _SZ,
         "mla_status_string": ctypes.c_char_p}
 
 
@@ -380,6 +384,36 @@ def mla_absorb_out(dims, o_lat, w_uv, w_o, u, workspace, stream=None):
     _expect(u, (B, dims.hidden), torch.float32, "u")
     _check("mla_absorb_out", load().mla_absorb_out(
         ctypes.byref(dims), _ptr(o_lat), _ptr(w_uv), _ptr(w_o), B, _ptr(u), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def mla_merge_absorb_out_workspace_bytes(dims: MlaDims, batch: int) -> int:
+    return int(load().mla_merge_absorb_out_workspace_bytes(ctypes.byref(dims), batch))
+
+
+def mla_merge_absorb_out(dims, o_part, lse_part, w_uv, w_o, u, workspace, lse=None, plan=None,
+                         n_units=0, stream=None):
+    """mla_merge_lse (uniform splits: o_part [B, S, n_h, d_c]; or over a plan:
+    o_part [n_units, n_h, d_c]) then mla_absorb_out, in one call: u, and lse if given."""
+    import torch
+    B, nh, e = u.shape[0], dims.n_heads, _elem(dims)
+    if plan is None:
+        S = o_part.shape[1]
+        _expect(o_part, (B, S, nh, dims.d_latent), torch.float32, "o_part")
+        _expect(lse_part, (B, S, nh), torch.float32, "lse_part")
+    else:
+        S = 1
+        _expect(o_part, (n_units, nh, dims.d_latent), torch.float32, "o_part")
+        _expect(lse_part, (n_units, nh), torch.float32, "lse_part")
+        _expect(plan, (3 * n_units + B + 1,), torch.int32, "plan")
+    _expect(w_uv, (nh * dims.d_head, dims.d_latent), e, "w_uv")
+    _expect(w_o, (dims.hidden, nh * dims.d_head), e, "w_o")
+    _expect(u, (B, dims.hidden), torch.float32, "u")
+    if lse is not None:
+        _expect(lse, (B, nh), torch.float32, "lse")
+    _check("mla_merge_absorb_out", load().mla_merge_absorb_out(
+        ctypes.byref(dims), _ptr(o_part), _ptr(lse_part), B, S, _ptr(plan), n_units, _ptr(w_uv),
+        _ptr(w_o), _ptr(u), _ptr(lse), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
 
 

@@ -324,7 +324,7 @@ __global__ __launch_bounds__(64 * kXsWaves, 1) void k_gemm_xs(GemmArgs a, int d,
   }
   // the RoPE table (split instances): entry blockIdx + grid * tid, once the
   // thread's strips are done (the fp64 angles would otherwise stall the stream)
-  const int tab_e = blockIdx.x + gridDim.x * tid, tab_stride = gridDim.x * 256;
+  const int tab_e = blockIdx.x + gridDim.x * tid, tab_stride = gridDim.x * blockDim.x;
   if (my == 0) {
     if constexpr (kSplit) rope_table_fill(a, tab_e, tab_stride);
     return;
@@ -706,8 +706,20 @@ constexpr int kUwN = 256;   // columns per workgroup of the fp32-X W_UK product
 // (d half w & 1, b half w >> 1) over the 32 k-steps.  The two d halves of a head
 // run on one XCD (workgroups 8 apart), so the second reads X from its L2.
 constexpr int kUvK = 512, kUvN = 64, kUvM = 64;
+// merge: rows per pass, partials per load batch
+constexpr int kUvMergeRows = 8, kUvMergeUnits = 4;
 
-__global__ __launch_bounds__(256, 1) void k_gemm_uv_wide(GemmArgs a) {
+// kMerge: X(b, c) of head i is not read from o_lat but formed from the split
+// partials of row b ([Report] §2.3 absorbs W_UV into the output side, so the
+// merged latent output is only ever an operand of this product): per row, m =
+// max lse_u, w_u = exp(lse_u - m), X = sum_u w_u o_u / sum_u w_u, in the order and
+// arithmetic of k_merge_rows, so the bf16 operand is the one the same product
+// takes from mla_merge_lse's o_lat.  Eight waves form X (twice the loads in
+// flight of four); four of them then run the products as the plain form does.
+// The first half's workgroups write the merged lse when asked for.
+template <bool kMerge>
+__global__ __launch_bounds__(kMerge ? 512 : 256, 1) void k_gemm_uv_wide(GemmArgs a, MergeArgs mg) {
+  constexpr int kWaves = kMerge ? 8 : 4;
   __shared__ __attribute__((aligned(1024))) char lds[(kUvN + kUvM) * 1024];   // W rows, X rows
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -720,14 +732,138 @@ __global__ __launch_bounds__(256, 1) void k_gemm_uv_wide(GemmArgs a) {
   {
     const uint64_t wg = reinterpret_cast<uint64_t>(static_cast<const bf16_t*>(a.w1) +
                                                    head * a.w_bs + static_cast<int64_t>(n0) * a.ldw_n);
-    for (int r = wv; r < kUvN; r += 4) {
+    for (int r = wv; r < kUvN; r += kWaves) {
       const uint32_t voff = static_cast<uint32_t>((static_cast<int64_t>(r) * a.ldw_n +
                                                    8 * (lane ^ (r & 15))) * 2);
       dma_block(wg, voff, wl + 1024 * r);
     }
   }
-  // ---- X rows: 32 float4 per thread in flight, then bf16 into LDS
-  {
+  // X element (b, c) at xl + 1024 b + 16 ((c >> 3) ^ (b & 15)) + 8 ((c >> 2) & 1), bf16
+  auto x_store = [&](int b, int c, float4 v) {
+    const uint32_t addr = xl + 1024 * b + 16 * ((c >> 3) ^ (b & 15)) + 8 * ((c >> 2) & 1);
+    *reinterpret_cast<__attribute__((address_space(3))) u32x2_t*>(static_cast<uintptr_t>(addr)) =
+        (u32x2_t){cvt2(v.x, v.y), cvt2(v.z, v.w)};
+  };
+  if constexpr (kMerge) {
+    // ---- thread: columns c..c+3 of rows 4i + rq (a wave's rows are uniform), in two
+    // passes of kUvMergeRows rows; rows past M repeat the last one.  Per pass the
+    // partials go in batches of kUvMergeUnits per row; a row of at most that many
+    // takes its reference from the same batch, else a first sweep over its lse
+    // finds it.  Lane r U + k of a wave fetches the lse of partial k of the batch
+    // for row r (one load per batch; the values are read back lane by lane).
+    typedef float f32x4_t __attribute__((ext_vector_type(4)));
+    constexpr int R = kUvMergeRows, U = kUvMergeUnits;
+    static_assert(R * U <= 64, "one lse lane per (row, partial) of a batch");
+    const int nh = mg.n_heads;
+    const int c = 4 * (tid & 127), rq = tid >> 7;
+    const float* op = mg.o_part + static_cast<int64_t>(head) * kUvK + c;
+    const float* lp = mg.lse_part + head;
+    const int64_t ustride = static_cast<int64_t>(nh) * kUvK;   // floats between units
+    const bool lead = (tid & 127) == 0 && half == 0;   // writes the rows' lse
+    const int jr = min(lane / U, R - 1), jk = lane % U;   // lse lane: row jr, partial jk
+#pragma unroll 1
+    for (int g = 0; g < kUvM / 4 / R; ++g) {
+      // the lse lane's row: first partial and count (a bad range flagged once per row)
+      int jfirst, jcount;
+      {
+        const int bq = m0 + 4 * (R * g + jr) + rq;
+        const bool flag = (tid & 127) < 64 && lane < R * U && jk == 0 && head == 0 && half == 0 &&
+                          bq < a.M;
+        merge_units(mg, bq < a.M ? bq : a.M - 1, flag, &jfirst, &jcount);
+        if (jcount <= 0) jfirst = 0;   // no partials: unit 0, weight 0
+      }
+      int fr[R], cn[R], cmax = 0;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        fr[r] = __builtin_amdgcn_readlane(jfirst, r * U);
+        cn[r] = __builtin_amdgcn_readlane(jcount, r * U);
+        cmax = max(cmax, cn[r]);
+      }
+      // lse of partial s0 + jk of row jr (-inf past the row's count)
+      auto lse_lane = [&](int s0) {
+        const bool in = s0 + jk < jcount;
+        const float lv = lp[static_cast<int64_t>(in ? jfirst + s0 + jk : jfirst) * nh];
+        return in ? lv : -INFINITY;
+      };
+      float m[R], zz[R];
+      float4 acc[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        m[r] = -INFINITY;
+        zz[r] = 0.f;
+        acc[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      if (cmax > U) {   // the references first
+        for (int s0 = 0; s0 < cmax; s0 += U) {
+          const float lv = lse_lane(s0);
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int k = 0; k < U; ++k)
+              m[r] = fmaxf(m[r], __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                             __builtin_bit_cast(int, lv), r * U + k)));
+        }
+      }
+      for (int s0 = 0; s0 < cmax; s0 += U) {
+        const float lv = lse_lane(s0);
+        f32x4_t x[R][U];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int k = 0; k < U; ++k) {
+            const int u = s0 + k < cn[r] ? fr[r] + s0 + k : fr[r];
+            x[r][k] = *reinterpret_cast<const f32x4_t*>(op + u * ustride);
+          }
+        // every load of the batch is issued before the first is used (the weighted
+        // add below is a select, which the compiler would otherwise turn into a
+        // branch around a load of its own)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int k = 0; k < U; ++k) asm volatile("" : "+v"(x[r][k]));
+        float l[R][U];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int k = 0; k < U; ++k)
+            l[r][k] = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lv), r * U + k));
+        if (cmax <= U) {
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int k = 0; k < U; ++k) m[r] = fmaxf(m[r], l[r][k]);
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int k = 0; k < U; ++k) {
+            // partials past the row's count have l = -inf: weight 0, nothing added
+            const float w = l[r][k] == -INFINITY ? 0.f : __expf(l[r][k] - m[r]);
+            zz[r] += w;
+            const bool on = w != 0.f;
+            float n0 = acc[r].x, n1 = acc[r].y, n2 = acc[r].z, n3 = acc[r].w;
+            n0 += w * x[r][k][0]; n1 += w * x[r][k][1]; n2 += w * x[r][k][2]; n3 += w * x[r][k][3];
+            acc[r].x = on ? n0 : acc[r].x;
+            acc[r].y = on ? n1 : acc[r].y;
+            acc[r].z = on ? n2 : acc[r].z;
+            acc[r].w = on ? n3 : acc[r].w;
+          }
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int row = 4 * (R * g + r) + rq, bq = m0 + row;
+        const float inv = zz[r] > 0.f ? 1.f / zz[r] : 0.f;
+        x_store(row, c, make_float4(acc[r].x * inv, acc[r].y * inv, acc[r].z * inv, acc[r].w * inv));
+        if (lead && mg.lse && bq < a.M)
+          mg.lse[static_cast<int64_t>(bq) * nh + head] =
+              zz[r] > 0.f ? m[r] + __logf(zz[r]) : -INFINITY;
+      }
+    }
+    wait_vmcnt<0>();   // the W copies
+    __syncthreads();
+  } else {
+    // ---- X rows: 32 float4 per thread in flight, then bf16 into LDS
     const float* xb = static_cast<const float*>(a.x) + head * a.x_bs;
     float4 v[32];
 #pragma unroll
@@ -740,14 +876,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_uv_wide(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       const int e = 4 * (256 * i + tid);
-      const int b = e >> 9, c = e & 511;
-      const uint32_t addr = xl + 1024 * b + 16 * ((c >> 3) ^ (b & 15)) + 8 * ((c >> 2) & 1);
-      *reinterpret_cast<__attribute__((address_space(3))) u32x2_t*>(static_cast<uintptr_t>(addr)) =
-          (u32x2_t){cvt2(v[i].x, v[i].y), cvt2(v[i].z, v[i].w)};
+      x_store(e >> 9, e & 511, v[i]);
     }
     wait_vmcnt<0>();   // the W copies
     __syncthreads();
   }
+  if (wv >= 4) return;   // (merge form) waves 4..7 only formed X
 
   // ---- products: wave tile (d rows 32(wv & 1) .., b rows 32(wv >> 1) ..)
   const int j32 = lane & 31, g = lane >> 5;
@@ -1144,6 +1278,22 @@ static bool uv_wide_ok(const GemmArgs& a) {
 
 bool fast_gemm_ok(const GemmArgs& a) { return ws_ok(a) || uk_ok(a); }
 
+// W_UV with the merge folded in: the k_gemm_uv_wide form, the partials of every
+// head at 512 latent columns (16-byte aligned rows), one merge row per product row.
+bool uv_merge_ok(const GemmArgs& a, const MergeArgs& m) {
+  return uv_wide_ok(a) && m.d_latent == kUvK && m.n_heads == a.batch && m.batch == a.M &&
+         m.o_part != nullptr && m.lse_part != nullptr && aligned16(m.o_part) &&
+         (m.unit_start != nullptr || m.num_splits >= 1);
+}
+
+hipError_t launch_uv_merge(const GemmArgs& a, const MergeArgs& m, hipStream_t stream) {
+  if (a.M == 0) return hipSuccess;
+  if (!uv_merge_ok(a, m)) return hipErrorInvalidValue;
+  const dim3 grid(a.batch * (a.N / kUvN), (a.M + kUvM - 1) / kUvM);
+  hipLaunchKernelGGL(k_gemm_uv_wide<true>, grid, dim3(512), 0, stream, a, m);
+  return hipGetLastError();
+}
+
 size_t gemm_partial_bytes(const GemmArgs& a) {
   if (!ws_ok(a) || tile_ok(a) || uv_wide_ok(a) || small_tile_ok(a)) return 0;
   if (xs_ok(a)) {
@@ -1182,7 +1332,7 @@ hipError_t launch_gemm_fast(const GemmArgs& a, void* partial, size_t partial_byt
   }
   if (uv_wide_ok(a)) {
     const dim3 grid(a.batch * (a.N / kUvN), (a.M + kUvM - 1) / kUvM);
-    hipLaunchKernelGGL(k_gemm_uv_wide, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_gemm_uv_wide<false>, grid, dim3(256), 0, stream, a, MergeArgs{});
     return hipGetLastError();
   }
   if (small_tile_ok(a)) {

@@ -26,5 +26,9 @@ hipError_t launch_attention_fp8(const AttnArgs& a, hipStream_t stream);
 
 bool fast_merge_ok(const MergeArgs& a);
 hipError_t launch_merge_fast(const MergeArgs& a, hipStream_t stream);
+// the per-head W_UV product (`a`, as mla_absorb_out sets it up, x unused) with
+// the split merge `m` folded into its operand loads (m.o_lat unused)
+bool uv_merge_ok(const GemmArgs& a, const MergeArgs& m);
+hipError_t launch_uv_merge(const GemmArgs& a, const MergeArgs& m, hipStream_t stream);
 
 }  // namespace mla

@@ -816,6 +816,57 @@ mla_status mla_absorb_out(const mla_dims* d, const float* o_lat, const void* w_u
   return absorb_out_run(d, o_lat, w_uv, w_o, batch, u, ws, ws_bytes, stream);
 }
 
+size_t mla_merge_absorb_out_workspace_bytes(const mla_dims* d, int32_t batch) {
+  if (check_dims(d) != MLA_OK || batch < 0 || batch > 65535) return 0;
+  return align256(mla_workspace_bytes(d, batch)) +
+         align256(static_cast<size_t>(batch) * d->n_heads * d->d_latent * sizeof(float));
+}
+
+mla_status mla_merge_absorb_out(const mla_dims* d, const float* o_part, const float* lse_part,
+                                int32_t batch, int32_t num_splits, const int32_t* plan,
+                                int32_t n_units, const void* w_uv, const void* w_o, float* u,
+                                float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || batch > 65535) return MLA_ERR_SHAPE;
+  if (plan) {
+    if ((st = plan_args(plan, n_units)) != MLA_OK) return st;
+  } else if (num_splits < 1 || num_splits > 4096) {
+    return MLA_ERR_SHAPE;
+  }
+  if (batch == 0) return MLA_OK;
+  if (!o_part || !lse_part || !w_uv || !w_o || !u) return MLA_ERR_NULL;
+  if (!ws || ws_bytes < mla_merge_absorb_out_workspace_bytes(d, batch) || !ws_aligned(ws))
+    return MLA_ERR_WORKSPACE;
+  // workspace: [mla_absorb_out's region][o_lat, fp32: the merged rows where the
+  // merge runs on its own]
+  const size_t base = align256(mla_workspace_bytes(d, batch));
+  float* o_lat = reinterpret_cast<float*>(static_cast<char*>(ws) + base);
+  mla::MergeArgs m{};
+  m.o_part = o_part; m.lse_part = lse_part; m.batch = batch;
+  m.num_splits = plan ? 1 : num_splits;
+  m.n_heads = d->n_heads; m.d_latent = d->d_latent; m.o_lat = o_lat; m.lse = lse;
+  m.unit_start = plan ? plan + 3 * static_cast<int64_t>(n_units) : nullptr;
+  m.units = plan ? n_units : batch * num_splits;
+  m.err = err_word();
+  if (!m.err) return MLA_ERR_HIP;
+  mla::GemmArgs g = uv_args(d, batch);
+  g.x = o_part; g.w1 = w_uv; g.w2 = w_uv; g.y = ws;
+  if (use_fast() && d->dtype == MLA_BF16 && mla::uv_merge_ok(g, m)) {
+    // 1) o = W_UV,i (merged partials) per head, the merge inside the product -> workspace
+    if (mla::launch_uv_merge(g, m, stream) != hipSuccess) return MLA_ERR_HIP;
+    // 2) u = o W_O^T
+    mla::GemmArgs a = oproj_args(d, batch);
+    a.x = ws; a.w1 = w_o; a.w2 = w_o; a.y = u;
+    return hip_status(run_gemm(d, a, static_cast<char*>(ws) + act_bytes(d, batch),
+                               base - act_bytes(d, batch), stream));
+  }
+  st = merge_run(d, o_part, lse_part, batch, m.num_splits, m.unit_start, m.units, o_lat, lse,
+                 stream);
+  if (st != MLA_OK) return st;
+  return absorb_out_run(d, o_lat, w_uv, w_o, batch, u, ws, base, stream);
+}
+
 size_t mla_absorb_out_noalloc_max_bytes(void) { return kScratchBytes; }
 
 mla_status mla_absorb_out_noalloc(const mla_dims* d, const float* o_lat, const void* w_uv,

@@ -13,7 +13,7 @@ from . import (make_dims, mla_absorb_out, mla_absorb_q, mla_absorb_q_append, mla
                mla_append_latent_fp8, mla_append_workspace_bytes, mla_append_workspace_bytes_fp8,
                mla_decode_attention, mla_decode_attention_fp8, mla_decode_attention_fp8_planned,
                mla_decode_attention_planned, mla_decode_plan, mla_fp8_page_bytes, mla_merge_lse,
-               mla_merge_lse_planned,
+               mla_merge_lse_planned, mla_merge_absorb_out, mla_merge_absorb_out_workspace_bytes,
                mla_prefill_attention, mla_quantize_rows_fp8, mla_workspace_bytes,
                mla_workspace_bytes_cq)
 from . import inputs as I
@@ -133,7 +133,8 @@ class DeviceWorkload:
             self.o_lat = torch.empty((B, nh, w.d_latent), dtype=f32, device=self.dev)
             self.lse = torch.empty((B, nh), dtype=torch.float32, device=self.dev)
         self.u = torch.empty((B, w.hidden), dtype=f32, device=self.dev)
-        ws_bytes = mla_workspace_bytes(self.dims, B)
+        ws_bytes = max(mla_workspace_bytes(self.dims, B),
+                       mla_merge_absorb_out_workspace_bytes(self.dims, B))
         if w.d_cq:
             ws_bytes = max(ws_bytes, mla_workspace_bytes_cq(self.dims, w.d_cq, B))
         self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=self.dev)
@@ -218,13 +219,35 @@ class DeviceWorkload:
         mla_absorb_out(self.dims, self.o_lat, self.weights["w_uv"], self.weights["w_o"], self.u,
                        self.ws)
 
+    def merge_absorb_out(self):
+        """merge then absorb_out as one call (the merged o_lat is not stored; lse is)."""
+        if self.plan is not None:
+            mla_merge_absorb_out(self.dims, self.o_part, self.lse_part, self.weights["w_uv"],
+                                 self.weights["w_o"], self.u, self.ws, lse=self.lse,
+                                 plan=self.plan, n_units=self.n_units)
+            return
+        # one split: lse is the split's own (a view of lse_part), nothing to write
+        mla_merge_absorb_out(self.dims, self.o_part, self.lse_part, self.weights["w_uv"],
+                             self.weights["w_o"], self.u, self.ws,
+                             lse=None if self.S == 1 else self.lse)
+
+    def merge_o_lat(self):
+        """Store the merged o_lat of the last attention (the step's fused merge +
+        absorb_out does not): mla_merge_lse of the same partials, lse left as the
+        step wrote it."""
+        if self.plan is not None:
+            mla_merge_lse_planned(self.dims, self.o_part, self.lse_part, self.plan, self.n_units,
+                                  self.o_lat, None)
+        elif self.S > 1:
+            mla_merge_lse(self.dims, self.o_part, self.lse_part, self.o_lat, None)
+
     def step(self):
         """absorb_q -> append (decode token at L-1) -> attention -> merge -> absorb_out
-        (the first two as one call where the pool format and query form allow)."""
+        (the first two as one call where the pool format and query form allow, the
+        last two as one call)."""
         self.query_and_append()
         self.attention()
-        self.merge()
-        self.absorb_out()
+        self.merge_absorb_out()
         return self.u
 
     # ---- host copies of the same inputs, for the oracle ------------------

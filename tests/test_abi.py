@@ -214,3 +214,27 @@ def test_device_fill_argument_checks():
     assert lib.mla_fill_normal(None, 0, 0, 1, 0, 1.0, None) == 0
     assert lib.mla_fill_normal(None, 5, 0, 1, 0, 1.0, None) == -1
     assert lib.mla_fill_normal(P, 5, 9, 1, 0, 1.0, None) == -3
+
+
+def test_merge_absorb_out_argument_checks():
+    lib = M.load()
+    d = _dims(dtype="bf16")
+    dp = ctypes.byref(d)
+    misaligned = ctypes.c_void_p(0x1008)
+    big = 1 << 24
+    need = M.mla_merge_absorb_out_workspace_bytes(d, 8)
+    # room for mla_absorb_out's scratch and one fp32 o_lat
+    assert need >= M.mla_workspace_bytes(d, 8) + 8 * d.n_heads * d.d_latent * 4
+    assert M.mla_merge_absorb_out_workspace_bytes(d, -1) == 0
+    assert M.mla_merge_absorb_out_workspace_bytes(_dims(d_rope=7), 8) == 0
+    # (dims, o_part, lse_part, batch, num_splits, plan, n_units, w_uv, w_o, u, lse, ws, bytes, stream)
+    f = lib.mla_merge_absorb_out
+    assert f(dp, P, P, -1, 2, None, 0, P, P, P, None, P, big, None) == -2
+    assert f(dp, P, P, 8, 0, None, 0, P, P, P, None, P, big, None) == -2     # no splits
+    assert f(dp, P, P, 8, 0, P, 7, P, P, P, None, P, big, None) == -2        # plan of 7 units
+    assert f(dp, P, P, 8, 0, P, 12, P, P, P, None, P, big, None) == -2       # not a multiple of 8
+    assert f(dp, None, P, 8, 2, None, 0, P, P, P, None, P, big, None) == -1
+    assert f(dp, P, P, 8, 2, None, 0, P, None, P, None, P, big, None) == -1
+    assert f(dp, P, P, 8, 2, None, 0, P, P, P, None, P, need - 1, None) == -4
+    assert f(dp, P, P, 8, 2, None, 0, P, P, P, None, misaligned, big, None) == -4
+    assert f(dp, None, None, 0, 2, None, 0, None, None, None, None, None, 0, None) == 0

@@ -33,15 +33,19 @@ def _context_rows(dw: DeviceWorkload, b: int, hw) -> np.ndarray:
     return rows
 
 
-def _check(dw: DeviceWorkload, seqs, full_def=(), hw=None, path=0):
+def _check(dw: DeviceWorkload, seqs, full_def=(), hw=None, path=0, merge=True):
     """Compare u, q_lat, o_lat and lse of sequences ``seqs`` with the absorbed fp64
-    companion and, for ``full_def``, u with the non-absorbed definition.  Where the
+    companion and, for ``full_def``, u with the non-absorbed definition (o_lat, which
+    the step's fused merge does not store, merged from the step's partials first
+    unless ``merge`` is False: already done by the caller).  Where the
     attention runs on a matrix-core kernel, which rounds the queries it is handed
     to bf16 (its stated input precision), o_lat is compared with the oracle's
     attention over the oracle's own queries rounded the same way; u, q_lat and lse
     are always held against the exact oracle."""
     w = dw.w
     hw = hw or dw.host_weights()
+    if merge:
+        dw.merge_o_lat()
     got = {k: to_np(getattr(dw, k)) for k in ("u", "q_lat", "o_lat", "lse")}
     ref = {k: [] for k in got}
     rounded = attention_rounds_queries(w, path)
@@ -143,6 +147,7 @@ def test_step_ragged_60_layers():
     for l, dw in enumerate(layers):
         dw.step()
         if l in (0, w.layers - 1):
+            dw.merge_o_lat()     # the layers share their partials: merge this layer's now
             saved[l] = {k: getattr(dw, k).clone() for k in ("u", "q_lat", "o_lat", "lse")}
     torch.cuda.synchronize()
     assert M.mla_device_error() == 0
@@ -154,7 +159,7 @@ def test_step_ragged_60_layers():
         for k, v in outs.items():
             setattr(dw, k, v)
         note(f"oracle layer {l}")
-        _check(dw, seqs, full_def=full_def[l])
+        _check(dw, seqs, full_def=full_def[l], merge=False)
 
 
 @pytest.mark.parametrize("path", [0, 1])

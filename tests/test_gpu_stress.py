@@ -315,6 +315,7 @@ def test_step_twice_is_bit_identical():
     outs = []
     for _ in range(2):
         dw.step()
+        dw.merge_o_lat()
         torch.cuda.synchronize()
         outs.append({k: getattr(dw, k).clone() for k in ("u", "q_lat", "o_lat", "lse")})
     for k in outs[0]:

@@ -707,7 +707,7 @@ constexpr int kUwN = 256;   // columns per workgroup of the fp32-X W_UK product
 // run on one XCD (workgroups 8 apart), so the second reads X from its L2.
 constexpr int kUvK = 512, kUvN = 64, kUvM = 64;
 // merge: rows per pass, partials per load batch
-constexpr int kUvMergeRows = 8, kUvMergeUnits = 4;
+constexpr int kUvMergeRows = 2, kUvMergeUnits = 4;
 
 // kMerge: X(b, c) of head i is not read from o_lat but formed from the split
 // partials of row b ([Report] §2.3 absorbs W_UV into the output side, so the
@@ -745,15 +745,28 @@ __global__ __launch_bounds__(kMerge ? 512 : 256, 1) void k_gemm_uv_wide(GemmArgs
         (u32x2_t){cvt2(v.x, v.y), cvt2(v.z, v.w)};
   };
   if constexpr (kMerge) {
-    // ---- thread: columns c..c+3 of rows 4i + rq (a wave's rows are uniform), in two
-    // passes of kUvMergeRows rows; rows past M repeat the last one.  Per pass the
-    // partials go in batches of kUvMergeUnits per row; a row of at most that many
-    // takes its reference from the same batch, else a first sweep over its lse
-    // finds it.  Lane r U + k of a wave fetches the lse of partial k of the batch
-    // for row r (one load per batch; the values are read back lane by lane).
+    // ---- the partials of every row of the block: first unit and count (rows past M
+    // repeat the last one; a bad range is flagged once, by head 0)
+    __shared__ int st_first[kUvM], st_count[kUvM];
+    if (tid < kUvM) {
+      const int bq = m0 + tid;
+      int first, count;
+      merge_units(mg, bq < a.M ? bq : a.M - 1, head == 0 && half == 0 && bq < a.M, &first, &count);
+      st_first[tid] = count > 0 ? first : 0;   // no partials: unit 0, weight 0
+      st_count[tid] = count;
+    }
+    __syncthreads();
+    // ---- thread: columns c..c+3 of rows 4i + rq (a wave's rows are uniform), in
+    // passes of R rows.  A pass reads the partials in batches of U per row, each
+    // batch one load per (row, partial) plus one lse load per wave (lane r U + k
+    // fetches partial k of row r; the values are read back lane by lane).  A row of
+    // at most U partials takes its reference from its one batch, else a first sweep
+    // over its lse finds it.  (Small batches measured fastest: 2 rows x 4 partials
+    // per pass beat 8 x 4, 4 x 4 and 1 x 4, and issuing the next pass's batch
+    // before combining the current one gained nothing.)
     typedef float f32x4_t __attribute__((ext_vector_type(4)));
-    constexpr int R = kUvMergeRows, U = kUvMergeUnits;
-    static_assert(R * U <= 64, "one lse lane per (row, partial) of a batch");
+    constexpr int R = kUvMergeRows, U = kUvMergeUnits, P = kUvM / 4 / R;
+    static_assert(R * U <= 64 && P * R * 4 == kUvM, "merge batch shape");
     const int nh = mg.n_heads;
     const int c = 4 * (tid & 127), rq = tid >> 7;
     const float* op = mg.o_part + static_cast<int64_t>(head) * kUvK + c;
@@ -761,30 +774,52 @@ __global__ __launch_bounds__(kMerge ? 512 : 256, 1) void k_gemm_uv_wide(GemmArgs
     const int64_t ustride = static_cast<int64_t>(nh) * kUvK;   // floats between units
     const bool lead = (tid & 127) == 0 && half == 0;   // writes the rows' lse
     const int jr = min(lane / U, R - 1), jk = lane % U;   // lse lane: row jr, partial jk
-#pragma unroll 1
-    for (int g = 0; g < kUvM / 4 / R; ++g) {
-      // the lse lane's row: first partial and count (a bad range flagged once per row)
-      int jfirst, jcount;
-      {
-        const int bq = m0 + 4 * (R * g + jr) + rq;
-        const bool flag = (tid & 127) < 64 && lane < R * U && jk == 0 && head == 0 && half == 0 &&
-                          bq < a.M;
-        merge_units(mg, bq < a.M ? bq : a.M - 1, flag, &jfirst, &jcount);
-        if (jcount <= 0) jfirst = 0;   // no partials: unit 0, weight 0
-      }
-      int fr[R], cn[R], cmax = 0;
+    struct Batch {
+      f32x4_t x[R][U];
+      float lv;
+    };
+    auto row_of = [&](int p, int r) { return 4 * (R * p + r) + rq; };
+    // lse of partial s0 + jk of the lse lane's row of pass p (-inf past its count)
+    auto lse_lane = [&](int p, int s0) {
+      const int row = row_of(p, jr), f = st_first[row];
+      const bool in = s0 + jk < st_count[row];
+      const float lv = lp[static_cast<int64_t>(in ? f + s0 + jk : f) * nh];
+      return in ? lv : -INFINITY;
+    };
+    auto load = [&](int p, int s0, Batch& bt) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        fr[r] = __builtin_amdgcn_readlane(jfirst, r * U);
-        cn[r] = __builtin_amdgcn_readlane(jcount, r * U);
-        cmax = max(cmax, cn[r]);
+        const int row = row_of(p, r);
+        const int f = __builtin_amdgcn_readfirstlane(st_first[row]);
+        const int n = __builtin_amdgcn_readfirstlane(st_count[row]);
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+          const int u = s0 + k < n ? f + s0 + k : f;
+          bt.x[r][k] = *reinterpret_cast<const f32x4_t*>(op + u * ustride);
+        }
       }
-      // lse of partial s0 + jk of row jr (-inf past the row's count)
-      auto lse_lane = [&](int s0) {
-        const bool in = s0 + jk < jcount;
-        const float lv = lp[static_cast<int64_t>(in ? jfirst + s0 + jk : jfirst) * nh];
-        return in ? lv : -INFINITY;
-      };
+      bt.lv = lse_lane(p, s0);
+    };
+    // every load of a batch is issued before its first use (the weighted add below
+    // is a select, which the compiler would otherwise turn into a branch around a
+    // load of its own)
+    auto settle = [&](Batch& bt) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int k = 0; k < U; ++k) asm volatile("" : "+v"(bt.x[r][k]));
+    };
+    auto lse_at = [&](float lv, int r, int k) {
+      return __builtin_bit_cast(float,
+                                __builtin_amdgcn_readlane(__builtin_bit_cast(int, lv), r * U + k));
+    };
+    Batch cur;
+#pragma unroll 1
+    for (int p = 0; p < P; ++p) {
+      int cmax = 0;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        cmax = max(cmax, __builtin_amdgcn_readfirstlane(st_count[row_of(p, r)]));
       float m[R], zz[R];
       float4 acc[R];
 #pragma unroll
@@ -795,39 +830,21 @@ __global__ __launch_bounds__(kMerge ? 512 : 256, 1) void k_gemm_uv_wide(GemmArgs
       }
       if (cmax > U) {   // the references first
         for (int s0 = 0; s0 < cmax; s0 += U) {
-          const float lv = lse_lane(s0);
+          const float lv = lse_lane(p, s0);
 #pragma unroll
           for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int k = 0; k < U; ++k)
-              m[r] = fmaxf(m[r], __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                                             __builtin_bit_cast(int, lv), r * U + k)));
+            for (int k = 0; k < U; ++k) m[r] = fmaxf(m[r], lse_at(lv, r, k));
         }
       }
       for (int s0 = 0; s0 < cmax; s0 += U) {
-        const float lv = lse_lane(s0);
-        f32x4_t x[R][U];
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-          for (int k = 0; k < U; ++k) {
-            const int u = s0 + k < cn[r] ? fr[r] + s0 + k : fr[r];
-            x[r][k] = *reinterpret_cast<const f32x4_t*>(op + u * ustride);
-          }
-        // every load of the batch is issued before the first is used (the weighted
-        // add below is a select, which the compiler would otherwise turn into a
-        // branch around a load of its own)
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-          for (int k = 0; k < U; ++k) asm volatile("" : "+v"(x[r][k]));
+        load(p, s0, cur);
+        settle(cur);
         float l[R][U];
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
-          for (int k = 0; k < U; ++k)
-            l[r][k] = __builtin_bit_cast(
-                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lv), r * U + k));
+          for (int k = 0; k < U; ++k) l[r][k] = lse_at(cur.lv, r, k);
         if (cmax <= U) {
 #pragma unroll
           for (int r = 0; r < R; ++r)
@@ -843,7 +860,8 @@ __global__ __launch_bounds__(kMerge ? 512 : 256, 1) void k_gemm_uv_wide(GemmArgs
             zz[r] += w;
             const bool on = w != 0.f;
             float n0 = acc[r].x, n1 = acc[r].y, n2 = acc[r].z, n3 = acc[r].w;
-            n0 += w * x[r][k][0]; n1 += w * x[r][k][1]; n2 += w * x[r][k][2]; n3 += w * x[r][k][3];
+            n0 += w * cur.x[r][k][0]; n1 += w * cur.x[r][k][1];
+            n2 += w * cur.x[r][k][2]; n3 += w * cur.x[r][k][3];
             acc[r].x = on ? n0 : acc[r].x;
             acc[r].y = on ? n1 : acc[r].y;
             acc[r].z = on ? n2 : acc[r].z;
@@ -852,7 +870,7 @@ __global__ __launch_bounds__(kMerge ? 512 : 256, 1) void k_gemm_uv_wide(GemmArgs
       }
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const int row = 4 * (R * g + r) + rq, bq = m0 + row;
+        const int row = row_of(p, r), bq = m0 + row;
         const float inv = zz[r] > 0.f ? 1.f / zz[r] : 0.f;
         x_store(row, c, make_float4(acc[r].x * inv, acc[r].y * inv, acc[r].z * inv, acc[r].w * inv));
         if (lead && mg.lse && bq < a.M)

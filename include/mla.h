@@ -281,9 +281,13 @@ mla_status mla_absorb_out(const mla_dims* dims, const float* o_lat, const void* 
  * mla_decode_plan, o_part [n_units, n_h, d_c], lse_part [n_units, n_h],
  * num_splits ignored; bad ranges as mla_merge_lse_planned.
  * Workspace: at least mla_merge_absorb_out_workspace_bytes(dims, batch) bytes,
- * 256-byte aligned.  bf16 runs at n_h % 8 = 0, d_c = 512, d_h % 64 = 0 take the
+ * 256-byte aligned.  bf16 decode batches (batch <= 64) at n_h % 8 = 0,
+ * n_h * d_h / 64 >= 256, d_c = 512, with a plan or at most 16 splits take the
  * fused product, whose u and lse are bit-identical to the two calls; other
- * shapes run the two calls inside (same results).
+ * shapes run the two calls inside (same results).  One uniform split (and no
+ * plan) merges nothing: o_part is taken as o_lat and lse_part copied to lse,
+ * which is what the merge gives for partials as the attention calls write them
+ * (an empty split has lse -inf and o 0).
  */
 mla_status mla_merge_absorb_out(const mla_dims* dims, const float* o_part, const float* lse_part,
                                 int32_t batch, int32_t num_splits, const int32_t* plan,

@@ -745,19 +745,20 @@ __global__ __launch_bounds__(kMerge ? 512 : 256, 1) void k_gemm_uv_wide(GemmArgs
         (u32x2_t){cvt2(v.x, v.y), cvt2(v.z, v.w)};
   };
   if constexpr (kMerge) {
-    // ---- the partials of every row of the block: first unit and count (rows past M
-    // repeat the last one; a bad range is flagged once, by head 0)
+    // ---- the partials of every row of the block: first unit and count (a bad range
+    // is flagged once, by head 0)
     __shared__ int st_first[kUvM], st_count[kUvM];
     if (tid < kUvM) {
       const int bq = m0 + tid;
-      int first, count;
-      merge_units(mg, bq < a.M ? bq : a.M - 1, head == 0 && half == 0 && bq < a.M, &first, &count);
+      int first = 0, count = 0;   // rows past M: no partials (zero X rows, never stored)
+      if (bq < a.M) merge_units(mg, bq, head == 0 && half == 0, &first, &count);
       st_first[tid] = count > 0 ? first : 0;   // no partials: unit 0, weight 0
       st_count[tid] = count;
     }
     __syncthreads();
     // ---- thread: columns c..c+3 of rows 4i + rq (a wave's rows are uniform), in
-    // passes of R rows.  A pass reads the partials in batches of U per row, each
+    // passes of R rows (a pass whose rows are all past M reads nothing).  A pass
+    // reads the partials in batches of U per row, each
     // batch one load per (row, partial) plus one lse load per wave (lane r U + k
     // fetches partial k of row r; the values are read back lane by lane).  A row of
     // at most U partials takes its reference from its one batch, else a first sweep
@@ -1287,14 +1288,16 @@ static bool small_tile_ok(const GemmArgs& a) {
 // The per-head W_UV form for an fp32 X and bf16 output: K = 512, N a multiple of
 // 64, heads a multiple of 8 (XCD pairing), rows 16-byte aligned, bf16 stores of 8 bytes.
 static bool uv_wide_ok(const GemmArgs& a) {
-  return ws_ok(a) && a.epi == EPI_STORE && a.x_f32 && !a.y_f32 && a.K == kUvK &&
-         a.N % kUvN == 0 && a.batch % 8 == 0 && a.n_split >= a.N && a.x_bs % 4 == 0 &&
-         a.ldx_m % 4 == 0 && a.ldy % 4 == 0 && a.y_bs % 4 == 0 &&
-         (reinterpret_cast<uintptr_t>(a.y) & 7) == 0 &&
+  return a.ldw_k == 1 && a.ldx_k == 1 && a.M > 0 && a.N > 0 && a.batch > 0 &&
+         a.epi == EPI_STORE && a.x_f32 && !a.y_f32 && a.K == kUvK && a.N % kUvN == 0 &&
+         a.batch % 8 == 0 && a.n_split >= a.N && a.ldw_n % 8 == 0 && a.w_bs % 8 == 0 &&
+         a.x_bs % 4 == 0 && a.ldx_m % 4 == 0 && a.ldy % 4 == 0 && a.y_bs % 4 == 0 &&
+         aligned16(a.x) && aligned16(a.w1) && (reinterpret_cast<uintptr_t>(a.y) & 7) == 0 &&
+         static_cast<int64_t>(a.batch) * a.M * a.N < (int64_t{1} << 31) &&
          static_cast<int64_t>(a.batch) * (a.N / kUvN) < 65536;
 }
 
-bool fast_gemm_ok(const GemmArgs& a) { return ws_ok(a) || uk_ok(a); }
+bool fast_gemm_ok(const GemmArgs& a) { return ws_ok(a) || uk_ok(a) || uv_wide_ok(a); }
 
 // W_UV with the merge folded in: the k_gemm_uv_wide form, the partials of every
 // head at 512 latent columns (16-byte aligned rows), one merge row per product row.
@@ -1302,6 +1305,16 @@ bool uv_merge_ok(const GemmArgs& a, const MergeArgs& m) {
   return uv_wide_ok(a) && m.d_latent == kUvK && m.n_heads == a.batch && m.batch == a.M &&
          m.o_part != nullptr && m.lse_part != nullptr && aligned16(m.o_part) &&
          (m.unit_start != nullptr || m.num_splits >= 1);
+}
+
+// Where the fused form is the faster one (measured): decode batches (one 64-row
+// block), a grid that covers the chip, and few partials per row.  Larger batches
+// (a tiled W_UV, and many more merge rows) and small grids (16 heads) go faster as
+// the two separate kernels, and so do long rows of uniform splits (64 per row),
+// which a workgroup would merge serially.
+bool uv_merge_pays(const GemmArgs& a, const MergeArgs& m) {
+  return a.M <= kUvM && static_cast<int64_t>(a.batch) * (a.N / kUvN) >= 256 &&
+         (m.unit_start != nullptr || m.num_splits <= 16);
 }
 
 hipError_t launch_uv_merge(const GemmArgs& a, const MergeArgs& m, hipStream_t stream) {
@@ -1327,6 +1340,11 @@ hipError_t launch_gemm_fast(const GemmArgs& a, void* partial, size_t partial_byt
   if (a.M == 0 || a.N == 0 || a.batch == 0) return hipSuccess;
   if (a.epi == EPI_QPROJ_APPEND && !xs_ok(a)) return hipErrorInvalidValue;
   if (!ws_ok(a)) {
+    if (uv_wide_ok(a)) {   // small batches, whose K granule the weight stream does not take
+      const dim3 grid(a.batch * (a.N / kUvN), (a.M + kUvM - 1) / kUvM);
+      hipLaunchKernelGGL(k_gemm_uv_wide<false>, grid, dim3(256), 0, stream, a, MergeArgs{});
+      return hipGetLastError();
+    }
     if (!uk_ok(a)) return hipErrorInvalidValue;
     if (uk_wide_ok(a)) {
       dim3 grid(a.batch, a.N / kUwN, (a.M + kUwM - 1) / kUwM);

@@ -29,6 +29,8 @@ hipError_t launch_merge_fast(const MergeArgs& a, hipStream_t stream);
 // the per-head W_UV product (`a`, as mla_absorb_out sets it up, x unused) with
 // the split merge `m` folded into its operand loads (m.o_lat unused)
 bool uv_merge_ok(const GemmArgs& a, const MergeArgs& m);
+// the shapes where the fused form beats the merge and the product run apart
+bool uv_merge_pays(const GemmArgs& a, const MergeArgs& m);
 hipError_t launch_uv_merge(const GemmArgs& a, const MergeArgs& m, hipStream_t stream);
 
 }  // namespace mla

@@ -850,9 +850,18 @@ mla_status mla_merge_absorb_out(const mla_dims* d, const float* o_part, const fl
   m.units = plan ? n_units : batch * num_splits;
   m.err = err_word();
   if (!m.err) return MLA_ERR_HIP;
+  if (!plan && num_splits == 1) {
+    // one split: the merge is the identity (weight exp(0) = 1, sum 1), so the
+    // partials are o_lat and lse_part is lse
+    if (lse && lse != lse_part &&
+        hipMemcpyAsync(lse, lse_part, sizeof(float) * batch * d->n_heads,
+                       hipMemcpyDeviceToDevice, stream) != hipSuccess)
+      return MLA_ERR_HIP;
+    return absorb_out_run(d, o_part, w_uv, w_o, batch, u, ws, base, stream);
+  }
   mla::GemmArgs g = uv_args(d, batch);
   g.x = o_part; g.w1 = w_uv; g.w2 = w_uv; g.y = ws;
-  if (use_fast() && d->dtype == MLA_BF16 && mla::uv_merge_ok(g, m)) {
+  if (use_fast() && d->dtype == MLA_BF16 && mla::uv_merge_ok(g, m) && mla::uv_merge_pays(g, m)) {
     // 1) o = W_UV,i (merged partials) per head, the merge inside the product -> workspace
     if (mla::launch_uv_merge(g, m, stream) != hipSuccess) return MLA_ERR_HIP;
     // 2) u = o W_O^T

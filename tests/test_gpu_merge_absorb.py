@@ -98,8 +98,10 @@ def _oracle_rows(w, host, o_h, l_h, groups):
     return np.stack(us), np.stack(ls)
 
 
-@pytest.mark.parametrize("name,B,S", [("full", 6, 4), ("full", 70, 3), ("lite", 9, 8),
-                                      ("tiny", 5, 3)])
+# full B = 6, S = 4: the fused product; S = 1: no merge at all; B = 70 (past one 64-row
+# block), S = 64 (long rows), lite (a small grid) and tiny (fp32): the two calls inside
+@pytest.mark.parametrize("name,B,S", [("full", 6, 4), ("full", 6, 1), ("full", 70, 3),
+                                      ("full", 3, 64), ("lite", 9, 8), ("tiny", 5, 3)])
 @pytest.mark.parametrize("path", PATHS)
 def test_merge_absorb_out_uniform(name, B, S, path):
     w = I.WORKLOADS[name]
@@ -111,6 +113,8 @@ def test_merge_absorb_out_uniform(name, B, S, path):
     empty = np.zeros((B * S, nh), dtype=bool)
     empty.reshape(B, S, nh)[1, ::2] = True       # every other split of row 1
     empty.reshape(B, S, nh)[2, :, 0] = True      # every split of (row 2, head 0)
+    if S > 1:
+        empty.reshape(B, S, nh)[0, 1:] = True    # row 0: one live split
     o, lse, o_h, l_h = _partials(w, B * S, nh, empty)
     o4, lse3 = o.view(B, S, nh, w.d_latent), lse.view(B, S, nh)
     M.mla_device_error(clear=True)

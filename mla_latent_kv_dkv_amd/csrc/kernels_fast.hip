@@ -1539,6 +1539,74 @@ __global__ __launch_bounds__(256) void k_merge_rows(MergeArgs a, int rows) {
   if (a.lse && lane == 0) a.lse[row] = z > 0.f ? m + __logf(z) : -INFINITY;
 }
 
+// Rows of many uniform splits (64 per row at 128K context): one workgroup per
+// (b, i) row, wave w weighing splits w, w + 4, ... in batches of kMergeWideB (every
+// load of a batch in flight at once), the four partial sums added in a fixed order
+// through LDS.  Same weights as k_merge_rows; the sums go in another (fixed) order.
+// d_c = 512: a lane holds float4 columns lane and lane + 64.
+constexpr int kMergeWideS = 16;   // uniform splits above this take the wide form
+constexpr int kMergeWideB = 8;    // splits per load batch of a wave
+
+__global__ __launch_bounds__(256) void k_merge_rows_wide(MergeArgs a) {
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  __shared__ f32x4_t part[4][128];
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nh = a.n_heads, S = a.num_splits;
+  const int b = row / nh, i = row - b * nh;
+  const float* lse = a.lse_part + static_cast<int64_t>(b) * S * nh + i;
+  float m = -INFINITY;
+  for (int s = lane; s < S; s += 64) m = fmaxf(m, lse[static_cast<int64_t>(s) * nh]);
+  m = wave_max(m);
+  float z = 0.f;
+  for (int s = lane; s < S; s += 64) {
+    const float l = lse[static_cast<int64_t>(s) * nh];
+    z += (m == -INFINITY || l == -INFINITY) ? 0.f : __expf(l - m);
+  }
+  z = wave_sum(z);
+  const f32x4_t* src =
+      reinterpret_cast<const f32x4_t*>(a.o_part) + (static_cast<int64_t>(b) * S * nh + i) * 128;
+  const int64_t split_stride = static_cast<int64_t>(nh) * 128;   // float4s between splits
+  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  if (m != -INFINITY) {
+    for (int s0 = wv; s0 < S; s0 += 4 * kMergeWideB) {
+      f32x4_t x0[kMergeWideB], x1[kMergeWideB];
+      float w[kMergeWideB];
+#pragma unroll
+      for (int j = 0; j < kMergeWideB; ++j) {
+        const int s = s0 + 4 * j;
+        const int sc = s < S ? s : s0;   // past S: reload split s0, weight 0
+        x0[j] = src[sc * split_stride + lane];
+        x1[j] = src[sc * split_stride + lane + 64];
+        const float l = lse[static_cast<int64_t>(sc) * nh];
+        w[j] = (s >= S || l == -INFINITY) ? 0.f : __expf(l - m);
+      }
+      // the whole batch is issued before its first use (the skip of a zero weight
+      // below is a select, which the compiler would otherwise turn into a branch
+      // around a load of its own)
+#pragma unroll
+      for (int j = 0; j < kMergeWideB; ++j) {
+        asm volatile("" : "+v"(x0[j]));
+        asm volatile("" : "+v"(x1[j]));
+      }
+#pragma unroll
+      for (int j = 0; j < kMergeWideB; ++j) {
+        const f32x4_t n0 = acc0 + w[j] * x0[j], n1 = acc1 + w[j] * x1[j];
+        acc0 = w[j] != 0.f ? n0 : acc0;
+        acc1 = w[j] != 0.f ? n1 : acc1;
+      }
+    }
+  }
+  part[wv][lane] = acc0;
+  part[wv][lane + 64] = acc1;
+  __syncthreads();
+  const float inv = z > 0.f ? 1.f / z : 0.f;
+  if (tid < 128) {
+    const f32x4_t o = ((part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid])) * inv;
+    reinterpret_cast<f32x4_t*>(a.o_lat)[static_cast<int64_t>(row) * 128 + tid] = o;
+  }
+  if (a.lse && tid == 0) a.lse[row] = z > 0.f ? m + __logf(z) : -INFINITY;
+}
+
 bool fast_merge_ok(const MergeArgs& a) {
   return a.d_latent % 4 == 0 && (reinterpret_cast<uintptr_t>(a.o_part) & 15) == 0 &&
          (reinterpret_cast<uintptr_t>(a.o_lat) & 15) == 0 &&
@@ -1548,6 +1616,10 @@ bool fast_merge_ok(const MergeArgs& a) {
 hipError_t launch_merge_fast(const MergeArgs& a, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
   const int rows = a.batch * a.n_heads;
+  if (!a.unit_start && a.num_splits > kMergeWideS && a.d_latent == 512) {
+    hipLaunchKernelGGL(k_merge_rows_wide, dim3(rows), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_merge_rows, dim3((rows + 3) / 4), dim3(256), 0, stream, a, rows);
   return hipGetLastError();
 }

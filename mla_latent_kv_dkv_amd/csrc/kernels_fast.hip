@@ -1517,18 +1517,36 @@ __global__ __launch_bounds__(256) void k_merge_rows(MergeArgs a, int rows) {
   const int64_t split_stride = static_cast<int64_t>(nh) * dq;   // float4s between splits
   float4* dst = reinterpret_cast<float4*>(a.o_lat) + static_cast<int64_t>(row) * dq;
   float z = 0.f;
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  constexpr int kB = 8;   // splits per load batch (all in flight at once)
   for (int v = lane; v < dq; v += 64) {   // lane 0 always runs: dq >= 1
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float zz = 0.f;
     if (m != -INFINITY) {
-#pragma unroll 4
-      for (int s = 0; s < S; ++s) {
-        const float l = lse[static_cast<int64_t>(s) * nh];
-        const float w = l == -INFINITY ? 0.f : __expf(l - m);
-        zz += w;
-        if (w != 0.f) {
-          const float4 x = src[s * split_stride + v];
-          acc.x += w * x.x; acc.y += w * x.y; acc.z += w * x.z; acc.w += w * x.w;
+      for (int s0 = 0; s0 < S; s0 += kB) {
+        f32x4_t x[kB];
+        float w[kB];
+#pragma unroll
+        for (int j = 0; j < kB; ++j) {
+          const int sc = s0 + j < S ? s0 + j : s0;   // past S: split s0 again, weight 0
+          x[j] = reinterpret_cast<const f32x4_t*>(src)[sc * split_stride + v];
+          const float l = lse[static_cast<int64_t>(sc) * nh];
+          w[j] = (s0 + j >= S || l == -INFINITY) ? 0.f : __expf(l - m);
+        }
+        // the batch is issued before its first use (the skip of a zero weight is a
+        // select, which the compiler would otherwise turn into a branch around a load)
+#pragma unroll
+        for (int j = 0; j < kB; ++j) asm volatile("" : "+v"(x[j]));
+#pragma unroll
+        for (int j = 0; j < kB; ++j) {
+          zz += w[j];   // (+0 past S: exact)
+          float n0 = acc.x, n1 = acc.y, n2 = acc.z, n3 = acc.w;
+          n0 += w[j] * x[j][0]; n1 += w[j] * x[j][1]; n2 += w[j] * x[j][2]; n3 += w[j] * x[j][3];
+          const bool on = w[j] != 0.f;
+          acc.x = on ? n0 : acc.x;
+          acc.y = on ? n1 : acc.y;
+          acc.z = on ? n2 : acc.z;
+          acc.w = on ? n3 : acc.w;
         }
       }
     }

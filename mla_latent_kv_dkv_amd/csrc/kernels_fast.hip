@@ -1460,6 +1460,285 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h16(
   }
 }
 
+
+// ---- FP8 pool, 16 heads --------------------------------------------------------
+// The 16-head kernel above over the FP8 pool: each wave's tile copy is split in
+// two.  The k^R part (bf16 in the page) is copied asynchronously into the slot as
+// before; the latent codes and the row scales go to registers one tile ahead and
+// are dequantized into the slot's bf16 latent rows when the tile's turn comes.
+// e4m3 times a power-of-two scale is exact in bf16, so from there on the tile is
+// the bf16 tile of the dequantized rows and the products, softmax and combine are
+// the bf16 kernel's.  Rows past the split's end or of an unusable page are written
+// as zeros (NaN codes of a foreign page never reach a product).
+// Per tile and lane: 8 loads of 16 codes (rows 2i + (lane >> 5), codes
+// 16 (lane & 31) ..) and 8 of the rows' scales, then the 2 k^R copies.
+constexpr int kH16F8Copies = 8 + 8 + 2;
+
+struct F8H16Regs {
+  u32x4_t code[8];
+  float scale[8];
+};
+
+__global__ __launch_bounds__(kThreads, 1) void k_attn_f8_h16(
+    AttnArgs a, const int32_t* __restrict__ block_table, const char* __restrict__ pool) {
+  __shared__ __attribute__((aligned(1024))) char ring[kWaves * 2 * kH16Slot];   // 155,648 B
+  __shared__ float wstate[kWaves][2][16];   // per wave: reference and sum of each head
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane & 15, g = lane >> 4;   // head (B/D column) and row group of this lane
+  const int unit = unit_of(blockIdx.x, a.units);
+  constexpr int nh = 16;
+
+  int b, sq, t0, t1;
+  attn_unit(a, unit, tid == 0, &b, &sq, &t0, &t1);
+  b = __builtin_amdgcn_readfirstlane(b);
+  sq = __builtin_amdgcn_readfirstlane(sq);
+  t0 = __builtin_amdgcn_readfirstlane(t0);
+  t1 = __builtin_amdgcn_readfirstlane(t1);
+  const int64_t ob = static_cast<int64_t>(unit) * nh;
+  float* o_out = a.o_part + ob * kDc;
+  float* lse_out = a.lse_part + ob;
+  if (t0 >= t1) {   // empty split (uniform across the workgroup)
+    for (int e = tid; e < nh * kDc; e += kThreads) o_out[e] = 0.f;
+    if (tid < nh) lse_out[tid] = -INFINITY;
+    return;
+  }
+  const int32_t* bt = block_table + static_cast<int64_t>(sq) * a.max_pages;
+  const int ntiles = (t1 - t0 + kH16Tok - 1) / kH16Tok;
+  const int mine = ntiles > wv ? (ntiles - wv + kWaves - 1) / kWaves : 0;   // this wave's tiles
+
+  // queries as B fragments: head h, k = 32 ks + 8 g .. + 7, rounded to bf16
+  bf16x8_t qf[kH16Steps];
+  {
+    const float* ql = a.q_lat + (static_cast<int64_t>(b) * nh + h) * kDc;
+    const float* qp = a.q_pe + (static_cast<int64_t>(b) * nh + h) * kDr;
+#pragma unroll
+    for (int ks = 0; ks < kH16Steps; ++ks) {
+      const float* src = ks < kDc / 32 ? ql + 32 * ks + 8 * g : qp + 32 * (ks - kDc / 32) + 8 * g;
+      const float4 v0 = *reinterpret_cast<const float4*>(src);
+      const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
+      const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      qf[ks] = pack8(v);
+    }
+  }
+
+  const uint32_t slot0 = lds_addr(ring) + static_cast<uint32_t>(2 * kH16Slot) * wv;
+  // operand offsets inside a slot: as the bf16 kernel
+  const int ar = h16row(lane & 15);
+  const uint32_t aoff = kPitch * ar;
+  const int akey = h16key(ar);
+  uint32_t roff_r[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    roff_r[q] = kH16Tok * kPitch + 128 * ar + 16 * ((4 * q + g) ^ rkey(ar));
+  const int s16 = lane & 15;
+  const int br = h16row(4 * g + (s16 >> 2));
+  const int bkey = h16key(br);
+  const uint32_t boff = kPitch * br + 8 * (s16 & 1);
+  const int bsub = (s16 & 3) >> 1;
+  // dequantization: this lane's rows 2i + (lane >> 5) and code chunk lane & 31
+  // (latent columns 16 (lane & 31) .. + 15, bf16 chunks 2 (lane & 31) and + 1)
+  const int crow = lane >> 5, cchunk = lane & 31;
+
+  const float cs = a.scale * kLog2e;
+  bool bad_page = false;
+
+  const int p0 = t0 / kPage, p_end = (t1 - 1) / kPage + 1;
+  int pwin = 0, wbase = -kPage;
+  auto page_of = [&](int u) {
+    if (u - wbase >= 64) {        // uniform; drains this wave's copies in flight
+      wbase = u;
+      const int pg = p0 + wbase + lane;
+      pwin = pg < p_end ? bt[pg] : 0;
+      wait_vmcnt<0>();
+    }
+    return __builtin_amdgcn_readlane(pwin, u - wbase);
+  };
+  // tile u of this wave (tokens t0 + 16 (wv + 4u) ..): codes and scales into `rg`,
+  // the k^R rows into slot u & 1; returns the valid rows
+  auto issue = [&](int u, F8H16Regs& rg) {
+    const int tok = t0 + kH16Tok * (wv + kWaves * u);
+    const int pg = page_of(u);
+    const bool ok = pg >= 0 && pg < a.num_pages;
+    bad_page |= !ok;
+    const int nvalid = ok ? min(kH16Tok, t1 - tok) : 0;
+    const char* page = pool + (ok ? static_cast<int64_t>(pg) * kF8PageBytes : 0);
+    const int r0 = tok & (kPage - 1);   // the tile's first row in its page
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 2 * i + crow, rv = r < nvalid ? r : 0;
+      rg.code[i] = *reinterpret_cast<const u32x4_t*>(page + (r0 + rv) * kF8Row + 16 * cchunk);
+      rg.scale[i] = *reinterpret_cast<const float*>(page + kF8ScaleOff + 4 * (r0 + rv));
+    }
+    const uint64_t rows = reinterpret_cast<uint64_t>(page + r0 * kF8Row);
+    const uint32_t slot = slot0 + (u & 1) * kH16Slot;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int rr = 8 * q + (lane >> 3);
+      const int rv = rr < nvalid ? rr : 0;
+      dma_block(rows, kF8Row * rv + kDc + 16 * ((lane & 7) ^ rkey(rr)),
+                slot + kH16Tok * kPitch + 1024 * q);
+    }
+    return nvalid;
+  };
+  // the codes of `rg` as bf16 latent rows of slot T (zeros for rows nvalid..)
+  auto dequantize = [&](const F8H16Regs& rg, uint32_t T, int nvalid) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 2 * i + crow;
+      const float sc = r < nvalid ? rg.scale[i] : 0.f;
+      u32x4_t lo, hi;   // bf16 columns 16 cchunk + 0..7 and + 8..15
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int c = static_cast<int>(rg.code[i][w]);
+        const f32x2_t f0 = __builtin_amdgcn_cvt_pk_f32_fp8(c, false);
+        const f32x2_t f1 = __builtin_amdgcn_cvt_pk_f32_fp8(c, true);
+        // a zero scale must give zeros even for NaN codes
+        const unsigned p0 = r < nvalid ? cvt2(f0[0] * sc, f0[1] * sc) : 0u;
+        const unsigned p1 = r < nvalid ? cvt2(f1[0] * sc, f1[1] * sc) : 0u;
+        if (w < 2) { lo[2 * w] = p0; lo[2 * w + 1] = p1; }
+        else { hi[2 * (w - 2)] = p0; hi[2 * (w - 2) + 1] = p1; }
+      }
+      const int key = h16key(r);
+      lds_st128(T + kPitch * r + 16 * ((2 * cchunk) ^ key), lo);
+      lds_st128(T + kPitch * r + 16 * ((2 * cchunk + 1) ^ key), hi);
+    }
+  };
+
+  f32x4_t o[kH16Blocks];
+#pragma unroll
+  for (int nb = 0; nb < kH16Blocks; ++nb) o[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY, l_part = 0.f;
+  constexpr int kAAhead = 4, kARing = 6;    // score operands read ahead
+  constexpr int kBAhead = 6, kBRing = 8;    // P.C operands read ahead
+  F8H16Regs rga, rgb;   // codes of tiles u (even u: rga) and u + 1
+  for (int pass = 0; pass < 2 && mine > 0; ++pass) {
+    if (pass > 0) {
+#pragma unroll
+      for (int nb = 0; nb < kH16Blocks; ++nb) o[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    l_part = 0.f;
+    float seen = -INFINITY;
+    int nv0 = issue(0, rga), nv1 = mine > 1 ? issue(1, rgb) : 0;
+    // tile u, its codes in `cur` (refilled with tile u + 2 at the end)
+    auto tile = [&](int u, F8H16Regs& cur) {
+      if (u + 1 < mine) wait_vmcnt<kH16F8Copies>();
+      else wait_vmcnt<0>();
+      const uint32_t T = slot0 + (u & 1) * kH16Slot;
+      dequantize(cur, T, nv0);
+      wait_lgkm(0);   // the wave's own rows are in LDS before it reads them
+      auto lda = [&](int ks) {
+        return ks < kDc / 32 ? lds_b128(T + aoff + 16 * ((4 * ks + g) ^ akey))
+                             : lds_b128(T + roff_r[ks - kDc / 32]);
+      };
+      bf16x8_t arr[kARing];
+#pragma unroll
+      for (int d = 0; d < kAAhead; ++d) arr[d] = lda(d);
+      f32x4_t x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kH16Steps; ++ks) {
+        if (ks + kAAhead < kH16Steps) arr[(ks + kAAhead) % kARing] = lda(ks + kAAhead);
+        wait_lgkm(min(kAAhead, kH16Steps - 1 - ks));
+        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(arr[ks % kARing], qf[ks], x, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      auto ldb = [&](int nb) { return lds_tr16(T + boff + 16 * ((2 * nb + bsub) ^ bkey)); };
+      s16x4_t bb[kBRing];
+#pragma unroll
+      for (int d = 0; d < kBAhead; ++d) bb[d] = ldb(d);
+      if (nv0 < kH16Tok) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (h16row(4 * g + i) >= nv0) x[i] = -INFINITY;
+      }
+      if (pass == 0 && u == 0) {
+        float tm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
+        tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+        m_ref = tm * cs;
+      }
+      const float mr = fmaxf(m_ref, -1e30f);
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        seen = fmaxf(seen, x[i]);
+        p[i] = __builtin_amdgcn_exp2f(fmaf(x[i], cs, -mr));
+      }
+      const unsigned w01 = cvt2(p[0], p[1]), w23 = cvt2(p[2], p[3]);
+      l_part += (__uint_as_float(w01 << 16) + __uint_as_float(w01 & 0xFFFF0000u)) +
+                (__uint_as_float(w23 << 16) + __uint_as_float(w23 & 0xFFFF0000u));
+      const u32x2_t pw = {w01, w23};
+      const s16x4_t pa = __builtin_bit_cast(s16x4_t, pw);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int nb = 0; nb < kH16Blocks; ++nb) {
+        if (nb + kBAhead < kH16Blocks) bb[(nb + kBAhead) % kBRing] = ldb(nb + kBAhead);
+        wait_lgkm(min(kBAhead, kH16Blocks - 1 - nb));
+        o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, bb[nb % kBRing], o[nb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // every read of this slot has returned (the last wait was lgkmcnt(0)): refill it
+      nv0 = nv1;
+      if (u + 2 < mine) nv1 = issue(u + 2, cur);
+    };
+    for (int u = 0; u < mine; u += 2) {
+      tile(u, rga);
+      if (u + 1 < mine) tile(u + 1, rgb);
+    }
+    seen = fmaxf(seen, __shfl_xor(seen, 16, 64));
+    seen = fmaxf(seen, __shfl_xor(seen, 32, 64));
+    seen *= cs;
+    if (__ballot(seen > m_ref + kHeadroom) == 0) break;
+    m_ref = seen;
+  }
+  if (bad_page) set_err(a.err, ERR_PAGE);
+
+  // ---- combine the 4 waves (as the bf16 kernel)
+  float lsum = l_part + __shfl_xor(l_part, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  const float mw = mine > 0 ? m_ref : -INFINITY;
+  __syncthreads();
+  if (g == 0) {
+    wstate[wv][0][h] = mw;
+    wstate[wv][1][h] = mine > 0 ? lsum : 0.f;
+  }
+  __syncthreads();
+  float mh = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) mh = fmaxf(mh, wstate[w][0][h]);
+  const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - mh);
+  if (wv == 0 && g == 0) {
+    float z = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float m = wstate[w][0][h];
+      if (m != -INFINITY) z += wstate[w][1][h] * __builtin_amdgcn_exp2f(m - mh);
+    }
+    wstate[0][1][h] = z > 0.f ? 1.f / z : 0.f;
+    lse_out[h] = z > 0.f ? (mh + __log2f(z)) * 0.6931471805599453f : -INFINITY;
+  }
+  constexpr int kRowW = kDc + 4;
+  float* stage = reinterpret_cast<float*>(ring) + wv * nh * kRowW;
+  float fh[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fh[i] = __shfl(f, 4 * g + i, 64);
+#pragma unroll
+  for (int nb = 0; nb < kH16Blocks; ++nb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) stage[(4 * g + i) * kRowW + 16 * nb + s16] = o[nb][i] * fh[i];
+  __syncthreads();
+  const float* st_all = reinterpret_cast<const float*>(ring);
+#pragma unroll 4
+  for (int i = 0; i < 2 * nh; ++i) {
+    const int hr = i >> 1, c = 128 * wv + 64 * (i & 1) + lane;
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) acc += st_all[(w * nh + hr) * kRowW + c];
+    o_out[hr * kDc + c] = acc * wstate[0][1][hr];
+  }
+}
+
 }  // namespace
 
 // the matrix-core kernels read the fp32 queries 16 bytes at a time
@@ -1492,8 +1771,12 @@ hipError_t launch_attention_fast(const AttnArgs& a, hipStream_t stream) {
 hipError_t launch_attention_fp8(const AttnArgs& a, hipStream_t stream) {
   if (a.units == 0) return hipSuccess;
   const int units = a.units;
-  hipLaunchKernelGGL(k_attn_f8mma_h128, dim3(units), dim3(kThreads), 0, stream, a, a.block_table,
-                     static_cast<const char*>(a.pool));
+  if (fast_attention_h16_ok(a))
+    hipLaunchKernelGGL(k_attn_f8_h16, dim3(units), dim3(kThreads), 0, stream, a, a.block_table,
+                       static_cast<const char*>(a.pool));
+  else
+    hipLaunchKernelGGL(k_attn_f8mma_h128, dim3(units), dim3(kThreads), 0, stream, a,
+                       a.block_table, static_cast<const char*>(a.pool));
   return hipGetLastError();
 }
 

@@ -19,9 +19,10 @@ hipError_t launch_gemm_fast(const GemmArgs& a, void* partial, size_t partial_byt
                             hipStream_t stream);
 
 bool fast_attention_ok(const AttnArgs& a);      // n_h = 128 (bf16 and FP8 pools)
-bool fast_attention_h16_ok(const AttnArgs& a);  // n_h = 16 (bf16 pool)
+bool fast_attention_h16_ok(const AttnArgs& a);  // n_h = 16 (bf16 and FP8 pools)
 hipError_t launch_attention_fast(const AttnArgs& a, hipStream_t stream);
-// FP8 pool (pages of 64 rows [512 e4m3 | 64 bf16] + 64 fp32 scales); same shapes as fast_attention_ok
+// FP8 pool (pages of 64 rows [512 e4m3 | 64 bf16] + 64 fp32 scales); the shapes of
+// fast_attention_ok or fast_attention_h16_ok
 hipError_t launch_attention_fp8(const AttnArgs& a, hipStream_t stream);
 
 bool fast_merge_ok(const MergeArgs& a);

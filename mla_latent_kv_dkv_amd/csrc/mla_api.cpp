@@ -331,7 +331,8 @@ hipError_t launch_attention_plain(const mla_dims* d, const mla::AttnArgs& a, hip
 }
 
 hipError_t launch_attention_f8(const mla_dims* d, const mla::AttnArgs& a, hipStream_t stream) {
-  if (use_fast() && d->dtype == MLA_BF16 && mla::fast_attention_ok(a))
+  if (use_fast() && d->dtype == MLA_BF16 &&
+      (mla::fast_attention_ok(a) || mla::fast_attention_h16_ok(a)))
     return mla::launch_attention_fp8(a, stream);
   return mla::launch_attention_generic_fp8(a, stream);
 }

@@ -225,7 +225,7 @@ WORKLOADS = {
     # rows, or built through the FP8 append for the cache-from-h ones)
     "tiny-fp8": Workload("tiny-fp8", 64, 4, 16, 32, 8, "f32", 1, 64, 1009, num_splits=1,
                          permute_pages=False, cache_from_h=True, cache="fp8"),
-    "lite-fp8": Workload("lite-fp8", 2048, 16, 128, 512, 64, "bf16", 32, 4096, 1010, num_splits=2,
+    "lite-fp8": Workload("lite-fp8", 2048, 16, 128, 512, 64, "bf16", 32, 4096, 1010, num_splits=8,
                          cache_from_h=True, cache="fp8"),
     "full-fp8": Workload("full-fp8", 5120, 128, 128, 512, 64, "bf16", 64, 4096, 1011, num_splits=4,
                          cache="fp8"),

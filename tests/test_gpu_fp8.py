@@ -276,15 +276,16 @@ def _row_factor(phys):
     return np.ldexp(1.0, (np.asarray(phys) % 7) - 3)
 
 
+@pytest.mark.parametrize("name", ["full-fp8", "lite-fp8"])
 @pytest.mark.parametrize("path", PATHS)
-def test_attention_fp8_rows_with_different_scales(path):
+def test_attention_fp8_rows_with_different_scales(name, path):
     """Each row's own scale must weigh its codes: rows of one tile alternate over
     seven magnitudes (2^-3 .. 2^3), so a scale taken from the wrong row shows."""
-    w = _wl("full-fp8", batch=3)
+    w = _wl(name, batch=3)
     lens = (1000, 4096, 77)
     S = 4
     M.mla_set_kernel_path(path)
-    note(f"attention fp8 varied row scales path={path}")
+    note(f"attention fp8 varied row scales {name} path={path}")
     d = _dims(w)
     bt, total = I.page_table(w, np.array(lens, dtype=np.int32))
     nh = w.n_heads
@@ -316,15 +317,16 @@ def test_attention_fp8_rows_with_different_scales(path):
     assert M.mla_device_error() == 0
 
 
+@pytest.mark.parametrize("name", ["full-fp8", "lite-fp8"])
 @pytest.mark.parametrize("path", PATHS)
-def test_attention_fp8_skips_bad_page(path):
+def test_attention_fp8_skips_bad_page(name, path):
     """An out-of-pool table entry on the split's first page takes no weight and is
     flagged.  Physical page 0, which no sequence owns here, holds NaN codes: the
     kernels must not let those bytes reach the output either."""
-    w = _wl("full-fp8", batch=1)
+    w = _wl(name, batch=1)
     M.mla_set_kernel_path(path)
     L = 200
-    note(f"attention fp8 bad first page path={path}")
+    note(f"attention fp8 bad first page {name} path={path}")
     bt, total = I.page_table(w, np.array([L], dtype=np.int32))
     bt = bt + 1                                            # pages 1..total; page 0 unowned
     d = _dims(w)

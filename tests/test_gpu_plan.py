@@ -24,6 +24,7 @@ CASES = [
     ("lite", [17, 4096, 130, 2], 12),              # 16 heads
     ("tiny", [1, 64, 100, 129], 5),                # fp32: the vector kernel
     ("full-fp8", [1, 65, 1000, 4096, 0], 10),      # FP8 pool
+    ("lite-fp8", [17, 4096, 130, 2], 12),          # FP8 pool, 16 heads
 ]
 
 

@@ -99,6 +99,8 @@ PEAKY = [
     ("fp8", "full-fp8", (1000, 700), 2, [[(300, 5), (900, 77), (995, 100)], [(650, 31)]], 56.0),
     ("bf16", "lite", (1000, 700), 2, [[(300, 5), (900, 7), (995, 12)], [(650, 15)]], 90.0),
     ("bf16", "lite", (1000, 700), 2, [[(300, 5), (900, 7), (995, 12)], [(650, 15)]], 56.0),
+    ("fp8", "lite-fp8", (1000, 700), 2, [[(300, 5), (900, 7), (995, 12)], [(650, 15)]], 90.0),
+    ("fp8", "lite-fp8", (1000, 700), 2, [[(300, 5), (900, 7), (995, 12)], [(650, 15)]], 56.0),
 ]
 
 

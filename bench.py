@@ -57,9 +57,13 @@ def parse():
 
 def attention_kernel(w) -> str:
     """Name of the attention kernel that runs for workload `w`."""
-    if w.n_heads != 128 or w.dtype != "bf16":
+    fp8 = w.cache == "fp8"
+    if (w.dtype != "bf16" or w.d_latent != 512 or w.d_rope != 64 or w.page_size != 64 or
+            w.n_heads not in (16, 128)):
         return "k_attention_generic"
-    return "k_attn_f8mma_h128" if w.cache == "fp8" else "k_attn_mfma_h128"
+    if w.n_heads == 16:
+        return "k_attn_f8_h16" if fp8 else "k_attn_mfma_h16"
+    return "k_attn_f8mma_h128" if fp8 else "k_attn_mfma_h128"
 
 
 def host_info():

@@ -1219,6 +1219,197 @@ __device__ __forceinline__ int h16row(int t) {   // LDS row of MFMA row t
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+// ---- pieces of the two 16-head kernels (bf16 and FP8 pools) ----------------
+
+// queries of head h as B fragments: k = 32 ks + 8 g .. + 7, rounded to bf16
+__device__ __forceinline__ void h16_queries(const AttnArgs& a, int b, int h, int g,
+                                            bf16x8_t (&qf)[kH16Steps]) {
+  constexpr int nh = 16;
+  const float* ql = a.q_lat + (static_cast<int64_t>(b) * nh + h) * kDc;
+  const float* qp = a.q_pe + (static_cast<int64_t>(b) * nh + h) * kDr;
+#pragma unroll
+  for (int ks = 0; ks < kH16Steps; ++ks) {
+    const float* src = ks < kDc / 32 ? ql + 32 * ks + 8 * g : qp + 32 * (ks - kDc / 32) + 8 * g;
+    const float4 v0 = *reinterpret_cast<const float4*>(src);
+    const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
+    const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    qf[ks] = pack8(v);
+  }
+}
+
+// per-lane operand offsets inside a slot.  Score A operand of MFMA row t = lane & 15
+// (LDS row h16row(t)), latent chunk 4 ks + g: aoff + 16 ((4 ks + g) ^ akey); RoPE
+// chunk 4 (ks - 16) + g: roff[ks - 16].  P.C B operand (transposed read) of row group
+// g, lane s16 = lane & 15: LDS row h16row(4 g + (s16 >> 2)), bytes 8 (s16 & 3) of
+// column block nb's 32 bytes: boff + 16 ((2 nb + bsub) ^ bkey)
+struct H16Lane {
+  uint32_t aoff, roff[2], boff;
+  int akey, bkey, bsub;
+};
+
+__device__ __forceinline__ H16Lane h16_lane(int lane) {
+  const int g = lane >> 4, s16 = lane & 15;
+  H16Lane L;
+  const int ar = h16row(lane & 15);
+  L.aoff = kPitch * ar;
+  L.akey = h16key(ar);
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    L.roff[q] = kH16Tok * kPitch + 128 * ar + 16 * ((4 * q + g) ^ rkey(ar));
+  const int br = h16row(4 * g + (s16 >> 2));
+  L.bkey = h16key(br);
+  L.boff = kPitch * br + 8 * (s16 & 1);
+  L.bsub = (s16 & 3) >> 1;
+  return L;
+}
+
+// One staged tile in slot T (nv valid rows): scores of the 16 heads (lane: head
+// lane & 15, MFMA rows 4g + i), weights against the reference (`fix_ref`: the
+// wave's first tile sets it), O += P.C.  `seen` tracks the largest raw score.
+__device__ __forceinline__ void h16_tile(uint32_t T, int nv, const bf16x8_t (&qf)[kH16Steps],
+                                         const H16Lane& L, int g, float cs, bool fix_ref,
+                                         f32x4_t (&o)[kH16Blocks], float& m_ref, float& l_part,
+                                         float& seen) {
+  constexpr int kAAhead = 4, kARing = 6;    // score operands read ahead
+  constexpr int kBAhead = 6, kBRing = 8;    // P.C operands read ahead
+  // scores: operands read kAAhead steps ahead, waited for one by one
+  auto lda = [&](int ks) {
+    return ks < kDc / 32 ? lds_b128(T + L.aoff + 16 * ((4 * ks + g) ^ L.akey))
+                         : lds_b128(T + L.roff[ks - kDc / 32]);
+  };
+  bf16x8_t ar[kARing];
+#pragma unroll
+  for (int d = 0; d < kAAhead; ++d) ar[d] = lda(d);
+  f32x4_t x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < kH16Steps; ++ks) {
+    if (ks + kAAhead < kH16Steps) ar[(ks + kAAhead) % kARing] = lda(ks + kAAhead);
+    wait_lgkm(min(kAAhead, kH16Steps - 1 - ks));
+    x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar[ks % kARing], qf[ks], x, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // the P.C operands of the first blocks are read while the weights are formed
+  auto ldb = [&](int nb) { return lds_tr16(T + L.boff + 16 * ((2 * nb + L.bsub) ^ L.bkey)); };
+  s16x4_t bb[kBRing];
+#pragma unroll
+  for (int d = 0; d < kBAhead; ++d) bb[d] = ldb(d);
+  if (nv < kH16Tok) {   // rows past the split's end (or of an unusable page)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (h16row(4 * g + i) >= nv) x[i] = -INFINITY;
+  }
+  if (fix_ref) {   // the wave's first tile fixes its reference
+    float tm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
+    tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+    m_ref = tm * cs;
+  }
+  const float mr = fmaxf(m_ref, -1e30f);
+  float p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    seen = fmaxf(seen, x[i]);
+    p[i] = __builtin_amdgcn_exp2f(fmaf(x[i], cs, -mr));
+  }
+  // P as bf16 (the A operand as it stands); the sum takes the rounded values
+  const unsigned w01 = cvt2(p[0], p[1]), w23 = cvt2(p[2], p[3]);
+  l_part += (__uint_as_float(w01 << 16) + __uint_as_float(w01 & 0xFFFF0000u)) +
+            (__uint_as_float(w23 << 16) + __uint_as_float(w23 & 0xFFFF0000u));
+  const u32x2_t pw = {w01, w23};
+  const s16x4_t pa = __builtin_bit_cast(s16x4_t, pw);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int nb = 0; nb < kH16Blocks; ++nb) {
+    if (nb + kBAhead < kH16Blocks) bb[(nb + kBAhead) % kBRing] = ldb(nb + kBAhead);
+    wait_lgkm(min(kBAhead, kH16Blocks - 1 - nb));
+    o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, bb[nb % kBRing], o[nb], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Combine the 4 waves: common reference M_h per head, each wave's share of O
+// scaled by 2^(m_w - M_h), summed per column by the wave that owns the column
+// block; the normaliser and the lse are formed once per head.  The ring is free
+// once every wave's copies have landed and been read (the first barrier).
+__device__ __forceinline__ void h16_combine(char* ring, float (*wstate)[2][16],
+                                            const f32x4_t (&o)[kH16Blocks], float l_part,
+                                            float m_ref, int mine, int wv, int lane, float* o_out,
+                                            float* lse_out) {
+  constexpr int nh = 16;
+  const int h = lane & 15, g = lane >> 4, s16 = lane & 15;
+  float lsum = l_part + __shfl_xor(l_part, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  const float mw = mine > 0 ? m_ref : -INFINITY;
+  __syncthreads();
+  if (g == 0) {
+    wstate[wv][0][h] = mw;
+    wstate[wv][1][h] = mine > 0 ? lsum : 0.f;
+  }
+  __syncthreads();
+  float mh = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) mh = fmaxf(mh, wstate[w][0][h]);
+  const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - mh);
+  if (wv == 0 && g == 0) {   // head h: 1 / sum_w l_w 2^(m_w - M) and the lse
+    float z = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float m = wstate[w][0][h];
+      if (m != -INFINITY) z += wstate[w][1][h] * __builtin_amdgcn_exp2f(m - mh);
+    }
+    wstate[0][1][h] = z > 0.f ? 1.f / z : 0.f;   // read back below (after the barrier)
+    lse_out[h] = z > 0.f ? (mh + __log2f(z)) * 0.6931471805599453f : -INFINITY;
+  }
+  // this wave's scaled O: head row hr at kRowW hr floats (padded: conflict-free writes)
+  constexpr int kRowW = kDc + 4;
+  float* stage = reinterpret_cast<float*>(ring) + wv * nh * kRowW;
+  float fh[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fh[i] = __shfl(f, 4 * g + i, 64);   // scale of head 4g + i
+#pragma unroll
+  for (int nb = 0; nb < kH16Blocks; ++nb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) stage[(4 * g + i) * kRowW + 16 * nb + s16] = o[nb][i] * fh[i];
+  __syncthreads();
+  // wave wv: columns 128 wv .. 128 wv + 127 of every head; step i covers head i / 2
+  const float* st_all = reinterpret_cast<const float*>(ring);
+#pragma unroll 4
+  for (int i = 0; i < 2 * nh; ++i) {
+    const int hr = i >> 1, c = 128 * wv + 64 * (i & 1) + lane;
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) acc += st_all[(w * nh + hr) * kRowW + c];
+    o_out[hr * kDc + c] = acc * wstate[0][1][hr];
+  }
+}
+
+// The unit's range and outputs (an empty split writes its empty result and says so).
+struct H16Unit {
+  int b, sq, t0, t1;
+  float* o_out;
+  float* lse_out;
+};
+
+__device__ __forceinline__ bool h16_unit(const AttnArgs& a, int tid, H16Unit& U) {
+  constexpr int nh = 16;
+  const int unit = unit_of(blockIdx.x, a.units);
+  int b, sq, t0, t1;
+  attn_unit(a, unit, tid == 0, &b, &sq, &t0, &t1);
+  U.b = __builtin_amdgcn_readfirstlane(b);
+  U.sq = __builtin_amdgcn_readfirstlane(sq);
+  U.t0 = __builtin_amdgcn_readfirstlane(t0);
+  U.t1 = __builtin_amdgcn_readfirstlane(t1);
+  const int64_t ob = static_cast<int64_t>(unit) * nh;
+  U.o_out = a.o_part + ob * kDc;
+  U.lse_out = a.lse_part + ob;
+  if (U.t0 >= U.t1) {   // empty split (uniform across the workgroup)
+    for (int e = tid; e < nh * kDc; e += kThreads) U.o_out[e] = 0.f;
+    if (tid < nh) U.lse_out[tid] = -INFINITY;
+    return false;
+  }
+  return true;
+}
+
 __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h16(
     AttnArgs a, const int32_t* __restrict__ block_table, const char* __restrict__ pool) {
   __shared__ __attribute__((aligned(1024))) char ring[kWaves * 2 * kH16Slot];   // 155,648 B
@@ -1227,59 +1418,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h16(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane & 15, g = lane >> 4;   // head (B/D column) and row group of this lane
-  const int unit = unit_of(blockIdx.x, a.units);
-  constexpr int nh = 16;
-
-  int b, sq, t0, t1;
-  attn_unit(a, unit, tid == 0, &b, &sq, &t0, &t1);
-  b = __builtin_amdgcn_readfirstlane(b);
-  sq = __builtin_amdgcn_readfirstlane(sq);
-  t0 = __builtin_amdgcn_readfirstlane(t0);
-  t1 = __builtin_amdgcn_readfirstlane(t1);
-  const int64_t ob = static_cast<int64_t>(unit) * nh;
-  float* o_out = a.o_part + ob * kDc;
-  float* lse_out = a.lse_part + ob;
-  if (t0 >= t1) {   // empty split (uniform across the workgroup)
-    for (int e = tid; e < nh * kDc; e += kThreads) o_out[e] = 0.f;
-    if (tid < nh) lse_out[tid] = -INFINITY;
-    return;
-  }
-  const int32_t* bt = block_table + static_cast<int64_t>(sq) * a.max_pages;
+  H16Unit U;
+  if (!h16_unit(a, tid, U)) return;
+  const int t0 = U.t0, t1 = U.t1;
+  const int32_t* bt = block_table + static_cast<int64_t>(U.sq) * a.max_pages;
   const int ntiles = (t1 - t0 + kH16Tok - 1) / kH16Tok;
   const int mine = ntiles > wv ? (ntiles - wv + kWaves - 1) / kWaves : 0;   // this wave's tiles
 
-  // queries as B fragments: head h, k = 32 ks + 8 g .. + 7, rounded to bf16
   bf16x8_t qf[kH16Steps];
-  {
-    const float* ql = a.q_lat + (static_cast<int64_t>(b) * nh + h) * kDc;
-    const float* qp = a.q_pe + (static_cast<int64_t>(b) * nh + h) * kDr;
-#pragma unroll
-    for (int ks = 0; ks < kH16Steps; ++ks) {
-      const float* src = ks < kDc / 32 ? ql + 32 * ks + 8 * g : qp + 32 * (ks - kDc / 32) + 8 * g;
-      const float4 v0 = *reinterpret_cast<const float4*>(src);
-      const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
-      const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-      qf[ks] = pack8(v);
-    }
-  }
-
+  h16_queries(a, U.b, h, g, qf);
   const uint32_t slot0 = lds_addr(ring) + static_cast<uint32_t>(2 * kH16Slot) * wv;
-  // score A operand of MFMA row t = lane & 15 (LDS row h16row(t)), latent chunk
-  // 4 ks + g: aoff + 16 ((4 ks + g) ^ key); RoPE chunk 4 (ks - 16) + g: roff_r
-  const int ar = h16row(lane & 15);
-  const uint32_t aoff = kPitch * ar;
-  const int akey = h16key(ar);
-  uint32_t roff_r[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q)
-    roff_r[q] = kH16Tok * kPitch + 128 * ar + 16 * ((4 * q + g) ^ rkey(ar));
-  // P.C B operand (transposed read) of row group g, lane s16 = lane & 15: LDS row
-  // h16row(4 g + (s16 >> 2)), bytes 8 (s16 & 3) of column block nb's 32 bytes
-  const int s16 = lane & 15;
-  const int br = h16row(4 * g + (s16 >> 2));
-  const int bkey = h16key(br);
-  const uint32_t boff = kPitch * br + 8 * (s16 & 1);
-  const int bsub = (s16 & 3) >> 1;
+  const H16Lane L = h16_lane(lane);
 
   const float cs = a.scale * kLog2e;
   bool bad_page = false;
@@ -1328,8 +1477,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h16(
 #pragma unroll
   for (int nb = 0; nb < kH16Blocks; ++nb) o[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_ref = -INFINITY, l_part = 0.f;
-  constexpr int kAAhead = 4, kARing = 6;    // score operands read ahead
-  constexpr int kBAhead = 6, kBRing = 8;    // P.C operands read ahead
   for (int pass = 0; pass < 2 && mine > 0; ++pass) {
     if (pass > 0) {
 #pragma unroll
@@ -1341,61 +1488,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h16(
     for (int u = 0; u < mine; ++u) {
       if (u + 1 < mine) wait_vmcnt<kH16Copies>();
       else wait_vmcnt<0>();
-      const uint32_t T = slot0 + (u & 1) * kH16Slot;
-      // scores of the tile: lane holds head h, MFMA rows 4g + i; operands read
-      // kAAhead steps ahead, waited for one by one
-      auto lda = [&](int ks) {
-        return ks < kDc / 32 ? lds_b128(T + aoff + 16 * ((4 * ks + g) ^ akey))
-                             : lds_b128(T + roff_r[ks - kDc / 32]);
-      };
-      bf16x8_t ar[kARing];
-#pragma unroll
-      for (int d = 0; d < kAAhead; ++d) ar[d] = lda(d);
-      f32x4_t x = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < kH16Steps; ++ks) {
-        if (ks + kAAhead < kH16Steps) ar[(ks + kAAhead) % kARing] = lda(ks + kAAhead);
-        wait_lgkm(min(kAAhead, kH16Steps - 1 - ks));
-        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar[ks % kARing], qf[ks], x, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // the P.C operands of the first blocks are read while the weights are formed
-      auto ldb = [&](int nb) { return lds_tr16(T + boff + 16 * ((2 * nb + bsub) ^ bkey)); };
-      s16x4_t bb[kBRing];
-#pragma unroll
-      for (int d = 0; d < kBAhead; ++d) bb[d] = ldb(d);
-      if (nv0 < kH16Tok) {   // rows past the split's end (or of an unusable page)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (h16row(4 * g + i) >= nv0) x[i] = -INFINITY;
-      }
-      if (pass == 0 && u == 0) {   // the wave's first tile fixes its reference
-        float tm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-        tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
-        tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
-        m_ref = tm * cs;
-      }
-      const float mr = fmaxf(m_ref, -1e30f);
-      float p[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        seen = fmaxf(seen, x[i]);
-        p[i] = __builtin_amdgcn_exp2f(fmaf(x[i], cs, -mr));
-      }
-      // P as bf16 (the A operand as it stands); the sum takes the rounded values
-      const unsigned w01 = cvt2(p[0], p[1]), w23 = cvt2(p[2], p[3]);
-      l_part += (__uint_as_float(w01 << 16) + __uint_as_float(w01 & 0xFFFF0000u)) +
-                (__uint_as_float(w23 << 16) + __uint_as_float(w23 & 0xFFFF0000u));
-      const u32x2_t pw = {w01, w23};
-      const s16x4_t pa = __builtin_bit_cast(s16x4_t, pw);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int nb = 0; nb < kH16Blocks; ++nb) {
-        if (nb + kBAhead < kH16Blocks) bb[(nb + kBAhead) % kBRing] = ldb(nb + kBAhead);
-        wait_lgkm(min(kBAhead, kH16Blocks - 1 - nb));
-        o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, bb[nb % kBRing], o[nb], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      h16_tile(slot0 + (u & 1) * kH16Slot, nv0, qf, L, g, cs, pass == 0 && u == 0, o, m_ref,
+               l_part, seen);
       // every read of this slot has returned (the last wait was lgkmcnt(0)): refill it
       nv0 = nv1;
       if (u + 2 < mine) nv1 = issue(u + 2);
@@ -1410,56 +1504,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h16(
     m_ref = seen;                // this wave runs its tiles again with its heads' maxima
   }
   if (bad_page) set_err(a.err, ERR_PAGE);
-
-  // ---- combine the 4 waves: common reference M_h per head, each wave's share of
-  // O scaled by 2^(m_w - M_h), summed per column by the wave that owns the column
-  // block; the normaliser and the lse are formed once per head
-  float lsum = l_part + __shfl_xor(l_part, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
-  const float mw = mine > 0 ? m_ref : -INFINITY;
-  __syncthreads();   // every wave's copies have landed and been read: the ring is free
-  if (g == 0) {
-    wstate[wv][0][h] = mw;
-    wstate[wv][1][h] = mine > 0 ? lsum : 0.f;
-  }
-  __syncthreads();
-  float mh = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) mh = fmaxf(mh, wstate[w][0][h]);
-  const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - mh);
-  if (wv == 0 && g == 0) {   // head h: 1 / sum_w l_w 2^(m_w - M) and the lse
-    float z = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float m = wstate[w][0][h];
-      if (m != -INFINITY) z += wstate[w][1][h] * __builtin_amdgcn_exp2f(m - mh);
-    }
-    wstate[0][1][h] = z > 0.f ? 1.f / z : 0.f;   // read back below (after the barrier)
-    lse_out[h] = z > 0.f ? (mh + __log2f(z)) * 0.6931471805599453f : -INFINITY;
-  }
-  // this wave's scaled O: head row hr at kRowW hr floats (padded: conflict-free writes)
-  constexpr int kRowW = kDc + 4;
-  float* stage = reinterpret_cast<float*>(ring) + wv * nh * kRowW;
-  float fh[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) fh[i] = __shfl(f, 4 * g + i, 64);   // scale of head 4g + i
-#pragma unroll
-  for (int nb = 0; nb < kH16Blocks; ++nb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) stage[(4 * g + i) * kRowW + 16 * nb + s16] = o[nb][i] * fh[i];
-  __syncthreads();
-  // wave wv: columns 128 wv .. 128 wv + 127 of every head; step i covers head i / 2
-  const float* st_all = reinterpret_cast<const float*>(ring);
-#pragma unroll 4
-  for (int i = 0; i < 2 * nh; ++i) {
-    const int hr = i >> 1, c = 128 * wv + 64 * (i & 1) + lane;
-    float acc = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) acc += st_all[(w * nh + hr) * kRowW + c];
-    o_out[hr * kDc + c] = acc * wstate[0][1][hr];
-  }
+  h16_combine(ring, wstate, o, l_part, m_ref, mine, wv, lane, U.o_out, U.lse_out);
 }
-
 
 // ---- FP8 pool, 16 heads --------------------------------------------------------
 // The 16-head kernel above over the FP8 pool: each wave's tile copy is split in
@@ -1486,57 +1532,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_f8_h16(
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = lane & 15, g = lane >> 4;   // head (B/D column) and row group of this lane
-  const int unit = unit_of(blockIdx.x, a.units);
-  constexpr int nh = 16;
-
-  int b, sq, t0, t1;
-  attn_unit(a, unit, tid == 0, &b, &sq, &t0, &t1);
-  b = __builtin_amdgcn_readfirstlane(b);
-  sq = __builtin_amdgcn_readfirstlane(sq);
-  t0 = __builtin_amdgcn_readfirstlane(t0);
-  t1 = __builtin_amdgcn_readfirstlane(t1);
-  const int64_t ob = static_cast<int64_t>(unit) * nh;
-  float* o_out = a.o_part + ob * kDc;
-  float* lse_out = a.lse_part + ob;
-  if (t0 >= t1) {   // empty split (uniform across the workgroup)
-    for (int e = tid; e < nh * kDc; e += kThreads) o_out[e] = 0.f;
-    if (tid < nh) lse_out[tid] = -INFINITY;
-    return;
-  }
-  const int32_t* bt = block_table + static_cast<int64_t>(sq) * a.max_pages;
+  const int h = lane & 15, g = lane >> 4;
+  H16Unit U;
+  if (!h16_unit(a, tid, U)) return;
+  const int t0 = U.t0, t1 = U.t1;
+  const int32_t* bt = block_table + static_cast<int64_t>(U.sq) * a.max_pages;
   const int ntiles = (t1 - t0 + kH16Tok - 1) / kH16Tok;
-  const int mine = ntiles > wv ? (ntiles - wv + kWaves - 1) / kWaves : 0;   // this wave's tiles
+  const int mine = ntiles > wv ? (ntiles - wv + kWaves - 1) / kWaves : 0;
 
-  // queries as B fragments: head h, k = 32 ks + 8 g .. + 7, rounded to bf16
   bf16x8_t qf[kH16Steps];
-  {
-    const float* ql = a.q_lat + (static_cast<int64_t>(b) * nh + h) * kDc;
-    const float* qp = a.q_pe + (static_cast<int64_t>(b) * nh + h) * kDr;
-#pragma unroll
-    for (int ks = 0; ks < kH16Steps; ++ks) {
-      const float* src = ks < kDc / 32 ? ql + 32 * ks + 8 * g : qp + 32 * (ks - kDc / 32) + 8 * g;
-      const float4 v0 = *reinterpret_cast<const float4*>(src);
-      const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
-      const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-      qf[ks] = pack8(v);
-    }
-  }
-
+  h16_queries(a, U.b, h, g, qf);
   const uint32_t slot0 = lds_addr(ring) + static_cast<uint32_t>(2 * kH16Slot) * wv;
-  // operand offsets inside a slot: as the bf16 kernel
-  const int ar = h16row(lane & 15);
-  const uint32_t aoff = kPitch * ar;
-  const int akey = h16key(ar);
-  uint32_t roff_r[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q)
-    roff_r[q] = kH16Tok * kPitch + 128 * ar + 16 * ((4 * q + g) ^ rkey(ar));
-  const int s16 = lane & 15;
-  const int br = h16row(4 * g + (s16 >> 2));
-  const int bkey = h16key(br);
-  const uint32_t boff = kPitch * br + 8 * (s16 & 1);
-  const int bsub = (s16 & 3) >> 1;
+  const H16Lane L = h16_lane(lane);
   // dequantization: this lane's rows 2i + (lane >> 5) and code chunk lane & 31
   // (latent columns 16 (lane & 31) .. + 15, bf16 chunks 2 (lane & 31) and + 1)
   const int crow = lane >> 5, cchunk = lane & 31;
@@ -1610,8 +1617,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_f8_h16(
 #pragma unroll
   for (int nb = 0; nb < kH16Blocks; ++nb) o[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_ref = -INFINITY, l_part = 0.f;
-  constexpr int kAAhead = 4, kARing = 6;    // score operands read ahead
-  constexpr int kBAhead = 6, kBRing = 8;    // P.C operands read ahead
   F8H16Regs rga, rgb;   // codes of tiles u (even u: rga) and u + 1
   for (int pass = 0; pass < 2 && mine > 0; ++pass) {
     if (pass > 0) {
@@ -1628,56 +1633,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_f8_h16(
       const uint32_t T = slot0 + (u & 1) * kH16Slot;
       dequantize(cur, T, nv0);
       wait_lgkm(0);   // the wave's own rows are in LDS before it reads them
-      auto lda = [&](int ks) {
-        return ks < kDc / 32 ? lds_b128(T + aoff + 16 * ((4 * ks + g) ^ akey))
-                             : lds_b128(T + roff_r[ks - kDc / 32]);
-      };
-      bf16x8_t arr[kARing];
-#pragma unroll
-      for (int d = 0; d < kAAhead; ++d) arr[d] = lda(d);
-      f32x4_t x = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < kH16Steps; ++ks) {
-        if (ks + kAAhead < kH16Steps) arr[(ks + kAAhead) % kARing] = lda(ks + kAAhead);
-        wait_lgkm(min(kAAhead, kH16Steps - 1 - ks));
-        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(arr[ks % kARing], qf[ks], x, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      auto ldb = [&](int nb) { return lds_tr16(T + boff + 16 * ((2 * nb + bsub) ^ bkey)); };
-      s16x4_t bb[kBRing];
-#pragma unroll
-      for (int d = 0; d < kBAhead; ++d) bb[d] = ldb(d);
-      if (nv0 < kH16Tok) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (h16row(4 * g + i) >= nv0) x[i] = -INFINITY;
-      }
-      if (pass == 0 && u == 0) {
-        float tm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-        tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
-        tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
-        m_ref = tm * cs;
-      }
-      const float mr = fmaxf(m_ref, -1e30f);
-      float p[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        seen = fmaxf(seen, x[i]);
-        p[i] = __builtin_amdgcn_exp2f(fmaf(x[i], cs, -mr));
-      }
-      const unsigned w01 = cvt2(p[0], p[1]), w23 = cvt2(p[2], p[3]);
-      l_part += (__uint_as_float(w01 << 16) + __uint_as_float(w01 & 0xFFFF0000u)) +
-                (__uint_as_float(w23 << 16) + __uint_as_float(w23 & 0xFFFF0000u));
-      const u32x2_t pw = {w01, w23};
-      const s16x4_t pa = __builtin_bit_cast(s16x4_t, pw);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int nb = 0; nb < kH16Blocks; ++nb) {
-        if (nb + kBAhead < kH16Blocks) bb[(nb + kBAhead) % kBRing] = ldb(nb + kBAhead);
-        wait_lgkm(min(kBAhead, kH16Blocks - 1 - nb));
-        o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, bb[nb % kBRing], o[nb], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      h16_tile(T, nv0, qf, L, g, cs, pass == 0 && u == 0, o, m_ref, l_part, seen);
       // every read of this slot has returned (the last wait was lgkmcnt(0)): refill it
       nv0 = nv1;
       if (u + 2 < mine) nv1 = issue(u + 2, cur);
@@ -1693,50 +1649,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_f8_h16(
     m_ref = seen;
   }
   if (bad_page) set_err(a.err, ERR_PAGE);
-
-  // ---- combine the 4 waves (as the bf16 kernel)
-  float lsum = l_part + __shfl_xor(l_part, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
-  const float mw = mine > 0 ? m_ref : -INFINITY;
-  __syncthreads();
-  if (g == 0) {
-    wstate[wv][0][h] = mw;
-    wstate[wv][1][h] = mine > 0 ? lsum : 0.f;
-  }
-  __syncthreads();
-  float mh = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) mh = fmaxf(mh, wstate[w][0][h]);
-  const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - mh);
-  if (wv == 0 && g == 0) {
-    float z = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float m = wstate[w][0][h];
-      if (m != -INFINITY) z += wstate[w][1][h] * __builtin_amdgcn_exp2f(m - mh);
-    }
-    wstate[0][1][h] = z > 0.f ? 1.f / z : 0.f;
-    lse_out[h] = z > 0.f ? (mh + __log2f(z)) * 0.6931471805599453f : -INFINITY;
-  }
-  constexpr int kRowW = kDc + 4;
-  float* stage = reinterpret_cast<float*>(ring) + wv * nh * kRowW;
-  float fh[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) fh[i] = __shfl(f, 4 * g + i, 64);
-#pragma unroll
-  for (int nb = 0; nb < kH16Blocks; ++nb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) stage[(4 * g + i) * kRowW + 16 * nb + s16] = o[nb][i] * fh[i];
-  __syncthreads();
-  const float* st_all = reinterpret_cast<const float*>(ring);
-#pragma unroll 4
-  for (int i = 0; i < 2 * nh; ++i) {
-    const int hr = i >> 1, c = 128 * wv + 64 * (i & 1) + lane;
-    float acc = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) acc += st_all[(w * nh + hr) * kRowW + c];
-    o_out[hr * kDc + c] = acc * wstate[0][1][hr];
-  }
+  h16_combine(ring, wstate, o, l_part, m_ref, mine, wv, lane, U.o_out, U.lse_out);
 }
 
 }  // namespace

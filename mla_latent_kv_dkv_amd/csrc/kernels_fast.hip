@@ -364,36 +364,48 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
   // ---- this wave's queries as MFMA B fragments: head 32wv + r32, k = 16ks + 8g2 + j
   bf16x8_t qf[kKSteps];
   {
-    // the wave's 32 query rows are read as contiguous 1 KB blocks (every load a
-    // run of whole cache lines), turned into bf16 rows in the still unused tile
-    // ring (wave w at 32 kQPitch w, row r at kQPitch r: 1152 bytes + 16 of pad,
-    // so a fragment read of 32 rows is conflict-free), and read back as fragments
-    constexpr int kQPitch = (kDc + kDr) * 2 + 16;
-    const uint32_t qst = lds_addr(ring) + static_cast<uint32_t>(kHeads * kQPitch) * wv;
-    const float* qlb = a.q_lat + (static_cast<int64_t>(b) * nh + kHeads * wv) * kDc;
-    const float* qpb = a.q_pe + (static_cast<int64_t>(b) * nh + kHeads * wv) * kDr;
+    // The wave's 32 latent query rows go into the still unused tile ring by
+    // asynchronous copies, every copy of a half in flight at once (wave w at 32 KB w;
+    // half hf: columns 256 hf .., row r at 1 KB r, fp32, 16-byte chunk c at
+    // c ^ (r & 15), so a fragment read of 32 rows is conflict-free), and are read
+    // back as bf16 fragments; the k^R part (64 columns) goes straight to registers
+    // while the copies run.
+    const uint32_t qst = lds_addr(ring) + 32768u * static_cast<uint32_t>(wv);
+    const uint64_t qlb = reinterpret_cast<uint64_t>(
+        a.q_lat + (static_cast<int64_t>(b) * nh + kHeads * wv) * kDc);
+    const float* qpr = a.q_pe + (static_cast<int64_t>(b) * nh + kHeads * wv + r32) * kDr;
+    float4 pe[8];   // k^R columns 16 q + 8 g2 .. + 7 of row r32
 #pragma unroll
-    for (int i = 0; i < kHeads * kDc / 256; ++i) {   // 64 blocks of 64 float4
-      const int e = 4 * (64 * i + lane);
-      const float4 v = *reinterpret_cast<const float4*>(qlb + e);
-      const u32x2_t w2 = {cvt2(v.x, v.y), cvt2(v.z, v.w)};
-      *reinterpret_cast<__attribute__((address_space(3))) u32x2_t*>(static_cast<uintptr_t>(
-          qst + kQPitch * (e / kDc) + 2 * (e % kDc))) = w2;
-      if ((i & 7) == 7) __builtin_amdgcn_sched_barrier(0);   // bounded loads in flight
+    for (int q = 0; q < 4; ++q) {
+      pe[2 * q] = *reinterpret_cast<const float4*>(qpr + 16 * q + 8 * g2);
+      pe[2 * q + 1] = *reinterpret_cast<const float4*>(qpr + 16 * q + 8 * g2 + 4);
+    }
+    const int sw = r32 & 15;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+      for (int r = 0; r < kHeads; ++r)
+        dma_block(qlb, static_cast<uint32_t>(r * kDc * 4 + hf * 1024 + 16 * (lane ^ (r & 15))),
+                  qst + 1024 * r);
+      wait_vmcnt<0>();   // this wave's half is in LDS (a wave reads only its own rows)
+#pragma unroll
+      for (int kl = 0; kl < 16; ++kl) {
+        const int c0 = 4 * kl + 2 * g2;   // fp32 chunk of columns 16 kl + 8 g2 ..
+        const u32x4_t x0 = lds_ld128(qst + 1024 * r32 + 16 * (c0 ^ sw));
+        const u32x4_t x1 = lds_ld128(qst + 1024 * r32 + 16 * ((c0 + 1) ^ sw));
+        const float v[8] = {__uint_as_float(x0[0]), __uint_as_float(x0[1]), __uint_as_float(x0[2]),
+                            __uint_as_float(x0[3]), __uint_as_float(x1[0]), __uint_as_float(x1[1]),
+                            __uint_as_float(x1[2]), __uint_as_float(x1[3])};
+        qf[16 * hf + kl] = pack8(v);
+      }
+      wait_lgkm(0);   // read before the next half's copies land on the same rows
     }
 #pragma unroll
-    for (int i = 0; i < kHeads * kDr / 256; ++i) {   // 8 blocks
-      const int e = 4 * (64 * i + lane);
-      const float4 v = *reinterpret_cast<const float4*>(qpb + e);
-      const u32x2_t w2 = {cvt2(v.x, v.y), cvt2(v.z, v.w)};
-      *reinterpret_cast<__attribute__((address_space(3))) u32x2_t*>(static_cast<uintptr_t>(
-          qst + kQPitch * (e / kDr) + 2 * (kDc + e % kDr))) = w2;
+    for (int q = 0; q < 4; ++q) {
+      const float v[8] = {pe[2 * q].x, pe[2 * q].y, pe[2 * q].z, pe[2 * q].w,
+                          pe[2 * q + 1].x, pe[2 * q + 1].y, pe[2 * q + 1].z, pe[2 * q + 1].w};
+      qf[kLatSteps + q] = pack8(v);
     }
-    wait_lgkm(0);   // this wave's rows are in LDS (a wave reads only its own rows)
-#pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks)
-      qf[ks] = lds_b128(qst + kQPitch * r32 + 2 * (16 * ks + 8 * g2));
-    wait_lgkm(0);
     lds_barrier();  // every wave is done with the ring before tiles are copied into it
   }
 

@@ -1074,6 +1074,121 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile(GemmArgs a) {
   }
 }
 
+
+// The tiled product for a bf16 X with both operand tiles staged by asynchronous
+// global->LDS copies (no register staging, so no compiler-placed waits between a
+// chunk's loads and its use): 2 stages of (TN + TM) rows x 64 k (128 bytes per row,
+// 16-byte chunk c of row r at c ^ ((r >> 1) & 7): conflict-free fragment reads).  A
+// copy instruction moves 8 rows; wave w issues instructions w, w + 4, ...  Chunk
+// c + 1 is in flight while chunk c is multiplied.  Products and epilogue as
+// k_gemm_tile.  The 8 weight rows of a copy never straddle w1 / w2 (n_split is a
+// multiple of TN or past N).
+template <int TN, int TM>
+__global__ __launch_bounds__(256, 2) void k_gemm_tile_dma(GemmArgs a) {
+  constexpr int BN = TN / 64, BM = TM / 64;   // 32-row blocks per wave
+  constexpr int kRows = TN + TM, kStage = kRows * kTk * 2;
+  constexpr int kInstr = kRows / 8, kPerWave = kInstr / 4;   // copies per stage, per wave
+  constexpr int kOPitch = TN + 4;   // floats per staged output row
+  constexpr int kBytes = 2 * kStage > TM * kOPitch * 4 ? 2 * kStage : TM * kOPitch * 4;
+  __shared__ __attribute__((aligned(1024))) char tiles[kBytes];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int z = blockIdx.z, n0 = blockIdx.x * TN, m0 = blockIdx.y * TM;
+  const uint32_t lds0 = lds_addr(tiles);
+  auto key = [](int r) { return (r >> 1) & 7; };
+  // copy j of this wave: stage rows 8q .. 8q + 7 (q = wv + 4j); base of its first
+  // row (uniform) and this lane's byte offset (row 8q + (lane >> 3), source chunk
+  // (lane & 7) ^ key(row)); rows past N or M re-read the last row (never stored)
+  uint64_t gb[kPerWave];
+  uint32_t vo[kPerWave];
+#pragma unroll
+  for (int j = 0; j < kPerWave; ++j) {
+    const int q = wv + 4 * j, row = 8 * q + (lane >> 3), ch = (lane & 7) ^ key(row);
+    if (8 * q < TN) {
+      const int nb = min(n0 + 8 * q, a.N - 1), nr = min(n0 + row, a.N - 1);
+      const bf16_t* w = nb < a.n_split
+                            ? static_cast<const bf16_t*>(a.w1) + static_cast<int64_t>(nb) * a.ldw_n
+                            : static_cast<const bf16_t*>(a.w2) +
+                                  static_cast<int64_t>(nb - a.n_split) * a.ldw_n;
+      gb[j] = reinterpret_cast<uint64_t>(w + static_cast<int64_t>(z) * a.w_bs);
+      vo[j] = static_cast<uint32_t>(((nr - nb) * a.ldw_n + 8 * ch) * 2);
+    } else {
+      const int mb = min(m0 + 8 * q - TN, a.M - 1), mr = min(m0 + row - TN, a.M - 1);
+      gb[j] = reinterpret_cast<uint64_t>(static_cast<const bf16_t*>(a.x) +
+                                         static_cast<int64_t>(z) * a.x_bs +
+                                         static_cast<int64_t>(mb) * a.ldx_m);
+      vo[j] = static_cast<uint32_t>(((mr - mb) * a.ldx_m + 8 * ch) * 2);
+    }
+  }
+  auto issue = [&](int stage, int k0) {
+#pragma unroll
+    for (int j = 0; j < kPerWave; ++j)
+      dma_block(gb[j] + 2 * static_cast<uint64_t>(k0), vo[j],
+                lds0 + stage * kStage + 1024 * (wv + 4 * j));
+  };
+  const int wn = wv & 1, wm = wv >> 1, r32 = lane & 31, h = lane >> 5;
+  f32x16_t acc[BN][BM];
+#pragma unroll
+  for (int i = 0; i < BN; ++i)
+#pragma unroll
+    for (int j = 0; j < BM; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  // operand of 32-row block i at k-step s: row 32i + r32 of the wave's half, chunk 2s + h
+  auto frag = [&](uint32_t st, int row, int s) {
+    return __builtin_bit_cast(bf16x8_t,
+                              lds_u128(st + 128 * row + 16 * ((2 * s + h) ^ key(row))));
+  };
+  auto multiply = [&](int stage) {
+    const uint32_t st = lds0 + stage * kStage;
+#pragma unroll
+    for (int s = 0; s < kTk / 16; ++s) {
+      bf16x8_t af[BN], bfr[BM];
+#pragma unroll
+      for (int i = 0; i < BN; ++i) af[i] = frag(st, 32 * BN * wn + 32 * i + r32, s);
+#pragma unroll
+      for (int j = 0; j < BM; ++j) bfr[j] = frag(st, TN + 32 * BM * wm + 32 * j + r32, s);
+#pragma unroll
+      for (int i = 0; i < BN; ++i)
+#pragma unroll
+        for (int j = 0; j < BM; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  };
+  const int nk = a.K / kTk;
+  issue(0, 0);
+  if (nk > 1) issue(1, kTk);
+  for (int kb = 0; kb < nk; ++kb) {
+    if (kb + 1 < nk) wait_vmcnt<kPerWave>();   // chunk kb has landed (kb + 1 may fly)
+    else wait_vmcnt<0>();
+    __syncthreads();   // ... for every wave's copies
+    multiply(kb & 1);
+    __syncthreads();   // every wave is done with this stage before it is refilled
+    if (kb + 2 < nk) issue(kb & 1, (kb + 2) * kTk);
+  }
+  // acc[i][j] element e of lane (r32, h): row 32 BM wm + 32j + r32, column
+  // 32 BN wn + 32i + 8(e >> 2) + 4h + (e & 3) of the tile; through LDS (the stages
+  // are free after the last barrier) to the epilogue's column pairs
+  float* ot = reinterpret_cast<float*>(tiles);
+#pragma unroll
+  for (int j = 0; j < BM; ++j)
+#pragma unroll
+    for (int i = 0; i < BN; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; e += 2)
+        *reinterpret_cast<float2*>(&ot[(32 * BM * wm + 32 * j + r32) * kOPitch + 32 * BN * wn + 32 * i +
+                                       8 * (e >> 2) + 4 * h + (e & 3)]) =
+            make_float2(acc[i][j][e], acc[i][j][e + 1]);
+  __syncthreads();
+  for (int q = tid; q < TM * TN / 2; q += 256) {   // pair q: row q / (TN/2), columns 2 (q % (TN/2)), +1
+    const int ml = q / (TN / 2), nl = 2 * (q % (TN / 2));
+    const int m = m0 + ml, n = n0 + nl;
+    if (m < a.M && n < a.N) {
+      const float2 v = *reinterpret_cast<const float2*>(&ot[ml * kOPitch + nl]);
+      gemm_epilogue<bf16_t>(a, z, m, n, v.x, v.y);
+    }
+  }
+}
+
 constexpr int kWsMinGroups = 512;   // workgroups wanted before K is split further
 
 struct WsPlan {
@@ -1362,6 +1477,8 @@ hipError_t launch_gemm_fast(const GemmArgs& a, void* partial, size_t partial_byt
     const dim3 grid((a.N + kTt - 1) / kTt, (a.M + kTt - 1) / kTt, a.batch);
     if (a.x_f32)
       hipLaunchKernelGGL((k_gemm_tile<float, kTt, kTt>), grid, dim3(256), 0, stream, a);
+    else if (a.n_split % kTt == 0 || a.n_split >= a.N)
+      hipLaunchKernelGGL((k_gemm_tile_dma<kTt, kTt>), grid, dim3(256), 0, stream, a);
     else
       hipLaunchKernelGGL((k_gemm_tile<bf16_t, kTt, kTt>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();

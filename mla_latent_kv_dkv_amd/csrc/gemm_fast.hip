@@ -1082,9 +1082,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile(GemmArgs a) {
 // copy instruction moves 8 rows; wave w issues instructions w, w + 4, ...  Chunk
 // c + 1 is in flight while chunk c is multiplied.  Products and epilogue as
 // k_gemm_tile.  The 8 weight rows of a copy never straddle w1 / w2 (n_split is a
-// multiple of TN or past N).
+// multiple of TN or past N).  With ksplit > 1 (grid z = batch x ksplit) a workgroup
+// takes K slice ks and writes its fp32 tile to partial[ks][z][m][n] for
+// k_gemm_finish instead of applying the epilogue.
 template <int TN, int TM>
-__global__ __launch_bounds__(256, 2) void k_gemm_tile_dma(GemmArgs a) {
+__global__ __launch_bounds__(256, 2) void k_gemm_tile_dma(GemmArgs a, int ksplit, float* partial) {
   constexpr int BN = TN / 64, BM = TM / 64;   // 32-row blocks per wave
   constexpr int kRows = TN + TM, kStage = kRows * kTk * 2;
   constexpr int kInstr = kRows / 8, kPerWave = kInstr / 4;   // copies per stage, per wave
@@ -1092,7 +1094,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile_dma(GemmArgs a) {
   constexpr int kBytes = 2 * kStage > TM * kOPitch * 4 ? 2 * kStage : TM * kOPitch * 4;
   __shared__ __attribute__((aligned(1024))) char tiles[kBytes];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int z = blockIdx.z, n0 = blockIdx.x * TN, m0 = blockIdx.y * TM;
+  const int z = blockIdx.z / ksplit, ks = blockIdx.z - z * ksplit;
+  const int n0 = blockIdx.x * TN, m0 = blockIdx.y * TM;
+  const int kslice = a.K / ksplit;
+  const int64_t kbeg = static_cast<int64_t>(ks) * kslice;
   const uint32_t lds0 = lds_addr(tiles);
   auto key = [](int r) { return (r >> 1) & 7; };
   // copy j of this wave: stage rows 8q .. 8q + 7 (q = wv + 4j); base of its first
@@ -1109,13 +1114,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile_dma(GemmArgs a) {
                             ? static_cast<const bf16_t*>(a.w1) + static_cast<int64_t>(nb) * a.ldw_n
                             : static_cast<const bf16_t*>(a.w2) +
                                   static_cast<int64_t>(nb - a.n_split) * a.ldw_n;
-      gb[j] = reinterpret_cast<uint64_t>(w + static_cast<int64_t>(z) * a.w_bs);
+      gb[j] = reinterpret_cast<uint64_t>(w + static_cast<int64_t>(z) * a.w_bs + kbeg);
       vo[j] = static_cast<uint32_t>(((nr - nb) * a.ldw_n + 8 * ch) * 2);
     } else {
       const int mb = min(m0 + 8 * q - TN, a.M - 1), mr = min(m0 + row - TN, a.M - 1);
       gb[j] = reinterpret_cast<uint64_t>(static_cast<const bf16_t*>(a.x) +
                                          static_cast<int64_t>(z) * a.x_bs +
-                                         static_cast<int64_t>(mb) * a.ldx_m);
+                                         static_cast<int64_t>(mb) * a.ldx_m + kbeg);
       vo[j] = static_cast<uint32_t>(((mr - mb) * a.ldx_m + 8 * ch) * 2);
     }
   }
@@ -1154,7 +1159,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile_dma(GemmArgs a) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
   };
-  const int nk = a.K / kTk;
+  const int nk = kslice / kTk;
   issue(0, 0);
   if (nk > 1) issue(1, kTk);
   for (int kb = 0; kb < nk; ++kb) {
@@ -1184,7 +1189,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile_dma(GemmArgs a) {
     const int m = m0 + ml, n = n0 + nl;
     if (m < a.M && n < a.N) {
       const float2 v = *reinterpret_cast<const float2*>(&ot[ml * kOPitch + nl]);
-      gemm_epilogue<bf16_t>(a, z, m, n, v.x, v.y);
+      if (ksplit > 1)
+        *reinterpret_cast<float2*>(partial + ((static_cast<int64_t>(ks) * a.batch + z) * a.M + m) *
+                                                 a.N + n) = v;
+      else
+        gemm_epilogue<bf16_t>(a, z, m, n, v.x, v.y);
     }
   }
 }
@@ -1414,6 +1423,21 @@ static bool uv_wide_ok(const GemmArgs& a) {
 
 bool fast_gemm_ok(const GemmArgs& a) { return ws_ok(a) || uk_ok(a) || uv_wide_ok(a); }
 
+// Large-batch plain products whose 128 x 128 tiles would not cover the chip (W_O at
+// 256 rows: 80 tiles): the copy-staged tiled product over d K slices, d the smallest
+// divisor of K / 64 that gives 256 workgroups, then k_gemm_finish.  0 where it does
+// not apply.
+static int tile_split_d(const GemmArgs& a) {
+  if (!(ws_ok(a) && a.epi == EPI_STORE && !a.x_f32 && a.M >= 256 && a.K % kTk == 0 &&
+        a.N % 4 == 0 && (a.n_split % kTt == 0 || a.n_split >= a.N) && !tile_ok(a)))
+    return 0;
+  const int64_t groups = static_cast<int64_t>((a.N + kTt - 1) / kTt) * ((a.M + kTt - 1) / kTt) * a.batch;
+  const int chunks = a.K / kTk;
+  for (int d = 2; d <= chunks; ++d)
+    if (chunks % d == 0 && groups * d >= 256) return static_cast<int64_t>(d) * a.batch < 65536 ? d : 0;
+  return 0;
+}
+
 // W_UV with the merge folded in: the k_gemm_uv_wide form, the partials of every
 // head at 512 latent columns (16-byte aligned rows), one merge row per product row.
 bool uv_merge_ok(const GemmArgs& a, const MergeArgs& m) {
@@ -1442,6 +1466,8 @@ hipError_t launch_uv_merge(const GemmArgs& a, const MergeArgs& m, hipStream_t st
 
 size_t gemm_partial_bytes(const GemmArgs& a) {
   if (!ws_ok(a) || tile_ok(a) || uv_wide_ok(a) || small_tile_ok(a)) return 0;
+  if (const int d = tile_split_d(a))
+    return static_cast<size_t>(d) * a.batch * a.M * a.N * sizeof(float);
   if (xs_ok(a)) {
     const XsPlan q = xs_plan(a);
     return q.d > 1 ? xs_tiles_bytes(a, q) + xs_rope_bytes(a) : 0;
@@ -1478,7 +1504,7 @@ hipError_t launch_gemm_fast(const GemmArgs& a, void* partial, size_t partial_byt
     if (a.x_f32)
       hipLaunchKernelGGL((k_gemm_tile<float, kTt, kTt>), grid, dim3(256), 0, stream, a);
     else if (a.n_split % kTt == 0 || a.n_split >= a.N)
-      hipLaunchKernelGGL((k_gemm_tile_dma<kTt, kTt>), grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((k_gemm_tile_dma<kTt, kTt>), grid, dim3(256), 0, stream, a, 1, nullptr);
     else
       hipLaunchKernelGGL((k_gemm_tile<bf16_t, kTt, kTt>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
@@ -1487,6 +1513,15 @@ hipError_t launch_gemm_fast(const GemmArgs& a, void* partial, size_t partial_byt
     const dim3 grid(a.batch * (a.N / kUvN), (a.M + kUvM - 1) / kUvM);
     hipLaunchKernelGGL(k_gemm_uv_wide<false>, grid, dim3(256), 0, stream, a, MergeArgs{});
     return hipGetLastError();
+  }
+  if (const int d = tile_split_d(a)) {
+    if (partial == nullptr || !aligned16(partial) || partial_bytes < gemm_partial_bytes(a))
+      return hipErrorInvalidValue;
+    const dim3 grid((a.N + kTt - 1) / kTt, (a.M + kTt - 1) / kTt, a.batch * d);
+    hipLaunchKernelGGL((k_gemm_tile_dma<kTt, kTt>), grid, dim3(256), 0, stream, a, d,
+                       static_cast<float*>(partial));
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    return launch_finish(a, d, static_cast<float*>(partial), stream);
   }
   if (small_tile_ok(a)) {
     const dim3 grid(a.N / 64, 1, a.batch);

@@ -407,6 +407,34 @@ mla_status mla_append_latent_fp8(const mla_dims* dims, const void* h, const void
 size_t mla_append_workspace_bytes_fp8(const mla_dims* dims, int32_t n_rows);
 
 /*
+ * mla_absorb_q and mla_append_latent_fp8 of the same rows in one call (the
+ * FP8-pool form of mla_absorb_q_append, [Report] §2.2/§2.3/§3.1: the step's new
+ * token is queried and cached from the same h).  Row b is token
+ * (row_seq[b], pos[b]); its absorbed query goes to q_lat / q_pe and its latent
+ * row, computed in fp32, rotated and quantized exactly as mla_append_latent_fp8
+ * defines it, to the FP8 pool.  On the matrix-core path (bf16 dtype,
+ * batch <= 64) one projection over [W_Q; W_QR; W_DKV; W_KR] reads h once and
+ * leaves the fp32 rows in the workspace for the quantizer; other shapes make
+ * the two calls in turn.  The queries are those of mla_absorb_q bit for bit;
+ * the rows' fp32 sums may differ from mla_append_latent_fp8's in rounding order.
+ * Arguments as in mla_absorb_q_append (pos serves as row_pos; pool is the FP8
+ * pool, 16-byte aligned; d_c a multiple of 8).  Workspace: at least
+ * mla_absorb_q_append_fp8_workspace_bytes(dims, batch) bytes, 256-byte aligned,
+ * scratch for the call.  Out-of-range rows are not written to the pool and set
+ * the device error word; their queries are still computed.
+ */
+mla_status mla_absorb_q_append_fp8(const mla_dims* dims, const void* h, const void* w_q,
+                                   const void* w_qr, const void* w_uk, const void* w_dkv,
+                                   const void* w_kr, const int32_t* pos, const int32_t* row_seq,
+                                   int32_t batch, const int32_t* block_table, int32_t n_seqs,
+                                   int32_t max_pages, void* pool, int64_t num_pages,
+                                   float* q_lat, float* q_pe, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+/* Workspace bytes needed by mla_absorb_q_append_fp8 (0 if dims are invalid or
+ * d_c is not a multiple of 8). */
+size_t mla_absorb_q_append_fp8_workspace_bytes(const mla_dims* dims, int32_t batch);
+
+/*
  * Split-KV latent attention over the FP8 pool: mla_decode_attention with every
  * cached row replaced by its dequantized value [value(code) * 2^e | k^R].
  * The matrix-core path (bf16 dtype, n_h = 128, d_c = 512, d_R = 64,

@@ -24,6 +24,7 @@ __all__ = ["MlaDims", "MlaError", "make_dims", "load", "mla_append_latent", "mla
            "mla_append_workspace_bytes", "mla_device_error", "mla_set_kernel_path",
            "mla_status_string", "mla_fp8_page_bytes", "mla_quantize_rows_fp8",
            "mla_append_latent_fp8", "mla_append_workspace_bytes_fp8", "mla_decode_attention_fp8",
+           "mla_absorb_q_append_fp8", "mla_absorb_q_append_fp8_workspace_bytes",
            "mla_prefill_attention", "mla_prefill_attention_fp8", "mla_absorb_out_noalloc",
            "mla_absorb_out_noalloc_max_bytes", "mla_decode_plan", "mla_decode_plan_capacity",
            "mla_decode_attention_planned", "mla_decode_attention_fp8_planned",
@@ -89,6 +90,9 @@ _SIGS = {
     "mla_append_latent_fp8": [_DIMS, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _P, _I64, _P, _SZ,
                               _P],
     "mla_append_workspace_bytes_fp8": [_DIMS, _I32],
+    "mla_absorb_q_append_fp8": [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _P,
+                                _I64, _P, _P, _P, _SZ, _P],
+    "mla_absorb_q_append_fp8_workspace_bytes": [_DIMS, _I32],
     "mla_decode_attention_fp8": [_DIMS, _P, _P, _P, _I64, _P, _I32, _P, _I32, _I32, _P, _P, _P],
     "mla_prefill_attention": [_DIMS, _P, _P, _P, _I64, _P, _I32, _I32, _P, _P, _I32, _I32, _P, _P, _P],
     "mla_prefill_attention_fp8": [_DIMS, _P, _P, _P, _I64, _P, _I32, _I32, _P, _P, _I32, _I32, _P, _P,
@@ -100,6 +104,7 @@ _SIGS = {
 }
 _RES = {"mla_workspace_bytes": _SZ, "mla_workspace_bytes_cq": _SZ, "mla_append_workspace_bytes": _SZ,
         "mla_fp8_page_bytes": _SZ, "mla_append_workspace_bytes_fp8": _SZ,
+        "mla_absorb_q_append_fp8_workspace_bytes": _SZ,
         "mla_absorb_out_noalloc_max_bytes": _SZ, "mla_decode_plan_capacity": _I64,
         "mla_merge_absorb_out_workspace_bytes": _SZ,
         "mla_status_string": ctypes.c_char_p}
@@ -495,6 +500,38 @@ def mla_append_latent_fp8(dims, h, w_dkv, w_kr, row_seq, row_pos, block_table, p
         ctypes.byref(dims), _ptr(h), _ptr(w_dkv), _ptr(w_kr), _ptr(row_seq), _ptr(row_pos), n,
         _ptr(block_table), block_table.shape[0], block_table.shape[1], _ptr(pool), pool.shape[0],
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def mla_absorb_q_append_fp8_workspace_bytes(dims: MlaDims, batch: int) -> int:
+    return int(load().mla_absorb_q_append_fp8_workspace_bytes(ctypes.byref(dims), batch))
+
+
+def mla_absorb_q_append_fp8(dims, h, w_q, w_qr, w_uk, w_dkv, w_kr, pos, row_seq, block_table,
+                            pool, q_lat, q_pe, workspace, stream=None):
+    """mla_absorb_q and mla_append_latent_fp8 of the same rows (row b = token
+    (row_seq[b], pos[b])) in one call; one projection over all four weights where
+    the matrix-core path applies.  ``workspace``: at least
+    mla_absorb_q_append_fp8_workspace_bytes(dims, batch) bytes."""
+    import torch
+    B, nh = h.shape[0], dims.n_heads
+    e = _elem(dims)
+    _expect(h, (B, dims.hidden), e, "h")
+    _expect(w_q, (nh * dims.d_head, dims.hidden), e, "w_q")
+    _expect(w_qr, (nh * dims.d_rope, dims.hidden), e, "w_qr")
+    _expect(w_uk, (nh * dims.d_head, dims.d_latent), e, "w_uk")
+    _expect(w_dkv, (dims.d_latent, dims.hidden), e, "w_dkv")
+    _expect(w_kr, (dims.d_rope, dims.hidden), e, "w_kr")
+    _expect(pos, (B,), torch.int32, "pos")
+    _expect(row_seq, (B,), torch.int32, "row_seq")
+    _expect_table(block_table)
+    _expect_fp8_pool(dims, pool)
+    _expect(q_lat, (B, nh, dims.d_latent), torch.float32, "q_lat")
+    _expect(q_pe, (B, nh, dims.d_rope), torch.float32, "q_pe")
+    _check("mla_absorb_q_append_fp8", load().mla_absorb_q_append_fp8(
+        ctypes.byref(dims), _ptr(h), _ptr(w_q), _ptr(w_qr), _ptr(w_uk), _ptr(w_dkv), _ptr(w_kr),
+        _ptr(pos), _ptr(row_seq), B, _ptr(block_table), block_table.shape[0], block_table.shape[1],
+        _ptr(pool), pool.shape[0], _ptr(q_lat), _ptr(q_pe), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def mla_decode_attention_fp8(dims, q_lat, q_pe, pool, block_table, seq_lens, o_part, lse_part,

@@ -67,7 +67,13 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, int z, int m, i
     return;
   }
   if (a.epi == EPI_QPROJ_APPEND && n >= a.n_append) {
-    append_pair<T>(a, a.y3, a.n_split3, m, n - a.n_append, v0, v1);
+    if (a.ld3 > 0) {   // fp32 rows for a quantizer
+      float* r = static_cast<float*>(a.y3) + m * a.ld3 + (n - a.n_append);
+      r[0] = v0;
+      r[1] = v1;
+    } else {
+      append_pair<T>(a, a.y3, a.n_split3, m, n - a.n_append, v0, v1);
+    }
     return;
   }
   if (a.epi == EPI_QPROJ || a.epi == EPI_QPROJ_APPEND) {
@@ -106,6 +112,13 @@ __device__ __forceinline__ void gemm_epilogue4(const GemmArgs& a, int z, int m, 
   }
   const bool qproj = a.epi == EPI_QPROJ || a.epi == EPI_QPROJ_APPEND;
   const int n_q = a.epi == EPI_QPROJ_APPEND ? a.n_append : a.N;   // end of the query columns
+  if (a.epi == EPI_QPROJ_APPEND && a.ld3 > 0 && n >= a.n_append && n + 3 < a.N) {
+    float* r = static_cast<float*>(a.y3) + m * a.ld3 + (n - a.n_append);
+    if (aligned(r)) {
+      *reinterpret_cast<float4*>(r) = v;
+      return;
+    }
+  }
   if (qproj && a.y_f32 && n + 3 < a.n_split) {
     float* y = static_cast<float*>(a.y) + static_cast<int64_t>(m) * a.ldy + n;
     if (aligned(y)) {

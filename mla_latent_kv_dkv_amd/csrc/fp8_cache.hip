@@ -16,11 +16,27 @@ namespace {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-// One wave per row (4 rows per 256-thread block).
+// One wave per row (4 rows per 256-thread block).  The row's first 512 latent
+// values and first 64 k^R pairs (all of them at d_c <= 512, d_R <= 128) are loaded,
+// and their RoPE angles evaluated, before the slot lookup resolves: the three
+// do not depend on one another, so their latencies overlap.
 __global__ __launch_bounds__(256) void k_quantize_rows(QuantArgs a) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= a.n_rows) return;
+  const float* src = a.rows + static_cast<int64_t>(row) * a.ld_rows;
   const int seq = a.row_seq[row], pos = a.row_pos[row];
+  const int c0 = 8 * lane, p0 = lane;
+  f32x4_t lo0 = (f32x4_t){0.f, 0.f, 0.f, 0.f}, hi0 = lo0;
+  if (c0 < a.d_latent) {
+    lo0 = *reinterpret_cast<const f32x4_t*>(src + c0);
+    hi0 = *reinterpret_cast<const f32x4_t*>(src + c0 + 4);
+  }
+  float k0 = 0.f, k1 = 0.f, cs0 = 1.f, sn0 = 0.f;
+  if (p0 < a.d_rope / 2) {
+    k0 = src[a.d_latent + 2 * p0];
+    k1 = src[a.d_latent + 2 * p0 + 1];
+    if (a.rope) rope_cs(pos, p0, a.d_rope, a.rs, &cs0, &sn0);
+  }
   if (seq < 0 || seq >= a.n_seqs) { if (lane == 0) set_err(a.err, ERR_SEQ); return; }
   if (pos < 0 || pos >= a.max_pages * a.page_size) { if (lane == 0) set_err(a.err, ERR_POS); return; }
   const int page = a.block_table[static_cast<int64_t>(seq) * a.max_pages + pos / a.page_size];
@@ -28,11 +44,12 @@ __global__ __launch_bounds__(256) void k_quantize_rows(QuantArgs a) {
   const int slot = pos % a.page_size;
   uint8_t* pg = a.pool + static_cast<int64_t>(page) * a.page_bytes;
   uint8_t* dst = pg + static_cast<int64_t>(slot) * a.row_bytes;
-  const float* src = a.rows + static_cast<int64_t>(row) * a.ld_rows;
 
   // row scale exponent from the largest |c| (exact: frexp and the comparison)
   float amax = 0.f;
-  for (int c = 8 * lane; c < a.d_latent; c += 512) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fmaxf(fabsf(lo0[j]), fabsf(hi0[j])));
+  for (int c = c0 + 512; c < a.d_latent; c += 512) {
     const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(src + c);
     const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(src + c + 4);
 #pragma unroll
@@ -47,23 +64,22 @@ __global__ __launch_bounds__(256) void k_quantize_rows(QuantArgs a) {
     e = e < -126 ? -126 : (e > 127 ? 127 : e);
   }
   // codes: 8 latent values per lane and step, round to nearest even into e4m3
-  for (int c = 8 * lane; c < a.d_latent; c += 512) {
-    const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(src + c);
-    const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(src + c + 4);
+  // (rows are 4-byte aligned in the page: d_c % 8 == 0, d_R even)
+  auto put_codes = [&](int c, const f32x4_t& lo, const f32x4_t& hi) {
     int q0 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(lo[0], -e), ldexpf(lo[1], -e), 0, false);
     q0 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(lo[2], -e), ldexpf(lo[3], -e), q0, true);
     int q1 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(hi[0], -e), ldexpf(hi[1], -e), 0, false);
     q1 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(hi[2], -e), ldexpf(hi[3], -e), q1, true);
-    // rows are 4-byte aligned in the page (d_c % 8 == 0, d_R even)
     reinterpret_cast<uint32_t*>(dst + c)[0] = static_cast<uint32_t>(q0);
     reinterpret_cast<uint32_t*>(dst + c)[1] = static_cast<uint32_t>(q1);
-  }
+  };
+  if (c0 < a.d_latent) put_codes(c0, lo0, hi0);
+  for (int c = c0 + 512; c < a.d_latent; c += 512)
+    put_codes(c, *reinterpret_cast<const f32x4_t*>(src + c),
+              *reinterpret_cast<const f32x4_t*>(src + c + 4));
   // k^R in bf16, rotated at the row's position when asked
-  for (int p = lane; p < a.d_rope / 2; p += 64) {
-    float v0 = src[a.d_latent + 2 * p], v1 = src[a.d_latent + 2 * p + 1];
+  auto put_pair = [&](int p, float v0, float v1, float cs, float sn) {
     if (a.rope) {
-      float cs, sn;
-      rope_cs(pos, p, a.d_rope, a.rs, &cs, &sn);
       const float r0 = v0 * cs - v1 * sn, r1 = v0 * sn + v1 * cs;
       v0 = r0;
       v1 = r1;
@@ -71,6 +87,12 @@ __global__ __launch_bounds__(256) void k_quantize_rows(QuantArgs a) {
     const uint32_t w = static_cast<uint32_t>(f32_to_bf16(v0)) |
                        (static_cast<uint32_t>(f32_to_bf16(v1)) << 16);
     *reinterpret_cast<uint32_t*>(dst + a.d_latent + 4 * p) = w;
+  };
+  if (p0 < a.d_rope / 2) put_pair(p0, k0, k1, cs0, sn0);
+  for (int p = p0 + 64; p < a.d_rope / 2; p += 64) {
+    float cs = 1.f, sn = 0.f;
+    if (a.rope) rope_cs(pos, p, a.d_rope, a.rs, &cs, &sn);
+    put_pair(p, src[a.d_latent + 2 * p], src[a.d_latent + 2 * p + 1], cs, sn);
   }
   if (lane == 0)
     *reinterpret_cast<float*>(pg + static_cast<int64_t>(a.page_size) * a.row_bytes + 4 * slot) =

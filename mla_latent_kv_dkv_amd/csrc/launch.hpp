@@ -16,7 +16,7 @@ enum GemmEpilogue : int {
   EPI_QPROJ = 2,   // n < n_split -> y (q^C); n >= n_split -> RoPE per head -> y2 (q_pe)
   // EPI_QPROJ for n < n_append, and the latent append of the same rows for
   // n >= n_append: W rows from w3 (c^KV, n - n_append < n_split3) and w4 (k^R),
-  // written as EPI_APPEND does into the pool y3
+  // written as EPI_APPEND does into the pool y3 (or, with ld3 > 0, as fp32 rows)
   EPI_QPROJ_APPEND = 3,
 };
 
@@ -50,6 +50,10 @@ struct GemmArgs {
   const void* w4;
   int n_append, n_split3;
   void* y3;
+  // 0: the append columns go into the pool y3 as EPI_APPEND writes them; > 0:
+  // they stay fp32 and unrotated, row m at y3 + m * ld3 (the rows an FP8 pool's
+  // quantizer rotates, scales and scatters)
+  int64_t ld3;
 };
 
 hipError_t launch_gemm_generic(const GemmArgs& a, bool bf16, hipStream_t stream);

@@ -283,6 +283,23 @@ size_t rows_bytes(const mla_dims* d, int n_rows) {
   return align256(static_cast<size_t>(n_rows) * static_cast<size_t>(rows_ld(d)) * sizeof(float));
 }
 
+// Appended fp32 rows [c | k^R] (k^R not yet rotated, stride rows_ld) of tokens
+// (row_seq[i], row_pos[i]): RoPE on k^R, quantize, scatter into the FP8 pages.
+hipError_t quantize_appended(const mla_dims* d, const float* rows, int n_rows,
+                             const int32_t* row_seq, const int32_t* row_pos,
+                             const int32_t* block_table, int n_seqs, int max_pages, void* pool,
+                             int64_t num_pages, int* err, hipStream_t stream) {
+  mla::QuantArgs q{};
+  q.rows = rows; q.ld_rows = rows_ld(d); q.n_rows = n_rows;
+  q.d_latent = d->d_latent; q.d_rope = d->d_rope; q.rope = 1;
+  q.rs = rope_spec(d);
+  q.row_seq = row_seq; q.row_pos = row_pos; q.block_table = block_table;
+  q.n_seqs = n_seqs; q.max_pages = max_pages; q.page_size = d->page_size;
+  q.num_pages = num_pages; q.page_bytes = fp8_page_bytes(d); q.row_bytes = fp8_row_bytes(d);
+  q.pool = static_cast<uint8_t*>(pool); q.err = err;
+  return mla::launch_quantize_rows(q, stream);
+}
+
 // Checks shared by the attention calls; fills `a` (pool format aside).  Decode
 // units are sequences (seq_lens); prefill units are query tokens (q_seq, q_pos
 // into n_seqs block-table rows).
@@ -633,15 +650,64 @@ mla_status mla_append_latent_fp8(const mla_dims* d, const void* h, const void* w
   if (run_gemm(d, a, part, ws_bytes - rows_bytes(d, n_rows), stream) != hipSuccess)
     return MLA_ERR_HIP;
   // 2) RoPE on k^R at row_pos, quantize, scatter into the pages
-  mla::QuantArgs q{};
-  q.rows = rows; q.ld_rows = rows_ld(d); q.n_rows = n_rows;
-  q.d_latent = d->d_latent; q.d_rope = d->d_rope; q.rope = 1;
-  q.rs = rope_spec(d);
-  q.row_seq = row_seq; q.row_pos = row_pos; q.block_table = block_table;
-  q.n_seqs = n_seqs; q.max_pages = max_pages; q.page_size = d->page_size;
-  q.num_pages = num_pages; q.page_bytes = fp8_page_bytes(d); q.row_bytes = fp8_row_bytes(d);
-  q.pool = static_cast<uint8_t*>(pool); q.err = err;
-  return hip_status(mla::launch_quantize_rows(q, stream));
+  return hip_status(quantize_appended(d, rows, n_rows, row_seq, row_pos, block_table, n_seqs,
+                                      max_pages, pool, num_pages, err, stream));
+}
+
+size_t mla_absorb_q_append_fp8_workspace_bytes(const mla_dims* d, int32_t batch) {
+  if (check_dims(d) != MLA_OK || batch < 0 || !fp8_ok(d)) return 0;
+  // [q^C][fp32 rows [c^KV | k^R]][fp32 K-split partials]; no less than the two
+  // separate calls take when the fused product does not apply
+  return std::max(mla_workspace_bytes(d, batch) + rows_bytes(d, batch),
+                  mla_append_workspace_bytes_fp8(d, batch));
+}
+
+mla_status mla_absorb_q_append_fp8(const mla_dims* d, const void* h, const void* w_q,
+                                   const void* w_qr, const void* w_uk, const void* w_dkv,
+                                   const void* w_kr, const int32_t* pos, const int32_t* row_seq,
+                                   int32_t batch, const int32_t* block_table, int32_t n_seqs,
+                                   int32_t max_pages, void* pool, int64_t num_pages, float* q_lat,
+                                   float* q_pe, void* ws, size_t ws_bytes, hipStream_t stream) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (!fp8_ok(d)) return MLA_ERR_UNSUPPORTED;
+  if (batch < 0 || batch > (1 << 20) || n_seqs < 0 || max_pages < 0 || num_pages < 0)
+    return MLA_ERR_SHAPE;
+  if (batch == 0) return MLA_OK;
+  if (n_seqs < 1 || max_pages < 1 || num_pages < 1) return MLA_ERR_SHAPE;
+  if (static_cast<int64_t>(max_pages) * d->page_size > (int64_t{1} << 30)) return MLA_ERR_SHAPE;
+  if (!h || !w_q || !w_qr || !w_uk || !w_dkv || !w_kr || !pos || !row_seq || !block_table ||
+      !pool || !q_lat || !q_pe)
+    return MLA_ERR_NULL;
+  if (!aligned16(pool)) return MLA_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < mla_absorb_q_append_fp8_workspace_bytes(d, batch) || !ws_aligned(ws))
+    return MLA_ERR_WORKSPACE;
+  int* err = err_word();
+  if (!err) return MLA_ERR_HIP;
+  float* rows = reinterpret_cast<float*>(static_cast<char*>(ws) + act_bytes(d, batch));
+  char* part = reinterpret_cast<char*>(rows) + rows_bytes(d, batch);
+  const size_t pbytes = ws_bytes - act_bytes(d, batch) - rows_bytes(d, batch);
+  // 1) [q^C | q^R | c^KV | k^R] = h [W_Q; W_QR; W_DKV; W_KR]^T: q^C -> workspace,
+  //    RoPE'd q^R -> q_pe, the rows [c^KV | k^R] -> workspace in fp32
+  mla::GemmArgs a = qa_args(d, batch);
+  a.x = h; a.w1 = w_q; a.w2 = w_qr; a.w3 = w_dkv; a.w4 = w_kr;
+  a.y = ws; a.y2 = q_pe; a.y3 = rows; a.ld3 = rows_ld(d); a.pos = pos;
+  if (!(use_fast() && d->dtype == MLA_BF16 && mla::fused_qa_ok(a))) {
+    // shapes the fused product does not take: the two calls one after the other
+    st = mla_absorb_q(d, h, w_q, w_qr, w_uk, pos, batch, q_lat, q_pe, ws, ws_bytes, stream);
+    if (st != MLA_OK) return st;
+    return mla_append_latent_fp8(d, h, w_dkv, w_kr, row_seq, pos, batch, block_table, n_seqs,
+                                 max_pages, pool, num_pages, ws, ws_bytes, stream);
+  }
+  if (mla::launch_gemm_fast(a, part, pbytes, stream) != hipSuccess) return MLA_ERR_HIP;
+  // 2) RoPE on k^R at pos, quantize, scatter into the rows' pages
+  if (quantize_appended(d, rows, batch, row_seq, pos, block_table, n_seqs, max_pages, pool,
+                        num_pages, err, stream) != hipSuccess)
+    return MLA_ERR_HIP;
+  // 3) q_lat[b, i, :] = W_UK,i^T q^C[b, i, :] per head i (q^C in fp32)
+  mla::GemmArgs g = uk_args(d, batch, true);
+  g.x = ws; g.w1 = w_uk; g.w2 = w_uk; g.y = q_lat;
+  return hip_status(run_gemm(d, g, part, pbytes, stream));
 }
 
 mla_status mla_decode_attention_fp8(const mla_dims* d, const float* q_lat, const float* q_pe,

@@ -9,7 +9,7 @@ from __future__ import annotations
 import numpy as np
 
 from . import (make_dims, mla_absorb_out, mla_absorb_q, mla_absorb_q_append, mla_absorb_q_cq,
-               mla_append_latent,
+               mla_absorb_q_append_fp8, mla_absorb_q_append_fp8_workspace_bytes, mla_append_latent,
                mla_append_latent_fp8, mla_append_workspace_bytes, mla_append_workspace_bytes_fp8,
                mla_decode_attention, mla_decode_attention_fp8, mla_decode_attention_fp8_planned,
                mla_decode_attention_planned, mla_decode_plan, mla_fp8_page_bytes, mla_merge_lse,
@@ -137,6 +137,8 @@ class DeviceWorkload:
                        mla_merge_absorb_out_workspace_bytes(self.dims, B))
         if w.d_cq:
             ws_bytes = max(ws_bytes, mla_workspace_bytes_cq(self.dims, w.d_cq, B))
+        if self.fp8:
+            ws_bytes = max(ws_bytes, mla_absorb_q_append_fp8_workspace_bytes(self.dims, B))
         self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=self.dev)
 
     def fill_fp8_pool(self):
@@ -176,17 +178,17 @@ class DeviceWorkload:
                self.pos, self.block_table, self.pool, self.ws_append)
 
     def absorb_q_append(self):
-        """absorb_q and append of the step's tokens in one call (bf16 or f32 pool,
-        uncompressed query): one projection reads h for both."""
+        """absorb_q and append of the step's tokens in one call (uncompressed
+        query; any pool format): one projection reads h for both."""
         W = self.weights
-        mla_absorb_q_append(self.dims, self.h, W["w_q"], W["w_qr"], W["w_uk"], W["w_dkv"],
-                            W["w_kr"], self.pos, self.seq_ids, self.block_table, self.pool,
-                            self.q_lat, self.q_pe, self.ws)
+        fused = mla_absorb_q_append_fp8 if self.fp8 else mla_absorb_q_append
+        fused(self.dims, self.h, W["w_q"], W["w_qr"], W["w_uk"], W["w_dkv"], W["w_kr"], self.pos,
+              self.seq_ids, self.block_table, self.pool, self.q_lat, self.q_pe, self.ws)
 
     def query_and_append(self):
-        """The step's first two calls: fused where the pool format and query form
-        allow, else absorb_q then append."""
-        if self.fp8 or self.w.d_cq:
+        """The step's first two calls: fused for the uncompressed query, else
+        absorb_q then append."""
+        if self.w.d_cq:
             self.absorb_q()
             self.append()
         else:

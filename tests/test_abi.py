@@ -182,6 +182,24 @@ def test_fp8_pool_sizes_and_argument_checks():
                                      None) == -3
     assert lib.mla_append_latent_fp8(d, None, None, None, None, None, 0, None, 0, 0, None, 0, None,
                                      0, None) == 0
+    # fused query + FP8 append: (dims, h, w_q, w_qr, w_uk, w_dkv, w_kr, pos, row_seq, batch,
+    # table, n_seqs, max_pages, pool, num_pages, q_lat, q_pe, ws, ws_bytes, stream)
+    qa = lib.mla_absorb_q_append_fp8
+    big = 1 << 20
+    assert qa(d36, P, P, P, P, P, P, P, P, 4, P, 1, 1, P, 1, P, P, P, big, None) == -3
+    assert qa(d, P, P, P, P, None, P, P, P, 4, P, 1, 1, P, 1, P, P, P, big, None) == -1
+    assert qa(d, P, P, P, P, P, P, P, P, 4, P, 1, 1, P, 1, None, P, P, big, None) == -1
+    assert qa(d, P, P, P, P, P, P, P, P, -1, P, 1, 1, P, 1, P, P, P, big, None) == -2
+    assert qa(d, P, P, P, P, P, P, P, P, 4, P, 0, 1, P, 1, P, P, P, big, None) == -2
+    assert qa(d, P, P, P, P, P, P, P, P, 4, P, 1, 1, P, 1, P, P, P, 64, None) == -4
+    assert qa(d, P, P, P, P, P, P, P, P, 4, P, 1, 1, P, 1, P, P, misaligned, big, None) == -4
+    assert qa(d, P, P, P, P, P, P, P, P, 4, P, 1, 1, misaligned, 1, P, P, P, big, None) == -3
+    assert qa(d, None, None, None, None, None, None, None, None, 0, None, 0, 0, None, 0, None,
+              None, None, 0, None) == 0
+    need = M.mla_absorb_q_append_fp8_workspace_bytes(full, 64)
+    assert need >= M.mla_workspace_bytes(full, 64) + 64 * 576 * 4
+    assert need >= M.mla_append_workspace_bytes_fp8(full, 64)
+    assert M.mla_absorb_q_append_fp8_workspace_bytes(_dims(d_latent=36), 4) == 0
     # attention_fp8: the same checks as the plain call, plus the FP8 format's
     assert lib.mla_decode_attention_fp8(d36, P, P, P, 1, P, 1, P, 1, 1, P, P, None) == -3
     assert lib.mla_decode_attention_fp8(d, None, P, P, 1, P, 1, P, 1, 1, P, P, None) == -1

@@ -214,6 +214,100 @@ def test_append_latent_fp8(name, path):
     assert M.mla_device_error() == 0
 
 
+# ------------------------------------------------ fused query + FP8 append --
+def _fused_fp8_case(w, B, lens, seqs, poss, bt, total):
+    """Run mla_absorb_q_append_fp8 on seeded weights; return the pool bytes, the
+    queries, mla_absorb_q's queries and the host operands."""
+    sh = {n: w.weight_shape(n) for n in ("w_q", "w_qr", "w_uk", "w_dkv", "w_kr")}
+    std = {n: 1 / np.sqrt(w.fan_in(n)) for n in sh}
+    dev = {n: device_tensor(torch, w, n, sh[n], std[n]) for n in sh}
+    h = device_tensor(torch, w, "h_q", (B, w.hidden))
+    d = _dims(w)
+    ws = torch.empty(M.mla_absorb_q_append_fp8_workspace_bytes(d, B), dtype=torch.uint8,
+                     device="cuda")
+    q_lat = torch.empty((B, w.n_heads, w.d_latent), dtype=torch.float32, device="cuda")
+    q_pe = torch.empty((B, w.n_heads, w.d_rope), dtype=torch.float32, device="cuda")
+    pool = torch.full((total, M.mla_fp8_page_bytes(d)), SENTINEL, dtype=torch.uint8, device="cuda")
+    pos_t = torch.tensor(poss, device="cuda")
+    M.mla_absorb_q_append_fp8(d, h, dev["w_q"], dev["w_qr"], dev["w_uk"], dev["w_dkv"],
+                              dev["w_kr"], pos_t, torch.tensor(seqs, device="cuda"),
+                              torch.tensor(bt, device="cuda"), pool, q_lat, q_pe, ws)
+    q_lat2, q_pe2 = torch.empty_like(q_lat), torch.empty_like(q_pe)
+    ws2 = torch.empty(M.mla_workspace_bytes(d, B), dtype=torch.uint8, device="cuda")
+    M.mla_absorb_q(d, h, dev["w_q"], dev["w_qr"], dev["w_uk"], pos_t, q_lat2, q_pe2, ws2)
+    hh = host_tensor(w, "h_q", (B, w.hidden))
+    hw = {n: host_tensor(w, n, sh[n], std[n]) for n in sh}
+    return pool.cpu().numpy(), (q_lat, q_pe), (q_lat2, q_pe2), hh, hw
+
+
+def _check_appended(w, got, bt, total, seqs, poss, ref_rows, rows):
+    """Each row in `rows` at its slot near the oracle's row; every other byte untouched."""
+    P, rb, pb = w.page_size, w.d_latent + 2 * w.d_rope, got.shape[1]
+    written = np.zeros((total, pb), bool)
+    flips = 0
+    for r in rows:
+        pg, slot = bt[seqs[r], poss[r] // P], poss[r] % P
+        img = np.concatenate([got[pg, slot * rb:(slot + 1) * rb],
+                              got[pg, P * rb + 4 * slot:P * rb + 4 * slot + 4]])
+        flips += _assert_codes_near(img, ref_rows[r], w.d_latent, w.d_rope, f"row {r}")
+        written[pg, slot * rb:(slot + 1) * rb] = True
+        written[pg, P * rb + 4 * slot:P * rb + 4 * slot + 4] = True
+    assert (got[~written] == SENTINEL).all(), "bytes outside the appended slots changed"
+    return flips
+
+
+# full-fp8 B = 5: the K-split product and its finish pass; B = 64: the largest batch of
+# the fused product; lite-fp8 B = 32: one K slice (rows straight from the product's
+# epilogue); tiny-fp8 (fp32): the two separate calls
+@pytest.mark.parametrize("name,B", [("full-fp8", 5), ("full-fp8", 64), ("lite-fp8", 32),
+                                    ("tiny-fp8", 5)])
+def test_absorb_q_append_fp8(name, B):
+    """The fused query + FP8 append: queries equal to mla_absorb_q's bit for bit and
+    at the oracle's bar; each appended row quantized as the oracle quantizes its
+    fp64 row (scale equal, codes equal up to a tie within fp32 rounding, k^R
+    within bf16 rounding); the rest of the pool untouched."""
+    w = _wl(name, batch=B)
+    note(f"absorb_q_append_fp8 {name} B={B}")
+    lens = np.array([3 + 37 * b for b in range(B)], dtype=np.int32)   # token b at lens[b] - 1
+    bt, total = I.page_table(w, lens)
+    seqs = np.arange(B, dtype=np.int32)
+    poss = (lens - 1).astype(np.int32)
+    M.mla_device_error(clear=True)
+    got, q, q2, hh, hw = _fused_fp8_case(w, B, lens, seqs, poss, bt, total)
+    assert torch.equal(q[0], q2[0]) and torch.equal(q[1], q2[1]), "queries differ from mla_absorb_q"
+    rl, rp = zip(*[O.absorb_q(hh[b], hw["w_q"], hw["w_qr"], hw["w_uk"], int(poss[b]), w.n_heads,
+                              w.d_head, w.d_latent, w.d_rope, w.rope_base) for b in range(B)])
+    assert_parity(to_np(q[0]), np.stack(rl), w.dtype, "q_lat")
+    assert_parity(to_np(q[1]), np.stack(rp), w.dtype, "q_pe")
+    ref_rows = O.latent_rows(hh, hw["w_dkv"], hw["w_kr"], poss, w.rope_base)
+    flips = _check_appended(w, got, bt, total, seqs, poss, ref_rows, range(B))
+    note(f"  codes at a tie resolved the other way: {flips} of {B * w.d_latent}")
+    assert M.mla_device_error() == 0
+
+
+@pytest.mark.parametrize("B", [5, 64])
+def test_absorb_q_append_fp8_out_of_range_rows(B):
+    """A row whose table entry is outside the pool and one whose sequence is
+    outside the table: neither is written, the error word names both, and the
+    queries are still mla_absorb_q's."""
+    w = _wl("full-fp8", batch=B)
+    note(f"absorb_q_append_fp8 out-of-range rows B={B}")
+    lens = np.array([3 + 37 * b for b in range(B)], dtype=np.int32)
+    bt, total = I.page_table(w, lens)
+    seqs = np.arange(B, dtype=np.int32)
+    poss = (lens - 1).astype(np.int32)
+    bt[1, poss[1] // w.page_size] = total + 3
+    seqs[3] = B + 9
+    M.mla_device_error(clear=True)
+    got, q, q2, hh, hw = _fused_fp8_case(w, B, lens, seqs, poss, bt, total)
+    err = M.mla_device_error(clear=True)
+    assert err & 1 and err & 4, err
+    assert torch.equal(q[0], q2[0]) and torch.equal(q[1], q2[1])
+    ref_rows = O.latent_rows(hh, hw["w_dkv"], hw["w_kr"], poss, w.rope_base)
+    _check_appended(w, got, bt, total, seqs, poss, ref_rows,
+                    [b for b in range(B) if b not in (1, 3)])
+
+
 # ------------------------------------------------------------ attention --
 @functools.lru_cache(maxsize=None)
 def _deq_rows(name, page, lens, b):

@@ -257,10 +257,10 @@ def _check_appended(w, got, bt, total, seqs, poss, ref_rows, rows):
 
 
 # full-fp8 B = 5: the K-split product and its finish pass; B = 64: the largest batch of
-# the fused product; lite-fp8 B = 32: one K slice (rows straight from the product's
-# epilogue); tiny-fp8 (fp32): the two separate calls
-@pytest.mark.parametrize("name,B", [("full-fp8", 5), ("full-fp8", 64), ("lite-fp8", 32),
-                                    ("tiny-fp8", 5)])
+# the fused product; B = 65 and tiny-fp8 (fp32): the two separate calls; lite-fp8
+# B = 32: one K slice (rows straight from the product's epilogue)
+@pytest.mark.parametrize("name,B", [("full-fp8", 5), ("full-fp8", 64), ("full-fp8", 65),
+                                    ("lite-fp8", 32), ("tiny-fp8", 5)])
 def test_absorb_q_append_fp8(name, B):
     """The fused query + FP8 append: queries equal to mla_absorb_q's bit for bit and
     at the oracle's bar; each appended row quantized as the oracle quantizes its
@@ -306,6 +306,48 @@ def test_absorb_q_append_fp8_out_of_range_rows(B):
     ref_rows = O.latent_rows(hh, hw["w_dkv"], hw["w_kr"], poss, w.rope_base)
     _check_appended(w, got, bt, total, seqs, poss, ref_rows,
                     [b for b in range(B) if b not in (1, 3)])
+
+
+def test_absorb_q_append_fp8_misaligned_input_falls_back():
+    """h starting 2 bytes past a 16-byte boundary: the fused product cannot take
+    it, so the call makes mla_absorb_q and mla_append_latent_fp8 in turn and gives
+    their results byte for byte."""
+    w = _wl("full-fp8", batch=8)
+    B = 8
+    lens = np.array([100 + 9 * b for b in range(B)], dtype=np.int32)
+    bt, total = I.page_table(w, lens)
+    poss = (lens - 1).astype(np.int32)
+    note("absorb_q_append_fp8 misaligned h")
+    sh = {n: w.weight_shape(n) for n in ("w_q", "w_qr", "w_uk", "w_dkv", "w_kr")}
+    std = {n: 1 / np.sqrt(w.fan_in(n)) for n in sh}
+    dev = {n: device_tensor(torch, w, n, sh[n], std[n]) for n in sh}
+    h_al = device_tensor(torch, w, "h_q", (B, w.hidden))
+    flat = torch.empty(B * w.hidden + 1, dtype=h_al.dtype, device="cuda")
+    h = flat[1:].view(B, w.hidden)
+    h.copy_(h_al)
+    assert h.data_ptr() % 16 == 2 and h.is_contiguous()
+    d = _dims(w)
+    ws = torch.empty(M.mla_absorb_q_append_fp8_workspace_bytes(d, B), dtype=torch.uint8,
+                     device="cuda")
+    pos_t = torch.tensor(poss, device="cuda")
+    seq_t = torch.arange(B, dtype=torch.int32, device="cuda")
+    bt_t = torch.tensor(bt, device="cuda")
+    outs = []
+    for fused in (True, False):
+        q_lat = torch.empty((B, w.n_heads, w.d_latent), dtype=torch.float32, device="cuda")
+        q_pe = torch.empty((B, w.n_heads, w.d_rope), dtype=torch.float32, device="cuda")
+        pool = torch.full((total, M.mla_fp8_page_bytes(d)), SENTINEL, dtype=torch.uint8,
+                          device="cuda")
+        if fused:
+            M.mla_absorb_q_append_fp8(d, h, dev["w_q"], dev["w_qr"], dev["w_uk"], dev["w_dkv"],
+                                      dev["w_kr"], pos_t, seq_t, bt_t, pool, q_lat, q_pe, ws)
+        else:
+            M.mla_absorb_q(d, h, dev["w_q"], dev["w_qr"], dev["w_uk"], pos_t, q_lat, q_pe, ws)
+            M.mla_append_latent_fp8(d, h, dev["w_dkv"], dev["w_kr"], seq_t, pos_t, bt_t, pool)
+        outs.append((q_lat, q_pe, pool))
+    for x, y in zip(outs[0], outs[1]):
+        assert torch.equal(x, y)
+    assert M.mla_device_error() == 0
 
 
 # ------------------------------------------------------------ attention --

@@ -45,6 +45,8 @@
 // no phase of a score read (16 rows, one chunk) or of a transposed read (4
 // rows, 4 chunks) puts two addresses on one bank, and the per-step offsets of
 // both reads are instruction immediates.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch_fast.hpp"
 #include "lds_copy.hpp"
@@ -169,6 +171,7 @@ __device__ __forceinline__ void wait_lgkm(int n) {
 // partial tile, rows past the split's end re-read row 0 (finite data whose
 // score is masked); a page outside the pool reads pool row 0 (masked, and
 // flagged by the caller).
+template <bool kStream>
 __device__ __forceinline__ void tile_issue(const char* __restrict__ pool, int page, bool ok,
                                            int tok0, int t1, uint32_t slot, int wv, int lane) {
   const int nvalid = ok ? min(kTileTok, t1 - tok0) : 0;
@@ -178,65 +181,77 @@ __device__ __forceinline__ void tile_issue(const char* __restrict__ pool, int pa
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const int r = 8 * wv + q;
-    dma_block(tile + (r < nvalid ? r : 0) * kRowBytes, 16 * (lane ^ lkey(r)), slot + kPitch * r);
+    dma_block<kStream>(tile + (r < nvalid ? r : 0) * kRowBytes, 16 * (lane ^ lkey(r)),
+                       slot + kPitch * r);
   }
   const int rr = 8 * wv + (lane >> 3);
   const uint32_t voff =
       (rr < nvalid ? rr : 0) * kRowBytes + 2 * kDc + 16 * ((lane & 7) ^ rkey(rr));
-  dma_block(tile, voff, slot + kRopeOff + 1024 * wv);
+  dma_block<kStream>(tile, voff, slot + kRopeOff + 1024 * wv);
 }
 
+// Text of the full-tile copies below; NT is the cache-policy suffix of each copy.
+#define MLA_TILE_COPY_ASM(NT) \
+  "s_mov_b32 %0, m0\n\t" \
+  "s_mov_b32 m0, %6\n\t" \
+  "s_nop 4\n\t" \
+  "global_load_lds_dwordx4 %2, %5" NT "\n\t" \
+  "v_add_u32 %1, 0x480, %2\n\t" \
+  "s_add_u32 m0, m0, 0x440\n\t" \
+  "s_nop 0\n\t" \
+  "global_load_lds_dwordx4 %1, %5" NT "\n\t" \
+  "v_add_u32 %1, 0x900, %2\n\t" \
+  "s_add_u32 m0, m0, 0x440\n\t" \
+  "s_nop 0\n\t" \
+  "global_load_lds_dwordx4 %1, %5" NT "\n\t" \
+  "v_add_u32 %1, 0xd80, %2\n\t" \
+  "s_add_u32 m0, m0, 0x440\n\t" \
+  "s_nop 0\n\t" \
+  "global_load_lds_dwordx4 %1, %5" NT "\n\t" \
+  "s_add_u32 m0, m0, 0x440\n\t" \
+  "s_nop 0\n\t" \
+  "global_load_lds_dwordx4 %3, %5" NT "\n\t" \
+  "v_add_u32 %1, 0x480, %3\n\t" \
+  "s_add_u32 m0, m0, 0x440\n\t" \
+  "s_nop 0\n\t" \
+  "global_load_lds_dwordx4 %1, %5" NT "\n\t" \
+  "v_add_u32 %1, 0x900, %3\n\t" \
+  "s_add_u32 m0, m0, 0x440\n\t" \
+  "s_nop 0\n\t" \
+  "global_load_lds_dwordx4 %1, %5" NT "\n\t" \
+  "v_add_u32 %1, 0xd80, %3\n\t" \
+  "s_add_u32 m0, m0, 0x440\n\t" \
+  "s_nop 0\n\t" \
+  "global_load_lds_dwordx4 %1, %5" NT "\n\t" \
+  "s_mov_b32 m0, %7\n\t" \
+  "s_nop 0\n\t" \
+  "global_load_lds_dwordx4 %4, %5" NT "\n\t" \
+  "s_mov_b32 m0, %0"
 // The same copies for a full tile of a valid page, as one block: M0 steps by
 // the LDS row pitch and the per-lane offset by the row stride, so the block
 // needs one VGPR temporary and no 64-bit address arithmetic.  `voff` =
 // 1152 (8 wv) + 16 (lane ^ lkey(8 wv)), `voff_hi` the same for row 8 wv + 4
 // (the key changes every 4 rows), `voff_rope` the RoPE copy's offset, `lds` =
 // slot + kPitch (8 wv).  Wait states: 5 after any VALU write of the SGPR
-// operands, 1 after each M0 write before the copy that reads it.
+// operands, 1 after each M0 write before the copy that reads it.  kStream: the
+// copies are non-temporal (decode, where each work unit reads its rows once).
+template <bool kStream>
 __device__ __forceinline__ void tile_issue_full(uint64_t tile, uint32_t voff, uint32_t voff_hi,
                                                 uint32_t voff_rope, uint32_t lds,
                                                 uint32_t lds_rope) {
   uint32_t save, tmp;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %6\n\t"
-      "s_nop 4\n\t"
-      "global_load_lds_dwordx4 %2, %5\n\t"
-      "v_add_u32 %1, 0x480, %2\n\t"
-      "s_add_u32 m0, m0, 0x440\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %5\n\t"
-      "v_add_u32 %1, 0x900, %2\n\t"
-      "s_add_u32 m0, m0, 0x440\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %5\n\t"
-      "v_add_u32 %1, 0xd80, %2\n\t"
-      "s_add_u32 m0, m0, 0x440\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %5\n\t"
-      "s_add_u32 m0, m0, 0x440\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %3, %5\n\t"
-      "v_add_u32 %1, 0x480, %3\n\t"
-      "s_add_u32 m0, m0, 0x440\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %5\n\t"
-      "v_add_u32 %1, 0x900, %3\n\t"
-      "s_add_u32 m0, m0, 0x440\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %5\n\t"
-      "v_add_u32 %1, 0xd80, %3\n\t"
-      "s_add_u32 m0, m0, 0x440\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %5\n\t"
-      "s_mov_b32 m0, %7\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %4, %5\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(save), "=&v"(tmp)
-      : "v"(voff), "v"(voff_hi), "v"(voff_rope), "s"(tile), "s"(lds), "s"(lds_rope)
-      : "memory");
+  if constexpr (kStream)
+    asm volatile(MLA_TILE_COPY_ASM(" nt")
+                 : "=&s"(save), "=&v"(tmp)
+                 : "v"(voff), "v"(voff_hi), "v"(voff_rope), "s"(tile), "s"(lds), "s"(lds_rope)
+                 : "memory");
+  else
+    asm volatile(MLA_TILE_COPY_ASM("")
+                 : "=&s"(save), "=&v"(tmp)
+                 : "v"(voff), "v"(voff_hi), "v"(voff_rope), "s"(tile), "s"(lds), "s"(lds_rope)
+                 : "memory");
 }
+#undef MLA_TILE_COPY_ASM
 
 // Wait until this wave's copies of a tile have landed, `after` tiles (0..2)
 // having been issued since.
@@ -329,6 +344,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
   const int r32 = lane & 31;          // token row (scores A) / head (scores B, P.C A)
   const int unit = unit_of(blockIdx.x, a.units);
   const int nh = 128;
+  // decode units read their rows once (non-temporal copies); prefill units share
+  // a sequence's rows, which stay cacheable
+  const bool stream = a.q_seq == nullptr;
 
   int b, sq, t0, t1;
   attn_unit(a, unit, tid == 0, &b, &sq, &t0, &t1);
@@ -503,10 +521,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h128(
     if (nvalid == kTileTok) {
       const uint64_t tile = reinterpret_cast<uint64_t>(
           pool + (static_cast<int64_t>(pg) * kPage + (tok & (kPage - 1))) * kRowBytes);
-      tile_issue_full(tile, voff_lo, voff_hi, voff_rope, slot + kPitch * 8 * wv,
-                      slot + kRopeOff + 1024 * wv);
+      if (stream)
+        tile_issue_full<true>(tile, voff_lo, voff_hi, voff_rope, slot + kPitch * 8 * wv,
+                              slot + kRopeOff + 1024 * wv);
+      else
+        tile_issue_full<false>(tile, voff_lo, voff_hi, voff_rope, slot + kPitch * 8 * wv,
+                               slot + kRopeOff + 1024 * wv);
+    } else if (stream) {
+      tile_issue<true>(pool, pg, ok, tok, t1, slot, wv, lane);
     } else {
-      tile_issue(pool, pg, ok, tok, t1, slot, wv, lane);
+      tile_issue<false>(pool, pg, ok, tok, t1, slot, wv, lane);
     }
     return nvalid;
   };
@@ -1432,6 +1456,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h16(
   const int h = lane & 15, g = lane >> 4;   // head (B/D column) and row group of this lane
   H16Unit U;
   if (!h16_unit(a, tid, U)) return;
+  const bool stream = a.q_seq == nullptr;   // decode: rows read once (non-temporal copies)
   const int t0 = U.t0, t1 = U.t1;
   const int32_t* bt = block_table + static_cast<int64_t>(U.sq) * a.max_pages;
   const int ntiles = (t1 - t0 + kH16Tok - 1) / kH16Tok;
@@ -1469,18 +1494,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma_h16(
     const uint64_t tile = reinterpret_cast<uint64_t>(
         ok ? pool + (static_cast<int64_t>(pg) * kPage + (tok & (kPage - 1))) * kRowBytes : pool);
     const uint32_t slot = slot0 + (u & 1) * kH16Slot;
+    auto copies = [&](auto policy) {
+      constexpr bool kS = decltype(policy)::value;
 #pragma unroll
-    for (int r = 0; r < kH16Tok; ++r) {
-      const int rv = r < nvalid ? r : 0;
-      dma_block(tile, kRowBytes * rv + 16 * (lane ^ h16key(r)), slot + kPitch * r);
-    }
+      for (int r = 0; r < kH16Tok; ++r) {
+        const int rv = r < nvalid ? r : 0;
+        dma_block<kS>(tile, kRowBytes * rv + 16 * (lane ^ h16key(r)), slot + kPitch * r);
+      }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int rr = 8 * q + (lane >> 3);
-      const int rv = rr < nvalid ? rr : 0;
-      dma_block(tile, kRowBytes * rv + 2 * kDc + 16 * ((lane & 7) ^ rkey(rr)),
-                slot + kH16Tok * kPitch + 1024 * q);
-    }
+      for (int q = 0; q < 2; ++q) {
+        const int rr = 8 * q + (lane >> 3);
+        const int rv = rr < nvalid ? rr : 0;
+        dma_block<kS>(tile, kRowBytes * rv + 2 * kDc + 16 * ((lane & 7) ^ rkey(rr)),
+                      slot + kH16Tok * kPitch + 1024 * q);
+      }
+    };
+    if (stream) copies(std::true_type{});
+    else copies(std::false_type{});
     return nvalid;
   };
 

@@ -34,6 +34,10 @@ __device__ __forceinline__ void lds_barrier() {
 // outstanding copy before each LDS read it cannot prove disjoint); completion
 // is ordered explicitly with wait_vmcnt + lds_barrier.  The block writes no
 // VGPR; M0 (the LDS base) is saved and restored and gets one wait state.
+// kStream marks the read non-temporal: for bytes read once (the latent cache
+// streamed by a decode attention), so they do not displace data that later
+// reads reuse.
+template <bool kStream = false>
 __device__ __forceinline__ void dma_block(uint64_t gbase, uint32_t voff, uint32_t lds) {
   // both bases are wave-uniform by construction; make that explicit for the SGPR
   // operands (readfirstlane yields int: widen through uint32_t, never sign-extend)
@@ -46,15 +50,26 @@ __device__ __forceinline__ void dma_block(uint64_t gbase, uint32_t voff, uint32_
   uint32_t save;
   // s_nop 4: five wait states between any VALU write of the base SGPRs and the
   // vector-memory read of them (a hazard the compiler does not see inside asm)
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 4\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(save)
-      : "v"(voff), "s"(gbase), "s"(lds)
-      : "memory");
+  if constexpr (kStream)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 4\n\t"
+        "global_load_lds_dwordx4 %1, %2 nt\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "v"(voff), "s"(gbase), "s"(lds)
+        : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 4\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "v"(voff), "s"(gbase), "s"(lds)
+        : "memory");
 }
 
 }  // namespace mla

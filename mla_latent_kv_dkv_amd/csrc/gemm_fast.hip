@@ -1265,21 +1265,28 @@ struct XsPlan {
 };
 
 // K slices d: the fewest whole groups of 32 kXsRing k (a strip's steps fill
-// whole ring turns) whose X slice fits kXsLdsBytes.  The plan depends on M and
-// K only, so the fused query projection + latent append takes the same slices,
-// and produces the same queries bit for bit, as the query projection alone.
-// (At 64 rows: 5 slices of 1024 for K = 5120, where the 1572 strips of the fused
-// call come to 7.7 per wave against a busiest wave's 8, and 16 slices for
-// K = 16384.)
+// whole ring turns) whose X slice fits kXsLdsBytes and whose (strip, slice)
+// pairs give at least 3/4 of the grid's waves a strip to stream.  A narrow
+// weight (the 16-head shape: 192 query strips, 128 output strips) would
+// otherwise leave most waves idle and the few busy ones latency bound, one
+// long strip each.  The plan depends on M, K, the query (or output) columns
+// and the chip only, so the fused query projection + latent append takes the
+// same slices, and produces the same queries bit for bit, as the query
+// projection alone.  (At 64 rows: 5 slices of 1024 for K = 5120, where the 1572
+// strips of the fused call come to 7.7 per wave against a busiest wave's 8, and
+// 16 slices for K = 16384; at 32 rows and K = 2048: 4 slices for 192 query
+// strips, 8 for the 128 strips of W_O.)
 XsPlan xs_plan(const GemmArgs& a) {
   XsPlan p{};
   p.mb = a.M <= 16 ? 1 : a.M <= 32 ? 2 : 4;
   constexpr int kUnit = 32 * kXsRing;
   const int kw_max = kXsLdsBytes / (2 * 16 * p.mb) / kUnit * kUnit;
   const int groups = a.K / kUnit;
+  const int64_t strips = (a.epi == EPI_QPROJ_APPEND ? a.n_append : a.N) / 16;
+  const int64_t waves = static_cast<int64_t>(cu_count()) * kXsWaves;
   p.d = groups;
   for (int d = 1; d <= groups; ++d)
-    if (groups % d == 0 && a.K / d <= kw_max) {
+    if (groups % d == 0 && a.K / d <= kw_max && 4 * strips * d >= 3 * waves) {
       p.d = d;
       break;
     }
@@ -1488,8 +1495,16 @@ hipError_t launch_gemm_fast(const GemmArgs& a, void* partial, size_t partial_byt
     }
     if (!uk_ok(a)) return hipErrorInvalidValue;
     if (uk_wide_ok(a)) {
-      dim3 grid(a.batch, a.N / kUwN, (a.M + kUwM - 1) / kUwM);
-      hipLaunchKernelGGL(k_gemm_uk_wide<kUwN>, grid, dim3(256), 0, stream, a);
+      // grids of fewer than 256 workgroups (16 heads) take 128-column tiles: twice
+      // the workgroups for the same products in the same order (bit-identical q_lat)
+      const int tiles_m = (a.M + kUwM - 1) / kUwM;
+      if (static_cast<int64_t>(a.batch) * (a.N / kUwN) * tiles_m < 256) {
+        dim3 grid(a.batch, a.N / (kUwN / 2), tiles_m);
+        hipLaunchKernelGGL(k_gemm_uk_wide<kUwN / 2>, grid, dim3(256), 0, stream, a);
+      } else {
+        dim3 grid(a.batch, a.N / kUwN, tiles_m);
+        hipLaunchKernelGGL(k_gemm_uk_wide<kUwN>, grid, dim3(256), 0, stream, a);
+      }
       return hipGetLastError();
     }
     dim3 grid(a.batch, a.N / kUkN, (a.M + kTile - 1) / kTile);

@@ -1264,32 +1264,46 @@ struct XsPlan {
   int mb, d, kw;
 };
 
-// K slices d: the fewest whole groups of 32 kXsRing k (a strip's steps fill
-// whole ring turns) whose X slice fits kXsLdsBytes and whose (strip, slice)
-// pairs give at least 3/4 of the grid's waves a strip to stream.  A narrow
-// weight (the 16-head shape: 192 query strips, 128 output strips) would
-// otherwise leave most waves idle and the few busy ones latency bound, one
-// long strip each.  The plan depends on M, K, the query (or output) columns
-// and the chip only, so the fused query projection + latent append takes the
-// same slices, and produces the same queries bit for bit, as the query
-// projection alone.  (At 64 rows: 5 slices of 1024 for K = 5120, where the 1572
-// strips of the fused call come to 7.7 per wave against a busiest wave's 8, and
-// 16 slices for K = 16384; at 32 rows and K = 2048: 4 slices for 192 query
-// strips, 8 for the 128 strips of W_O.)
+// K slices d.  A slice is a whole number of ring turns (32 kXsRing k) whose X
+// slice fits kXsLdsBytes; among those, d minimises a cost in weight-step units
+// (one step: 1 KB per wave, ≈0.2 µs of the whole chip's stream): the busiest
+// wave's (strip, slice) pairs times their steps plus the MB KB partial tile each
+// writes, and for d > 1 the finish pass (≈12 steps of launch, plus reading every
+// partial tile at the chip's rate).  The grid has cu_count() / d workgroups per
+// slice.  A narrow weight (16 heads: 228 strips of the fused query product) gets
+// slices that give its idle waves strips; a few rows (M <= 16) get more slices,
+// whose partial tiles are small, to even out the busiest wave (the 4-row query
+// projection: 8 against 3.07 strips per wave, 5 slices instead of 2).  The plan
+// depends on M, K, the planned columns and the chip only, so the fused query
+// projection + latent append takes the same slices, and produces the same
+// queries bit for bit, as the query projection alone.  (At 64 rows: 5 slices of
+// 1024 for K = 5120, where the 1572 strips of the fused call come to 7.7 per
+// wave against a busiest wave's 8, and 16 slices for K = 16384.)
 XsPlan xs_plan(const GemmArgs& a) {
   XsPlan p{};
   p.mb = a.M <= 16 ? 1 : a.M <= 32 ? 2 : 4;
   constexpr int kUnit = 32 * kXsRing;
+  constexpr int64_t kFinishSteps = 12;
   const int kw_max = kXsLdsBytes / (2 * 16 * p.mb) / kUnit * kUnit;
   const int groups = a.K / kUnit;
-  const int64_t strips = (a.epi == EPI_QPROJ_APPEND ? a.n_append : a.N) / 16;
-  const int64_t waves = static_cast<int64_t>(cu_count()) * kXsWaves;
+  const int64_t strips = (a.plan_cols > 0 ? a.plan_cols : a.N) / 16;
+  const int cus = cu_count();
+  const int64_t waves = static_cast<int64_t>(cus) * kXsWaves;
+  int64_t best = -1;
   p.d = groups;
-  for (int d = 1; d <= groups; ++d)
-    if (groups % d == 0 && a.K / d <= kw_max && 4 * strips * d >= 3 * waves) {
+  for (int d = 1; d <= groups; ++d) {
+    if (groups % d != 0 || a.K / d > kw_max) continue;
+    const int64_t nw = static_cast<int64_t>(std::max(1, cus / d)) * kXsWaves;
+    const int64_t busiest = (strips + nw - 1) / nw;
+    const int64_t steps = a.K / d / 32;
+    const int64_t cost =
+        d == 1 ? busiest * steps
+               : busiest * (steps + p.mb) + kFinishSteps + d * strips * p.mb / waves;
+    if (best < 0 || cost < best) {
+      best = cost;
       p.d = d;
-      break;
     }
+  }
   p.kw = a.K / p.d;
   return p;
 }

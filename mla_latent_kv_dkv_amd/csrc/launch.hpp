@@ -54,6 +54,10 @@ struct GemmArgs {
   // they stay fp32 and unrotated, row m at y3 + m * ld3 (the rows an FP8 pool's
   // quantizer rotates, scales and scatters)
   int64_t ld3;
+  // columns the weight stream's K-slice plan counts (0: N).  The query projection
+  // counts the latent-append columns as well, so that it takes the slices of the
+  // fused query/append product and gives the same queries bit for bit.
+  int plan_cols;
 };
 
 hipError_t launch_gemm_generic(const GemmArgs& a, bool bf16, hipStream_t stream);

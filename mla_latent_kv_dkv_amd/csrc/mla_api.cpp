@@ -125,6 +125,7 @@ mla::GemmArgs qproj_args(const mla_dims* d, int batch) {
   a.epi = mla::EPI_QPROJ; a.x_f32 = !bf16; a.y_f32 = 1;
   a.ldy = nhdh; a.d_rope = d->d_rope;
   a.rope = rope_spec(d);
+  a.plan_cols = a.N + d->d_latent + d->d_rope;   // the fused product's columns
   return a;
 }
 

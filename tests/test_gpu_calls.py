@@ -422,13 +422,17 @@ def test_absorb_out_large_batch(name):
 
 
 # ------------------------------------------------- fused absorb_q + append --
-@pytest.mark.parametrize("name,B", [("tiny", 5), ("full", 5), ("full", 64)])
-def test_absorb_q_append(name, B):
+# K slices of the fused product: lite 4 (B = 32 and B = 5), full 5 (B = 64, and
+# B = 5 with one-block partial tiles), lite with a 512-wide hidden state 1 (the
+# output stage straight from the product); tiny (fp32) takes the two calls
+@pytest.mark.parametrize("name,B,hidden", [("tiny", 5, 0), ("lite", 5, 0), ("lite", 32, 0),
+                                           ("lite", 32, 512), ("full", 5, 0), ("full", 64, 0)])
+def test_absorb_q_append(name, B, hidden):
     """The fused call against the oracle (queries and appended rows), its queries
     equal to mla_absorb_q's, the pool untouched outside the appended slots (the
     f32 shape exercises the fallback to the two calls)."""
-    w = _wl(name, batch=B)
-    note(f"absorb_q_append {name} B={B}")
+    w = _wl(name, batch=B, **({"hidden": hidden} if hidden else {}))
+    note(f"absorb_q_append {name} B={B} hidden={w.hidden}")
     lens = np.array([3 + 37 * b for b in range(B)], dtype=np.int32)   # token b at lens[b] - 1
     bt, total = I.page_table(w, lens)
     seqs = np.arange(B, dtype=np.int32)

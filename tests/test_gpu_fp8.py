@@ -258,16 +258,18 @@ def _check_appended(w, got, bt, total, seqs, poss, ref_rows, rows):
 
 # full-fp8 B = 5: the K-split product and its finish pass; B = 64: the largest batch of
 # the fused product; B = 65 and tiny-fp8 (fp32): the two separate calls; lite-fp8
-# B = 32: one K slice (rows straight from the product's epilogue)
-@pytest.mark.parametrize("name,B", [("full-fp8", 5), ("full-fp8", 64), ("full-fp8", 65),
-                                    ("lite-fp8", 32), ("tiny-fp8", 5)])
-def test_absorb_q_append_fp8(name, B):
+# B = 32: 4 K slices; lite-fp8 with a 512-wide hidden state: one K slice (rows
+# straight from the product's epilogue)
+@pytest.mark.parametrize("name,B,hidden", [("full-fp8", 5, 0), ("full-fp8", 64, 0),
+                                           ("full-fp8", 65, 0), ("lite-fp8", 32, 0),
+                                           ("lite-fp8", 32, 512), ("tiny-fp8", 5, 0)])
+def test_absorb_q_append_fp8(name, B, hidden):
     """The fused query + FP8 append: queries equal to mla_absorb_q's bit for bit and
     at the oracle's bar; each appended row quantized as the oracle quantizes its
     fp64 row (scale equal, codes equal up to a tie within fp32 rounding, k^R
     within bf16 rounding); the rest of the pool untouched."""
-    w = _wl(name, batch=B)
-    note(f"absorb_q_append_fp8 {name} B={B}")
+    w = _wl(name, batch=B, **({"hidden": hidden} if hidden else {}))
+    note(f"absorb_q_append_fp8 {name} B={B} hidden={w.hidden}")
     lens = np.array([3 + 37 * b for b in range(B)], dtype=np.int32)   # token b at lens[b] - 1
     bt, total = I.page_table(w, lens)
     seqs = np.arange(B, dtype=np.int32)

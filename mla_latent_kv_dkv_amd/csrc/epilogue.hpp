@@ -31,19 +31,28 @@ __device__ __forceinline__ void rope_row(const GemmArgs& a, int m, int pos, int 
   }
 }
 
-// Latent-append columns (n even) of row m: [c | RoPE(k^R, row_pos[m])] into
-// the pool slot of (row_seq[m], row_pos[m]); pool, c/k^R split given.
-template <typename T>
-__device__ __forceinline__ void append_pair(const GemmArgs& a, void* pool, int split, int m, int n,
-                                            float v0, float v1) {
+// Element offset of the pool row that appended row m goes to, the slot of
+// (row_seq[m], row_pos[m]), or -1 when its sequence, position or page is out of
+// range (flagged in the error word when `flag`).
+__device__ __forceinline__ int64_t append_row_offset(const GemmArgs& a, int m, bool flag) {
   const int seq = a.row_seq[m];
   const int pos = a.pos[m];
-  if (seq < 0 || seq >= a.n_seqs) { if (n == 0) set_err(a.err, ERR_SEQ); return; }
-  if (pos < 0 || pos >= a.max_pages * a.page_size) { if (n == 0) set_err(a.err, ERR_POS); return; }
+  if (seq < 0 || seq >= a.n_seqs) { if (flag) set_err(a.err, ERR_SEQ); return -1; }
+  if (pos < 0 || pos >= a.max_pages * a.page_size) { if (flag) set_err(a.err, ERR_POS); return -1; }
   const int page = a.block_table[static_cast<int64_t>(seq) * a.max_pages + pos / a.page_size];
-  if (page < 0 || page >= a.num_pages) { if (n == 0) set_err(a.err, ERR_PAGE); return; }
-  T* row = static_cast<T*>(pool) +
-           (static_cast<int64_t>(page) * a.page_size + pos % a.page_size) * a.row_width;
+  if (page < 0 || page >= a.num_pages) { if (flag) set_err(a.err, ERR_PAGE); return -1; }
+  return (static_cast<int64_t>(page) * a.page_size + pos % a.page_size) * a.row_width;
+}
+
+// Latent-append columns n, n+1 (n even) of row m, at position pos, into the pool
+// row at element offset `off` (nothing when off < 0): [c | RoPE(k^R, pos)];
+// pool, c/k^R split given.
+template <typename T>
+__device__ __forceinline__ void append_pair_at(const GemmArgs& a, void* pool, int split,
+                                               int64_t off, int m, int pos, int n, float v0,
+                                               float v1) {
+  if (off < 0) return;
+  T* row = static_cast<T*>(pool) + off;
   if (n < split) {
     st(row + n, v0);
     st(row + n + 1, v1);
@@ -54,6 +63,15 @@ __device__ __forceinline__ void append_pair(const GemmArgs& a, void* pool, int s
     st(row + n, v0 * c - v1 * s);
     st(row + n + 1, v0 * s + v1 * c);
   }
+}
+
+// Latent-append columns (n even) of row m: [c | RoPE(k^R, row_pos[m])] into
+// the pool slot of (row_seq[m], row_pos[m]); pool, c/k^R split given.
+template <typename T>
+__device__ __forceinline__ void append_pair(const GemmArgs& a, void* pool, int split, int m, int n,
+                                            float v0, float v1) {
+  const int64_t off = append_row_offset(a, m, n == 0);
+  if (off >= 0) append_pair_at<T>(a, pool, split, off, m, a.pos[m], n, v0, v1);
 }
 
 template <typename T>

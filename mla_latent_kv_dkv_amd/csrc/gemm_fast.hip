@@ -238,6 +238,13 @@ __device__ __forceinline__ void rope_table_fill(const GemmArgs& a, int e0, int s
   }
 }
 
+// The same table as a kernel of its own, ahead of a tiled product whose output
+// stage rotates (otherwise each of its RoPE tiles would evaluate the fp64 angles
+// of every (row, pair) it holds).
+__global__ __launch_bounds__(256) void k_rope_table(GemmArgs a) {
+  rope_table_fill(a, blockIdx.x * blockDim.x + threadIdx.x, gridDim.x * blockDim.x);
+}
+
 // ---- X-stationary weight stream (one K slice of X held in LDS per workgroup) ----
 // For one activation matrix (batch 1, M <= 64) the grid is one workgroup per CU;
 // workgroup w owns K slice w % d and keeps X[:, slice] in LDS for its whole
@@ -1096,13 +1103,18 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile_dma(GemmArgs a, int ksplit
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int z = blockIdx.z / ksplit, ks = blockIdx.z - z * ksplit;
   const int n0 = blockIdx.x * TN, m0 = blockIdx.y * TM;
+  // the grid's x is padded to a multiple of 8 (the two row tiles of a weight tile,
+  // blocks x and x + gridDim.x, then share an XCD and its L2): padding exits here
+  if (n0 >= a.N) return;
   const int kslice = a.K / ksplit;
   const int64_t kbeg = static_cast<int64_t>(ks) * kslice;
   const uint32_t lds0 = lds_addr(tiles);
   auto key = [](int r) { return (r >> 1) & 7; };
   // copy j of this wave: stage rows 8q .. 8q + 7 (q = wv + 4j); base of its first
   // row (uniform) and this lane's byte offset (row 8q + (lane >> 3), source chunk
-  // (lane & 7) ^ key(row)); rows past N or M re-read the last row (never stored)
+  // (lane & 7) ^ key(row)); rows past N or M re-read the last row (never stored).
+  // With the fused latent append, weight rows from n_append on come from w3 / w4
+  // (an 8-row group never straddles them: n_append and n_split3 are multiples of 8)
   uint64_t gb[kPerWave];
   uint32_t vo[kPerWave];
 #pragma unroll
@@ -1110,10 +1122,17 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile_dma(GemmArgs a, int ksplit
     const int q = wv + 4 * j, row = 8 * q + (lane >> 3), ch = (lane & 7) ^ key(row);
     if (8 * q < TN) {
       const int nb = min(n0 + 8 * q, a.N - 1), nr = min(n0 + row, a.N - 1);
-      const bf16_t* w = nb < a.n_split
-                            ? static_cast<const bf16_t*>(a.w1) + static_cast<int64_t>(nb) * a.ldw_n
-                            : static_cast<const bf16_t*>(a.w2) +
-                                  static_cast<int64_t>(nb - a.n_split) * a.ldw_n;
+      const bf16_t* w;
+      if (a.epi == EPI_QPROJ_APPEND && nb >= a.n_append) {   // the fused latent append's rows
+        const int r = nb - a.n_append;
+        w = r < a.n_split3
+                ? static_cast<const bf16_t*>(a.w3) + static_cast<int64_t>(r) * a.ldw_n
+                : static_cast<const bf16_t*>(a.w4) + static_cast<int64_t>(r - a.n_split3) * a.ldw_n;
+      } else {
+        w = nb < a.n_split
+                ? static_cast<const bf16_t*>(a.w1) + static_cast<int64_t>(nb) * a.ldw_n
+                : static_cast<const bf16_t*>(a.w2) + static_cast<int64_t>(nb - a.n_split) * a.ldw_n;
+      }
       gb[j] = reinterpret_cast<uint64_t>(w + static_cast<int64_t>(z) * a.w_bs + kbeg);
       vo[j] = static_cast<uint32_t>(((nr - nb) * a.ldw_n + 8 * ch) * 2);
     } else {
@@ -1183,6 +1202,17 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile_dma(GemmArgs a, int ksplit
         *reinterpret_cast<float2*>(&ot[(32 * BM * wm + 32 * j + r32) * kOPitch + 32 * BN * wn + 32 * i +
                                        8 * (e >> 2) + 4 * h + (e & 3)]) =
             make_float2(acc[i][j][e], acc[i][j][e + 1]);
+  // fused latent append into the pool: each output row's pool row and position,
+  // looked up once per row instead of once per column pair
+  __shared__ int64_t app_off[TM];
+  __shared__ int app_pos[TM];
+  const bool app = a.epi == EPI_QPROJ_APPEND && a.ld3 == 0 && n0 + TN > a.n_append;
+  if (app)
+    for (int r = tid; r < TM; r += 256) {
+      const bool in = m0 + r < a.M;
+      app_off[r] = in ? append_row_offset(a, m0 + r, n0 <= a.n_append) : -1;
+      app_pos[r] = in ? a.pos[m0 + r] : 0;
+    }
   __syncthreads();
   for (int q = tid; q < TM * TN / 2; q += 256) {   // pair q: row q / (TN/2), columns 2 (q % (TN/2)), +1
     const int ml = q / (TN / 2), nl = 2 * (q % (TN / 2));
@@ -1192,6 +1222,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile_dma(GemmArgs a, int ksplit
       if (ksplit > 1)
         *reinterpret_cast<float2*>(partial + ((static_cast<int64_t>(ks) * a.batch + z) * a.M + m) *
                                                  a.N + n) = v;
+      else if (app && n >= a.n_append)
+        append_pair_at<bf16_t>(a, a.y3, a.n_split3, app_off[ml], m, app_pos[ml], n - a.n_append,
+                               v.x, v.y);
       else
         gemm_epilogue<bf16_t>(a, z, m, n, v.x, v.y);
     }
@@ -1410,17 +1443,33 @@ static bool xs_ok(const GemmArgs& a) {
          (static_cast<int64_t>(a.M) * a.ldx_m + a.K) * 4 < (int64_t{1} << 31);
 }
 
-// The fused query projection + latent append runs only on k_gemm_xs.
-bool fused_qa_ok(const GemmArgs& a) { return a.epi == EPI_QPROJ_APPEND && xs_ok(a); }
-
 // Prefill-sized activations (M >= 256): the tiled product.  Same operand forms as
 // k_gemm_ws; K a multiple of the 64-wide chunk.
 static bool tile_ok(const GemmArgs& a) {
   const int64_t groups = static_cast<int64_t>((a.N + kTt - 1) / kTt) * ((a.M + kTt - 1) / kTt) * a.batch;
+  // the fused query projection + latent append runs on the copy-staged form only
+  // (bf16 X, the query split on a tile boundary), whose weight copies know w3 / w4
+  if (a.epi == EPI_QPROJ_APPEND) {
+    if (!(!a.x_f32 && a.batch == 1 && a.n_split % kTt == 0 && a.n_split < a.n_append &&
+          a.n_append % 8 == 0 && a.n_split3 % 8 == 0 && aligned16(a.w3) && aligned16(a.w4)))
+      return false;
+    // ... and only where the appended rows' tiles fit the rounds of workgroups (two
+    // per CU) that the query tiles take anyway: at M = 1024 the 1536 query tiles fill
+    // three rounds exactly, and 40 more would add a fourth (the two calls are faster)
+    const int64_t slots = 2 * static_cast<int64_t>(cu_count());
+    const int64_t mt = (a.M + kTt - 1) / kTt;
+    const int64_t tq = (a.n_append + kTt - 1) / kTt * mt, tf = (a.N + kTt - 1) / kTt * mt;
+    if ((tf + slots - 1) / slots > (tq + slots - 1) / slots) return false;
+  }
   // grids of fewer than 256 output tiles (narrow outputs such as the latent append)
   // would leave most of the chip idle: those stay with the K-split weight stream
-  return ws_ok(a) && a.epi != EPI_QPROJ_APPEND && a.M >= 256 && a.K % kTk == 0 &&
-         a.n_split % 2 == 0 && groups >= 256;
+  return ws_ok(a) && a.M >= 256 && a.K % kTk == 0 && a.n_split % 2 == 0 && groups >= 256;
+}
+
+// The fused query projection + latent append runs on k_gemm_xs (decode batches)
+// and on the copy-staged tiled product (M >= 256).
+bool fused_qa_ok(const GemmArgs& a) {
+  return a.epi == EPI_QPROJ_APPEND && (xs_ok(a) || tile_ok(a));
 }
 
 // Per-head batched products at decode sizes (M <= 64, N a multiple of 64): one
@@ -1486,7 +1535,8 @@ hipError_t launch_uv_merge(const GemmArgs& a, const MergeArgs& m, hipStream_t st
 }
 
 size_t gemm_partial_bytes(const GemmArgs& a) {
-  if (!ws_ok(a) || tile_ok(a) || uv_wide_ok(a) || small_tile_ok(a)) return 0;
+  if (ws_ok(a) && tile_ok(a)) return xs_rope_bytes(a);   // the RoPE table of a rotating output
+  if (!ws_ok(a) || uv_wide_ok(a) || small_tile_ok(a)) return 0;
   if (const int d = tile_split_d(a))
     return static_cast<size_t>(d) * a.batch * a.M * a.N * sizeof(float);
   if (xs_ok(a)) {
@@ -1500,7 +1550,7 @@ size_t gemm_partial_bytes(const GemmArgs& a) {
 hipError_t launch_gemm_fast(const GemmArgs& a, void* partial, size_t partial_bytes,
                             hipStream_t stream) {
   if (a.M == 0 || a.N == 0 || a.batch == 0) return hipSuccess;
-  if (a.epi == EPI_QPROJ_APPEND && !xs_ok(a)) return hipErrorInvalidValue;
+  if (a.epi == EPI_QPROJ_APPEND && !fused_qa_ok(a)) return hipErrorInvalidValue;
   if (!ws_ok(a)) {
     if (uv_wide_ok(a)) {   // small batches, whose K granule the weight stream does not take
       const dim3 grid(a.batch * (a.N / kUvN), (a.M + kUvM - 1) / kUvM);
@@ -1529,13 +1579,25 @@ hipError_t launch_gemm_fast(const GemmArgs& a, void* partial, size_t partial_byt
     return hipGetLastError();
   }
   if (tile_ok(a)) {
+    // a rotating output stage reads its cos/sin from a table made first (in the
+    // partial region), once per (row, pair) of the call
+    GemmArgs b = a;
+    if (epi_rotates(a)) {
+      if (partial == nullptr || !aligned16(partial) || partial_bytes < xs_rope_bytes(a))
+        return hipErrorInvalidValue;
+      b.rope_tab = static_cast<float*>(partial);
+      const int entries = a.M * (a.d_rope / 2);
+      hipLaunchKernelGGL(k_rope_table, dim3((entries + 255) / 256), dim3(256), 0, stream, b);
+      if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    }
     const dim3 grid((a.N + kTt - 1) / kTt, (a.M + kTt - 1) / kTt, a.batch);
     if (a.x_f32)
-      hipLaunchKernelGGL((k_gemm_tile<float, kTt, kTt>), grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((k_gemm_tile<float, kTt, kTt>), grid, dim3(256), 0, stream, b);
     else if (a.n_split % kTt == 0 || a.n_split >= a.N)
-      hipLaunchKernelGGL((k_gemm_tile_dma<kTt, kTt>), grid, dim3(256), 0, stream, a, 1, nullptr);
+      hipLaunchKernelGGL((k_gemm_tile_dma<kTt, kTt>), dim3((grid.x + 7) / 8 * 8, grid.y, grid.z),
+                         dim3(256), 0, stream, b, 1, nullptr);
     else
-      hipLaunchKernelGGL((k_gemm_tile<bf16_t, kTt, kTt>), grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((k_gemm_tile<bf16_t, kTt, kTt>), grid, dim3(256), 0, stream, b);
     return hipGetLastError();
   }
   if (uv_wide_ok(a)) {
@@ -1546,7 +1608,7 @@ hipError_t launch_gemm_fast(const GemmArgs& a, void* partial, size_t partial_byt
   if (const int d = tile_split_d(a)) {
     if (partial == nullptr || !aligned16(partial) || partial_bytes < gemm_partial_bytes(a))
       return hipErrorInvalidValue;
-    const dim3 grid((a.N + kTt - 1) / kTt, (a.M + kTt - 1) / kTt, a.batch * d);
+    const dim3 grid(((a.N + kTt - 1) / kTt + 7) / 8 * 8, (a.M + kTt - 1) / kTt, a.batch * d);
     hipLaunchKernelGGL((k_gemm_tile_dma<kTt, kTt>), grid, dim3(256), 0, stream, a, d,
                        static_cast<float*>(partial));
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;

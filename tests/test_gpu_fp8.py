@@ -257,12 +257,13 @@ def _check_appended(w, got, bt, total, seqs, poss, ref_rows, rows):
 
 
 # full-fp8 B = 5: the K-split product and its finish pass; B = 64: the largest batch of
-# the fused product; B = 65 and tiny-fp8 (fp32): the two separate calls; lite-fp8
-# B = 32: 4 K slices; lite-fp8 with a 512-wide hidden state: one K slice (rows
-# straight from the product's epilogue)
+# the fused weight stream; B = 65 and tiny-fp8 (fp32): the two separate calls;
+# B = 256: the fused tiled product; lite-fp8 B = 32: 4 K slices; lite-fp8 with a
+# 512-wide hidden state: one K slice (rows straight from the product's epilogue)
 @pytest.mark.parametrize("name,B,hidden", [("full-fp8", 5, 0), ("full-fp8", 64, 0),
-                                           ("full-fp8", 65, 0), ("lite-fp8", 32, 0),
-                                           ("lite-fp8", 32, 512), ("tiny-fp8", 5, 0)])
+                                           ("full-fp8", 65, 0), ("full-fp8", 256, 0),
+                                           ("lite-fp8", 32, 0), ("lite-fp8", 32, 512),
+                                           ("tiny-fp8", 5, 0)])
 def test_absorb_q_append_fp8(name, B, hidden):
     """The fused query + FP8 append: queries equal to mla_absorb_q's bit for bit and
     at the oracle's bar; each appended row quantized as the oracle quantizes its
@@ -270,31 +271,37 @@ def test_absorb_q_append_fp8(name, B, hidden):
     within bf16 rounding); the rest of the pool untouched."""
     w = _wl(name, batch=B, **({"hidden": hidden} if hidden else {}))
     note(f"absorb_q_append_fp8 {name} B={B} hidden={w.hidden}")
-    lens = np.array([3 + 37 * b for b in range(B)], dtype=np.int32)   # token b at lens[b] - 1
+    # token b at lens[b] - 1; the 256-row batch stays under 300 tokens (a small pool)
+    lens = np.array([3 + 37 * b if B <= 64 else 1 + (37 * b) % 300 for b in range(B)],
+                    dtype=np.int32)
     bt, total = I.page_table(w, lens)
     seqs = np.arange(B, dtype=np.int32)
     poss = (lens - 1).astype(np.int32)
     M.mla_device_error(clear=True)
     got, q, q2, hh, hw = _fused_fp8_case(w, B, lens, seqs, poss, bt, total)
     assert torch.equal(q[0], q2[0]) and torch.equal(q[1], q2[1]), "queries differ from mla_absorb_q"
+    # every row bit for bit against mla_absorb_q; every 8th (and the last) of a
+    # 256-row batch against the fp64 oracle
+    rows = list(range(B)) if B <= 64 else sorted(set(range(0, B, 8)) | {B - 1})
     rl, rp = zip(*[O.absorb_q(hh[b], hw["w_q"], hw["w_qr"], hw["w_uk"], int(poss[b]), w.n_heads,
-                              w.d_head, w.d_latent, w.d_rope, w.rope_base) for b in range(B)])
-    assert_parity(to_np(q[0]), np.stack(rl), w.dtype, "q_lat")
-    assert_parity(to_np(q[1]), np.stack(rp), w.dtype, "q_pe")
+                              w.d_head, w.d_latent, w.d_rope, w.rope_base) for b in rows])
+    assert_parity(to_np(q[0])[rows], np.stack(rl), w.dtype, "q_lat")
+    assert_parity(to_np(q[1])[rows], np.stack(rp), w.dtype, "q_pe")
     ref_rows = O.latent_rows(hh, hw["w_dkv"], hw["w_kr"], poss, w.rope_base)
     flips = _check_appended(w, got, bt, total, seqs, poss, ref_rows, range(B))
     note(f"  codes at a tie resolved the other way: {flips} of {B * w.d_latent}")
     assert M.mla_device_error() == 0
 
 
-@pytest.mark.parametrize("B", [5, 64])
+@pytest.mark.parametrize("B", [5, 64, 256])
 def test_absorb_q_append_fp8_out_of_range_rows(B):
     """A row whose table entry is outside the pool and one whose sequence is
     outside the table: neither is written, the error word names both, and the
-    queries are still mla_absorb_q's."""
+    queries are still mla_absorb_q's (B = 256: the fused tiled product)."""
     w = _wl("full-fp8", batch=B)
     note(f"absorb_q_append_fp8 out-of-range rows B={B}")
-    lens = np.array([3 + 37 * b for b in range(B)], dtype=np.int32)
+    lens = np.array([3 + 37 * b if B <= 64 else 1 + (37 * b) % 300 for b in range(B)],
+                    dtype=np.int32)
     bt, total = I.page_table(w, lens)
     seqs = np.arange(B, dtype=np.int32)
     poss = (lens - 1).astype(np.int32)

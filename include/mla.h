@@ -178,9 +178,11 @@ mla_status mla_decode_attention(const mla_dims* dims, const float* q_lat, const 
  * Length-proportional work list for the decode attention of a ragged batch
  * ([Report] §2.3: the work of one head group is a pass over its sequence's
  * cached rows, so equal work means equal token counts).  Host function: from
- * seq_lens [batch] (host memory), unit length
- *   U = page_size * ceil(ceil(sum_b L_b / target_units) / page_size),
- * sequence b gets n_b = max(1, ceil(L_b / U)) units, the page-aligned chunks of
+ * seq_lens [batch] (host memory), the unit length U is the smallest multiple of
+ * page_size for which sum_b max(1, ceil(L_b / U)) <= target_units (the longest
+ * length rounded up to a page when batch alone exceeds target_units), so a
+ * target of k times the device's compute units gives at most k rounds of work
+ * units; sequence b gets n_b = max(1, ceil(L_b / U)) units, the page-aligned chunks of
  * mla_decode_attention's split rule with S = n_b (trailing empty chunks dropped;
  * an empty sequence keeps one empty unit).  Writes to plan (host memory, at
  * least mla_decode_plan_capacity(batch, target_units) entries):

@@ -788,14 +788,24 @@ int32_t mla_decode_plan(const int32_t* seq_lens, int32_t batch, int32_t page_siz
       target_units > (1 << 20))
     return MLA_ERR_SHAPE;
   if (capacity < mla_decode_plan_capacity(batch, target_units)) return MLA_ERR_WORKSPACE;
-  int64_t total = 0;
-  for (int b = 0; b < batch; ++b) {
+  for (int b = 0; b < batch; ++b)
     if (seq_lens[b] < 0) return MLA_ERR_SHAPE;
-    total += seq_lens[b];
+  // unit length: the fewest whole pages whose unit count stays within the target
+  // (the count falls as the length grows, so a bisection over pages finds it); one
+  // unit per sequence when even that is over the target
+  int64_t max_len = 0;
+  for (int b = 0; b < batch; ++b) max_len = std::max<int64_t>(max_len, seq_lens[b]);
+  auto count = [&](int64_t u) {
+    int64_t c = 0;
+    for (int b = 0; b < batch; ++b) c += std::max<int64_t>(1, (seq_lens[b] + u - 1) / u);
+    return c;
+  };
+  int64_t lo = 1, hi = std::max<int64_t>(1, (max_len + page_size - 1) / page_size);   // pages
+  while (lo < hi) {
+    const int64_t mid = lo + (hi - lo) / 2;
+    if (count(mid * page_size) <= target_units) hi = mid; else lo = mid + 1;
   }
-  // unit length: the tokens of one target unit, in whole pages
-  int64_t unit = (total + target_units - 1) / target_units;
-  unit = std::max<int64_t>(page_size, (unit + page_size - 1) / page_size * page_size);
+  const int64_t unit = lo * page_size;
   int32_t* units = plan;
   std::vector<int32_t> start(batch + 1);
   int64_t n = 0;

@@ -172,7 +172,7 @@ class Workload:
                                     # are the step's prompt tokens (0: decode, one token)
     yarn: tuple = ()                # YaRN-stretched RoPE: (scale, orig_len, alpha, beta)
     plan_units: int = 0             # decode attention over a length-proportional plan of
-                                    # about this many units (0: num_splits uniform splits)
+                                    # at most this many units (0: num_splits uniform splits)
     notes: str = field(default="", compare=False)
 
     @property
@@ -212,8 +212,9 @@ WORKLOADS = {
                      cache_from_h=True),
     "full": Workload("full", 5120, 128, 128, 512, 64, "bf16", 64, 4096, 1003, num_splits=4),
     "long": Workload("long", 5120, 128, 128, 512, 64, "bf16", 4, 131072, 1004, num_splits=64),
+    # ragged: a plan of at most 768 units, three rounds of work units over the 256 CUs
     "ragged": Workload("ragged", 5120, 128, 128, 512, 64, "bf16", 256, 0, 1005, num_splits=16,
-                       layers=60, ragged=(512, 32768), plan_units=1024),
+                       layers=60, ragged=(512, 32768), plan_units=768),
     # the same shapes with the query's low-rank compression (d_c' = 1536 at full size)
     "tiny-cq": Workload("tiny-cq", 64, 4, 16, 32, 8, "f32", 1, 64, 1006, num_splits=1,
                         permute_pages=False, cache_from_h=True, d_cq=24),

@@ -703,6 +703,131 @@ __global__ __launch_bounds__(256, 2) void k_gemm_uk_wide(GemmArgs a) {
 
 constexpr int kUwN = 256;   // columns per workgroup of the fp32-X W_UK product
 
+// ---- the same product for batches of several 64-row tiles ----------------------
+// Workgroup = (head, NW columns c) for all the rows: the W tile is copied to LDS
+// once and stays; the fp32 X tiles of the rows pass through two LDS buffers, the
+// next tile's copies in flight during the current tile's products, and each lane
+// stores its outputs straight from the accumulators (four columns, 16 bytes).  The
+// products are k_gemm_uk_wide's, in the same order (bit-identical q_lat); one
+// workgroup per (head, column tile) instead of one per row tile as well, so at 256
+// and 1024 rows the W tiles are read once and the grid is one round.
+template <int NW>
+__global__ __launch_bounds__(256, 1) void k_gemm_uk_rows(GemmArgs a) {
+  constexpr int kWRow = 2 * NW, kWBytes = kUkK * kWRow, kCT = NW / 128;
+  constexpr int kXBytes = kUwM * 512;               // one fp32 X tile: 64 rows x 128 d
+  constexpr int kXPerWave = kXBytes / 1024 / 4;     // copies of one X tile per wave
+  __shared__ __attribute__((aligned(1024))) char lds[kWBytes + 2 * kXBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int head = blockIdx.x, c0 = blockIdx.y * NW;
+  const uint32_t wl = lds_addr(lds), xl0 = wl + kWBytes;
+  const int tiles = (a.M + kUwM - 1) / kUwM;
+  const uint64_t xg = reinterpret_cast<uint64_t>(static_cast<const float*>(a.x) + head * a.x_bs);
+  // X tile t -> buffer t & 1: block j = rows 2j, 2j + 1 of the tile, row b at 512 b,
+  // 16-byte chunk q at q ^ (b & 15); rows past M repeat the last one (never stored)
+  auto issue_x = [&](int t) {
+    const uint32_t xl = xl0 + static_cast<uint32_t>(t & 1) * kXBytes;
+    for (int j = wv; j < kUwM / 2; j += 4) {
+      const int b = 2 * j + (lane >> 5), qs = lane & 31;
+      const int br = t * kUwM + b < a.M ? t * kUwM + b : a.M - 1;
+      const uint32_t voff =
+          static_cast<uint32_t>((static_cast<int64_t>(br) * a.ldx_m + 4 * (qs ^ (b & 15))) * 4);
+      dma_block(xg, voff, xl + 1024 * j);
+    }
+  };
+  {  // the W tile, once: block j = rows (1024 / kWRow) j .., chunk q at q ^ 4(d & 3)
+    const uint64_t wg = reinterpret_cast<uint64_t>(static_cast<const bf16_t*>(a.w1) +
+                                                   head * a.w_bs + c0);
+    for (int j = wv; j < kWBytes / 1024; j += 4) {
+      const int byte = 1024 * j + 16 * lane;
+      const int d = byte / kWRow, qs = (byte % kWRow) >> 4;
+      const uint32_t voff = static_cast<uint32_t>((static_cast<int64_t>(d) * a.ldw_k +
+                                                   8 * (qs ^ (4 * (d & 3)))) * 2);
+      dma_block(wg, voff, wl + 1024 * j);
+    }
+  }
+  issue_x(0);
+
+  const int i16 = lane & 15, G = lane >> 4, j32 = lane & 31, g = lane >> 5;
+  float* y = static_cast<float*>(a.y) + head * a.y_bs + c0;
+  for (int t = 0; t < tiles; ++t) {
+    if (t + 1 < tiles) {   // (buffer (t + 1) & 1 was freed by the barrier ending tile t - 1)
+      issue_x(t + 1);
+      wait_vmcnt<kXPerWave>();   // W and tile t have landed; tile t + 1 may fly
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();   // ... for every wave's copies
+    const uint32_t xl = xl0 + static_cast<uint32_t>(t & 1) * kXBytes;
+    f32x16_t acc[kCT][2];
+#pragma unroll
+    for (int ct = 0; ct < kCT; ++ct)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[ct][mt][e] = 0.f;
+#pragma unroll 2
+    for (int s = 0; s < kUkK / 16; ++s) {
+      bf16x8_t af[kCT];
+#pragma unroll
+      for (int ct = 0; ct < kCT; ++ct) {
+        const int col = 32 * (kCT * wv + ct) + 16 * (G & 1) + 4 * (i16 & 3);
+        const int d = 16 * s + 8 * (G >> 1) + (i16 >> 2);
+        const int q = col >> 3, h8 = 8 * ((col >> 2) & 1);
+        const s16x4_t v0 = lds_tr16_u(wl + kWRow * d + 16 * (q ^ (4 * (d & 3))) + h8);
+        const s16x4_t v1 = lds_tr16_u(wl + kWRow * (d + 4) + 16 * (q ^ (4 * ((d + 4) & 3))) + h8);
+        const s16x4_t vv[2] = {v0, v1};
+        af[ct] = __builtin_bit_cast(bf16x8_t, vv);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const int b = 32 * mt + j32;
+        const int q = 4 * s + 2 * g;
+        const u32x4_t x0 = lds_u128(xl + 512 * b + 16 * (q ^ (b & 15)));
+        const u32x4_t x1 = lds_u128(xl + 512 * b + 16 * ((q + 1) ^ (b & 15)));
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = __uint_as_float(x0[e]);
+          v[4 + e] = __uint_as_float(x1[e]);
+        }
+        const u32x4_t hi = {cvt2(v[0], v[1]), cvt2(v[2], v[3]), cvt2(v[4], v[5]), cvt2(v[6], v[7])};
+        float rl[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          rl[2 * e] = v[2 * e] - __uint_as_float(hi[e] << 16);
+          rl[2 * e + 1] = v[2 * e + 1] - __uint_as_float(hi[e] & 0xFFFF0000u);
+        }
+        const u32x4_t lo = {cvt2(rl[0], rl[1]), cvt2(rl[2], rl[3]), cvt2(rl[4], rl[5]),
+                            cvt2(rl[6], rl[7])};
+#pragma unroll
+        for (int ct = 0; ct < kCT; ++ct) {
+          acc[ct][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ct], __builtin_bit_cast(bf16x8_t, hi),
+                                                                acc[ct][mt], 0, 0, 0);
+          acc[ct][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ct], __builtin_bit_cast(bf16x8_t, lo),
+                                                                acc[ct][mt], 0, 0, 0);
+        }
+      }
+    }
+    // acc[ct][mt] lane (j32, g): columns 32(kCT wv + ct) + 8 e4 + 4g + (0..3), row 32mt + j32
+#pragma unroll
+    for (int ct = 0; ct < kCT; ++ct)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const int m = t * kUwM + 32 * mt + j32;
+        if (m < a.M) {
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4)
+            *reinterpret_cast<float4*>(y + static_cast<int64_t>(m) * a.ldy + 32 * (kCT * wv + ct) +
+                                       8 * e4 + 4 * g) =
+                make_float4(acc[ct][mt][4 * e4], acc[ct][mt][4 * e4 + 1], acc[ct][mt][4 * e4 + 2],
+                            acc[ct][mt][4 * e4 + 3]);
+        }
+      }
+    lds_barrier();   // every wave is done with buffer t & 1 before tile t + 2 goes there
+  }
+}
+
 // ---- per-head o[b, i, d] = sum_c X[b, i, c] W_UV[i*d_h + d, c], fp32 X ---------
 // (the absorbed output's first product: X = o_lat, K = d_c = 512, N = d_h.)
 // Workgroup = (head, 64 rows d of W, 64 rows b).  The W rows (64 KB) arrive by
@@ -1559,9 +1684,16 @@ hipError_t launch_gemm_fast(const GemmArgs& a, void* partial, size_t partial_byt
     }
     if (!uk_ok(a)) return hipErrorInvalidValue;
     if (uk_wide_ok(a)) {
+      const int tiles_m = (a.M + kUwM - 1) / kUwM;
+      // several row tiles and a grid of (head, 256 columns) that covers the chip:
+      // one workgroup per (head, column tile) walks the row tiles
+      if (tiles_m > 1 && static_cast<int64_t>(a.batch) * (a.N / kUwN) >= 256 &&
+          static_cast<int64_t>(a.M) * a.ldx_m * 4 < (int64_t{1} << 32)) {
+        hipLaunchKernelGGL(k_gemm_uk_rows<kUwN>, dim3(a.batch, a.N / kUwN), dim3(256), 0, stream, a);
+        return hipGetLastError();
+      }
       // grids of fewer than 256 workgroups (16 heads) take 128-column tiles: twice
       // the workgroups for the same products in the same order (bit-identical q_lat)
-      const int tiles_m = (a.M + kUwM - 1) / kUwM;
       if (static_cast<int64_t>(a.batch) * (a.N / kUwN) * tiles_m < 256) {
         dim3 grid(a.batch, a.N / (kUwN / 2), tiles_m);
         hipLaunchKernelGGL(k_gemm_uk_wide<kUwN / 2>, grid, dim3(256), 0, stream, a);

@@ -1228,8 +1228,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tile_dma(GemmArgs a, int ksplit
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int z = blockIdx.z / ksplit, ks = blockIdx.z - z * ksplit;
   const int n0 = blockIdx.x * TN, m0 = blockIdx.y * TM;
-  // the grid's x is padded to a multiple of 8 (the two row tiles of a weight tile,
-  // blocks x and x + gridDim.x, then share an XCD and its L2): padding exits here
+  // a grid's x of more than 8 is padded to a multiple of 8 (the two row tiles of a
+  // weight tile, blocks x and x + gridDim.x, then share an XCD and its L2): padding
+  // exits here
   if (n0 >= a.N) return;
   const int kslice = a.K / ksplit;
   const int64_t kbeg = static_cast<int64_t>(ks) * kslice;
@@ -1591,6 +1592,11 @@ static bool tile_ok(const GemmArgs& a) {
   return ws_ok(a) && a.M >= 256 && a.K % kTk == 0 && a.n_split % 2 == 0 && groups >= 256;
 }
 
+// Column tiles of a tiled product's grid: more than 8 are padded to a multiple of 8
+// (k_gemm_tile_dma), so that blocks x and x + gridDim.x share an XCD; fewer stay as
+// they are (padding one column tile to 8 would put every real block on one XCD).
+static unsigned xcd_pad(unsigned x) { return x > 8 ? (x + 7) / 8 * 8 : x; }
+
 // The fused query projection + latent append runs on k_gemm_xs (decode batches)
 // and on the copy-staged tiled product (M >= 256).
 bool fused_qa_ok(const GemmArgs& a) {
@@ -1726,7 +1732,7 @@ hipError_t launch_gemm_fast(const GemmArgs& a, void* partial, size_t partial_byt
     if (a.x_f32)
       hipLaunchKernelGGL((k_gemm_tile<float, kTt, kTt>), grid, dim3(256), 0, stream, b);
     else if (a.n_split % kTt == 0 || a.n_split >= a.N)
-      hipLaunchKernelGGL((k_gemm_tile_dma<kTt, kTt>), dim3((grid.x + 7) / 8 * 8, grid.y, grid.z),
+      hipLaunchKernelGGL((k_gemm_tile_dma<kTt, kTt>), dim3(xcd_pad(grid.x), grid.y, grid.z),
                          dim3(256), 0, stream, b, 1, nullptr);
     else
       hipLaunchKernelGGL((k_gemm_tile<bf16_t, kTt, kTt>), grid, dim3(256), 0, stream, b);
@@ -1740,7 +1746,7 @@ hipError_t launch_gemm_fast(const GemmArgs& a, void* partial, size_t partial_byt
   if (const int d = tile_split_d(a)) {
     if (partial == nullptr || !aligned16(partial) || partial_bytes < gemm_partial_bytes(a))
       return hipErrorInvalidValue;
-    const dim3 grid(((a.N + kTt - 1) / kTt + 7) / 8 * 8, (a.M + kTt - 1) / kTt, a.batch * d);
+    const dim3 grid(xcd_pad((a.N + kTt - 1) / kTt), (a.M + kTt - 1) / kTt, a.batch * d);
     hipLaunchKernelGGL((k_gemm_tile_dma<kTt, kTt>), grid, dim3(256), 0, stream, a, d,
                        static_cast<float*>(partial));
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;

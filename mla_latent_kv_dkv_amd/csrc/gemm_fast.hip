@@ -1592,6 +1592,8 @@ static bool tile_ok(const GemmArgs& a) {
   return ws_ok(a) && a.M >= 256 && a.K % kTk == 0 && a.n_split % 2 == 0 && groups >= 256;
 }
 
+bool gemm_tiled_ok(const GemmArgs& a) { return ws_ok(a) && tile_ok(a); }
+
 // Column tiles of a tiled product's grid: more than 8 are padded to a multiple of 8
 // (k_gemm_tile_dma), so that blocks x and x + gridDim.x share an XCD; fewer stay as
 // they are (padding one column tile to 8 would put every real block on one XCD).

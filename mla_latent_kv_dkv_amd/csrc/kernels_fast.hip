@@ -1790,7 +1790,12 @@ __global__ __launch_bounds__(256) void k_merge_rows(MergeArgs a, int rows) {
     }
     z = zz;
     const float inv = zz > 0.f ? 1.f / zz : 0.f;
-    dst[v] = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    const float4 r = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    if (a.o_lat_bf16)
+      reinterpret_cast<uint2*>(a.o_lat_bf16)[static_cast<int64_t>(row) * dq + v] =
+          make_uint2(cvt2(r.x, r.y), cvt2(r.z, r.w));
+    else
+      dst[v] = r;
   }
   if (a.lse && lane == 0) a.lse[row] = z > 0.f ? m + __logf(z) : -INFINITY;
 }
@@ -1863,6 +1868,13 @@ __global__ __launch_bounds__(256) void k_merge_rows_wide(MergeArgs a) {
   if (a.lse && tid == 0) a.lse[row] = z > 0.f ? m + __logf(z) : -INFINITY;
 }
 
+// The bf16 output form (k_merge_rows only: a plan, or at most kMergeWideS
+// uniform splits; 8-byte aligned rows).
+bool merge_bf16_ok(const MergeArgs& a) {
+  return (a.unit_start != nullptr || a.num_splits <= kMergeWideS) && a.d_latent % 4 == 0 &&
+         (reinterpret_cast<uintptr_t>(a.o_lat_bf16) & 7) == 0;
+}
+
 bool fast_merge_ok(const MergeArgs& a) {
   return a.d_latent % 4 == 0 && (reinterpret_cast<uintptr_t>(a.o_part) & 15) == 0 &&
          (reinterpret_cast<uintptr_t>(a.o_lat) & 15) == 0 &&
@@ -1872,6 +1884,7 @@ bool fast_merge_ok(const MergeArgs& a) {
 hipError_t launch_merge_fast(const MergeArgs& a, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
   const int rows = a.batch * a.n_heads;
+  if (a.o_lat_bf16 && !merge_bf16_ok(a)) return hipErrorInvalidValue;
   if (!a.unit_start && a.num_splits > kMergeWideS && a.d_latent == 512) {
     hipLaunchKernelGGL(k_merge_rows_wide, dim3(rows), dim3(256), 0, stream, a);
     return hipGetLastError();

@@ -145,6 +145,9 @@ struct MergeArgs {
   const int32_t* unit_start;
   int units;
   int* err;
+  // when set, k_merge_rows writes the merged rows here as bf16 (round to nearest
+  // even, the W_UV product's input precision) instead of fp32 to o_lat
+  void* o_lat_bf16;
 };
 
 // Partials of merge row b: first unit and count.

@@ -11,6 +11,8 @@ namespace mla {
 int* error_word_address();
 
 bool fast_gemm_ok(const GemmArgs& a);
+// the product runs on the tiled kernels (M >= 256 and enough output tiles)
+bool gemm_tiled_ok(const GemmArgs& a);
 // the query projection with the fused latent append (EPI_QPROJ_APPEND) on k_gemm_xs
 bool fused_qa_ok(const GemmArgs& a);
 // fp32 scratch the fast GEMM needs for its K-split partials (0 if none)
@@ -26,6 +28,7 @@ hipError_t launch_attention_fast(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attention_fp8(const AttnArgs& a, hipStream_t stream);
 
 bool fast_merge_ok(const MergeArgs& a);
+bool merge_bf16_ok(const MergeArgs& a);
 hipError_t launch_merge_fast(const MergeArgs& a, hipStream_t stream);
 // the per-head W_UV product (`a`, as mla_absorb_out sets it up, x unused) with
 // the split merge `m` folded into its operand loads (m.o_lat unused)

@@ -364,13 +364,16 @@ size_t absorb_out_bytes(const mla_dims* d, int batch) {
 
 // The two products of the absorbed output with `ws` (256-byte aligned, at least
 // absorb_out_bytes) as their scratch.
-mla_status absorb_out_run(const mla_dims* d, const float* o_lat, const void* w_uv, const void* w_o,
-                          int32_t batch, float* u, void* ws, size_t ws_bytes, hipStream_t stream) {
+mla_status absorb_out_run(const mla_dims* d, const void* o_lat, const void* w_uv, const void* w_o,
+                          int32_t batch, float* u, void* ws, size_t ws_bytes, hipStream_t stream,
+                          bool o_lat_bf16 = false) {
   char* part = static_cast<char*>(ws) + act_bytes(d, batch);
   const size_t pbytes = ws_bytes - act_bytes(d, batch);
   // 1) o[b, i*d_h + e] = sum_c W_UV[i*d_h + e, c] o_lat[b, i, c] per head i -> workspace
+  //    (o_lat fp32, or already rounded to bf16, the product's input precision)
   mla::GemmArgs g = uv_args(d, batch);
   g.x = o_lat; g.w1 = w_uv; g.w2 = w_uv; g.y = ws;
+  if (o_lat_bf16) g.x_f32 = 0;
   if (run_gemm(d, g, part, pbytes, stream) != hipSuccess) return MLA_ERR_HIP;
   // 2) u = o W_O^T
   mla::GemmArgs a = oproj_args(d, batch);
@@ -947,6 +950,18 @@ mla_status mla_merge_absorb_out(const mla_dims* d, const float* o_part, const fl
     a.x = ws; a.w1 = w_o; a.w2 = w_o; a.y = u;
     return hip_status(run_gemm(d, a, static_cast<char*>(ws) + act_bytes(d, batch),
                                base - act_bytes(d, batch), stream));
+  }
+  // Batches whose W_UV runs on the tiled product (>= 256 rows): the merge writes its
+  // rows in bf16, the precision that product reads them in, and the product takes
+  // them as such (half the bytes of an fp32 o_lat, each way; the same products)
+  mla::GemmArgs gb = uv_args(d, batch);
+  gb.x = o_lat; gb.w1 = w_uv; gb.w2 = w_uv; gb.y = ws; gb.x_f32 = 0;
+  mla::MergeArgs mb = m;
+  mb.o_lat_bf16 = o_lat;
+  if (use_fast() && d->dtype == MLA_BF16 && mla::fast_merge_ok(mb) && mla::merge_bf16_ok(mb) &&
+      mla::gemm_tiled_ok(gb)) {
+    if (mla::launch_merge_fast(mb, stream) != hipSuccess) return MLA_ERR_HIP;
+    return absorb_out_run(d, o_lat, w_uv, w_o, batch, u, ws, base, stream, true);
   }
   st = merge_run(d, o_part, lse_part, batch, m.num_splits, m.unit_start, m.units, o_lat, lse,
                  stream);

@@ -185,3 +185,31 @@ def test_merge_absorb_out_bad_plan_range(path):
     starts = plan[3 * n:]
     ru, rl = _oracle_rows(w, host, o_h, l_h, [list(range(starts[0], starts[1]))])
     assert_parity(to_np(u_f)[:1], ru, w.dtype, "u row 0 beside the bad one")
+
+
+def test_merge_absorb_out_256_rows_bf16_merge():
+    """256 rows (the ragged batch): W_UV runs on the tiled product, so the merge
+    writes its rows in bf16, the precision that product reads them in.  u and lse
+    equal the two calls' bit for bit (mla_merge_lse writes fp32 o_lat, which
+    mla_absorb_out's product rounds the same way), and the oracle's on sampled rows."""
+    w = I.WORKLOADS["full"]
+    B, S, nh = 256, 3, w.n_heads
+    note(f"merge_absorb_out full B={B} S={S} (bf16 merge rows)")
+    d = _dims(w)
+    wdev, host = _weights(w)
+    empty = np.zeros((B * S, nh), dtype=bool)
+    empty.reshape(B, S, nh)[1, ::2] = True
+    empty.reshape(B, S, nh)[2, :, 0] = True
+    empty.reshape(B, S, nh)[0, 1:] = True
+    o, lse, o_h, l_h = _partials(w, B * S, nh, empty)
+    o4, lse3 = o.view(B, S, nh, w.d_latent), lse.view(B, S, nh)
+    M.mla_device_error(clear=True)
+    u_f, lse_f = _fused(d, o4, lse3, wdev, B)
+    u_t, lse_t = _two_calls(d, o4, lse3, wdev, B)
+    np.testing.assert_array_equal(to_np(u_f), to_np(u_t))
+    np.testing.assert_array_equal(to_np(lse_f), to_np(lse_t))
+    rows = [0, 1, 2, 127, 128, B - 1]
+    ru, rl = _oracle_rows(w, host, o_h, l_h, [list(range(b * S, (b + 1) * S)) for b in rows])
+    assert_parity(to_np(u_f)[rows], ru, w.dtype, "u")
+    assert_parity(to_np(lse_f)[rows], rl, w.dtype, "lse")
+    assert M.mla_device_error() == 0

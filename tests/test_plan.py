@@ -91,3 +91,19 @@ def test_plan_errors():
     assert lib.mla_decode_plan(P(bad), 2, 64, 4, P(out), cap) == -2
     assert M.mla_decode_plan_capacity(-1, 4) == 0
     assert lib.mla_decode_plan(P(lens), 2, 64, 4, P(out), cap) == 8
+
+
+def test_plan_random_batches():
+    """Seeded random ragged batches (empty sequences included, targets below and far
+    above the batch size): every property above, and a count within the target
+    whenever the batch alone does not exceed it."""
+    rng = np.random.default_rng(20261204)
+    for _ in range(40):
+        B = int(rng.integers(1, 90))
+        lens = rng.integers(0, 20000, size=B)
+        lens[rng.random(B) < 0.1] = 0
+        page = int(rng.choice([16, 64]))
+        target = int(rng.integers(1, 1200))
+        n, units, start = _check_plan(lens, page, target)
+        if target >= B:
+            assert start[-1] <= target

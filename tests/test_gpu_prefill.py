@@ -99,9 +99,10 @@ def test_prefill_attention(name, lens, page, S, queries, path, fp8):
             assert_parity(got_m[i], ref_m, dt, f"o_lat {what}")
             assert_parity(got_ml[i], ref_ml, dt, f"lse {what}")
             assert_parity(got_l[i], ref[k][1], dt, f"lse_part {what}")
-            if dt == "f32":
-                assert_parity(got_o[i], ref[k][0], dt, f"o_part {what}")
-            else:
+            # each split's output at the stated bar, and for bf16 also within the bound
+            # its bf16 weights allow element by element
+            assert_parity(got_o[i], ref[k][0], dt, f"o_part {what}")
+            if dt != "f32":
                 assert_partials_within_weight_rounding(got_o[i], ref[k][0], hq[i], hp[i], rows,
                                                        int(qp[i]) + 1, S, page, tau, w.d_latent,
                                                        what, exact_normaliser=fp8)
